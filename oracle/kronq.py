@@ -1,0 +1,402 @@
+"""Float64 oracle of the per-layer KronQ solver.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring): imported by tests, the
+smoke check and the CPU-baseline leg of the benchmark, never by the GPU library.
+
+Notation. W is o x i (row r = output channel, y = W x), X is n x i, H_X = X^T X / n,
+H_G is o x o symmetric positive definite, and the layer loss under the
+Kronecker-factored Hessian H ~ H_X (x) H_G is
+
+    L(W^) = tr(H_G dW H_X dW^T),   dW = W^ - W
+
+(KronQ review page, Background: "the full weight Hessian factorizes as H ~ H_X (x)
+H_G"; GPTQ-style methods take H_G = I). With column-stacking vec, vec(dW)^T (H_X (x)
+H_G) vec(dW) equals that trace.
+
+Pipeline (KronQ review page, Method and Key idea; spec reading):
+  1. H_X from the calibration activations.
+  2. Input side: W' = W U, H_X' = U^T H_X U with U = D_s H_i^T / sqrt(i).
+  3. Output side: W'' = V S W' with S = H_G^{1/2} (principal root), V = H_o D_t / sqrt(o).
+     Then S^{-T} H_G S^{-1} = I, so L = tr(dW'' H_X' dW''^T): a plain GPTQ loss
+     ("H_G cancels out of the quantization update", review page, Method).
+  4. Damped H = H_X' + lambda I, lambda = 0.01 mean diag; R upper with H^{-1} = R^T R.
+  5. Column sweep on W'' with R (GPTQ; the review page's Prior limitations / Goal:
+     the solver itself is unchanged).
+  6. Sensitivity tr(H_G) tr(H_X) (review page, Method (2)).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from . import hadamard
+
+# ============================================================================= step 1: H_X
+
+
+def hessian(X: np.ndarray) -> np.ndarray:
+    """H_X = X^T X / n in float64 from the exact input values (review page, Background:
+    the input activation covariance used as the layer-Hessian proxy)."""
+    X = np.asarray(X, dtype=np.float64)
+    return X.T @ X / X.shape[0]
+
+
+# ============================================================================= step 2: input rotation
+
+
+def _rot(x: np.ndarray, sign: np.ndarray, axis: int) -> np.ndarray:
+    """x -> H_d (sign * x) / sqrt(d) along ``axis``."""
+    d = x.shape[axis]
+    shape = [1] * x.ndim
+    shape[axis] = d
+    return hadamard.apply(x * np.asarray(sign, dtype=np.float64).reshape(shape), axis=axis) / np.sqrt(d)
+
+
+def _unrot(x: np.ndarray, sign: np.ndarray, axis: int) -> np.ndarray:
+    """Inverse of ``_rot``: x -> sign * (H_d^T x) / sqrt(d)."""
+    d = x.shape[axis]
+    shape = [1] * x.ndim
+    shape[axis] = d
+    return hadamard.apply(x, axis=axis, transpose=True) / np.sqrt(d) * np.asarray(sign, np.float64).reshape(shape)
+
+
+def rotation_matrix(sign: np.ndarray) -> np.ndarray:
+    """U = D_s H_d^T / sqrt(d) as a dense matrix (small d only)."""
+    d = len(sign)
+    return np.diag(np.asarray(sign, np.float64)) @ hadamard.hadamard(d).T.astype(np.float64) / np.sqrt(d)
+
+
+def rotate_in_weights(W: np.ndarray, s: np.ndarray) -> np.ndarray:
+    """W' = W U: every row w -> H_i (s * w) / sqrt(i) (review page, "Where this paper sits":
+    the QuIP/QuIP# input-side random Hadamard incoherence rotation)."""
+    return _rot(np.asarray(W, np.float64), s, axis=1)
+
+
+def rotate_in_hessian(HX: np.ndarray, s: np.ndarray) -> np.ndarray:
+    """H_X' = U^T H_X U (curvature transforms by congruence; Hessian-guided PTQ page,
+    appendix "Range clipping for weights derivation": G_{W_T} = T^T G_W)."""
+    A = _rot(np.asarray(HX, np.float64), s, axis=1)    # H_X U   (rows)
+    return _rot(A, s, axis=0)                          # U^T (.) (columns)
+
+
+# ============================================================================= step 3: output transform
+
+
+def hg_sqrt(HG: np.ndarray, form: str) -> tuple[np.ndarray, np.ndarray]:
+    """S = H_G^{1/2} (principal, symmetric positive definite) and S^{-1}, in the storage form
+    of H_G: diag -> (o,), block -> (nb, b, b), full -> (o, o).
+
+    The pages only write H_G^{1/2}; the principal root is its literal meaning."""
+    HG = np.asarray(HG, np.float64)
+    if form == "diag":
+        if np.any(HG <= 0):
+            raise np.linalg.LinAlgError("H_G not positive definite")
+        return np.sqrt(HG), 1.0 / np.sqrt(HG)
+
+    def one(A):
+        lam, Q = np.linalg.eigh(0.5 * (A + A.T))
+        if lam[0] <= 0:
+            raise np.linalg.LinAlgError("H_G not positive definite")
+        return (Q * np.sqrt(lam)) @ Q.T, (Q / np.sqrt(lam)) @ Q.T
+
+    if form == "block":
+        S = np.empty_like(HG)
+        Si = np.empty_like(HG)
+        for k in range(HG.shape[0]):
+            S[k], Si[k] = one(HG[k])
+        return S, Si
+    if form == "full":
+        return one(HG)
+    raise ValueError(form)
+
+
+def form_matmul(S: np.ndarray, form: str, M: np.ndarray) -> np.ndarray:
+    """S @ M for S in diag / block / full storage form; M has o rows."""
+    M = np.asarray(M, np.float64)
+    if form == "diag":
+        return S[:, None] * M
+    if form == "block":
+        nb, b, _ = S.shape
+        return np.einsum("kab,kbc->kac", S, M.reshape(nb, b, -1)).reshape(M.shape)
+    return S @ M
+
+
+def form_dense(S: np.ndarray, form: str) -> np.ndarray:
+    if form == "diag":
+        return np.diag(S)
+    if form == "block":
+        nb, b, _ = S.shape
+        out = np.zeros((nb * b, nb * b))
+        for k in range(nb):
+            out[k * b:(k + 1) * b, k * b:(k + 1) * b] = S[k]
+        return out
+    return np.asarray(S)
+
+
+def rotate_out(W1: np.ndarray, S: np.ndarray, form: str, t: np.ndarray) -> np.ndarray:
+    """W'' = V S W' with V = H_o D_t / sqrt(o), applied along the output axis (KronQ abstract:
+    the input-side rotation is extended to the output dimension using the gradient covariance)."""
+    return _rot(form_matmul(S, form, W1), t, axis=0)
+
+
+# ============================================================================= step 4: damping and factor
+
+
+def damped(HX2: np.ndarray, damp: float = 0.01) -> tuple[np.ndarray, float]:
+    """H = H_X'' + lambda I with lambda = damp * mean(diag H_X'') (GPTQ damping)."""
+    HX2 = np.asarray(HX2, np.float64)
+    lam = damp * float(np.mean(np.diag(HX2)))
+    return HX2 + lam * np.eye(HX2.shape[0]), lam
+
+
+def inverse_upper_factor(H: np.ndarray) -> np.ndarray:
+    """R: the upper-triangular matrix with positive diagonal such that H^{-1} = R^T R
+    (GPTQ's Cholesky form of the inverse Hessian). Definition written out."""
+    Hinv = np.linalg.inv(np.asarray(H, np.float64))
+    Hinv = 0.5 * (Hinv + Hinv.T)
+    return np.linalg.cholesky(Hinv).T
+
+
+# ============================================================================= step 5: grid and sweep
+
+
+def grid_params(v: np.ndarray, bits: int) -> tuple[np.ndarray, np.ndarray]:
+    """Asymmetric min-max grid over the last axis: shift mu = min v, step s = (max v - min v) / (2^b - 1)
+    (Hessian-guided PTQ page, Background: a grid step s and a shift mu; asymmetric shifted grid)."""
+    mu = v.min(axis=-1)
+    return mu, (v.max(axis=-1) - mu) / (2 ** bits - 1)
+
+
+def quantize(w: np.ndarray, mu: np.ndarray, s: np.ndarray, bits: int):
+    """Round to the grid: q = clamp(rne((w - mu) / s), 0, 2^b - 1), w^ = mu + s q; s = 0 gives q = 0.
+    Also returns the tie distance |u - (floor(u) + 1/2)| in grid steps."""
+    L = 2 ** bits - 1
+    pos = s > 0
+    u = np.where(pos, (w - mu) / np.where(pos, s, 1.0), 0.0)
+    q = np.clip(np.rint(u), 0, L)
+    q = np.where(pos, q, 0.0)
+    delta = np.where(pos, np.abs(u - (np.floor(u) + 0.5)), np.inf)
+    return q.astype(np.int64), mu + s * q, delta
+
+
+def sweep_plain(W2: np.ndarray, R: np.ndarray, bits: int, group: int = 0,
+                force_mask: np.ndarray | None = None, force_codes: np.ndarray | None = None,
+                stop: int | None = None) -> dict:
+    """GPTQ column sweep, per-column definition (KronQ review page, Prior limitations: GPTQ
+    solves the column-wise OBS update using H_X; "Where this paper sits": GPTQ recast the OBS
+    update column-wise). For j = 0..i-1:
+
+        at a group start set (mu, s) from the current W[:, j:j+g]  (per-row grids: once, before)
+        q_j = Q(W[:, j]);  e = (W[:, j] - w^_j) / R_jj
+        W[:, j+1:] -= e R[j, j+1:];  W[:, j] = w^_j;  row_loss += e^2
+
+    ``force_mask``/``force_codes`` (o x i) override the rounding decision at given positions
+    (used to replay a row after a near-tie flip). ``stop`` ends the sweep after that many columns
+    and returns the partially updated matrix (columns >= stop still continuous)."""
+    W = np.array(W2, dtype=np.float64)
+    o, i = W.shape
+    ng = i // group if group else 1
+    codes = np.zeros((o, i), dtype=np.int64)
+    delta = np.zeros((o, i))
+    mu_all = np.zeros((o, ng))
+    sc_all = np.zeros((o, ng))
+    loss = np.zeros(o)
+    if not group:
+        mu, s = grid_params(W, bits)
+        mu_all[:, 0], sc_all[:, 0] = mu, s
+    for j in range(i if stop is None else stop):
+        if group and j % group == 0:
+            mu, s = grid_params(W[:, j:j + group], bits)
+            mu_all[:, j // group], sc_all[:, j // group] = mu, s
+        q, deq, dl = quantize(W[:, j], mu, s, bits)
+        if force_mask is not None and force_mask[:, j].any():
+            f = force_mask[:, j]
+            q = q.copy()
+            q[f] = force_codes[f, j]
+            deq = mu + s * q
+        e = (W[:, j] - deq) / R[j, j]
+        W[:, j + 1:] -= np.outer(e, R[j, j + 1:])
+        W[:, j] = deq
+        codes[:, j], delta[:, j] = q, dl
+        loss += e * e
+    return {"codes": codes, "mu": mu_all, "scale": sc_all, "Q": W, "row_loss": loss, "delta": delta}
+
+
+def sweep_blocked(W2: np.ndarray, R: np.ndarray, bits: int, group: int = 0, block: int = 128,
+                  force_mask: np.ndarray | None = None, force_codes: np.ndarray | None = None) -> dict:
+    """Same sweep with GPTQ's lazy batch updates over ``block`` columns: in-block steps update only
+    the block's own columns, and after the block W[:, b1:] -= E R[b0:b1, b1:] (spec:
+    "lazy trailing updates W[:, j+B:] -= E Hinv[B, j+B:]"). Exactly equal to ``sweep_plain`` in exact
+    arithmetic when group divides block or block divides group."""
+    W = np.array(W2, dtype=np.float64)
+    o, i = W.shape
+    if group and (block % group) and (group % block):
+        raise ValueError("group and block must divide one another")
+    ng = i // group if group else 1
+    codes = np.zeros((o, i), dtype=np.int64)
+    delta = np.zeros((o, i))
+    mu_all = np.zeros((o, ng))
+    sc_all = np.zeros((o, ng))
+    loss = np.zeros(o)
+    if not group:
+        mu, s = grid_params(W, bits)
+        mu_all[:, 0], sc_all[:, 0] = mu, s
+    for b0 in range(0, i, block):
+        b1 = min(b0 + block, i)
+        E = np.zeros((o, b1 - b0))
+        for j in range(b0, b1):
+            if group and j % group == 0:
+                mu, s = grid_params(W[:, j:j + group], bits)
+                mu_all[:, j // group], sc_all[:, j // group] = mu, s
+            q, deq, dl = quantize(W[:, j], mu, s, bits)
+            if force_mask is not None and force_mask[:, j].any():
+                f = force_mask[:, j]
+                q = q.copy()
+                q[f] = force_codes[f, j]
+                deq = mu + s * q
+            e = (W[:, j] - deq) / R[j, j]
+            W[:, j + 1:b1] -= np.outer(e, R[j, j + 1:b1])
+            W[:, j] = deq
+            E[:, j - b0] = e
+            codes[:, j], delta[:, j] = q, dl
+            loss += e * e
+        if b1 < i:
+            W[:, b1:] -= E @ R[b0:b1, b1:]
+    return {"codes": codes, "mu": mu_all, "scale": sc_all, "Q": W, "row_loss": loss, "delta": delta}
+
+
+def sweep_obs_naive(W2: np.ndarray, H: np.ndarray, bits: int, group: int = 0) -> dict:
+    """Optimal Brain Surgeon sweep with an explicitly maintained inverse (the principle GPTQ
+    recasts column-wise; review page, "Where this paper sits"). For each column j in order:
+    quantize, update the remaining free weights w_F -= (w_j - w^_j) / Hinv_jj * Hinv_{j,F}, then
+    remove j: Hinv <- Hinv - Hinv_{:,j} Hinv_{j,:} / Hinv_jj. Slow; small cases only."""
+    W = np.array(W2, dtype=np.float64)
+    o, i = W.shape
+    Hinv = np.linalg.inv(np.asarray(H, np.float64))
+    codes = np.zeros((o, i), dtype=np.int64)
+    loss = np.zeros(o)
+    if not group:
+        mu, s = grid_params(W, bits)
+    for j in range(i):
+        if group and j % group == 0:
+            mu, s = grid_params(W[:, j:j + group], bits)
+        q, deq, _ = quantize(W[:, j], mu, s, bits)
+        err = W[:, j] - deq
+        d = Hinv[j, j]
+        W[:, j + 1:] -= np.outer(err / d, Hinv[j, j + 1:])
+        W[:, j] = deq
+        loss += err * err / d
+        Hinv = Hinv - np.outer(Hinv[:, j], Hinv[j, :]) / d
+        codes[:, j] = q
+    return {"codes": codes, "Q": W, "row_loss": loss}
+
+
+# ============================================================================= packing
+
+
+def pack(codes: np.ndarray, bits: int) -> np.ndarray:
+    """Row-major b-bit codes -> little-endian uint32 words, LSB-first bit stream per row,
+    each row starting on a word boundary (requires i * b to be a multiple of 32)."""
+    o, i = codes.shape
+    if (i * bits) % 32:
+        raise ValueError("i * bits must be a multiple of 32")
+    words = np.zeros((o, i * bits // 32), dtype=np.uint64)
+    for j in range(i):
+        for t in range(bits):
+            pos = j * bits + t
+            bit = (codes[:, j].astype(np.uint64) >> np.uint64(t)) & np.uint64(1)
+            words[:, pos // 32] |= bit << np.uint64(pos % 32)
+    return words.astype(np.uint32)
+
+
+def unpack(words: np.ndarray, bits: int, i: int) -> np.ndarray:
+    w = words.astype(np.uint64)
+    out = np.zeros((w.shape[0], i), dtype=np.int64)
+    for j in range(i):
+        for t in range(bits):
+            pos = j * bits + t
+            out[:, j] |= (((w[:, pos // 32] >> np.uint64(pos % 32)) & np.uint64(1)) << np.uint64(t)).astype(np.int64)
+    return out
+
+
+def dequantize(codes: np.ndarray, mu: np.ndarray, scale: np.ndarray, group: int) -> np.ndarray:
+    """w^ = mu + s q with the group (or per-row) parameters."""
+    o, i = codes.shape
+    g = group if group else i
+    return np.repeat(mu, g, axis=1)[:, :i] + np.repeat(scale, g, axis=1)[:, :i] * codes
+
+
+# ============================================================================= verification
+
+
+def unrotate(Q2: np.ndarray, s: np.ndarray, t: np.ndarray, Sinv: np.ndarray, form: str) -> np.ndarray:
+    """W^ = S^{-1} V^T Q'' U^T: the dequantized weights in the original coordinates."""
+    A = _unrot(np.asarray(Q2, np.float64), t, axis=0)      # V^T Q''
+    A = form_matmul(Sinv, form, A)                          # S^{-1} (.)
+    return _unrot(A, s, axis=1)                             # (.) U^T: row a -> s * (H_i^T a) / sqrt(i)
+
+
+def kfac_loss(W: np.ndarray, What: np.ndarray, HX: np.ndarray, HG: np.ndarray, form: str) -> float:
+    """tr(H_G dW H_X dW^T) with the undamped H_X."""
+    dW = np.asarray(What, np.float64) - np.asarray(W, np.float64)
+    A = dW @ np.asarray(HX, np.float64)                     # o x i
+    B = form_matmul(np.asarray(HG, np.float64), form, dW)   # H_G dW
+    return float(np.sum(B * A))
+
+
+def rotated_loss(W2: np.ndarray, Q2: np.ndarray, HX2: np.ndarray) -> np.ndarray:
+    """Per-row dw''_r H dw''_r^T (sum over rows = tr(dW'' H dW''^T))."""
+    dW = np.asarray(Q2, np.float64) - np.asarray(W2, np.float64)
+    return np.einsum("ri,ri->r", dW @ np.asarray(HX2, np.float64), dW)
+
+
+# ============================================================================= step 6: sensitivity
+
+
+def trace_form(HG: np.ndarray, form: str) -> float:
+    HG = np.asarray(HG, np.float64)
+    if form == "diag":
+        return float(HG.sum())
+    if form == "block":
+        return float(np.einsum("kaa->", HG))
+    return float(np.trace(HG))
+
+
+def sensitivity(HX: np.ndarray, HG: np.ndarray, form: str) -> float:
+    """tr(H_G) tr(H_X), both undamped (review page, Method (2): the joint sensitivity metric)."""
+    return trace_form(HG, form) * float(np.trace(np.asarray(HX, np.float64)))
+
+
+# ============================================================================= whole layer
+
+
+def quantize_layer(X, W, HG, form: str, s, t, bits: int, group: int, block: int = 128,
+                   damp: float = 0.01, rotate_in: bool = True, rotate_out_on: bool = True,
+                   mode: str = "blocked", verify: bool = True) -> dict:
+    """All steps of the per-layer solver on float64 copies of the inputs."""
+    HX = hessian(X)
+    W = np.asarray(W, np.float64)
+    o, i = W.shape
+    if rotate_in:
+        W1, HX2 = rotate_in_weights(W, s), rotate_in_hessian(HX, s)
+    else:
+        W1, HX2 = W.copy(), HX.copy()
+    S, Sinv = hg_sqrt(HG, form)
+    if rotate_out_on:
+        W2 = rotate_out(W1, S, form, t)
+    else:
+        W2 = form_matmul(S, form, W1)
+    H, lam = damped(HX2, damp)
+    R = inverse_upper_factor(H)
+    sw = (sweep_blocked(W2, R, bits, group, block) if mode == "blocked" else sweep_plain(W2, R, bits, group))
+    out = {"HX": HX, "W1": W1, "HX2": HX2, "S": S, "Sinv": Sinv, "W2": W2, "lam": lam, "R": R,
+           "score": sensitivity(HX, HG, form), "words": pack(sw["codes"], bits) if (i * bits) % 32 == 0 else None, **sw}
+    if verify:
+        if rotate_in and rotate_out_on:
+            What = unrotate(sw["Q"], s, t, Sinv, form)
+        else:
+            A = form_matmul(Sinv, form, sw["Q"] if not rotate_out_on else _unrot(sw["Q"], t, axis=0))
+            What = _unrot(A, s, axis=1) if rotate_in else A
+        out["What"] = What
+        out["loss"] = kfac_loss(W, What, HX, HG, form)
+        out["loss_rot"] = float(rotated_loss(W2, sw["Q"], HX2).sum())
+    return out
