@@ -1,0 +1,196 @@
+/*
+ * kq.h — C ABI of the KronQ per-layer quantization solver on AMD Instinct MI355X (gfx950).
+ *
+ * The solver follows the KronQ method (paper review page "KronQ: LLM Quantization via
+ * Kronecker-Factored Hessian", sections Background, Method, Key idea; KronQ abstract on the
+ * Hugging Face paper page): under the Kronecker-factored Hessian H ~ H_X (x) H_G the layer loss
+ * is tr(H_G dW H_X dW^T); bidirectional incoherence processing rotates the input side with a
+ * random-sign Hadamard matrix and the output side with a rotation applied after H_G^{1/2}, which
+ * turns the loss into a plain GPTQ loss so that the unchanged GPTQ column sweep applies; a
+ * per-sublayer score tr(H_G) tr(H_X) drives mixed-precision bit allocation.
+ *
+ * Conventions shared by every call
+ *  - W is o x i (row r = output channel), X is n x i, H_X is i x i, H_G is o x o (or a diagonal,
+ *    or o/blk dense blk x blk blocks). All matrices are row-major with a leading dimension
+ *    (elements) >= the row length; leading dimensions and base pointers must be multiples of
+ *    4 elements / 16 bytes.
+ *  - Every pointer is a DEVICE pointer unless stated otherwise. The caller owns every buffer; the
+ *    library allocates no device memory. Scratch memory comes from the caller's workspace
+ *    (ws, ws_bytes), sized by kq_workspace_bytes(); a call with a smaller workspace returns
+ *    KQ_EWORKSPACE and enqueues nothing.
+ *  - Calls validate their arguments on the host, enqueue their kernels on `stream` (a
+ *    hipStream_t; NULL = the default stream) and return without synchronising the host. Errors
+ *    found on the host are returned; numerical failures found on the device (a matrix that is
+ *    not positive definite) are written to a device int32 `info` (0 = success) that the caller
+ *    reads after synchronising the stream.
+ *  - Results are deterministic: fixed reduction orders, no order-dependent atomics.
+ *  - No C++ exception crosses the ABI. The library keeps no state between calls and is safe to
+ *    call from several host threads on different streams.
+ */
+#ifndef KQ_H
+#define KQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* kq_stream; /* same type as hipStream_t */
+
+typedef enum {
+    KQ_OK = 0,
+    KQ_EINVAL = 1,        /* null / misaligned pointer, bad enum, bad scalar */
+    KQ_ESHAPE = 2,        /* inconsistent or unsupported sizes */
+    KQ_ENOTPD = 3,        /* reserved: host-detected non-PD input */
+    KQ_EUNSUPPORTED = 4,  /* dimension without a Hadamard order, bits/group not supported */
+    KQ_EHIP = 5,          /* a HIP launch failed; detail in kq_last_error() */
+    KQ_EWORKSPACE = 6     /* workspace smaller than kq_workspace_bytes() */
+} kq_status;
+
+typedef enum { KQ_F32 = 0, KQ_BF16 = 1 } kq_dtype;
+
+typedef enum {
+    KQ_HG_DIAG = 0,   /* o floats */
+    KQ_HG_BLOCK = 1,  /* (o/blk) dense blk x blk blocks, stored one after another */
+    KQ_HG_FULL = 2    /* o x o dense, leading dimension o */
+} kq_hg_form;
+
+typedef enum {
+    KQ_OP_HESSIAN = 0,
+    KQ_OP_ROTATE_IN = 1,
+    KQ_OP_HG_SQRT = 2,
+    KQ_OP_ROTATE_OUT = 3,
+    KQ_OP_CHOLINV = 4,
+    KQ_OP_QUANTIZE = 5,
+    KQ_OP_UNROTATE = 6,
+    KQ_OP_LOSS = 7
+} kq_op;
+
+/* Workspace bytes needed by `op` for a layer of o x i weights, n calibration tokens (X dtype
+ * xdt), `bits`, `group` and H_G `form`/`blk`. Arguments an op does not use are ignored. */
+size_t kq_workspace_bytes(kq_op op, int64_t o, int64_t i, int64_t n, kq_dtype xdt, int bits, int group,
+                          kq_hg_form form, int64_t blk);
+
+/*
+ * H_X accumulation (review page, Background: the input activation covariance H_X as the
+ * layer-Hessian proxy; Prior limitations: GPTQ's OBS update uses H_X only).
+ *     H <- beta * H + alpha * X^T X
+ * X: n x d, row-major, leading dimension ldx, fp32 or bf16 (xdt). H: d x d fp32, leading
+ * dimension d, written in full (both triangles, exactly symmetric). With alpha = 1/n_total and
+ * beta = 0 for the first token batch and 1 for later ones, H becomes X^T X / n_total over all
+ * batches. bf16 inputs are multiplied exactly (bf16 x bf16 products are exact in fp32) and
+ * accumulated in fp32. n = 0 only scales H by beta.
+ */
+kq_status kq_hessian_accum(const void* X, kq_dtype xdt, int64_t n, int64_t d, int64_t ldx, float alpha,
+                           float beta, float* H, void* ws, size_t ws_bytes, kq_stream stream);
+
+/*
+ * Input-side incoherence rotation (review page, "Where this paper sits": the QuIP / QuIP#
+ * random Hadamard rotations; Method (1)).
+ *     U = D_s H_i^T / sqrt(i),   Wout = Win U,   HX <- U^T HX U   (HX may be NULL)
+ * Every row w of W becomes H_i (s * w) / sqrt(i). H_i = P_m (x) H_{2^k} with i = m 2^k, H_{2^k}
+ * Sylvester's matrix and P_m a Paley type-I matrix of order m = q + 1 (q a prime, 27 or 343,
+ * q = 3 mod 4), m the smallest such order dividing i; KQ_EUNSUPPORTED if none exists.
+ * Win: o x i, fp32 or bf16 (wdt), leading dimension ldwin. Wout: o x i fp32, leading dimension
+ * ldw; Wout may equal Win when wdt = KQ_F32 and ldw = ldwin. sign_in: i int8 values +-1.
+ * HX: i x i fp32, leading dimension i, transformed in place.
+ */
+kq_status kq_rotate_in(const void* Win, kq_dtype wdt, int64_t ldwin, float* Wout, int64_t ldw, int64_t o,
+                       int64_t i, float* HX, const int8_t* sign_in, void* ws, size_t ws_bytes, kq_stream stream);
+
+/*
+ * Output-side factor S = H_G^{1/2}, the principal (symmetric positive definite) square root, and
+ * S^{-1} (KronQ abstract and review page Method (1): the output side of bidirectional
+ * incoherence processing uses the gradient covariance; S^{-1} H_G S^{-1} = I makes H_G cancel).
+ * HG, S and Sinv share the storage form: diag (o floats), block (o/blk blocks of blk x blk), or
+ * full (o x o). Diagonal: elementwise square root. Block and full: scaled Denman-Beavers
+ * iteration in fp64 with Cholesky-based SPD inverses, stopped on a device-side convergence test.
+ * Sinv may be NULL. info (device int32): 0, or k > 0 if H_G (or an iterate) is not positive
+ * definite (k = 1 + index of the failing pivot). The caller may free HG once the work has
+ * completed in stream order (H_G is only needed transiently).
+ */
+kq_status kq_hg_sqrt(const float* HG, kq_hg_form form, int64_t o, int64_t blk, float* S, float* Sinv,
+                     int32_t* info, void* ws, size_t ws_bytes, kq_stream stream);
+
+/*
+ * Output-side transform: W <- V S W with V = H_o D_t / sqrt(o) applied along the output axis
+ * (columns of the row-major W). S in the storage form given (from kq_hg_sqrt).
+ * W: o x i fp32, leading dimension ldw, in place. sign_out: o int8 values +-1.
+ */
+kq_status kq_rotate_out(float* W, int64_t o, int64_t i, int64_t ldw, const float* S, kq_hg_form form,
+                        int64_t blk, const int8_t* sign_out, void* ws, size_t ws_bytes, kq_stream stream);
+
+/*
+ * Damped factor of the inverse Hessian (GPTQ's Cholesky form of H^{-1}).
+ *     lambda = damp * mean(diag HX),   H = HX + lambda I,   R upper-triangular, H^{-1} = R^T R
+ * computed without forming H^{-1}: with J the reversal permutation, J H J = L L^T (Cholesky) and
+ * R = J L^{-1} J. The factorisation and the triangular inverse run in fp64 (MFMA); R is rounded to
+ * fp32, so its error is that rounding rather than sqrt(cond(H)) fp32 steps.
+ * HX: i x i fp32 (only its lower triangle is read), leading dimension ldh.
+ * R: i x i fp32, leading dimension i, upper triangle written, strict lower triangle zeroed.
+ * info (device int32): 0, or k > 0 if H is not positive definite (k = 1 + index, counted from the
+ * last row, of the first failing pivot). No automatic re-damping.
+ */
+kq_status kq_cholinv(const float* HX, int64_t i, int64_t ldh, float damp, float* R, int32_t* info, void* ws,
+                     size_t ws_bytes, kq_stream stream);
+
+/*
+ * GPTQ column sweep (review page, Prior limitations and Goal: the column-wise OBS update with H_X
+ * only, kept unchanged; the H_G factor does not appear). For j = 0 .. i-1 in natural order:
+ *     q_j = clamp(rne((W[:,j] - mu) / s), 0, 2^b - 1),  w^_j = mu + s q_j
+ *     e = (W[:,j] - w^_j) / R_jj,  W[:, j+1:] -= e R[j, j+1:],  W[:,j] = w^_j,  row_loss += e^2
+ * run in column blocks of `block` (128) with lazy trailing updates W[:, b1:] -= E R[b0:b1, b1:].
+ * Grid: asymmetric min-max, mu = min v, s = (max v - min v) / (2^b - 1) (s = 0 gives q = 0), over
+ * v = the whole row before the sweep (group = 0) or v = W[r, j:j+group] as updated when the sweep
+ * reaches j (group > 0; group must divide block or block divide group).
+ * W: o x i fp32, leading dimension ldw; in: W'' (rotated weights), out: w^ (dequantized, rotated
+ * coordinates). R: i x i upper fp32 from kq_cholinv, leading dimension ldr.
+ * codes: o x (i*bits/32) uint32 words, row-major; per row an LSB-first stream of b-bit fields in
+ * little-endian words (i*bits must be a multiple of 32). scale, offset: o x (i/group) fp32 (or o
+ * when group = 0); dequantize with offset + scale * q. row_loss: o fp32 (may be NULL).
+ * bits in 2..8; i must be a multiple of `block`.
+ */
+kq_status kq_quantize_layer(float* W, int64_t o, int64_t i, int64_t ldw, const float* R, int64_t ldr, int bits,
+                            int group, int block, uint32_t* codes, float* scale, float* offset, float* row_loss,
+                            void* ws, size_t ws_bytes, kq_stream stream);
+
+/*
+ * Sublayer sensitivity tr(H_G) * tr(H_X), both undamped (review page, Method (2)). HX: i x i fp32,
+ * leading dimension ldh (a rotated H_X gives the same trace up to rounding). HG in its storage
+ * form. score: one device double.
+ */
+kq_status kq_sensitivity(const float* HX, int64_t i, int64_t ldh, const float* HG, kq_hg_form form, int64_t o,
+                         int64_t blk, double* score, kq_stream stream);
+
+/*
+ * Verification: dequantized weights in the original coordinates,
+ *     What = S^{-1} V^T Q U^T
+ * Q: o x i fp32 (the w^ output of kq_quantize_layer), leading dimension ldq; What: o x i fp32,
+ * leading dimension ldw (must not alias Q). Sinv in the storage form of H_G.
+ */
+kq_status kq_unrotate(const float* Q, int64_t o, int64_t i, int64_t ldq, const int8_t* sign_in,
+                      const int8_t* sign_out, const float* Sinv, kq_hg_form form, int64_t blk, float* What,
+                      int64_t ldw, void* ws, size_t ws_bytes, kq_stream stream);
+
+/*
+ * Verification: layer loss in rotated coordinates, sum_r (Q - W2)_r HX2 (Q - W2)_r^T, which equals
+ * tr(H_G dW H_X dW^T) in the original coordinates when HX2 is the rotated, undamped H_X.
+ * W2, Q: o x i fp32 (leading dimension ldw); HX2: i x i fp32 (leading dimension ldh).
+ * row_loss (may be NULL): o doubles; loss: one device double.
+ */
+kq_status kq_layer_loss(const float* W2, const float* Q, int64_t o, int64_t i, int64_t ldw, const float* HX2,
+                        int64_t ldh, double* row_loss, double* loss, void* ws, size_t ws_bytes, kq_stream stream);
+
+/* Text of a status code; thread-local detail of the last error on this host thread. */
+const char* kq_strerror(kq_status status);
+const char* kq_last_error(void);
+/* Hadamard decomposition used for dimension d: returns m (and 2^k in *pow2), or 0 if unsupported. */
+int64_t kq_hadamard_order(int64_t d, int64_t* pow2);
+int kq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KQ_H */

@@ -169,5 +169,5 @@ def apply(x: np.ndarray, axis: int = -1, transpose: bool = False) -> np.ndarray:
         P = paley(m).astype(np.float64)
         if transpose:
             P = P.T
-        y = np.einsum("ab,...bc->...ac", P, y)
+        y = np.matmul(P, y)
     return np.moveaxis(y.reshape(x.shape), -1, axis)

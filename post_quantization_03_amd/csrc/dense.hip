@@ -1,0 +1,759 @@
+// Dense linear algebra on MFMA for gfx950: a batched GEMM (fp32 and fp64 matrix cores), a blocked
+// Cholesky factorisation, a triangular inverse, and the two ABI calls built on them:
+//   kq_cholinv  - damped factor R of H^{-1} (GPTQ's Cholesky form of the inverse Hessian), factorised
+//                 in fp64 and rounded to fp32
+//   kq_hg_sqrt  - principal square root of H_G and its inverse (output side of bidirectional
+//                 incoherence processing), by the scaled Denman-Beavers iteration in fp64.
+#include <cmath>
+
+#include "kq_internal.h"
+
+namespace kq {
+
+typedef float f4v __attribute__((ext_vector_type(4)));
+typedef double d4v __attribute__((ext_vector_type(4)));
+
+template <typename T>
+struct Mfma;
+// Accumulator layouts differ: fp32 16x16x4 keeps rows 4*(l/16)+r in lane l, fp64 16x16x4 keeps
+// rows 4*r + l/16 (both with column l%16); checked with a one-wave probe on gfx950.
+template <>
+struct Mfma<float> {
+    typedef f4v acc_t;
+    __device__ static inline acc_t mma(float a, float b, acc_t c) {
+        return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+    }
+    __device__ static inline int row(int lane, int r) { return 4 * (lane >> 4) + r; }
+};
+template <>
+struct Mfma<double> {
+    typedef d4v acc_t;
+    __device__ static inline acc_t mma(double a, double b, acc_t c) {
+        return __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0);
+    }
+    __device__ static inline int row(int lane, int r) { return 4 * r + (lane >> 4); }
+};
+
+template <typename T>
+struct alignas(16) V16 {
+    T v[16 / sizeof(T)];
+};
+
+constexpr int GBM = 128, GBN = 128, GPAD = 16;
+
+// ===================================================================================== GEMM kernel
+// 256 threads = 4 waves in a 2 x 2 arrangement; each wave owns a 64 x 64 block of C as 4 x 4
+// MFMA 16x16 tiles (K = 4 per instruction). K is staged through LDS in slices of 64 bytes per row
+// (16 floats / 8 doubles), double-buffered with one barrier per slice. LDS tiles are stored
+// k-major with a 16-element pad so that the 16-lane groups of an MFMA operand read hit disjoint
+// banks. MFMA operand layout (16x16x4): lane l holds A[l%16][l/16] and B[l/16][l%16]; the 4
+// accumulator registers hold column l%16 of C in the rows given by Mfma<T>::row.
+template <typename T, bool TA, bool TB, bool VEC>
+__global__ __launch_bounds__(256) void gemm_kernel(GemmArgs<T> g) {
+    if (g.skip && *g.skip) return;
+    constexpr int BK = 64 / sizeof(T);
+    constexpr int VN = 16 / sizeof(T);
+    __shared__ T As[2][BK][GBM + GPAD];
+    __shared__ T Bs[2][BK][GBN + GPAD];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t m0 = (int64_t)blockIdx.y * GBM, n0 = (int64_t)blockIdx.x * GBN;
+    if (g.tri == 1 && n0 > m0 + GBM - 1) return;
+    if (g.tri == 2 && m0 > n0 + GBN - 1) return;
+    const int64_t z = blockIdx.z, z1 = z / g.nb2, z2 = z % g.nb2;
+    const T* __restrict__ A = g.A + z1 * g.sA1 + z2 * g.sA2;
+    const T* __restrict__ B = g.B + z1 * g.sB1 + z2 * g.sB2;
+    T* C = g.C + z1 * g.sC1 + z2 * g.sC2;
+    const int8_t* rs = g.rsign ? g.rsign + z1 * g.sR1 + z2 * g.sR2 : nullptr;
+    const int8_t* cs = g.csign ? g.csign + z1 * g.sS1 + z2 * g.sS2 : nullptr;
+    const int64_t M = g.M, N = g.N;
+    int64_t kb = 0, ke = g.K;
+    if (g.kmode & 1) kb = kb > m0 ? kb : m0;
+    if (g.kmode & 2) kb = kb > n0 ? kb : n0;
+    if (g.kmode & 4) ke = ke < m0 + GBM ? ke : m0 + GBM;
+    if (g.kmode & 8) ke = ke < n0 + GBN ? ke : n0 + GBN;
+    kb = (kb / BK) * BK;
+
+    typename Mfma<T>::acc_t acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int j = 0; j < 4; j++) acc[i][j] = typename Mfma<T>::acc_t{0, 0, 0, 0};
+
+    const int wm = wave >> 1, wn = wave & 1;
+    T ra[2][VN], rb[2][VN];
+    const bool fullMN = (m0 + GBM <= M) && (n0 + GBN <= N);
+
+    auto gload = [&](int64_t k0) {
+        const bool full = VEC && fullMN && (k0 + BK <= ke);
+#pragma unroll
+        for (int q = 0; q < 2; q++) {
+            const int v = tid + 256 * q;
+            // ---- A
+            {
+                int64_t gm, gk;
+                if (!TA) { gm = m0 + (v >> 2); gk = k0 + (v & 3) * VN; }
+                else { gk = k0 + v / (GBM / VN); gm = m0 + (v % (GBM / VN)) * VN; }
+                const T* p = TA ? A + gk * g.lda + gm : A + gm * g.lda + gk;
+                if (full) {
+                    V16<T> t = *reinterpret_cast<const V16<T>*>(p);
+#pragma unroll
+                    for (int e = 0; e < VN; e++) ra[q][e] = t.v[e];
+                } else {
+#pragma unroll
+                    for (int e = 0; e < VN; e++) {
+                        bool in = TA ? (gk < ke && gm + e < M) : (gm < M && gk + e < ke);
+                        ra[q][e] = in ? p[e] : T(0);
+                    }
+                }
+            }
+            // ---- B
+            {
+                int64_t gn, gk;
+                if (TB) { gn = n0 + (v >> 2); gk = k0 + (v & 3) * VN; }
+                else { gk = k0 + v / (GBN / VN); gn = n0 + (v % (GBN / VN)) * VN; }
+                const T* p = TB ? B + gn * g.ldb + gk : B + gk * g.ldb + gn;
+                if (full) {
+                    V16<T> t = *reinterpret_cast<const V16<T>*>(p);
+#pragma unroll
+                    for (int e = 0; e < VN; e++) rb[q][e] = t.v[e];
+                } else {
+#pragma unroll
+                    for (int e = 0; e < VN; e++) {
+                        bool in = TB ? (gn < N && gk + e < ke) : (gk < ke && gn + e < N);
+                        rb[q][e] = in ? p[e] : T(0);
+                    }
+                }
+            }
+        }
+    };
+    auto sstore = [&](int buf) {
+#pragma unroll
+        for (int q = 0; q < 2; q++) {
+            const int v = tid + 256 * q;
+            if (!TA) {
+#pragma unroll
+                for (int e = 0; e < VN; e++) As[buf][(v & 3) * VN + e][v >> 2] = ra[q][e];
+            } else {
+#pragma unroll
+                for (int e = 0; e < VN; e++) As[buf][v / (GBM / VN)][(v % (GBM / VN)) * VN + e] = ra[q][e];
+            }
+            if (TB) {
+#pragma unroll
+                for (int e = 0; e < VN; e++) Bs[buf][(v & 3) * VN + e][v >> 2] = rb[q][e];
+            } else {
+#pragma unroll
+                for (int e = 0; e < VN; e++) Bs[buf][v / (GBN / VN)][(v % (GBN / VN)) * VN + e] = rb[q][e];
+            }
+        }
+    };
+
+    if (kb < ke) {
+        gload(kb);
+        sstore(0);
+        __syncthreads();
+        int buf = 0;
+        for (int64_t k0 = kb; k0 < ke; k0 += BK) {
+            const bool more = k0 + BK < ke;
+            if (more) gload(k0 + BK);
+#pragma unroll
+            for (int kk = 0; kk < BK; kk += 4) {
+                T a[4], b[4];
+                const int kr = kk + (lane >> 4);
+#pragma unroll
+                for (int i = 0; i < 4; i++) a[i] = As[buf][kr][wm * 64 + 16 * i + (lane & 15)];
+#pragma unroll
+                for (int j = 0; j < 4; j++) b[j] = Bs[buf][kr][wn * 64 + 16 * j + (lane & 15)];
+#pragma unroll
+                for (int i = 0; i < 4; i++)
+#pragma unroll
+                    for (int j = 0; j < 4; j++) acc[i][j] = Mfma<T>::mma(a[i], b[j], acc[i][j]);
+            }
+            if (more) sstore(buf ^ 1);
+            __syncthreads();
+            buf ^= 1;
+        }
+    }
+
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                const int64_t m = m0 + wm * 64 + 16 * i + Mfma<T>::row(lane, r);
+                const int64_t n = n0 + wn * 64 + 16 * j + (lane & 15);
+                if (m >= M || n >= N) continue;
+                if (g.tri == 1 && n > m) continue;
+                if (g.tri == 2 && m > n) continue;
+                T v = g.alpha * acc[i][j][r];
+                if (rs) v *= T(rs[m]);
+                if (cs) v *= T(cs[n]);
+                T* pc = C + m * g.ldc + n;
+                if (g.beta != T(0)) v += g.beta * *pc;
+                *pc = v;
+            }
+}
+
+template <typename T>
+kq_status gemm(const GemmArgs<T>& g, bool ta, bool tb, hipStream_t st) {
+    if (g.M <= 0 || g.N <= 0) return KQ_OK;
+    constexpr int VN = 16 / sizeof(T);
+    const bool vec = aligned16(g.A) && aligned16(g.B) && g.lda % VN == 0 && g.ldb % VN == 0 &&
+                     g.sA1 % VN == 0 && g.sA2 % VN == 0 && g.sB1 % VN == 0 && g.sB2 % VN == 0;
+    dim3 grid((unsigned)((g.N + GBN - 1) / GBN), (unsigned)((g.M + GBM - 1) / GBM), (unsigned)(g.nb1 * g.nb2));
+    if (grid.y > 65535 || grid.z > 65535) return fail(KQ_ESHAPE, "gemm grid too large");
+#define KQ_GEMM_LAUNCH(TA_, TB_, V_) hipLaunchKernelGGL((gemm_kernel<T, TA_, TB_, V_>), grid, dim3(256), 0, st, g)
+    if (vec) {
+        if (!ta && !tb) KQ_GEMM_LAUNCH(false, false, true);
+        else if (!ta && tb) KQ_GEMM_LAUNCH(false, true, true);
+        else if (ta && !tb) KQ_GEMM_LAUNCH(true, false, true);
+        else KQ_GEMM_LAUNCH(true, true, true);
+    } else {
+        if (!ta && !tb) KQ_GEMM_LAUNCH(false, false, false);
+        else if (!ta && tb) KQ_GEMM_LAUNCH(false, true, false);
+        else if (ta && !tb) KQ_GEMM_LAUNCH(true, false, false);
+        else KQ_GEMM_LAUNCH(true, true, false);
+    }
+#undef KQ_GEMM_LAUNCH
+    return check_launch("gemm");
+}
+template kq_status gemm<float>(const GemmArgs<float>&, bool, bool, hipStream_t);
+template kq_status gemm<double>(const GemmArgs<double>&, bool, bool, hipStream_t);
+
+// ========================================================================================= helpers
+template <typename T>
+__global__ void fill_kernel(T* p, size_t count, T value, const int* skip) {
+    if (skip && *skip) return;
+    for (size_t e = blockIdx.x * (size_t)blockDim.x + threadIdx.x; e < count; e += (size_t)gridDim.x * blockDim.x)
+        p[e] = value;
+}
+
+template <typename T>
+kq_status fill(T* p, size_t count, T value, hipStream_t st, const int* skip) {
+    if (!count) return KQ_OK;
+    size_t blocks = (count + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    hipLaunchKernelGGL(fill_kernel<T>, dim3((unsigned)blocks), dim3(256), 0, st, p, count, value, skip);
+    return check_launch("fill");
+}
+template kq_status fill<float>(float*, size_t, float, hipStream_t, const int*);
+template kq_status fill<double>(double*, size_t, double, hipStream_t, const int*);
+template kq_status fill<int>(int*, size_t, int, hipStream_t, const int*);
+template kq_status fill<uint32_t>(uint32_t*, size_t, uint32_t, hipStream_t, const int*);
+
+// ============================================================================== Cholesky, blocked
+template <>
+int potrf_nb<float>() { return 128; }
+template <>
+int potrf_nb<double>() { return 64; }
+
+// One work-group per batch item factors the NB x NB diagonal block at (k0, k0) in LDS (16-column
+// sub-panels: a single wave factors the sub-panel with shuffles, then all threads apply the rank-16
+// update with 4 x 4 register micro-tiles), writes L back to A, and writes L^{-1} (computed in LDS
+// by forward substitution on 16 x 16 diagonal sub-blocks and recursive doubling
+// X21 = -X22 L21 X11) to X. Rows beyond n are padded with the identity.
+template <typename T, int NB>
+__global__ __launch_bounds__(256) void potrf_diag_kernel(T* A, int64_t lda, int64_t sA, T* X, int64_t ldx, int64_t sX,
+                                                         int64_t n, int64_t k0, int32_t* info, int64_t info_stride,
+                                                         double* logdet, const int* skip) {
+    if (skip && *skip) return;
+    constexpr int LD = NB + 1;
+    extern __shared__ __align__(16) unsigned char smem_raw[];
+    T* L = reinterpret_cast<T*>(smem_raw);
+    T* Xs = L + NB * LD;
+    __shared__ int failed, fail_idx;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t z = blockIdx.x;
+    A += z * sA + k0 * lda + k0;
+    X += z * sX + k0 * ldx + k0;
+    const int nbe = (int)((n - k0) < NB ? (n - k0) : NB);
+    for (int e = tid; e < NB * NB; e += 256) {
+        const int r = e / NB, c = e % NB;
+        T v;
+        if (r < nbe && c < nbe) v = (c <= r) ? A[(int64_t)r * lda + c] : T(0);
+        else v = (r == c) ? T(1) : T(0);
+        L[r * LD + c] = v;
+        Xs[r * LD + c] = T(0);
+    }
+    if (tid == 0) { failed = 0; fail_idx = 0; }
+    __syncthreads();
+
+    for (int c0 = 0; c0 < NB; c0 += 16) {
+        if (wave == 0) {
+            T val[2][16];
+#pragma unroll
+            for (int t = 0; t < 2; t++) {
+                const int r = c0 + lane + 64 * t;
+#pragma unroll
+                for (int cc = 0; cc < 16; cc++) val[t][cc] = (r < NB) ? L[r * LD + c0 + cc] : T(0);
+            }
+#pragma unroll
+            for (int cc = 0; cc < 16; cc++) {
+                const T piv = __shfl(val[0][cc], cc);
+                const bool bad = !(piv > T(0));
+                if (bad && lane == 0 && !failed) { failed = 1; fail_idx = c0 + cc; }
+                const T d = sqrt(bad ? T(1) : piv);
+                const T inv = T(1) / d;
+#pragma unroll
+                for (int t = 0; t < 2; t++) {
+                    const int r = c0 + lane + 64 * t;
+                    if (r == c0 + cc) val[t][cc] = d;
+                    else if (r > c0 + cc) val[t][cc] *= inv;
+                }
+#pragma unroll
+                for (int c2 = cc + 1; c2 < 16; c2++) {
+                    const T l2 = __shfl(val[0][cc], c2);
+#pragma unroll
+                    for (int t = 0; t < 2; t++) {
+                        const int r = c0 + lane + 64 * t;
+                        if (r >= c0 + c2) val[t][c2] -= val[t][cc] * l2;
+                    }
+                }
+            }
+#pragma unroll
+            for (int t = 0; t < 2; t++) {
+                const int r = c0 + lane + 64 * t;
+                if (r < NB) {
+#pragma unroll
+                    for (int cc = 0; cc < 16; cc++)
+                        if (r >= c0 + cc) L[r * LD + c0 + cc] = val[t][cc];
+                }
+            }
+        }
+        __syncthreads();
+        const int base = c0 + 16, rem = NB - base;
+        if (rem > 0) {
+            const int mt = rem / 4;  // micro-tiles per side (rem is a multiple of 16)
+            for (int e = tid; e < mt * mt; e += 256) {
+                const int br = e / mt, bc = e % mt;
+                if (bc > br) continue;
+                const int r = base + 4 * br, c = base + 4 * bc;
+                T s[4][4] = {};
+#pragma unroll
+                for (int t = 0; t < 16; t++) {
+                    T a[4], b[4];
+#pragma unroll
+                    for (int u = 0; u < 4; u++) { a[u] = L[(r + u) * LD + c0 + t]; b[u] = L[(c + u) * LD + c0 + t]; }
+#pragma unroll
+                    for (int u = 0; u < 4; u++)
+#pragma unroll
+                        for (int w = 0; w < 4; w++) s[u][w] += a[u] * b[w];
+                }
+#pragma unroll
+                for (int u = 0; u < 4; u++)
+#pragma unroll
+                    for (int w = 0; w < 4; w++)
+                        if (c + w <= r + u) L[(r + u) * LD + c + w] -= s[u][w];
+            }
+        }
+        __syncthreads();
+    }
+
+    // ---- L^{-1}: 16 x 16 diagonal sub-blocks by forward substitution (one thread per column)
+    if (tid < NB) {
+        const int b = tid >> 4, c = tid & 15, bs = 16 * b;
+        T x[16];
+#pragma unroll
+        for (int r = 0; r < 16; r++) {
+            T s = (r == c) ? T(1) : T(0);
+#pragma unroll
+            for (int t = 0; t < r; t++) s -= L[(bs + r) * LD + bs + t] * x[t];
+            x[r] = (r >= c) ? s / L[(bs + r) * LD + bs + r] : T(0);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; r++) Xs[(bs + r) * LD + bs + c] = x[r];
+    }
+    __syncthreads();
+    // ---- recursive doubling: X21 = -X22 (L21 X11), temporaries in the (zero) upper block
+    for (int s = 16; s < NB; s *= 2) {
+        const int np = NB / (2 * s), cnt = np * s * s;
+        for (int e = tid; e < cnt; e += 256) {
+            const int p = e / (s * s), rr = (e / s) % s, cc = e % s, r0 = 2 * p * s;
+            T a = 0;
+            for (int k = cc; k < s; k++) a += L[(r0 + s + rr) * LD + r0 + k] * Xs[(r0 + k) * LD + r0 + cc];
+            Xs[(r0 + rr) * LD + r0 + s + cc] = a;
+        }
+        __syncthreads();
+        for (int e = tid; e < cnt; e += 256) {
+            const int p = e / (s * s), rr = (e / s) % s, cc = e % s, r0 = 2 * p * s;
+            T a = 0;
+            for (int k = 0; k <= rr; k++) a += Xs[(r0 + s + rr) * LD + r0 + s + k] * Xs[(r0 + k) * LD + r0 + s + cc];
+            Xs[(r0 + s + rr) * LD + r0 + cc] = -a;
+        }
+        __syncthreads();
+        for (int e = tid; e < cnt; e += 256) {
+            const int p = e / (s * s), rr = (e / s) % s, cc = e % s, r0 = 2 * p * s;
+            Xs[(r0 + rr) * LD + r0 + s + cc] = T(0);
+        }
+        __syncthreads();
+    }
+
+    for (int e = tid; e < nbe * nbe; e += 256) {
+        const int r = e / nbe, c = e % nbe;
+        if (c <= r) {
+            A[(int64_t)r * lda + c] = L[r * LD + c];
+            X[(int64_t)r * ldx + c] = Xs[r * LD + c];
+        }
+    }
+    if (tid == 0) {
+        if (logdet) {
+            double s = 0;
+            for (int r = 0; r < nbe; r++) s += log((double)L[r * LD + r]);
+            logdet[z] += s;
+        }
+        if (failed && info && fail_idx < nbe && info[z * info_stride] == 0)
+            info[z * info_stride] = (int32_t)(k0 + fail_idx + 1);
+    }
+}
+
+template <typename T, int NB>
+static kq_status launch_diag(T* A, int64_t lda, int64_t sA, T* X, int64_t ldx, int64_t sX, int64_t n, int64_t k0,
+                             int64_t batch, int32_t* info, int64_t info_stride, double* logdet, const int* skip,
+                             hipStream_t st) {
+    const size_t smem = size_t(2) * NB * (NB + 1) * sizeof(T);
+    static bool attr = false;
+    if (!attr) {
+        hipFuncSetAttribute(reinterpret_cast<const void*>(&potrf_diag_kernel<T, NB>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+        attr = true;
+    }
+    hipLaunchKernelGGL((potrf_diag_kernel<T, NB>), dim3((unsigned)batch), dim3(256), smem, st, A, lda, sA, X, ldx, sX,
+                       n, k0, info, info_stride, logdet, skip);
+    return check_launch("potrf_diag");
+}
+
+template <typename T>
+kq_status potrf_batched(T* A, int64_t lda, int64_t sA, T* X, int64_t ldx, int64_t sX, int64_t n, int64_t batch,
+                        int32_t* info, int64_t info_stride, double* logdet, const int* skip, hipStream_t st) {
+    const int NB = potrf_nb<T>();
+    if (batch > 65535) return fail(KQ_ESHAPE, "potrf batch too large");
+    for (int64_t k0 = 0; k0 < n; k0 += NB) {
+        const int64_t nbe = (n - k0) < NB ? (n - k0) : NB, k1 = k0 + nbe;
+        if (sizeof(T) == 4)
+            KQ_TRY((launch_diag<T, 128>(A, lda, sA, X, ldx, sX, n, k0, batch, info, info_stride, logdet, skip, st)));
+        else
+            KQ_TRY((launch_diag<T, 64>(A, lda, sA, X, ldx, sX, n, k0, batch, info, info_stride, logdet, skip, st)));
+        if (k1 >= n) break;
+        // panel: A[k1:, k0:k1] <- A[k1:, k0:k1] X_kk^T   (in place: one tile column per work-group row)
+        GemmArgs<T> p = gemm_args<T>(n - k1, nbe, nbe, A + k1 * lda + k0, lda, X + k0 * ldx + k0, ldx,
+                                     A + k1 * lda + k0, lda, T(1), T(0));
+        p.nb1 = batch; p.sA1 = sA; p.sB1 = sX; p.sC1 = sA; p.skip = skip;
+        KQ_TRY(gemm<T>(p, false, true, st));
+        // trailing: A[k1:, k1:] -= P P^T (lower triangle)
+        GemmArgs<T> u = gemm_args<T>(n - k1, n - k1, nbe, A + k1 * lda + k0, lda, A + k1 * lda + k0, lda,
+                                     A + k1 * lda + k1, lda, T(-1), T(1));
+        u.nb1 = batch; u.sA1 = sA; u.sB1 = sA; u.sC1 = sA; u.tri = 1; u.skip = skip;
+        KQ_TRY(gemm<T>(u, false, true, st));
+    }
+    return KQ_OK;
+}
+template kq_status potrf_batched<float>(float*, int64_t, int64_t, float*, int64_t, int64_t, int64_t, int64_t, int32_t*,
+                                        int64_t, double*, const int*, hipStream_t);
+template kq_status potrf_batched<double>(double*, int64_t, int64_t, double*, int64_t, int64_t, int64_t, int64_t,
+                                         int32_t*, int64_t, double*, const int*, hipStream_t);
+
+template <typename T>
+kq_status trtri_batched(const T* L, int64_t ldl, int64_t sL, T* X, int64_t ldx, int64_t sX, int64_t n, int64_t batch,
+                        T* Tscr, const int* skip, hipStream_t st) {
+    const int64_t NB = potrf_nb<T>();
+    const int64_t sT = n * n / 2 + NB * NB;
+    for (int64_t s = NB; s < n; s *= 2) {
+        const int64_t np = n / (2 * s);
+        const int64_t r0r = np * 2 * s, s2r = n - r0r - s;  // ragged pair (if s2r > 0)
+        for (int pass = 0; pass < 2; pass++) {
+            const int64_t cnt = pass == 0 ? np : (s2r > 0 ? 1 : 0);
+            if (!cnt) continue;
+            const int64_t r0 = pass == 0 ? 0 : r0r, s2 = pass == 0 ? s : s2r;
+            // T = L21 X11
+            GemmArgs<T> a = gemm_args<T>(s2, s, s, L + (r0 + s) * ldl + r0, ldl, X + r0 * ldx + r0, ldx,
+                                         Tscr + (pass == 0 ? 0 : np * s * s), s, T(1), T(0));
+            a.nb1 = batch; a.nb2 = cnt; a.sA1 = sL; a.sA2 = 2 * s * (ldl + 1); a.sB1 = sX; a.sB2 = 2 * s * (ldx + 1);
+            a.sC1 = sT; a.sC2 = s * s; a.kmode = 2; a.skip = skip;
+            KQ_TRY(gemm<T>(a, false, false, st));
+            // X21 = -X22 T
+            GemmArgs<T> b = gemm_args<T>(s2, s, s2, X + (r0 + s) * ldx + (r0 + s), ldx, Tscr + (pass == 0 ? 0 : np * s * s),
+                                         s, X + (r0 + s) * ldx + r0, ldx, T(-1), T(0));
+            b.nb1 = batch; b.nb2 = cnt; b.sA1 = sX; b.sA2 = 2 * s * (ldx + 1); b.sB1 = sT; b.sB2 = s * s;
+            b.sC1 = sX; b.sC2 = 2 * s * (ldx + 1); b.kmode = 4; b.skip = skip;
+            KQ_TRY(gemm<T>(b, false, false, st));
+        }
+    }
+    return KQ_OK;
+}
+template kq_status trtri_batched<float>(const float*, int64_t, int64_t, float*, int64_t, int64_t, int64_t, int64_t,
+                                        float*, const int*, hipStream_t);
+template kq_status trtri_batched<double>(const double*, int64_t, int64_t, double*, int64_t, int64_t, int64_t, int64_t,
+                                         double*, const int*, hipStream_t);
+
+}  // namespace kq
+
+using namespace kq;
+
+// ==================================================================================== kq_cholinv
+// lambda = damp * mean(diag H) in fp64 with a fixed reduction order (one work-group).
+__global__ void damp_kernel(const float* H, int64_t n, int64_t ldh, float damp, float* lam, int32_t* info) {
+    __shared__ double part[256];
+    double s = 0;
+    for (int64_t r = threadIdx.x; r < n; r += 256) s += (double)H[r * ldh + r];
+    part[threadIdx.x] = s;
+    __syncthreads();
+    for (int w = 128; w > 0; w >>= 1) {
+        if ((int)threadIdx.x < w) part[threadIdx.x] += part[threadIdx.x + w];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) {
+        *lam = (float)((double)damp * part[0] / (double)n);
+        *info = 0;
+    }
+}
+
+// Hr[a][b] = H[n-1-a][n-1-b] + lambda [a == b] in fp64, lower triangle only (read from H's lower
+// triangle).
+__global__ void reverse_damped_kernel(const float* H, int64_t n, int64_t ldh, const float* lam, double* Hr) {
+    const int64_t a = blockIdx.y;
+    for (int64_t b = blockIdx.x * 256 + threadIdx.x; b <= a && b < n; b += (int64_t)gridDim.x * 256) {
+        double v = (double)H[(n - 1 - b) * ldh + (n - 1 - a)];
+        if (a == b) v += (double)*lam;
+        Hr[a * n + b] = v;
+    }
+}
+
+// R[a][b] = X[n-1-a][n-1-b] for a <= b (rounded to fp32), 0 below the diagonal.
+__global__ void reverse_upper_kernel(const double* X, int64_t n, float* R) {
+    const int64_t a = blockIdx.y;
+    for (int64_t b = blockIdx.x * 256 + threadIdx.x; b < n; b += (int64_t)gridDim.x * 256)
+        R[a * n + b] = (b >= a) ? (float)X[(n - 1 - a) * n + (n - 1 - b)] : 0.0f;
+}
+
+static void cholinv_layout(Sizer& z, int64_t n) {
+    z.take<float>(1);
+    z.take<double>((size_t)n * n);
+    z.take<double>((size_t)n * n);
+    z.take<double>((size_t)(n * n / 2 + 64 * 64));
+}
+
+size_t cholinv_ws(int64_t n) {
+    Sizer z;
+    cholinv_layout(z, n);
+    return z.used;
+}
+
+extern "C" kq_status kq_cholinv(const float* HX, int64_t n, int64_t ldh, float damp, float* R, int32_t* info, void* ws,
+                                size_t ws_bytes, kq_stream stream) {
+    if (!HX || !R || !info) return fail(KQ_EINVAL, "kq_cholinv: null pointer");
+    if (n <= 0 || ldh < n) return fail(KQ_ESHAPE, "kq_cholinv: bad size n=%lld ldh=%lld", (long long)n, (long long)ldh);
+    if (!(damp >= 0.0f)) return fail(KQ_EINVAL, "kq_cholinv: damp must be >= 0");
+    if (ws_bytes < cholinv_ws(n) || !ws) return fail(KQ_EWORKSPACE, "kq_cholinv: workspace too small");
+    hipStream_t st = hs(stream);
+    Arena ar(ws, ws_bytes);
+    float* lam = ar.take<float>(1);
+    double* Hr = ar.take<double>((size_t)n * n);
+    double* X = ar.take<double>((size_t)n * n);
+    double* Tscr = ar.take<double>((size_t)(n * n / 2 + 64 * 64));
+    hipLaunchKernelGGL(damp_kernel, dim3(1), dim3(256), 0, st, HX, n, ldh, damp, lam, info);
+    KQ_TRY(check_launch("damp"));
+    dim3 g2((unsigned)((n + 255) / 256 < 64 ? (n + 255) / 256 : 64), (unsigned)n);
+    if (n > 65535) return fail(KQ_ESHAPE, "kq_cholinv: n too large");
+    hipLaunchKernelGGL(reverse_damped_kernel, g2, dim3(256), 0, st, HX, n, ldh, lam, Hr);
+    KQ_TRY(check_launch("reverse"));
+    KQ_TRY(fill<double>(X, (size_t)n * n, 0.0, st));
+    KQ_TRY(potrf_batched<double>(Hr, n, 0, X, n, 0, n, 1, info, 0, nullptr, nullptr, st));
+    KQ_TRY(trtri_batched<double>(Hr, n, 0, X, n, 0, n, 1, Tscr, nullptr, st));
+    hipLaunchKernelGGL(reverse_upper_kernel, g2, dim3(256), 0, st, X, n, R);
+    return check_launch("reverse_upper");
+}
+
+// ==================================================================================== kq_hg_sqrt
+namespace {
+constexpr int DB_MAXIT = 24;
+constexpr double DB_TOL = 1e-8;
+}
+
+__global__ void hg_diag_kernel(const float* h, int64_t o, float* S, float* Si, int32_t* info) {
+    for (int64_t r = blockIdx.x * 256 + threadIdx.x; r < o; r += (int64_t)gridDim.x * 256) {
+        const float v = h[r];
+        if (!(v > 0.0f)) {
+            atomicCAS(info, 0, (int32_t)(r + 1));  // any failing index; tests only check info > 0
+        }
+        const float sq = sqrtf(v > 0.0f ? v : 1.0f);
+        S[r] = sq;
+        if (Si) Si[r] = 1.0f / sq;
+    }
+}
+
+// Y_b = H_G block b (fp64), Z_b = I.
+__global__ void db_init_kernel(const float* HG, int64_t n, int64_t nbk, double* YZ, int* flags, double* ld) {
+    const int64_t nn = n * n;
+    for (int64_t e = blockIdx.x * 256 + threadIdx.x; e < nbk * nn; e += (int64_t)gridDim.x * 256) {
+        const int64_t b = e / nn, rc = e % nn, r = rc / n, c = rc % n;
+        YZ[e] = (double)HG[b * nn + rc];
+        YZ[(nbk + b) * nn + rc] = (r == c) ? 1.0 : 0.0;
+    }
+    if (blockIdx.x == 0 && threadIdx.x < 4) flags[threadIdx.x] = 0;
+    (void)ld;
+}
+
+__global__ void copy_d_kernel(const double* src, double* dst, size_t count, const int* skip) {
+    if (*skip) return;
+    for (size_t e = blockIdx.x * (size_t)256 + threadIdx.x; e < count; e += (size_t)gridDim.x * 256) dst[e] = src[e];
+}
+
+// Scaled Denman-Beavers update for the lower triangle, written symmetrically:
+//   mu = |det Y det Z|^{-1/(2n)},  Y <- (mu Y + Z^{-1} / mu) / 2,  Z <- (mu Z + Y^{-1} / mu) / 2
+// INV holds the inverses (lower triangles) in the same item order as YZ. Per-block partial sums
+// of ||Y_new - Y||^2 and ||Y_new||^2 go to part.
+__global__ void db_update_kernel(double* YZ, const double* INV, const double* ld, int64_t n, int64_t nbk, double* part,
+                                 const int* skip) {
+    if (*skip) return;
+    __shared__ double sd[256], sn[256];
+    const int64_t nn = n * n, tri = n * (n + 1) / 2;
+    double acc_d = 0, acc_n = 0;
+    for (int64_t e = blockIdx.x * 256 + threadIdx.x; e < nbk * tri; e += (int64_t)gridDim.x * 256) {
+        const int64_t b = e / tri;
+        int64_t t = e % tri;
+        // row r such that r(r+1)/2 <= t < (r+1)(r+2)/2
+        int64_t r = (int64_t)((sqrt(8.0 * (double)t + 1.0) - 1.0) * 0.5);
+        while (r * (r + 1) / 2 > t) r--;
+        while ((r + 1) * (r + 2) / 2 <= t) r++;
+        const int64_t c = t - r * (r + 1) / 2;
+        const double lmu = -(ld[b] + ld[nbk + b]) / (double)n;
+        const double mu = exp(lmu);
+        double* Y = YZ + b * nn;
+        double* Z = YZ + (nbk + b) * nn;
+        const double* Yi = INV + b * nn;
+        const double* Zi = INV + (nbk + b) * nn;
+        const double y = Y[r * n + c], zz = Z[r * n + c];
+        const double yn = 0.5 * (mu * y + Zi[r * n + c] / mu);
+        const double zn = 0.5 * (mu * zz + Yi[r * n + c] / mu);
+        const double w = (r == c) ? 1.0 : 2.0;
+        acc_d += w * (yn - y) * (yn - y);
+        acc_n += w * yn * yn;
+        Y[r * n + c] = yn;
+        Y[c * n + r] = yn;
+        Z[r * n + c] = zn;
+        Z[c * n + r] = zn;
+    }
+    sd[threadIdx.x] = acc_d;
+    sn[threadIdx.x] = acc_n;
+    __syncthreads();
+    for (int w = 128; w > 0; w >>= 1) {
+        if ((int)threadIdx.x < w) {
+            sd[threadIdx.x] += sd[threadIdx.x + w];
+            sn[threadIdx.x] += sn[threadIdx.x + w];
+        }
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) {
+        part[2 * blockIdx.x] = sd[0];
+        part[2 * blockIdx.x + 1] = sn[0];
+    }
+}
+
+// flags[0]: done, flags[1]: iterations run. Stops on convergence, non-finite values or a failed
+// factorisation (info of any item), and reports the failure to the caller's info.
+__global__ void db_converge_kernel(const double* part, int nblk, int* flags, const int32_t* finfo, int64_t nitems,
+                                   int32_t* info, double tol) {
+    if (flags[0]) return;
+    if (threadIdx.x != 0) return;
+    double d = 0, nn = 0;
+    for (int b = 0; b < nblk; b++) { d += part[2 * b]; nn += part[2 * b + 1]; }
+    int32_t bad = 0;
+    for (int64_t k = 0; k < nitems; k++)
+        if (finfo[k] != 0) { bad = finfo[k]; break; }
+    flags[1] += 1;
+    const double rel = sqrt(d / nn);
+    if (bad) { *info = bad; flags[0] = 1; return; }
+    if (!(rel == rel) || !(nn > 0)) { *info = 1; flags[0] = 1; return; }
+    if (rel < tol) flags[0] = 1;
+}
+
+__global__ void db_out_kernel(const double* YZ, int64_t n, int64_t nbk, float* S, float* Si) {
+    const int64_t nn = n * n;
+    for (int64_t e = blockIdx.x * 256 + threadIdx.x; e < nbk * nn; e += (int64_t)gridDim.x * 256) {
+        S[e] = (float)YZ[e];
+        if (Si) Si[e] = (float)YZ[nbk * nn + e];
+    }
+}
+
+namespace {
+constexpr int DB_UPD_BLOCKS = 1024;
+
+template <typename Ar>
+void hg_layout(Ar& a, int64_t n, int64_t nbk) {
+    const size_t nn = (size_t)n * n, items = 2 * (size_t)nbk;
+    a.template take<double>(items * nn);                                   // YZ
+    a.template take<double>(items * nn);                                   // LYZ / inverses
+    a.template take<double>(items * nn);                                   // X = L^{-1}
+    a.template take<double>(items * ((size_t)(n * n / 2) + 64 * 64));      // trtri scratch
+    a.template take<double>(items);                                        // logdet
+    a.template take<int32_t>(items);                                       // per-item info
+    a.template take<double>(2 * DB_UPD_BLOCKS);                            // partial sums
+    a.template take<int>(4);                                               // flags
+}
+}  // namespace
+
+size_t hg_sqrt_ws(kq_hg_form form, int64_t o, int64_t blk) {
+    if (form == KQ_HG_DIAG) return 0;
+    const int64_t n = form == KQ_HG_FULL ? o : blk, nbk = form == KQ_HG_FULL ? 1 : o / blk;
+    Sizer z;
+    hg_layout(z, n, nbk);
+    return z.used;
+}
+
+extern "C" kq_status kq_hg_sqrt(const float* HG, kq_hg_form form, int64_t o, int64_t blk, float* S, float* Sinv,
+                                int32_t* info, void* ws, size_t ws_bytes, kq_stream stream) {
+    if (!HG || !S || !info) return fail(KQ_EINVAL, "kq_hg_sqrt: null pointer");
+    if (o <= 0) return fail(KQ_ESHAPE, "kq_hg_sqrt: o must be positive");
+    hipStream_t st = hs(stream);
+    if (form == KQ_HG_DIAG) {
+        KQ_TRY(fill<int>(reinterpret_cast<int*>(info), 1, 0, st));
+        unsigned blocks = (unsigned)((o + 255) / 256 < 1024 ? (o + 255) / 256 : 1024);
+        hipLaunchKernelGGL(hg_diag_kernel, dim3(blocks), dim3(256), 0, st, HG, o, S, Sinv, info);
+        return check_launch("hg_diag");
+    }
+    if (form != KQ_HG_BLOCK && form != KQ_HG_FULL) return fail(KQ_EINVAL, "kq_hg_sqrt: bad form");
+    if (form == KQ_HG_BLOCK && (blk <= 0 || o % blk)) return fail(KQ_ESHAPE, "kq_hg_sqrt: o must be a multiple of blk");
+    const int64_t n = form == KQ_HG_FULL ? o : blk, nbk = form == KQ_HG_FULL ? 1 : o / blk;
+    if (ws_bytes < hg_sqrt_ws(form, o, blk) || !ws) return fail(KQ_EWORKSPACE, "kq_hg_sqrt: workspace too small");
+    Arena ar(ws, ws_bytes);
+    const size_t nn = (size_t)n * n, items = 2 * (size_t)nbk;
+    double* YZ = ar.take<double>(items * nn);
+    double* LYZ = ar.take<double>(items * nn);
+    double* XYZ = ar.take<double>(items * nn);
+    double* Tscr = ar.take<double>(items * ((size_t)(n * n / 2) + 64 * 64));
+    double* ld = ar.take<double>(items);
+    int32_t* finfo = ar.take<int32_t>(items);
+    double* part = ar.take<double>(2 * DB_UPD_BLOCKS);
+    int* flags = ar.take<int>(4);
+    const int* done = flags;
+
+    KQ_TRY(fill<int>(reinterpret_cast<int*>(info), 1, 0, st));
+    KQ_TRY(fill<int>(reinterpret_cast<int*>(finfo), items, 0, st));
+    unsigned eb = (unsigned)((nbk * nn + 255) / 256 < 4096 ? (nbk * nn + 255) / 256 : 4096);
+    hipLaunchKernelGGL(db_init_kernel, dim3(eb), dim3(256), 0, st, HG, n, nbk, YZ, flags, ld);
+    KQ_TRY(check_launch("db_init"));
+    const int64_t tsz = (int64_t)(n * n / 2) + 64 * 64;
+    for (int it = 0; it < DB_MAXIT; it++) {
+        unsigned cb = (unsigned)((items * nn + 255) / 256 < 4096 ? (items * nn + 255) / 256 : 4096);
+        hipLaunchKernelGGL(copy_d_kernel, dim3(cb), dim3(256), 0, st, YZ, LYZ, items * nn, done);
+        KQ_TRY(check_launch("db_copy"));
+        KQ_TRY(fill<double>(XYZ, items * nn, 0.0, st, done));
+        KQ_TRY(fill<double>(ld, items, 0.0, st, done));
+        KQ_TRY(potrf_batched<double>(LYZ, n, (int64_t)nn, XYZ, n, (int64_t)nn, n, (int64_t)items, finfo, 1, ld, done,
+                                     st));
+        KQ_TRY(trtri_batched<double>(LYZ, n, (int64_t)nn, XYZ, n, (int64_t)nn, n, (int64_t)items, Tscr, done, st));
+        (void)tsz;
+        // inverse = X^T X (lower), written over the factor copies
+        GemmArgs<double> g = gemm_args<double>(n, n, n, XYZ, n, XYZ, n, LYZ, n, 1.0, 0.0);
+        g.nb1 = (int64_t)items; g.sA1 = (int64_t)nn; g.sB1 = (int64_t)nn; g.sC1 = (int64_t)nn;
+        g.tri = 1; g.kmode = 1; g.skip = done;
+        KQ_TRY(gemm<double>(g, true, false, st));
+        hipLaunchKernelGGL(db_update_kernel, dim3(DB_UPD_BLOCKS), dim3(256), 0, st, YZ, LYZ, ld, n, nbk, part, done);
+        KQ_TRY(check_launch("db_update"));
+        hipLaunchKernelGGL(db_converge_kernel, dim3(1), dim3(64), 0, st, part, DB_UPD_BLOCKS, flags, finfo,
+                           (int64_t)items, info, DB_TOL);
+        KQ_TRY(check_launch("db_converge"));
+    }
+    hipLaunchKernelGGL(db_out_kernel, dim3(eb), dim3(256), 0, st, YZ, n, nbk, S, Sinv);
+    return check_launch("db_out");
+}

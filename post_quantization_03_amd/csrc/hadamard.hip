@@ -1,0 +1,522 @@
+// Random-sign Hadamard rotations of bidirectional incoherence processing (KronQ review page, Method
+// (1) and "Where this paper sits": the input-side QuIP/QuIP# Hadamard rotation, extended to the
+// output side after the H_G^{1/2} factor).
+//
+// H_d = P_m (x) H_{2^k} for d = m 2^k: Sylvester's H_{2^k} acts on every contiguous 2^k chunk of an
+// index, and a Paley type-I matrix P_m (order q + 1 over GF(q), q = 3 mod 4) mixes the m chunks.
+//  - along rows (contiguous): one work-group per row keeps the row in LDS and runs radix-4/radix-2
+//    butterflies; sign and scale are fused into the load and the store;
+//  - along columns (the output axis of row-major W, and the second side of H_X): "digit passes"
+//    load a D x 64 tile of rows that differ in one base-D digit of the row index into LDS and
+//    transform along it, so every pass streams the matrix once with 256-byte row segments;
+//  - the P_m factor is a dense +-1 contraction, run on the fp32 MFMA GEMM (P is generated on the
+//    device from the finite-field quadratic character).
+#include <cmath>
+
+#include "kq_internal.h"
+
+namespace kq {
+
+// ------------------------------------------------------------------------------ finite fields
+struct Field {
+    int q = 0, p = 0, e = 0, c0 = 0, c1 = 0, c2 = 0;  // GF(p^e); e = 3: modulus t^3 + c2 t^2 + c1 t + c0
+};
+
+static bool is_prime(int64_t n) {
+    if (n < 2) return false;
+    for (int64_t f = 2; f * f <= n; f++)
+        if (n % f == 0) return false;
+    return true;
+}
+
+static bool field_for(int64_t q, Field& f) {
+    if (q % 4 != 3) return false;
+    if (is_prime(q) && q < 46341) { f.q = (int)q; f.p = (int)q; f.e = 1; return true; }
+    if (q == 27) { f.q = 27; f.p = 3; f.e = 3; f.c0 = 2; f.c1 = 2; f.c2 = 0; return true; }
+    if (q == 343) { f.q = 343; f.p = 7; f.e = 3; f.c0 = 5; f.c1 = 0; f.c2 = 0; return true; }
+    return false;
+}
+
+// d = m * p2 with m the smallest order (odd part of d) * 2^a that is 1 or q + 1 for a supported q.
+static bool hadamard_split(int64_t d, int64_t& m, int64_t& p2, Field& f) {
+    if (d <= 0) return false;
+    const int64_t two = d & (-d), odd = d / two;
+    for (int64_t a = 1; a <= two; a *= 2) {
+        const int64_t mm = odd * a;
+        if (mm == 1) { m = 1; p2 = d; f = Field{}; return true; }
+        if (field_for(mm - 1, f)) { m = mm; p2 = d / mm; return true; }
+    }
+    return false;
+}
+
+__device__ inline void gf_mul3(const int* a, const int* b, int* out, int p, int c0, int c1, int c2) {
+    int t[5] = {0, 0, 0, 0, 0};
+    for (int i = 0; i < 3; i++)
+        for (int j = 0; j < 3; j++) t[i + j] = (t[i + j] + a[i] * b[j]) % p;
+    for (int deg = 4; deg >= 3; deg--) {
+        const int c = t[deg];
+        if (!c) continue;
+        t[deg] = 0;
+        t[deg - 1] = ((t[deg - 1] - c * c2) % p + p) % p;
+        t[deg - 2] = ((t[deg - 2] - c * c1) % p + p) % p;
+        t[deg - 3] = ((t[deg - 3] - c * c0) % p + p) % p;
+    }
+    out[0] = t[0]; out[1] = t[1]; out[2] = t[2];
+}
+
+// Quadratic character of element index x (base-p digits) of GF(q): x^((q-1)/2) is 1 or -1.
+__device__ inline int gf_chi(int x, Field f) {
+    if (x == 0) return 0;
+    const int ex = (f.q - 1) / 2;
+    if (f.e == 1) {
+        int64_t r = 1, b = x, k = ex;
+        while (k) {
+            if (k & 1) r = (r * b) % f.q;
+            b = (b * b) % f.q;
+            k >>= 1;
+        }
+        return r == 1 ? 1 : -1;
+    }
+    int base[3] = {x % f.p, (x / f.p) % f.p, x / (f.p * f.p)};
+    int r[3] = {1, 0, 0};
+    int k = ex;
+    while (k) {
+        if (k & 1) gf_mul3(r, base, r, f.p, f.c0, f.c1, f.c2);
+        gf_mul3(base, base, base, f.p, f.c0, f.c1, f.c2);
+        k >>= 1;
+    }
+    return (r[0] == 1 && r[1] == 0 && r[2] == 0) ? 1 : -1;
+}
+
+__device__ inline int gf_sub(int a, int b, Field f) {
+    if (f.e == 1) return ((a - b) % f.q + f.q) % f.q;
+    int out = 0, place = 1;
+    for (int i = 0; i < 3; i++) {
+        out += (((a % f.p) - (b % f.p) + f.p) % f.p) * place;
+        a /= f.p;
+        b /= f.p;
+        place *= f.p;
+    }
+    return out;
+}
+
+// P = I + [[0, 1^T], [-1, Q]] with Q_ab = chi(a - b); writes P (or P^T) as an m x m fp32 matrix.
+__global__ void paley_kernel(float* P, int m, Field f, int transpose) {
+    for (int e = blockIdx.x * 256 + threadIdx.x; e < m * m; e += gridDim.x * 256) {
+        int a = e / m, b = e % m;
+        if (transpose) { int t = a; a = b; b = t; }
+        int v;
+        if (a == 0) v = (b == 0) ? 1 : 1;
+        else if (b == 0) v = -1;
+        else v = gf_chi(gf_sub(a - 1, b - 1, f), f) + (a == b ? 1 : 0);
+        P[e] = (float)v;
+    }
+}
+
+// ------------------------------------------------------------------------------ row transform
+template <bool BF16>
+__global__ __launch_bounds__(256) void fwht_rows_kernel(const void* __restrict__ in, int64_t ldin,
+                                                        float* __restrict__ out, int64_t ldout, int64_t d, int lp2,
+                                                        const int8_t* __restrict__ pre, const int8_t* __restrict__ post,
+                                                        float scale) {
+    extern __shared__ __align__(16) float xr[];
+    const int64_t r = blockIdx.x;
+    const int tid = threadIdx.x;
+    if (BF16) {
+        const uint16_t* src = static_cast<const uint16_t*>(in) + r * ldin;
+        for (int64_t c = 4 * tid; c < d; c += 1024) {
+            const uint2 u = *reinterpret_cast<const uint2*>(src + c);
+            float v[4] = {__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xFFFF0000u), __uint_as_float(u.y << 16),
+                          __uint_as_float(u.y & 0xFFFF0000u)};
+#pragma unroll
+            for (int e = 0; e < 4; e++) xr[c + e] = pre ? v[e] * (float)pre[c + e] : v[e];
+        }
+    } else {
+        const float* src = static_cast<const float*>(in) + r * ldin;
+        for (int64_t c = 4 * tid; c < d; c += 1024) {
+            const float4 u = *reinterpret_cast<const float4*>(src + c);
+            float v[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+            for (int e = 0; e < 4; e++) xr[c + e] = pre ? v[e] * (float)pre[c + e] : v[e];
+        }
+    }
+    __syncthreads();
+    const int64_t p2 = int64_t(1) << lp2;
+    int lh = 0;
+    while ((int64_t(1) << lh) < p2) {
+        const int64_t h = int64_t(1) << lh;
+        if (2 * h < p2) {
+            for (int64_t g = tid; g < d / 4; g += 256) {
+                const int64_t j = ((g >> lh) << (lh + 2)) + (g & (h - 1));
+                const float a0 = xr[j], a1 = xr[j + h], a2 = xr[j + 2 * h], a3 = xr[j + 3 * h];
+                const float b0 = a0 + a1, b1 = a0 - a1, b2 = a2 + a3, b3 = a2 - a3;
+                xr[j] = b0 + b2;
+                xr[j + h] = b1 + b3;
+                xr[j + 2 * h] = b0 - b2;
+                xr[j + 3 * h] = b1 - b3;
+            }
+            lh += 2;
+        } else {
+            for (int64_t g = tid; g < d / 2; g += 256) {
+                const int64_t j = ((g >> lh) << (lh + 1)) + (g & (h - 1));
+                const float a0 = xr[j], a1 = xr[j + h];
+                xr[j] = a0 + a1;
+                xr[j + h] = a0 - a1;
+            }
+            lh += 1;
+        }
+        __syncthreads();
+    }
+    float* dst = out + r * ldout;
+    for (int64_t c = 4 * tid; c < d; c += 1024) {
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; e++) v[e] = post ? xr[c + e] * scale * (float)post[c + e] : xr[c + e] * scale;
+        *reinterpret_cast<float4*>(dst + c) = make_float4(v[0], v[1], v[2], v[3]);
+    }
+}
+
+// --------------------------------------------------------------------------- column digit pass
+// Rows r = (hi * D + t) * S + lo, t = 0..D-1, transformed along t for 64 columns per work-group.
+__global__ __launch_bounds__(256) void fwht_cols_kernel(const float* __restrict__ in, int64_t ldin,
+                                                        float* __restrict__ out, int64_t ldout, int64_t ncols, int lD,
+                                                        int64_t S, const float* __restrict__ pre_scale,
+                                                        const int8_t* __restrict__ pre_sign,
+                                                        const float* __restrict__ post_scale,
+                                                        const int8_t* __restrict__ post_sign, float scale) {
+    extern __shared__ __align__(16) float xc[];
+    const int D = 1 << lD;
+    const int tid = threadIdx.x;
+    const int64_t c0 = (int64_t)blockIdx.x * 64, lo = blockIdx.y, hi = blockIdx.z;
+    const int c = tid & 63;
+    const bool cin = c0 + c < ncols;
+    for (int t = tid >> 6; t < D; t += 4) {
+        const int64_t r = (hi * D + t) * S + lo;
+        float v = cin ? in[r * ldin + c0 + c] : 0.0f;
+        if (pre_scale) v *= pre_scale[r];
+        if (pre_sign) v *= (float)pre_sign[r];
+        xc[t * 64 + c] = v;
+    }
+    __syncthreads();
+    int lh = 0;
+    while (lh < lD) {
+        const int h = 1 << lh;
+        if (lh + 1 < lD) {
+            for (int g = tid >> 6; g < D / 4; g += 4) {
+                const int j = ((g >> lh) << (lh + 2)) + (g & (h - 1));
+                const float a0 = xc[j * 64 + c], a1 = xc[(j + h) * 64 + c], a2 = xc[(j + 2 * h) * 64 + c],
+                            a3 = xc[(j + 3 * h) * 64 + c];
+                const float b0 = a0 + a1, b1 = a0 - a1, b2 = a2 + a3, b3 = a2 - a3;
+                xc[j * 64 + c] = b0 + b2;
+                xc[(j + h) * 64 + c] = b1 + b3;
+                xc[(j + 2 * h) * 64 + c] = b0 - b2;
+                xc[(j + 3 * h) * 64 + c] = b1 - b3;
+            }
+            lh += 2;
+        } else {
+            for (int g = tid >> 6; g < D / 2; g += 4) {
+                const int j = ((g >> lh) << (lh + 1)) + (g & (h - 1));
+                const float a0 = xc[j * 64 + c], a1 = xc[(j + h) * 64 + c];
+                xc[j * 64 + c] = a0 + a1;
+                xc[(j + h) * 64 + c] = a0 - a1;
+            }
+            lh += 1;
+        }
+        __syncthreads();
+    }
+    if (!cin) return;
+    for (int t = tid >> 6; t < D; t += 4) {
+        const int64_t r = (hi * D + t) * S + lo;
+        float v = xc[t * 64 + c] * scale;
+        if (post_scale) v *= post_scale[r];
+        if (post_sign) v *= (float)post_sign[r];
+        out[r * ldout + c0 + c] = v;
+    }
+}
+
+// ------------------------------------------------------------------------------- host helpers
+static kq_status rows_transform(const void* in, bool bf16, int64_t ldin, float* out, int64_t ldout, int64_t R,
+                                int64_t d, int64_t p2, const int8_t* pre, const int8_t* post, float scale,
+                                hipStream_t st) {
+    if (R <= 0) return KQ_OK;
+    int lp2 = 0;
+    while ((int64_t(1) << lp2) < p2) lp2++;
+    const size_t smem = (size_t)d * sizeof(float);
+    if (smem > 160 * 1024) return fail(KQ_ESHAPE, "row transform: row of %lld elements does not fit in LDS", (long long)d);
+    static bool attr = false;
+    if (!attr) {
+        hipFuncSetAttribute(reinterpret_cast<const void*>(&fwht_rows_kernel<true>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+        hipFuncSetAttribute(reinterpret_cast<const void*>(&fwht_rows_kernel<false>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+        attr = true;
+    }
+    if (R > 2147483647) return fail(KQ_ESHAPE, "row transform: too many rows");
+    if (bf16)
+        hipLaunchKernelGGL(fwht_rows_kernel<true>, dim3((unsigned)R), dim3(256), smem, st, in, ldin, out, ldout, d, lp2,
+                           pre, post, scale);
+    else
+        hipLaunchKernelGGL(fwht_rows_kernel<false>, dim3((unsigned)R), dim3(256), smem, st, in, ldin, out, ldout, d,
+                           lp2, pre, post, scale);
+    return check_launch("fwht_rows");
+}
+
+struct ColOps {
+    const float* pre_scale = nullptr;
+    const int8_t* pre_sign = nullptr;
+    const float* post_scale = nullptr;
+    const int8_t* post_sign = nullptr;
+    float scale = 1.0f;
+};
+
+// Sylvester transform along the row index within every chunk of p2 rows (R = m * p2 rows), as a
+// sequence of digit passes of at most 2^8 rows each. The first pass reads `in`, later passes work in
+// place on `out`. Pre-multipliers go to the first pass, post-multipliers and the scale to the last.
+static kq_status cols_transform(const float* in, int64_t ldin, float* out, int64_t ldout, int64_t R, int64_t ncols,
+                                int64_t p2, const ColOps& ops, hipStream_t st) {
+    int k = 0;
+    while ((int64_t(1) << k) < p2) k++;
+    int npass = (k + 7) / 8;
+    if (npass == 0) npass = 1;
+    int64_t S = 1;
+    int done = 0;
+    for (int ps = 0; ps < npass; ps++) {
+        const int lD = (k - done) / (npass - ps);
+        const int D = 1 << lD;
+        const bool first = ps == 0, last = ps == npass - 1;
+        const size_t smem = (size_t)D * 64 * sizeof(float);
+        dim3 grid((unsigned)((ncols + 63) / 64), (unsigned)S, (unsigned)(R / ((int64_t)D * S)));
+        if (S > 65535 || R / ((int64_t)D * S) > 65535) return fail(KQ_ESHAPE, "column transform grid too large");
+        hipLaunchKernelGGL(fwht_cols_kernel, grid, dim3(256), smem, st, first ? in : out, first ? ldin : ldout, out,
+                           ldout, ncols, lD, S, first ? ops.pre_scale : nullptr, first ? ops.pre_sign : nullptr,
+                           last ? ops.post_scale : nullptr, last ? ops.post_sign : nullptr, last ? ops.scale : 1.0f);
+        KQ_TRY(check_launch("fwht_cols"));
+        S *= D;
+        done += lD;
+    }
+    return KQ_OK;
+}
+
+static kq_status make_paley(float* P, int64_t m, const Field& f, bool transpose, hipStream_t st) {
+    const unsigned blocks = (unsigned)((m * m + 255) / 256 < 1024 ? (m * m + 255) / 256 : 1024);
+    hipLaunchKernelGGL(paley_kernel, dim3(blocks), dim3(256), 0, st, P, (int)m, f, transpose ? 1 : 0);
+    return check_launch("paley");
+}
+
+// out_r = alpha * P in_r for every row r, each row seen as an m x p2 matrix (row mix of chunks).
+static kq_status paley_rows(const float* P, const float* in, int64_t ldin, float* out, int64_t ldout, int64_t R,
+                            int64_t m, int64_t p2, float alpha, hipStream_t st) {
+    for (int64_t r0 = 0; r0 < R; r0 += 65535) {
+        const int64_t cnt = (R - r0) < 65535 ? (R - r0) : 65535;
+        GemmArgs<float> g = gemm_args<float>(m, p2, m, P, m, in + r0 * ldin, p2, out + r0 * ldout, p2, alpha, 0.0f);
+        g.nb1 = cnt; g.sA1 = 0; g.sB1 = ldin; g.sC1 = ldout;
+        KQ_TRY(gemm<float>(g, false, false, st));
+    }
+    return KQ_OK;
+}
+
+// out = alpha * (P (x) I_{p2}) in along the row index (rows grouped in m chunks of p2 rows).
+static kq_status paley_cols(const float* P, const float* in, int64_t ldin, float* out, int64_t ldout, int64_t m,
+                            int64_t p2, int64_t ncols, float alpha, hipStream_t st) {
+    if (ldin == ncols && ldout == ncols) {
+        GemmArgs<float> g = gemm_args<float>(m, p2 * ncols, m, P, m, in, p2 * ncols, out, p2 * ncols, alpha, 0.0f);
+        return gemm<float>(g, false, false, st);
+    }
+    // general leading dimensions: one batched GEMM per chunk row b of every block
+    GemmArgs<float> g = gemm_args<float>(m, ncols, m, P, m, in, p2 * ldin, out, p2 * ldout, alpha, 0.0f);
+    g.nb1 = p2; g.sA1 = 0; g.sB1 = ldin; g.sC1 = ldout;
+    return gemm<float>(g, false, false, st);
+}
+
+}  // namespace kq
+
+using namespace kq;
+
+extern "C" int64_t kq_hadamard_order(int64_t d, int64_t* pow2) {
+    int64_t m, p2;
+    Field f;
+    if (!hadamard_split(d, m, p2, f)) return 0;
+    if (pow2) *pow2 = p2;
+    return m;
+}
+
+size_t rotate_in_ws(int64_t o, int64_t i) {
+    int64_t m, p2;
+    Field f;
+    if (!hadamard_split(i, m, p2, f)) return 0;
+    Sizer z;
+    z.take<float>((size_t)m * m);
+    if (m > 1) z.take<float>((size_t)(o > i ? o : i) * i);
+    return z.used;
+}
+
+extern "C" kq_status kq_rotate_in(const void* Win, kq_dtype wdt, int64_t ldwin, float* Wout, int64_t ldw, int64_t o,
+                                  int64_t i, float* HX, const int8_t* sign_in, void* ws, size_t ws_bytes,
+                                  kq_stream stream) {
+    if (!sign_in || (o > 0 && (!Win || !Wout))) return fail(KQ_EINVAL, "kq_rotate_in: null pointer");
+    if (o < 0 || i <= 0 || (o > 0 && (ldwin < i || ldw < i))) return fail(KQ_ESHAPE, "kq_rotate_in: bad sizes");
+    if (wdt != KQ_F32 && wdt != KQ_BF16) return fail(KQ_EINVAL, "kq_rotate_in: bad dtype");
+    if (i % 4 || ldwin % 4 || ldw % 4 || (Win && !aligned16(Win)) || (Wout && !aligned16(Wout)) || (HX && !aligned16(HX)))
+        return fail(KQ_EINVAL, "kq_rotate_in: i, leading dimensions and pointers must be 16-byte multiples");
+    int64_t m, p2;
+    Field f;
+    if (!hadamard_split(i, m, p2, f)) return fail(KQ_EUNSUPPORTED, "kq_rotate_in: no Hadamard order for i=%lld", (long long)i);
+    if (ws_bytes < rotate_in_ws(o, i) || (m > 1 && !ws)) return fail(KQ_EWORKSPACE, "kq_rotate_in: workspace too small");
+    hipStream_t st = hs(stream);
+    Arena ar(ws, ws_bytes);
+    float* P = ar.take<float>((size_t)m * m);
+    float* T = m > 1 ? ar.take<float>((size_t)(o > i ? o : i) * i) : nullptr;
+    const float inv = (float)(1.0 / std::sqrt((double)i));
+    if (m > 1) KQ_TRY(make_paley(P, m, f, false, st));
+    // W' = W U: rows w -> H (s * w) / sqrt(i)
+    if (o > 0) {
+        if (m == 1) {
+            KQ_TRY(rows_transform(Win, wdt == KQ_BF16, ldwin, Wout, ldw, o, i, p2, sign_in, nullptr, inv, st));
+        } else {
+            KQ_TRY(rows_transform(Win, wdt == KQ_BF16, ldwin, T, i, o, i, p2, sign_in, nullptr, 1.0f, st));
+            KQ_TRY(paley_rows(P, T, i, Wout, ldw, o, m, p2, inv, st));
+        }
+    }
+    // H_X' = U^T H_X U: rows, then columns
+    if (HX) {
+        if (m == 1) {
+            KQ_TRY(rows_transform(HX, false, i, HX, i, i, i, p2, sign_in, nullptr, inv, st));
+            ColOps ops;
+            ops.pre_sign = sign_in;
+            ops.scale = inv;
+            KQ_TRY(cols_transform(HX, i, HX, i, i, i, p2, ops, st));
+        } else {
+            KQ_TRY(rows_transform(HX, false, i, HX, i, i, i, p2, sign_in, nullptr, 1.0f, st));
+            KQ_TRY(paley_rows(P, HX, i, T, i, i, m, p2, inv, st));
+            ColOps ops;
+            ops.pre_sign = sign_in;
+            KQ_TRY(cols_transform(T, i, T, i, i, i, p2, ops, st));
+            KQ_TRY(paley_cols(P, T, i, HX, i, m, p2, i, inv, st));
+        }
+    }
+    return KQ_OK;
+}
+
+size_t rotate_out_ws(int64_t o, int64_t i, kq_hg_form form) {
+    int64_t m, p2;
+    Field f;
+    if (!hadamard_split(o, m, p2, f)) return 0;
+    Sizer z;
+    z.take<float>((size_t)m * m);
+    if (m > 1 || form != KQ_HG_DIAG) z.take<float>((size_t)o * i);
+    return z.used;
+}
+
+extern "C" kq_status kq_rotate_out(float* W, int64_t o, int64_t i, int64_t ldw, const float* S, kq_hg_form form,
+                                   int64_t blk, const int8_t* sign_out, void* ws, size_t ws_bytes, kq_stream stream) {
+    if (!W || !S || !sign_out) return fail(KQ_EINVAL, "kq_rotate_out: null pointer");
+    if (o <= 0 || i <= 0 || ldw < i) return fail(KQ_ESHAPE, "kq_rotate_out: bad sizes");
+    if (i % 4 || ldw % 4 || !aligned16(W) || !aligned16(S)) return fail(KQ_EINVAL, "kq_rotate_out: alignment");
+    if (form != KQ_HG_DIAG && form != KQ_HG_BLOCK && form != KQ_HG_FULL) return fail(KQ_EINVAL, "kq_rotate_out: bad form");
+    if (form == KQ_HG_BLOCK && (blk <= 0 || o % blk || blk % 4)) return fail(KQ_ESHAPE, "kq_rotate_out: bad block size");
+    int64_t m, p2;
+    Field f;
+    if (!hadamard_split(o, m, p2, f)) return fail(KQ_EUNSUPPORTED, "kq_rotate_out: no Hadamard order for o=%lld", (long long)o);
+    if (ws_bytes < rotate_out_ws(o, i, form) || (rotate_out_ws(o, i, form) && !ws))
+        return fail(KQ_EWORKSPACE, "kq_rotate_out: workspace too small");
+    hipStream_t st = hs(stream);
+    Arena ar(ws, ws_bytes);
+    float* P = ar.take<float>((size_t)m * m);
+    float* T = (m > 1 || form != KQ_HG_DIAG) ? ar.take<float>((size_t)o * i) : nullptr;
+    const float inv = (float)(1.0 / std::sqrt((double)o));
+    if (m > 1) KQ_TRY(make_paley(P, m, f, false, st));
+    ColOps ops;
+    const float* src = W;
+    int64_t ldsrc = ldw;
+    if (form == KQ_HG_DIAG) {
+        ops.pre_scale = S;
+        ops.pre_sign = sign_out;
+    } else {
+        // T = D_t S W
+        if (form == KQ_HG_FULL) {
+            GemmArgs<float> g = gemm_args<float>(o, i, o, S, o, W, ldw, T, i, 1.0f, 0.0f);
+            g.rsign = sign_out;
+            KQ_TRY(gemm<float>(g, false, false, st));
+        } else {
+            GemmArgs<float> g = gemm_args<float>(blk, i, blk, S, blk, W, ldw, T, i, 1.0f, 0.0f);
+            g.nb1 = o / blk; g.sA1 = blk * blk; g.sB1 = blk * ldw; g.sC1 = blk * i;
+            g.rsign = sign_out; g.sR1 = blk;
+            KQ_TRY(gemm<float>(g, false, false, st));
+        }
+        src = T;
+        ldsrc = i;
+    }
+    if (m == 1) {
+        ops.scale = inv;
+        return cols_transform(src, ldsrc, W, ldw, o, i, p2, ops, st);
+    }
+    // FWHT of the chunks into T (in place when T already holds D_t S W), then the Paley mix into W
+    KQ_TRY(cols_transform(src, ldsrc, T, i, o, i, p2, ops, st));
+    return paley_cols(P, T, i, W, ldw, m, p2, i, inv, st);
+}
+
+size_t unrotate_ws(int64_t o, int64_t i, kq_hg_form form) {
+    int64_t mo, po, mi, pi;
+    Field f;
+    if (!hadamard_split(o, mo, po, f) || !hadamard_split(i, mi, pi, f)) return 0;
+    Sizer z;
+    z.take<float>((size_t)mo * mo);
+    z.take<float>((size_t)mi * mi);
+    z.take<float>((size_t)o * i);
+    z.take<float>((size_t)o * i);
+    (void)form;
+    return z.used;
+}
+
+extern "C" kq_status kq_unrotate(const float* Q, int64_t o, int64_t i, int64_t ldq, const int8_t* sign_in,
+                                 const int8_t* sign_out, const float* Sinv, kq_hg_form form, int64_t blk, float* What,
+                                 int64_t ldw, void* ws, size_t ws_bytes, kq_stream stream) {
+    if (!Q || !sign_in || !sign_out || !Sinv || !What) return fail(KQ_EINVAL, "kq_unrotate: null pointer");
+    if (o <= 0 || i <= 0 || ldq < i || ldw < i) return fail(KQ_ESHAPE, "kq_unrotate: bad sizes");
+    if (i % 4 || ldq % 4 || ldw % 4 || !aligned16(Q) || !aligned16(What)) return fail(KQ_EINVAL, "kq_unrotate: alignment");
+    if (form == KQ_HG_BLOCK && (blk <= 0 || o % blk)) return fail(KQ_ESHAPE, "kq_unrotate: bad block size");
+    int64_t mo, po, mi, pi;
+    Field fo, fi;
+    if (!hadamard_split(o, mo, po, fo) || !hadamard_split(i, mi, pi, fi))
+        return fail(KQ_EUNSUPPORTED, "kq_unrotate: no Hadamard order");
+    if (!ws || ws_bytes < unrotate_ws(o, i, form)) return fail(KQ_EWORKSPACE, "kq_unrotate: workspace too small");
+    hipStream_t st = hs(stream);
+    Arena ar(ws, ws_bytes);
+    float* Po = ar.take<float>((size_t)mo * mo);
+    float* Pi = ar.take<float>((size_t)mi * mi);
+    float* T1 = ar.take<float>((size_t)o * i);
+    float* T2 = ar.take<float>((size_t)o * i);
+    // A = D_t H_o^T Q / sqrt(o) ; H_o^T = P_o^T (x) H
+    ColOps ops;
+    ops.post_sign = sign_out;
+    ops.scale = (float)(1.0 / std::sqrt((double)o));
+    if (form == KQ_HG_DIAG) ops.post_scale = Sinv;
+    if (mo > 1) {
+        KQ_TRY(make_paley(Po, mo, fo, true, st));
+        KQ_TRY(paley_cols(Po, Q, ldq, T1, i, mo, po, i, 1.0f, st));
+        KQ_TRY(cols_transform(T1, i, T1, i, o, i, po, ops, st));
+    } else {
+        KQ_TRY(cols_transform(Q, ldq, T1, i, o, i, po, ops, st));
+    }
+    float* cur = T1;
+    if (form != KQ_HG_DIAG) {
+        if (form == KQ_HG_FULL) {
+            GemmArgs<float> g = gemm_args<float>(o, i, o, Sinv, o, T1, i, T2, i, 1.0f, 0.0f);
+            KQ_TRY(gemm<float>(g, false, false, st));
+        } else {
+            GemmArgs<float> g = gemm_args<float>(blk, i, blk, Sinv, blk, T1, i, T2, i, 1.0f, 0.0f);
+            g.nb1 = o / blk; g.sA1 = blk * blk; g.sB1 = blk * i; g.sC1 = blk * i;
+            KQ_TRY(gemm<float>(g, false, false, st));
+        }
+        cur = T2;
+    }
+    // rows a -> s * (H_i^T a) / sqrt(i)
+    const float inv_i = (float)(1.0 / std::sqrt((double)i));
+    if (mi > 1) {
+        float* other = (cur == T1) ? T2 : T1;
+        KQ_TRY(make_paley(Pi, mi, fi, true, st));
+        KQ_TRY(paley_rows(Pi, cur, i, other, i, o, mi, pi, 1.0f, st));
+        cur = other;
+    }
+    return rows_transform(cur, false, i, What, ldw, o, i, pi, nullptr, sign_in, inv_i, st);
+}

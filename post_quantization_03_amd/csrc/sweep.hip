@@ -1,0 +1,326 @@
+// GPTQ column sweep (KronQ review page, Prior limitations / Goal: the column-wise OBS update with H_X
+// only, left unchanged by KronQ), the layer loss used for verification, and the sensitivity score
+// tr(H_G) tr(H_X) (review page, Method (2)).
+//
+// Sweep layout. Columns are processed in blocks of 128. Inside a block every row is owned by a group
+// of 16 lanes of one wavefront; lane q holds the 8 columns q, q + 16, ..., q + 112 in registers, so
+// the columns still to be updated stay spread over all 16 lanes as the sweep advances. For column j
+// the owning lane's value is broadcast within the 16-lane group, every lane rounds it to the grid
+// (same arithmetic on every lane, so no second broadcast), and updates its own later columns with
+// the row j of the block's R (staged once per work-group in LDS). After the block, the trailing
+// columns receive the lazy update W[:, b1:] -= E R[b0:b1, b1:] on the fp32 MFMA GEMM.
+#include <cmath>
+
+#include "kq_internal.h"
+
+namespace kq {
+
+constexpr int SW_B = 128;         // column block
+constexpr int SW_ROWS = 16;       // rows per work-group (16 lanes each)
+
+// Per-row grid over the whole row before the sweep (group = 0): offset = min, scale = (max-min)/L.
+__global__ __launch_bounds__(256) void row_grid_kernel(const float* __restrict__ W, int64_t i, int64_t ldw, float L,
+                                                       float* __restrict__ scale, float* __restrict__ offset) {
+    __shared__ float smin[256], smax[256];
+    const int64_t r = blockIdx.x;
+    float mn = INFINITY, mx = -INFINITY;
+    for (int64_t c = threadIdx.x; c < i; c += 256) {
+        const float v = W[r * ldw + c];
+        mn = fminf(mn, v);
+        mx = fmaxf(mx, v);
+    }
+    smin[threadIdx.x] = mn;
+    smax[threadIdx.x] = mx;
+    __syncthreads();
+    for (int w = 128; w > 0; w >>= 1) {
+        if ((int)threadIdx.x < w) {
+            smin[threadIdx.x] = fminf(smin[threadIdx.x], smin[threadIdx.x + w]);
+            smax[threadIdx.x] = fmaxf(smax[threadIdx.x], smax[threadIdx.x + w]);
+        }
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) {
+        offset[r] = smin[0];
+        scale[r] = (smax[0] - smin[0]) / L;
+    }
+}
+
+template <int G>
+__global__ __launch_bounds__(256) void sweep_block_kernel(float* __restrict__ W, int64_t o, int64_t i, int64_t ldw,
+                                                          const float* __restrict__ R, int64_t ldr, int64_t b0,
+                                                          int bits, uint32_t* __restrict__ codes,
+                                                          float* __restrict__ scale, float* __restrict__ offset,
+                                                          float* __restrict__ row_loss, float* __restrict__ E,
+                                                          int first) {
+    extern __shared__ __align__(16) float sm[];
+    float* Rb = sm;                        // 128 x 128
+    float* rdiag = sm + SW_B * SW_B;       // 128 reciprocals of R_jj
+    uint8_t* cl = reinterpret_cast<uint8_t*>(rdiag + SW_B);  // 16 rows x 128 codes
+    const int tid = threadIdx.x;
+    for (int e = tid; e < SW_B * SW_B / 4; e += 256) {
+        const int a = e / (SW_B / 4), c4 = (e % (SW_B / 4)) * 4;
+        const float4 v = *reinterpret_cast<const float4*>(R + (b0 + a) * ldr + b0 + c4);
+        *reinterpret_cast<float4*>(Rb + a * SW_B + c4) = v;
+    }
+    __syncthreads();
+    if (tid < SW_B) rdiag[tid] = 1.0f / Rb[tid * SW_B + tid];
+    __syncthreads();
+
+    const int q = tid & 15, rl = tid >> 4;
+    const int64_t row = (int64_t)blockIdx.x * SW_ROWS + rl;
+    const bool live = row < o;
+    const int64_t rr = live ? row : 0;
+    const float L = (float)((1 << bits) - 1);
+    const int ng = G ? (int)(i / G) : 1;
+    float* wrow = W + rr * ldw + b0;
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; u++) v[u] = live ? wrow[16 * u + q] : 0.0f;
+    float mu = 0.0f, s = 0.0f, invs = 0.0f;
+    if (G == 0) {
+        mu = offset[rr];
+        s = scale[rr];
+        invs = s > 0.0f ? 1.0f / s : 0.0f;
+    }
+    int code[8];
+    float eown[8];
+    float loss = 0.0f;
+#pragma unroll
+    for (int u = 0; u < 8; u++) { code[u] = 0; eown[u] = 0.0f; }
+
+#pragma unroll
+    for (int j = 0; j < SW_B; j++) {
+        const int uj = j >> 4, qj = j & 15;
+        if (G > 0 && (j % (G > 0 ? G : 1)) == 0) {
+            float mn = INFINITY, mx = -INFINITY;
+#pragma unroll
+            for (int u = 0; u < 8; u++) {
+                if (16 * u + 15 < j || 16 * u >= j + G) continue;
+                const int col = 16 * u + q;
+                if (col >= j && col < j + G) { mn = fminf(mn, v[u]); mx = fmaxf(mx, v[u]); }
+            }
+#pragma unroll
+            for (int w = 8; w > 0; w >>= 1) {
+                mn = fminf(mn, __shfl_xor(mn, w, 16));
+                mx = fmaxf(mx, __shfl_xor(mx, w, 16));
+            }
+            mu = mn;
+            s = (mx - mn) / L;
+            invs = s > 0.0f ? 1.0f / s : 0.0f;
+            if (live && q == 0) {
+                const int64_t gidx = (b0 + j) / (G > 0 ? G : 1);
+                offset[rr * ng + gidx] = mu;
+                scale[rr * ng + gidx] = s;
+            }
+        }
+        const float w = __shfl(v[uj], qj, 16);
+        const float uu = (w - mu) * invs;
+        const float qf = fminf(fmaxf(rintf(uu), 0.0f), L);
+        const float deq = fmaf(s, qf, mu);
+        const float e = (w - deq) * rdiag[j];
+        loss = fmaf(e, e, loss);
+        const bool own = (q == qj);
+        if (own) {
+            v[uj] = deq;
+            code[uj] = (int)qf;
+            eown[uj] = e;
+        }
+        const float* Rj = Rb + j * SW_B;
+#pragma unroll
+        for (int u = 0; u < 8; u++) {
+            if (16 * u + 15 <= j) continue;            // every lane's column is done
+            const int col = 16 * u + q;
+            const float rv = Rj[col];
+            if (col > j) v[u] = fmaf(-e, rv, v[u]);
+        }
+    }
+
+    // outputs: w^ back into W, scaled errors into E, codes packed per row, loss
+    if (live) {
+#pragma unroll
+        for (int u = 0; u < 8; u++) {
+            wrow[16 * u + q] = v[u];
+            E[rr * SW_B + 16 * u + q] = eown[u];
+        }
+        if (q == 0 && row_loss) row_loss[rr] = (first ? 0.0f : row_loss[rr]) + loss;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; u++) cl[rl * SW_B + 16 * u + q] = (uint8_t)code[u];
+    __syncthreads();
+    const int nw = 4 * bits;   // words per row per block
+    const int64_t wpr = i * bits / 32;
+    if (live) {
+        for (int wd = q; wd < nw; wd += 16) {
+            uint32_t word = 0;
+            for (int p = 0; p < 32; p++) {
+                const int B = 32 * wd + p, col = B / bits, t = B % bits;
+                word |= (uint32_t)((cl[rl * SW_B + col] >> t) & 1) << p;
+            }
+            codes[rr * wpr + (b0 / 32) * bits + wd] = word;
+        }
+    }
+}
+
+}  // namespace kq
+
+using namespace kq;
+
+size_t quantize_ws(int64_t o) {
+    Sizer z;
+    z.take<float>((size_t)o * SW_B);
+    return z.used;
+}
+
+extern "C" kq_status kq_quantize_layer(float* W, int64_t o, int64_t i, int64_t ldw, const float* R, int64_t ldr, int bits,
+                                       int group, int block, uint32_t* codes, float* scale, float* offset,
+                                       float* row_loss, void* ws, size_t ws_bytes, kq_stream stream) {
+    if (!W || !R || !codes || !scale || !offset) return fail(KQ_EINVAL, "kq_quantize_layer: null pointer");
+    if (o <= 0 || i <= 0 || ldw < i || ldr < i) return fail(KQ_ESHAPE, "kq_quantize_layer: bad sizes");
+    if (bits < 2 || bits > 8) return fail(KQ_EUNSUPPORTED, "kq_quantize_layer: bits must be in 2..8");
+    if (block != SW_B) return fail(KQ_EUNSUPPORTED, "kq_quantize_layer: block must be 128");
+    if (i % SW_B) return fail(KQ_ESHAPE, "kq_quantize_layer: i must be a multiple of 128");
+    if (!(group == 0 || group == 16 || group == 32 || group == 64 || group == 128))
+        return fail(KQ_EUNSUPPORTED, "kq_quantize_layer: group must be 0, 16, 32, 64 or 128");
+    if ((i * bits) % 32) return fail(KQ_ESHAPE, "kq_quantize_layer: i*bits must be a multiple of 32");
+    if (ldw % 4 || ldr % 4 || !aligned16(W) || !aligned16(R)) return fail(KQ_EINVAL, "kq_quantize_layer: alignment");
+    if (!ws || ws_bytes < quantize_ws(o)) return fail(KQ_EWORKSPACE, "kq_quantize_layer: workspace too small");
+    hipStream_t st = hs(stream);
+    Arena ar(ws, ws_bytes);
+    float* E = ar.take<float>((size_t)o * SW_B);
+    if (o > 2147483647LL * SW_ROWS) return fail(KQ_ESHAPE, "kq_quantize_layer: o too large");
+    const float L = (float)((1 << bits) - 1);
+    if (group == 0) {
+        hipLaunchKernelGGL(row_grid_kernel, dim3((unsigned)o), dim3(256), 0, st, W, i, ldw, L, scale, offset);
+        KQ_TRY(check_launch("row_grid"));
+    }
+    const size_t smem = (SW_B * SW_B + SW_B) * sizeof(float) + SW_ROWS * SW_B;
+    static bool attr = false;
+    if (!attr) {
+        hipFuncSetAttribute(reinterpret_cast<const void*>(&sweep_block_kernel<0>), hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+        hipFuncSetAttribute(reinterpret_cast<const void*>(&sweep_block_kernel<16>), hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+        hipFuncSetAttribute(reinterpret_cast<const void*>(&sweep_block_kernel<32>), hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+        hipFuncSetAttribute(reinterpret_cast<const void*>(&sweep_block_kernel<64>), hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+        hipFuncSetAttribute(reinterpret_cast<const void*>(&sweep_block_kernel<128>), hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+        attr = true;
+    }
+    const dim3 grid((unsigned)((o + SW_ROWS - 1) / SW_ROWS));
+    for (int64_t b0 = 0; b0 < i; b0 += SW_B) {
+        const int first = b0 == 0;
+        switch (group) {
+            case 0: hipLaunchKernelGGL(sweep_block_kernel<0>, grid, dim3(256), smem, st, W, o, i, ldw, R, ldr, b0, bits, codes, scale, offset, row_loss, E, first); break;
+            case 16: hipLaunchKernelGGL(sweep_block_kernel<16>, grid, dim3(256), smem, st, W, o, i, ldw, R, ldr, b0, bits, codes, scale, offset, row_loss, E, first); break;
+            case 32: hipLaunchKernelGGL(sweep_block_kernel<32>, grid, dim3(256), smem, st, W, o, i, ldw, R, ldr, b0, bits, codes, scale, offset, row_loss, E, first); break;
+            case 64: hipLaunchKernelGGL(sweep_block_kernel<64>, grid, dim3(256), smem, st, W, o, i, ldw, R, ldr, b0, bits, codes, scale, offset, row_loss, E, first); break;
+            default: hipLaunchKernelGGL(sweep_block_kernel<128>, grid, dim3(256), smem, st, W, o, i, ldw, R, ldr, b0, bits, codes, scale, offset, row_loss, E, first); break;
+        }
+        KQ_TRY(check_launch("sweep_block"));
+        const int64_t b1 = b0 + SW_B;
+        if (b1 < i) {
+            GemmArgs<float> g = gemm_args<float>(o, i - b1, SW_B, E, SW_B, R + b0 * ldr + b1, ldr, W + b1, ldw, -1.0f, 1.0f);
+            KQ_TRY(gemm<float>(g, false, false, st));
+        }
+    }
+    return KQ_OK;
+}
+
+// ----------------------------------------------------------------------------------- sensitivity
+__global__ void sensitivity_kernel(const float* HX, int64_t i, int64_t ldh, const float* HG, int form, int64_t o,
+                                   int64_t blk, double* score) {
+    __shared__ double sx[256], sg[256];
+    double ax = 0, ag = 0;
+    for (int64_t r = threadIdx.x; r < i; r += 256) ax += (double)HX[r * ldh + r];
+    for (int64_t r = threadIdx.x; r < o; r += 256) {
+        if (form == KQ_HG_DIAG) ag += (double)HG[r];
+        else if (form == KQ_HG_FULL) ag += (double)HG[r * o + r];
+        else ag += (double)HG[(r / blk) * blk * blk + (r % blk) * blk + (r % blk)];
+    }
+    sx[threadIdx.x] = ax;
+    sg[threadIdx.x] = ag;
+    __syncthreads();
+    for (int w = 128; w > 0; w >>= 1) {
+        if ((int)threadIdx.x < w) {
+            sx[threadIdx.x] += sx[threadIdx.x + w];
+            sg[threadIdx.x] += sg[threadIdx.x + w];
+        }
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) *score = sx[0] * sg[0];
+}
+
+extern "C" kq_status kq_sensitivity(const float* HX, int64_t i, int64_t ldh, const float* HG, kq_hg_form form, int64_t o,
+                                    int64_t blk, double* score, kq_stream stream) {
+    if (!HX || !HG || !score) return fail(KQ_EINVAL, "kq_sensitivity: null pointer");
+    if (i <= 0 || o <= 0 || ldh < i) return fail(KQ_ESHAPE, "kq_sensitivity: bad sizes");
+    if (form != KQ_HG_DIAG && form != KQ_HG_BLOCK && form != KQ_HG_FULL) return fail(KQ_EINVAL, "kq_sensitivity: bad form");
+    if (form == KQ_HG_BLOCK && (blk <= 0 || o % blk)) return fail(KQ_ESHAPE, "kq_sensitivity: bad block size");
+    hipLaunchKernelGGL(sensitivity_kernel, dim3(1), dim3(256), 0, hs(stream), HX, i, ldh, HG, (int)form, o, blk, score);
+    return check_launch("sensitivity");
+}
+
+// ------------------------------------------------------------------------------------ layer loss
+__global__ void diff_kernel(const float* Q, const float* W2, int64_t o, int64_t i, int64_t ldw, float* D) {
+    const int64_t tot = o * i;
+    for (int64_t e = blockIdx.x * (int64_t)256 + threadIdx.x; e < tot; e += (int64_t)gridDim.x * 256) {
+        const int64_t r = e / i, c = e % i;
+        D[e] = Q[r * ldw + c] - W2[r * ldw + c];
+    }
+}
+
+// row_loss[r] = sum_c D[r][c] G[r][c] in fp64 (one work-group per row), then the total in row order.
+__global__ void rowdot_kernel(const float* D, const float* G, int64_t i, double* out) {
+    __shared__ double sp[256];
+    const int64_t r = blockIdx.x;
+    double a = 0;
+    for (int64_t c = threadIdx.x; c < i; c += 256) a += (double)D[r * i + c] * (double)G[r * i + c];
+    sp[threadIdx.x] = a;
+    __syncthreads();
+    for (int w = 128; w > 0; w >>= 1) {
+        if ((int)threadIdx.x < w) sp[threadIdx.x] += sp[threadIdx.x + w];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) out[r] = sp[0];
+}
+
+__global__ void sum_rows_kernel(const double* rl, int64_t o, double* total) {
+    __shared__ double sp[256];
+    double a = 0;
+    for (int64_t r = threadIdx.x; r < o; r += 256) a += rl[r];
+    sp[threadIdx.x] = a;
+    __syncthreads();
+    for (int w = 128; w > 0; w >>= 1) {
+        if ((int)threadIdx.x < w) sp[threadIdx.x] += sp[threadIdx.x + w];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) *total = sp[0];
+}
+
+size_t loss_ws(int64_t o, int64_t i) {
+    Sizer z;
+    z.take<float>((size_t)o * i);
+    z.take<float>((size_t)o * i);
+    z.take<double>((size_t)o);
+    return z.used;
+}
+
+extern "C" kq_status kq_layer_loss(const float* W2, const float* Q, int64_t o, int64_t i, int64_t ldw, const float* HX2,
+                                   int64_t ldh, double* row_loss, double* loss, void* ws, size_t ws_bytes,
+                                   kq_stream stream) {
+    if (!W2 || !Q || !HX2 || !loss) return fail(KQ_EINVAL, "kq_layer_loss: null pointer");
+    if (o <= 0 || i <= 0 || ldw < i || ldh < i) return fail(KQ_ESHAPE, "kq_layer_loss: bad sizes");
+    if (!ws || ws_bytes < loss_ws(o, i)) return fail(KQ_EWORKSPACE, "kq_layer_loss: workspace too small");
+    hipStream_t st = hs(stream);
+    Arena ar(ws, ws_bytes);
+    float* D = ar.take<float>((size_t)o * i);
+    float* G = ar.take<float>((size_t)o * i);
+    double* rl = ar.take<double>((size_t)o);
+    if (row_loss) rl = row_loss;
+    unsigned b = (unsigned)((o * i + 255) / 256 < 8192 ? (o * i + 255) / 256 : 8192);
+    hipLaunchKernelGGL(diff_kernel, dim3(b), dim3(256), 0, st, Q, W2, o, i, ldw, D);
+    KQ_TRY(check_launch("loss diff"));
+    GemmArgs<float> g = gemm_args<float>(o, i, i, D, i, HX2, ldh, G, i, 1.0f, 0.0f);
+    KQ_TRY(gemm<float>(g, false, false, st));
+    hipLaunchKernelGGL(rowdot_kernel, dim3((unsigned)o), dim3(256), 0, st, D, G, i, rl);
+    KQ_TRY(check_launch("loss rowdot"));
+    hipLaunchKernelGGL(sum_rows_kernel, dim3(1), dim3(256), 0, st, rl, o, loss);
+    return check_launch("loss sum");
+}

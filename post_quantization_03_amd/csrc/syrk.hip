@@ -1,0 +1,261 @@
+// H_X accumulation H <- beta H + alpha X^T X (KronQ review page, Background: the input activation
+// covariance used as the layer-Hessian proxy).
+//
+// bf16 X: bf16 x bf16 products are exact in fp32, so the gfx950 bf16 matrix cores
+// (v_mfma_f32_16x16x32_bf16, fp32 accumulation) compute exactly the products an fp32 contraction
+// of the widened values would, at 16x the fp32 MFMA rate. Only the lower-triangle 128 x 128 tiles
+// of H are computed; a fixed split over tokens with a fixed-order reduction keeps the result
+// deterministic, and the reduction writes both triangles.
+// fp32 X: the fp32 MFMA GEMM with a lower-triangle epilogue, then a mirror pass.
+#include "kq_internal.h"
+
+namespace kq {
+
+typedef float f4v __attribute__((ext_vector_type(4)));
+typedef __bf16 bf8v __attribute__((ext_vector_type(8)));
+
+constexpr int SY_T = 128;   // output tile
+constexpr int SY_K = 64;    // tokens per LDS stage
+
+struct alignas(16) U4 {
+    uint32_t w[4];
+};
+
+// Tile t of the lower triangle (row-major over tm >= tn) -> (tm, tn).
+__device__ inline void tri_decode(int t, int& tm, int& tn) {
+    int r = (int)((sqrtf(8.0f * (float)t + 1.0f) - 1.0f) * 0.5f);
+    while (r * (r + 1) / 2 > t) r--;
+    while ((r + 1) * (r + 2) / 2 <= t) r++;
+    tm = r;
+    tn = t - r * (r + 1) / 2;
+}
+
+// LDS tile [128 rows][64 k] bf16, rows of 128 bytes made of eight 16-byte chunks; chunk c of row m is
+// stored at position c ^ (m & 7) so that the 16 consecutive rows read by an MFMA operand spread over
+// the banks.
+__device__ inline int lds_off(int m, int c) { return m * SY_K + ((c ^ (m & 7)) << 3); }
+
+__global__ __launch_bounds__(256) void syrk_bf16_kernel(const uint16_t* __restrict__ X, int64_t n, int64_t d,
+                                                        int64_t ldx, int64_t tok_per_split, float alpha, float beta,
+                                                        float* __restrict__ H, float* __restrict__ part,
+                                                        int ntiles) {
+    __shared__ __align__(16) uint16_t As[2][SY_T * SY_K];
+    __shared__ __align__(16) uint16_t Bs[2][SY_T * SY_K];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tile = blockIdx.x, split = blockIdx.y;
+    int tm, tn;
+    tri_decode(tile, tm, tn);
+    const int64_t m0 = (int64_t)tm * SY_T, n0 = (int64_t)tn * SY_T;
+    const int64_t kb = (int64_t)split * tok_per_split;
+    const int64_t ke = (kb + tok_per_split < n) ? kb + tok_per_split : n;
+
+    // loader role: threads 0..127 stage the row block (A), 128..255 the column block (B)
+    const int op = tid >> 7, p = tid & 127, kg = p >> 4, mc = p & 15;
+    const int64_t cbase = (op ? n0 : m0) + 8 * mc;
+    const bool fullc = cbase + 8 <= d;
+    U4 v[8];
+
+    auto gload = [&](int64_t k0) {
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            const int64_t k = k0 + 8 * kg + j;
+            const uint16_t* src = X + k * ldx + cbase;
+            if (k < ke && fullc) {
+                v[j] = *reinterpret_cast<const U4*>(src);
+            } else {
+                uint16_t tmp[8];
+#pragma unroll
+                for (int e = 0; e < 8; e++) tmp[e] = (k < ke && cbase + e < d) ? src[e] : (uint16_t)0;
+#pragma unroll
+                for (int q = 0; q < 4; q++) v[j].w[q] = (uint32_t)tmp[2 * q] | ((uint32_t)tmp[2 * q + 1] << 16);
+            }
+        }
+    };
+    auto sstore = [&](int buf) {
+        // 8 x 8 transpose of 16-bit elements: out[mm] holds k = 0..7 of column 8*mc + mm
+        U4 out[8];
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+#pragma unroll
+            for (int jp = 0; jp < 4; jp++) {
+                const uint32_t x = v[2 * jp].w[q], y = v[2 * jp + 1].w[q];
+                out[2 * q].w[jp] = (x & 0xFFFFu) | (y << 16);
+                out[2 * q + 1].w[jp] = (x >> 16) | (y & 0xFFFF0000u);
+            }
+        }
+        uint16_t* dst = op ? Bs[buf] : As[buf];
+#pragma unroll
+        for (int mm = 0; mm < 8; mm++) {
+            const int m = 8 * mc + mm;
+            *reinterpret_cast<U4*>(dst + lds_off(m, kg)) = out[mm];
+        }
+    };
+
+    f4v acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int j = 0; j < 4; j++) acc[i][j] = f4v{0, 0, 0, 0};
+    const int wm = wave >> 1, wn = wave & 1;
+
+    if (kb < ke) {
+        gload(kb);
+        sstore(0);
+        __syncthreads();
+        int buf = 0;
+        for (int64_t k0 = kb; k0 < ke; k0 += SY_K) {
+            const bool more = k0 + SY_K < ke;
+            if (more) gload(k0 + SY_K);
+#pragma unroll
+            for (int s = 0; s < 2; s++) {
+                bf8v a[4], b[4];
+                const int c = 4 * s + (lane >> 4);
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    const int m = wm * 64 + 16 * i + (lane & 15);
+                    a[i] = *reinterpret_cast<const bf8v*>(As[buf] + lds_off(m, c));
+                }
+#pragma unroll
+                for (int j = 0; j < 4; j++) {
+                    const int nn = wn * 64 + 16 * j + (lane & 15);
+                    b[j] = *reinterpret_cast<const bf8v*>(Bs[buf] + lds_off(nn, c));
+                }
+#pragma unroll
+                for (int i = 0; i < 4; i++)
+#pragma unroll
+                    for (int j = 0; j < 4; j++)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+            }
+            if (more) sstore(buf ^ 1);
+            __syncthreads();
+            buf ^= 1;
+        }
+    }
+
+    if (part) {
+        float* out = part + ((int64_t)split * ntiles + tile) * (SY_T * SY_T);
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+#pragma unroll
+            for (int j = 0; j < 4; j++)
+#pragma unroll
+                for (int r = 0; r < 4; r++) {
+                    const int mm = wm * 64 + 16 * i + 4 * (lane >> 4) + r, nn = wn * 64 + 16 * j + (lane & 15);
+                    out[mm * SY_T + nn] = acc[i][j][r];
+                }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+#pragma unroll
+            for (int j = 0; j < 4; j++)
+#pragma unroll
+                for (int r = 0; r < 4; r++) {
+                    const int64_t m = m0 + wm * 64 + 16 * i + 4 * (lane >> 4) + r;
+                    const int64_t c = n0 + wn * 64 + 16 * j + (lane & 15);
+                    if (m >= d || c >= d || c > m) continue;
+                    float val = alpha * acc[i][j][r];
+                    if (beta != 0.0f) val += beta * H[m * d + c];
+                    H[m * d + c] = val;
+                    H[c * d + m] = val;
+                }
+    }
+}
+
+// Sum the token splits in order, scale, and write both triangles.
+__global__ void syrk_reduce_kernel(const float* __restrict__ part, int nsplit, int ntiles, int64_t d, float alpha,
+                                   float beta, float* __restrict__ H) {
+    const int tile = blockIdx.x;
+    int tm, tn;
+    tri_decode(tile, tm, tn);
+    for (int e = threadIdx.x; e < SY_T * SY_T; e += blockDim.x) {
+        const int mm = e / SY_T, nn = e % SY_T;
+        const int64_t m = (int64_t)tm * SY_T + mm, c = (int64_t)tn * SY_T + nn;
+        if (m >= d || c >= d || c > m) continue;
+        float s = 0.0f;
+        for (int k = 0; k < nsplit; k++) s += part[((int64_t)k * ntiles + tile) * (SY_T * SY_T) + e];
+        float val = alpha * s;
+        if (beta != 0.0f) val += beta * H[m * d + c];
+        H[m * d + c] = val;
+        H[c * d + m] = val;
+    }
+}
+
+__global__ void mirror_lower_kernel(float* H, int64_t d) {
+    const int64_t r = blockIdx.y;
+    for (int64_t c = r + 1 + blockIdx.x * 256 + threadIdx.x; c < d; c += (int64_t)gridDim.x * 256) H[r * d + c] = H[c * d + r];
+}
+
+__global__ void scale_kernel(float* H, int64_t count, float beta) {
+    for (int64_t e = blockIdx.x * (int64_t)256 + threadIdx.x; e < count; e += (int64_t)gridDim.x * 256)
+        H[e] = beta == 0.0f ? 0.0f : beta * H[e];
+}
+
+static void syrk_plan(int64_t n, int64_t d, int& ntiles, int& nsplit, int64_t& tps) {
+    const int64_t nt = (d + SY_T - 1) / SY_T;
+    ntiles = (int)(nt * (nt + 1) / 2);
+    int64_t s = (2048 + ntiles - 1) / ntiles;
+    const int64_t smax = (n + 1023) / 1024;
+    if (s > smax) s = smax;
+    if (s < 1) s = 1;
+    tps = ((n + s - 1) / s + SY_K - 1) / SY_K * SY_K;
+    nsplit = (int)((n + tps - 1) / tps);
+    if (nsplit < 1) nsplit = 1;
+}
+
+}  // namespace kq
+
+using namespace kq;
+
+size_t hessian_ws(int64_t n, int64_t d, kq_dtype xdt) {
+    if (xdt != KQ_BF16 || n <= 0) return 0;
+    int ntiles, nsplit;
+    int64_t tps;
+    syrk_plan(n, d, ntiles, nsplit, tps);
+    if (nsplit <= 1) return 0;
+    return (size_t)nsplit * ntiles * SY_T * SY_T * sizeof(float) + 256;
+}
+
+extern "C" kq_status kq_hessian_accum(const void* X, kq_dtype xdt, int64_t n, int64_t d, int64_t ldx, float alpha,
+                                      float beta, float* H, void* ws, size_t ws_bytes, kq_stream stream) {
+    if (!H) return fail(KQ_EINVAL, "kq_hessian_accum: null H");
+    if (d <= 0 || n < 0) return fail(KQ_ESHAPE, "kq_hessian_accum: bad sizes");
+    if (xdt != KQ_F32 && xdt != KQ_BF16) return fail(KQ_EINVAL, "kq_hessian_accum: bad dtype");
+    if (!aligned16(H)) return fail(KQ_EINVAL, "kq_hessian_accum: H must be 16-byte aligned");
+    hipStream_t st = hs(stream);
+    if (n == 0) {
+        unsigned b = (unsigned)((d * d + 255) / 256 < 4096 ? (d * d + 255) / 256 : 4096);
+        hipLaunchKernelGGL(scale_kernel, dim3(b), dim3(256), 0, st, H, d * d, beta);
+        return check_launch("hessian scale");
+    }
+    if (!X) return fail(KQ_EINVAL, "kq_hessian_accum: null X");
+    if (ldx < d) return fail(KQ_ESHAPE, "kq_hessian_accum: ldx < d");
+    if (!aligned16(X) || (xdt == KQ_BF16 ? ldx % 8 : ldx % 4))
+        return fail(KQ_EINVAL, "kq_hessian_accum: X must be 16-byte aligned with ldx a multiple of 16 bytes");
+    if (xdt == KQ_F32) {
+        GemmArgs<float> g = gemm_args<float>(d, d, n, static_cast<const float*>(X), ldx, static_cast<const float*>(X),
+                                             ldx, H, d, alpha, beta);
+        g.tri = 1;
+        KQ_TRY(gemm<float>(g, true, false, st));
+        if (d > 65535) return fail(KQ_ESHAPE, "kq_hessian_accum: d too large");
+        dim3 gm((unsigned)((d + 255) / 256 < 64 ? (d + 255) / 256 : 64), (unsigned)d);
+        hipLaunchKernelGGL(mirror_lower_kernel, gm, dim3(256), 0, st, H, d);
+        return check_launch("hessian mirror");
+    }
+    int ntiles, nsplit;
+    int64_t tps;
+    syrk_plan(n, d, ntiles, nsplit, tps);
+    float* part = nullptr;
+    if (nsplit > 1) {
+        if (!ws || ws_bytes < hessian_ws(n, d, xdt)) return fail(KQ_EWORKSPACE, "kq_hessian_accum: workspace too small");
+        part = reinterpret_cast<float*>((reinterpret_cast<uintptr_t>(ws) + 255) & ~uintptr_t(255));
+    }
+    hipLaunchKernelGGL(syrk_bf16_kernel, dim3((unsigned)ntiles, (unsigned)nsplit), dim3(256), 0, st,
+                       static_cast<const uint16_t*>(X), n, d, ldx, tps, alpha, beta, H, part, ntiles);
+    KQ_TRY(check_launch("syrk_bf16"));
+    if (nsplit > 1) {
+        hipLaunchKernelGGL(syrk_reduce_kernel, dim3((unsigned)ntiles), dim3(256), 0, st, part, nsplit, ntiles, d, alpha,
+                           beta, H);
+        KQ_TRY(check_launch("syrk_reduce"));
+    }
+    return KQ_OK;
+}

@@ -1,0 +1,92 @@
+"""One-layer KronQ pipeline on the GPU through the C ABI (include/kq.h).
+
+Order of the calls (KronQ review page, Method and Key idea):
+  kq_hessian_accum  H_X = X^T X / n
+  kq_sensitivity    tr(H_G) tr(H_X)         (before the rotation: undamped, unrotated H_X)
+  kq_rotate_in      W' = W U, H_X' = U^T H_X U
+  kq_hg_sqrt        S = H_G^{1/2}, S^{-1}    (skipped when a cached S is passed)
+  kq_rotate_out     W'' = V S W'
+  kq_cholinv        R with (H_X' + lambda I)^{-1} = R^T R
+  kq_quantize_layer GPTQ sweep on W'' -> codes, scale, offset, w^ (rotated), row loss
+Torch only allocates device memory and supplies the stream.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import torch
+
+from . import _lib as K
+
+
+@dataclass
+class LayerCfg:
+    bits: int
+    group: int = 128
+    block: int = 128
+    damp: float = 0.01
+    form: str = "diag"      # H_G storage form
+    blk: int = 0            # block size of a block-diagonal H_G
+
+
+def workspace_bytes(o: int, i: int, n: int, xdt: int, cfg: LayerCfg, verify: bool = False) -> int:
+    ops = ["hessian", "rotate_in", "hg_sqrt", "rotate_out", "cholinv", "quantize"] + (["unrotate", "loss"] if verify else [])
+    return max(K.kq_workspace_bytes(op, o, i, n, xdt, cfg.bits, cfg.group, cfg.form, cfg.blk) for op in ops)
+
+
+def hg_factor_shape(o: int, cfg: LayerCfg):
+    if cfg.form == "diag":
+        return (o,)
+    if cfg.form == "block":
+        return (o // cfg.blk, cfg.blk, cfg.blk)
+    return (o, o)
+
+
+def quantize_layer(X: torch.Tensor, W: torch.Tensor, HG: torch.Tensor, s: torch.Tensor, t: torch.Tensor,
+                   cfg: LayerCfg, ws: torch.Tensor | None = None, S_cached=None, verify: bool = False,
+                   x_batch: int | None = None) -> dict:
+    """All steps of the per-layer solver on device-resident inputs. Returns device tensors."""
+    dev = W.device
+    o, i = W.shape
+    n = X.shape[0]
+    xdt = K.KQ_BF16 if X.dtype == torch.bfloat16 else K.KQ_F32
+    if ws is None:
+        ws = torch.empty(max(workspace_bytes(o, i, n if x_batch is None else min(n, x_batch), xdt, cfg, verify), 256),
+                         dtype=torch.uint8, device=dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    H = torch.empty((i, i), **f32)
+    if x_batch is None or x_batch >= n:
+        K.kq_hessian_accum(X, H, 1.0 / n, 0.0, ws)
+    else:
+        for k0 in range(0, n, x_batch):
+            K.kq_hessian_accum(X[k0:k0 + x_batch], H, 1.0 / n, 0.0 if k0 == 0 else 1.0, ws)
+    score = torch.empty((1,), dtype=torch.float64, device=dev)
+    K.kq_sensitivity(H, HG, cfg.form, o, cfg.blk, score)
+    W2 = torch.empty((o, i), **f32)
+    K.kq_rotate_in(W, W2, H, s, ws)
+    info = torch.zeros((2,), dtype=torch.int32, device=dev)
+    if S_cached is None:
+        S = torch.empty(hg_factor_shape(o, cfg), **f32)
+        Sinv = torch.empty_like(S) if verify else None
+        K.kq_hg_sqrt(HG, cfg.form, o, cfg.blk, S, Sinv, info[0:1], ws)
+    else:
+        S, Sinv = S_cached
+    K.kq_rotate_out(W2, S, cfg.form, cfg.blk, t, ws)
+    R = torch.empty((i, i), **f32)
+    K.kq_cholinv(H, cfg.damp, R, info[1:2], ws)
+    W2_in = W2.clone() if verify else None
+    ng = i // cfg.group if cfg.group else 1
+    codes = torch.empty((o, i * cfg.bits // 32), dtype=torch.int32, device=dev)
+    scale = torch.empty((o, ng), **f32)
+    offset = torch.empty((o, ng), **f32)
+    row_loss = torch.empty((o,), **f32)
+    K.kq_quantize_layer(W2, R, cfg.bits, cfg.group, cfg.block, codes, scale, offset, row_loss, ws)
+    out = {"H": H, "score": score, "Q": W2, "R": R, "codes": codes, "scale": scale, "offset": offset,
+           "row_loss": row_loss, "info": info, "S": S, "Sinv": Sinv}
+    if verify:
+        What = torch.empty((o, i), **f32)
+        K.kq_unrotate(W2, s, t, Sinv, cfg.form, cfg.blk, What, ws)
+        loss = torch.empty((1,), dtype=torch.float64, device=dev)
+        K.kq_layer_loss(W2_in, W2, H, None, loss, ws)
+        out.update({"W2": W2_in, "What": What, "loss": loss})
+    return out

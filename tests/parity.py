@@ -1,0 +1,64 @@
+"""Comparison rules between the GPU path and the float64 oracle (test helpers).
+
+Codes: rows are independent given R, so a rounding flip at a near-tie only cascades along its own
+row. Each row is walked in sweep order; where the codes differ at a position whose oracle tie
+distance is <= TIE (1e-4 grid steps), the row is replayed in the oracle with the GPU's code forced
+there, and the walk continues. After replay every code, and every packed word, must match
+bit-exactly; a difference at a position with tie distance > TIE is a failure.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from oracle import kronq as kq
+
+TIE = 1e-4
+
+
+def gpu_words_to_codes(words: np.ndarray, bits: int, i: int) -> np.ndarray:
+    return kq.unpack(words.view(np.uint32), bits, i)
+
+
+def replay_compare(gpu_codes: np.ndarray, W2: np.ndarray, R: np.ndarray, bits: int, group: int, block: int,
+                   rows=None, tie: float = TIE, max_replays_per_row: int = 64) -> dict:
+    """Compare GPU codes with the oracle sweep on W2 / R (float64), replaying near-tie flips.
+
+    ``rows``: row indices of W2 / gpu_codes to check (all by default). W2 and gpu_codes are indexed by
+    the same row numbers. Returns counts and the oracle codes / outputs after replay for those rows."""
+    o, i = gpu_codes.shape
+    rows = np.arange(o) if rows is None else np.asarray(rows)
+    out = {"replays": 0, "fail": [], "codes": {}, "Q": {}, "row_loss": {}, "mu": {}, "scale": {}}
+    for r in rows:
+        w = W2[r:r + 1]
+        g = gpu_codes[r]
+        fm = np.zeros((1, i), bool)
+        fc = np.zeros((1, i), np.int64)
+        n_rep = 0
+        while True:
+            res = kq.sweep_blocked(w, R, bits, group, block, force_mask=fm, force_codes=fc)
+            c = res["codes"][0]
+            diff = np.nonzero(c != g)[0]
+            if diff.size == 0:
+                break
+            j = diff[0]
+            d = res["delta"][0, j]
+            if d > tie or n_rep >= max_replays_per_row:
+                out["fail"].append((int(r), int(j), float(d), int(c[j]), int(g[j])))
+                break
+            fm[0, j] = True
+            fc[0, j] = g[j]
+            n_rep += 1
+        out["replays"] += n_rep
+        out["codes"][int(r)] = res["codes"][0]
+        out["Q"][int(r)] = res["Q"][0]
+        out["row_loss"][int(r)] = res["row_loss"][0]
+        out["mu"][int(r)] = res["mu"][0]
+        out["scale"][int(r)] = res["scale"][0]
+    return out
+
+
+def rel_fro(a, b) -> float:
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    nb = np.linalg.norm(b)
+    return float(np.linalg.norm(a - b) / (nb if nb > 0 else 1.0))

@@ -1,0 +1,264 @@
+"""Per-call parity of the HIP library (through the C ABI) against the float64 oracle.
+
+Each call gets the same input bits as the oracle (bf16 / fp32 values widened exactly); inputs that
+come from an earlier step are produced by the oracle and rounded to fp32, so a call is checked in
+isolation. Sizes span several tiles and a ragged tail.
+"""
+import numpy as np
+import pytest
+
+import synth
+from oracle import kronq as kq
+from post_quantization_03_amd import _lib as K
+from tests.gpu_util import host, say, to_dev, torch_dev, ws_tensor
+from tests.parity import gpu_words_to_codes, rel_fro, replay_compare
+
+pytestmark = pytest.mark.gpu
+f32 = np.float32
+
+
+def spd_f32(rng, d, n=None, spread=1.0):
+    n = n or 3 * d
+    G = rng.standard_normal((n, d)) * np.exp(spread * rng.standard_normal(d))
+    return (G.T @ G / n).astype(f32)
+
+
+def signs(rng, d):
+    return (rng.integers(0, 2, d) * 2 - 1).astype(np.int8)
+
+
+# ----------------------------------------------------------------------------- H_X
+@pytest.mark.parametrize("n,d,dt", [(1000, 200, "bf16"), (4096, 384, "bf16"), (300, 132, "f32"), (64, 8, "bf16"),
+                                    (70000, 256, "bf16")])
+def test_hessian_accum(n, d, dt):
+    torch, dev = torch_dev()
+    say(f"hessian n={n} d={d} {dt}")
+    sp = synth.scaled(synth.CONFIGS["C2"], n=n, i=d, x_dtype=dt, n_outliers=max(1, d // 100))
+    Xs = synth.gen_X(sp)
+    ref = kq.hessian(synth.widen(Xs, dt))
+    X = to_dev(Xs, dt)
+    H = torch.empty((d, d), dtype=torch.float32, device=dev)
+    ws = ws_tensor(K.kq_workspace_bytes("hessian", 0, d, n, K.KQ_BF16 if dt == "bf16" else K.KQ_F32))
+    K.kq_hessian_accum(X, H, 1.0 / n, 0.0, ws)
+    Hg = host(H).astype(np.float64)
+    assert np.array_equal(Hg, Hg.T)
+    assert rel_fro(Hg, ref) <= 1e-5
+    assert np.abs(Hg - ref).max() <= 1e-5 * np.diag(ref).max()
+
+
+def test_hessian_accumulates_batches():
+    torch, dev = torch_dev()
+    sp = synth.scaled(synth.CONFIGS["C2"], n=3000, i=256)
+    Xs = synth.gen_X(sp)
+    ref = kq.hessian(synth.widen(Xs, "bf16"))
+    X = to_dev(Xs, "bf16")
+    H = torch.empty((256, 256), dtype=torch.float32, device=dev)
+    ws = ws_tensor(K.kq_workspace_bytes("hessian", 0, 256, 3000))
+    for k0, beta in ((0, 0.0), (1000, 1.0), (2000, 1.0)):
+        K.kq_hessian_accum(X[k0:k0 + 1000], H, 1.0 / 3000, beta, ws)
+    assert rel_fro(host(H), ref) <= 1e-5
+
+
+# ----------------------------------------------------------------------------- input rotation
+@pytest.mark.parametrize("o,i,wdt,with_h", [(40, 256, "f32", True), (33, 320, "bf16", True), (16, 224, "f32", True),
+                                            (8, 384, "bf16", True), (24, 1728, "bf16", True), (5, 11008, "bf16", False),
+                                            (3, 5120, "f32", True)])
+def test_rotate_in(o, i, wdt, with_h):
+    torch, dev = torch_dev()
+    say(f"rotate_in o={o} i={i} {wdt} H={with_h}")
+    rng = np.random.default_rng(o * 7 + i)
+    W64 = rng.standard_normal((o, i)) * 0.02
+    Ws = synth.f32_to_bf16_bits(W64.astype(f32)) if wdt == "bf16" else W64.astype(f32)
+    s = signs(rng, i)
+    H32 = spd_f32(rng, i, n=i + 16) if with_h else None
+    W1_ref = kq.rotate_in_weights(synth.widen(Ws, wdt), s)
+    Win = to_dev(Ws, wdt)
+    Wout = torch.empty((o, i), dtype=torch.float32, device=dev)
+    Hd = to_dev(H32) if with_h else None
+    ws = ws_tensor(K.kq_workspace_bytes("rotate_in", o, i))
+    K.kq_rotate_in(Win, Wout, Hd, to_dev(s, "i8"), ws)
+    assert rel_fro(host(Wout), W1_ref) <= 2e-6
+    if with_h:
+        H2_ref = kq.rotate_in_hessian(H32.astype(np.float64), s)
+        assert rel_fro(host(Hd), H2_ref) <= 2e-6
+
+
+# ----------------------------------------------------------------------------- H_G square root
+@pytest.mark.parametrize("form,o,blk", [("diag", 1000, 0), ("block", 384, 128), ("full", 256, 0), ("full", 200, 0),
+                                        ("block", 256, 64)])
+def test_hg_sqrt(form, o, blk):
+    torch, dev = torch_dev()
+    say(f"hg_sqrt {form} o={o} blk={blk}")
+    if form == "diag":
+        hg = synth.gen_HG(synth.scaled(synth.CONFIGS["C3"], o=o))
+    elif form == "block":
+        hg = synth.gen_HG(synth.scaled(synth.CONFIGS["C4"], o=o, hg_blk=blk))
+    else:
+        hg = synth.gen_HG(synth.scaled(synth.CONFIGS["C2"], o=o, hg_ng=2 * o))
+    S_ref, Si_ref = kq.hg_sqrt(hg.astype(np.float64), form)
+    S = torch.empty(hg.shape, dtype=torch.float32, device=dev)
+    Si = torch.empty_like(S)
+    info = torch.zeros(1, dtype=torch.int32, device=dev)
+    ws = ws_tensor(K.kq_workspace_bytes("hg_sqrt", o, 0, 0, form=form, blk=blk))
+    K.kq_hg_sqrt(to_dev(hg), form, o, blk, S, Si, info, ws)
+    assert int(host(info)[0]) == 0
+    assert rel_fro(host(S), S_ref) <= 1e-6
+    assert rel_fro(host(Si), Si_ref) <= 1e-6
+
+
+def test_hg_sqrt_reports_not_positive_definite():
+    torch, dev = torch_dev()
+    for form, hg in (("full", -np.eye(128, dtype=f32)), ("diag", -np.ones(64, f32))):
+        o = hg.shape[0]
+        S = torch.empty(hg.shape, dtype=torch.float32, device=dev)
+        info = torch.zeros(1, dtype=torch.int32, device=dev)
+        ws = ws_tensor(K.kq_workspace_bytes("hg_sqrt", o, 0, 0, form=form))
+        K.kq_hg_sqrt(to_dev(hg), form, o, 0, S, None, info, ws)
+        assert int(host(info)[0]) > 0
+
+
+# ----------------------------------------------------------------------------- output transform
+@pytest.mark.parametrize("form,o,i,blk", [("diag", 256, 128, 0), ("diag", 320, 64, 0), ("full", 256, 192, 0),
+                                          ("block", 384, 128, 128), ("full", 224, 64, 0), ("block", 5120, 16, 128)])
+def test_rotate_out(form, o, i, blk):
+    torch, dev = torch_dev()
+    say(f"rotate_out {form} o={o} i={i}")
+    rng = np.random.default_rng(o + i)
+    W = (rng.standard_normal((o, i)) * 0.02).astype(f32)
+    t = signs(rng, o)
+    if form == "diag":
+        S = np.exp(rng.standard_normal(o)).astype(f32)
+    elif form == "block":
+        S = np.stack([spd_f32(rng, blk) for _ in range(o // blk)])
+    else:
+        S = spd_f32(rng, o)
+    ref = kq.rotate_out(W.astype(np.float64), S.astype(np.float64), form, t)
+    Wd = to_dev(W)
+    ws = ws_tensor(K.kq_workspace_bytes("rotate_out", o, i, form=form, blk=blk))
+    K.kq_rotate_out(Wd, to_dev(S), form, blk, to_dev(t, "i8"), ws)
+    assert rel_fro(host(Wd), ref) <= 2e-6
+
+
+# ----------------------------------------------------------------------------- damped factor
+@pytest.mark.parametrize("i", [200, 384, 1000, 128])
+def test_cholinv(i):
+    torch, dev = torch_dev()
+    say(f"cholinv i={i}")
+    sp = synth.scaled(synth.CONFIGS["C2"], n=4 * i, i=i, n_outliers=max(1, i // 100))
+    H32 = kq.hessian(synth.widen(synth.gen_X(sp), "bf16")).astype(f32)
+    H, _ = kq.damped(H32.astype(np.float64), 0.01)
+    R_ref = kq.inverse_upper_factor(H)
+    R = torch.empty((i, i), dtype=torch.float32, device=dev)
+    info = torch.full((1,), 7, dtype=torch.int32, device=dev)
+    ws = ws_tensor(K.kq_workspace_bytes("cholinv", 0, i))
+    K.kq_cholinv(to_dev(H32), 0.01, R, info, ws)
+    Rg = host(R).astype(np.float64)
+    assert int(host(info)[0]) == 0
+    assert np.all(np.tril(Rg, -1) == 0)
+    err = rel_fro(Rg, R_ref)
+    say(f"  R rel err {err:.3e} cond {np.linalg.cond(H):.3e}")
+    assert err <= 1e-6
+
+
+def test_cholinv_reports_not_positive_definite():
+    torch, dev = torch_dev()
+    i = 256
+    H = -np.eye(i, dtype=f32)
+    R = torch.empty((i, i), dtype=torch.float32, device=dev)
+    info = torch.zeros(1, dtype=torch.int32, device=dev)
+    K.kq_cholinv(to_dev(H), 0.0, R, info, ws_tensor(K.kq_workspace_bytes("cholinv", 0, i)))
+    assert int(host(info)[0]) > 0
+
+
+# ----------------------------------------------------------------------------- sweep
+@pytest.mark.parametrize("o,i,bits,group", [(37, 384, 3, 128), (37, 384, 4, 0), (64, 256, 2, 128), (20, 512, 2, 0),
+                                            (16, 256, 3, 64), (9, 256, 8, 32), (130, 1024, 3, 128)])
+def test_quantize_layer(o, i, bits, group):
+    torch, dev = torch_dev()
+    say(f"quantize o={o} i={i} b={bits} g={group}")
+    sp = synth.scaled(synth.CONFIGS["C2"], o=o, i=i, n=4 * i, hg_ng=2 * o if o >= 64 else 256, n_outliers=2)
+    d = synth.layer_inputs(sp)
+    hg = d["HG"] if o >= 64 else np.ones(o, f32)
+    form = "full" if o >= 64 else "diag"
+    r = kq.quantize_layer(synth.widen(d["X"], "bf16"), synth.widen(d["W"], "bf16"), hg.astype(np.float64), form,
+                          d["s"], d["t"], bits, group, verify=False, rotate_out_on=False)
+    W2 = r["W2"].astype(f32)
+    R = r["R"].astype(f32)
+    Wd = to_dev(W2)
+    codes = torch.empty((o, i * bits // 32), dtype=torch.int32, device=dev)
+    ng = i // group if group else 1
+    scale = torch.empty((o, ng), dtype=torch.float32, device=dev)
+    offset = torch.empty((o, ng), dtype=torch.float32, device=dev)
+    rl = torch.empty((o,), dtype=torch.float32, device=dev)
+    ws = ws_tensor(K.kq_workspace_bytes("quantize", o, i))
+    K.kq_quantize_layer(Wd, to_dev(R), bits, group, 128, codes, scale, offset, rl, ws)
+    words = host(codes)
+    gc = gpu_words_to_codes(words, bits, i)
+    cmp = replay_compare(gc, W2.astype(np.float64), R.astype(np.float64), bits, group, 128)
+    say(f"  replays={cmp['replays']} fail={cmp['fail'][:3]}")
+    assert not cmp["fail"]
+    oc = np.stack([cmp["codes"][k] for k in range(o)])
+    assert np.array_equal(kq.pack(oc, bits), words.view(np.uint32))
+    Q = np.stack([cmp["Q"][k] for k in range(o)])
+    assert rel_fro(host(Wd), Q) <= 1e-5
+    loss = np.array([cmp["row_loss"][k] for k in range(o)])
+    assert np.allclose(host(rl), loss, rtol=1e-3, atol=1e-12)
+    mu = np.stack([cmp["mu"][k] for k in range(o)])
+    sc = np.stack([cmp["scale"][k] for k in range(o)])
+    assert rel_fro(host(offset), mu) <= 1e-5 and rel_fro(host(scale), sc) <= 1e-5
+
+
+# ----------------------------------------------------------------------------- sensitivity, unrotate, loss
+@pytest.mark.parametrize("form", ["diag", "block", "full"])
+def test_sensitivity(form):
+    torch, dev = torch_dev()
+    rng = np.random.default_rng(3)
+    i, o = 300, 256
+    H = spd_f32(rng, i)
+    hg = {"diag": np.exp(rng.standard_normal(o)).astype(f32),
+          "block": np.stack([spd_f32(rng, 64) for _ in range(4)]),
+          "full": spd_f32(rng, o)}[form]
+    score = torch.empty(1, dtype=torch.float64, device=dev)
+    K.kq_sensitivity(to_dev(H), to_dev(hg), form, o, 64, score)
+    ref = kq.sensitivity(H.astype(np.float64), hg.astype(np.float64), form)
+    assert abs(host(score)[0] / ref - 1) <= 1e-12
+
+
+@pytest.mark.parametrize("form,o,i,blk", [("full", 256, 320, 0), ("diag", 320, 256, 0), ("block", 256, 1728, 128)])
+def test_unrotate_and_loss(form, o, i, blk):
+    torch, dev = torch_dev()
+    say(f"unrotate {form} o={o} i={i}")
+    rng = np.random.default_rng(o * i)
+    Q = (rng.standard_normal((o, i)) * 0.02).astype(f32)
+    W2 = (Q + rng.standard_normal((o, i)) * 0.002).astype(f32)
+    s, t = signs(rng, i), signs(rng, o)
+    if form == "diag":
+        Si = np.exp(rng.standard_normal(o)).astype(f32)
+    elif form == "block":
+        Si = np.stack([spd_f32(rng, blk) for _ in range(o // blk)])
+    else:
+        Si = spd_f32(rng, o)
+    ref = kq.unrotate(Q.astype(np.float64), s, t, Si.astype(np.float64), form)
+    What = torch.empty((o, i), dtype=torch.float32, device=dev)
+    ws = ws_tensor(max(K.kq_workspace_bytes("unrotate", o, i, form=form, blk=blk), K.kq_workspace_bytes("loss", o, i)))
+    K.kq_unrotate(to_dev(Q), to_dev(s, "i8"), to_dev(t, "i8"), to_dev(Si), form, blk, What, ws)
+    assert rel_fro(host(What), ref) <= 2e-6
+    H = spd_f32(rng, i)
+    loss = torch.empty(1, dtype=torch.float64, device=dev)
+    rl = torch.empty(o, dtype=torch.float64, device=dev)
+    K.kq_layer_loss(to_dev(W2), to_dev(Q), to_dev(H), rl, loss, ws)
+    lref = kq.rotated_loss(W2.astype(np.float64), Q.astype(np.float64), H.astype(np.float64))
+    assert abs(host(loss)[0] / lref.sum() - 1) <= 1e-5
+    assert np.allclose(host(rl), lref, rtol=1e-4)
+
+
+def test_argument_errors_are_reported():
+    torch, dev = torch_dev()
+    W = torch.zeros((8, 100), dtype=torch.float32, device=dev)
+    R = torch.zeros((100, 100), dtype=torch.float32, device=dev)
+    with pytest.raises(K.KQError) as e:
+        K.kq_quantize_layer(W, R, 3, 128, 128, W, W, W, None, ws_tensor(1 << 20))
+    assert e.value.status == 2   # i not a multiple of 128
+    with pytest.raises(K.KQError) as e:
+        K.kq_rotate_in(W, W, None, torch.ones(100, dtype=torch.int8, device=dev), ws_tensor(1 << 20))
+    assert e.value.status == 4   # 100 = 25 * 4: no Hadamard order
