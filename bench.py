@@ -1,0 +1,231 @@
+"""Layer-quantization throughput of the KronQ per-layer solver on one MI355X.
+
+One step = the whole per-layer path on device-resident inputs (X, W, H_G, signs):
+  H_X accumulation, sensitivity, input rotation, H_G^{1/2} (+ inverse), output transform,
+  damped inverse factor, GPTQ sweep with packing.
+Workload: 4096 x 4096 layer, 65536 bf16 calibration tokens, full H_G, 3-bit asymmetric, group 128
+(synthetic, seeded; stands in for the LLaMA-2-7B q_proj layer the KronQ pages quantize).
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+
+PEAK = {"hbm": 8.0e12, "fp32_mfma": 157.3e12, "fp64_mfma": 78.6e12, "bf16_mfma": 2.5e15}
+
+
+def algorithmic_work(sp, iters_db: int) -> dict:
+    """Per-phase algorithmic FLOP / bytes of one layer (what the method must compute or move)."""
+    o, i, n, b, g = sp.o, sp.i, sp.n, sp.bits, sp.group
+    xb = 2 if sp.x_dtype == "bf16" else 4
+    wb = 2 if sp.w_dtype == "bf16" else 4
+    w = {
+        "hessian": {"flop": n * i * (i + 1), "bytes": n * i * xb + 4 * i * i},
+        "rotate_in": {"bytes": o * i * (wb + 4) + 16 * i * i},
+        "hg_sqrt": {"flop": (2 * iters_db * o ** 3) if sp.hg_form == "full" else 0},
+        "rotate_out": {"flop": 2 * o * o * i if sp.hg_form == "full" else 0, "bytes": 8 * o * i},
+        "cholinv": {"flop": 2 * i ** 3 // 3},
+        "quantize": {"flop": o * i * (i - 128), "bytes": int((8 + b / 8 + (8 / g if g else 0)) * o * i + 2 * i * i)},
+    }
+    return w
+
+
+def run_gpu(sp, steps: int, warmup: int, phases: bool):
+    import torch
+
+    from post_quantization_03_amd import _lib as K
+    from post_quantization_03_amd.layer import LayerCfg, quantize_layer, workspace_bytes
+
+    dev = torch.device("cuda:0")
+    t0 = time.time()
+    d = synth.layer_inputs(sp)
+    print(f"# inputs generated in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+
+    def to(a, kind):
+        if kind == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    X, W, HG = to(d["X"], sp.x_dtype), to(d["W"], sp.w_dtype), to(d["HG"], "f32")
+    s, t = to(d["s"], "i8"), to(d["t"], "i8")
+    del d
+    cfg = LayerCfg(bits=sp.bits, group=sp.group, damp=sp.damp, form=sp.hg_form,
+                   blk=sp.hg_blk if sp.hg_form == "block" else 0)
+    xdt = K.KQ_BF16 if sp.x_dtype == "bf16" else K.KQ_F32
+    ws = torch.empty(workspace_bytes(sp.o, sp.i, sp.n, xdt, cfg), dtype=torch.uint8, device=dev)
+
+    def step():
+        return quantize_layer(X, W, HG, s, t, cfg, ws=ws)
+
+    for k in range(warmup):
+        out = step()
+        torch.cuda.synchronize()
+        print(f"# warmup {k + 1}/{warmup} done", file=sys.stderr, flush=True)
+    info = out["info"].cpu().tolist()
+    if info != [0, 0]:
+        raise RuntimeError(f"factorisation failed: info={info}")
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for _ in range(steps):
+        out = step()
+    torch.cuda.synchronize()
+    t_total = time.perf_counter() - t_start
+    ms = 1e3 * t_total / steps
+    print(f"# timed {steps} steps: {ms:.3f} ms/step", file=sys.stderr, flush=True)
+
+    ph = None
+    if phases:
+        ph = phase_times(sp, X, W, HG, s, t, cfg, ws)
+    return ms, ph, out
+
+
+def phase_times(sp, X, W, HG, s, t, cfg, ws, reps: int = 3) -> dict:
+    """Median per-phase time (ms) of the same calls, with HIP events on the stream they run on."""
+    import torch
+
+    from post_quantization_03_amd import _lib as K
+    from post_quantization_03_amd.layer import hg_factor_shape
+
+    dev = X.device
+    o, i, n = sp.o, sp.i, sp.n
+    f32 = dict(dtype=torch.float32, device=dev)
+    H = torch.empty((i, i), **f32)
+    W2 = torch.empty((o, i), **f32)
+    S = torch.empty(hg_factor_shape(o, cfg), **f32)
+    R = torch.empty((i, i), **f32)
+    info = torch.zeros(2, dtype=torch.int32, device=dev)
+    score = torch.empty(1, dtype=torch.float64, device=dev)
+    ng = i // cfg.group if cfg.group else 1
+    codes = torch.empty((o, i * cfg.bits // 32), dtype=torch.int32, device=dev)
+    scale = torch.empty((o, ng), **f32)
+    offset = torch.empty((o, ng), **f32)
+    rl = torch.empty((o,), **f32)
+    calls = [
+        ("hessian", lambda: K.kq_hessian_accum(X, H, 1.0 / n, 0.0, ws)),
+        ("sensitivity", lambda: K.kq_sensitivity(H, HG, cfg.form, o, cfg.blk, score)),
+        ("rotate_in", lambda: K.kq_rotate_in(W, W2, H, s, ws)),
+        ("hg_sqrt", lambda: K.kq_hg_sqrt(HG, cfg.form, o, cfg.blk, S, None, info[0:1], ws)),
+        ("rotate_out", lambda: K.kq_rotate_out(W2, S, cfg.form, cfg.blk, t, ws)),
+        ("cholinv", lambda: K.kq_cholinv(H, cfg.damp, R, info[1:2], ws)),
+        ("quantize", lambda: K.kq_quantize_layer(W2, R, cfg.bits, cfg.group, cfg.block, codes, scale, offset, rl, ws)),
+    ]
+    res = {name: [] for name, _ in calls}
+    for _ in range(reps):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)]
+        ev[0].record()
+        for k, (name, fn) in enumerate(calls):
+            fn()
+            ev[k + 1].record()
+        torch.cuda.synchronize()
+        for k, (name, _) in enumerate(calls):
+            res[name].append(ev[k].elapsed_time(ev[k + 1]))
+    return {k: float(np.median(v)) for k, v in res.items()}
+
+
+def cpu_baseline(sp, budget_s: float = 30.0) -> dict:
+    """The float64 oracle, as it stands, on a bounded sample of the same layer; extrapolated per phase."""
+    from oracle import kronq as kq
+
+    cores = len(os.sched_getaffinity(0))
+    try:
+        from threadpoolctl import threadpool_limits
+        limiter = threadpool_limits(limits=cores)
+    except Exception:  # pragma: no cover
+        limiter = None
+    n_tok = 2048
+    n_rows = 128
+    d = synth.layer_inputs(sp, x_rows=n_tok)
+    X = synth.widen(d["X"], sp.x_dtype)
+    W = synth.widen(d["W"], sp.w_dtype)
+    HG = d["HG"].astype(np.float64)
+    t = {}
+    t0 = time.perf_counter()
+    HX = kq.hessian(X)
+    t["hessian"] = (time.perf_counter() - t0) * sp.n / n_tok
+    t0 = time.perf_counter()
+    W1 = kq.rotate_in_weights(W, d["s"])
+    HX2 = kq.rotate_in_hessian(HX, d["s"])
+    t["rotate_in"] = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    S, _ = kq.hg_sqrt(HG, sp.hg_form)
+    t["hg_sqrt"] = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    W2 = kq.rotate_out(W1, S, sp.hg_form, d["t"])
+    t["rotate_out"] = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    H, _ = kq.damped(HX2, sp.damp)
+    R = kq.inverse_upper_factor(H)
+    t["cholinv"] = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    kq.sweep_blocked(W2[:n_rows], R, sp.bits, sp.group, sp.block)
+    t["quantize"] = (time.perf_counter() - t0) * sp.o / n_rows
+    if limiter is not None:
+        limiter.unregister() if hasattr(limiter, "unregister") else None
+    total = sum(t.values())
+    return {"value": sp.o * sp.i / total / 1e6, "unit": "Mweights/s", "cores": cores, "kind": "oracle",
+            "sample": (f"float64 oracle phases on the same layer: H_X on the first {n_tok} of {sp.n} tokens "
+                       f"(x{sp.n // n_tok}), sweep on {n_rows} of {sp.o} rows (x{sp.o // n_rows}), rotations, "
+                       f"H_G square root (eigh) and damped factor in full; extrapolated layer time {total:.1f} s"),
+            "phases_s": {k: round(v, 3) for k, v in t.items()}}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="C2", choices=["C2", "C3", "C4"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-phases", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the per-layer solver runs on a single MI355X in this build "
+              "(multi-GPU sharding is described in DESIGN.md, not implemented).", file=sys.stderr)
+        sys.exit(2)
+    sp = synth.CONFIGS[args.workload]
+    ms, ph, out = run_gpu(sp, args.steps, args.warmup, not args.no_phases)
+    value = sp.o * sp.i / (ms / 1e3) / 1e6
+    roof = None
+    if ph:
+        work = algorithmic_work(sp, iters_db=8)
+        dom = max((k for k in ph if k in work), key=lambda k: ph[k])
+        wk = work[dom]
+        if "flop" in wk and wk["flop"]:
+            bound = "mfma"
+            peak = PEAK["fp64_mfma"] if dom == "hg_sqrt" else (PEAK["bf16_mfma"] if dom == "hessian" else PEAK["fp32_mfma"])
+            ach = wk["flop"] / (ph[dom] / 1e3)
+            roof = {"bound": bound, "kernel": dom, "achieved": ach / 1e12, "peak": peak / 1e12, "unit": "TFLOP/s",
+                    "frac": ach / peak, "traffic": None}
+        else:
+            ach = wk["bytes"] / (ph[dom] / 1e3)
+            roof = {"bound": "hbm", "kernel": dom, "achieved": ach / 1e9, "peak": PEAK["hbm"] / 1e9, "unit": "GB/s",
+                    "frac": ach / PEAK["hbm"], "traffic": None}
+    cpu = None if args.no_cpu_baseline else cpu_baseline(sp)
+    line = {"metric": "layer-quant throughput: Mweights/s (4096x4096 W3 g128) + % MFMA/HBM peak",
+            "value": round(value, 3), "unit": "Mweights/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "fp32", "data": "synthetic",
+            "config": {"workload": sp.name, "o": sp.o, "i": sp.i, "tokens": sp.n, "x_dtype": sp.x_dtype,
+                       "hg_form": sp.hg_form, "bits": sp.bits, "group": sp.group,
+                       "arith": "bf16 MFMA (exact products) for H_X, fp64 for H_G^1/2 and the damped factor, fp32 elsewhere"},
+            "phases_ms": {k: round(v, 4) for k, v in ph.items()} if ph else None,
+            "roofline": roof, "cpu_baseline": cpu}
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
