@@ -39,7 +39,11 @@ struct alignas(16) V16 {
     T v[16 / sizeof(T)];
 };
 
-constexpr int GBM = 128, GBN = 128, GPAD = 16;
+constexpr int GBM = 128, GBN = 128;
+// LDS row pad (elements): makes the row stride 16 banks modulo 32 for both element sizes, so the
+// four 16-lane groups of an operand read (rows kr..kr+3) fall on alternate bank halves.
+template <typename T>
+constexpr int gpad() { return sizeof(T) == 8 ? 8 : 16; }
 
 // ===================================================================================== GEMM kernel
 // 256 threads = 4 waves in a 2 x 2 arrangement; each wave owns a 64 x 64 block of C as 4 x 4
@@ -53,12 +57,13 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs<T> g) {
     if (g.skip && *g.skip) return;
     constexpr int BK = 64 / sizeof(T);
     constexpr int VN = 16 / sizeof(T);
-    __shared__ T As[2][BK][GBM + GPAD];
-    __shared__ T Bs[2][BK][GBN + GPAD];
+    __shared__ T As[2][BK][GBM + gpad<T>()];
+    __shared__ T Bs[2][BK][GBN + gpad<T>()];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int64_t m0 = (int64_t)blockIdx.y * GBM, n0 = (int64_t)blockIdx.x * GBN;
     if (g.tri == 1 && n0 > m0 + GBM - 1) return;
     if (g.tri == 2 && m0 > n0 + GBN - 1) return;
+    if ((int64_t)blockIdx.y == g.skip_tile || (int64_t)blockIdx.x == g.skip_tile) return;
     const int64_t z = blockIdx.z, z1 = z / g.nb2, z2 = z % g.nb2;
     const T* __restrict__ A = g.A + z1 * g.sA1 + z2 * g.sA2;
     const T* __restrict__ B = g.B + z1 * g.sB1 + z2 * g.sB2;
@@ -174,24 +179,39 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs<T> g) {
         }
     }
 
+    // epilogue in four chunks of 16 values per lane: all loads of C for a chunk are issued before
+    // any of them is used, so the read-modify-write pays one memory latency per chunk
+    const int64_t nl = n0 + wn * 64 + (lane & 15);
 #pragma unroll
-    for (int i = 0; i < 4; i++)
+    for (int i = 0; i < 4; i++) {
+        T cv[4][4];
+        int64_t mr[4];
+#pragma unroll
+        for (int r = 0; r < 4; r++) mr[r] = m0 + wm * 64 + 16 * i + Mfma<T>::row(lane, r);
+        if (g.beta != T(0)) {
+#pragma unroll
+            for (int j = 0; j < 4; j++)
+#pragma unroll
+                for (int r = 0; r < 4; r++) {
+                    const int64_t n = nl + 16 * j;
+                    cv[j][r] = (mr[r] < M && n < N) ? C[mr[r] * g.ldc + n] : T(0);
+                }
+        }
 #pragma unroll
         for (int j = 0; j < 4; j++)
 #pragma unroll
             for (int r = 0; r < 4; r++) {
-                const int64_t m = m0 + wm * 64 + 16 * i + Mfma<T>::row(lane, r);
-                const int64_t n = n0 + wn * 64 + 16 * j + (lane & 15);
+                const int64_t m = mr[r], n = nl + 16 * j;
                 if (m >= M || n >= N) continue;
                 if (g.tri == 1 && n > m) continue;
                 if (g.tri == 2 && m > n) continue;
                 T v = g.alpha * acc[i][j][r];
                 if (rs) v *= T(rs[m]);
                 if (cs) v *= T(cs[n]);
-                T* pc = C + m * g.ldc + n;
-                if (g.beta != T(0)) v += g.beta * *pc;
-                *pc = v;
+                if (g.beta != T(0)) v += g.beta * cv[j][r];
+                C[m * g.ldc + n] = v;
             }
+    }
 }
 
 template <typename T>
@@ -563,197 +583,3 @@ extern "C" kq_status kq_cholinv(const float* HX, int64_t n, int64_t ldh, float d
     return check_launch("reverse_upper");
 }
 
-// ==================================================================================== kq_hg_sqrt
-namespace {
-constexpr int DB_MAXIT = 24;
-constexpr double DB_TOL = 1e-8;
-}
-
-__global__ void hg_diag_kernel(const float* h, int64_t o, float* S, float* Si, int32_t* info) {
-    for (int64_t r = blockIdx.x * 256 + threadIdx.x; r < o; r += (int64_t)gridDim.x * 256) {
-        const float v = h[r];
-        if (!(v > 0.0f)) {
-            atomicCAS(info, 0, (int32_t)(r + 1));  // any failing index; tests only check info > 0
-        }
-        const float sq = sqrtf(v > 0.0f ? v : 1.0f);
-        S[r] = sq;
-        if (Si) Si[r] = 1.0f / sq;
-    }
-}
-
-// Y_b = H_G block b (fp64), Z_b = I.
-__global__ void db_init_kernel(const float* HG, int64_t n, int64_t nbk, double* YZ, int* flags, double* ld) {
-    const int64_t nn = n * n;
-    for (int64_t e = blockIdx.x * 256 + threadIdx.x; e < nbk * nn; e += (int64_t)gridDim.x * 256) {
-        const int64_t b = e / nn, rc = e % nn, r = rc / n, c = rc % n;
-        YZ[e] = (double)HG[b * nn + rc];
-        YZ[(nbk + b) * nn + rc] = (r == c) ? 1.0 : 0.0;
-    }
-    if (blockIdx.x == 0 && threadIdx.x < 4) flags[threadIdx.x] = 0;
-    (void)ld;
-}
-
-__global__ void copy_d_kernel(const double* src, double* dst, size_t count, const int* skip) {
-    if (*skip) return;
-    for (size_t e = blockIdx.x * (size_t)256 + threadIdx.x; e < count; e += (size_t)gridDim.x * 256) dst[e] = src[e];
-}
-
-// Scaled Denman-Beavers update for the lower triangle, written symmetrically:
-//   mu = |det Y det Z|^{-1/(2n)},  Y <- (mu Y + Z^{-1} / mu) / 2,  Z <- (mu Z + Y^{-1} / mu) / 2
-// INV holds the inverses (lower triangles) in the same item order as YZ. Per-block partial sums
-// of ||Y_new - Y||^2 and ||Y_new||^2 go to part.
-__global__ void db_update_kernel(double* YZ, const double* INV, const double* ld, int64_t n, int64_t nbk, double* part,
-                                 const int* skip) {
-    if (*skip) return;
-    __shared__ double sd[256], sn[256];
-    const int64_t nn = n * n, tri = n * (n + 1) / 2;
-    double acc_d = 0, acc_n = 0;
-    for (int64_t e = blockIdx.x * 256 + threadIdx.x; e < nbk * tri; e += (int64_t)gridDim.x * 256) {
-        const int64_t b = e / tri;
-        int64_t t = e % tri;
-        // row r such that r(r+1)/2 <= t < (r+1)(r+2)/2
-        int64_t r = (int64_t)((sqrt(8.0 * (double)t + 1.0) - 1.0) * 0.5);
-        while (r * (r + 1) / 2 > t) r--;
-        while ((r + 1) * (r + 2) / 2 <= t) r++;
-        const int64_t c = t - r * (r + 1) / 2;
-        const double lmu = -(ld[b] + ld[nbk + b]) / (double)n;
-        const double mu = exp(lmu);
-        double* Y = YZ + b * nn;
-        double* Z = YZ + (nbk + b) * nn;
-        const double* Yi = INV + b * nn;
-        const double* Zi = INV + (nbk + b) * nn;
-        const double y = Y[r * n + c], zz = Z[r * n + c];
-        const double yn = 0.5 * (mu * y + Zi[r * n + c] / mu);
-        const double zn = 0.5 * (mu * zz + Yi[r * n + c] / mu);
-        const double w = (r == c) ? 1.0 : 2.0;
-        acc_d += w * (yn - y) * (yn - y);
-        acc_n += w * yn * yn;
-        Y[r * n + c] = yn;
-        Y[c * n + r] = yn;
-        Z[r * n + c] = zn;
-        Z[c * n + r] = zn;
-    }
-    sd[threadIdx.x] = acc_d;
-    sn[threadIdx.x] = acc_n;
-    __syncthreads();
-    for (int w = 128; w > 0; w >>= 1) {
-        if ((int)threadIdx.x < w) {
-            sd[threadIdx.x] += sd[threadIdx.x + w];
-            sn[threadIdx.x] += sn[threadIdx.x + w];
-        }
-        __syncthreads();
-    }
-    if (threadIdx.x == 0) {
-        part[2 * blockIdx.x] = sd[0];
-        part[2 * blockIdx.x + 1] = sn[0];
-    }
-}
-
-// flags[0]: done, flags[1]: iterations run. Stops on convergence, non-finite values or a failed
-// factorisation (info of any item), and reports the failure to the caller's info.
-__global__ void db_converge_kernel(const double* part, int nblk, int* flags, const int32_t* finfo, int64_t nitems,
-                                   int32_t* info, double tol) {
-    if (flags[0]) return;
-    if (threadIdx.x != 0) return;
-    double d = 0, nn = 0;
-    for (int b = 0; b < nblk; b++) { d += part[2 * b]; nn += part[2 * b + 1]; }
-    int32_t bad = 0;
-    for (int64_t k = 0; k < nitems; k++)
-        if (finfo[k] != 0) { bad = finfo[k]; break; }
-    flags[1] += 1;
-    const double rel = sqrt(d / nn);
-    if (bad) { *info = bad; flags[0] = 1; return; }
-    if (!(rel == rel) || !(nn > 0)) { *info = 1; flags[0] = 1; return; }
-    if (rel < tol) flags[0] = 1;
-}
-
-__global__ void db_out_kernel(const double* YZ, int64_t n, int64_t nbk, float* S, float* Si) {
-    const int64_t nn = n * n;
-    for (int64_t e = blockIdx.x * 256 + threadIdx.x; e < nbk * nn; e += (int64_t)gridDim.x * 256) {
-        S[e] = (float)YZ[e];
-        if (Si) Si[e] = (float)YZ[nbk * nn + e];
-    }
-}
-
-namespace {
-constexpr int DB_UPD_BLOCKS = 1024;
-
-template <typename Ar>
-void hg_layout(Ar& a, int64_t n, int64_t nbk) {
-    const size_t nn = (size_t)n * n, items = 2 * (size_t)nbk;
-    a.template take<double>(items * nn);                                   // YZ
-    a.template take<double>(items * nn);                                   // LYZ / inverses
-    a.template take<double>(items * nn);                                   // X = L^{-1}
-    a.template take<double>(items * ((size_t)(n * n / 2) + 64 * 64));      // trtri scratch
-    a.template take<double>(items);                                        // logdet
-    a.template take<int32_t>(items);                                       // per-item info
-    a.template take<double>(2 * DB_UPD_BLOCKS);                            // partial sums
-    a.template take<int>(4);                                               // flags
-}
-}  // namespace
-
-size_t hg_sqrt_ws(kq_hg_form form, int64_t o, int64_t blk) {
-    if (form == KQ_HG_DIAG) return 0;
-    const int64_t n = form == KQ_HG_FULL ? o : blk, nbk = form == KQ_HG_FULL ? 1 : o / blk;
-    Sizer z;
-    hg_layout(z, n, nbk);
-    return z.used;
-}
-
-extern "C" kq_status kq_hg_sqrt(const float* HG, kq_hg_form form, int64_t o, int64_t blk, float* S, float* Sinv,
-                                int32_t* info, void* ws, size_t ws_bytes, kq_stream stream) {
-    if (!HG || !S || !info) return fail(KQ_EINVAL, "kq_hg_sqrt: null pointer");
-    if (o <= 0) return fail(KQ_ESHAPE, "kq_hg_sqrt: o must be positive");
-    hipStream_t st = hs(stream);
-    if (form == KQ_HG_DIAG) {
-        KQ_TRY(fill<int>(reinterpret_cast<int*>(info), 1, 0, st));
-        unsigned blocks = (unsigned)((o + 255) / 256 < 1024 ? (o + 255) / 256 : 1024);
-        hipLaunchKernelGGL(hg_diag_kernel, dim3(blocks), dim3(256), 0, st, HG, o, S, Sinv, info);
-        return check_launch("hg_diag");
-    }
-    if (form != KQ_HG_BLOCK && form != KQ_HG_FULL) return fail(KQ_EINVAL, "kq_hg_sqrt: bad form");
-    if (form == KQ_HG_BLOCK && (blk <= 0 || o % blk)) return fail(KQ_ESHAPE, "kq_hg_sqrt: o must be a multiple of blk");
-    const int64_t n = form == KQ_HG_FULL ? o : blk, nbk = form == KQ_HG_FULL ? 1 : o / blk;
-    if (ws_bytes < hg_sqrt_ws(form, o, blk) || !ws) return fail(KQ_EWORKSPACE, "kq_hg_sqrt: workspace too small");
-    Arena ar(ws, ws_bytes);
-    const size_t nn = (size_t)n * n, items = 2 * (size_t)nbk;
-    double* YZ = ar.take<double>(items * nn);
-    double* LYZ = ar.take<double>(items * nn);
-    double* XYZ = ar.take<double>(items * nn);
-    double* Tscr = ar.take<double>(items * ((size_t)(n * n / 2) + 64 * 64));
-    double* ld = ar.take<double>(items);
-    int32_t* finfo = ar.take<int32_t>(items);
-    double* part = ar.take<double>(2 * DB_UPD_BLOCKS);
-    int* flags = ar.take<int>(4);
-    const int* done = flags;
-
-    KQ_TRY(fill<int>(reinterpret_cast<int*>(info), 1, 0, st));
-    KQ_TRY(fill<int>(reinterpret_cast<int*>(finfo), items, 0, st));
-    unsigned eb = (unsigned)((nbk * nn + 255) / 256 < 4096 ? (nbk * nn + 255) / 256 : 4096);
-    hipLaunchKernelGGL(db_init_kernel, dim3(eb), dim3(256), 0, st, HG, n, nbk, YZ, flags, ld);
-    KQ_TRY(check_launch("db_init"));
-    const int64_t tsz = (int64_t)(n * n / 2) + 64 * 64;
-    for (int it = 0; it < DB_MAXIT; it++) {
-        unsigned cb = (unsigned)((items * nn + 255) / 256 < 4096 ? (items * nn + 255) / 256 : 4096);
-        hipLaunchKernelGGL(copy_d_kernel, dim3(cb), dim3(256), 0, st, YZ, LYZ, items * nn, done);
-        KQ_TRY(check_launch("db_copy"));
-        KQ_TRY(fill<double>(XYZ, items * nn, 0.0, st, done));
-        KQ_TRY(fill<double>(ld, items, 0.0, st, done));
-        KQ_TRY(potrf_batched<double>(LYZ, n, (int64_t)nn, XYZ, n, (int64_t)nn, n, (int64_t)items, finfo, 1, ld, done,
-                                     st));
-        KQ_TRY(trtri_batched<double>(LYZ, n, (int64_t)nn, XYZ, n, (int64_t)nn, n, (int64_t)items, Tscr, done, st));
-        (void)tsz;
-        // inverse = X^T X (lower), written over the factor copies
-        GemmArgs<double> g = gemm_args<double>(n, n, n, XYZ, n, XYZ, n, LYZ, n, 1.0, 0.0);
-        g.nb1 = (int64_t)items; g.sA1 = (int64_t)nn; g.sB1 = (int64_t)nn; g.sC1 = (int64_t)nn;
-        g.tri = 1; g.kmode = 1; g.skip = done;
-        KQ_TRY(gemm<double>(g, true, false, st));
-        hipLaunchKernelGGL(db_update_kernel, dim3(DB_UPD_BLOCKS), dim3(256), 0, st, YZ, LYZ, ld, n, nbk, part, done);
-        KQ_TRY(check_launch("db_update"));
-        hipLaunchKernelGGL(db_converge_kernel, dim3(1), dim3(64), 0, st, part, DB_UPD_BLOCKS, flags, finfo,
-                           (int64_t)items, info, DB_TOL);
-        KQ_TRY(check_launch("db_converge"));
-    }
-    hipLaunchKernelGGL(db_out_kernel, dim3(eb), dim3(256), 0, st, YZ, n, nbk, S, Sinv);
-    return check_launch("db_out");
-}

@@ -1,0 +1,508 @@
+// Symmetric block Gauss-Jordan sweep (fp64) and the principal square root of H_G built on it.
+//
+// kq_hg_sqrt: S = H_G^{1/2} (principal) and S^{-1} for the output side of bidirectional incoherence
+// processing (KronQ review page, Method (1)). Scaled Denman-Beavers iteration
+//     Y_0 = A, Z_0 = I,  Y_{k+1} = (mu_k Y_k + Z_k^{-1} / mu_k) / 2,  Z_{k+1} = (mu_k Z_k + Y_k^{-1} / mu_k) / 2
+// In the eigenbasis of A both iterates follow the scalar Newton sign step x <- (mu x + 1/(mu x)) / 2
+// on x_0 = sqrt(lambda). The scale uses rigorous spectral bounds lambda_max <= ||A||_F and
+// lambda_min >= 1 / ||A^{-1}||_F: with the x-interval [a, b], mu = 1/sqrt(ab) maps it to
+// [1, (sqrt(b/a) + sqrt(a/b)) / 2], so the interval width after every step is known in closed form
+// and the iteration stops once it is below 1e-10 (about 7 steps for cond(A) = 4e9).
+//
+// The SPD inverses come from a lower-triangle block sweep with 128-wide pivots: per pivot block k
+// the panel C = A[:, k] is gathered (symmetric), the pivot P = C[k] is inverted in registers of one
+// work-group, T = C P^{-1} and A_RR -= T C^T (fp64 MFMA GEMM, lower triangle, pivot tiles skipped),
+// then T and -P^{-1} are scattered back. After all pivots A holds -A^{-1}. Y and Z of every block are
+// one batch.
+#include <cmath>
+
+#include "kq_internal.h"
+
+namespace kq {
+
+constexpr int GJ_NB = 128;
+constexpr int GJ_RT = 32;  // rows per gather/scatter work-group
+
+// Panel C[r][c] = A(r, k0 + c) of the symmetric matrix stored in its lower triangle; c >= nbk -> 0.
+__global__ __launch_bounds__(256) void gj_gather_kernel(const double* __restrict__ A, int64_t n, int64_t lda, int64_t sA,
+                                                        int64_t k0, int nbk, double* __restrict__ C, int64_t sC,
+                                                        const int* skip) {
+    if (skip && *skip) return;
+    __shared__ double tile[GJ_RT][GJ_NB + 1];
+    const int tid = threadIdx.x;
+    const int64_t r0 = (int64_t)blockIdx.x * GJ_RT, z = blockIdx.y;
+    A += z * sA;
+    C += z * sC;
+    const int64_t k1 = k0 + nbk;
+    if (r0 >= k1) {
+        for (int e = tid; e < GJ_RT * GJ_NB; e += 256) {
+            const int64_t r = r0 + e / GJ_NB;
+            const int c = e % GJ_NB;
+            if (r < n) C[r * GJ_NB + c] = c < nbk ? A[r * lda + k0 + c] : 0.0;
+        }
+    } else if (r0 + GJ_RT <= k0) {
+        for (int e = tid; e < GJ_RT * GJ_NB; e += 256) {
+            const int c = e / GJ_RT, rr = e % GJ_RT;
+            tile[rr][c] = c < nbk ? A[(k0 + c) * lda + r0 + rr] : 0.0;
+        }
+        __syncthreads();
+        for (int e = tid; e < GJ_RT * GJ_NB; e += 256) {
+            const int rr = e / GJ_NB, c = e % GJ_NB;
+            C[(r0 + rr) * GJ_NB + c] = tile[rr][c];
+        }
+    } else {
+        for (int e = tid; e < GJ_RT * GJ_NB; e += 256) {
+            const int64_t r = r0 + e / GJ_NB;
+            const int c = e % GJ_NB;
+            if (r >= n) continue;
+            double v = 0.0;
+            if (c < nbk) {
+                const int64_t q = k0 + c;
+                v = r >= q ? A[r * lda + q] : A[q * lda + r];
+            }
+            C[r * GJ_NB + c] = v;
+        }
+    }
+}
+
+// Pinv = P^{-1} for the nbk x nbk pivot P = C[k0 : k0 + nbk][0 : nbk] (identity-padded to 128) by a
+// Gauss-Jordan sweep held in registers: thread (tr, tc) owns rows 8tr..8tr+7 and columns 8tc..8tc+7.
+// Pivots are taken four at a time: the 4 pivot rows and columns go through LDS (double-buffered, one
+// barrier per step), every thread inverts the 4 x 4 pivot block itself and applies the rank-4 update
+//     A_RR -= A_RJ D^{-1} A_JR,  A_RJ <- A_RJ D^{-1},  A_JR <- D^{-1} A_JR,  A_JJ <- -D^{-1}.
+__global__ __launch_bounds__(256) void gj_pivot_kernel(const double* __restrict__ C, int64_t sC, int64_t k0, int nbk,
+                                                       double* __restrict__ Pinv, int32_t* info, const int* skip) {
+    if (skip && *skip) return;
+    __shared__ double rowb[2][4][GJ_NB], colb[2][GJ_NB][4];
+    __shared__ int bad;
+    const int tid = threadIdx.x, tr = tid >> 4, tc = tid & 15;
+    const int64_t z = blockIdx.x;
+    const double* P = C + z * sC + k0 * GJ_NB;
+    double a[8][8];
+#pragma unroll
+    for (int rr = 0; rr < 8; rr++)
+#pragma unroll
+        for (int cc = 0; cc < 8; cc++) {
+            const int r = 8 * tr + rr, c = 8 * tc + cc;
+            a[rr][cc] = (r < nbk && c < nbk) ? P[r * GJ_NB + c] : (r == c ? 1.0 : 0.0);
+        }
+    if (tid == 0) bad = 0;
+    for (int jb = 0; jb < 16; jb++) {
+#pragma unroll
+        for (int half = 0; half < 2; half++) {
+            const int jo = 4 * half, j0 = 8 * jb + jo, buf = half;
+            if (tr == jb) {
+#pragma unroll
+                for (int q = 0; q < 4; q++)
+#pragma unroll
+                    for (int cc = 0; cc < 8; cc++) rowb[buf][q][8 * tc + cc] = a[jo + q][cc];
+            }
+            if (tc == jb) {
+#pragma unroll
+                for (int rr = 0; rr < 8; rr++)
+#pragma unroll
+                    for (int q = 0; q < 4; q++) colb[buf][8 * tr + rr][q] = a[rr][jo + q];
+            }
+            __syncthreads();
+            // 4 x 4 pivot block and its inverse (unpivoted Gauss-Jordan; SPD pivots are positive)
+            double D[4][4];
+#pragma unroll
+            for (int q = 0; q < 4; q++)
+#pragma unroll
+                for (int q2 = 0; q2 < 4; q2++) D[q][q2] = rowb[buf][q][j0 + q2];
+#pragma unroll
+            for (int t = 0; t < 4; t++) {
+                double p = D[t][t];
+                if (!(p > 0.0)) {
+                    if (tid == 0 && !bad) bad = j0 + t + 1;
+                    p = 1.0;
+                }
+                const double ip = 1.0 / p;
+#pragma unroll
+                for (int q = 0; q < 4; q++)
+#pragma unroll
+                    for (int q2 = 0; q2 < 4; q2++)
+                        if (q != t && q2 != t) D[q][q2] -= D[q][t] * D[t][q2] * ip;
+#pragma unroll
+                for (int q = 0; q < 4; q++)
+                    if (q != t) { D[q][t] *= ip; D[t][q] *= ip; }
+                D[t][t] = -ip;
+            }
+            // D now holds -D^{-1}
+            double cv[8][4], rv[4][8], Tm[8][4];
+#pragma unroll
+            for (int rr = 0; rr < 8; rr++)
+#pragma unroll
+                for (int q = 0; q < 4; q++) cv[rr][q] = colb[buf][8 * tr + rr][q];
+#pragma unroll
+            for (int q = 0; q < 4; q++)
+#pragma unroll
+                for (int cc = 0; cc < 8; cc++) rv[q][cc] = rowb[buf][q][8 * tc + cc];
+#pragma unroll
+            for (int rr = 0; rr < 8; rr++)
+#pragma unroll
+                for (int q = 0; q < 4; q++) {
+                    double t = 0.0;
+#pragma unroll
+                    for (int q2 = 0; q2 < 4; q2++) t = fma(cv[rr][q2], -D[q2][q], t);
+                    Tm[rr][q] = t;
+                }
+#pragma unroll
+            for (int rr = 0; rr < 8; rr++)
+#pragma unroll
+                for (int cc = 0; cc < 8; cc++) {
+                    double t = a[rr][cc];
+#pragma unroll
+                    for (int q = 0; q < 4; q++) t = fma(-Tm[rr][q], rv[q][cc], t);
+                    a[rr][cc] = t;
+                }
+            if (tr == jb) {
+#pragma unroll
+                for (int q = 0; q < 4; q++)
+#pragma unroll
+                    for (int cc = 0; cc < 8; cc++) {
+                        double t = 0.0;
+#pragma unroll
+                        for (int q2 = 0; q2 < 4; q2++) t = fma(-D[q][q2], rv[q2][cc], t);
+                        a[jo + q][cc] = t;
+                    }
+            }
+            if (tc == jb) {
+#pragma unroll
+                for (int rr = 0; rr < 8; rr++)
+#pragma unroll
+                    for (int q = 0; q < 4; q++) a[rr][jo + q] = Tm[rr][q];
+            }
+            if (tr == jb && tc == jb) {
+#pragma unroll
+                for (int q = 0; q < 4; q++)
+#pragma unroll
+                    for (int q2 = 0; q2 < 4; q2++) a[jo + q][jo + q2] = D[q][q2];
+            }
+        }
+    }
+    // the swept block holds -P^{-1}
+    double* out = Pinv + z * GJ_NB * GJ_NB;
+#pragma unroll
+    for (int rr = 0; rr < 8; rr++)
+#pragma unroll
+        for (int cc = 0; cc < 8; cc++) out[(8 * tr + rr) * GJ_NB + 8 * tc + cc] = -a[rr][cc];
+    __syncthreads();
+    if (tid == 0 && bad && info && info[z] == 0) info[z] = (int32_t)(k0 + bad);
+}
+
+// A(r, k0 + c) <- T[r][c] for r outside the pivot block (lower-triangle position), and the pivot
+// block <- -Pinv (lower triangle).
+__global__ __launch_bounds__(256) void gj_scatter_kernel(double* __restrict__ A, int64_t n, int64_t lda, int64_t sA,
+                                                         int64_t k0, int nbk, const double* __restrict__ T, int64_t sT,
+                                                         const double* __restrict__ Pinv, const int* skip) {
+    if (skip && *skip) return;
+    __shared__ double tile[GJ_RT][GJ_NB + 1];
+    const int tid = threadIdx.x;
+    const int64_t r0 = (int64_t)blockIdx.x * GJ_RT, z = blockIdx.y;
+    A += z * sA;
+    T += z * sT;
+    Pinv += z * GJ_NB * GJ_NB;
+    const int64_t k1 = k0 + nbk;
+    if (r0 >= k1) {
+        for (int e = tid; e < GJ_RT * GJ_NB; e += 256) {
+            const int64_t r = r0 + e / GJ_NB;
+            const int c = e % GJ_NB;
+            if (r < n && c < nbk) A[r * lda + k0 + c] = T[r * GJ_NB + c];
+        }
+    } else if (r0 + GJ_RT <= k0) {
+        for (int e = tid; e < GJ_RT * GJ_NB; e += 256) {
+            const int rr = e / GJ_NB, c = e % GJ_NB;
+            tile[rr][c] = T[(r0 + rr) * GJ_NB + c];
+        }
+        __syncthreads();
+        for (int e = tid; e < GJ_RT * GJ_NB; e += 256) {
+            const int c = e / GJ_RT, rr = e % GJ_RT;
+            if (c < nbk) A[(k0 + c) * lda + r0 + rr] = tile[rr][c];
+        }
+    } else {
+        for (int e = tid; e < GJ_RT * GJ_NB; e += 256) {
+            const int64_t r = r0 + e / GJ_NB;
+            const int c = e % GJ_NB;
+            if (r >= n || c >= nbk) continue;
+            const int64_t q = k0 + c;
+            if (r >= k0 && r < k1) {
+                if (c <= r - k0) A[r * lda + q] = -Pinv[(r - k0) * GJ_NB + c];
+            } else if (r > q) {
+                A[r * lda + q] = T[r * GJ_NB + c];
+            } else {
+                A[q * lda + r] = T[r * GJ_NB + c];
+            }
+        }
+    }
+}
+
+// A <- -A^{-1} for a batch of SPD matrices stored in their lower triangles (n x n, leading dimension
+// lda, item stride sA). Scratch: C, T (batch x n x 128) and Pinv (batch x 128 x 128).
+static kq_status gj_inverse_batched(double* A, int64_t n, int64_t lda, int64_t sA, int64_t batch, double* C, double* T,
+                                    double* Pinv, int32_t* info, const int* skip, hipStream_t st) {
+    if (batch > 65535) return fail(KQ_ESHAPE, "sweep batch too large");
+    const int64_t sC = n * GJ_NB;
+    const dim3 gr((unsigned)((n + GJ_RT - 1) / GJ_RT), (unsigned)batch);
+    for (int64_t k0 = 0, kt = 0; k0 < n; k0 += GJ_NB, kt++) {
+        const int nbk = (int)((n - k0) < GJ_NB ? (n - k0) : GJ_NB);
+        hipLaunchKernelGGL(gj_gather_kernel, gr, dim3(256), 0, st, A, n, lda, sA, k0, nbk, C, sC, skip);
+        KQ_TRY(check_launch("gj_gather"));
+        hipLaunchKernelGGL(gj_pivot_kernel, dim3((unsigned)batch), dim3(256), 0, st, C, sC, k0, nbk, Pinv, info, skip);
+        KQ_TRY(check_launch("gj_pivot"));
+        // T = C Pinv
+        GemmArgs<double> t = gemm_args<double>(n, nbk, nbk, C, GJ_NB, Pinv, GJ_NB, T, GJ_NB, 1.0, 0.0);
+        t.nb1 = batch; t.sA1 = sC; t.sB1 = GJ_NB * GJ_NB; t.sC1 = sC; t.skip = skip;
+        KQ_TRY(gemm<double>(t, false, false, st));
+        // A_RR -= T C^T (lower triangle, pivot tile row/column untouched)
+        if (n > nbk) {
+            GemmArgs<double> u = gemm_args<double>(n, n, nbk, T, GJ_NB, C, GJ_NB, A, lda, -1.0, 1.0);
+            u.nb1 = batch; u.sA1 = sC; u.sB1 = sC; u.sC1 = sA; u.tri = 1; u.skip = skip; u.skip_tile = kt;
+            KQ_TRY(gemm<double>(u, false, true, st));
+        }
+        hipLaunchKernelGGL(gj_scatter_kernel, gr, dim3(256), 0, st, A, n, lda, sA, k0, nbk, T, sC, Pinv, skip);
+        KQ_TRY(check_launch("gj_scatter"));
+    }
+    return KQ_OK;
+}
+
+// ---------------------------------------------------------------------------------- DB kernels
+constexpr int DB_MAXIT = 14;
+constexpr double DB_TOL = 1e-10;
+constexpr int NORM_PARTS = 32;
+
+__global__ void db_init_kernel(const float* HG, int64_t n, int64_t nbk, double* YZ, int* flags) {
+    const int64_t nn = n * n;
+    for (int64_t e = blockIdx.x * 256 + threadIdx.x; e < nbk * nn; e += (int64_t)gridDim.x * 256) {
+        const int64_t b = e / nn, rc = e % nn, r = rc / n, c = rc % n;
+        YZ[e] = (double)HG[b * nn + rc];
+        YZ[(nbk + b) * nn + rc] = (r == c) ? 1.0 : 0.0;
+    }
+    if (blockIdx.x == 0 && threadIdx.x < 4) flags[threadIdx.x] = 0;
+}
+
+// Partial sums of the squared Frobenius norm of symmetric matrices stored in their lower triangles;
+// part[z][p]. Runs only while flags[1] (iterations done) == it_only (or always when it_only < 0).
+__global__ void sym_norm_part_kernel(const double* A, int64_t n, int64_t sA, double* part, const int* flags,
+                                     int it_only) {
+    if (it_only >= 0 && (flags[0] || flags[1] != it_only)) return;
+    __shared__ double sp[256];
+    const int64_t z = blockIdx.y;
+    const int p = blockIdx.x;
+    const double* M = A + z * sA;
+    double acc = 0;
+    for (int64_t r = p; r < n; r += NORM_PARTS) {
+        for (int64_t c = threadIdx.x; c <= r; c += 256) {
+            const double v = M[r * n + c];
+            acc += (c == r ? 1.0 : 2.0) * v * v;
+        }
+    }
+    sp[threadIdx.x] = acc;
+    __syncthreads();
+    for (int w = 128; w > 0; w >>= 1) {
+        if ((int)threadIdx.x < w) sp[threadIdx.x] += sp[threadIdx.x + w];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) part[z * NORM_PARTS + p] = sp[0];
+}
+
+// Per block b: the scale mu_b of this step and the bound of the next x-interval [1, bnd_b].
+// flags[1] == 0: x in [sqrt(lo), sqrt(hi)], hi = ||A||_F, lo = 1 / ||A^{-1}||_F.
+__global__ void db_scale_kernel(const double* nrmA, const double* nrmInv, int64_t nbk, double* mu, double* bnd,
+                                const int* flags) {
+    if (flags[0]) return;
+    for (int64_t b = blockIdx.x * 256 + threadIdx.x; b < nbk; b += (int64_t)gridDim.x * 256) {
+        double sA = 0, sI = 0;
+        if (flags[1] == 0) {
+            for (int p = 0; p < NORM_PARTS; p++) { sA += nrmA[b * NORM_PARTS + p]; sI += nrmInv[b * NORM_PARTS + p]; }
+            const double hi = sqrt(sA), lo = 1.0 / sqrt(sI);
+            const double r = sqrt(hi / lo);                  // x-interval ratio
+            mu[b] = 1.0 / sqrt(sqrt(hi * lo));
+            bnd[b] = 0.5 * (sqrt(r) + 1.0 / sqrt(r));
+        } else {
+            const double bb = bnd[b];
+            mu[b] = 1.0 / sqrt(bb);
+            bnd[b] = 0.5 * (sqrt(bb) + 1.0 / sqrt(bb));
+        }
+    }
+}
+
+// Y <- (mu Y + Zinv / mu) / 2, Z <- (mu Z + Yinv / mu) / 2; NINV holds -inverses (lower triangles).
+// Lower triangle read, both triangles written; per-work-group partial sums of ||dY||^2 and ||Y||^2.
+constexpr int DB_UPD_BLOCKS = 1024;
+__global__ void db_update_kernel(double* YZ, const double* NINV, const double* mu, int64_t n, int64_t nbk, double* part,
+                                 const int* flags) {
+    if (flags[0]) return;
+    __shared__ double sd[256], sn[256];
+    const int64_t nn = n * n, tri = n * (n + 1) / 2;
+    double acc_d = 0, acc_n = 0;
+    for (int64_t e = blockIdx.x * 256 + threadIdx.x; e < nbk * tri; e += (int64_t)gridDim.x * 256) {
+        const int64_t b = e / tri;
+        const int64_t t = e % tri;
+        int64_t r = (int64_t)((sqrt(8.0 * (double)t + 1.0) - 1.0) * 0.5);
+        while (r * (r + 1) / 2 > t) r--;
+        while ((r + 1) * (r + 2) / 2 <= t) r++;
+        const int64_t c = t - r * (r + 1) / 2;
+        const double m = mu[b];
+        double* Y = YZ + b * nn;
+        double* Z = YZ + (nbk + b) * nn;
+        const double yi = -NINV[b * nn + r * n + c], zi = -NINV[(nbk + b) * nn + r * n + c];
+        const double y = Y[r * n + c], zz = Z[r * n + c];
+        const double yn = 0.5 * (m * y + zi / m);
+        const double zn = 0.5 * (m * zz + yi / m);
+        const double w = (r == c) ? 1.0 : 2.0;
+        acc_d += w * (yn - y) * (yn - y);
+        acc_n += w * yn * yn;
+        Y[r * n + c] = yn;
+        Y[c * n + r] = yn;
+        Z[r * n + c] = zn;
+        Z[c * n + r] = zn;
+    }
+    sd[threadIdx.x] = acc_d;
+    sn[threadIdx.x] = acc_n;
+    __syncthreads();
+    for (int w = 128; w > 0; w >>= 1) {
+        if ((int)threadIdx.x < w) {
+            sd[threadIdx.x] += sd[threadIdx.x + w];
+            sn[threadIdx.x] += sn[threadIdx.x + w];
+        }
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) {
+        part[2 * blockIdx.x] = sd[0];
+        part[2 * blockIdx.x + 1] = sn[0];
+    }
+}
+
+// flags[0]: done, flags[1]: steps taken. Done when every block's interval bound is within DB_TOL of
+// 1 and the last step moved Y by less than 1e-6 (relative); a failed pivot or a non-finite value
+// stops the iteration and is reported through info.
+__global__ void db_converge_kernel(const double* part, const double* bnd, int64_t nbk, int* flags,
+                                   const int32_t* finfo, int64_t nitems, int32_t* info) {
+    if (flags[0] || threadIdx.x != 0) return;
+    double d = 0, nn = 0, bmax = 0;
+    for (int b = 0; b < DB_UPD_BLOCKS; b++) { d += part[2 * b]; nn += part[2 * b + 1]; }
+    for (int64_t b = 0; b < nbk; b++) bmax = fmax(bmax, bnd[b] - 1.0);
+    int32_t bad = 0;
+    for (int64_t k = 0; k < nitems; k++)
+        if (finfo[k] != 0) { bad = finfo[k]; break; }
+    flags[1] += 1;
+    const double rel = sqrt(d / nn);
+    if (bad) { *info = bad; flags[0] = 1; return; }
+    if (!(rel == rel) || !(nn > 0) || !(bmax == bmax)) { *info = 1; flags[0] = 1; return; }
+    if (bmax < DB_TOL && rel < 1e-6) flags[0] = 1;
+}
+
+__global__ void db_out_kernel(const double* YZ, int64_t n, int64_t nbk, float* S, float* Si) {
+    const int64_t nn = n * n;
+    for (int64_t e = blockIdx.x * 256 + threadIdx.x; e < nbk * nn; e += (int64_t)gridDim.x * 256) {
+        S[e] = (float)YZ[e];
+        if (Si) Si[e] = (float)YZ[nbk * nn + e];
+    }
+}
+
+__global__ void copy_d_kernel(const double* src, double* dst, size_t count, const int* skip) {
+    if (*skip) return;
+    for (size_t e = blockIdx.x * (size_t)256 + threadIdx.x; e < count; e += (size_t)gridDim.x * 256) dst[e] = src[e];
+}
+
+__global__ void hg_diag_kernel(const float* h, int64_t o, float* S, float* Si, int32_t* info) {
+    for (int64_t r = blockIdx.x * 256 + threadIdx.x; r < o; r += (int64_t)gridDim.x * 256) {
+        const float v = h[r];
+        if (!(v > 0.0f)) atomicCAS(info, 0, (int32_t)(r + 1));  // tests only check info > 0
+        const float sq = sqrtf(v > 0.0f ? v : 1.0f);
+        S[r] = sq;
+        if (Si) Si[r] = 1.0f / sq;
+    }
+}
+
+template <typename Ar>
+static void hg_layout(Ar& a, int64_t n, int64_t nbk) {
+    const size_t nn = (size_t)n * n, items = 2 * (size_t)nbk;
+    a.template take<double>(items * nn);                     // YZ
+    a.template take<double>(items * nn);                     // sweep buffer (-inverses)
+    a.template take<double>(items * n * GJ_NB);              // C
+    a.template take<double>(items * n * GJ_NB);              // T
+    a.template take<double>(items * GJ_NB * GJ_NB);          // Pinv
+    a.template take<double>((size_t)nbk * NORM_PARTS);       // ||A||_F^2 parts
+    a.template take<double>(items * NORM_PARTS);             // ||A^{-1}||_F^2 parts
+    a.template take<double>(nbk);                            // mu
+    a.template take<double>(nbk);                            // interval bound
+    a.template take<int32_t>(items);                         // per-item info
+    a.template take<double>(2 * DB_UPD_BLOCKS);              // partial sums
+    a.template take<int>(4);                                 // flags
+}
+
+}  // namespace kq
+
+using namespace kq;
+
+size_t hg_sqrt_ws(kq_hg_form form, int64_t o, int64_t blk) {
+    if (form == KQ_HG_DIAG) return 0;
+    const int64_t n = form == KQ_HG_FULL ? o : blk, nbk = form == KQ_HG_FULL ? 1 : o / blk;
+    Sizer z;
+    hg_layout(z, n, nbk);
+    return z.used;
+}
+
+extern "C" kq_status kq_hg_sqrt(const float* HG, kq_hg_form form, int64_t o, int64_t blk, float* S, float* Sinv,
+                                int32_t* info, void* ws, size_t ws_bytes, kq_stream stream) {
+    if (!HG || !S || !info) return fail(KQ_EINVAL, "kq_hg_sqrt: null pointer");
+    if (o <= 0) return fail(KQ_ESHAPE, "kq_hg_sqrt: o must be positive");
+    hipStream_t st = hs(stream);
+    if (form == KQ_HG_DIAG) {
+        KQ_TRY(fill<int>(reinterpret_cast<int*>(info), 1, 0, st));
+        const unsigned blocks = (unsigned)((o + 255) / 256 < 1024 ? (o + 255) / 256 : 1024);
+        hipLaunchKernelGGL(hg_diag_kernel, dim3(blocks), dim3(256), 0, st, HG, o, S, Sinv, info);
+        return check_launch("hg_diag");
+    }
+    if (form != KQ_HG_BLOCK && form != KQ_HG_FULL) return fail(KQ_EINVAL, "kq_hg_sqrt: bad form");
+    if (form == KQ_HG_BLOCK && (blk <= 0 || o % blk)) return fail(KQ_ESHAPE, "kq_hg_sqrt: o must be a multiple of blk");
+    const int64_t n = form == KQ_HG_FULL ? o : blk, nbk = form == KQ_HG_FULL ? 1 : o / blk;
+    if (n > 65535 * (int64_t)GJ_RT) return fail(KQ_ESHAPE, "kq_hg_sqrt: too large");
+    if (!ws || ws_bytes < hg_sqrt_ws(form, o, blk)) return fail(KQ_EWORKSPACE, "kq_hg_sqrt: workspace too small");
+    Arena ar(ws, ws_bytes);
+    const size_t nn = (size_t)n * n, items = 2 * (size_t)nbk;
+    double* YZ = ar.take<double>(items * nn);
+    double* NI = ar.take<double>(items * nn);
+    double* C = ar.take<double>(items * n * GJ_NB);
+    double* T = ar.take<double>(items * n * GJ_NB);
+    double* Pinv = ar.take<double>(items * GJ_NB * GJ_NB);
+    double* nrmA = ar.take<double>((size_t)nbk * NORM_PARTS);
+    double* nrmI = ar.take<double>(items * NORM_PARTS);
+    double* mu = ar.take<double>(nbk);
+    double* bnd = ar.take<double>(nbk);
+    int32_t* finfo = ar.take<int32_t>(items);
+    double* part = ar.take<double>(2 * DB_UPD_BLOCKS);
+    int* flags = ar.take<int>(4);
+    const int* done = flags;
+
+    KQ_TRY(fill<int>(reinterpret_cast<int*>(info), 1, 0, st));
+    KQ_TRY(fill<int>(reinterpret_cast<int*>(finfo), items, 0, st));
+    const unsigned eb = (unsigned)((nbk * nn + 255) / 256 < 4096 ? (nbk * nn + 255) / 256 : 4096);
+    hipLaunchKernelGGL(db_init_kernel, dim3(eb), dim3(256), 0, st, HG, n, nbk, YZ, flags);
+    KQ_TRY(check_launch("db_init"));
+    hipLaunchKernelGGL(sym_norm_part_kernel, dim3(NORM_PARTS, (unsigned)nbk), dim3(256), 0, st, YZ, n, (int64_t)nn, nrmA,
+                       flags, -1);
+    KQ_TRY(check_launch("db_norm"));
+    const unsigned cb = (unsigned)((items * nn + 255) / 256 < 4096 ? (items * nn + 255) / 256 : 4096);
+    for (int it = 0; it < DB_MAXIT; it++) {
+        hipLaunchKernelGGL(copy_d_kernel, dim3(cb), dim3(256), 0, st, YZ, NI, items * nn, done);
+        KQ_TRY(check_launch("db_copy"));
+        KQ_TRY(gj_inverse_batched(NI, n, n, (int64_t)nn, (int64_t)items, C, T, Pinv, finfo, done, st));
+        // ||A^{-1}||_F of Y_0 = A (first step only; NI holds -A^{-1})
+        hipLaunchKernelGGL(sym_norm_part_kernel, dim3(NORM_PARTS, (unsigned)nbk), dim3(256), 0, st, NI, n, (int64_t)nn,
+                           nrmI, flags, 0);
+        KQ_TRY(check_launch("db_norm_inv"));
+        hipLaunchKernelGGL(db_scale_kernel, dim3((unsigned)((nbk + 255) / 256)), dim3(256), 0, st, nrmA, nrmI, nbk, mu,
+                           bnd, flags);
+        KQ_TRY(check_launch("db_scale"));
+        hipLaunchKernelGGL(db_update_kernel, dim3(DB_UPD_BLOCKS), dim3(256), 0, st, YZ, NI, mu, n, nbk, part, flags);
+        KQ_TRY(check_launch("db_update"));
+        hipLaunchKernelGGL(db_converge_kernel, dim3(1), dim3(64), 0, st, part, bnd, nbk, flags, finfo, (int64_t)items,
+                           info);
+        KQ_TRY(check_launch("db_converge"));
+    }
+    hipLaunchKernelGGL(db_out_kernel, dim3(eb), dim3(256), 0, st, YZ, n, nbk, S, Sinv);
+    return check_launch("db_out");
+}
