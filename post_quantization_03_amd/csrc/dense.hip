@@ -47,23 +47,46 @@ constexpr int gpad() { return sizeof(T) == 8 ? 8 : 16; }
 
 // ===================================================================================== GEMM kernel
 // 256 threads = 4 waves in a 2 x 2 arrangement; each wave owns a 64 x 64 block of C as 4 x 4
-// MFMA 16x16 tiles (K = 4 per instruction). K is staged through LDS in slices of 64 bytes per row
-// (16 floats / 8 doubles), double-buffered with one barrier per slice. LDS tiles are stored
+// MFMA 16x16 tiles (K = 4 per instruction). K is staged through LDS in slices, double-buffered with
+// one barrier per slice. LDS tiles are stored
 // k-major with a 16-element pad so that the 16-lane groups of an MFMA operand read hit disjoint
-// banks. MFMA operand layout (16x16x4): lane l holds A[l%16][l/16] and B[l/16][l%16]; the 4
+// banks. K slices are 16 elements deep (gemm_bk). MFMA operand layout (16x16x4): lane l holds A[l%16][l/16] and B[l/16][l%16]; the 4
 // accumulator registers hold column l%16 of C in the rows given by Mfma<T>::row.
+template <typename T>
+constexpr int gemm_bk() { return sizeof(T) == 8 ? 16 : 16; }
+
 template <typename T, bool TA, bool TB, bool VEC>
 __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs<T> g) {
     if (g.skip && *g.skip) return;
-    constexpr int BK = 64 / sizeof(T);
+    constexpr int BK = gemm_bk<T>();
     constexpr int VN = 16 / sizeof(T);
+    constexpr int VPR = BK / VN;                  // 16-byte vectors per tile row (k direction)
+    constexpr int NV = GBM * BK / VN / 256;       // vectors per thread per operand
     __shared__ T As[2][BK][GBM + gpad<T>()];
     __shared__ T Bs[2][BK][GBN + gpad<T>()];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int64_t m0 = (int64_t)blockIdx.y * GBM, n0 = (int64_t)blockIdx.x * GBN;
-    if (g.tri == 1 && n0 > m0 + GBM - 1) return;
-    if (g.tri == 2 && m0 > n0 + GBN - 1) return;
-    if ((int64_t)blockIdx.y == g.skip_tile || (int64_t)blockIdx.x == g.skip_tile) return;
+    // Tile order: work-groups are dealt round-robin to the 8 XCDs, so the linear id is remapped so
+    // that each XCD works on a contiguous range of tiles (neighbouring tiles share A / B panels in
+    // that XCD's L2). Triangular products launch only the stored triangle (1-D grid).
+    int64_t tm, tn;
+    {
+        const int64_t nx = (g.N + GBN - 1) / GBN;
+        const int64_t L = g.tri ? (int64_t)gridDim.x : (int64_t)gridDim.x * gridDim.y;
+        int64_t lid = g.tri ? (int64_t)blockIdx.x : (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
+        if (L % 8 == 0) lid = (lid % 8) * (L / 8) + lid / 8;
+        if (g.tri) {
+            int64_t r = (int64_t)((sqrt(8.0 * (double)lid + 1.0) - 1.0) * 0.5);
+            while (r * (r + 1) / 2 > lid) r--;
+            while ((r + 1) * (r + 2) / 2 <= lid) r++;
+            const int64_t c = lid - r * (r + 1) / 2;
+            if (g.tri == 1) { tm = r; tn = c; } else { tm = c; tn = r; }
+        } else {
+            tm = lid / nx;
+            tn = lid % nx;
+        }
+    }
+    const int64_t m0 = tm * GBM, n0 = tn * GBN;
+    if (tm == g.skip_tile || tn == g.skip_tile) return;
     const int64_t z = blockIdx.z, z1 = z / g.nb2, z2 = z % g.nb2;
     const T* __restrict__ A = g.A + z1 * g.sA1 + z2 * g.sA2;
     const T* __restrict__ B = g.B + z1 * g.sB1 + z2 * g.sB2;
@@ -85,18 +108,18 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs<T> g) {
         for (int j = 0; j < 4; j++) acc[i][j] = typename Mfma<T>::acc_t{0, 0, 0, 0};
 
     const int wm = wave >> 1, wn = wave & 1;
-    T ra[2][VN], rb[2][VN];
+    T ra[NV][VN], rb[NV][VN];
     const bool fullMN = (m0 + GBM <= M) && (n0 + GBN <= N);
 
     auto gload = [&](int64_t k0) {
         const bool full = VEC && fullMN && (k0 + BK <= ke);
 #pragma unroll
-        for (int q = 0; q < 2; q++) {
+        for (int q = 0; q < NV; q++) {
             const int v = tid + 256 * q;
             // ---- A
             {
                 int64_t gm, gk;
-                if (!TA) { gm = m0 + (v >> 2); gk = k0 + (v & 3) * VN; }
+                if (!TA) { gm = m0 + v / VPR; gk = k0 + (v % VPR) * VN; }
                 else { gk = k0 + v / (GBM / VN); gm = m0 + (v % (GBM / VN)) * VN; }
                 const T* p = TA ? A + gk * g.lda + gm : A + gm * g.lda + gk;
                 if (full) {
@@ -114,7 +137,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs<T> g) {
             // ---- B
             {
                 int64_t gn, gk;
-                if (TB) { gn = n0 + (v >> 2); gk = k0 + (v & 3) * VN; }
+                if (TB) { gn = n0 + v / VPR; gk = k0 + (v % VPR) * VN; }
                 else { gk = k0 + v / (GBN / VN); gn = n0 + (v % (GBN / VN)) * VN; }
                 const T* p = TB ? B + gn * g.ldb + gk : B + gk * g.ldb + gn;
                 if (full) {
@@ -133,18 +156,18 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs<T> g) {
     };
     auto sstore = [&](int buf) {
 #pragma unroll
-        for (int q = 0; q < 2; q++) {
+        for (int q = 0; q < NV; q++) {
             const int v = tid + 256 * q;
             if (!TA) {
 #pragma unroll
-                for (int e = 0; e < VN; e++) As[buf][(v & 3) * VN + e][v >> 2] = ra[q][e];
+                for (int e = 0; e < VN; e++) As[buf][(v % VPR) * VN + e][v / VPR] = ra[q][e];
             } else {
 #pragma unroll
                 for (int e = 0; e < VN; e++) As[buf][v / (GBM / VN)][(v % (GBM / VN)) * VN + e] = ra[q][e];
             }
             if (TB) {
 #pragma unroll
-                for (int e = 0; e < VN; e++) Bs[buf][(v & 3) * VN + e][v >> 2] = rb[q][e];
+                for (int e = 0; e < VN; e++) Bs[buf][(v % VPR) * VN + e][v / VPR] = rb[q][e];
             } else {
 #pragma unroll
                 for (int e = 0; e < VN; e++) Bs[buf][v / (GBN / VN)][(v % (GBN / VN)) * VN + e] = rb[q][e];
@@ -220,7 +243,9 @@ kq_status gemm(const GemmArgs<T>& g, bool ta, bool tb, hipStream_t st) {
     constexpr int VN = 16 / sizeof(T);
     const bool vec = aligned16(g.A) && aligned16(g.B) && g.lda % VN == 0 && g.ldb % VN == 0 &&
                      g.sA1 % VN == 0 && g.sA2 % VN == 0 && g.sB1 % VN == 0 && g.sB2 % VN == 0;
-    dim3 grid((unsigned)((g.N + GBN - 1) / GBN), (unsigned)((g.M + GBM - 1) / GBM), (unsigned)(g.nb1 * g.nb2));
+    const int64_t nx = (g.N + GBN - 1) / GBN, ny = (g.M + GBM - 1) / GBM;
+    if (g.tri && nx != ny) return fail(KQ_ESHAPE, "gemm: triangular products need a square tile grid");
+    dim3 grid((unsigned)(g.tri ? nx * (nx + 1) / 2 : nx), (unsigned)(g.tri ? 1 : ny), (unsigned)(g.nb1 * g.nb2));
     if (grid.y > 65535 || grid.z > 65535) return fail(KQ_ESHAPE, "gemm grid too large");
 #define KQ_GEMM_LAUNCH(TA_, TB_, V_) hipLaunchKernelGGL((gemm_kernel<T, TA_, TB_, V_>), grid, dim3(256), 0, st, g)
     if (vec) {

@@ -52,8 +52,8 @@ struct Sizer {
 // C = alpha * op(A) op(B) [* rowsign[m]] [* colsign[n]] + beta * C on MFMA, row-major operands.
 // op(A) is M x K (A stored M x K, or K x M when ta), op(B) is K x N (B stored K x N, or N x K when
 // tb). Two batch levels: z = z1 * nb2 + z2, operand offset z1 * s?1 + z2 * s?2.
-// tri: 0 full, 1 store only m >= n (lower), 2 store only m <= n (upper); tiles entirely outside
-// the stored triangle are skipped. kmode restricts the K range per tile to skip structural zeros
+// tri: 0 full, 1 store only m >= n (lower), 2 store only m <= n (upper); only tiles touching the
+// stored triangle are launched (M and N must give the same tile count). kmode restricts the K range per tile to skip structural zeros
 // of triangular operands: bit0 k >= m0, bit1 k >= n0, bit2 k < m0 + 128, bit3 k < n0 + 128.
 template <typename T>
 struct GemmArgs {
