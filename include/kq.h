@@ -183,6 +183,19 @@ kq_status kq_unrotate(const float* Q, int64_t o, int64_t i, int64_t ldq, const i
 kq_status kq_layer_loss(const float* W2, const float* Q, int64_t o, int64_t i, int64_t ldw, const float* HX2,
                         int64_t ldh, double* row_loss, double* loss, void* ws, size_t ws_bytes, kq_stream stream);
 
+/*
+ * Sublayer mixed-precision bit allocation (review page, Method (2) and Comparison: the joint score
+ * tr(H_G) tr(H_X) orders sublayer upgrades). HOST pointers; runs on the calling thread.
+ * Every sublayer starts at bmin bits; repeatedly the single upgrade b -> b + 1 (b < bmax) with the
+ * largest scores[l] * (c(b) - c(b + 1)) / sizes[l], c(b) = (2^b - 1)^-2, that keeps
+ * sum_l sizes[l] * bits[l] <= budget * sum_l sizes[l] is applied; ties go to the lower index.
+ * c(b) is the expected squared rounding error per unit squared range of a b-bit grid (uniform
+ * rounding errors of step d have variance d^2 / 12; the range is (2^b - 1) d).
+ * scores: count doubles (>= 0); sizes: count weights per sublayer (> 0); bits: count int32 out.
+ */
+kq_status kq_allocate_bits(const double* scores, const int64_t* sizes, int64_t count, double budget, int bmin,
+                           int bmax, int32_t* bits);
+
 /* Text of a status code; thread-local detail of the last error on this host thread. */
 const char* kq_strerror(kq_status status);
 const char* kq_last_error(void);

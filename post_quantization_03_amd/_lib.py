@@ -16,7 +16,7 @@ OP = {"hessian": 0, "rotate_in": 1, "hg_sqrt": 2, "rotate_out": 3, "cholinv": 4,
       "loss": 7}
 EXPORTS = ("kq_workspace_bytes", "kq_hessian_accum", "kq_rotate_in", "kq_hg_sqrt", "kq_rotate_out", "kq_cholinv",
            "kq_quantize_layer", "kq_sensitivity", "kq_unrotate", "kq_layer_loss", "kq_strerror", "kq_last_error",
-           "kq_hadamard_order", "kq_version")
+           "kq_hadamard_order", "kq_version", "kq_allocate_bits")
 
 
 class KQError(RuntimeError):
@@ -52,6 +52,8 @@ def lib() -> ctypes.CDLL:
         "kq_last_error": (ctypes.c_char_p, []),
         "kq_hadamard_order": (_i64, [_i64, ctypes.POINTER(_i64)]),
         "kq_version": (_int, []),
+        "kq_allocate_bits": (_int, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_i64), _i64, ctypes.c_double, _int,
+                                    _int, ctypes.POINTER(ctypes.c_int32)]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -122,6 +124,14 @@ def kq_rotate_in(Win, Wout, HX, sign_in, ws=None, stream=None) -> None:
                                               _p(HX), _p(sign_in), w, wb, _stream(stream)))
 
 
+def kq_rotate_in_hessian(HX, sign_in, ws=None, stream=None) -> None:
+    """kq_rotate_in with no weights: HX <- U^T HX U."""
+    i = HX.shape[0]
+    w, wb = _ws(ws)
+    _check("kq_rotate_in", lib().kq_rotate_in(None, KQ_F32, i, None, i, 0, i, _p(HX), _p(sign_in), w, wb,
+                                              _stream(stream)))
+
+
 def kq_hg_sqrt(HG, form: str, o: int, blk: int, S, Sinv, info, ws=None, stream=None) -> None:
     w, wb = _ws(ws)
     _check("kq_hg_sqrt", lib().kq_hg_sqrt(_p(HG), HG_FORM[form], o, blk, _p(S), _p(Sinv), _p(info), w, wb,
@@ -168,3 +178,15 @@ def kq_layer_loss(W2, Q, HX2, row_loss, loss, ws=None, stream=None) -> None:
     w, wb = _ws(ws)
     _check("kq_layer_loss", lib().kq_layer_loss(_p(W2), _p(Q), o, i, W2.stride(0), _p(HX2), HX2.stride(0),
                                                 _p(row_loss), _p(loss), w, wb, _stream(stream)))
+
+
+def kq_allocate_bits(scores, sizes, budget: float = 3.0, bmin: int = 2, bmax: int = 4):
+    """Host call: bit-width per sublayer from the sensitivity scores (see include/kq.h)."""
+    import numpy as np
+    sc = np.ascontiguousarray(scores, dtype=np.float64)
+    sz = np.ascontiguousarray(sizes, dtype=np.int64)
+    out = np.zeros(len(sc), dtype=np.int32)
+    _check("kq_allocate_bits", lib().kq_allocate_bits(sc.ctypes.data_as(ctypes.POINTER(ctypes.c_double)),
+                                                      sz.ctypes.data_as(ctypes.POINTER(_i64)), len(sc), budget, bmin,
+                                                      bmax, out.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))))
+    return out

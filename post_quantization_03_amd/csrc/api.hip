@@ -1,6 +1,8 @@
 // Error reporting, workspace sizing and version of the C ABI.
+#include <cmath>
 #include <cstdarg>
 #include <cstring>
+#include <vector>
 
 #include "kq_internal.h"
 
@@ -72,4 +74,31 @@ extern "C" size_t kq_workspace_bytes(kq_op op, int64_t o, int64_t i, int64_t n, 
         case KQ_OP_LOSS: return loss_ws(o, i);
     }
     return 0;
+}
+
+extern "C" kq_status kq_allocate_bits(const double* scores, const int64_t* sizes, int64_t count, double budget,
+                                      int bmin, int bmax, int32_t* bits) {
+    if (!scores || !sizes || !bits) return kq::fail(KQ_EINVAL, "kq_allocate_bits: null pointer");
+    if (count <= 0 || bmin < 1 || bmax < bmin || bmax > 16) return kq::fail(KQ_EINVAL, "kq_allocate_bits: bad arguments");
+    double total = 0.0;
+    for (int64_t l = 0; l < count; l++) {
+        if (!(sizes[l] > 0) || !(scores[l] >= 0.0)) return kq::fail(KQ_EINVAL, "kq_allocate_bits: bad size or score");
+        total += (double)sizes[l];
+        bits[l] = bmin;
+    }
+    auto unit = [](int b) { const double r = std::ldexp(1.0, b) - 1.0; return 1.0 / (r * r); };
+    const double cap = budget * total;
+    double used = (double)bmin * total;
+    for (;;) {
+        int64_t best = -1;
+        double best_gain = -1.0;
+        for (int64_t l = 0; l < count; l++) {
+            if (bits[l] >= bmax || used + (double)sizes[l] > cap) continue;
+            const double gain = scores[l] * (unit(bits[l]) - unit(bits[l] + 1)) / (double)sizes[l];
+            if (gain > best_gain) { best = l; best_gain = gain; }
+        }
+        if (best < 0) return KQ_OK;
+        bits[best] += 1;
+        used += (double)sizes[best];
+    }
 }

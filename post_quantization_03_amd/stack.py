@@ -1,0 +1,128 @@
+"""Mixed-precision quantization of a stack of layers through the C ABI (include/kq.h).
+
+KronQ review page, Method (2) and Comparison: every sublayer is scored with tr(H_G) tr(H_X), the
+scores order sublayer bit upgrades under an average budget, then every sublayer is quantized with the
+unchanged per-layer solver.
+
+Pass 1 (per layer): H_X for each distinct input (kq_hessian_accum), the score of every sublayer that
+reads it (kq_sensitivity). Host: kq_allocate_bits over all scores.
+Pass 2 (per layer): per distinct input one rotation of H_X and one damped factor R (kq_rotate_in with
+no weights, kq_cholinv): sublayers that read the same input share U and R. Per sublayer: kq_rotate_in
+(weights), kq_hg_sqrt, kq_rotate_out, kq_quantize_layer at its bit-width.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import torch
+
+from . import _lib as K
+
+
+@dataclass
+class Sublayer:
+    W: torch.Tensor          # o x i, bf16 or fp32
+    HG: torch.Tensor         # diagonal H_G (o)
+    t: torch.Tensor          # output-side signs (o)
+    x: int                   # index of the input it reads
+
+
+@dataclass
+class Layer:
+    X: list                  # calibration activations per distinct input (n x i)
+    s: list                  # input-side signs per distinct input
+    subs: list               # Sublayer
+
+
+@dataclass
+class StackOut:
+    scores: torch.Tensor
+    bits: list
+    codes: list = field(default_factory=list)
+    scale: list = field(default_factory=list)
+    offset: list = field(default_factory=list)
+    row_loss: list = field(default_factory=list)
+    Q: list = field(default_factory=list)
+    R: list = field(default_factory=list)
+    H: list = field(default_factory=list)
+
+
+def _ws_bytes(layers, group: int) -> int:
+    need = 256
+    for L in layers:
+        for x, X in enumerate(L.X):
+            n, i = X.shape
+            need = max(need, K.kq_workspace_bytes("hessian", 0, i, n), K.kq_workspace_bytes("rotate_in", 0, i),
+                       K.kq_workspace_bytes("cholinv", 0, i))
+        for sl in L.subs:
+            o, i = sl.W.shape
+            need = max(need, K.kq_workspace_bytes("rotate_in", o, i), K.kq_workspace_bytes("rotate_out", o, i),
+                       K.kq_workspace_bytes("quantize", o, i))
+    return need
+
+
+def quantize_stack(layers: list, budget: float = 3.0, group: int = 128, damp: float = 0.01, keep_q: bool = False,
+                   keep_h: bool = False, ws: torch.Tensor | None = None, H_cache: list | None = None) -> StackOut:
+    dev = layers[0].X[0].device
+    if ws is None:
+        ws = torch.empty(_ws_bytes(layers, group), dtype=torch.uint8, device=dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    nsub = sum(len(L.subs) for L in layers)
+    scores = torch.empty(nsub, dtype=torch.float64, device=dev)
+    # ---- pass 1: H_X per distinct input, scores
+    Hs = []
+    k = 0
+    for li, L in enumerate(layers):
+        hl = []
+        for x, X in enumerate(L.X):
+            n, i = X.shape
+            H = H_cache[li][x] if H_cache is not None else torch.empty((i, i), **f32)
+            K.kq_hessian_accum(X, H, 1.0 / n, 0.0, ws)
+            hl.append(H)
+        for sl in L.subs:
+            o = sl.W.shape[0]
+            K.kq_sensitivity(hl[sl.x], sl.HG, "diag", o, 0, scores[k:k + 1])
+            k += 1
+        Hs.append(hl)
+    sizes = [sl.W.shape[0] * sl.W.shape[1] for L in layers for sl in L.subs]
+    bits = K.kq_allocate_bits(scores.cpu().numpy(), sizes, budget, 2, 4).tolist()
+    out = StackOut(scores=scores, bits=bits)
+    # ---- pass 2
+    # info[layer, input] from the damped factors, info[layer, 8 + sublayer] from the H_G roots
+    info = torch.zeros((len(layers), 16), dtype=torch.int32, device=dev)
+    k = 0
+    for li, L in enumerate(layers):
+        Rs = []
+        for x, H in enumerate(Hs[li]):
+            i = H.shape[0]
+            K.kq_rotate_in_hessian(H, L.s[x], ws)
+            R = torch.empty((i, i), **f32)
+            K.kq_cholinv(H, damp, R, info[li, x:x + 1], ws)
+            Rs.append(R)
+        for j, sl in enumerate(L.subs):
+            o, i = sl.W.shape
+            b = bits[k]
+            W2 = torch.empty((o, i), **f32)
+            K.kq_rotate_in(sl.W, W2, None, L.s[sl.x], ws)
+            S = torch.empty((o,), **f32)
+            K.kq_hg_sqrt(sl.HG, "diag", o, 0, S, None, info[li, 8 + j:9 + j], ws)
+            K.kq_rotate_out(W2, S, "diag", 0, sl.t, ws)
+            ng = i // group if group else 1
+            codes = torch.empty((o, i * b // 32), dtype=torch.int32, device=dev)
+            scale = torch.empty((o, ng), **f32)
+            offset = torch.empty((o, ng), **f32)
+            rl = torch.empty((o,), **f32)
+            K.kq_quantize_layer(W2, Rs[sl.x], b, group, 128, codes, scale, offset, rl, ws)
+            out.codes.append(codes)
+            out.scale.append(scale)
+            out.offset.append(offset)
+            out.row_loss.append(rl)
+            if keep_q:
+                out.Q.append(W2)
+            k += 1
+        if keep_h:
+            out.H.append(Hs[li])
+            out.R.append(Rs)
+    out.info = info
+    return out
+
