@@ -103,7 +103,7 @@ def phase_times(sp, X, W, HG, s, t, cfg, ws, reps: int = 3) -> dict:
     dev = X.device
     o, i, n = sp.o, sp.i, sp.n
     f32 = dict(dtype=torch.float32, device=dev)
-    H = torch.empty((i, i), **f32)
+    H = torch.empty((i, i), dtype=torch.float64, device=dev)
     W2 = torch.empty((o, i), **f32)
     S = torch.empty(hg_factor_shape(o, cfg), **f32)
     R = torch.empty((i, i), **f32)

@@ -77,14 +77,16 @@ size_t kq_workspace_bytes(kq_op op, int64_t o, int64_t i, int64_t n, kq_dtype xd
  * H_X accumulation (review page, Background: the input activation covariance H_X as the
  * layer-Hessian proxy; Prior limitations: GPTQ's OBS update uses H_X only).
  *     H <- beta * H + alpha * X^T X
- * X: n x d, row-major, leading dimension ldx, fp32 or bf16 (xdt). H: d x d fp32, leading
+ * X: n x d, row-major, leading dimension ldx, fp32 or bf16 (xdt). H: d x d fp64, leading
  * dimension d, written in full (both triangles, exactly symmetric). With alpha = 1/n_total and
  * beta = 0 for the first token batch and 1 for later ones, H becomes X^T X / n_total over all
- * batches. bf16 inputs are multiplied exactly (bf16 x bf16 products are exact in fp32) and
- * accumulated in fp32. n = 0 only scales H by beta.
+ * batches. bf16 inputs are multiplied exactly on the bf16 matrix cores; each instruction's
+ * 32-product fp32 sum is accumulated in fp64. H stays fp64 through the rotation and the damped
+ * factor because R moves with H as cond(H) makes it: rounding H to fp32 alone would shift the
+ * sweep's pre-rounding values by up to ~2e-4 grid steps on 4096-wide layers. n = 0 only scales H.
  */
-kq_status kq_hessian_accum(const void* X, kq_dtype xdt, int64_t n, int64_t d, int64_t ldx, float alpha,
-                           float beta, float* H, void* ws, size_t ws_bytes, kq_stream stream);
+kq_status kq_hessian_accum(const void* X, kq_dtype xdt, int64_t n, int64_t d, int64_t ldx, double alpha,
+                           double beta, double* H, void* ws, size_t ws_bytes, kq_stream stream);
 
 /*
  * Input-side incoherence rotation (review page, "Where this paper sits": the QuIP / QuIP#
@@ -95,10 +97,11 @@ kq_status kq_hessian_accum(const void* X, kq_dtype xdt, int64_t n, int64_t d, in
  * q = 3 mod 4), m the smallest such order dividing i; KQ_EUNSUPPORTED if none exists.
  * Win: o x i, fp32 or bf16 (wdt), leading dimension ldwin. Wout: o x i fp32, leading dimension
  * ldw; Wout may equal Win when wdt = KQ_F32 and ldw = ldwin. sign_in: i int8 values +-1.
- * HX: i x i fp32, leading dimension i, transformed in place.
+ * HX: i x i fp64, leading dimension i, transformed in place (fp64 arithmetic). o = 0 rotates
+ * only HX (Win, Wout may then be NULL).
  */
 kq_status kq_rotate_in(const void* Win, kq_dtype wdt, int64_t ldwin, float* Wout, int64_t ldw, int64_t o,
-                       int64_t i, float* HX, const int8_t* sign_in, void* ws, size_t ws_bytes, kq_stream stream);
+                       int64_t i, double* HX, const int8_t* sign_in, void* ws, size_t ws_bytes, kq_stream stream);
 
 /*
  * Output-side factor S = H_G^{1/2}, the principal (symmetric positive definite) square root, and
@@ -128,12 +131,12 @@ kq_status kq_rotate_out(float* W, int64_t o, int64_t i, int64_t ldw, const float
  * computed without forming H^{-1}: with J the reversal permutation, J H J = L L^T (Cholesky) and
  * R = J L^{-1} J. The factorisation and the triangular inverse run in fp64 (MFMA); R is rounded to
  * fp32, so its error is that rounding rather than sqrt(cond(H)) fp32 steps.
- * HX: i x i fp32 (only its lower triangle is read), leading dimension ldh.
+ * HX: i x i fp64 (only its lower triangle is read), leading dimension ldh.
  * R: i x i fp32, leading dimension i, upper triangle written, strict lower triangle zeroed.
  * info (device int32): 0, or k > 0 if H is not positive definite (k = 1 + index, counted from the
  * last row, of the first failing pivot). No automatic re-damping.
  */
-kq_status kq_cholinv(const float* HX, int64_t i, int64_t ldh, float damp, float* R, int32_t* info, void* ws,
+kq_status kq_cholinv(const double* HX, int64_t i, int64_t ldh, double damp, float* R, int32_t* info, void* ws,
                      size_t ws_bytes, kq_stream stream);
 
 /*
@@ -157,11 +160,11 @@ kq_status kq_quantize_layer(float* W, int64_t o, int64_t i, int64_t ldw, const f
                             void* ws, size_t ws_bytes, kq_stream stream);
 
 /*
- * Sublayer sensitivity tr(H_G) * tr(H_X), both undamped (review page, Method (2)). HX: i x i fp32,
+ * Sublayer sensitivity tr(H_G) * tr(H_X), both undamped (review page, Method (2)). HX: i x i fp64,
  * leading dimension ldh (a rotated H_X gives the same trace up to rounding). HG in its storage
  * form. score: one device double.
  */
-kq_status kq_sensitivity(const float* HX, int64_t i, int64_t ldh, const float* HG, kq_hg_form form, int64_t o,
+kq_status kq_sensitivity(const double* HX, int64_t i, int64_t ldh, const float* HG, kq_hg_form form, int64_t o,
                          int64_t blk, double* score, kq_stream stream);
 
 /*
@@ -177,10 +180,10 @@ kq_status kq_unrotate(const float* Q, int64_t o, int64_t i, int64_t ldq, const i
 /*
  * Verification: layer loss in rotated coordinates, sum_r (Q - W2)_r HX2 (Q - W2)_r^T, which equals
  * tr(H_G dW H_X dW^T) in the original coordinates when HX2 is the rotated, undamped H_X.
- * W2, Q: o x i fp32 (leading dimension ldw); HX2: i x i fp32 (leading dimension ldh).
+ * W2, Q: o x i fp32 (leading dimension ldw); HX2: i x i fp64 (leading dimension ldh).
  * row_loss (may be NULL): o doubles; loss: one device double.
  */
-kq_status kq_layer_loss(const float* W2, const float* Q, int64_t o, int64_t i, int64_t ldw, const float* HX2,
+kq_status kq_layer_loss(const float* W2, const float* Q, int64_t o, int64_t i, int64_t ldw, const double* HX2,
                         int64_t ldh, double* row_loss, double* loss, void* ws, size_t ws_bytes, kq_stream stream);
 
 /*

@@ -38,11 +38,11 @@ def lib() -> ctypes.CDLL:
     L = ctypes.CDLL(LIB_PATH)
     sig = {
         "kq_workspace_bytes": (_sz, [_int, _i64, _i64, _i64, _int, _int, _int, _int, _i64]),
-        "kq_hessian_accum": (_int, [_vp, _int, _i64, _i64, _i64, _f32, _f32, _vp, _vp, _sz, _vp]),
+        "kq_hessian_accum": (_int, [_vp, _int, _i64, _i64, _i64, ctypes.c_double, ctypes.c_double, _vp, _vp, _sz, _vp]),
         "kq_rotate_in": (_int, [_vp, _int, _i64, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _sz, _vp]),
         "kq_hg_sqrt": (_int, [_vp, _int, _i64, _i64, _vp, _vp, _vp, _vp, _sz, _vp]),
         "kq_rotate_out": (_int, [_vp, _i64, _i64, _i64, _vp, _int, _i64, _vp, _vp, _sz, _vp]),
-        "kq_cholinv": (_int, [_vp, _i64, _i64, _f32, _vp, _vp, _vp, _sz, _vp]),
+        "kq_cholinv": (_int, [_vp, _i64, _i64, ctypes.c_double, _vp, _vp, _vp, _sz, _vp]),
         "kq_quantize_layer": (_int, [_vp, _i64, _i64, _i64, _vp, _i64, _int, _int, _int, _vp, _vp, _vp, _vp, _vp, _sz,
                                      _vp]),
         "kq_sensitivity": (_int, [_vp, _i64, _i64, _vp, _int, _i64, _i64, _vp, _vp]),

@@ -536,10 +536,10 @@ using namespace kq;
 
 // ==================================================================================== kq_cholinv
 // lambda = damp * mean(diag H) in fp64 with a fixed reduction order (one work-group).
-__global__ void damp_kernel(const float* H, int64_t n, int64_t ldh, float damp, float* lam, int32_t* info) {
+__global__ void damp_kernel(const double* H, int64_t n, int64_t ldh, double damp, double* lam, int32_t* info) {
     __shared__ double part[256];
     double s = 0;
-    for (int64_t r = threadIdx.x; r < n; r += 256) s += (double)H[r * ldh + r];
+    for (int64_t r = threadIdx.x; r < n; r += 256) s += H[r * ldh + r];
     part[threadIdx.x] = s;
     __syncthreads();
     for (int w = 128; w > 0; w >>= 1) {
@@ -547,18 +547,18 @@ __global__ void damp_kernel(const float* H, int64_t n, int64_t ldh, float damp, 
         __syncthreads();
     }
     if (threadIdx.x == 0) {
-        *lam = (float)((double)damp * part[0] / (double)n);
+        *lam = damp * part[0] / (double)n;
         *info = 0;
     }
 }
 
 // Hr[a][b] = H[n-1-a][n-1-b] + lambda [a == b] in fp64, lower triangle only (read from H's lower
 // triangle).
-__global__ void reverse_damped_kernel(const float* H, int64_t n, int64_t ldh, const float* lam, double* Hr) {
+__global__ void reverse_damped_kernel(const double* H, int64_t n, int64_t ldh, const double* lam, double* Hr) {
     const int64_t a = blockIdx.y;
     for (int64_t b = blockIdx.x * 256 + threadIdx.x; b <= a && b < n; b += (int64_t)gridDim.x * 256) {
-        double v = (double)H[(n - 1 - b) * ldh + (n - 1 - a)];
-        if (a == b) v += (double)*lam;
+        double v = H[(n - 1 - b) * ldh + (n - 1 - a)];
+        if (a == b) v += *lam;
         Hr[a * n + b] = v;
     }
 }
@@ -571,7 +571,7 @@ __global__ void reverse_upper_kernel(const double* X, int64_t n, float* R) {
 }
 
 static void cholinv_layout(Sizer& z, int64_t n) {
-    z.take<float>(1);
+    z.take<double>(1);
     z.take<double>((size_t)n * n);
     z.take<double>((size_t)n * n);
     z.take<double>((size_t)(n * n / 2 + 64 * 64));
@@ -583,15 +583,15 @@ size_t cholinv_ws(int64_t n) {
     return z.used;
 }
 
-extern "C" kq_status kq_cholinv(const float* HX, int64_t n, int64_t ldh, float damp, float* R, int32_t* info, void* ws,
-                                size_t ws_bytes, kq_stream stream) {
+extern "C" kq_status kq_cholinv(const double* HX, int64_t n, int64_t ldh, double damp, float* R, int32_t* info,
+                                void* ws, size_t ws_bytes, kq_stream stream) {
     if (!HX || !R || !info) return fail(KQ_EINVAL, "kq_cholinv: null pointer");
     if (n <= 0 || ldh < n) return fail(KQ_ESHAPE, "kq_cholinv: bad size n=%lld ldh=%lld", (long long)n, (long long)ldh);
-    if (!(damp >= 0.0f)) return fail(KQ_EINVAL, "kq_cholinv: damp must be >= 0");
+    if (!(damp >= 0.0)) return fail(KQ_EINVAL, "kq_cholinv: damp must be >= 0");
     if (ws_bytes < cholinv_ws(n) || !ws) return fail(KQ_EWORKSPACE, "kq_cholinv: workspace too small");
     hipStream_t st = hs(stream);
     Arena ar(ws, ws_bytes);
-    float* lam = ar.take<float>(1);
+    double* lam = ar.take<double>(1);
     double* Hr = ar.take<double>((size_t)n * n);
     double* X = ar.take<double>((size_t)n * n);
     double* Tscr = ar.take<double>((size_t)(n * n / 2 + 64 * 64));

@@ -101,7 +101,8 @@ __device__ inline int gf_sub(int a, int b, Field f) {
 }
 
 // P = I + [[0, 1^T], [-1, Q]] with Q_ab = chi(a - b); writes P (or P^T) as an m x m fp32 matrix.
-__global__ void paley_kernel(float* P, int m, Field f, int transpose) {
+template <typename T>
+__global__ void paley_kernel(T* P, int m, Field f, int transpose) {
     for (int e = blockIdx.x * 256 + threadIdx.x; e < m * m; e += gridDim.x * 256) {
         int a = e / m, b = e % m;
         if (transpose) { int t = a; a = b; b = t; }
@@ -109,36 +110,39 @@ __global__ void paley_kernel(float* P, int m, Field f, int transpose) {
         if (a == 0) v = (b == 0) ? 1 : 1;
         else if (b == 0) v = -1;
         else v = gf_chi(gf_sub(a - 1, b - 1, f), f) + (a == b ? 1 : 0);
-        P[e] = (float)v;
+        P[e] = (T)v;
     }
 }
 
 // ------------------------------------------------------------------------------ row transform
-template <bool BF16>
-__global__ __launch_bounds__(256) void fwht_rows_kernel(const void* __restrict__ in, int64_t ldin,
-                                                        float* __restrict__ out, int64_t ldout, int64_t d, int lp2,
-                                                        const int8_t* __restrict__ pre, const int8_t* __restrict__ post,
-                                                        float scale) {
-    extern __shared__ __align__(16) float xr[];
+// IN: 0 = bf16 bits, 1 = fp32, 2 = fp64. T: arithmetic and output type (fp32 or fp64).
+template <int IN, typename T>
+__global__ __launch_bounds__(256) void fwht_rows_kernel(const void* __restrict__ in, int64_t ldin, T* __restrict__ out,
+                                                        int64_t ldout, int64_t d, int lp2, const int8_t* __restrict__ pre,
+                                                        const int8_t* __restrict__ post, T scale) {
+    extern __shared__ __align__(16) unsigned char xr_raw[];
+    T* xr = reinterpret_cast<T*>(xr_raw);
     const int64_t r = blockIdx.x;
     const int tid = threadIdx.x;
-    if (BF16) {
-        const uint16_t* src = static_cast<const uint16_t*>(in) + r * ldin;
-        for (int64_t c = 4 * tid; c < d; c += 1024) {
-            const uint2 u = *reinterpret_cast<const uint2*>(src + c);
-            float v[4] = {__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xFFFF0000u), __uint_as_float(u.y << 16),
-                          __uint_as_float(u.y & 0xFFFF0000u)};
-#pragma unroll
-            for (int e = 0; e < 4; e++) xr[c + e] = pre ? v[e] * (float)pre[c + e] : v[e];
+    for (int64_t c = 4 * tid; c < d; c += 1024) {
+        T v[4];
+        if (IN == 0) {
+            const uint2 u = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(in) + r * ldin + c);
+            v[0] = (T)__uint_as_float(u.x << 16);
+            v[1] = (T)__uint_as_float(u.x & 0xFFFF0000u);
+            v[2] = (T)__uint_as_float(u.y << 16);
+            v[3] = (T)__uint_as_float(u.y & 0xFFFF0000u);
+        } else if (IN == 1) {
+            const float4 u = *reinterpret_cast<const float4*>(static_cast<const float*>(in) + r * ldin + c);
+            v[0] = (T)u.x; v[1] = (T)u.y; v[2] = (T)u.z; v[3] = (T)u.w;
+        } else {
+            const double* src = static_cast<const double*>(in) + r * ldin + c;
+            const double2 u0 = *reinterpret_cast<const double2*>(src);
+            const double2 u1 = *reinterpret_cast<const double2*>(src + 2);
+            v[0] = (T)u0.x; v[1] = (T)u0.y; v[2] = (T)u1.x; v[3] = (T)u1.y;
         }
-    } else {
-        const float* src = static_cast<const float*>(in) + r * ldin;
-        for (int64_t c = 4 * tid; c < d; c += 1024) {
-            const float4 u = *reinterpret_cast<const float4*>(src + c);
-            float v[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
-            for (int e = 0; e < 4; e++) xr[c + e] = pre ? v[e] * (float)pre[c + e] : v[e];
-        }
+        for (int e = 0; e < 4; e++) xr[c + e] = pre ? v[e] * (T)pre[c + e] : v[e];
     }
     __syncthreads();
     const int64_t p2 = int64_t(1) << lp2;
@@ -148,8 +152,8 @@ __global__ __launch_bounds__(256) void fwht_rows_kernel(const void* __restrict__
         if (2 * h < p2) {
             for (int64_t g = tid; g < d / 4; g += 256) {
                 const int64_t j = ((g >> lh) << (lh + 2)) + (g & (h - 1));
-                const float a0 = xr[j], a1 = xr[j + h], a2 = xr[j + 2 * h], a3 = xr[j + 3 * h];
-                const float b0 = a0 + a1, b1 = a0 - a1, b2 = a2 + a3, b3 = a2 - a3;
+                const T a0 = xr[j], a1 = xr[j + h], a2 = xr[j + 2 * h], a3 = xr[j + 3 * h];
+                const T b0 = a0 + a1, b1 = a0 - a1, b2 = a2 + a3, b3 = a2 - a3;
                 xr[j] = b0 + b2;
                 xr[j + h] = b1 + b3;
                 xr[j + 2 * h] = b0 - b2;
@@ -159,7 +163,7 @@ __global__ __launch_bounds__(256) void fwht_rows_kernel(const void* __restrict__
         } else {
             for (int64_t g = tid; g < d / 2; g += 256) {
                 const int64_t j = ((g >> lh) << (lh + 1)) + (g & (h - 1));
-                const float a0 = xr[j], a1 = xr[j + h];
+                const T a0 = xr[j], a1 = xr[j + h];
                 xr[j] = a0 + a1;
                 xr[j + h] = a0 - a1;
             }
@@ -167,24 +171,24 @@ __global__ __launch_bounds__(256) void fwht_rows_kernel(const void* __restrict__
         }
         __syncthreads();
     }
-    float* dst = out + r * ldout;
+    T* dst = out + r * ldout;
     for (int64_t c = 4 * tid; c < d; c += 1024) {
-        float v[4];
 #pragma unroll
-        for (int e = 0; e < 4; e++) v[e] = post ? xr[c + e] * scale * (float)post[c + e] : xr[c + e] * scale;
-        *reinterpret_cast<float4*>(dst + c) = make_float4(v[0], v[1], v[2], v[3]);
+        for (int e = 0; e < 4; e++) dst[c + e] = post ? xr[c + e] * scale * (T)post[c + e] : xr[c + e] * scale;
     }
 }
 
 // --------------------------------------------------------------------------- column digit pass
 // Rows r = (hi * D + t) * S + lo, t = 0..D-1, transformed along t for 64 columns per work-group.
-__global__ __launch_bounds__(256) void fwht_cols_kernel(const float* __restrict__ in, int64_t ldin,
-                                                        float* __restrict__ out, int64_t ldout, int64_t ncols, int lD,
-                                                        int64_t S, const float* __restrict__ pre_scale,
+template <typename T>
+__global__ __launch_bounds__(256) void fwht_cols_kernel(const T* __restrict__ in, int64_t ldin, T* __restrict__ out,
+                                                        int64_t ldout, int64_t ncols, int lD, int64_t S,
+                                                        const float* __restrict__ pre_scale,
                                                         const int8_t* __restrict__ pre_sign,
                                                         const float* __restrict__ post_scale,
-                                                        const int8_t* __restrict__ post_sign, float scale) {
-    extern __shared__ __align__(16) float xc[];
+                                                        const int8_t* __restrict__ post_sign, T scale) {
+    extern __shared__ __align__(16) unsigned char xc_raw[];
+    T* xc = reinterpret_cast<T*>(xc_raw);
     const int D = 1 << lD;
     const int tid = threadIdx.x;
     const int64_t c0 = (int64_t)blockIdx.x * 64, lo = blockIdx.y, hi = blockIdx.z;
@@ -192,9 +196,9 @@ __global__ __launch_bounds__(256) void fwht_cols_kernel(const float* __restrict_
     const bool cin = c0 + c < ncols;
     for (int t = tid >> 6; t < D; t += 4) {
         const int64_t r = (hi * D + t) * S + lo;
-        float v = cin ? in[r * ldin + c0 + c] : 0.0f;
-        if (pre_scale) v *= pre_scale[r];
-        if (pre_sign) v *= (float)pre_sign[r];
+        T v = cin ? in[r * ldin + c0 + c] : T(0);
+        if (pre_scale) v *= (T)pre_scale[r];
+        if (pre_sign) v *= (T)pre_sign[r];
         xc[t * 64 + c] = v;
     }
     __syncthreads();
@@ -204,9 +208,9 @@ __global__ __launch_bounds__(256) void fwht_cols_kernel(const float* __restrict_
         if (lh + 1 < lD) {
             for (int g = tid >> 6; g < D / 4; g += 4) {
                 const int j = ((g >> lh) << (lh + 2)) + (g & (h - 1));
-                const float a0 = xc[j * 64 + c], a1 = xc[(j + h) * 64 + c], a2 = xc[(j + 2 * h) * 64 + c],
-                            a3 = xc[(j + 3 * h) * 64 + c];
-                const float b0 = a0 + a1, b1 = a0 - a1, b2 = a2 + a3, b3 = a2 - a3;
+                const T a0 = xc[j * 64 + c], a1 = xc[(j + h) * 64 + c], a2 = xc[(j + 2 * h) * 64 + c],
+                        a3 = xc[(j + 3 * h) * 64 + c];
+                const T b0 = a0 + a1, b1 = a0 - a1, b2 = a2 + a3, b3 = a2 - a3;
                 xc[j * 64 + c] = b0 + b2;
                 xc[(j + h) * 64 + c] = b1 + b3;
                 xc[(j + 2 * h) * 64 + c] = b0 - b2;
@@ -216,7 +220,7 @@ __global__ __launch_bounds__(256) void fwht_cols_kernel(const float* __restrict_
         } else {
             for (int g = tid >> 6; g < D / 2; g += 4) {
                 const int j = ((g >> lh) << (lh + 1)) + (g & (h - 1));
-                const float a0 = xc[j * 64 + c], a1 = xc[(j + h) * 64 + c];
+                const T a0 = xc[j * 64 + c], a1 = xc[(j + h) * 64 + c];
                 xc[j * 64 + c] = a0 + a1;
                 xc[(j + h) * 64 + c] = a0 - a1;
             }
@@ -227,37 +231,37 @@ __global__ __launch_bounds__(256) void fwht_cols_kernel(const float* __restrict_
     if (!cin) return;
     for (int t = tid >> 6; t < D; t += 4) {
         const int64_t r = (hi * D + t) * S + lo;
-        float v = xc[t * 64 + c] * scale;
-        if (post_scale) v *= post_scale[r];
-        if (post_sign) v *= (float)post_sign[r];
+        T v = xc[t * 64 + c] * scale;
+        if (post_scale) v *= (T)post_scale[r];
+        if (post_sign) v *= (T)post_sign[r];
         out[r * ldout + c0 + c] = v;
     }
 }
 
 // ------------------------------------------------------------------------------- host helpers
-static kq_status rows_transform(const void* in, bool bf16, int64_t ldin, float* out, int64_t ldout, int64_t R,
-                                int64_t d, int64_t p2, const int8_t* pre, const int8_t* post, float scale,
-                                hipStream_t st) {
+// in_kind: 0 bf16, 1 fp32, 2 fp64.
+template <typename T>
+static kq_status rows_transform(const void* in, int in_kind, int64_t ldin, T* out, int64_t ldout, int64_t R, int64_t d,
+                                int64_t p2, const int8_t* pre, const int8_t* post, T scale, hipStream_t st) {
     if (R <= 0) return KQ_OK;
     int lp2 = 0;
     while ((int64_t(1) << lp2) < p2) lp2++;
-    const size_t smem = (size_t)d * sizeof(float);
+    const size_t smem = (size_t)d * sizeof(T);
     if (smem > 160 * 1024) return fail(KQ_ESHAPE, "row transform: row of %lld elements does not fit in LDS", (long long)d);
+    if (R > 2147483647) return fail(KQ_ESHAPE, "row transform: too many rows");
     static bool attr = false;
     if (!attr) {
-        hipFuncSetAttribute(reinterpret_cast<const void*>(&fwht_rows_kernel<true>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-        hipFuncSetAttribute(reinterpret_cast<const void*>(&fwht_rows_kernel<false>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+        hipFuncSetAttribute(reinterpret_cast<const void*>(&fwht_rows_kernel<0, T>), hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+        hipFuncSetAttribute(reinterpret_cast<const void*>(&fwht_rows_kernel<1, T>), hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+        hipFuncSetAttribute(reinterpret_cast<const void*>(&fwht_rows_kernel<2, T>), hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
         attr = true;
     }
-    if (R > 2147483647) return fail(KQ_ESHAPE, "row transform: too many rows");
-    if (bf16)
-        hipLaunchKernelGGL(fwht_rows_kernel<true>, dim3((unsigned)R), dim3(256), smem, st, in, ldin, out, ldout, d, lp2,
-                           pre, post, scale);
+    if (in_kind == 0)
+        hipLaunchKernelGGL((fwht_rows_kernel<0, T>), dim3((unsigned)R), dim3(256), smem, st, in, ldin, out, ldout, d, lp2, pre, post, scale);
+    else if (in_kind == 1)
+        hipLaunchKernelGGL((fwht_rows_kernel<1, T>), dim3((unsigned)R), dim3(256), smem, st, in, ldin, out, ldout, d, lp2, pre, post, scale);
     else
-        hipLaunchKernelGGL(fwht_rows_kernel<false>, dim3((unsigned)R), dim3(256), smem, st, in, ldin, out, ldout, d,
-                           lp2, pre, post, scale);
+        hipLaunchKernelGGL((fwht_rows_kernel<2, T>), dim3((unsigned)R), dim3(256), smem, st, in, ldin, out, ldout, d, lp2, pre, post, scale);
     return check_launch("fwht_rows");
 }
 
@@ -266,17 +270,20 @@ struct ColOps {
     const int8_t* pre_sign = nullptr;
     const float* post_scale = nullptr;
     const int8_t* post_sign = nullptr;
-    float scale = 1.0f;
+    double scale = 1.0;
 };
 
 // Sylvester transform along the row index within every chunk of p2 rows (R = m * p2 rows), as a
-// sequence of digit passes of at most 2^8 rows each. The first pass reads `in`, later passes work in
-// place on `out`. Pre-multipliers go to the first pass, post-multipliers and the scale to the last.
-static kq_status cols_transform(const float* in, int64_t ldin, float* out, int64_t ldout, int64_t R, int64_t ncols,
-                                int64_t p2, const ColOps& ops, hipStream_t st) {
+// sequence of digit passes of at most 2^8 (fp32) or 2^7 (fp64) rows each, so a pass's tile stays
+// within 64 KB of LDS. The first pass reads `in`, later passes work in place on `out`.
+// Pre-multipliers go to the first pass, post-multipliers and the scale to the last.
+template <typename T>
+static kq_status cols_transform(const T* in, int64_t ldin, T* out, int64_t ldout, int64_t R, int64_t ncols, int64_t p2,
+                                const ColOps& ops, hipStream_t st) {
+    const int maxbits = sizeof(T) == 8 ? 7 : 8;
     int k = 0;
     while ((int64_t(1) << k) < p2) k++;
-    int npass = (k + 7) / 8;
+    int npass = (k + maxbits - 1) / maxbits;
     if (npass == 0) npass = 1;
     int64_t S = 1;
     int done = 0;
@@ -284,12 +291,12 @@ static kq_status cols_transform(const float* in, int64_t ldin, float* out, int64
         const int lD = (k - done) / (npass - ps);
         const int D = 1 << lD;
         const bool first = ps == 0, last = ps == npass - 1;
-        const size_t smem = (size_t)D * 64 * sizeof(float);
+        const size_t smem = (size_t)D * 64 * sizeof(T);
         dim3 grid((unsigned)((ncols + 63) / 64), (unsigned)S, (unsigned)(R / ((int64_t)D * S)));
         if (S > 65535 || R / ((int64_t)D * S) > 65535) return fail(KQ_ESHAPE, "column transform grid too large");
-        hipLaunchKernelGGL(fwht_cols_kernel, grid, dim3(256), smem, st, first ? in : out, first ? ldin : ldout, out,
+        hipLaunchKernelGGL(fwht_cols_kernel<T>, grid, dim3(256), smem, st, first ? in : out, first ? ldin : ldout, out,
                            ldout, ncols, lD, S, first ? ops.pre_scale : nullptr, first ? ops.pre_sign : nullptr,
-                           last ? ops.post_scale : nullptr, last ? ops.post_sign : nullptr, last ? ops.scale : 1.0f);
+                           last ? ops.post_scale : nullptr, last ? ops.post_sign : nullptr, (T)(last ? ops.scale : 1.0));
         KQ_TRY(check_launch("fwht_cols"));
         S *= D;
         done += lD;
@@ -297,35 +304,37 @@ static kq_status cols_transform(const float* in, int64_t ldin, float* out, int64
     return KQ_OK;
 }
 
-static kq_status make_paley(float* P, int64_t m, const Field& f, bool transpose, hipStream_t st) {
+template <typename T>
+static kq_status make_paley(T* P, int64_t m, const Field& f, bool transpose, hipStream_t st) {
     const unsigned blocks = (unsigned)((m * m + 255) / 256 < 1024 ? (m * m + 255) / 256 : 1024);
-    hipLaunchKernelGGL(paley_kernel, dim3(blocks), dim3(256), 0, st, P, (int)m, f, transpose ? 1 : 0);
+    hipLaunchKernelGGL(paley_kernel<T>, dim3(blocks), dim3(256), 0, st, P, (int)m, f, transpose ? 1 : 0);
     return check_launch("paley");
 }
 
 // out_r = alpha * P in_r for every row r, each row seen as an m x p2 matrix (row mix of chunks).
-static kq_status paley_rows(const float* P, const float* in, int64_t ldin, float* out, int64_t ldout, int64_t R,
-                            int64_t m, int64_t p2, float alpha, hipStream_t st) {
+template <typename T>
+static kq_status paley_rows(const T* P, const T* in, int64_t ldin, T* out, int64_t ldout, int64_t R, int64_t m,
+                            int64_t p2, T alpha, hipStream_t st) {
     for (int64_t r0 = 0; r0 < R; r0 += 65535) {
         const int64_t cnt = (R - r0) < 65535 ? (R - r0) : 65535;
-        GemmArgs<float> g = gemm_args<float>(m, p2, m, P, m, in + r0 * ldin, p2, out + r0 * ldout, p2, alpha, 0.0f);
+        GemmArgs<T> g = gemm_args<T>(m, p2, m, P, m, in + r0 * ldin, p2, out + r0 * ldout, p2, alpha, T(0));
         g.nb1 = cnt; g.sA1 = 0; g.sB1 = ldin; g.sC1 = ldout;
-        KQ_TRY(gemm<float>(g, false, false, st));
+        KQ_TRY(gemm<T>(g, false, false, st));
     }
     return KQ_OK;
 }
 
 // out = alpha * (P (x) I_{p2}) in along the row index (rows grouped in m chunks of p2 rows).
-static kq_status paley_cols(const float* P, const float* in, int64_t ldin, float* out, int64_t ldout, int64_t m,
-                            int64_t p2, int64_t ncols, float alpha, hipStream_t st) {
+template <typename T>
+static kq_status paley_cols(const T* P, const T* in, int64_t ldin, T* out, int64_t ldout, int64_t m, int64_t p2,
+                            int64_t ncols, T alpha, hipStream_t st) {
     if (ldin == ncols && ldout == ncols) {
-        GemmArgs<float> g = gemm_args<float>(m, p2 * ncols, m, P, m, in, p2 * ncols, out, p2 * ncols, alpha, 0.0f);
-        return gemm<float>(g, false, false, st);
+        GemmArgs<T> g = gemm_args<T>(m, p2 * ncols, m, P, m, in, p2 * ncols, out, p2 * ncols, alpha, T(0));
+        return gemm<T>(g, false, false, st);
     }
-    // general leading dimensions: one batched GEMM per chunk row b of every block
-    GemmArgs<float> g = gemm_args<float>(m, ncols, m, P, m, in, p2 * ldin, out, p2 * ldout, alpha, 0.0f);
+    GemmArgs<T> g = gemm_args<T>(m, ncols, m, P, m, in, p2 * ldin, out, p2 * ldout, alpha, T(0));
     g.nb1 = p2; g.sA1 = 0; g.sB1 = ldin; g.sC1 = ldout;
-    return gemm<float>(g, false, false, st);
+    return gemm<T>(g, false, false, st);
 }
 
 }  // namespace kq
@@ -346,12 +355,13 @@ size_t rotate_in_ws(int64_t o, int64_t i) {
     if (!hadamard_split(i, m, p2, f)) return 0;
     Sizer z;
     z.take<float>((size_t)m * m);
-    if (m > 1) z.take<float>((size_t)(o > i ? o : i) * i);
+    z.take<double>((size_t)m * m);
+    if (m > 1) z.take<double>((size_t)(o > i ? o : i) * i);
     return z.used;
 }
 
 extern "C" kq_status kq_rotate_in(const void* Win, kq_dtype wdt, int64_t ldwin, float* Wout, int64_t ldw, int64_t o,
-                                  int64_t i, float* HX, const int8_t* sign_in, void* ws, size_t ws_bytes,
+                                  int64_t i, double* HX, const int8_t* sign_in, void* ws, size_t ws_bytes,
                                   kq_stream stream) {
     if (!sign_in || (o > 0 && (!Win || !Wout))) return fail(KQ_EINVAL, "kq_rotate_in: null pointer");
     if (o < 0 || i <= 0 || (o > 0 && (ldwin < i || ldw < i))) return fail(KQ_ESHAPE, "kq_rotate_in: bad sizes");
@@ -365,33 +375,37 @@ extern "C" kq_status kq_rotate_in(const void* Win, kq_dtype wdt, int64_t ldwin, 
     hipStream_t st = hs(stream);
     Arena ar(ws, ws_bytes);
     float* P = ar.take<float>((size_t)m * m);
-    float* T = m > 1 ? ar.take<float>((size_t)(o > i ? o : i) * i) : nullptr;
-    const float inv = (float)(1.0 / std::sqrt((double)i));
-    if (m > 1) KQ_TRY(make_paley(P, m, f, false, st));
-    // W' = W U: rows w -> H (s * w) / sqrt(i)
+    double* Pd = ar.take<double>((size_t)m * m);
+    double* T = m > 1 ? ar.take<double>((size_t)(o > i ? o : i) * i) : nullptr;
+    const double inv = 1.0 / std::sqrt((double)i);
+    // W' = W U: rows w -> H (s * w) / sqrt(i)   (fp32)
     if (o > 0) {
         if (m == 1) {
-            KQ_TRY(rows_transform(Win, wdt == KQ_BF16, ldwin, Wout, ldw, o, i, p2, sign_in, nullptr, inv, st));
+            KQ_TRY(rows_transform<float>(Win, wdt == KQ_BF16 ? 0 : 1, ldwin, Wout, ldw, o, i, p2, sign_in, nullptr,
+                                         (float)inv, st));
         } else {
-            KQ_TRY(rows_transform(Win, wdt == KQ_BF16, ldwin, T, i, o, i, p2, sign_in, nullptr, 1.0f, st));
-            KQ_TRY(paley_rows(P, T, i, Wout, ldw, o, m, p2, inv, st));
+            float* Tf = reinterpret_cast<float*>(T);
+            KQ_TRY(make_paley<float>(P, m, f, false, st));
+            KQ_TRY(rows_transform<float>(Win, wdt == KQ_BF16 ? 0 : 1, ldwin, Tf, i, o, i, p2, sign_in, nullptr, 1.0f, st));
+            KQ_TRY(paley_rows<float>(P, Tf, i, Wout, ldw, o, m, p2, (float)inv, st));
         }
     }
-    // H_X' = U^T H_X U: rows, then columns
+    // H_X' = U^T H_X U: rows, then columns   (fp64)
     if (HX) {
         if (m == 1) {
-            KQ_TRY(rows_transform(HX, false, i, HX, i, i, i, p2, sign_in, nullptr, inv, st));
+            KQ_TRY(rows_transform<double>(HX, 2, i, HX, i, i, i, p2, sign_in, nullptr, inv, st));
             ColOps ops;
             ops.pre_sign = sign_in;
             ops.scale = inv;
-            KQ_TRY(cols_transform(HX, i, HX, i, i, i, p2, ops, st));
+            KQ_TRY(cols_transform<double>(HX, i, HX, i, i, i, p2, ops, st));
         } else {
-            KQ_TRY(rows_transform(HX, false, i, HX, i, i, i, p2, sign_in, nullptr, 1.0f, st));
-            KQ_TRY(paley_rows(P, HX, i, T, i, i, m, p2, inv, st));
+            KQ_TRY(make_paley<double>(Pd, m, f, false, st));
+            KQ_TRY(rows_transform<double>(HX, 2, i, HX, i, i, i, p2, sign_in, nullptr, 1.0, st));
+            KQ_TRY(paley_rows<double>(Pd, HX, i, T, i, i, m, p2, inv, st));
             ColOps ops;
             ops.pre_sign = sign_in;
-            KQ_TRY(cols_transform(T, i, T, i, i, i, p2, ops, st));
-            KQ_TRY(paley_cols(P, T, i, HX, i, m, p2, i, inv, st));
+            KQ_TRY(cols_transform<double>(T, i, T, i, i, i, p2, ops, st));
+            KQ_TRY(paley_cols<double>(Pd, T, i, HX, i, m, p2, i, inv, st));
         }
     }
     return KQ_OK;
@@ -424,7 +438,7 @@ extern "C" kq_status kq_rotate_out(float* W, int64_t o, int64_t i, int64_t ldw, 
     float* P = ar.take<float>((size_t)m * m);
     float* T = (m > 1 || form != KQ_HG_DIAG) ? ar.take<float>((size_t)o * i) : nullptr;
     const float inv = (float)(1.0 / std::sqrt((double)o));
-    if (m > 1) KQ_TRY(make_paley(P, m, f, false, st));
+    if (m > 1) KQ_TRY(make_paley<float>(P, m, f, false, st));
     ColOps ops;
     const float* src = W;
     int64_t ldsrc = ldw;
@@ -448,11 +462,11 @@ extern "C" kq_status kq_rotate_out(float* W, int64_t o, int64_t i, int64_t ldw, 
     }
     if (m == 1) {
         ops.scale = inv;
-        return cols_transform(src, ldsrc, W, ldw, o, i, p2, ops, st);
+        return cols_transform<float>(src, ldsrc, W, ldw, o, i, p2, ops, st);
     }
     // FWHT of the chunks into T (in place when T already holds D_t S W), then the Paley mix into W
-    KQ_TRY(cols_transform(src, ldsrc, T, i, o, i, p2, ops, st));
-    return paley_cols(P, T, i, W, ldw, m, p2, i, inv, st);
+    KQ_TRY(cols_transform<float>(src, ldsrc, T, i, o, i, p2, ops, st));
+    return paley_cols<float>(P, T, i, W, ldw, m, p2, i, inv, st);
 }
 
 size_t unrotate_ws(int64_t o, int64_t i, kq_hg_form form) {
@@ -489,14 +503,14 @@ extern "C" kq_status kq_unrotate(const float* Q, int64_t o, int64_t i, int64_t l
     // A = D_t H_o^T Q / sqrt(o) ; H_o^T = P_o^T (x) H
     ColOps ops;
     ops.post_sign = sign_out;
-    ops.scale = (float)(1.0 / std::sqrt((double)o));
+    ops.scale = 1.0 / std::sqrt((double)o);
     if (form == KQ_HG_DIAG) ops.post_scale = Sinv;
     if (mo > 1) {
-        KQ_TRY(make_paley(Po, mo, fo, true, st));
-        KQ_TRY(paley_cols(Po, Q, ldq, T1, i, mo, po, i, 1.0f, st));
-        KQ_TRY(cols_transform(T1, i, T1, i, o, i, po, ops, st));
+        KQ_TRY(make_paley<float>(Po, mo, fo, true, st));
+        KQ_TRY(paley_cols<float>(Po, Q, ldq, T1, i, mo, po, i, 1.0f, st));
+        KQ_TRY(cols_transform<float>(T1, i, T1, i, o, i, po, ops, st));
     } else {
-        KQ_TRY(cols_transform(Q, ldq, T1, i, o, i, po, ops, st));
+        KQ_TRY(cols_transform<float>(Q, ldq, T1, i, o, i, po, ops, st));
     }
     float* cur = T1;
     if (form != KQ_HG_DIAG) {
@@ -514,9 +528,9 @@ extern "C" kq_status kq_unrotate(const float* Q, int64_t o, int64_t i, int64_t l
     const float inv_i = (float)(1.0 / std::sqrt((double)i));
     if (mi > 1) {
         float* other = (cur == T1) ? T2 : T1;
-        KQ_TRY(make_paley(Pi, mi, fi, true, st));
-        KQ_TRY(paley_rows(Pi, cur, i, other, i, o, mi, pi, 1.0f, st));
+        KQ_TRY(make_paley<float>(Pi, mi, fi, true, st));
+        KQ_TRY(paley_rows<float>(Pi, cur, i, other, i, o, mi, pi, 1.0f, st));
         cur = other;
     }
-    return rows_transform(cur, false, i, What, ldw, o, i, pi, nullptr, sign_in, inv_i, st);
+    return rows_transform<float>(cur, 1, i, What, ldw, o, i, pi, nullptr, sign_in, inv_i, st);
 }

@@ -224,11 +224,11 @@ extern "C" kq_status kq_quantize_layer(float* W, int64_t o, int64_t i, int64_t l
 }
 
 // ----------------------------------------------------------------------------------- sensitivity
-__global__ void sensitivity_kernel(const float* HX, int64_t i, int64_t ldh, const float* HG, int form, int64_t o,
+__global__ void sensitivity_kernel(const double* HX, int64_t i, int64_t ldh, const float* HG, int form, int64_t o,
                                    int64_t blk, double* score) {
     __shared__ double sx[256], sg[256];
     double ax = 0, ag = 0;
-    for (int64_t r = threadIdx.x; r < i; r += 256) ax += (double)HX[r * ldh + r];
+    for (int64_t r = threadIdx.x; r < i; r += 256) ax += HX[r * ldh + r];
     for (int64_t r = threadIdx.x; r < o; r += 256) {
         if (form == KQ_HG_DIAG) ag += (double)HG[r];
         else if (form == KQ_HG_FULL) ag += (double)HG[r * o + r];
@@ -247,7 +247,7 @@ __global__ void sensitivity_kernel(const float* HX, int64_t i, int64_t ldh, cons
     if (threadIdx.x == 0) *score = sx[0] * sg[0];
 }
 
-extern "C" kq_status kq_sensitivity(const float* HX, int64_t i, int64_t ldh, const float* HG, kq_hg_form form, int64_t o,
+extern "C" kq_status kq_sensitivity(const double* HX, int64_t i, int64_t ldh, const float* HG, kq_hg_form form, int64_t o,
                                     int64_t blk, double* score, kq_stream stream) {
     if (!HX || !HG || !score) return fail(KQ_EINVAL, "kq_sensitivity: null pointer");
     if (i <= 0 || o <= 0 || ldh < i) return fail(KQ_ESHAPE, "kq_sensitivity: bad sizes");
@@ -294,15 +294,21 @@ __global__ void sum_rows_kernel(const double* rl, int64_t o, double* total) {
     if (threadIdx.x == 0) *total = sp[0];
 }
 
+__global__ void narrow_kernel(const double* H, int64_t n, int64_t ldh, float* Hf) {
+    for (int64_t e = blockIdx.x * (int64_t)256 + threadIdx.x; e < n * n; e += (int64_t)gridDim.x * 256)
+        Hf[e] = (float)H[(e / n) * ldh + e % n];
+}
+
 size_t loss_ws(int64_t o, int64_t i) {
     Sizer z;
     z.take<float>((size_t)o * i);
     z.take<float>((size_t)o * i);
     z.take<double>((size_t)o);
+    z.take<float>((size_t)i * i);
     return z.used;
 }
 
-extern "C" kq_status kq_layer_loss(const float* W2, const float* Q, int64_t o, int64_t i, int64_t ldw, const float* HX2,
+extern "C" kq_status kq_layer_loss(const float* W2, const float* Q, int64_t o, int64_t i, int64_t ldw, const double* HX2,
                                    int64_t ldh, double* row_loss, double* loss, void* ws, size_t ws_bytes,
                                    kq_stream stream) {
     if (!W2 || !Q || !HX2 || !loss) return fail(KQ_EINVAL, "kq_layer_loss: null pointer");
@@ -313,11 +319,15 @@ extern "C" kq_status kq_layer_loss(const float* W2, const float* Q, int64_t o, i
     float* D = ar.take<float>((size_t)o * i);
     float* G = ar.take<float>((size_t)o * i);
     double* rl = ar.take<double>((size_t)o);
+    float* Hf = ar.take<float>((size_t)i * i);
     if (row_loss) rl = row_loss;
     unsigned b = (unsigned)((o * i + 255) / 256 < 8192 ? (o * i + 255) / 256 : 8192);
     hipLaunchKernelGGL(diff_kernel, dim3(b), dim3(256), 0, st, Q, W2, o, i, ldw, D);
     KQ_TRY(check_launch("loss diff"));
-    GemmArgs<float> g = gemm_args<float>(o, i, i, D, i, HX2, ldh, G, i, 1.0f, 0.0f);
+    const unsigned hb = (unsigned)((i * i + 255) / 256 < 8192 ? (i * i + 255) / 256 : 8192);
+    hipLaunchKernelGGL(narrow_kernel, dim3(hb), dim3(256), 0, st, HX2, i, ldh, Hf);
+    KQ_TRY(check_launch("loss narrow"));
+    GemmArgs<float> g = gemm_args<float>(o, i, i, D, i, Hf, i, G, i, 1.0f, 0.0f);
     KQ_TRY(gemm<float>(g, false, false, st));
     hipLaunchKernelGGL(rowdot_kernel, dim3((unsigned)o), dim3(256), 0, st, D, G, i, rl);
     KQ_TRY(check_launch("loss rowdot"));

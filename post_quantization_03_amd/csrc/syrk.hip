@@ -1,12 +1,16 @@
 // H_X accumulation H <- beta H + alpha X^T X (KronQ review page, Background: the input activation
 // covariance used as the layer-Hessian proxy).
 //
-// bf16 X: bf16 x bf16 products are exact in fp32, so the gfx950 bf16 matrix cores
-// (v_mfma_f32_16x16x32_bf16, fp32 accumulation) compute exactly the products an fp32 contraction
-// of the widened values would, at 16x the fp32 MFMA rate. Only the lower-triangle 128 x 128 tiles
-// of H are computed; a fixed split over tokens with a fixed-order reduction keeps the result
-// deterministic, and the reduction writes both triangles.
-// fp32 X: the fp32 MFMA GEMM with a lower-triangle epilogue, then a mirror pass.
+// H is kept in fp64: the damped factor R of H^{-1} is as sensitive to H as cond(H) makes it, and
+// rounding H to fp32 alone moves the sweep's pre-rounding values by up to ~2e-4 grid steps on the
+// 4096-wide layers (cond ~2e5 after damping).
+// bf16 X: bf16 x bf16 products are exact, so the gfx950 bf16 matrix cores
+// (v_mfma_f32_16x16x32_bf16) form exact products; every instruction starts from a zero accumulator
+// and its 32-product fp32 sum is added into fp64 registers, so only one fp32 rounding per 32 tokens
+// enters the result. Only the lower-triangle 128 x 128 tiles of H are computed; a fixed split over
+// tokens with a fixed-order fp64 reduction keeps the result deterministic, and both triangles are
+// written.
+// fp32 X: the fp64 MFMA GEMM on the widened values (small workloads only).
 #include "kq_internal.h"
 
 namespace kq {
@@ -36,8 +40,8 @@ __device__ inline void tri_decode(int t, int& tm, int& tn) {
 __device__ inline int lds_off(int m, int c) { return m * SY_K + ((c ^ (m & 7)) << 3); }
 
 __global__ __launch_bounds__(256) void syrk_bf16_kernel(const uint16_t* __restrict__ X, int64_t n, int64_t d,
-                                                        int64_t ldx, int64_t tok_per_split, float alpha, float beta,
-                                                        float* __restrict__ H, float* __restrict__ part,
+                                                        int64_t ldx, int64_t tok_per_split, double alpha, double beta,
+                                                        double* __restrict__ H, double* __restrict__ part,
                                                         int ntiles) {
     __shared__ __align__(16) uint16_t As[2][SY_T * SY_K];
     __shared__ __align__(16) uint16_t Bs[2][SY_T * SY_K];
@@ -91,11 +95,13 @@ __global__ __launch_bounds__(256) void syrk_bf16_kernel(const uint16_t* __restri
         }
     };
 
-    f4v acc[4][4];
+    double acc[4][4][4];
 #pragma unroll
     for (int i = 0; i < 4; i++)
 #pragma unroll
-        for (int j = 0; j < 4; j++) acc[i][j] = f4v{0, 0, 0, 0};
+        for (int j = 0; j < 4; j++)
+#pragma unroll
+            for (int r = 0; r < 4; r++) acc[i][j][r] = 0.0;
     const int wm = wave >> 1, wn = wave & 1;
 
     if (kb < ke) {
@@ -123,8 +129,11 @@ __global__ __launch_bounds__(256) void syrk_bf16_kernel(const uint16_t* __restri
 #pragma unroll
                 for (int i = 0; i < 4; i++)
 #pragma unroll
-                    for (int j = 0; j < 4; j++)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+                    for (int j = 0; j < 4; j++) {
+                        const f4v p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], f4v{0, 0, 0, 0}, 0, 0, 0);
+#pragma unroll
+                        for (int r = 0; r < 4; r++) acc[i][j][r] += (double)p[r];
+                    }
             }
             if (more) sstore(buf ^ 1);
             __syncthreads();
@@ -133,7 +142,7 @@ __global__ __launch_bounds__(256) void syrk_bf16_kernel(const uint16_t* __restri
     }
 
     if (part) {
-        float* out = part + ((int64_t)split * ntiles + tile) * (SY_T * SY_T);
+        double* out = part + ((int64_t)split * ntiles + tile) * (SY_T * SY_T);
 #pragma unroll
         for (int i = 0; i < 4; i++)
 #pragma unroll
@@ -153,8 +162,8 @@ __global__ __launch_bounds__(256) void syrk_bf16_kernel(const uint16_t* __restri
                     const int64_t m = m0 + wm * 64 + 16 * i + 4 * (lane >> 4) + r;
                     const int64_t c = n0 + wn * 64 + 16 * j + (lane & 15);
                     if (m >= d || c >= d || c > m) continue;
-                    float val = alpha * acc[i][j][r];
-                    if (beta != 0.0f) val += beta * H[m * d + c];
+                    double val = alpha * acc[i][j][r];
+                    if (beta != 0.0) val += beta * H[m * d + c];
                     H[m * d + c] = val;
                     H[c * d + m] = val;
                 }
@@ -162,8 +171,8 @@ __global__ __launch_bounds__(256) void syrk_bf16_kernel(const uint16_t* __restri
 }
 
 // Sum the token splits in order, scale, and write both triangles.
-__global__ void syrk_reduce_kernel(const float* __restrict__ part, int nsplit, int ntiles, int64_t d, float alpha,
-                                   float beta, float* __restrict__ H) {
+__global__ void syrk_reduce_kernel(const double* __restrict__ part, int nsplit, int ntiles, int64_t d, double alpha,
+                                   double beta, double* __restrict__ H) {
     const int tile = blockIdx.x;
     int tm, tn;
     tri_decode(tile, tm, tn);
@@ -171,23 +180,29 @@ __global__ void syrk_reduce_kernel(const float* __restrict__ part, int nsplit, i
         const int mm = e / SY_T, nn = e % SY_T;
         const int64_t m = (int64_t)tm * SY_T + mm, c = (int64_t)tn * SY_T + nn;
         if (m >= d || c >= d || c > m) continue;
-        float s = 0.0f;
+        double s = 0.0;
         for (int k = 0; k < nsplit; k++) s += part[((int64_t)k * ntiles + tile) * (SY_T * SY_T) + e];
-        float val = alpha * s;
-        if (beta != 0.0f) val += beta * H[m * d + c];
+        double val = alpha * s;
+        if (beta != 0.0) val += beta * H[m * d + c];
         H[m * d + c] = val;
         H[c * d + m] = val;
     }
 }
 
-__global__ void mirror_lower_kernel(float* H, int64_t d) {
+__global__ void mirror_lower_kernel(double* H, int64_t d) {
     const int64_t r = blockIdx.y;
     for (int64_t c = r + 1 + blockIdx.x * 256 + threadIdx.x; c < d; c += (int64_t)gridDim.x * 256) H[r * d + c] = H[c * d + r];
 }
 
-__global__ void scale_kernel(float* H, int64_t count, float beta) {
+__global__ void scale_kernel(double* H, int64_t count, double beta) {
     for (int64_t e = blockIdx.x * (int64_t)256 + threadIdx.x; e < count; e += (int64_t)gridDim.x * 256)
-        H[e] = beta == 0.0f ? 0.0f : beta * H[e];
+        H[e] = beta == 0.0 ? 0.0 : beta * H[e];
+}
+
+// fp32 X widened to fp64 (exact), for the fp64 GEMM path.
+__global__ void widen_kernel(const float* __restrict__ X, int64_t n, int64_t d, int64_t ldx, double* __restrict__ Y) {
+    for (int64_t e = blockIdx.x * (int64_t)256 + threadIdx.x; e < n * d; e += (int64_t)gridDim.x * 256)
+        Y[e] = (double)X[(e / d) * ldx + e % d];
 }
 
 static void syrk_plan(int64_t n, int64_t d, int& ntiles, int& nsplit, int64_t& tps) {
@@ -207,16 +222,17 @@ static void syrk_plan(int64_t n, int64_t d, int& ntiles, int& nsplit, int64_t& t
 using namespace kq;
 
 size_t hessian_ws(int64_t n, int64_t d, kq_dtype xdt) {
-    if (xdt != KQ_BF16 || n <= 0) return 0;
+    if (n <= 0) return 0;
+    if (xdt != KQ_BF16) return (size_t)n * d * sizeof(double) + 256;
     int ntiles, nsplit;
     int64_t tps;
     syrk_plan(n, d, ntiles, nsplit, tps);
     if (nsplit <= 1) return 0;
-    return (size_t)nsplit * ntiles * SY_T * SY_T * sizeof(float) + 256;
+    return (size_t)nsplit * ntiles * SY_T * SY_T * sizeof(double) + 256;
 }
 
-extern "C" kq_status kq_hessian_accum(const void* X, kq_dtype xdt, int64_t n, int64_t d, int64_t ldx, float alpha,
-                                      float beta, float* H, void* ws, size_t ws_bytes, kq_stream stream) {
+extern "C" kq_status kq_hessian_accum(const void* X, kq_dtype xdt, int64_t n, int64_t d, int64_t ldx, double alpha,
+                                      double beta, double* H, void* ws, size_t ws_bytes, kq_stream stream) {
     if (!H) return fail(KQ_EINVAL, "kq_hessian_accum: null H");
     if (d <= 0 || n < 0) return fail(KQ_ESHAPE, "kq_hessian_accum: bad sizes");
     if (xdt != KQ_F32 && xdt != KQ_BF16) return fail(KQ_EINVAL, "kq_hessian_accum: bad dtype");
@@ -231,12 +247,16 @@ extern "C" kq_status kq_hessian_accum(const void* X, kq_dtype xdt, int64_t n, in
     if (ldx < d) return fail(KQ_ESHAPE, "kq_hessian_accum: ldx < d");
     if (!aligned16(X) || (xdt == KQ_BF16 ? ldx % 8 : ldx % 4))
         return fail(KQ_EINVAL, "kq_hessian_accum: X must be 16-byte aligned with ldx a multiple of 16 bytes");
+    if (d > 65535) return fail(KQ_ESHAPE, "kq_hessian_accum: d too large");
     if (xdt == KQ_F32) {
-        GemmArgs<float> g = gemm_args<float>(d, d, n, static_cast<const float*>(X), ldx, static_cast<const float*>(X),
-                                             ldx, H, d, alpha, beta);
+        if (!ws || ws_bytes < hessian_ws(n, d, xdt)) return fail(KQ_EWORKSPACE, "kq_hessian_accum: workspace too small");
+        double* Y = reinterpret_cast<double*>((reinterpret_cast<uintptr_t>(ws) + 255) & ~uintptr_t(255));
+        unsigned b = (unsigned)((n * d + 255) / 256 < 8192 ? (n * d + 255) / 256 : 8192);
+        hipLaunchKernelGGL(widen_kernel, dim3(b), dim3(256), 0, st, static_cast<const float*>(X), n, d, ldx, Y);
+        KQ_TRY(check_launch("hessian widen"));
+        GemmArgs<double> g = gemm_args<double>(d, d, n, Y, d, Y, d, H, d, alpha, beta);
         g.tri = 1;
-        KQ_TRY(gemm<float>(g, true, false, st));
-        if (d > 65535) return fail(KQ_ESHAPE, "kq_hessian_accum: d too large");
+        KQ_TRY(gemm<double>(g, true, false, st));
         dim3 gm((unsigned)((d + 255) / 256 < 64 ? (d + 255) / 256 : 64), (unsigned)d);
         hipLaunchKernelGGL(mirror_lower_kernel, gm, dim3(256), 0, st, H, d);
         return check_launch("hessian mirror");
@@ -244,10 +264,10 @@ extern "C" kq_status kq_hessian_accum(const void* X, kq_dtype xdt, int64_t n, in
     int ntiles, nsplit;
     int64_t tps;
     syrk_plan(n, d, ntiles, nsplit, tps);
-    float* part = nullptr;
+    double* part = nullptr;
     if (nsplit > 1) {
         if (!ws || ws_bytes < hessian_ws(n, d, xdt)) return fail(KQ_EWORKSPACE, "kq_hessian_accum: workspace too small");
-        part = reinterpret_cast<float*>((reinterpret_cast<uintptr_t>(ws) + 255) & ~uintptr_t(255));
+        part = reinterpret_cast<double*>((reinterpret_cast<uintptr_t>(ws) + 255) & ~uintptr_t(255));
     }
     hipLaunchKernelGGL(syrk_bf16_kernel, dim3((unsigned)ntiles, (unsigned)nsplit), dim3(256), 0, st,
                        static_cast<const uint16_t*>(X), n, d, ldx, tps, alpha, beta, H, part, ntiles);

@@ -54,7 +54,7 @@ def quantize_layer(X: torch.Tensor, W: torch.Tensor, HG: torch.Tensor, s: torch.
         ws = torch.empty(max(workspace_bytes(o, i, n if x_batch is None else min(n, x_batch), xdt, cfg, verify), 256),
                          dtype=torch.uint8, device=dev)
     f32 = dict(dtype=torch.float32, device=dev)
-    H = torch.empty((i, i), **f32)
+    H = torch.empty((i, i), dtype=torch.float64, device=dev)
     if x_batch is None or x_batch >= n:
         K.kq_hessian_accum(X, H, 1.0 / n, 0.0, ws)
     else:

@@ -76,7 +76,7 @@ def quantize_stack(layers: list, budget: float = 3.0, group: int = 128, damp: fl
         hl = []
         for x, X in enumerate(L.X):
             n, i = X.shape
-            H = H_cache[li][x] if H_cache is not None else torch.empty((i, i), **f32)
+            H = H_cache[li][x] if H_cache is not None else torch.empty((i, i), dtype=torch.float64, device=dev)
             K.kq_hessian_accum(X, H, 1.0 / n, 0.0, ws)
             hl.append(H)
         for sl in L.subs:

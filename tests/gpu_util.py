@@ -21,6 +21,8 @@ def to_dev(a: np.ndarray, kind: str = "f32"):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
     if kind == "i8":
         return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int8)).to(dev)
+    if kind == "f64":
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float64)).to(dev)
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
 
 

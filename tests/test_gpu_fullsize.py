@@ -66,7 +66,8 @@ def check_rows(g, r, sp, rows):
     assert np.allclose(host(g["row_loss"])[rows], loss, rtol=1e-3)
     mu = np.stack([cmp["mu"][k] for k in range(len(rows))])
     sc = np.stack([cmp["scale"][k] for k in range(len(rows))])
-    assert rel_fro(host(g["offset"])[rows], mu) <= 1e-5 and rel_fro(host(g["scale"])[rows], sc) <= 1e-5
+    # grid parameters come from the swept values, which carry the sweep's fp32 drift
+    assert rel_fro(host(g["offset"])[rows], mu) <= 1e-4 and rel_fro(host(g["scale"])[rows], sc) <= 1e-4
 
 
 @pytest.mark.parametrize("name", ["C2", "C4", "C3"])
@@ -85,7 +86,7 @@ def test_fullsize_layer(name):
     torch.cuda.synchronize()
     assert host(g["info"]).tolist() == [0, 0]
     # loss identity at full size: rotated-coordinate loss == tr(H_G dW H_X dW^T) with the GPU's W^
-    Hx = torch.empty((sp.i, sp.i), dtype=torch.float32, device=X.device)
+    Hx = torch.empty((sp.i, sp.i), dtype=torch.float64, device=X.device)
     K.kq_hessian_accum(X, Hx, 1.0 / sp.n, 0.0, ws_tensor(K.kq_workspace_bytes("hessian", 0, sp.i, sp.n)))
     dW = (g["What"].double() - (W.float() if sp.w_dtype == "bf16" else W).double())
     A = dW @ Hx.double()
@@ -107,7 +108,7 @@ def test_fullsize_layer(name):
     r = oracle_sampled(sp, d, rows)
     eh, er, es = rel_fro(gH, r["HX2"]), rel_fro(gR, r["R"]), rel_fro(gS, r["S"])
     say(f"  H_X' {eh:.2e}  R {er:.2e}  S {es:.2e}")
-    assert eh <= 1e-5 and es <= 1e-5 and er <= 1e-3
+    assert eh <= 4e-7 * np.sqrt(32.0 / sp.n) and es <= 1e-5 and er <= 1e-5
     assert abs(float(host(g["score"])[0]) / r["score"] - 1) <= 1e-5
     check_rows(g, r, sp, rows)
 
@@ -162,7 +163,7 @@ def test_fullsize_stack():
         HX2 = {k: kq.rotate_in_hessian(HX[k], xs[k][1]) for k in HX}
         R = {k: kq.inverse_upper_factor(kq.damped(HX2[k], 0.01)[0]) for k in HX}
         for k in HX:
-            assert rel_fro(host(out.H[li][k]), HX2[k]) <= 1e-5
+            assert rel_fro(host(out.H[li][k]), HX2[k]) <= 4e-7 * np.sqrt(32.0 / synth.C5_TOKENS)
         for j, (sp, w, h, tt) in enumerate(subs_h):
             kk = li * 7 + j
             b = int(gbits[kk])

@@ -27,6 +27,12 @@ def signs(rng, d):
     return (rng.integers(0, 2, d) * 2 - 1).astype(np.int8)
 
 
+def hx_tol(n):
+    """H_X error bound for bf16 inputs: each 32-token matrix-core sum is rounded to fp32 once
+    (relative 2^-24) before fp64 accumulation, so the error averages down as sqrt(32 / n)."""
+    return 4e-7 * np.sqrt(32.0 / n)
+
+
 # ----------------------------------------------------------------------------- H_X
 @pytest.mark.parametrize("n,d,dt", [(1000, 200, "bf16"), (4096, 384, "bf16"), (300, 132, "f32"), (64, 8, "bf16"),
                                     (70000, 256, "bf16")])
@@ -37,13 +43,16 @@ def test_hessian_accum(n, d, dt):
     Xs = synth.gen_X(sp)
     ref = kq.hessian(synth.widen(Xs, dt))
     X = to_dev(Xs, dt)
-    H = torch.empty((d, d), dtype=torch.float32, device=dev)
+    H = torch.empty((d, d), dtype=torch.float64, device=dev)
     ws = ws_tensor(K.kq_workspace_bytes("hessian", 0, d, n, K.KQ_BF16 if dt == "bf16" else K.KQ_F32))
     K.kq_hessian_accum(X, H, 1.0 / n, 0.0, ws)
-    Hg = host(H).astype(np.float64)
+    Hg = host(H)
+    err = rel_fro(Hg, ref)
+    say(f"  H_X rel err {err:.2e}")
     assert np.array_equal(Hg, Hg.T)
-    assert rel_fro(Hg, ref) <= 1e-5
-    assert np.abs(Hg - ref).max() <= 1e-5 * np.diag(ref).max()
+    tol = hx_tol(n) if dt == "bf16" else 1e-12
+    assert err <= tol
+    assert np.abs(Hg - ref).max() <= tol * np.diag(ref).max()
 
 
 def test_hessian_accumulates_batches():
@@ -52,11 +61,11 @@ def test_hessian_accumulates_batches():
     Xs = synth.gen_X(sp)
     ref = kq.hessian(synth.widen(Xs, "bf16"))
     X = to_dev(Xs, "bf16")
-    H = torch.empty((256, 256), dtype=torch.float32, device=dev)
+    H = torch.empty((256, 256), dtype=torch.float64, device=dev)
     ws = ws_tensor(K.kq_workspace_bytes("hessian", 0, 256, 3000))
     for k0, beta in ((0, 0.0), (1000, 1.0), (2000, 1.0)):
         K.kq_hessian_accum(X[k0:k0 + 1000], H, 1.0 / 3000, beta, ws)
-    assert rel_fro(host(H), ref) <= 1e-5
+    assert rel_fro(host(H), ref) <= hx_tol(1000)
 
 
 # ----------------------------------------------------------------------------- input rotation
@@ -70,17 +79,17 @@ def test_rotate_in(o, i, wdt, with_h):
     W64 = rng.standard_normal((o, i)) * 0.02
     Ws = synth.f32_to_bf16_bits(W64.astype(f32)) if wdt == "bf16" else W64.astype(f32)
     s = signs(rng, i)
-    H32 = spd_f32(rng, i, n=i + 16) if with_h else None
+    H64 = spd_f32(rng, i, n=i + 16).astype(np.float64) if with_h else None
     W1_ref = kq.rotate_in_weights(synth.widen(Ws, wdt), s)
     Win = to_dev(Ws, wdt)
     Wout = torch.empty((o, i), dtype=torch.float32, device=dev)
-    Hd = to_dev(H32) if with_h else None
+    Hd = to_dev(H64, "f64") if with_h else None
     ws = ws_tensor(K.kq_workspace_bytes("rotate_in", o, i))
     K.kq_rotate_in(Win, Wout, Hd, to_dev(s, "i8"), ws)
     assert rel_fro(host(Wout), W1_ref) <= 2e-6
     if with_h:
-        H2_ref = kq.rotate_in_hessian(H32.astype(np.float64), s)
-        assert rel_fro(host(Hd), H2_ref) <= 2e-6
+        H2_ref = kq.rotate_in_hessian(H64, s)
+        assert rel_fro(host(Hd), H2_ref) <= 1e-13
 
 
 # ----------------------------------------------------------------------------- H_G square root
@@ -145,13 +154,13 @@ def test_cholinv(i):
     torch, dev = torch_dev()
     say(f"cholinv i={i}")
     sp = synth.scaled(synth.CONFIGS["C2"], n=4 * i, i=i, n_outliers=max(1, i // 100))
-    H32 = kq.hessian(synth.widen(synth.gen_X(sp), "bf16")).astype(f32)
-    H, _ = kq.damped(H32.astype(np.float64), 0.01)
+    H64 = kq.hessian(synth.widen(synth.gen_X(sp), "bf16"))
+    H, _ = kq.damped(H64, 0.01)
     R_ref = kq.inverse_upper_factor(H)
     R = torch.empty((i, i), dtype=torch.float32, device=dev)
     info = torch.full((1,), 7, dtype=torch.int32, device=dev)
     ws = ws_tensor(K.kq_workspace_bytes("cholinv", 0, i))
-    K.kq_cholinv(to_dev(H32), 0.01, R, info, ws)
+    K.kq_cholinv(to_dev(H64, "f64"), 0.01, R, info, ws)
     Rg = host(R).astype(np.float64)
     assert int(host(info)[0]) == 0
     assert np.all(np.tril(Rg, -1) == 0)
@@ -163,10 +172,10 @@ def test_cholinv(i):
 def test_cholinv_reports_not_positive_definite():
     torch, dev = torch_dev()
     i = 256
-    H = -np.eye(i, dtype=f32)
+    H = -np.eye(i)
     R = torch.empty((i, i), dtype=torch.float32, device=dev)
     info = torch.zeros(1, dtype=torch.int32, device=dev)
-    K.kq_cholinv(to_dev(H), 0.0, R, info, ws_tensor(K.kq_workspace_bytes("cholinv", 0, i)))
+    K.kq_cholinv(to_dev(H, "f64"), 0.0, R, info, ws_tensor(K.kq_workspace_bytes("cholinv", 0, i)))
     assert int(host(info)[0]) > 0
 
 
@@ -205,7 +214,7 @@ def test_quantize_layer(o, i, bits, group):
     assert np.allclose(host(rl), loss, rtol=1e-3, atol=1e-12)
     mu = np.stack([cmp["mu"][k] for k in range(o)])
     sc = np.stack([cmp["scale"][k] for k in range(o)])
-    assert rel_fro(host(offset), mu) <= 1e-5 and rel_fro(host(scale), sc) <= 1e-5
+    assert rel_fro(host(offset), mu) <= 1e-4 and rel_fro(host(scale), sc) <= 1e-4
 
 
 # ----------------------------------------------------------------------------- sensitivity, unrotate, loss
@@ -219,7 +228,7 @@ def test_sensitivity(form):
           "block": np.stack([spd_f32(rng, 64) for _ in range(4)]),
           "full": spd_f32(rng, o)}[form]
     score = torch.empty(1, dtype=torch.float64, device=dev)
-    K.kq_sensitivity(to_dev(H), to_dev(hg), form, o, 64, score)
+    K.kq_sensitivity(to_dev(H, "f64"), to_dev(hg), form, o, 64, score)
     ref = kq.sensitivity(H.astype(np.float64), hg.astype(np.float64), form)
     assert abs(host(score)[0] / ref - 1) <= 1e-12
 
@@ -246,7 +255,7 @@ def test_unrotate_and_loss(form, o, i, blk):
     H = spd_f32(rng, i)
     loss = torch.empty(1, dtype=torch.float64, device=dev)
     rl = torch.empty(o, dtype=torch.float64, device=dev)
-    K.kq_layer_loss(to_dev(W2), to_dev(Q), to_dev(H), rl, loss, ws)
+    K.kq_layer_loss(to_dev(W2), to_dev(Q), to_dev(H, "f64"), rl, loss, ws)
     lref = kq.rotated_loss(W2.astype(np.float64), Q.astype(np.float64), H.astype(np.float64))
     assert abs(host(loss)[0] / lref.sum() - 1) <= 1e-5
     assert np.allclose(host(rl), lref, rtol=1e-4)
