@@ -263,7 +263,246 @@ kq_status gemm(const GemmArgs<T>& g, bool ta, bool tb, hipStream_t st) {
     return check_launch("gemm");
 }
 template kq_status gemm<float>(const GemmArgs<float>&, bool, bool, hipStream_t);
-template kq_status gemm<double>(const GemmArgs<double>&, bool, bool, hipStream_t);
+
+// ================================================================================ fp64 GEMM (VALU)
+// On gfx950 the fp64 matrix-core instruction (16x16x4) sustains about 36 TFLOP/s even in a
+// dependency-free loop, while the fp64 vector FMA pipe sustains about 59 (both measured on MI355X with
+// one-kernel probes), so fp64 products run on vector FMAs. 256 threads own a BM x BN tile of C; thread
+// (tr, tc) = (tid / 16, tid % 16) keeps a register tile of rows h * BM/2 + tr * RG + i and columns
+// h * BN/2 + tc * CG + j (h = 0, 1; RG = BM/32, CG = BN/32). Operands are staged k-major in LDS
+// (double-buffered 16-deep K slices, one barrier per slice) and read as 16-byte vectors; the lanes of a
+// wave that share a row group read the same A address (broadcast) and the 16 column groups read one
+// contiguous run of B. Tile order, triangular launch, K restriction and epilogue follow the MFMA
+// kernel above.
+template <int BM, int BN, bool TA, bool TB, bool VEC>
+__global__ __launch_bounds__(256) void dgemm_valu_kernel(GemmArgs<double> g) {
+    if (g.skip && *g.skip) return;
+    constexpr int BK = 16, PAD = 8;
+    constexpr int RG = BM / 32, CG = BN / 32;
+    constexpr int VPR = BK / 2;                  // 16-byte vectors per tile row (k direction)
+    constexpr int NVA = BM * BK / 2 / 256, NVB = BN * BK / 2 / 256;
+    static_assert(NVA >= 1 && NVB >= 1 && RG % 2 == 0 && CG % 2 == 0, "tile shape");
+    __shared__ __align__(16) double As[2][BK][BM + PAD];
+    __shared__ __align__(16) double Bs[2][BK][BN + PAD];
+    const int tid = threadIdx.x, tr = tid >> 4, tc = tid & 15;
+    int64_t tm, tn;
+    {
+        const int64_t nx = (g.N + BN - 1) / BN;
+        const int64_t L = g.tri ? (int64_t)gridDim.x : (int64_t)gridDim.x * gridDim.y;
+        int64_t lid = g.tri ? (int64_t)blockIdx.x : (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
+        if (L % 8 == 0) lid = (lid % 8) * (L / 8) + lid / 8;
+        if (g.tri) {
+            int64_t r = (int64_t)((sqrt(8.0 * (double)lid + 1.0) - 1.0) * 0.5);
+            while (r * (r + 1) / 2 > lid) r--;
+            while ((r + 1) * (r + 2) / 2 <= lid) r++;
+            const int64_t c = lid - r * (r + 1) / 2;
+            if (g.tri == 1) { tm = r; tn = c; } else { tm = c; tn = r; }
+        } else {
+            tm = lid / nx;
+            tn = lid % nx;
+        }
+    }
+    const int64_t m0 = tm * BM, n0 = tn * BN;
+    if (g.skip_tile >= 0 && ((m0 >> 7) == g.skip_tile || (n0 >> 7) == g.skip_tile)) return;
+    const int64_t z = blockIdx.z, z1 = z / g.nb2, z2 = z % g.nb2;
+    const double* __restrict__ A = g.A + z1 * g.sA1 + z2 * g.sA2;
+    const double* __restrict__ B = g.B + z1 * g.sB1 + z2 * g.sB2;
+    double* C = g.C + z1 * g.sC1 + z2 * g.sC2;
+    const int8_t* rs = g.rsign ? g.rsign + z1 * g.sR1 + z2 * g.sR2 : nullptr;
+    const int8_t* cs = g.csign ? g.csign + z1 * g.sS1 + z2 * g.sS2 : nullptr;
+    const int64_t M = g.M, N = g.N;
+    int64_t kb = 0, ke = g.K;
+    if (g.kmode & 1) kb = kb > m0 ? kb : m0;
+    if (g.kmode & 2) kb = kb > n0 ? kb : n0;
+    if (g.kmode & 4) ke = ke < m0 + BM ? ke : m0 + BM;
+    if (g.kmode & 8) ke = ke < n0 + BN ? ke : n0 + BN;
+    kb = (kb / BK) * BK;
+
+    double acc[2][RG][2][CG];
+#pragma unroll
+    for (int hi = 0; hi < 2; hi++)
+#pragma unroll
+        for (int i = 0; i < RG; i++)
+#pragma unroll
+            for (int hj = 0; hj < 2; hj++)
+#pragma unroll
+                for (int j = 0; j < CG; j++) acc[hi][i][hj][j] = 0.0;
+
+    double ra[NVA][2], rb[NVB][2];
+    const bool fullMN = (m0 + BM <= M) && (n0 + BN <= N);
+    auto gload = [&](int64_t k0) {
+        const bool full = VEC && fullMN && (k0 + BK <= ke);
+#pragma unroll
+        for (int q = 0; q < NVA; q++) {
+            const int v = tid + 256 * q;
+            int64_t gm, gk;
+            if (!TA) { gm = m0 + v / VPR; gk = k0 + (v % VPR) * 2; }
+            else { gk = k0 + v / (BM / 2); gm = m0 + (v % (BM / 2)) * 2; }
+            const double* p = TA ? A + gk * g.lda + gm : A + gm * g.lda + gk;
+            if (full) {
+                const V16<double> t = *reinterpret_cast<const V16<double>*>(p);
+                ra[q][0] = t.v[0]; ra[q][1] = t.v[1];
+            } else {
+#pragma unroll
+                for (int e = 0; e < 2; e++) {
+                    const bool in = TA ? (gk < ke && gm + e < M) : (gm < M && gk + e < ke);
+                    ra[q][e] = in ? p[e] : 0.0;
+                }
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < NVB; q++) {
+            const int v = tid + 256 * q;
+            int64_t gn, gk;
+            if (TB) { gn = n0 + v / VPR; gk = k0 + (v % VPR) * 2; }
+            else { gk = k0 + v / (BN / 2); gn = n0 + (v % (BN / 2)) * 2; }
+            const double* p = TB ? B + gn * g.ldb + gk : B + gk * g.ldb + gn;
+            if (full) {
+                const V16<double> t = *reinterpret_cast<const V16<double>*>(p);
+                rb[q][0] = t.v[0]; rb[q][1] = t.v[1];
+            } else {
+#pragma unroll
+                for (int e = 0; e < 2; e++) {
+                    const bool in = TB ? (gn < N && gk + e < ke) : (gk < ke && gn + e < N);
+                    rb[q][e] = in ? p[e] : 0.0;
+                }
+            }
+        }
+    };
+    auto sstore = [&](int buf) {
+#pragma unroll
+        for (int q = 0; q < NVA; q++) {
+            const int v = tid + 256 * q;
+            if (!TA) {
+                As[buf][(v % VPR) * 2][v / VPR] = ra[q][0];
+                As[buf][(v % VPR) * 2 + 1][v / VPR] = ra[q][1];
+            } else {
+                *reinterpret_cast<V16<double>*>(&As[buf][v / (BM / 2)][(v % (BM / 2)) * 2]) = V16<double>{{ra[q][0], ra[q][1]}};
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < NVB; q++) {
+            const int v = tid + 256 * q;
+            if (TB) {
+                Bs[buf][(v % VPR) * 2][v / VPR] = rb[q][0];
+                Bs[buf][(v % VPR) * 2 + 1][v / VPR] = rb[q][1];
+            } else {
+                *reinterpret_cast<V16<double>*>(&Bs[buf][v / (BN / 2)][(v % (BN / 2)) * 2]) = V16<double>{{rb[q][0], rb[q][1]}};
+            }
+        }
+    };
+
+    if (kb < ke) {
+        gload(kb);
+        sstore(0);
+        __syncthreads();
+        int buf = 0;
+        for (int64_t k0 = kb; k0 < ke; k0 += BK) {
+            const bool more = k0 + BK < ke;
+            if (more) gload(k0 + BK);
+#pragma unroll 2
+            for (int kk = 0; kk < BK; kk++) {
+                double a[2][RG], b[2][CG];
+#pragma unroll
+                for (int h = 0; h < 2; h++) {
+#pragma unroll
+                    for (int i = 0; i < RG; i += 2) {
+                        const V16<double> t = *reinterpret_cast<const V16<double>*>(&As[buf][kk][h * (BM / 2) + tr * RG + i]);
+                        a[h][i] = t.v[0]; a[h][i + 1] = t.v[1];
+                    }
+#pragma unroll
+                    for (int j = 0; j < CG; j += 2) {
+                        const V16<double> t = *reinterpret_cast<const V16<double>*>(&Bs[buf][kk][h * (BN / 2) + tc * CG + j]);
+                        b[h][j] = t.v[0]; b[h][j + 1] = t.v[1];
+                    }
+                }
+#pragma unroll
+                for (int hi = 0; hi < 2; hi++)
+#pragma unroll
+                    for (int i = 0; i < RG; i++)
+#pragma unroll
+                        for (int hj = 0; hj < 2; hj++)
+#pragma unroll
+                            for (int j = 0; j < CG; j++) acc[hi][i][hj][j] = fma(a[hi][i], b[hj][j], acc[hi][i][hj][j]);
+            }
+            if (more) sstore(buf ^ 1);
+            __syncthreads();
+            buf ^= 1;
+        }
+    }
+
+    // epilogue, one row half at a time: the C loads of a half are issued before any is used
+#pragma unroll
+    for (int hi = 0; hi < 2; hi++) {
+        double cv[RG][2][CG];
+        if (g.beta != 0.0) {
+#pragma unroll
+            for (int i = 0; i < RG; i++)
+#pragma unroll
+                for (int hj = 0; hj < 2; hj++)
+#pragma unroll
+                    for (int j = 0; j < CG; j++) {
+                        const int64_t m = m0 + hi * (BM / 2) + tr * RG + i, n = n0 + hj * (BN / 2) + tc * CG + j;
+                        cv[i][hj][j] = (m < M && n < N) ? C[m * g.ldc + n] : 0.0;
+                    }
+        }
+#pragma unroll
+        for (int i = 0; i < RG; i++)
+#pragma unroll
+            for (int hj = 0; hj < 2; hj++)
+#pragma unroll
+                for (int j = 0; j < CG; j++) {
+                    const int64_t m = m0 + hi * (BM / 2) + tr * RG + i, n = n0 + hj * (BN / 2) + tc * CG + j;
+                    if (m >= M || n >= N) continue;
+                    if (g.tri == 1 && n > m) continue;
+                    if (g.tri == 2 && m > n) continue;
+                    double v = g.alpha * acc[hi][i][hj][j];
+                    if (rs) v *= (double)rs[m];
+                    if (cs) v *= (double)cs[n];
+                    if (g.beta != 0.0) v += g.beta * cv[i][hj][j];
+                    C[m * g.ldc + n] = v;
+                }
+    }
+}
+
+template <int BM, int BN>
+static void dgemm_launch(const GemmArgs<double>& g, bool ta, bool tb, bool vec, hipStream_t st) {
+    const int64_t nx = (g.N + BN - 1) / BN, ny = (g.M + BM - 1) / BM;
+    const dim3 grid((unsigned)(g.tri ? nx * (nx + 1) / 2 : nx), (unsigned)(g.tri ? 1 : ny), (unsigned)(g.nb1 * g.nb2));
+#define KQ_DG(TA_, TB_, V_) hipLaunchKernelGGL((dgemm_valu_kernel<BM, BN, TA_, TB_, V_>), grid, dim3(256), 0, st, g)
+    if (vec) {
+        if (!ta && !tb) KQ_DG(false, false, true);
+        else if (!ta && tb) KQ_DG(false, true, true);
+        else if (ta && !tb) KQ_DG(true, false, true);
+        else KQ_DG(true, true, true);
+    } else {
+        if (!ta && !tb) KQ_DG(false, false, false);
+        else if (!ta && tb) KQ_DG(false, true, false);
+        else if (ta && !tb) KQ_DG(true, false, false);
+        else KQ_DG(true, true, false);
+    }
+#undef KQ_DG
+}
+
+// 128 x 128 tiles when they fill the chip (256 compute units), 64 x 64 otherwise.
+template <>
+kq_status gemm<double>(const GemmArgs<double>& g, bool ta, bool tb, hipStream_t st) {
+    if (g.M <= 0 || g.N <= 0) return KQ_OK;
+    const bool vec = aligned16(g.A) && aligned16(g.B) && g.lda % 2 == 0 && g.ldb % 2 == 0 && g.sA1 % 2 == 0 &&
+                     g.sA2 % 2 == 0 && g.sB1 % 2 == 0 && g.sB2 % 2 == 0;
+    const int64_t batch = g.nb1 * g.nb2;
+    if (batch > 65535) return fail(KQ_ESHAPE, "gemm: batch too large");
+    const int64_t nx = (g.N + 127) / 128, ny = (g.M + 127) / 128;
+    if (g.tri && nx != ny) return fail(KQ_ESHAPE, "gemm: triangular products need a square tile grid");
+    const int64_t tiles = (g.tri ? nx * (nx + 1) / 2 : nx * ny) * batch;
+    const bool big = tiles >= 256;
+    const int64_t ty = big ? ny : (g.M + 63) / 64;
+    if (!g.tri && ty > 65535) return fail(KQ_ESHAPE, "gemm grid too large");
+    if (g.tri && ((g.N + 63) / 64) != ((g.M + 63) / 64)) return fail(KQ_ESHAPE, "gemm: triangular products need a square tile grid");
+    if (big) dgemm_launch<128, 128>(g, ta, tb, vec, st);
+    else dgemm_launch<64, 64>(g, ta, tb, vec, st);
+    return check_launch("dgemm");
+}
 
 // ========================================================================================= helpers
 template <typename T>

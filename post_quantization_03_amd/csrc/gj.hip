@@ -65,128 +65,137 @@ __global__ __launch_bounds__(256) void gj_gather_kernel(const double* __restrict
     }
 }
 
+// 1/p to full fp64 precision: hardware reciprocal estimate refined by two Newton steps.
+__device__ inline double recip64(double p) {
+    double r = __builtin_amdgcn_rcp(p);
+    r = fma(r, fma(-p, r, 1.0), r);
+    return fma(r, fma(-p, r, 1.0), r);
+}
+
 // Pinv = P^{-1} for the nbk x nbk pivot P = C[k0 : k0 + nbk][0 : nbk] (identity-padded to 128) by a
-// Gauss-Jordan sweep held in registers: thread (tr, tc) owns rows 8tr..8tr+7 and columns 8tc..8tc+7.
-// Pivots are taken four at a time: the 4 pivot rows and columns go through LDS (double-buffered, one
-// barrier per step), every thread inverts the 4 x 4 pivot block itself and applies the rank-4 update
+// Gauss-Jordan sweep held in registers: 512 threads, thread (tr, tc) owns rows 4tr..4tr+3 and
+// columns 8tc..8tc+7 (two waves per SIMD). Pivots are taken four at a time: the 4 pivot rows and
+// columns go through LDS (double-buffered, one barrier per step), every thread inverts the 4 x 4
+// pivot block itself and applies the rank-4 update
 //     A_RR -= A_RJ D^{-1} A_JR,  A_RJ <- A_RJ D^{-1},  A_JR <- D^{-1} A_JR,  A_JJ <- -D^{-1}.
-__global__ __launch_bounds__(256) void gj_pivot_kernel(const double* __restrict__ C, int64_t sC, int64_t k0, int nbk,
-                                                       double* __restrict__ Pinv, int32_t* info, const int* skip) {
+constexpr int GJ_PIV_THREADS = 512;
+__global__ __launch_bounds__(GJ_PIV_THREADS) void gj_pivot_kernel(const double* __restrict__ C, int64_t sC,
+                                                                  int64_t k0, int nbk, double* __restrict__ Pinv,
+                                                                  int32_t* info, const int* skip) {
     if (skip && *skip) return;
-    __shared__ double rowb[2][4][GJ_NB], colb[2][GJ_NB][4];
+    __shared__ __align__(16) double rowb[2][4][GJ_NB];
+    __shared__ __align__(16) double colb[2][GJ_NB][4];
     __shared__ int bad;
     const int tid = threadIdx.x, tr = tid >> 4, tc = tid & 15;
     const int64_t z = blockIdx.x;
     const double* P = C + z * sC + k0 * GJ_NB;
-    double a[8][8];
+    double a[4][8];
 #pragma unroll
-    for (int rr = 0; rr < 8; rr++)
+    for (int rr = 0; rr < 4; rr++)
 #pragma unroll
         for (int cc = 0; cc < 8; cc++) {
-            const int r = 8 * tr + rr, c = 8 * tc + cc;
+            const int r = 4 * tr + rr, c = 8 * tc + cc;
             a[rr][cc] = (r < nbk && c < nbk) ? P[r * GJ_NB + c] : (r == c ? 1.0 : 0.0);
         }
     if (tid == 0) bad = 0;
-    for (int jb = 0; jb < 16; jb++) {
-#pragma unroll
-        for (int half = 0; half < 2; half++) {
-            const int jo = 4 * half, j0 = 8 * jb + jo, buf = half;
-            if (tr == jb) {
-#pragma unroll
-                for (int q = 0; q < 4; q++)
-#pragma unroll
-                    for (int cc = 0; cc < 8; cc++) rowb[buf][q][8 * tc + cc] = a[jo + q][cc];
-            }
-            if (tc == jb) {
-#pragma unroll
-                for (int rr = 0; rr < 8; rr++)
-#pragma unroll
-                    for (int q = 0; q < 4; q++) colb[buf][8 * tr + rr][q] = a[rr][jo + q];
-            }
-            __syncthreads();
-            // 4 x 4 pivot block and its inverse (unpivoted Gauss-Jordan; SPD pivots are positive)
-            double D[4][4];
+    for (int jb = 0; jb < 32; jb++) {
+        const int j0 = 4 * jb, buf = jb & 1, jo = (jb & 1) * 4;
+        const bool own_r = tr == jb, own_c = tc == (jb >> 1);
+        if (own_r) {
 #pragma unroll
             for (int q = 0; q < 4; q++)
 #pragma unroll
-                for (int q2 = 0; q2 < 4; q2++) D[q][q2] = rowb[buf][q][j0 + q2];
+                for (int cc = 0; cc < 8; cc++) rowb[buf][q][8 * tc + cc] = a[q][cc];
+        }
+        if (own_c) {
 #pragma unroll
-            for (int t = 0; t < 4; t++) {
-                double p = D[t][t];
-                if (!(p > 0.0)) {
-                    if (tid == 0 && !bad) bad = j0 + t + 1;
-                    p = 1.0;
-                }
-                const double ip = 1.0 / p;
-#pragma unroll
-                for (int q = 0; q < 4; q++)
-#pragma unroll
-                    for (int q2 = 0; q2 < 4; q2++)
-                        if (q != t && q2 != t) D[q][q2] -= D[q][t] * D[t][q2] * ip;
-#pragma unroll
-                for (int q = 0; q < 4; q++)
-                    if (q != t) { D[q][t] *= ip; D[t][q] *= ip; }
-                D[t][t] = -ip;
-            }
-            // D now holds -D^{-1}
-            double cv[8][4], rv[4][8], Tm[8][4];
-#pragma unroll
-            for (int rr = 0; rr < 8; rr++)
-#pragma unroll
-                for (int q = 0; q < 4; q++) cv[rr][q] = colb[buf][8 * tr + rr][q];
-#pragma unroll
-            for (int q = 0; q < 4; q++)
-#pragma unroll
-                for (int cc = 0; cc < 8; cc++) rv[q][cc] = rowb[buf][q][8 * tc + cc];
-#pragma unroll
-            for (int rr = 0; rr < 8; rr++)
+            for (int rr = 0; rr < 4; rr++)
 #pragma unroll
                 for (int q = 0; q < 4; q++) {
-                    double t = 0.0;
-#pragma unroll
-                    for (int q2 = 0; q2 < 4; q2++) t = fma(cv[rr][q2], -D[q2][q], t);
-                    Tm[rr][q] = t;
+                    const double lo = a[rr][q], hi = a[rr][4 + q];  // value selects keep a[][] in registers
+                    colb[buf][4 * tr + rr][q] = jo ? hi : lo;
                 }
+        }
+        __syncthreads();
+        // 4 x 4 pivot block and its inverse (unpivoted Gauss-Jordan; SPD pivots are positive)
+        double D[4][4];
 #pragma unroll
-            for (int rr = 0; rr < 8; rr++)
+        for (int q = 0; q < 4; q++)
+#pragma unroll
+            for (int q2 = 0; q2 < 4; q2++) D[q][q2] = rowb[buf][q][j0 + q2];
+#pragma unroll
+        for (int t = 0; t < 4; t++) {
+            double p = D[t][t];
+            if (!(p > 0.0)) {
+                if (tid == 0 && !bad) bad = j0 + t + 1;
+                p = 1.0;
+            }
+            const double ip = recip64(p);
+#pragma unroll
+            for (int q = 0; q < 4; q++)
+#pragma unroll
+                for (int q2 = 0; q2 < 4; q2++)
+                    if (q != t && q2 != t) D[q][q2] = fma(-D[q][t] * ip, D[t][q2], D[q][q2]);
+#pragma unroll
+            for (int q = 0; q < 4; q++)
+                if (q != t) { D[q][t] *= ip; D[t][q] *= ip; }
+            D[t][t] = -ip;
+        }
+        // D now holds -D^{-1}
+        double cv[4][4], rv[4][8], Tm[4][4];
+#pragma unroll
+        for (int rr = 0; rr < 4; rr++)
+#pragma unroll
+            for (int q = 0; q < 4; q++) cv[rr][q] = colb[buf][4 * tr + rr][q];
+#pragma unroll
+        for (int q = 0; q < 4; q++)
+#pragma unroll
+            for (int cc = 0; cc < 8; cc++) rv[q][cc] = rowb[buf][q][8 * tc + cc];
+#pragma unroll
+        for (int rr = 0; rr < 4; rr++)
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+                double t = 0.0;
+#pragma unroll
+                for (int q2 = 0; q2 < 4; q2++) t = fma(cv[rr][q2], -D[q2][q], t);
+                Tm[rr][q] = t;
+            }
+#pragma unroll
+        for (int rr = 0; rr < 4; rr++)
+#pragma unroll
+            for (int cc = 0; cc < 8; cc++) {
+                double t = a[rr][cc];
+#pragma unroll
+                for (int q = 0; q < 4; q++) t = fma(-Tm[rr][q], rv[q][cc], t);
+                a[rr][cc] = t;
+            }
+        if (own_r) {
+#pragma unroll
+            for (int q = 0; q < 4; q++)
 #pragma unroll
                 for (int cc = 0; cc < 8; cc++) {
-                    double t = a[rr][cc];
+                    double t = 0.0;
 #pragma unroll
-                    for (int q = 0; q < 4; q++) t = fma(-Tm[rr][q], rv[q][cc], t);
-                    a[rr][cc] = t;
+                    for (int q2 = 0; q2 < 4; q2++) t = fma(-D[q][q2], rv[q2][cc], t);
+                    a[q][cc] = t;
                 }
-            if (tr == jb) {
+        }
+        if (own_c) {
 #pragma unroll
-                for (int q = 0; q < 4; q++)
+            for (int rr = 0; rr < 4; rr++)
 #pragma unroll
-                    for (int cc = 0; cc < 8; cc++) {
-                        double t = 0.0;
-#pragma unroll
-                        for (int q2 = 0; q2 < 4; q2++) t = fma(-D[q][q2], rv[q2][cc], t);
-                        a[jo + q][cc] = t;
-                    }
-            }
-            if (tc == jb) {
-#pragma unroll
-                for (int rr = 0; rr < 8; rr++)
-#pragma unroll
-                    for (int q = 0; q < 4; q++) a[rr][jo + q] = Tm[rr][q];
-            }
-            if (tr == jb && tc == jb) {
-#pragma unroll
-                for (int q = 0; q < 4; q++)
-#pragma unroll
-                    for (int q2 = 0; q2 < 4; q2++) a[jo + q][jo + q2] = D[q][q2];
-            }
+                for (int cc = 0; cc < 8; cc++) {
+                    const double v = own_r ? D[rr][cc & 3] : Tm[rr][cc & 3];
+                    a[rr][cc] = ((cc >> 2) == (jb & 1)) ? v : a[rr][cc];
+                }
         }
     }
     // the swept block holds -P^{-1}
     double* out = Pinv + z * GJ_NB * GJ_NB;
 #pragma unroll
-    for (int rr = 0; rr < 8; rr++)
+    for (int rr = 0; rr < 4; rr++)
 #pragma unroll
-        for (int cc = 0; cc < 8; cc++) out[(8 * tr + rr) * GJ_NB + 8 * tc + cc] = -a[rr][cc];
+        for (int cc = 0; cc < 8; cc++) out[(4 * tr + rr) * GJ_NB + 8 * tc + cc] = -a[rr][cc];
     __syncthreads();
     if (tid == 0 && bad && info && info[z] == 0) info[z] = (int32_t)(k0 + bad);
 }
@@ -248,7 +257,7 @@ static kq_status gj_inverse_batched(double* A, int64_t n, int64_t lda, int64_t s
         const int nbk = (int)((n - k0) < GJ_NB ? (n - k0) : GJ_NB);
         hipLaunchKernelGGL(gj_gather_kernel, gr, dim3(256), 0, st, A, n, lda, sA, k0, nbk, C, sC, skip);
         KQ_TRY(check_launch("gj_gather"));
-        hipLaunchKernelGGL(gj_pivot_kernel, dim3((unsigned)batch), dim3(256), 0, st, C, sC, k0, nbk, Pinv, info, skip);
+        hipLaunchKernelGGL(gj_pivot_kernel, dim3((unsigned)batch), dim3(GJ_PIV_THREADS), 0, st, C, sC, k0, nbk, Pinv, info, skip);
         KQ_TRY(check_launch("gj_pivot"));
         // T = C Pinv
         GemmArgs<double> t = gemm_args<double>(n, nbk, nbk, C, GJ_NB, Pinv, GJ_NB, T, GJ_NB, 1.0, 0.0);
@@ -267,8 +276,11 @@ static kq_status gj_inverse_batched(double* A, int64_t n, int64_t lda, int64_t s
 }
 
 // ---------------------------------------------------------------------------------- DB kernels
-constexpr int DB_MAXIT = 10;  // 8 steps suffice for cond(A) <= 1e16 even with the loose norm bounds
-constexpr double DB_TOL = 1e-10;
+// With x-interval bound b after a step, the eigenvalues of Y are within about (b - 1) of those of
+// A^{1/2} (relative); 1e-8 is well below the fp32 rounding of the stored S. The bound recursion
+// reaches it within 7 steps for any cond(A) <= 1e16 even with the loose norm bounds.
+constexpr int DB_MAXIT = 8;
+constexpr double DB_TOL = 1e-8;
 constexpr int NORM_PARTS = 32;
 
 __global__ void db_init_kernel(const float* HG, int64_t n, int64_t nbk, double* YZ, int* flags) {
@@ -333,6 +345,7 @@ constexpr int DB_UPD_BLOCKS = 1024;
 __global__ void db_update_kernel(double* YZ, const double* NINV, const double* mu, int64_t n, int64_t nbk, double* part,
                                  const int* flags) {
     if (flags[0]) return;
+    const bool first = flags[1] == 0;
     __shared__ double sd[256], sn[256];
     const int64_t nn = n * n, tri = n * (n + 1) / 2;
     double acc_d = 0, acc_n = 0;
@@ -346,7 +359,9 @@ __global__ void db_update_kernel(double* YZ, const double* NINV, const double* m
         const double m = mu[b];
         double* Y = YZ + b * nn;
         double* Z = YZ + (nbk + b) * nn;
-        const double yi = -NINV[b * nn + r * n + c], zi = -NINV[(nbk + b) * nn + r * n + c];
+        // Z_0 = I: the first step needs no inverse of Z
+        const double yi = -NINV[b * nn + r * n + c];
+        const double zi = first ? (r == c ? 1.0 : 0.0) : -NINV[(nbk + b) * nn + r * n + c];
         const double y = Y[r * n + c], zz = Z[r * n + c];
         const double yn = 0.5 * (m * y + zi / m);
         const double zn = 0.5 * (m * zz + yi / m);
@@ -375,8 +390,7 @@ __global__ void db_update_kernel(double* YZ, const double* NINV, const double* m
 }
 
 // flags[0]: done, flags[1]: steps taken. Done when every block's interval bound is within DB_TOL of
-// 1 and the last step moved Y by less than 1e-6 (relative); a failed pivot or a non-finite value
-// stops the iteration and is reported through info.
+// 1; a failed pivot or a non-finite value stops the iteration and is reported through info.
 __global__ void db_converge_kernel(const double* part, const double* bnd, int64_t nbk, int* flags,
                                    const int32_t* finfo, int64_t nitems, int32_t* info) {
     if (flags[0] || threadIdx.x != 0) return;
@@ -390,7 +404,7 @@ __global__ void db_converge_kernel(const double* part, const double* bnd, int64_
     const double rel = sqrt(d / nn);
     if (bad) { *info = bad; flags[0] = 1; return; }
     if (!(rel == rel) || !(nn > 0) || !(bmax == bmax)) { *info = 1; flags[0] = 1; return; }
-    if (bmax < DB_TOL && rel < 1e-6) flags[0] = 1;
+    if (bmax < DB_TOL) flags[0] = 1;
 }
 
 __global__ void db_out_kernel(const double* YZ, int64_t n, int64_t nbk, float* S, float* Si) {
@@ -487,9 +501,11 @@ extern "C" kq_status kq_hg_sqrt(const float* HG, kq_hg_form form, int64_t o, int
     KQ_TRY(check_launch("db_norm"));
     const unsigned cb = (unsigned)((items * nn + 255) / 256 < 4096 ? (items * nn + 255) / 256 : 4096);
     for (int it = 0; it < DB_MAXIT; it++) {
-        hipLaunchKernelGGL(copy_d_kernel, dim3(cb), dim3(256), 0, st, YZ, NI, items * nn, done);
+        // the first step inverts Y_0 = A only (Z_0 = I)
+        const size_t inv_items = it == 0 ? (size_t)nbk : items;
+        hipLaunchKernelGGL(copy_d_kernel, dim3(cb), dim3(256), 0, st, YZ, NI, inv_items * nn, done);
         KQ_TRY(check_launch("db_copy"));
-        KQ_TRY(gj_inverse_batched(NI, n, n, (int64_t)nn, (int64_t)items, C, T, Pinv, finfo, done, st));
+        KQ_TRY(gj_inverse_batched(NI, n, n, (int64_t)nn, (int64_t)inv_items, C, T, Pinv, finfo, done, st));
         // ||A^{-1}||_F of Y_0 = A (first step only; NI holds -A^{-1})
         hipLaunchKernelGGL(sym_norm_part_kernel, dim3(NORM_PARTS, (unsigned)nbk), dim3(256), 0, st, NI, n, (int64_t)nn,
                            nrmI, flags, 0);
