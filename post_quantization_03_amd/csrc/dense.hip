@@ -240,6 +240,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs<T> g) {
 template <typename T>
 kq_status gemm(const GemmArgs<T>& g, bool ta, bool tb, hipStream_t st) {
     if (g.M <= 0 || g.N <= 0) return KQ_OK;
+    if (g.focus >= 0 || g.skip_tile2 >= 0) return fail(KQ_EUNSUPPORTED, "gemm: tile focus is fp64-only");
     constexpr int VN = 16 / sizeof(T);
     const bool vec = aligned16(g.A) && aligned16(g.B) && g.lda % VN == 0 && g.ldb % VN == 0 &&
                      g.sA1 % VN == 0 && g.sA2 % VN == 0 && g.sB1 % VN == 0 && g.sB2 % VN == 0;
@@ -286,7 +287,11 @@ __global__ __launch_bounds__(256) void dgemm_valu_kernel(GemmArgs<double> g) {
     __shared__ __align__(16) double Bs[2][BK][BN + PAD];
     const int tid = threadIdx.x, tr = tid >> 4, tc = tid & 15;
     int64_t tm, tn;
-    {
+    if (g.focus >= 0) {
+        // lower triangle, tile row `focus` (tiles (f, 0..f)) then tile column `focus` below it
+        const int64_t lid = blockIdx.x, f = g.focus;
+        if (lid <= f) { tm = f; tn = lid; } else { tm = lid; tn = f; }
+    } else {
         const int64_t nx = (g.N + BN - 1) / BN;
         const int64_t L = g.tri ? (int64_t)gridDim.x : (int64_t)gridDim.x * gridDim.y;
         int64_t lid = g.tri ? (int64_t)blockIdx.x : (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
@@ -304,6 +309,7 @@ __global__ __launch_bounds__(256) void dgemm_valu_kernel(GemmArgs<double> g) {
     }
     const int64_t m0 = tm * BM, n0 = tn * BN;
     if (g.skip_tile >= 0 && ((m0 >> 7) == g.skip_tile || (n0 >> 7) == g.skip_tile)) return;
+    if (g.skip_tile2 >= 0 && ((m0 >> 7) == g.skip_tile2 || (n0 >> 7) == g.skip_tile2)) return;
     const int64_t z = blockIdx.z, z1 = z / g.nb2, z2 = z % g.nb2;
     const double* __restrict__ A = g.A + z1 * g.sA1 + z2 * g.sA2;
     const double* __restrict__ B = g.B + z1 * g.sB1 + z2 * g.sB2;
@@ -431,7 +437,44 @@ __global__ __launch_bounds__(256) void dgemm_valu_kernel(GemmArgs<double> g) {
         }
     }
 
-    // epilogue, one row half at a time: the C loads of a half are issued before any is used
+    // Epilogue. Full tiles that lie inside the stored triangle, without sign vectors, take 16-byte
+    // loads and stores of C; every other tile goes element by element with the bounds checks.
+    const bool cvec = ((reinterpret_cast<uintptr_t>(C) & 15) == 0) && ((g.ldc & 1) == 0);
+    if (cvec && fullMN && !rs && !cs && (g.tri == 0 || tm != tn)) {
+        const double alpha = g.alpha, beta = g.beta;
+#pragma unroll
+        for (int hi = 0; hi < 2; hi++) {
+            V16<double> cv[RG][2][CG / 2];
+            if (beta != 0.0) {
+#pragma unroll
+                for (int i = 0; i < RG; i++)
+#pragma unroll
+                    for (int hj = 0; hj < 2; hj++)
+#pragma unroll
+                        for (int j = 0; j < CG; j += 2) {
+                            const int64_t m = m0 + hi * (BM / 2) + tr * RG + i, n = n0 + hj * (BN / 2) + tc * CG + j;
+                            cv[i][hj][j / 2] = *reinterpret_cast<const V16<double>*>(C + m * g.ldc + n);
+                        }
+            }
+#pragma unroll
+            for (int i = 0; i < RG; i++)
+#pragma unroll
+                for (int hj = 0; hj < 2; hj++)
+#pragma unroll
+                    for (int j = 0; j < CG; j += 2) {
+                        const int64_t m = m0 + hi * (BM / 2) + tr * RG + i, n = n0 + hj * (BN / 2) + tc * CG + j;
+                        V16<double> v;
+                        v.v[0] = alpha * acc[hi][i][hj][j];
+                        v.v[1] = alpha * acc[hi][i][hj][j + 1];
+                        if (beta != 0.0) {
+                            v.v[0] = fma(beta, cv[i][hj][j / 2].v[0], v.v[0]);
+                            v.v[1] = fma(beta, cv[i][hj][j / 2].v[1], v.v[1]);
+                        }
+                        *reinterpret_cast<V16<double>*>(C + m * g.ldc + n) = v;
+                    }
+        }
+        return;
+    }
 #pragma unroll
     for (int hi = 0; hi < 2; hi++) {
         double cv[RG][2][CG];
@@ -468,7 +511,8 @@ __global__ __launch_bounds__(256) void dgemm_valu_kernel(GemmArgs<double> g) {
 template <int BM, int BN>
 static void dgemm_launch(const GemmArgs<double>& g, bool ta, bool tb, bool vec, hipStream_t st) {
     const int64_t nx = (g.N + BN - 1) / BN, ny = (g.M + BM - 1) / BM;
-    const dim3 grid((unsigned)(g.tri ? nx * (nx + 1) / 2 : nx), (unsigned)(g.tri ? 1 : ny), (unsigned)(g.nb1 * g.nb2));
+    const dim3 grid((unsigned)(g.focus >= 0 ? nx : g.tri ? nx * (nx + 1) / 2 : nx), (unsigned)(g.tri ? 1 : ny),
+                    (unsigned)(g.nb1 * g.nb2));
 #define KQ_DG(TA_, TB_, V_) hipLaunchKernelGGL((dgemm_valu_kernel<BM, BN, TA_, TB_, V_>), grid, dim3(256), 0, st, g)
     if (vec) {
         if (!ta && !tb) KQ_DG(false, false, true);
@@ -494,8 +538,9 @@ kq_status gemm<double>(const GemmArgs<double>& g, bool ta, bool tb, hipStream_t 
     if (batch > 65535) return fail(KQ_ESHAPE, "gemm: batch too large");
     const int64_t nx = (g.N + 127) / 128, ny = (g.M + 127) / 128;
     if (g.tri && nx != ny) return fail(KQ_ESHAPE, "gemm: triangular products need a square tile grid");
+    if (g.focus >= 0 && (g.tri != 1 || g.focus >= nx)) return fail(KQ_EINVAL, "gemm: bad tile focus");
     const int64_t tiles = (g.tri ? nx * (nx + 1) / 2 : nx * ny) * batch;
-    const bool big = tiles >= 256;
+    const bool big = tiles >= 256 || g.focus >= 0;
     const int64_t ty = big ? ny : (g.M + 63) / 64;
     if (!g.tri && ty > 65535) return fail(KQ_ESHAPE, "gemm grid too large");
     if (g.tri && ((g.N + 63) / 64) != ((g.M + 63) / 64)) return fail(KQ_ESHAPE, "gemm: triangular products need a square tile grid");

@@ -15,6 +15,7 @@
 // then T and -P^{-1} are scattered back. After all pivots A holds -A^{-1}. Y and Z of every block are
 // one batch.
 #include <cmath>
+#include <mutex>
 
 #include "kq_internal.h"
 
@@ -72,62 +73,70 @@ __device__ inline double recip64(double p) {
     return fma(r, fma(-p, r, 1.0), r);
 }
 
-// Pinv = P^{-1} for the nbk x nbk pivot P = C[k0 : k0 + nbk][0 : nbk] (identity-padded to 128) by a
-// Gauss-Jordan sweep held in registers: 512 threads, thread (tr, tc) owns rows 4tr..4tr+3 and
-// columns 8tc..8tc+7 (two waves per SIMD). Pivots are taken four at a time: the 4 pivot rows and
-// columns go through LDS (double-buffered, one barrier per step), every thread inverts the 4 x 4
-// pivot block itself and applies the rank-4 update
-//     A_RR -= A_RJ D^{-1} A_JR,  A_RJ <- A_RJ D^{-1},  A_JR <- D^{-1} A_JR,  A_JJ <- -D^{-1}.
+// Pinv = P^{-1} for the nbk x nbk SPD pivot P = C[k0 : k0 + nbk][0 : nbk] (identity-padded to 128) by
+// a Gauss-Jordan sweep held in registers: 512 threads, thread (tr, tc) owns rows 4tr..4tr+3 and
+// columns 8tc..8tc+7 (two waves per SIMD). Pivots are taken four at a time (J = 4jb..4jb+3, pivot
+// block D = A_JJ) with the symmetric sweep
+//     A_RR -= A_RJ D^{-1} A_JR,  A_RJ <- A_RJ D^{-1},  A_JR <- D^{-1} A_JR,  A_JJ <- -D^{-1},
+// which keeps A symmetric. All four cases are one rank-4 update A -= (A_.J - E_.J) D^{-1} (A_J. - E_J.)
+// (E the identity) followed by A_JJ -= 2I, so every thread runs the same code: the owners of the
+// pivot rows put A_J. - E_J. in LDS (one barrier per step, double-buffered), every thread reads its
+// column factor from those rows by symmetry, inverts the 4 x 4 block itself and updates its tile.
+// The block is first scaled to unit diagonal (A = S P S, S = diag(P)^{-1/2}); every pivot block of
+// the sweep is then a Schur complement with entries of magnitude <= 1, so the identity shifts cancel
+// nothing larger than the result. After the last step the registers hold -A^{-1}, and
+// P^{-1} = S A^{-1} S.
 constexpr int GJ_PIV_THREADS = 512;
 __global__ __launch_bounds__(GJ_PIV_THREADS) void gj_pivot_kernel(const double* __restrict__ C, int64_t sC,
                                                                   int64_t k0, int nbk, double* __restrict__ Pinv,
                                                                   int32_t* info, const int* skip) {
     if (skip && *skip) return;
     __shared__ __align__(16) double rowb[2][4][GJ_NB];
-    __shared__ __align__(16) double colb[2][GJ_NB][4];
-    __shared__ int bad;
     const int tid = threadIdx.x, tr = tid >> 4, tc = tid & 15;
     const int64_t z = blockIdx.x;
     const double* P = C + z * sC + k0 * GJ_NB;
+    int bad = 0;  // first non-positive pivot (1-based), tracked by every thread alike
+    double sr[4], sc[8];
+#pragma unroll
+    for (int rr = 0; rr < 4; rr++) {
+        const int r = 4 * tr + rr;
+        const double p = r < nbk ? P[r * GJ_NB + r] : 1.0;
+        sr[rr] = p > 0.0 ? 1.0 / sqrt(p) : 1.0;
+    }
+#pragma unroll
+    for (int cc = 0; cc < 8; cc++) {
+        const int c = 8 * tc + cc;
+        const double p = c < nbk ? P[c * GJ_NB + c] : 1.0;
+        sc[cc] = p > 0.0 ? 1.0 / sqrt(p) : 1.0;
+    }
     double a[4][8];
 #pragma unroll
     for (int rr = 0; rr < 4; rr++)
 #pragma unroll
         for (int cc = 0; cc < 8; cc++) {
             const int r = 4 * tr + rr, c = 8 * tc + cc;
-            a[rr][cc] = (r < nbk && c < nbk) ? P[r * GJ_NB + c] : (r == c ? 1.0 : 0.0);
+            a[rr][cc] = (r < nbk && c < nbk) ? P[r * GJ_NB + c] * sr[rr] * sc[cc] : (r == c ? 1.0 : 0.0);
         }
-    if (tid == 0) bad = 0;
     for (int jb = 0; jb < 32; jb++) {
-        const int j0 = 4 * jb, buf = jb & 1, jo = (jb & 1) * 4;
-        const bool own_r = tr == jb, own_c = tc == (jb >> 1);
-        if (own_r) {
+        const int j0 = 4 * jb, buf = jb & 1;
+        if (tr == jb) {
 #pragma unroll
             for (int q = 0; q < 4; q++)
 #pragma unroll
-                for (int cc = 0; cc < 8; cc++) rowb[buf][q][8 * tc + cc] = a[q][cc];
-        }
-        if (own_c) {
-#pragma unroll
-            for (int rr = 0; rr < 4; rr++)
-#pragma unroll
-                for (int q = 0; q < 4; q++) {
-                    const double lo = a[rr][q], hi = a[rr][4 + q];  // value selects keep a[][] in registers
-                    colb[buf][4 * tr + rr][q] = jo ? hi : lo;
-                }
+                for (int cc = 0; cc < 8; cc++) rowb[buf][q][8 * tc + cc] = a[q][cc] - (8 * tc + cc == j0 + q ? 1.0 : 0.0);
         }
         __syncthreads();
-        // 4 x 4 pivot block and its inverse (unpivoted Gauss-Jordan; SPD pivots are positive)
+        // D = A_JJ and its inverse (unpivoted Gauss-Jordan; SPD pivots are positive)
         double D[4][4];
 #pragma unroll
         for (int q = 0; q < 4; q++)
 #pragma unroll
-            for (int q2 = 0; q2 < 4; q2++) D[q][q2] = rowb[buf][q][j0 + q2];
+            for (int q2 = 0; q2 < 4; q2++) D[q][q2] = rowb[buf][q][j0 + q2] + (q == q2 ? 1.0 : 0.0);
 #pragma unroll
         for (int t = 0; t < 4; t++) {
             double p = D[t][t];
             if (!(p > 0.0)) {
-                if (tid == 0 && !bad) bad = j0 + t + 1;
+                bad = bad ? bad : j0 + t + 1;
                 p = 1.0;
             }
             const double ip = recip64(p);
@@ -138,56 +147,41 @@ __global__ __launch_bounds__(GJ_PIV_THREADS) void gj_pivot_kernel(const double* 
                     if (q != t && q2 != t) D[q][q2] = fma(-D[q][t] * ip, D[t][q2], D[q][q2]);
 #pragma unroll
             for (int q = 0; q < 4; q++)
-                if (q != t) { D[q][t] *= ip; D[t][q] *= ip; }
-            D[t][t] = -ip;
+                if (q != t) { D[q][t] *= -ip; D[t][q] *= ip; }
+            D[t][t] = ip;
         }
-        // D now holds -D^{-1}
-        double cv[4][4], rv[4][8], Tm[4][4];
+        // D now holds D^{-1}; Tm = (A_RJ - E_RJ) D^{-1} with A_RJ read from the pivot rows (symmetry)
+        double Tm[4][4];
 #pragma unroll
-        for (int rr = 0; rr < 4; rr++)
+        for (int rr = 0; rr < 4; rr++) {
+            double cv[4];
 #pragma unroll
-            for (int q = 0; q < 4; q++) cv[rr][q] = colb[buf][4 * tr + rr][q];
-#pragma unroll
-        for (int q = 0; q < 4; q++)
-#pragma unroll
-            for (int cc = 0; cc < 8; cc++) rv[q][cc] = rowb[buf][q][8 * tc + cc];
-#pragma unroll
-        for (int rr = 0; rr < 4; rr++)
+            for (int q = 0; q < 4; q++) cv[q] = rowb[buf][q][4 * tr + rr];
 #pragma unroll
             for (int q = 0; q < 4; q++) {
                 double t = 0.0;
 #pragma unroll
-                for (int q2 = 0; q2 < 4; q2++) t = fma(cv[rr][q2], -D[q2][q], t);
+                for (int q2 = 0; q2 < 4; q2++) t = fma(cv[q2], D[q2][q], t);
                 Tm[rr][q] = t;
             }
-#pragma unroll
-        for (int rr = 0; rr < 4; rr++)
-#pragma unroll
-            for (int cc = 0; cc < 8; cc++) {
-                double t = a[rr][cc];
-#pragma unroll
-                for (int q = 0; q < 4; q++) t = fma(-Tm[rr][q], rv[q][cc], t);
-                a[rr][cc] = t;
-            }
-        if (own_r) {
-#pragma unroll
-            for (int q = 0; q < 4; q++)
-#pragma unroll
-                for (int cc = 0; cc < 8; cc++) {
-                    double t = 0.0;
-#pragma unroll
-                    for (int q2 = 0; q2 < 4; q2++) t = fma(-D[q][q2], rv[q2][cc], t);
-                    a[q][cc] = t;
-                }
         }
-        if (own_c) {
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+            double rv[8];
+#pragma unroll
+            for (int cc = 0; cc < 8; cc++) rv[cc] = rowb[buf][q][8 * tc + cc];
 #pragma unroll
             for (int rr = 0; rr < 4; rr++)
 #pragma unroll
-                for (int cc = 0; cc < 8; cc++) {
-                    const double v = own_r ? D[rr][cc & 3] : Tm[rr][cc & 3];
-                    a[rr][cc] = ((cc >> 2) == (jb & 1)) ? v : a[rr][cc];
-                }
+                for (int cc = 0; cc < 8; cc++) a[rr][cc] = fma(-Tm[rr][q], rv[cc], a[rr][cc]);
+        }
+        if (tr == jb && tc == (jb >> 1)) {
+            const int jo = (jb & 1) * 4;
+#pragma unroll
+            for (int q = 0; q < 4; q++)
+#pragma unroll
+                for (int cc = 0; cc < 8; cc++)
+                    if (cc == jo + q) a[q][cc] -= 2.0;
         }
     }
     // the swept block holds -P^{-1}
@@ -195,8 +189,7 @@ __global__ __launch_bounds__(GJ_PIV_THREADS) void gj_pivot_kernel(const double* 
 #pragma unroll
     for (int rr = 0; rr < 4; rr++)
 #pragma unroll
-        for (int cc = 0; cc < 8; cc++) out[(4 * tr + rr) * GJ_NB + 8 * tc + cc] = -a[rr][cc];
-    __syncthreads();
+        for (int cc = 0; cc < 8; cc++) out[(4 * tr + rr) * GJ_NB + 8 * tc + cc] = -a[rr][cc] * sr[rr] * sc[cc];
     if (tid == 0 && bad && info && info[z] == 0) info[z] = (int32_t)(k0 + bad);
 }
 
@@ -246,32 +239,106 @@ __global__ __launch_bounds__(256) void gj_scatter_kernel(double* __restrict__ A,
     }
 }
 
+// Second queue of a device for the look-ahead of the sweep (default priority). The events order its
+// work with the caller's stream; the mutex keeps the event sequence of one call intact when several
+// host threads enqueue at once.
+struct SideQueue {
+    hipStream_t s = nullptr;
+    hipEvent_t ev[6] = {};
+    bool ok = false;
+};
+static std::mutex g_side_mu;
+static SideQueue g_side[64];
+
+static kq_status side_queue(SideQueue** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return fail(KQ_EHIP, "side queue: no device");
+    SideQueue& q = g_side[dev];
+    if (!q.ok) {
+        if (hipStreamCreateWithFlags(&q.s, hipStreamNonBlocking) != hipSuccess)
+            return fail(KQ_EHIP, "side queue: stream creation failed");
+        for (hipEvent_t& e : q.ev)
+            if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess)
+                return fail(KQ_EHIP, "side queue: event creation failed");
+        q.ok = true;
+    }
+    *out = &q;
+    return KQ_OK;
+}
+
+#define KQ_HIP(expr)                                                                    \
+    do {                                                                                \
+        if ((expr) != hipSuccess) return fail(KQ_EHIP, "%s failed", #expr);            \
+    } while (0)
+
 // A <- -A^{-1} for a batch of SPD matrices stored in their lower triangles (n x n, leading dimension
-// lda, item stride sA). Scratch: C, T (batch x n x 128) and Pinv (batch x 128 x 128).
-static kq_status gj_inverse_batched(double* A, int64_t n, int64_t lda, int64_t sA, int64_t batch, double* C, double* T,
-                                    double* Pinv, int32_t* info, const int* skip, hipStream_t st) {
+// lda, item stride sA). Scratch (two of each, alternating by pivot): panels C and T
+// (batch x n x 128) and Pinv (batch x 128 x 128).
+//
+// Look-ahead: the pivot block k + 1 depends on the update of step k only through tile row / column
+// k + 1. The side queue updates those tiles first ("panel"), scatters step k, gathers panel k + 1,
+// inverts its pivot and forms T_{k+1}, while the caller's stream applies the rest of step k's update
+// (every tile outside rows / columns k and k + 1). Both queues touch disjoint tiles and read the
+// panel buffers of their own step.
+static kq_status gj_inverse_batched(double* A, int64_t n, int64_t lda, int64_t sA, int64_t batch, double* const C[2],
+                                    double* const T[2], double* const Pinv[2], int32_t* info, const int* skip,
+                                    hipStream_t st) {
     if (batch > 65535) return fail(KQ_ESHAPE, "sweep batch too large");
     const int64_t sC = n * GJ_NB;
+    const int64_t nt = (n + GJ_NB - 1) / GJ_NB;
     const dim3 gr((unsigned)((n + GJ_RT - 1) / GJ_RT), (unsigned)batch);
-    for (int64_t k0 = 0, kt = 0; k0 < n; k0 += GJ_NB, kt++) {
-        const int nbk = (int)((n - k0) < GJ_NB ? (n - k0) : GJ_NB);
-        hipLaunchKernelGGL(gj_gather_kernel, gr, dim3(256), 0, st, A, n, lda, sA, k0, nbk, C, sC, skip);
+    std::lock_guard<std::mutex> lock(g_side_mu);
+    SideQueue* q = nullptr;
+    KQ_TRY(side_queue(&q));
+    hipStream_t sb = q->s;
+    hipEvent_t ev0 = q->ev[0], evA[2] = {q->ev[1], q->ev[2]}, evB[2] = {q->ev[3], q->ev[4]}, evEnd = q->ev[5];
+    auto nb_of = [&](int64_t k) { return (int)((n - k * GJ_NB) < GJ_NB ? (n - k * GJ_NB) : GJ_NB); };
+    // gather panel k, invert its pivot, T = C Pinv; all on the side queue
+    auto prepare = [&](int64_t k) -> kq_status {
+        const int b = (int)(k & 1), nbk = nb_of(k);
+        const int64_t k0 = k * GJ_NB;
+        hipLaunchKernelGGL(gj_gather_kernel, gr, dim3(256), 0, sb, A, n, lda, sA, k0, nbk, C[b], sC, skip);
         KQ_TRY(check_launch("gj_gather"));
-        hipLaunchKernelGGL(gj_pivot_kernel, dim3((unsigned)batch), dim3(GJ_PIV_THREADS), 0, st, C, sC, k0, nbk, Pinv, info, skip);
+        hipLaunchKernelGGL(gj_pivot_kernel, dim3((unsigned)batch), dim3(GJ_PIV_THREADS), 0, sb, C[b], sC, k0, nbk,
+                           Pinv[b], info, skip);
         KQ_TRY(check_launch("gj_pivot"));
-        // T = C Pinv
-        GemmArgs<double> t = gemm_args<double>(n, nbk, nbk, C, GJ_NB, Pinv, GJ_NB, T, GJ_NB, 1.0, 0.0);
+        GemmArgs<double> t = gemm_args<double>(n, nbk, nbk, C[b], GJ_NB, Pinv[b], GJ_NB, T[b], GJ_NB, 1.0, 0.0);
         t.nb1 = batch; t.sA1 = sC; t.sB1 = GJ_NB * GJ_NB; t.sC1 = sC; t.skip = skip;
-        KQ_TRY(gemm<double>(t, false, false, st));
-        // A_RR -= T C^T (lower triangle, pivot tile row/column untouched)
-        if (n > nbk) {
-            GemmArgs<double> u = gemm_args<double>(n, n, nbk, T, GJ_NB, C, GJ_NB, A, lda, -1.0, 1.0);
-            u.nb1 = batch; u.sA1 = sC; u.sB1 = sC; u.sC1 = sA; u.tri = 1; u.skip = skip; u.skip_tile = kt;
-            KQ_TRY(gemm<double>(u, false, true, st));
+        return gemm<double>(t, false, false, sb);
+    };
+    KQ_HIP(hipEventRecord(ev0, st));
+    KQ_HIP(hipStreamWaitEvent(sb, ev0, 0));
+    KQ_TRY(prepare(0));
+    KQ_HIP(hipEventRecord(evB[0], sb));
+    for (int64_t k = 0; k < nt; k++) {
+        const int cur = (int)(k & 1), nxt = cur ^ 1, nbk = nb_of(k);
+        const int64_t k0 = k * GJ_NB;
+        // side queue: tiles of row / column k + 1, scatter of step k, pivot k + 1
+        if (k > 0) KQ_HIP(hipStreamWaitEvent(sb, evA[nxt], 0));
+        if (k + 1 < nt) {
+            GemmArgs<double> u = gemm_args<double>(n, n, nbk, T[cur], GJ_NB, C[cur], GJ_NB, A, lda, -1.0, 1.0);
+            u.nb1 = batch; u.sA1 = sC; u.sB1 = sC; u.sC1 = sA; u.tri = 1; u.skip = skip; u.skip_tile = k;
+            u.focus = k + 1;
+            KQ_TRY(gemm<double>(u, false, true, sb));
         }
-        hipLaunchKernelGGL(gj_scatter_kernel, gr, dim3(256), 0, st, A, n, lda, sA, k0, nbk, T, sC, Pinv, skip);
+        hipLaunchKernelGGL(gj_scatter_kernel, gr, dim3(256), 0, sb, A, n, lda, sA, k0, nbk, T[cur], sC, Pinv[cur], skip);
         KQ_TRY(check_launch("gj_scatter"));
+        if (k + 1 < nt) {
+            KQ_TRY(prepare(k + 1));
+            KQ_HIP(hipEventRecord(evB[nxt], sb));
+        }
+        // caller's stream: the rest of step k's update, A_RR -= T C^T (lower triangle)
+        if (nt > 1) {
+            KQ_HIP(hipStreamWaitEvent(st, evB[cur], 0));
+            GemmArgs<double> u = gemm_args<double>(n, n, nbk, T[cur], GJ_NB, C[cur], GJ_NB, A, lda, -1.0, 1.0);
+            u.nb1 = batch; u.sA1 = sC; u.sB1 = sC; u.sC1 = sA; u.tri = 1; u.skip = skip; u.skip_tile = k;
+            u.skip_tile2 = k + 1 < nt ? k + 1 : -1;
+            KQ_TRY(gemm<double>(u, false, true, st));
+            KQ_HIP(hipEventRecord(evA[cur], st));
+        }
     }
+    KQ_HIP(hipEventRecord(evEnd, sb));
+    KQ_HIP(hipStreamWaitEvent(st, evEnd, 0));
     return KQ_OK;
 }
 
@@ -435,9 +502,11 @@ static void hg_layout(Ar& a, int64_t n, int64_t nbk) {
     const size_t nn = (size_t)n * n, items = 2 * (size_t)nbk;
     a.template take<double>(items * nn);                     // YZ
     a.template take<double>(items * nn);                     // sweep buffer (-inverses)
-    a.template take<double>(items * n * GJ_NB);              // C
-    a.template take<double>(items * n * GJ_NB);              // T
-    a.template take<double>(items * GJ_NB * GJ_NB);          // Pinv
+    for (int b = 0; b < 2; b++) {
+        a.template take<double>(items * n * GJ_NB);          // C
+        a.template take<double>(items * n * GJ_NB);          // T
+        a.template take<double>(items * GJ_NB * GJ_NB);      // Pinv
+    }
     a.template take<double>((size_t)nbk * NORM_PARTS);       // ||A||_F^2 parts
     a.template take<double>(items * NORM_PARTS);             // ||A^{-1}||_F^2 parts
     a.template take<double>(nbk);                            // mu
@@ -479,9 +548,12 @@ extern "C" kq_status kq_hg_sqrt(const float* HG, kq_hg_form form, int64_t o, int
     const size_t nn = (size_t)n * n, items = 2 * (size_t)nbk;
     double* YZ = ar.take<double>(items * nn);
     double* NI = ar.take<double>(items * nn);
-    double* C = ar.take<double>(items * n * GJ_NB);
-    double* T = ar.take<double>(items * n * GJ_NB);
-    double* Pinv = ar.take<double>(items * GJ_NB * GJ_NB);
+    double *C[2], *T[2], *Pinv[2];
+    for (int b = 0; b < 2; b++) {
+        C[b] = ar.take<double>(items * n * GJ_NB);
+        T[b] = ar.take<double>(items * n * GJ_NB);
+        Pinv[b] = ar.take<double>(items * GJ_NB * GJ_NB);
+    }
     double* nrmA = ar.take<double>((size_t)nbk * NORM_PARTS);
     double* nrmI = ar.take<double>(items * NORM_PARTS);
     double* mu = ar.take<double>(nbk);

@@ -67,7 +67,10 @@ struct GemmArgs {
     const int8_t* csign; int64_t sS1, sS2;
     int tri, kmode;
     const int* skip;   // device flag: when nonzero every work-group returns at once (may be null)
-    int64_t skip_tile; // tile row and tile column to leave untouched (-1: none)
+    int64_t skip_tile; // tile row and tile column (128-wide) to leave untouched (-1: none)
+    int64_t skip_tile2;// a second one (-1: none)
+    int64_t focus;     // fp64 lower-triangular products only: launch just the 128-wide tile row and
+                       // column `focus` (-1: all tiles)
 };
 
 template <typename T>
@@ -76,7 +79,7 @@ GemmArgs<T> gemm_args(int64_t M, int64_t N, int64_t K, const T* A, int64_t lda, 
     GemmArgs<T> g{};
     g.M = M; g.N = N; g.K = K;
     g.A = A; g.lda = lda; g.B = B; g.ldb = ldb; g.C = C; g.ldc = ldc;
-    g.nb1 = 1; g.nb2 = 1; g.alpha = alpha; g.beta = beta; g.skip_tile = -1;
+    g.nb1 = 1; g.nb2 = 1; g.alpha = alpha; g.beta = beta; g.skip_tile = -1; g.skip_tile2 = -1; g.focus = -1;
     return g;
 }
 
