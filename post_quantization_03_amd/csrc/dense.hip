@@ -288,9 +288,19 @@ __global__ __launch_bounds__(256) void dgemm_valu_kernel(GemmArgs<double> g) {
     const int tid = threadIdx.x, tr = tid >> 4, tc = tid & 15;
     int64_t tm, tn;
     if (g.focus >= 0) {
-        // lower triangle, tile row `focus` (tiles (f, 0..f)) then tile column `focus` below it
-        const int64_t lid = blockIdx.x, f = g.focus;
-        if (lid <= f) { tm = f; tn = lid; } else { tm = lid; tn = f; }
+        // lower triangle: the BM-tile rows of the 128-wide row `focus` (tiles (i, 0..i)), then its
+        // BM-tile columns below them
+        constexpr int64_t R = 128 / BM;
+        const int64_t ntm = (g.M + BM - 1) / BM, f0 = g.focus * R;
+        const int64_t rf = ntm - f0 < R ? ntm - f0 : R;
+        int64_t lid = blockIdx.x;
+        tm = -1;
+        tn = 0;
+        for (int64_t q = 0; q < rf && tm < 0; q++) {
+            if (lid <= f0 + q) { tm = f0 + q; tn = lid; }
+            else lid -= f0 + q + 1;
+        }
+        if (tm < 0) { tm = f0 + rf + lid / rf; tn = f0 + lid % rf; }
     } else {
         const int64_t nx = (g.N + BN - 1) / BN;
         const int64_t L = g.tri ? (int64_t)gridDim.x : (int64_t)gridDim.x * gridDim.y;
@@ -511,8 +521,14 @@ __global__ __launch_bounds__(256) void dgemm_valu_kernel(GemmArgs<double> g) {
 template <int BM, int BN>
 static void dgemm_launch(const GemmArgs<double>& g, bool ta, bool tb, bool vec, hipStream_t st) {
     const int64_t nx = (g.N + BN - 1) / BN, ny = (g.M + BM - 1) / BM;
-    const dim3 grid((unsigned)(g.focus >= 0 ? nx : g.tri ? nx * (nx + 1) / 2 : nx), (unsigned)(g.tri ? 1 : ny),
-                    (unsigned)(g.nb1 * g.nb2));
+    int64_t gx = g.tri ? nx * (nx + 1) / 2 : nx;
+    if (g.focus >= 0) {  // tiles of the focus rows, then the focus columns below them
+        const int64_t R = 128 / BM, f0 = g.focus * R, rf = ny - f0 < R ? ny - f0 : R;
+        gx = 0;
+        for (int64_t q = 0; q < rf; q++) gx += f0 + q + 1;
+        gx += rf * (ny - f0 - rf);
+    }
+    const dim3 grid((unsigned)gx, (unsigned)(g.tri ? 1 : ny), (unsigned)(g.nb1 * g.nb2));
 #define KQ_DG(TA_, TB_, V_) hipLaunchKernelGGL((dgemm_valu_kernel<BM, BN, TA_, TB_, V_>), grid, dim3(256), 0, st, g)
     if (vec) {
         if (!ta && !tb) KQ_DG(false, false, true);
@@ -540,7 +556,7 @@ kq_status gemm<double>(const GemmArgs<double>& g, bool ta, bool tb, hipStream_t 
     if (g.tri && nx != ny) return fail(KQ_ESHAPE, "gemm: triangular products need a square tile grid");
     if (g.focus >= 0 && (g.tri != 1 || g.focus >= nx)) return fail(KQ_EINVAL, "gemm: bad tile focus");
     const int64_t tiles = (g.tri ? nx * (nx + 1) / 2 : nx * ny) * batch;
-    const bool big = tiles >= 256 || g.focus >= 0;
+    const bool big = tiles >= 256 && g.focus < 0;
     const int64_t ty = big ? ny : (g.M + 63) / 64;
     if (!g.tri && ty > 65535) return fail(KQ_ESHAPE, "gemm grid too large");
     if (g.tri && ((g.N + 63) / 64) != ((g.M + 63) / 64)) return fail(KQ_ESHAPE, "gemm: triangular products need a square tile grid");

@@ -25,8 +25,11 @@ constexpr int GJ_NB = 128;
 constexpr int GJ_RT = 32;  // rows per gather/scatter work-group
 
 // Panel C[r][c] = A(r, k0 + c) of the symmetric matrix stored in its lower triangle; c >= nbk -> 0.
+// Rows p0 <= r < p1 (the previous pivot block, whose column block has not been written back yet)
+// come from that step's T instead: A(r, k0 + c) = Tp[k0 + c][r - p0].
 __global__ __launch_bounds__(256) void gj_gather_kernel(const double* __restrict__ A, int64_t n, int64_t lda, int64_t sA,
                                                         int64_t k0, int nbk, double* __restrict__ C, int64_t sC,
+                                                        const double* __restrict__ Tp, int64_t p0, int64_t p1,
                                                         const int* skip) {
     if (skip && *skip) return;
     __shared__ double tile[GJ_RT][GJ_NB + 1];
@@ -35,7 +38,18 @@ __global__ __launch_bounds__(256) void gj_gather_kernel(const double* __restrict
     A += z * sA;
     C += z * sC;
     const int64_t k1 = k0 + nbk;
-    if (r0 >= k1) {
+    if (Tp && r0 >= p0 && r0 + GJ_RT <= p1) {
+        Tp += z * sC;
+        for (int e = tid; e < GJ_RT * GJ_NB; e += 256) {
+            const int c = e / GJ_RT, rr = e % GJ_RT;
+            tile[rr][c] = c < nbk ? Tp[(k0 + c) * GJ_NB + (r0 - p0) + rr] : 0.0;
+        }
+        __syncthreads();
+        for (int e = tid; e < GJ_RT * GJ_NB; e += 256) {
+            const int rr = e / GJ_NB, c = e % GJ_NB;
+            C[(r0 + rr) * GJ_NB + c] = tile[rr][c];
+        }
+    } else if (r0 >= k1) {
         for (int e = tid; e < GJ_RT * GJ_NB; e += 256) {
             const int64_t r = r0 + e / GJ_NB;
             const int c = e % GJ_NB;
@@ -75,27 +89,59 @@ __device__ inline double recip64(double p) {
 
 // Pinv = P^{-1} for the nbk x nbk SPD pivot P = C[k0 : k0 + nbk][0 : nbk] (identity-padded to 128) by
 // a Gauss-Jordan sweep held in registers: 512 threads, thread (tr, tc) owns rows 4tr..4tr+3 and
-// columns 8tc..8tc+7 (two waves per SIMD). Pivots are taken four at a time (J = 4jb..4jb+3, pivot
+// columns 4tc..4tc+3, 64+4tc..64+4tc+3 (two waves per SIMD). Pivots are taken four at a time (J = 4jb..4jb+3, pivot
 // block D = A_JJ) with the symmetric sweep
 //     A_RR -= A_RJ D^{-1} A_JR,  A_RJ <- A_RJ D^{-1},  A_JR <- D^{-1} A_JR,  A_JJ <- -D^{-1},
 // which keeps A symmetric. All four cases are one rank-4 update A -= (A_.J - E_.J) D^{-1} (A_J. - E_J.)
-// (E the identity) followed by A_JJ -= 2I, so every thread runs the same code: the owners of the
-// pivot rows put A_J. - E_J. in LDS (one barrier per step, double-buffered), every thread reads its
-// column factor from those rows by symmetry, inverts the 4 x 4 block itself and updates its tile.
+// (E the identity) followed by A_JJ -= 2I, so every thread runs the same code: it reads the shifted
+// pivot rows A_J. - E_J. and D^{-1} from LDS, takes its column factor from those rows by symmetry and
+// updates its tile. The next step's pivot rows are written by their owners right after their update,
+// and the single thread that holds the next 4 x 4 pivot block inverts it and writes D^{-1}, so one
+// barrier per step separates the steps (LDS double-buffered).
 // The block is first scaled to unit diagonal (A = S P S, S = diag(P)^{-1/2}); every pivot block of
 // the sweep is then a Schur complement with entries of magnitude <= 1, so the identity shifts cancel
 // nothing larger than the result. After the last step the registers hold -A^{-1}, and
 // P^{-1} = S A^{-1} S.
 constexpr int GJ_PIV_THREADS = 512;
+
+// D (4 x 4, SPD) -> D^{-1} in place by unpivoted Gauss-Jordan; returns 1 + the first non-positive
+// pivot (that pivot is replaced by 1), else 0.
+__device__ inline int inv4_spd(double D[4][4]) {
+    int bad = 0;
+#pragma unroll
+    for (int t = 0; t < 4; t++) {
+        double p = D[t][t];
+        if (!(p > 0.0)) {
+            bad = bad ? bad : t + 1;
+            p = 1.0;
+        }
+        const double ip = recip64(p);
+#pragma unroll
+        for (int q = 0; q < 4; q++)
+#pragma unroll
+            for (int q2 = 0; q2 < 4; q2++)
+                if (q != t && q2 != t) D[q][q2] = fma(-D[q][t] * ip, D[t][q2], D[q][q2]);
+#pragma unroll
+        for (int q = 0; q < 4; q++)
+            if (q != t) { D[q][t] *= -ip; D[t][q] *= ip; }
+        D[t][t] = ip;
+    }
+    return bad;
+}
+
 __global__ __launch_bounds__(GJ_PIV_THREADS) void gj_pivot_kernel(const double* __restrict__ C, int64_t sC,
                                                                   int64_t k0, int nbk, double* __restrict__ Pinv,
                                                                   int32_t* info, const int* skip) {
     if (skip && *skip) return;
     __shared__ __align__(16) double rowb[2][4][GJ_NB];
+    __shared__ __align__(16) double dinv[2][4][4];
+    __shared__ int bad_s;
     const int tid = threadIdx.x, tr = tid >> 4, tc = tid & 15;
+    // column cc of the thread's tile: two runs of four, 64 apart, so that the 16 column groups of a
+    // wave read one contiguous 512-byte run per LDS instruction
+    auto col = [&](int cc) { return (cc >> 2) * 64 + 4 * tc + (cc & 3); };
     const int64_t z = blockIdx.x;
     const double* P = C + z * sC + k0 * GJ_NB;
-    int bad = 0;  // first non-positive pivot (1-based), tracked by every thread alike
     double sr[4], sc[8];
 #pragma unroll
     for (int rr = 0; rr < 4; rr++) {
@@ -105,7 +151,7 @@ __global__ __launch_bounds__(GJ_PIV_THREADS) void gj_pivot_kernel(const double* 
     }
 #pragma unroll
     for (int cc = 0; cc < 8; cc++) {
-        const int c = 8 * tc + cc;
+        const int c = col(cc);
         const double p = c < nbk ? P[c * GJ_NB + c] : 1.0;
         sc[cc] = p > 0.0 ? 1.0 / sqrt(p) : 1.0;
     }
@@ -114,43 +160,46 @@ __global__ __launch_bounds__(GJ_PIV_THREADS) void gj_pivot_kernel(const double* 
     for (int rr = 0; rr < 4; rr++)
 #pragma unroll
         for (int cc = 0; cc < 8; cc++) {
-            const int r = 4 * tr + rr, c = 8 * tc + cc;
+            const int r = 4 * tr + rr, c = col(cc);
             a[rr][cc] = (r < nbk && c < nbk) ? P[r * GJ_NB + c] * sr[rr] * sc[cc] : (r == c ? 1.0 : 0.0);
         }
-    for (int jb = 0; jb < 32; jb++) {
-        const int j0 = 4 * jb, buf = jb & 1;
-        if (tr == jb) {
+    // Publish the shifted pivot rows of step j (owners: tr == j) and D_j^{-1} (the owner of the
+    // diagonal block: tr == j, tc == j / 2).
+    auto publish = [&](int j) {
+        if (tr == j) {
+            const int buf = j & 1;
 #pragma unroll
             for (int q = 0; q < 4; q++)
 #pragma unroll
-                for (int cc = 0; cc < 8; cc++) rowb[buf][q][8 * tc + cc] = a[q][cc] - (8 * tc + cc == j0 + q ? 1.0 : 0.0);
+                for (int cc = 0; cc < 8; cc++) rowb[buf][q][col(cc)] = a[q][cc] - (col(cc) == 4 * j + q ? 1.0 : 0.0);
+            if (tc == (j & 15)) {
+                double D[4][4];
+                const bool hi = j >= 16;
+#pragma unroll
+                for (int q = 0; q < 4; q++)
+#pragma unroll
+                    for (int q2 = 0; q2 < 4; q2++) D[q][q2] = hi ? a[q][4 + q2] : a[q][q2];
+                const int b = inv4_spd(D);
+                if (b && bad_s == 0) bad_s = 4 * j + b;
+#pragma unroll
+                for (int q = 0; q < 4; q++)
+#pragma unroll
+                    for (int q2 = 0; q2 < 4; q2++) dinv[buf][q][q2] = D[q][q2];
+            }
         }
-        __syncthreads();
-        // D = A_JJ and its inverse (unpivoted Gauss-Jordan; SPD pivots are positive)
-        double D[4][4];
+    };
+    if (tid == 0) bad_s = 0;
+    __syncthreads();
+    publish(0);
+    __syncthreads();
+    for (int jb = 0; jb < 32; jb++) {
+        const int buf = jb & 1;
+        double Di[4][4];
 #pragma unroll
         for (int q = 0; q < 4; q++)
 #pragma unroll
-            for (int q2 = 0; q2 < 4; q2++) D[q][q2] = rowb[buf][q][j0 + q2] + (q == q2 ? 1.0 : 0.0);
-#pragma unroll
-        for (int t = 0; t < 4; t++) {
-            double p = D[t][t];
-            if (!(p > 0.0)) {
-                bad = bad ? bad : j0 + t + 1;
-                p = 1.0;
-            }
-            const double ip = recip64(p);
-#pragma unroll
-            for (int q = 0; q < 4; q++)
-#pragma unroll
-                for (int q2 = 0; q2 < 4; q2++)
-                    if (q != t && q2 != t) D[q][q2] = fma(-D[q][t] * ip, D[t][q2], D[q][q2]);
-#pragma unroll
-            for (int q = 0; q < 4; q++)
-                if (q != t) { D[q][t] *= -ip; D[t][q] *= ip; }
-            D[t][t] = ip;
-        }
-        // D now holds D^{-1}; Tm = (A_RJ - E_RJ) D^{-1} with A_RJ read from the pivot rows (symmetry)
+            for (int q2 = 0; q2 < 4; q2++) Di[q][q2] = dinv[buf][q][q2];
+        // Tm = (A_RJ - E_RJ) D^{-1}, A_RJ read from the pivot rows (symmetry)
         double Tm[4][4];
 #pragma unroll
         for (int rr = 0; rr < 4; rr++) {
@@ -161,7 +210,7 @@ __global__ __launch_bounds__(GJ_PIV_THREADS) void gj_pivot_kernel(const double* 
             for (int q = 0; q < 4; q++) {
                 double t = 0.0;
 #pragma unroll
-                for (int q2 = 0; q2 < 4; q2++) t = fma(cv[q2], D[q2][q], t);
+                for (int q2 = 0; q2 < 4; q2++) t = fma(cv[q2], Di[q2][q], t);
                 Tm[rr][q] = t;
             }
         }
@@ -169,28 +218,30 @@ __global__ __launch_bounds__(GJ_PIV_THREADS) void gj_pivot_kernel(const double* 
         for (int q = 0; q < 4; q++) {
             double rv[8];
 #pragma unroll
-            for (int cc = 0; cc < 8; cc++) rv[cc] = rowb[buf][q][8 * tc + cc];
+            for (int cc = 0; cc < 8; cc++) rv[cc] = rowb[buf][q][col(cc)];
 #pragma unroll
             for (int rr = 0; rr < 4; rr++)
 #pragma unroll
                 for (int cc = 0; cc < 8; cc++) a[rr][cc] = fma(-Tm[rr][q], rv[cc], a[rr][cc]);
         }
-        if (tr == jb && tc == (jb >> 1)) {
-            const int jo = (jb & 1) * 4;
+        if (tr == jb && tc == (jb & 15)) {
+            const int jo = (jb >> 4) * 4;
 #pragma unroll
             for (int q = 0; q < 4; q++)
 #pragma unroll
                 for (int cc = 0; cc < 8; cc++)
                     if (cc == jo + q) a[q][cc] -= 2.0;
         }
+        if (jb + 1 < 32) publish(jb + 1);
+        __syncthreads();
     }
-    // the swept block holds -P^{-1}
+    // the swept block holds -A^{-1}
     double* out = Pinv + z * GJ_NB * GJ_NB;
 #pragma unroll
     for (int rr = 0; rr < 4; rr++)
 #pragma unroll
-        for (int cc = 0; cc < 8; cc++) out[(4 * tr + rr) * GJ_NB + 8 * tc + cc] = -a[rr][cc] * sr[rr] * sc[cc];
-    if (tid == 0 && bad && info && info[z] == 0) info[z] = (int32_t)(k0 + bad);
+        for (int cc = 0; cc < 8; cc++) out[(4 * tr + rr) * GJ_NB + col(cc)] = -a[rr][cc] * sr[rr] * sc[cc];
+    if (tid == 0 && bad_s && info && info[z] == 0) info[z] = (int32_t)(k0 + bad_s);
 }
 
 // A(r, k0 + c) <- T[r][c] for r outside the pivot block (lower-triangle position), and the pivot
@@ -244,7 +295,7 @@ __global__ __launch_bounds__(256) void gj_scatter_kernel(double* __restrict__ A,
 // host threads enqueue at once.
 struct SideQueue {
     hipStream_t s = nullptr;
-    hipEvent_t ev[6] = {};
+    hipEvent_t ev[5] = {};
     bool ok = false;
 };
 static std::mutex g_side_mu;
@@ -276,10 +327,10 @@ static kq_status side_queue(SideQueue** out) {
 // (batch x n x 128) and Pinv (batch x 128 x 128).
 //
 // Look-ahead: the pivot block k + 1 depends on the update of step k only through tile row / column
-// k + 1. The side queue updates those tiles first ("panel"), scatters step k, gathers panel k + 1,
-// inverts its pivot and forms T_{k+1}, while the caller's stream applies the rest of step k's update
-// (every tile outside rows / columns k and k + 1). Both queues touch disjoint tiles and read the
-// panel buffers of their own step.
+// k + 1. The caller's stream updates those tiles first and gathers panel k + 1; then the side queue
+// inverts its pivot and forms T_{k+1} while the caller's stream applies the rest of step k's update
+// (every tile outside rows / columns k and k + 1) and writes T_k back. The two queues touch disjoint
+// data and alternate panel buffers.
 static kq_status gj_inverse_batched(double* A, int64_t n, int64_t lda, int64_t sA, int64_t batch, double* const C[2],
                                     double* const T[2], double* const Pinv[2], int32_t* info, const int* skip,
                                     hipStream_t st) {
@@ -291,14 +342,20 @@ static kq_status gj_inverse_batched(double* A, int64_t n, int64_t lda, int64_t s
     SideQueue* q = nullptr;
     KQ_TRY(side_queue(&q));
     hipStream_t sb = q->s;
-    hipEvent_t ev0 = q->ev[0], evA[2] = {q->ev[1], q->ev[2]}, evB[2] = {q->ev[3], q->ev[4]}, evEnd = q->ev[5];
+    hipEvent_t ev0 = q->ev[0], evP[2] = {q->ev[1], q->ev[2]}, evB[2] = {q->ev[3], q->ev[4]};
     auto nb_of = [&](int64_t k) { return (int)((n - k * GJ_NB) < GJ_NB ? (n - k * GJ_NB) : GJ_NB); };
-    // gather panel k, invert its pivot, T = C Pinv; all on the side queue
-    auto prepare = [&](int64_t k) -> kq_status {
+    // gather panel k (on queue qg), then on the side queue invert its pivot and form T = C Pinv
+    auto prepare = [&](int64_t k, hipStream_t qg) -> kq_status {
         const int b = (int)(k & 1), nbk = nb_of(k);
         const int64_t k0 = k * GJ_NB;
-        hipLaunchKernelGGL(gj_gather_kernel, gr, dim3(256), 0, sb, A, n, lda, sA, k0, nbk, C[b], sC, skip);
+        const double* Tp = k > 0 ? T[b ^ 1] : nullptr;
+        const int64_t p0 = k > 0 ? k0 - GJ_NB : 0;
+        hipLaunchKernelGGL(gj_gather_kernel, gr, dim3(256), 0, qg, A, n, lda, sA, k0, nbk, C[b], sC, Tp, p0, k0, skip);
         KQ_TRY(check_launch("gj_gather"));
+        if (qg != sb) {
+            KQ_HIP(hipEventRecord(evP[b], qg));
+            KQ_HIP(hipStreamWaitEvent(sb, evP[b], 0));
+        }
         hipLaunchKernelGGL(gj_pivot_kernel, dim3((unsigned)batch), dim3(GJ_PIV_THREADS), 0, sb, C[b], sC, k0, nbk,
                            Pinv[b], info, skip);
         KQ_TRY(check_launch("gj_pivot"));
@@ -308,37 +365,33 @@ static kq_status gj_inverse_batched(double* A, int64_t n, int64_t lda, int64_t s
     };
     KQ_HIP(hipEventRecord(ev0, st));
     KQ_HIP(hipStreamWaitEvent(sb, ev0, 0));
-    KQ_TRY(prepare(0));
+    KQ_TRY(prepare(0, sb));
     KQ_HIP(hipEventRecord(evB[0], sb));
     for (int64_t k = 0; k < nt; k++) {
         const int cur = (int)(k & 1), nxt = cur ^ 1, nbk = nb_of(k);
         const int64_t k0 = k * GJ_NB;
-        // side queue: tiles of row / column k + 1, scatter of step k, pivot k + 1
-        if (k > 0) KQ_HIP(hipStreamWaitEvent(sb, evA[nxt], 0));
+        KQ_HIP(hipStreamWaitEvent(st, evB[cur], 0));
         if (k + 1 < nt) {
+            // caller's stream: tiles of row / column k + 1 (tile (k + 1, k) excepted) ...
             GemmArgs<double> u = gemm_args<double>(n, n, nbk, T[cur], GJ_NB, C[cur], GJ_NB, A, lda, -1.0, 1.0);
             u.nb1 = batch; u.sA1 = sC; u.sB1 = sC; u.sC1 = sA; u.tri = 1; u.skip = skip; u.skip_tile = k;
             u.focus = k + 1;
-            KQ_TRY(gemm<double>(u, false, true, sb));
-        }
-        hipLaunchKernelGGL(gj_scatter_kernel, gr, dim3(256), 0, sb, A, n, lda, sA, k0, nbk, T[cur], sC, Pinv[cur], skip);
-        KQ_TRY(check_launch("gj_scatter"));
-        if (k + 1 < nt) {
-            KQ_TRY(prepare(k + 1));
+            KQ_TRY(gemm<double>(u, false, true, st));
+            // ... and gathers panel k + 1 (tile (k + 1, k) from T_k); the side queue inverts its pivot
+            KQ_TRY(prepare(k + 1, st));
             KQ_HIP(hipEventRecord(evB[nxt], sb));
         }
-        // caller's stream: the rest of step k's update, A_RR -= T C^T (lower triangle)
+        // meanwhile the rest of step k's update, A_RR -= T C^T (lower triangle), then the write-back
+        // of T_k and -Pinv_k into row / column k
         if (nt > 1) {
-            KQ_HIP(hipStreamWaitEvent(st, evB[cur], 0));
             GemmArgs<double> u = gemm_args<double>(n, n, nbk, T[cur], GJ_NB, C[cur], GJ_NB, A, lda, -1.0, 1.0);
             u.nb1 = batch; u.sA1 = sC; u.sB1 = sC; u.sC1 = sA; u.tri = 1; u.skip = skip; u.skip_tile = k;
             u.skip_tile2 = k + 1 < nt ? k + 1 : -1;
             KQ_TRY(gemm<double>(u, false, true, st));
-            KQ_HIP(hipEventRecord(evA[cur], st));
         }
+        hipLaunchKernelGGL(gj_scatter_kernel, gr, dim3(256), 0, st, A, n, lda, sA, k0, nbk, T[cur], sC, Pinv[cur], skip);
+        KQ_TRY(check_launch("gj_scatter"));
     }
-    KQ_HIP(hipEventRecord(evEnd, sb));
-    KQ_HIP(hipStreamWaitEvent(st, evEnd, 0));
     return KQ_OK;
 }
 
