@@ -25,23 +25,87 @@ sys.path.insert(0, ROOT)
 
 import synth  # noqa: E402
 
-PEAK = {"hbm": 8.0e12, "fp32_mfma": 157.3e12, "fp64_mfma": 78.6e12, "bf16_mfma": 2.5e15}
+PEAK = {"hbm": 8.0e12, "fp32_mfma": 157.3e12, "fp64_alu": 78.6e12, "bf16_mfma": 2.5e15}
+DB_TOL = 1e-8   # stopping bound of the Denman-Beavers square root (same constant as the library)
 
 
-def algorithmic_work(sp, iters_db: int) -> dict:
-    """Per-phase algorithmic FLOP / bytes of one layer (what the method must compute or move)."""
+def db_steps(HG: np.ndarray) -> int:
+    """Number of Denman-Beavers steps the library takes for a full H_G: the x-interval starts at
+    [sqrt(1/||A^-1||_F), sqrt(||A||_F)] and its bound b follows b <- (sqrt(b) + 1/sqrt(b)) / 2 after
+    the first step; the loop stops once b - 1 < DB_TOL."""
+    A = HG.astype(np.float64)
+    hi = np.linalg.norm(A)
+    lo = 1.0 / np.linalg.norm(np.linalg.inv(A))
+    r = math.sqrt(hi / lo)
+    b = 0.5 * (math.sqrt(r) + 1.0 / math.sqrt(r))
+    k = 1
+    while b - 1.0 >= DB_TOL and k < 8:
+        b = 0.5 * (math.sqrt(b) + 1.0 / math.sqrt(b))
+        k += 1
+    return k
+
+
+def algorithmic_work(sp, db_iters: int) -> dict:
+    """Per-phase algorithmic FLOP / bytes of one layer: what the method must compute or move.
+
+    hessian: the symmetric product n i (i+1); rotate_in: W read (bf16/fp32) and W' written (fp32),
+    H_X read and written twice (fp64, rows then columns); hg_sqrt (full H_G): one SPD inverse of n^3
+    FLOP in the first Denman-Beavers step and two in every later one; rotate_out: 8 B per weight for
+    the V pass plus the 2 o^2 i FLOP of S W' (full H_G); cholinv: 2 i^3 / 3; quantize: the sweep's
+    bytes (W'' read and Q'' written, codes, grid parameters, R) and the trailing-update FLOP."""
     o, i, n, b, g = sp.o, sp.i, sp.n, sp.bits, sp.group
     xb = 2 if sp.x_dtype == "bf16" else 4
     wb = 2 if sp.w_dtype == "bf16" else 4
-    w = {
-        "hessian": {"flop": n * i * (i + 1), "bytes": n * i * xb + 4 * i * i},
-        "rotate_in": {"bytes": o * i * (wb + 4) + 16 * i * i},
-        "hg_sqrt": {"flop": (2 * iters_db * o ** 3) if sp.hg_form == "full" else 0},
-        "rotate_out": {"flop": 2 * o * o * i if sp.hg_form == "full" else 0, "bytes": 8 * o * i},
-        "cholinv": {"flop": 2 * i ** 3 // 3},
-        "quantize": {"flop": o * i * (i - 128), "bytes": int((8 + b / 8 + (8 / g if g else 0)) * o * i + 2 * i * i)},
+    full = sp.hg_form == "full"
+    return {
+        "hessian": {"flop": n * i * (i + 1), "bytes": n * i * xb + 8 * i * i, "peak": "bf16_mfma"},
+        "rotate_in": {"bytes": o * i * (wb + 4) + 32 * i * i, "peak": "hbm"},
+        "hg_sqrt": {"flop": (2 * db_iters - 1) * o ** 3 if full else 0, "peak": "fp64_alu"},
+        "rotate_out": ({"flop": 2 * o * o * i, "peak": "fp32_mfma"} if full else {"bytes": 8 * o * i, "peak": "hbm"}),
+        "cholinv": {"flop": 2 * i ** 3 // 3, "peak": "fp64_alu"},
+        "quantize": {"bytes": int((8 + b / 8 + (8 / g if g else 0)) * o * i + 2 * i * i),
+                     "flop": o * i * (i - 128), "peak": "hbm"},
     }
-    return w
+
+
+def sources_digest() -> str:
+    """sha256 over the library's HIP sources, to tie a committed counter measurement to a build."""
+    import hashlib
+    import glob
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "post_quantization_03_amd", "csrc", "*"))):
+        with open(f, "rb") as fh:
+            h.update(os.path.basename(f).encode() + b"\0" + fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(phase: str):
+    """HBM bytes per call of a phase from the committed rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE
+    summary (profiles/<phase>_c2_traffic.md), or None when the sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"{phase}_c2_traffic.md")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as fh:
+        for line in fh:
+            if ":" in line and line.split(":", 1)[0].strip() in ("sources-sha256", "bytes-per-call"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip().strip("`")
+    if vals.get("sources-sha256") != sources_digest() or "bytes-per-call" not in vals:
+        return None
+    return int(vals["bytes-per-call"])
+
+
+def roofline_of(name: str, wk: dict, ms: float) -> dict:
+    pk = wk["peak"]
+    if pk == "hbm":
+        ach = wk["bytes"] / (ms / 1e3)
+        return {"bound": "hbm", "kernel": name, "achieved": round(ach / 1e9, 2), "peak": PEAK["hbm"] / 1e9,
+                "unit": "GB/s", "frac": round(ach / PEAK["hbm"], 4), "traffic": None}
+    ach = wk["flop"] / (ms / 1e3)
+    bound = "alu" if pk == "fp64_alu" else "mfma"
+    return {"bound": bound, "kernel": name, "achieved": round(ach / 1e12, 3), "peak": PEAK[pk] / 1e12,
+            "unit": "TFLOP/s", "frac": round(ach / PEAK[pk], 4), "traffic": None}
 
 
 def run_gpu(sp, steps: int, warmup: int, phases: bool):
@@ -60,6 +124,7 @@ def run_gpu(sp, steps: int, warmup: int, phases: bool):
             return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
         return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
+    iters = db_steps(d["HG"]) if sp.hg_form == "full" else 0
     X, W, HG = to(d["X"], sp.x_dtype), to(d["W"], sp.w_dtype), to(d["HG"], "f32")
     s, t = to(d["s"], "i8"), to(d["t"], "i8")
     del d
@@ -75,22 +140,22 @@ def run_gpu(sp, steps: int, warmup: int, phases: bool):
         out = step()
         torch.cuda.synchronize()
         print(f"# warmup {k + 1}/{warmup} done", file=sys.stderr, flush=True)
-    info = out["info"].cpu().tolist()
-    if info != [0, 0]:
-        raise RuntimeError(f"factorisation failed: info={info}")
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for _ in range(steps):
         out = step()
     torch.cuda.synchronize()
     t_total = time.perf_counter() - t_start
+    info = out["info"].cpu().tolist()
+    if info != [0, 0]:
+        raise RuntimeError(f"factorisation failed: info={info}")
     ms = 1e3 * t_total / steps
     print(f"# timed {steps} steps: {ms:.3f} ms/step", file=sys.stderr, flush=True)
 
     ph = None
     if phases:
         ph = phase_times(sp, X, W, HG, s, t, cfg, ws)
-    return ms, ph, out
+    return ms, ph, out, iters
 
 
 def phase_times(sp, X, W, HG, s, t, cfg, ws, reps: int = 3) -> dict:
@@ -191,29 +256,35 @@ def main():
     ap.add_argument("--workload", default="C2", choices=["C2", "C3", "C4"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-phases", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="first run one plain device copy of MIB MiB (fp32 elementwise kernel), the reference "
+                         "for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters to bytes")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the per-layer solver runs on a single MI355X in this build "
               "(multi-GPU sharding is described in DESIGN.md, not implemented).", file=sys.stderr)
         sys.exit(2)
     sp = synth.CONFIGS[args.workload]
-    ms, ph, out = run_gpu(sp, args.steps, args.warmup, not args.no_phases)
+    if args.copy_calibration:
+        import torch
+        src = torch.ones(args.copy_calibration * (1 << 18), dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        print(f"# copy calibration: read {src.numel() * 4} B, wrote {dst.numel() * 4} B", file=sys.stderr, flush=True)
+        del src, dst
+    ms, ph, out, iters = run_gpu(sp, args.steps, args.warmup, not args.no_phases)
     value = sp.o * sp.i / (ms / 1e3) / 1e6
-    roof = None
+    roof, per_phase, s_cached = None, None, None
     if ph:
-        work = algorithmic_work(sp, iters_db=8)
-        dom = max((k for k in ph if k in work), key=lambda k: ph[k])
-        wk = work[dom]
-        if "flop" in wk and wk["flop"]:
-            bound = "mfma"
-            peak = PEAK["fp64_mfma"] if dom == "hg_sqrt" else (PEAK["bf16_mfma"] if dom == "hessian" else PEAK["fp32_mfma"])
-            ach = wk["flop"] / (ph[dom] / 1e3)
-            roof = {"bound": bound, "kernel": dom, "achieved": ach / 1e12, "peak": peak / 1e12, "unit": "TFLOP/s",
-                    "frac": ach / peak, "traffic": None}
-        else:
-            ach = wk["bytes"] / (ph[dom] / 1e3)
-            roof = {"bound": "hbm", "kernel": dom, "achieved": ach / 1e9, "peak": PEAK["hbm"] / 1e9, "unit": "GB/s",
-                    "frac": ach / PEAK["hbm"], "traffic": None}
+        work = algorithmic_work(sp, iters)
+        per_phase = {k: roofline_of(k, work[k], ph[k]) for k in work if k in ph and
+                     (work[k].get("flop") or work[k].get("bytes"))}
+        dom = max(per_phase, key=lambda k: ph[k])
+        roof = per_phase[dom]
+        roof["traffic"] = measured_traffic(dom) if sp.name.startswith("C2") else None
+        if "hg_sqrt" in ph:
+            s_cached = round(sp.o * sp.i / ((ms - ph["hg_sqrt"]) / 1e3) / 1e6, 3)
     cpu = None if args.no_cpu_baseline else cpu_baseline(sp)
     line = {"metric": "layer-quant throughput: Mweights/s (4096x4096 W3 g128) + % MFMA/HBM peak",
             "value": round(value, 3), "unit": "Mweights/s", "n_gpus": 1, "steps": args.steps,
@@ -221,9 +292,11 @@ def main():
             "vs_baseline": None, "dtype": "fp32", "data": "synthetic",
             "config": {"workload": sp.name, "o": sp.o, "i": sp.i, "tokens": sp.n, "x_dtype": sp.x_dtype,
                        "hg_form": sp.hg_form, "bits": sp.bits, "group": sp.group,
-                       "arith": "bf16 MFMA (exact products) for H_X, fp64 for H_G^1/2 and the damped factor, fp32 elsewhere"},
+                       "arith": "bf16 MFMA (exact products, fp64 accumulation) for H_X; fp64 for H_G^1/2 "
+                                "and the damped factor; fp32 for the rotations of W and the sweep"},
             "phases_ms": {k: round(v, 4) for k, v in ph.items()} if ph else None,
-            "roofline": roof, "cpu_baseline": cpu}
+            "db_steps": iters, "s_cached_mweights_per_s": s_cached,
+            "roofline": roof, "phases_roofline": per_phase, "cpu_baseline": cpu}
     print(json.dumps(line), flush=True)
 
 
