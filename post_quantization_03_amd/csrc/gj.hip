@@ -290,27 +290,28 @@ __global__ __launch_bounds__(256) void gj_scatter_kernel(double* __restrict__ A,
     }
 }
 
-// Second queue of a device for the look-ahead of the sweep (default priority). The events order its
-// work with the caller's stream; the mutex keeps the event sequence of one call intact when several
-// host threads enqueue at once.
-struct SideQueue {
-    hipStream_t s = nullptr;
-    hipEvent_t ev[5] = {};
+// Queues of a device for the pipelined sweep (default priority): `side` runs the pivot chain,
+// `main` the wide rank-128 updates. Events order both with the caller's stream; the mutex keeps the
+// event sequence of one call intact when several host threads enqueue at once.
+struct SweepQueues {
+    hipStream_t side = nullptr, main = nullptr;
+    hipEvent_t ev[7] = {};
     bool ok = false;
 };
-static std::mutex g_side_mu;
-static SideQueue g_side[64];
+static std::mutex g_sweep_mu;
+static SweepQueues g_sweep[64];
 
-static kq_status side_queue(SideQueue** out) {
+static kq_status sweep_queues(SweepQueues** out) {
     int dev = -1;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return fail(KQ_EHIP, "side queue: no device");
-    SideQueue& q = g_side[dev];
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return fail(KQ_EHIP, "sweep queues: no device");
+    SweepQueues& q = g_sweep[dev];
     if (!q.ok) {
-        if (hipStreamCreateWithFlags(&q.s, hipStreamNonBlocking) != hipSuccess)
-            return fail(KQ_EHIP, "side queue: stream creation failed");
+        if (hipStreamCreateWithFlags(&q.side, hipStreamNonBlocking) != hipSuccess ||
+            hipStreamCreateWithFlags(&q.main, hipStreamNonBlocking) != hipSuccess)
+            return fail(KQ_EHIP, "sweep queues: stream creation failed");
         for (hipEvent_t& e : q.ev)
             if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess)
-                return fail(KQ_EHIP, "side queue: event creation failed");
+                return fail(KQ_EHIP, "sweep queues: event creation failed");
         q.ok = true;
     }
     *out = &q;
@@ -326,11 +327,17 @@ static kq_status side_queue(SideQueue** out) {
 // lda, item stride sA). Scratch (two of each, alternating by pivot): panels C and T
 // (batch x n x 128) and Pinv (batch x 128 x 128).
 //
-// Look-ahead: the pivot block k + 1 depends on the update of step k only through tile row / column
-// k + 1. The caller's stream updates those tiles first and gathers panel k + 1; then the side queue
-// inverts its pivot and forms T_{k+1} while the caller's stream applies the rest of step k's update
-// (every tile outside rows / columns k and k + 1) and writes T_k back. The two queues touch disjoint
-// data and alternate panel buffers.
+// Pipeline per pivot step k. The pivot block k + 1 depends on step k's update only through tile row
+// and column k + 1, so:
+//   caller's stream: update those tiles (tile (k + 1, k) excepted) and gather panel k + 1, taking
+//                    tile (k + 1, k) from T_k;
+//   side queue:      invert pivot k + 1, T_{k+1} = C_{k+1} Pinv_{k+1}, write T_k and -Pinv_k back into
+//                    row and column k;
+//   main queue:      the rest of step k's update A_RR -= T_k C_k^T (every tile outside rows and
+//                    columns k, k + 1), concurrently with the side queue.
+// Both queues start on the same event, so the two pivot work-groups are dispatched alongside the
+// update. The queues touch disjoint tiles and alternate the panel buffers; step k + 1 on the
+// caller's stream waits for both.
 static kq_status gj_inverse_batched(double* A, int64_t n, int64_t lda, int64_t sA, int64_t batch, double* const C[2],
                                     double* const T[2], double* const Pinv[2], int32_t* info, const int* skip,
                                     hipStream_t st) {
@@ -338,26 +345,25 @@ static kq_status gj_inverse_batched(double* A, int64_t n, int64_t lda, int64_t s
     const int64_t sC = n * GJ_NB;
     const int64_t nt = (n + GJ_NB - 1) / GJ_NB;
     const dim3 gr((unsigned)((n + GJ_RT - 1) / GJ_RT), (unsigned)batch);
-    std::lock_guard<std::mutex> lock(g_side_mu);
-    SideQueue* q = nullptr;
-    KQ_TRY(side_queue(&q));
-    hipStream_t sb = q->s;
-    hipEvent_t ev0 = q->ev[0], evP[2] = {q->ev[1], q->ev[2]}, evB[2] = {q->ev[3], q->ev[4]};
+    std::lock_guard<std::mutex> lock(g_sweep_mu);
+    SweepQueues* q = nullptr;
+    KQ_TRY(sweep_queues(&q));
+    hipStream_t sb = q->side, sm = q->main;
+    hipEvent_t ev0 = q->ev[0], evG[2] = {q->ev[1], q->ev[2]}, evB[2] = {q->ev[3], q->ev[4]},
+               evM[2] = {q->ev[5], q->ev[6]};
     auto nb_of = [&](int64_t k) { return (int)((n - k * GJ_NB) < GJ_NB ? (n - k * GJ_NB) : GJ_NB); };
-    // gather panel k (on queue qg), then on the side queue invert its pivot and form T = C Pinv
-    auto prepare = [&](int64_t k, hipStream_t qg) -> kq_status {
+    auto gather = [&](int64_t k, hipStream_t qg) -> kq_status {
         const int b = (int)(k & 1), nbk = nb_of(k);
         const int64_t k0 = k * GJ_NB;
         const double* Tp = k > 0 ? T[b ^ 1] : nullptr;
         const int64_t p0 = k > 0 ? k0 - GJ_NB : 0;
         hipLaunchKernelGGL(gj_gather_kernel, gr, dim3(256), 0, qg, A, n, lda, sA, k0, nbk, C[b], sC, Tp, p0, k0, skip);
-        KQ_TRY(check_launch("gj_gather"));
-        if (qg != sb) {
-            KQ_HIP(hipEventRecord(evP[b], qg));
-            KQ_HIP(hipStreamWaitEvent(sb, evP[b], 0));
-        }
-        hipLaunchKernelGGL(gj_pivot_kernel, dim3((unsigned)batch), dim3(GJ_PIV_THREADS), 0, sb, C[b], sC, k0, nbk,
-                           Pinv[b], info, skip);
+        return check_launch("gj_gather");
+    };
+    auto pivot_t = [&](int64_t k) -> kq_status {  // side queue: Pinv_k, T_k = C_k Pinv_k
+        const int b = (int)(k & 1), nbk = nb_of(k);
+        hipLaunchKernelGGL(gj_pivot_kernel, dim3((unsigned)batch), dim3(GJ_PIV_THREADS), 0, sb, C[b], sC, k * GJ_NB,
+                           nbk, Pinv[b], info, skip);
         KQ_TRY(check_launch("gj_pivot"));
         GemmArgs<double> t = gemm_args<double>(n, nbk, nbk, C[b], GJ_NB, Pinv[b], GJ_NB, T[b], GJ_NB, 1.0, 0.0);
         t.nb1 = batch; t.sA1 = sC; t.sB1 = GJ_NB * GJ_NB; t.sC1 = sC; t.skip = skip;
@@ -365,33 +371,41 @@ static kq_status gj_inverse_batched(double* A, int64_t n, int64_t lda, int64_t s
     };
     KQ_HIP(hipEventRecord(ev0, st));
     KQ_HIP(hipStreamWaitEvent(sb, ev0, 0));
-    KQ_TRY(prepare(0, sb));
+    KQ_TRY(gather(0, sb));
+    KQ_TRY(pivot_t(0));
     KQ_HIP(hipEventRecord(evB[0], sb));
     for (int64_t k = 0; k < nt; k++) {
         const int cur = (int)(k & 1), nxt = cur ^ 1, nbk = nb_of(k);
         const int64_t k0 = k * GJ_NB;
+        // caller's stream: T_k ready (and step k - 1 written back), step k - 1's update done
         KQ_HIP(hipStreamWaitEvent(st, evB[cur], 0));
+        if (k > 0) KQ_HIP(hipStreamWaitEvent(st, evM[nxt], 0));
         if (k + 1 < nt) {
-            // caller's stream: tiles of row / column k + 1 (tile (k + 1, k) excepted) ...
             GemmArgs<double> u = gemm_args<double>(n, n, nbk, T[cur], GJ_NB, C[cur], GJ_NB, A, lda, -1.0, 1.0);
             u.nb1 = batch; u.sA1 = sC; u.sB1 = sC; u.sC1 = sA; u.tri = 1; u.skip = skip; u.skip_tile = k;
             u.focus = k + 1;
             KQ_TRY(gemm<double>(u, false, true, st));
-            // ... and gathers panel k + 1 (tile (k + 1, k) from T_k); the side queue inverts its pivot
-            KQ_TRY(prepare(k + 1, st));
-            KQ_HIP(hipEventRecord(evB[nxt], sb));
+            KQ_TRY(gather(k + 1, st));
         }
-        // meanwhile the rest of step k's update, A_RR -= T C^T (lower triangle), then the write-back
-        // of T_k and -Pinv_k into row / column k
+        KQ_HIP(hipEventRecord(evG[cur], st));
+        // side queue: pivot k + 1 and the write-back of step k
+        KQ_HIP(hipStreamWaitEvent(sb, evG[cur], 0));
+        if (k + 1 < nt) KQ_TRY(pivot_t(k + 1));
+        hipLaunchKernelGGL(gj_scatter_kernel, gr, dim3(256), 0, sb, A, n, lda, sA, k0, nbk, T[cur], sC, Pinv[cur], skip);
+        KQ_TRY(check_launch("gj_scatter"));
+        KQ_HIP(hipEventRecord(evB[nxt], sb));
+        // main queue: the rest of step k's update
+        KQ_HIP(hipStreamWaitEvent(sm, evG[cur], 0));
         if (nt > 1) {
             GemmArgs<double> u = gemm_args<double>(n, n, nbk, T[cur], GJ_NB, C[cur], GJ_NB, A, lda, -1.0, 1.0);
             u.nb1 = batch; u.sA1 = sC; u.sB1 = sC; u.sC1 = sA; u.tri = 1; u.skip = skip; u.skip_tile = k;
             u.skip_tile2 = k + 1 < nt ? k + 1 : -1;
-            KQ_TRY(gemm<double>(u, false, true, st));
+            KQ_TRY(gemm<double>(u, false, true, sm));
         }
-        hipLaunchKernelGGL(gj_scatter_kernel, gr, dim3(256), 0, st, A, n, lda, sA, k0, nbk, T[cur], sC, Pinv[cur], skip);
-        KQ_TRY(check_launch("gj_scatter"));
+        KQ_HIP(hipEventRecord(evM[cur], sm));
     }
+    KQ_HIP(hipStreamWaitEvent(st, evM[(nt - 1) & 1], 0));
+    KQ_HIP(hipStreamWaitEvent(st, evB[nt & 1], 0));
     return KQ_OK;
 }
 

@@ -5,11 +5,11 @@
 // rounding H to fp32 alone moves the sweep's pre-rounding values by up to ~2e-4 grid steps on the
 // 4096-wide layers (cond ~2e5 after damping).
 // bf16 X: bf16 x bf16 products are exact, so the gfx950 bf16 matrix cores
-// (v_mfma_f32_16x16x32_bf16) form exact products; every instruction starts from a zero accumulator
-// and its 32-product fp32 sum is added into fp64 registers, so only one fp32 rounding per 32 tokens
-// enters the result. Only the lower-triangle 128 x 128 tiles of H are computed; a fixed split over
-// tokens with a fixed-order fp64 reduction keeps the result deterministic, and both triangles are
-// written.
+// (v_mfma_f32_16x16x32_bf16) form exact products; each 64-token stage runs two instructions into an
+// fp32 accumulator that starts at zero, and the stage's 64-product sum is added into fp64
+// registers, so two fp32 roundings per 64 tokens enter the result. Only the lower-triangle
+// 128 x 128 tiles of H are computed; a fixed split over tokens with a fixed-order fp64 reduction
+// keeps the result deterministic, and both triangles are written.
 // fp32 X: the fp64 MFMA GEMM on the widened values (small workloads only).
 #include "kq_internal.h"
 
@@ -39,10 +39,14 @@ __device__ inline void tri_decode(int t, int& tm, int& tn) {
 // the banks.
 __device__ inline int lds_off(int m, int c) { return m * SY_K + ((c ^ (m & 7)) << 3); }
 
-__global__ __launch_bounds__(256) void syrk_bf16_kernel(const uint16_t* __restrict__ X, int64_t n, int64_t d,
-                                                        int64_t ldx, int64_t tok_per_split, double alpha, double beta,
-                                                        double* __restrict__ H, double* __restrict__ part,
-                                                        int ntiles) {
+// 512 threads = 8 waves; wave w owns rows 32 (w / 2) .. + 31 and columns 64 (w % 2) .. + 63 of the
+// tile (2 x 4 MFMA tiles). Threads 0..255 stage X through registers into LDS (an 8 x 8 transpose of
+// 16-bit values per thread), double-buffered with one barrier per 64-token stage.
+constexpr int SY_THREADS = 512;
+__global__ __launch_bounds__(SY_THREADS) void syrk_bf16_kernel(const uint16_t* __restrict__ X, int64_t n, int64_t d,
+                                                               int64_t ldx, int64_t tok_per_split, double alpha,
+                                                               double beta, double* __restrict__ H,
+                                                               double* __restrict__ part, int ntiles) {
     __shared__ __align__(16) uint16_t As[2][SY_T * SY_K];
     __shared__ __align__(16) uint16_t Bs[2][SY_T * SY_K];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -53,8 +57,9 @@ __global__ __launch_bounds__(256) void syrk_bf16_kernel(const uint16_t* __restri
     const int64_t kb = (int64_t)split * tok_per_split;
     const int64_t ke = (kb + tok_per_split < n) ? kb + tok_per_split : n;
 
-    // loader role: threads 0..127 stage the row block (A), 128..255 the column block (B)
-    const int op = tid >> 7, p = tid & 127, kg = p >> 4, mc = p & 15;
+    // loader role (threads 0..255): 0..127 stage the row block (A), 128..255 the column block (B)
+    const bool loader = tid < 256;
+    const int op = (tid >> 7) & 1, p = tid & 127, kg = p >> 4, mc = p & 15;
     const int64_t cbase = (op ? n0 : m0) + 8 * mc;
     const bool fullc = cbase + 8 <= d;
     U4 v[8];
@@ -95,9 +100,9 @@ __global__ __launch_bounds__(256) void syrk_bf16_kernel(const uint16_t* __restri
         }
     };
 
-    double acc[4][4][4];
+    double acc[2][4][4];
 #pragma unroll
-    for (int i = 0; i < 4; i++)
+    for (int i = 0; i < 2; i++)
 #pragma unroll
         for (int j = 0; j < 4; j++)
 #pragma unroll
@@ -105,20 +110,23 @@ __global__ __launch_bounds__(256) void syrk_bf16_kernel(const uint16_t* __restri
     const int wm = wave >> 1, wn = wave & 1;
 
     if (kb < ke) {
-        gload(kb);
-        sstore(0);
+        if (loader) {
+            gload(kb);
+            sstore(0);
+        }
         __syncthreads();
         int buf = 0;
         for (int64_t k0 = kb; k0 < ke; k0 += SY_K) {
             const bool more = k0 + SY_K < ke;
-            if (more) gload(k0 + SY_K);
+            if (more && loader) gload(k0 + SY_K);
+            f4v pacc[2][4];
 #pragma unroll
             for (int s = 0; s < 2; s++) {
-                bf8v a[4], b[4];
+                bf8v a[2], b[4];
                 const int c = 4 * s + (lane >> 4);
 #pragma unroll
-                for (int i = 0; i < 4; i++) {
-                    const int m = wm * 64 + 16 * i + (lane & 15);
+                for (int i = 0; i < 2; i++) {
+                    const int m = wm * 32 + 16 * i + (lane & 15);
                     a[i] = *reinterpret_cast<const bf8v*>(As[buf] + lds_off(m, c));
                 }
 #pragma unroll
@@ -127,15 +135,19 @@ __global__ __launch_bounds__(256) void syrk_bf16_kernel(const uint16_t* __restri
                     b[j] = *reinterpret_cast<const bf8v*>(Bs[buf] + lds_off(nn, c));
                 }
 #pragma unroll
-                for (int i = 0; i < 4; i++)
+                for (int i = 0; i < 2; i++)
 #pragma unroll
-                    for (int j = 0; j < 4; j++) {
-                        const f4v p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], f4v{0, 0, 0, 0}, 0, 0, 0);
-#pragma unroll
-                        for (int r = 0; r < 4; r++) acc[i][j][r] += (double)p[r];
-                    }
+                    for (int j = 0; j < 4; j++)
+                        pacc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], s ? pacc[i][j] : f4v{0, 0, 0, 0},
+                                                                             0, 0, 0);
             }
-            if (more) sstore(buf ^ 1);
+#pragma unroll
+            for (int i = 0; i < 2; i++)
+#pragma unroll
+                for (int j = 0; j < 4; j++)
+#pragma unroll
+                    for (int r = 0; r < 4; r++) acc[i][j][r] += (double)pacc[i][j][r];
+            if (more && loader) sstore(buf ^ 1);
             __syncthreads();
             buf ^= 1;
         }
@@ -144,22 +156,22 @@ __global__ __launch_bounds__(256) void syrk_bf16_kernel(const uint16_t* __restri
     if (part) {
         double* out = part + ((int64_t)split * ntiles + tile) * (SY_T * SY_T);
 #pragma unroll
-        for (int i = 0; i < 4; i++)
+        for (int i = 0; i < 2; i++)
 #pragma unroll
             for (int j = 0; j < 4; j++)
 #pragma unroll
                 for (int r = 0; r < 4; r++) {
-                    const int mm = wm * 64 + 16 * i + 4 * (lane >> 4) + r, nn = wn * 64 + 16 * j + (lane & 15);
+                    const int mm = wm * 32 + 16 * i + 4 * (lane >> 4) + r, nn = wn * 64 + 16 * j + (lane & 15);
                     out[mm * SY_T + nn] = acc[i][j][r];
                 }
     } else {
 #pragma unroll
-        for (int i = 0; i < 4; i++)
+        for (int i = 0; i < 2; i++)
 #pragma unroll
             for (int j = 0; j < 4; j++)
 #pragma unroll
                 for (int r = 0; r < 4; r++) {
-                    const int64_t m = m0 + wm * 64 + 16 * i + 4 * (lane >> 4) + r;
+                    const int64_t m = m0 + wm * 32 + 16 * i + 4 * (lane >> 4) + r;
                     const int64_t c = n0 + wn * 64 + 16 * j + (lane & 15);
                     if (m >= d || c >= d || c > m) continue;
                     double val = alpha * acc[i][j][r];
@@ -269,7 +281,7 @@ extern "C" kq_status kq_hessian_accum(const void* X, kq_dtype xdt, int64_t n, in
         if (!ws || ws_bytes < hessian_ws(n, d, xdt)) return fail(KQ_EWORKSPACE, "kq_hessian_accum: workspace too small");
         part = reinterpret_cast<double*>((reinterpret_cast<uintptr_t>(ws) + 255) & ~uintptr_t(255));
     }
-    hipLaunchKernelGGL(syrk_bf16_kernel, dim3((unsigned)ntiles, (unsigned)nsplit), dim3(256), 0, st,
+    hipLaunchKernelGGL(syrk_bf16_kernel, dim3((unsigned)ntiles, (unsigned)nsplit), dim3(SY_THREADS), 0, st,
                        static_cast<const uint16_t*>(X), n, d, ldx, tps, alpha, beta, H, part, ntiles);
     KQ_TRY(check_launch("syrk_bf16"));
     if (nsplit > 1) {

@@ -11,7 +11,7 @@ import synth
 from oracle import kronq as kq
 from post_quantization_03_amd import _lib as K
 from tests.gpu_util import host, say, to_dev, torch_dev, ws_tensor
-from tests.parity import gpu_words_to_codes, rel_fro, replay_compare
+from tests.parity import gpu_words_to_codes, hx_tol, rel_fro, replay_compare
 
 pytestmark = pytest.mark.gpu
 f32 = np.float32
@@ -25,12 +25,6 @@ def spd_f32(rng, d, n=None, spread=1.0):
 
 def signs(rng, d):
     return (rng.integers(0, 2, d) * 2 - 1).astype(np.int8)
-
-
-def hx_tol(n):
-    """H_X error bound for bf16 inputs: each 32-token matrix-core sum is rounded to fp32 once
-    (relative 2^-24) before fp64 accumulation, so the error averages down as sqrt(32 / n)."""
-    return 4e-7 * np.sqrt(32.0 / n)
 
 
 # ----------------------------------------------------------------------------- H_X
