@@ -45,6 +45,21 @@ __global__ __launch_bounds__(256) void row_grid_kernel(const float* __restrict__
     }
 }
 
+// Value of lane `src` of each 16-lane row, broadcast to the whole row (DPP row_newbcast: a VALU move,
+// no LDS round trip). `src` must fold to a constant after unrolling.
+__device__ inline float row_bcast(float x, int src) {
+    const int xi = __float_as_int(x);
+    int r;
+    switch (src) {
+#define KQ_BC(n) case n: r = __builtin_amdgcn_update_dpp(0, xi, 0x150 + n, 0xF, 0xF, false); break;
+        KQ_BC(0) KQ_BC(1) KQ_BC(2) KQ_BC(3) KQ_BC(4) KQ_BC(5) KQ_BC(6) KQ_BC(7)
+        KQ_BC(8) KQ_BC(9) KQ_BC(10) KQ_BC(11) KQ_BC(12) KQ_BC(13) KQ_BC(14)
+        default: r = __builtin_amdgcn_update_dpp(0, xi, 0x150 + 15, 0xF, 0xF, false); break;
+#undef KQ_BC
+    }
+    return __int_as_float(r);
+}
+
 template <int G>
 __global__ __launch_bounds__(256) void sweep_block_kernel(float* __restrict__ W, int64_t o, int64_t i, int64_t ldw,
                                                           const float* __restrict__ R, int64_t ldr, int64_t b0,
@@ -88,50 +103,64 @@ __global__ __launch_bounds__(256) void sweep_block_kernel(float* __restrict__ W,
 #pragma unroll
     for (int u = 0; u < 8; u++) { code[u] = 0; eown[u] = 0.0f; }
 
+    // Two unrolled levels, so every column index below is a constant. The reciprocals of R_jj for the
+    // 16 columns of a lane group and the lane's entries of R row j + 1 are loaded one step ahead,
+    // so the per-column chain (broadcast, round, error, update) waits on no LDS access.
+    const int cq = q;  // lane's column within each 16-column group
+    float rnext[8];
 #pragma unroll
-    for (int j = 0; j < SW_B; j++) {
-        const int uj = j >> 4, qj = j & 15;
-        if (G > 0 && (j % (G > 0 ? G : 1)) == 0) {
-            float mn = INFINITY, mx = -INFINITY;
+    for (int u = 0; u < 8; u++) rnext[u] = Rb[16 * u + cq];  // row 0
 #pragma unroll
-            for (int u = 0; u < 8; u++) {
-                if (16 * u + 15 < j || 16 * u >= j + G) continue;
-                const int col = 16 * u + q;
-                if (col >= j && col < j + G) { mn = fminf(mn, v[u]); mx = fmaxf(mx, v[u]); }
+    for (int uj = 0; uj < SW_B / 16; uj++) {
+        float rd[16];
+#pragma unroll
+        for (int t = 0; t < 16; t++) rd[t] = rdiag[16 * uj + t];
+#pragma unroll
+        for (int qj = 0; qj < 16; qj++) {
+            const int j = 16 * uj + qj;
+            float rcur[8];
+#pragma unroll
+            for (int u = 0; u < 8; u++) rcur[u] = rnext[u];
+            if (j + 1 < SW_B) {
+#pragma unroll
+                for (int u = 0; u < 8; u++)
+                    if (16 * u + 15 > j + 1) rnext[u] = Rb[(j + 1) * SW_B + 16 * u + cq];
             }
+            if (G > 0 && (j % (G > 0 ? G : 1)) == 0) {
+                float mn = INFINITY, mx = -INFINITY;
 #pragma unroll
-            for (int w = 8; w > 0; w >>= 1) {
-                mn = fminf(mn, __shfl_xor(mn, w, 16));
-                mx = fmaxf(mx, __shfl_xor(mx, w, 16));
-            }
-            mu = mn;
-            s = (mx - mn) / L;
-            invs = s > 0.0f ? 1.0f / s : 0.0f;
-            if (live && q == 0) {
-                const int64_t gidx = (b0 + j) / (G > 0 ? G : 1);
-                offset[rr * ng + gidx] = mu;
-                scale[rr * ng + gidx] = s;
-            }
-        }
-        const float w = __shfl(v[uj], qj, 16);
-        const float uu = (w - mu) * invs;
-        const float qf = fminf(fmaxf(rintf(uu), 0.0f), L);
-        const float deq = fmaf(s, qf, mu);
-        const float e = (w - deq) * rdiag[j];
-        loss = fmaf(e, e, loss);
-        const bool own = (q == qj);
-        if (own) {
-            v[uj] = deq;
-            code[uj] = (int)qf;
-            eown[uj] = e;
-        }
-        const float* Rj = Rb + j * SW_B;
+                for (int u = 0; u < 8; u++) {
+                    if (16 * u + 15 < j || 16 * u >= j + G) continue;
+                    const int col = 16 * u + cq;
+                    if (col >= j && col < j + G) { mn = fminf(mn, v[u]); mx = fmaxf(mx, v[u]); }
+                }
 #pragma unroll
-        for (int u = 0; u < 8; u++) {
-            if (16 * u + 15 <= j) continue;            // every lane's column is done
-            const int col = 16 * u + q;
-            const float rv = Rj[col];
-            if (col > j) v[u] = fmaf(-e, rv, v[u]);
+                for (int w = 8; w > 0; w >>= 1) {
+                    mn = fminf(mn, __shfl_xor(mn, w, 16));
+                    mx = fmaxf(mx, __shfl_xor(mx, w, 16));
+                }
+                mu = mn;
+                s = (mx - mn) / L;
+                invs = s > 0.0f ? 1.0f / s : 0.0f;
+                if (live && cq == 0) {
+                    const int64_t gidx = (b0 + j) / (G > 0 ? G : 1);
+                    offset[rr * ng + gidx] = mu;
+                    scale[rr * ng + gidx] = s;
+                }
+            }
+            const float w = row_bcast(v[uj], qj);
+            const float uu = (w - mu) * invs;
+            const float qf = fminf(fmaxf(rintf(uu), 0.0f), L);
+            const float deq = fmaf(s, qf, mu);
+            const float e = (w - deq) * rd[qj];
+            loss = fmaf(e, e, loss);
+            const bool own = (cq == qj);
+            code[uj] = own ? (int)qf : code[uj];
+            eown[uj] = own ? e : eown[uj];
+            // columns of group uj: the owner takes the rounded value, later columns the update
+            v[uj] = own ? deq : (cq > qj ? fmaf(-e, rcur[uj], v[uj]) : v[uj]);
+#pragma unroll
+            for (int u = uj + 1; u < 8; u++) v[u] = fmaf(-e, rcur[u], v[u]);
         }
     }
 
