@@ -7,8 +7,8 @@
 // the columns still to be updated stay spread over all 16 lanes as the sweep advances. For column j
 // the owning lane's value is broadcast within the 16-lane group, every lane rounds it to the grid
 // (same arithmetic on every lane, so no second broadcast), and updates its own later columns with
-// the row j of the block's R (staged once per work-group in LDS). After the block, the trailing
-// columns receive the lazy update W[:, b1:] -= E R[b0:b1, b1:] on the fp32 MFMA GEMM.
+// the row j of the block's R (staged once per work-group in LDS). The lazy trailing updates
+// W[:, b1:] -= E R[b0:b1, b1:] run on the fp32 MFMA GEMM, in two levels (see SW_SB).
 #include <cmath>
 
 #include "kq_internal.h"
@@ -66,7 +66,7 @@ __global__ __launch_bounds__(256) void sweep_block_kernel(float* __restrict__ W,
                                                           int bits, uint32_t* __restrict__ codes,
                                                           float* __restrict__ scale, float* __restrict__ offset,
                                                           float* __restrict__ row_loss, float* __restrict__ E,
-                                                          int first) {
+                                                          int64_t lde, int first) {
     extern __shared__ __align__(16) float sm[];
     float* Rb = sm;                        // 128 x 128
     float* rdiag = sm + SW_B * SW_B;       // 128 reciprocals of R_jj
@@ -169,7 +169,7 @@ __global__ __launch_bounds__(256) void sweep_block_kernel(float* __restrict__ W,
 #pragma unroll
         for (int u = 0; u < 8; u++) {
             wrow[16 * u + q] = v[u];
-            E[rr * SW_B + 16 * u + q] = eown[u];
+            E[rr * lde + 16 * u + q] = eown[u];
         }
         if (q == 0 && row_loss) row_loss[rr] = (first ? 0.0f : row_loss[rr]) + loss;
     }
@@ -194,9 +194,14 @@ __global__ __launch_bounds__(256) void sweep_block_kernel(float* __restrict__ W,
 
 using namespace kq;
 
+// Lazy updates in two levels: inside a super-block of SW_SB columns each block's errors update the
+// rest of the super-block (K = 128); at the super-block's end the trailing columns receive one
+// update with K = SW_SB, so most of the trailing-update FLOP run in deep-K GEMMs.
+constexpr int SW_SB = 512;
+
 size_t quantize_ws(int64_t o) {
     Sizer z;
-    z.take<float>((size_t)o * SW_B);
+    z.take<float>((size_t)o * SW_SB);
     return z.used;
 }
 
@@ -215,7 +220,7 @@ extern "C" kq_status kq_quantize_layer(float* W, int64_t o, int64_t i, int64_t l
     if (!ws || ws_bytes < quantize_ws(o)) return fail(KQ_EWORKSPACE, "kq_quantize_layer: workspace too small");
     hipStream_t st = hs(stream);
     Arena ar(ws, ws_bytes);
-    float* E = ar.take<float>((size_t)o * SW_B);
+    float* E = ar.take<float>((size_t)o * SW_SB);
     if (o > 2147483647LL * SW_ROWS) return fail(KQ_ESHAPE, "kq_quantize_layer: o too large");
     const float L = (float)((1 << bits) - 1);
     if (group == 0) {
@@ -233,19 +238,31 @@ extern "C" kq_status kq_quantize_layer(float* W, int64_t o, int64_t i, int64_t l
         attr = true;
     }
     const dim3 grid((unsigned)((o + SW_ROWS - 1) / SW_ROWS));
-    for (int64_t b0 = 0; b0 < i; b0 += SW_B) {
-        const int first = b0 == 0;
-        switch (group) {
-            case 0: hipLaunchKernelGGL(sweep_block_kernel<0>, grid, dim3(256), smem, st, W, o, i, ldw, R, ldr, b0, bits, codes, scale, offset, row_loss, E, first); break;
-            case 16: hipLaunchKernelGGL(sweep_block_kernel<16>, grid, dim3(256), smem, st, W, o, i, ldw, R, ldr, b0, bits, codes, scale, offset, row_loss, E, first); break;
-            case 32: hipLaunchKernelGGL(sweep_block_kernel<32>, grid, dim3(256), smem, st, W, o, i, ldw, R, ldr, b0, bits, codes, scale, offset, row_loss, E, first); break;
-            case 64: hipLaunchKernelGGL(sweep_block_kernel<64>, grid, dim3(256), smem, st, W, o, i, ldw, R, ldr, b0, bits, codes, scale, offset, row_loss, E, first); break;
-            default: hipLaunchKernelGGL(sweep_block_kernel<128>, grid, dim3(256), smem, st, W, o, i, ldw, R, ldr, b0, bits, codes, scale, offset, row_loss, E, first); break;
+    for (int64_t s0 = 0; s0 < i; s0 += SW_SB) {
+        const int64_t s1 = s0 + SW_SB < i ? s0 + SW_SB : i;
+        for (int64_t b0 = s0; b0 < s1; b0 += SW_B) {
+            const int first = b0 == 0;
+            float* Eb = E + (b0 - s0);
+            switch (group) {
+                case 0: hipLaunchKernelGGL(sweep_block_kernel<0>, grid, dim3(256), smem, st, W, o, i, ldw, R, ldr, b0, bits, codes, scale, offset, row_loss, Eb, (int64_t)SW_SB, first); break;
+                case 16: hipLaunchKernelGGL(sweep_block_kernel<16>, grid, dim3(256), smem, st, W, o, i, ldw, R, ldr, b0, bits, codes, scale, offset, row_loss, Eb, (int64_t)SW_SB, first); break;
+                case 32: hipLaunchKernelGGL(sweep_block_kernel<32>, grid, dim3(256), smem, st, W, o, i, ldw, R, ldr, b0, bits, codes, scale, offset, row_loss, Eb, (int64_t)SW_SB, first); break;
+                case 64: hipLaunchKernelGGL(sweep_block_kernel<64>, grid, dim3(256), smem, st, W, o, i, ldw, R, ldr, b0, bits, codes, scale, offset, row_loss, Eb, (int64_t)SW_SB, first); break;
+                default: hipLaunchKernelGGL(sweep_block_kernel<128>, grid, dim3(256), smem, st, W, o, i, ldw, R, ldr, b0, bits, codes, scale, offset, row_loss, Eb, (int64_t)SW_SB, first); break;
+            }
+            KQ_TRY(check_launch("sweep_block"));
+            // the rest of the super-block: W[:, b1:s1] -= E_b R[b0:b1, b1:s1]
+            const int64_t b1 = b0 + SW_B;
+            if (b1 < s1) {
+                GemmArgs<float> g = gemm_args<float>(o, s1 - b1, SW_B, Eb, SW_SB, R + b0 * ldr + b1, ldr, W + b1, ldw,
+                                                     -1.0f, 1.0f);
+                KQ_TRY(gemm<float>(g, false, false, st));
+            }
         }
-        KQ_TRY(check_launch("sweep_block"));
-        const int64_t b1 = b0 + SW_B;
-        if (b1 < i) {
-            GemmArgs<float> g = gemm_args<float>(o, i - b1, SW_B, E, SW_B, R + b0 * ldr + b1, ldr, W + b1, ldw, -1.0f, 1.0f);
+        // columns after the super-block: W[:, s1:] -= E R[s0:s1, s1:]
+        if (s1 < i) {
+            GemmArgs<float> g = gemm_args<float>(o, i - s1, s1 - s0, E, SW_SB, R + s0 * ldr + s1, ldr, W + s1, ldw,
+                                                 -1.0f, 1.0f);
             KQ_TRY(gemm<float>(g, false, false, st));
         }
     }
