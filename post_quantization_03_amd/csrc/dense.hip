@@ -590,7 +590,7 @@ template kq_status fill<uint32_t>(uint32_t*, size_t, uint32_t, hipStream_t, cons
 template <>
 int potrf_nb<float>() { return 128; }
 template <>
-int potrf_nb<double>() { return 64; }
+int potrf_nb<double>() { return 128; }
 
 // One work-group per batch item factors the NB x NB diagonal block at (k0, k0) in LDS (16-column
 // sub-panels: a single wave factors the sub-panel with shuffles, then all threads apply the rank-16
@@ -769,15 +769,19 @@ static kq_status launch_diag(T* A, int64_t lda, int64_t sA, T* X, int64_t ldx, i
 
 template <typename T>
 kq_status potrf_batched(T* A, int64_t lda, int64_t sA, T* X, int64_t ldx, int64_t sX, int64_t n, int64_t batch,
-                        int32_t* info, int64_t info_stride, double* logdet, const int* skip, hipStream_t st) {
+                        int32_t* info, int64_t info_stride, double* logdet, const int* skip, hipStream_t st,
+                        double* scr) {
     const int NB = potrf_nb<T>();
     if (batch > 65535) return fail(KQ_ESHAPE, "potrf batch too large");
     for (int64_t k0 = 0; k0 < n; k0 += NB) {
         const int64_t nbe = (n - k0) < NB ? (n - k0) : NB, k1 = k0 + nbe;
         if (sizeof(T) == 4)
             KQ_TRY((launch_diag<T, 128>(A, lda, sA, X, ldx, sX, n, k0, batch, info, info_stride, logdet, skip, st)));
+        else if (!logdet)
+            KQ_TRY(chol_inv_diag128(reinterpret_cast<double*>(A), lda, sA, reinterpret_cast<double*>(X), ldx, sX, n,
+                                    k0, batch, scr, info, info_stride, skip, st));
         else
-            KQ_TRY((launch_diag<T, 64>(A, lda, sA, X, ldx, sX, n, k0, batch, info, info_stride, logdet, skip, st)));
+            return fail(KQ_EUNSUPPORTED, "potrf: fp64 log-determinant not supported");
         if (k1 >= n) break;
         // panel: A[k1:, k0:k1] <- A[k1:, k0:k1] X_kk^T   (in place: one tile column per work-group row)
         GemmArgs<T> p = gemm_args<T>(n - k1, nbe, nbe, A + k1 * lda + k0, lda, X + k0 * ldx + k0, ldx,
@@ -793,9 +797,9 @@ kq_status potrf_batched(T* A, int64_t lda, int64_t sA, T* X, int64_t ldx, int64_
     return KQ_OK;
 }
 template kq_status potrf_batched<float>(float*, int64_t, int64_t, float*, int64_t, int64_t, int64_t, int64_t, int32_t*,
-                                        int64_t, double*, const int*, hipStream_t);
+                                        int64_t, double*, const int*, hipStream_t, double*);
 template kq_status potrf_batched<double>(double*, int64_t, int64_t, double*, int64_t, int64_t, int64_t, int64_t,
-                                         int32_t*, int64_t, double*, const int*, hipStream_t);
+                                         int32_t*, int64_t, double*, const int*, hipStream_t, double*);
 
 template <typename T>
 kq_status trtri_batched(const T* L, int64_t ldl, int64_t sL, T* X, int64_t ldx, int64_t sX, int64_t n, int64_t batch,
@@ -874,7 +878,8 @@ static void cholinv_layout(Sizer& z, int64_t n) {
     z.take<double>(1);
     z.take<double>((size_t)n * n);
     z.take<double>((size_t)n * n);
-    z.take<double>((size_t)(n * n / 2 + 64 * 64));
+    z.take<double>((size_t)(n * n / 2 + 128 * 128));
+    z.take<double>((size_t)chol_scratch_doubles());
 }
 
 size_t cholinv_ws(int64_t n) {
@@ -894,7 +899,8 @@ extern "C" kq_status kq_cholinv(const double* HX, int64_t n, int64_t ldh, double
     double* lam = ar.take<double>(1);
     double* Hr = ar.take<double>((size_t)n * n);
     double* X = ar.take<double>((size_t)n * n);
-    double* Tscr = ar.take<double>((size_t)(n * n / 2 + 64 * 64));
+    double* Tscr = ar.take<double>((size_t)(n * n / 2 + 128 * 128));
+    double* Cscr = ar.take<double>((size_t)chol_scratch_doubles());
     hipLaunchKernelGGL(damp_kernel, dim3(1), dim3(256), 0, st, HX, n, ldh, damp, lam, info);
     KQ_TRY(check_launch("damp"));
     dim3 g2((unsigned)((n + 255) / 256 < 64 ? (n + 255) / 256 : 64), (unsigned)n);
@@ -902,7 +908,7 @@ extern "C" kq_status kq_cholinv(const double* HX, int64_t n, int64_t ldh, double
     hipLaunchKernelGGL(reverse_damped_kernel, g2, dim3(256), 0, st, HX, n, ldh, lam, Hr);
     KQ_TRY(check_launch("reverse"));
     KQ_TRY(fill<double>(X, (size_t)n * n, 0.0, st));
-    KQ_TRY(potrf_batched<double>(Hr, n, 0, X, n, 0, n, 1, info, 0, nullptr, nullptr, st));
+    KQ_TRY(potrf_batched<double>(Hr, n, 0, X, n, 0, n, 1, info, 0, nullptr, nullptr, st, Cscr));
     KQ_TRY(trtri_batched<double>(Hr, n, 0, X, n, 0, n, 1, Tscr, nullptr, st));
     hipLaunchKernelGGL(reverse_upper_kernel, g2, dim3(256), 0, st, X, n, R);
     return check_launch("reverse_upper");

@@ -80,6 +80,14 @@ __global__ __launch_bounds__(256) void gj_gather_kernel(const double* __restrict
     }
 }
 
+// Work-group barrier that orders LDS only: global stores issued before it may still be in flight
+// (nothing in the work-group reads them back).
+__device__ inline void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // 1/p to full fp64 precision: hardware reciprocal estimate refined by two Newton steps.
 __device__ inline double recip64(double p) {
     double r = __builtin_amdgcn_rcp(p);
@@ -243,6 +251,280 @@ __global__ __launch_bounds__(GJ_PIV_THREADS) void gj_pivot_kernel(const double* 
         for (int cc = 0; cc < 8; cc++) out[(4 * tr + rr) * GJ_NB + col(cc)] = -a[rr][cc] * sr[rr] * sc[cc];
     if (tid == 0 && bad_s && info && info[z] == 0) info[z] = (int32_t)(k0 + bad_s);
 }
+
+// D (4 x 4 SPD) = L L^T: L lower with positive diagonal, and Li = L^{-1} (lower). A non-positive
+// pivot is replaced by 1 (the caller reports it through inv4_spd's flag).
+__device__ inline void chol4_spd(const double D[4][4], double L[4][4], double Li[4][4]) {
+#pragma unroll
+    for (int c = 0; c < 4; c++) {
+        double sdiag = D[c][c];
+#pragma unroll
+        for (int k = 0; k < c; k++) sdiag = fma(-L[c][k], L[c][k], sdiag);
+        const double d = sqrt(sdiag > 0.0 ? sdiag : 1.0), inv = recip64(d);
+        L[c][c] = d;
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+            if (r <= c) { if (r < c) L[r][c] = 0.0; continue; }
+            double t = D[r][c];
+#pragma unroll
+            for (int k = 0; k < c; k++) t = fma(-L[r][k], L[c][k], t);
+            L[r][c] = t * inv;
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+        const double ir = recip64(L[r][r]);
+#pragma unroll
+        for (int c = 0; c < 4; c++) {
+            if (c > r) { Li[r][c] = 0.0; continue; }
+            if (c == r) { Li[r][r] = ir; continue; }
+            double t = 0.0;
+#pragma unroll
+            for (int k = 0; k < r; k++)
+                if (k >= c) t = fma(L[r][k], Li[k][c], t);
+            Li[r][c] = -t * ir;
+        }
+    }
+}
+
+// Cholesky factor and its inverse of the nb x nb SPD diagonal block at (k0, k0) of a matrix stored in
+// its lower triangle: L (lower) over the block's lower triangle, X = L^{-1} (lower) into X's block
+// (whose upper part the caller has zeroed). Two kernels:
+//  chol_sweep128_kernel: the register sweep of gj_pivot_kernel on the unit-diagonal-scaled block
+//    A = S P S, which after the 4-pivot step J holds -(A_{0:J,0:J})^{-1} in the swept rows. It saves,
+//    per step, the pre-step (identity-shifted) pivot rows, the post-step rows J and the 4 x 4
+//    factor L_JJ = chol(D) to a scratch area;
+//  chol_extract128_kernel: from those, in parallel,
+//    columns J of L:    L_JJ, and L_RJ = A_RJ L_JJ^{-T} (A_RJ the pre-step column, equal to the
+//                       pre-step row by symmetry),
+//    rows J of L^{-1}:  (L^{-1})_{J,0:J} = L_JJ^T M_{J,0:J} with M = (A_{0:J,0:J})^{-1}, because
+//                       M = L^{-T} L^{-1} on the leading block and (L^{-1})_JJ = L_JJ^{-1};
+//    and undoes the scaling: L_P = S^{-1} L_A, L_P^{-1} = L_A^{-1} S.
+// Scratch per item: CHOL_SCR doubles.
+constexpr int64_t CHOL_SCR = 2 * 32 * 4 * GJ_NB + 32 * 16;
+
+__global__ __launch_bounds__(GJ_PIV_THREADS) void chol_sweep128_kernel(const double* __restrict__ A, int64_t lda,
+                                                                       int64_t sA, int64_t n, int64_t k0,
+                                                                       double* __restrict__ scr, int32_t* info,
+                                                                       int64_t info_stride, const int* skip) {
+    if (skip && *skip) return;
+    __shared__ __align__(16) double rowb[2][4][GJ_NB];
+    __shared__ __align__(16) double dinv[2][4][4];
+    __shared__ int bad_s;
+    const int tid = threadIdx.x, tr = tid >> 4, tc = tid & 15;
+    auto col = [&](int cc) { return (cc >> 2) * 64 + 4 * tc + (cc & 3); };
+    const int64_t z = blockIdx.x;
+    A += z * sA + k0 * lda + k0;
+    scr += z * CHOL_SCR;
+    double* pre = scr;                       // [32][4][128]
+    double* post = scr + 32 * 4 * GJ_NB;     // [32][4][128]
+    double* lj = scr + 2 * 32 * 4 * GJ_NB;   // [32][4][4]
+    const int nbk = (int)((n - k0) < GJ_NB ? (n - k0) : GJ_NB);
+    auto Aget = [&](int r, int c) { return c <= r ? A[(int64_t)r * lda + c] : A[(int64_t)c * lda + r]; };
+    double sr[4], sc[8];
+#pragma unroll
+    for (int rr = 0; rr < 4; rr++) {
+        const int r = 4 * tr + rr;
+        const double p = r < nbk ? A[(int64_t)r * lda + r] : 1.0;
+        sr[rr] = p > 0.0 ? 1.0 / sqrt(p) : 1.0;
+    }
+#pragma unroll
+    for (int cc = 0; cc < 8; cc++) {
+        const int c = col(cc);
+        const double p = c < nbk ? A[(int64_t)c * lda + c] : 1.0;
+        sc[cc] = p > 0.0 ? 1.0 / sqrt(p) : 1.0;
+    }
+    double a[4][8];
+#pragma unroll
+    for (int rr = 0; rr < 4; rr++)
+#pragma unroll
+        for (int cc = 0; cc < 8; cc++) {
+            const int r = 4 * tr + rr, c = col(cc);
+            a[rr][cc] = (r < nbk && c < nbk) ? Aget(r, c) * sr[rr] * sc[cc] : (r == c ? 1.0 : 0.0);
+        }
+    auto publish = [&](int j) {
+        if (tr == j) {
+            const int buf = j & 1;
+#pragma unroll
+            for (int q = 0; q < 4; q++)
+#pragma unroll
+                for (int cc = 0; cc < 8; cc++) rowb[buf][q][col(cc)] = a[q][cc] - (col(cc) == 4 * j + q ? 1.0 : 0.0);
+            if (tc == (j & 15)) {
+                double D[4][4], Lc[4][4], Li[4][4];
+                const bool hi = j >= 16;
+#pragma unroll
+                for (int q = 0; q < 4; q++)
+#pragma unroll
+                    for (int q2 = 0; q2 < 4; q2++) D[q][q2] = hi ? a[q][4 + q2] : a[q][q2];
+                chol4_spd(D, Lc, Li);
+                const int b = inv4_spd(D);
+                if (b && bad_s == 0) bad_s = 4 * j + b;
+#pragma unroll
+                for (int q = 0; q < 4; q++)
+#pragma unroll
+                    for (int q2 = 0; q2 < 4; q2++) {
+                        dinv[buf][q][q2] = D[q][q2];
+                        lj[j * 16 + q * 4 + q2] = Lc[q][q2];
+                    }
+            }
+        }
+    };
+    if (tid == 0) bad_s = 0;
+    __syncthreads();
+    publish(0);
+    __syncthreads();
+    for (int jb = 0; jb < 32; jb++) {
+        const int buf = jb & 1;
+        pre[jb * 4 * GJ_NB + tid] = (&rowb[buf][0][0])[tid];  // 512 = 4 x 128 values, one per thread
+        double Di[4][4];
+#pragma unroll
+        for (int q = 0; q < 4; q++)
+#pragma unroll
+            for (int q2 = 0; q2 < 4; q2++) Di[q][q2] = dinv[buf][q][q2];
+        double Tm[4][4];
+#pragma unroll
+        for (int rr = 0; rr < 4; rr++) {
+            double cv[4];
+#pragma unroll
+            for (int q = 0; q < 4; q++) cv[q] = rowb[buf][q][4 * tr + rr];
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+                double t = 0.0;
+#pragma unroll
+                for (int q2 = 0; q2 < 4; q2++) t = fma(cv[q2], Di[q2][q], t);
+                Tm[rr][q] = t;
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+            double rv[8];
+#pragma unroll
+            for (int cc = 0; cc < 8; cc++) rv[cc] = rowb[buf][q][col(cc)];
+#pragma unroll
+            for (int rr = 0; rr < 4; rr++)
+#pragma unroll
+                for (int cc = 0; cc < 8; cc++) a[rr][cc] = fma(-Tm[rr][q], rv[cc], a[rr][cc]);
+        }
+        if (tr == jb && tc == (jb & 15)) {
+            const int jo = (jb >> 4) * 4;
+#pragma unroll
+            for (int q = 0; q < 4; q++)
+#pragma unroll
+                for (int cc = 0; cc < 8; cc++)
+                    if (cc == jo + q) a[q][cc] -= 2.0;
+        }
+        if (tr == jb) {
+#pragma unroll
+            for (int q = 0; q < 4; q++)
+#pragma unroll
+                for (int cc = 0; cc < 8; cc++) post[(jb * 4 + q) * GJ_NB + col(cc)] = a[q][cc];
+        }
+        if (jb + 1 < 32) publish(jb + 1);
+        lds_barrier();
+    }
+    if (tid == 0 && bad_s && bad_s <= nbk && info && info[z * info_stride] == 0)
+        info[z * info_stride] = (int32_t)(k0 + bad_s);
+}
+
+__global__ __launch_bounds__(512) void chol_extract128_kernel(double* __restrict__ A, int64_t lda, int64_t sA,
+                                                              double* __restrict__ X, int64_t ldx, int64_t sX,
+                                                              int64_t n, int64_t k0, const double* __restrict__ scr,
+                                                              const int* skip) {
+    if (skip && *skip) return;
+    __shared__ double sq[GJ_NB];    // sqrt(P_rr)
+    __shared__ double ljs[32][4][4], ljit[32][4][4];  // L_JJ and L_JJ^{-T}
+    const int tid = threadIdx.x;
+    const int64_t z = blockIdx.x;
+    A += z * sA + k0 * lda + k0;
+    X += z * sX + k0 * ldx + k0;
+    scr += z * CHOL_SCR;
+    const double* pre = scr;
+    const double* post = scr + 32 * 4 * GJ_NB;
+    const double* lj = scr + 2 * 32 * 4 * GJ_NB;
+    const int nbk = (int)((n - k0) < GJ_NB ? (n - k0) : GJ_NB);
+    if (tid < GJ_NB) {
+        const double p = tid < nbk ? A[(int64_t)tid * lda + tid] : 1.0;
+        sq[tid] = p > 0.0 ? sqrt(p) : 1.0;
+    }
+    if (tid < 32) {
+        double L[4][4], Li[4][4];
+#pragma unroll
+        for (int q = 0; q < 4; q++)
+#pragma unroll
+            for (int q2 = 0; q2 < 4; q2++) L[q][q2] = lj[tid * 16 + q * 4 + q2];
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+            const double ir = 1.0 / L[r][r];
+#pragma unroll
+            for (int c = 0; c < 4; c++) {
+                if (c > r) { Li[r][c] = 0.0; continue; }
+                if (c == r) { Li[r][r] = ir; continue; }
+                double t = 0.0;
+#pragma unroll
+                for (int k = 0; k < r; k++)
+                    if (k >= c) t = fma(L[r][k], Li[k][c], t);
+                Li[r][c] = -t * ir;
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < 4; q++)
+#pragma unroll
+            for (int q2 = 0; q2 < 4; q2++) {
+                ljs[tid][q][q2] = L[q][q2];
+                ljit[tid][q][q2] = Li[q2][q];
+            }
+    }
+    __syncthreads();
+    // L: entry (r, 4 jb + q) for r >= 4 jb
+    for (int e = tid; e < GJ_NB * 32; e += 512) {
+        const int r = e >> 5, jb = e & 31, j0 = 4 * jb;
+        if (r < j0 || r >= nbk) continue;
+        if (r < j0 + 4) {
+            const int q = r - j0;
+            for (int q2 = 0; q2 <= q; q2++)
+                if (j0 + q2 < nbk) A[(int64_t)r * lda + j0 + q2] = ljs[jb][q][q2] * sq[r];
+        } else {
+            double cv[4];
+#pragma unroll
+            for (int q2 = 0; q2 < 4; q2++) cv[q2] = pre[(jb * 4 + q2) * GJ_NB + r];
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+                double t = 0.0;
+#pragma unroll
+                for (int q2 = 0; q2 < 4; q2++) t = fma(cv[q2], ljit[jb][q2][q], t);
+                if (j0 + q < nbk) A[(int64_t)r * lda + j0 + q] = t * sq[r];
+            }
+        }
+    }
+    // X = L^{-1}: entry (4 jb + q, c) for c < 4 jb + 4
+    for (int e = tid; e < GJ_NB * GJ_NB; e += 512) {
+        const int r = e >> 7, c = e & 127, jb = r >> 2, q = r & 3;
+        if (c > 4 * jb + 3 || r >= nbk || c >= nbk) continue;
+        double t = 0.0;
+#pragma unroll
+        for (int q2 = 0; q2 < 4; q2++) t = fma(ljs[jb][q2][q], post[(jb * 4 + q2) * GJ_NB + c], t);
+        X[(int64_t)r * ldx + c] = -t / sq[c];
+    }
+}
+
+}  // namespace kq
+
+kq_status kq::chol_inv_diag128(double* A, int64_t lda, int64_t sA, double* X, int64_t ldx, int64_t sX, int64_t n,
+                               int64_t k0, int64_t batch, double* scr, int32_t* info, int64_t info_stride,
+                               const int* skip, hipStream_t st) {
+    if (batch > 65535) return fail(KQ_ESHAPE, "chol_inv_diag128: batch too large");
+    if (!scr) return fail(KQ_EWORKSPACE, "chol_inv_diag128: no scratch");
+    hipLaunchKernelGGL(chol_sweep128_kernel, dim3((unsigned)batch), dim3(GJ_PIV_THREADS), 0, st, A, lda, sA, n, k0, scr,
+                       info, info_stride, skip);
+    KQ_TRY(check_launch("chol_sweep128"));
+    hipLaunchKernelGGL(chol_extract128_kernel, dim3((unsigned)batch), dim3(512), 0, st, A, lda, sA, X, ldx, sX, n, k0,
+                       scr, skip);
+    return check_launch("chol_extract128");
+}
+
+int64_t kq::chol_scratch_doubles() { return CHOL_SCR; }
+
+namespace kq {
 
 // A(r, k0 + c) <- T[r][c] for r outside the pivot block (lower-triangle position), and the pivot
 // block <- -Pinv (lower triangle).

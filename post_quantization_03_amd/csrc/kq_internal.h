@@ -92,7 +92,8 @@ kq_status gemm(const GemmArgs<T>& g, bool ta, bool tb, hipStream_t st);
 // (may be null), info[z] set to 1 + index of the first failing pivot (may be null).
 template <typename T>
 kq_status potrf_batched(T* A, int64_t lda, int64_t sA, T* X, int64_t ldx, int64_t sX, int64_t n, int64_t batch,
-                        int32_t* info, int64_t info_stride, double* logdet, const int* skip, hipStream_t st);
+                        int32_t* info, int64_t info_stride, double* logdet, const int* skip, hipStream_t st,
+                        double* scr = nullptr);
 // X <- L^{-1} (lower) given L (lower, strictly below the diagonal blocks) and X holding the
 // inverses of the diagonal blocks (from potrf_batched). T scratch: batch * n * n / 4 elements.
 template <typename T>
@@ -100,6 +101,13 @@ kq_status trtri_batched(const T* L, int64_t ldl, int64_t sL, T* X, int64_t ldx, 
                         int64_t batch, T* Tscr, const int* skip, hipStream_t st);
 template <typename T>
 int potrf_nb();
+// fp64 diagonal-block step of potrf_batched: Cholesky factor L (lower, over the block) and L^{-1}
+// (into X's block) of the 128 x 128 block at (k0, k0), by a register-resident sweep.
+// scr: batch * chol_scratch_doubles() doubles.
+kq_status chol_inv_diag128(double* A, int64_t lda, int64_t sA, double* X, int64_t ldx, int64_t sX, int64_t n,
+                           int64_t k0, int64_t batch, double* scr, int32_t* info, int64_t info_stride,
+                           const int* skip, hipStream_t st);
+int64_t chol_scratch_doubles();
 
 // ------------------------------------------------------------------------------------ helpers
 template <typename T>
