@@ -35,9 +35,9 @@ __device__ inline void tri_decode(int t, int& tm, int& tn) {
 }
 
 // LDS tile [128 rows][64 k] bf16, rows of 128 bytes made of eight 16-byte chunks; chunk c of row m is
-// stored at position c ^ (m & 7) so that the 16 consecutive rows read by an MFMA operand spread over
-// the banks.
-__device__ inline int lds_off(int m, int c) { return m * SY_K + ((c ^ (m & 7)) << 3); }
+// stored at position c ^ (m & 7) ^ ((m >> 3) & 7): the 16 consecutive rows read by an MFMA operand
+// and the rows 8 apart written by one store instruction of the loaders both spread over the banks.
+__device__ inline int lds_off(int m, int c) { return m * SY_K + ((c ^ (m & 7) ^ ((m >> 3) & 7)) << 3); }
 
 // 512 threads = 8 waves; wave w owns rows 32 (w / 2) .. + 31 and columns 64 (w % 2) .. + 63 of the
 // tile (2 x 4 MFMA tiles). Threads 0..255 stage X through registers into LDS (an 8 x 8 transpose of
