@@ -278,7 +278,7 @@ template kq_status gemm<float>(const GemmArgs<float>&, bool, bool, hipStream_t);
 template <int BM, int BN, bool TA, bool TB, bool VEC>
 __global__ __launch_bounds__(256) void dgemm_valu_kernel(GemmArgs<double> g) {
     if (g.skip && *g.skip) return;
-    constexpr int BK = 16, PAD = 8;
+    constexpr int BK = 16, PAD = 2;  // row stride 130 doubles: the transposing stores of a slice spread over the banks
     constexpr int RG = BM / 32, CG = BN / 32;
     constexpr int VPR = BK / 2;                  // 16-byte vectors per tile row (k direction)
     constexpr int NVA = BM * BK / 2 / 256, NVB = BN * BK / 2 / 256;
