@@ -39,7 +39,7 @@ def db_steps(HG: np.ndarray) -> int:
     r = math.sqrt(hi / lo)
     b = 0.5 * (math.sqrt(r) + 1.0 / math.sqrt(r))
     k = 1
-    while b - 1.0 >= DB_TOL and k < 8:
+    while b - 1.0 >= DB_TOL and k < 7:
         b = 0.5 * (math.sqrt(b) + 1.0 / math.sqrt(b))
         k += 1
     return k

@@ -109,10 +109,13 @@ kq_status kq_rotate_in(const void* Win, kq_dtype wdt, int64_t ldwin, float* Wout
  * incoherence processing uses the gradient covariance; S^{-1} H_G S^{-1} = I makes H_G cancel).
  * HG, S and Sinv share the storage form: diag (o floats), block (o/blk blocks of blk x blk), or
  * full (o x o). Diagonal: elementwise square root. Block and full: scaled Denman-Beavers
- * iteration in fp64 with Cholesky-based SPD inverses, stopped on a device-side convergence test.
- * Sinv may be NULL. info (device int32): 0, or k > 0 if H_G (or an iterate) is not positive
- * definite (k = 1 + index of the failing pivot). The caller may free HG once the work has
- * completed in stream order (H_G is only needed transiently).
+ * iteration in fp64 whose SPD inverses are symmetric block Gauss-Jordan sweeps, stopped on a
+ * device-side convergence test (at most 7 steps; enough for cond(H_G) <= 1e16). The sweep runs on
+ * two extra queues of the device, forked from and joined back into `stream`.
+ * Sinv may be NULL. info (device int32): 0; k in 1..o if H_G (or an iterate) is not positive
+ * definite (k = 1 + index of the failing pivot); o + 1 if the iteration did not converge. The
+ * caller may free HG once the work has completed in stream order (H_G is only needed
+ * transiently).
  */
 kq_status kq_hg_sqrt(const float* HG, kq_hg_form form, int64_t o, int64_t blk, float* S, float* Sinv,
                      int32_t* info, void* ws, size_t ws_bytes, kq_stream stream);

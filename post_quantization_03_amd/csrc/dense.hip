@@ -47,11 +47,14 @@ constexpr int gpad() { return sizeof(T) == 8 ? 8 : 16; }
 
 // ===================================================================================== GEMM kernel
 // 256 threads = 4 waves in a 2 x 2 arrangement; each wave owns a 64 x 64 block of C as 4 x 4
-// MFMA 16x16 tiles (K = 4 per instruction). K is staged through LDS in slices, double-buffered with
-// one barrier per slice. LDS tiles are stored
-// k-major with a 16-element pad so that the 16-lane groups of an MFMA operand read hit disjoint
-// banks. K slices are 16 elements deep (gemm_bk). MFMA operand layout (16x16x4): lane l holds A[l%16][l/16] and B[l/16][l%16]; the 4
-// accumulator registers hold column l%16 of C in the rows given by Mfma<T>::row.
+// MFMA 16x16 tiles (K = 4 per instruction). K is staged through LDS in 16-deep slices,
+// double-buffered with one barrier per slice. Each operand keeps in LDS the contiguity it has in
+// memory, so that the slice stores are whole 16-byte vectors: an operand contiguous along M (or N)
+// is stored k-major ([k][m], rows padded by gpad so the 16-lane groups of an MFMA operand read hit
+// disjoint banks); an operand contiguous along K (A not transposed) is stored m-major ([m][k], row
+// stride BK + 4 = 20 floats: 20 m mod 64 is distinct for 16 consecutive m). MFMA operand layout
+// (16x16x4): lane l holds A[l%16][l/16] and B[l/16][l%16]; the 4 accumulator registers hold column
+// l%16 of C in the rows given by Mfma<T>::row.
 template <typename T>
 constexpr int gemm_bk() { return sizeof(T) == 8 ? 16 : 16; }
 
@@ -62,8 +65,10 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs<T> g) {
     constexpr int VN = 16 / sizeof(T);
     constexpr int VPR = BK / VN;                  // 16-byte vectors per tile row (k direction)
     constexpr int NV = GBM * BK / VN / 256;       // vectors per thread per operand
-    __shared__ T As[2][BK][GBM + gpad<T>()];
-    __shared__ T Bs[2][BK][GBN + gpad<T>()];
+    // A: [BK][GBM + pad] when contiguous along M (TA), else [GBM][BK + 4] (one layout unused)
+    constexpr int AKM = TA ? BK : GBM, AMN = TA ? GBM + gpad<T>() : BK + 16 / (int)sizeof(T);
+    __shared__ __align__(16) T As[2][AKM][AMN];
+    __shared__ __align__(16) T Bs[2][BK][GBN + gpad<T>()];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     // Tile order: work-groups are dealt round-robin to the 8 XCDs, so the linear id is remapped so
     // that each XCD works on a contiguous range of tiles (neighbouring tiles share A / B panels in
@@ -159,8 +164,10 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs<T> g) {
         for (int q = 0; q < NV; q++) {
             const int v = tid + 256 * q;
             if (!TA) {
+                V16<T> t;
 #pragma unroll
-                for (int e = 0; e < VN; e++) As[buf][(v % VPR) * VN + e][v / VPR] = ra[q][e];
+                for (int e = 0; e < VN; e++) t.v[e] = ra[q][e];
+                *reinterpret_cast<V16<T>*>(&As[buf][v / VPR][(v % VPR) * VN]) = t;
             } else {
 #pragma unroll
                 for (int e = 0; e < VN; e++) As[buf][v / (GBM / VN)][(v % (GBM / VN)) * VN + e] = ra[q][e];
@@ -188,7 +195,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs<T> g) {
                 T a[4], b[4];
                 const int kr = kk + (lane >> 4);
 #pragma unroll
-                for (int i = 0; i < 4; i++) a[i] = As[buf][kr][wm * 64 + 16 * i + (lane & 15)];
+                for (int i = 0; i < 4; i++)
+                    a[i] = TA ? As[buf][kr][wm * 64 + 16 * i + (lane & 15)] : As[buf][wm * 64 + 16 * i + (lane & 15)][kr];
 #pragma unroll
                 for (int j = 0; j < 4; j++) b[j] = Bs[buf][kr][wn * 64 + 16 * j + (lane & 15)];
 #pragma unroll

@@ -577,7 +577,7 @@ __global__ __launch_bounds__(256) void gj_scatter_kernel(double* __restrict__ A,
 // event sequence of one call intact when several host threads enqueue at once.
 struct SweepQueues {
     hipStream_t side = nullptr, main = nullptr;
-    hipEvent_t ev[7] = {};
+    hipEvent_t ev[9] = {};
     bool ok = false;
 };
 static std::mutex g_sweep_mu;
@@ -632,7 +632,7 @@ static kq_status gj_inverse_batched(double* A, int64_t n, int64_t lda, int64_t s
     KQ_TRY(sweep_queues(&q));
     hipStream_t sb = q->side, sm = q->main;
     hipEvent_t ev0 = q->ev[0], evG[2] = {q->ev[1], q->ev[2]}, evB[2] = {q->ev[3], q->ev[4]},
-               evM[2] = {q->ev[5], q->ev[6]};
+               evM[2] = {q->ev[5], q->ev[6]}, evS[2] = {q->ev[7], q->ev[8]};
     auto nb_of = [&](int64_t k) { return (int)((n - k * GJ_NB) < GJ_NB ? (n - k * GJ_NB) : GJ_NB); };
     auto gather = [&](int64_t k, hipStream_t qg) -> kq_status {
         const int b = (int)(k & 1), nbk = nb_of(k);
@@ -670,14 +670,17 @@ static kq_status gj_inverse_batched(double* A, int64_t n, int64_t lda, int64_t s
             KQ_TRY(gather(k + 1, st));
         }
         KQ_HIP(hipEventRecord(evG[cur], st));
-        // side queue: pivot k + 1 and the write-back of step k
+        // side queue: pivot k + 1 and the write-back of step k. The main queue starts its update only
+        // once the side queue has passed its wait (evS, recorded before the pivot launch), so the two
+        // pivot work-groups reach the dispatcher ahead of the update's tiles.
         KQ_HIP(hipStreamWaitEvent(sb, evG[cur], 0));
+        KQ_HIP(hipEventRecord(evS[cur], sb));
         if (k + 1 < nt) KQ_TRY(pivot_t(k + 1));
         hipLaunchKernelGGL(gj_scatter_kernel, gr, dim3(256), 0, sb, A, n, lda, sA, k0, nbk, T[cur], sC, Pinv[cur], skip);
         KQ_TRY(check_launch("gj_scatter"));
         KQ_HIP(hipEventRecord(evB[nxt], sb));
         // main queue: the rest of step k's update
-        KQ_HIP(hipStreamWaitEvent(sm, evG[cur], 0));
+        KQ_HIP(hipStreamWaitEvent(sm, evS[cur], 0));
         if (nt > 1) {
             GemmArgs<double> u = gemm_args<double>(n, n, nbk, T[cur], GJ_NB, C[cur], GJ_NB, A, lda, -1.0, 1.0);
             u.nb1 = batch; u.sA1 = sC; u.sB1 = sC; u.sC1 = sA; u.tri = 1; u.skip = skip; u.skip_tile = k;
@@ -694,8 +697,9 @@ static kq_status gj_inverse_batched(double* A, int64_t n, int64_t lda, int64_t s
 // ---------------------------------------------------------------------------------- DB kernels
 // With x-interval bound b after a step, the eigenvalues of Y are within about (b - 1) of those of
 // A^{1/2} (relative); 1e-8 is well below the fp32 rounding of the stored S. The bound recursion
-// reaches it within 7 steps for any cond(A) <= 1e16 even with the loose norm bounds.
-constexpr int DB_MAXIT = 8;
+// reaches it within 7 steps for any cond(A) <= 1e16 even with the loose norm bounds; a matrix that
+// has not converged after those steps is reported through info (= o + 1).
+constexpr int DB_MAXIT = 7;
 constexpr double DB_TOL = 1e-8;
 constexpr int NORM_PARTS = 32;
 
@@ -823,6 +827,10 @@ __global__ void db_converge_kernel(const double* part, const double* bnd, int64_
     if (bmax < DB_TOL) flags[0] = 1;
 }
 
+__global__ void db_final_kernel(const int* flags, int32_t* info, int32_t code) {
+    if (threadIdx.x == 0 && !flags[0] && *info == 0) *info = code;
+}
+
 __global__ void db_out_kernel(const double* YZ, int64_t n, int64_t nbk, float* S, float* Si) {
     const int64_t nn = n * n;
     for (int64_t e = blockIdx.x * 256 + threadIdx.x; e < nbk * nn; e += (int64_t)gridDim.x * 256) {
@@ -940,6 +948,8 @@ extern "C" kq_status kq_hg_sqrt(const float* HG, kq_hg_form form, int64_t o, int
                            info);
         KQ_TRY(check_launch("db_converge"));
     }
+    hipLaunchKernelGGL(db_final_kernel, dim3(1), dim3(64), 0, st, flags, info, (int32_t)(o + 1));
+    KQ_TRY(check_launch("db_final"));
     hipLaunchKernelGGL(db_out_kernel, dim3(eb), dim3(256), 0, st, YZ, n, nbk, S, Sinv);
     return check_launch("db_out");
 }
