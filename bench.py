@@ -155,7 +155,8 @@ def run_gpu(sp, steps: int, warmup: int, phases: bool):
     ph = None
     if phases:
         ph = phase_times(sp, X, W, HG, s, t, cfg, ws)
-    return ms, ph, out, iters
+    mv = matvec_times(sp, out, HG, s, t, cfg) if phases else None
+    return ms, ph, out, iters, mv
 
 
 def phase_times(sp, X, W, HG, s, t, cfg, ws, reps: int = 3) -> dict:
@@ -199,6 +200,112 @@ def phase_times(sp, X, W, HG, s, t, cfg, ws, reps: int = 3) -> dict:
         for k, (name, _) in enumerate(calls):
             res[name].append(ev[k].elapsed_time(ev[k + 1]))
     return {k: float(np.median(v)) for k, v in res.items()}
+
+
+def matvec_times(sp, out, HG, s, t, cfg, reps: int = 200) -> dict:
+    """Inference-side product y = W^ x from the packed codes this step wrote (kq_matvec_quantized:
+    x' = U^T x, the dequantizing product, then S^{-1} V^T), for 1 and 8 tokens. Time per call from HIP
+    events around `reps` calls replayed from a HIP graph (and, as `us_per_call_eager`, around `reps`
+    back-to-back calls from Python, which the host's launch cost bounds); algorithmic bytes = the
+    packed codes, the group scales and offsets, S^{-1} in its storage form, the signs, x and y."""
+    import torch
+
+    from post_quantization_03_amd import _lib as K
+
+    dev = HG.device
+    o, i = sp.o, sp.i
+    S = torch.empty_like(out["S"])
+    Sinv = torch.empty_like(out["S"])
+    info = torch.zeros(1, dtype=torch.int32, device=dev)
+    ws = torch.empty(max(K.kq_workspace_bytes("hg_sqrt", o, 0, form=cfg.form, blk=cfg.blk),
+                         K.kq_workspace_bytes("matvec", o, i, 8, form=cfg.form, blk=cfg.blk)), dtype=torch.uint8,
+                     device=dev)
+    K.kq_hg_sqrt(HG, cfg.form, o, cfg.blk, S, Sinv, info, ws)
+    res = time_matvec(sp, cfg, out["codes"], out["scale"], out["offset"], s, t, Sinv, ws, reps)
+    if int(info.item()) != 0:
+        raise RuntimeError("square root for the product did not converge")
+    return res
+
+
+def time_matvec(sp, cfg, codes, scale, offset, s, t, Sinv, ws, reps: int = 200) -> dict:
+    import torch
+
+    from post_quantization_03_amd import _lib as K
+
+    dev = codes.device
+    o, i, b = sp.o, sp.i, sp.bits
+    res = {}
+    for nt in (1, 8):
+        x = torch.randn((nt, i), dtype=torch.float32, device=dev)
+        y = torch.empty((nt, o), dtype=torch.float32, device=dev)
+
+        def call():
+            K.kq_matvec_quantized(codes, scale, offset, o, i, b, cfg.group, s, t, Sinv, cfg.form, cfg.blk, x, y, ws)
+
+        def timed(fn, n):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(n):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / n
+        for _ in range(10):
+            call()
+        torch.cuda.synchronize()
+        us_eager = 1e3 * timed(call, reps)
+        # the same call captured once in a HIP graph: replays show the device time without the
+        # host-side cost of each launch (a decode loop would replay it the same way)
+        per_graph = 20
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=side):
+                for _ in range(per_graph):
+                    call()
+        torch.cuda.current_stream().wait_stream(side)
+        g.replay()
+        torch.cuda.synchronize()
+        us = 1e3 * timed(g.replay, max(1, reps // per_graph)) / per_graph
+        nbytes = (codes.numel() * 4 + (scale.numel() + offset.numel()) * 4 + Sinv.numel() * 4 + i + o
+                  + 4 * nt * (i + o))
+        ach = nbytes / (us / 1e6)
+        res[f"nt{nt}"] = {"us_per_call": round(us, 2), "us_per_call_eager": round(us_eager, 2), "bytes": int(nbytes),
+                          "achieved_GBps": round(ach / 1e9, 1), "frac_hbm": round(ach / PEAK["hbm"], 4)}
+    return res
+
+
+def matvec_only(sp) -> dict:
+    """The inference-side product alone on the workload's layer shape and code layout: random packed
+    words (every word is a valid code stream), group scales and offsets, signs, and S^{-1} in the
+    workload's storage form (a positive diagonal, identity blocks or the identity), all device-resident."""
+    import torch
+
+    from post_quantization_03_amd import _lib as K
+    from post_quantization_03_amd.layer import LayerCfg
+
+    dev = torch.device("cuda:0")
+    cfg = LayerCfg(bits=sp.bits, group=sp.group, damp=sp.damp, form=sp.hg_form,
+                   blk=sp.hg_blk if sp.hg_form == "block" else 0)
+    g = torch.Generator(device=dev)
+    g.manual_seed(sp.o * 7 + sp.i)
+    o, i, b = sp.o, sp.i, sp.bits
+    ng = i // sp.group if sp.group else 1
+    codes = torch.randint(-2 ** 31, 2 ** 31 - 1, (o, i * b // 32), dtype=torch.int32, device=dev, generator=g)
+    scale = torch.rand((o, ng), device=dev, generator=g) * 0.01
+    offset = -scale * 2 ** (b - 1)
+    s = (torch.randint(0, 2, (i,), device=dev, generator=g) * 2 - 1).to(torch.int8)
+    t = (torch.randint(0, 2, (o,), device=dev, generator=g) * 2 - 1).to(torch.int8)
+    if cfg.form == "diag":
+        Sinv = torch.rand(o, device=dev, generator=g) + 0.5
+    elif cfg.form == "block":
+        Sinv = torch.eye(cfg.blk, device=dev).repeat(o // cfg.blk, 1, 1).contiguous()
+    else:
+        Sinv = torch.eye(o, device=dev)
+    ws = torch.empty(K.kq_workspace_bytes("matvec", o, i, 8, form=cfg.form, blk=cfg.blk), dtype=torch.uint8,
+                     device=dev)
+    return time_matvec(sp, cfg, codes, scale, offset, s, t, Sinv, ws)
 
 
 def cpu_baseline(sp, budget_s: float = 30.0) -> dict:
@@ -259,12 +366,19 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first run one plain device copy of MIB MiB (fp32 elementwise kernel), the reference "
                          "for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters to bytes")
+    ap.add_argument("--matvec-only", action="store_true",
+                    help="time only the inference-side product (kq_matvec_quantized) on the workload's layer shape "
+                         "with random codes, and print its own JSON line (not the benchmark line)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the per-layer solver runs on a single MI355X in this build "
               "(multi-GPU sharding is described in DESIGN.md, not implemented).", file=sys.stderr)
         sys.exit(2)
     sp = synth.CONFIGS[args.workload]
+    if args.matvec_only:
+        print(json.dumps({"workload": sp.name, "o": sp.o, "i": sp.i, "bits": sp.bits, "group": sp.group,
+                          "hg_form": sp.hg_form, "matvec_quantized": matvec_only(sp)}), flush=True)
+        return
     if args.copy_calibration:
         import torch
         src = torch.ones(args.copy_calibration * (1 << 18), dtype=torch.float32, device="cuda:0")
@@ -273,7 +387,7 @@ def main():
         torch.cuda.synchronize()
         print(f"# copy calibration: read {src.numel() * 4} B, wrote {dst.numel() * 4} B", file=sys.stderr, flush=True)
         del src, dst
-    ms, ph, out, iters = run_gpu(sp, args.steps, args.warmup, not args.no_phases)
+    ms, ph, out, iters, mv = run_gpu(sp, args.steps, args.warmup, not args.no_phases)
     value = sp.o * sp.i / (ms / 1e3) / 1e6
     roof, per_phase, s_cached = None, None, None
     if ph:
@@ -296,7 +410,8 @@ def main():
                                 "and the damped factor; fp32 for the rotations of W and the sweep"},
             "phases_ms": {k: round(v, 4) for k, v in ph.items()} if ph else None,
             "db_steps": iters, "s_cached_mweights_per_s": s_cached,
-            "roofline": roof, "phases_roofline": per_phase, "cpu_baseline": cpu}
+            "roofline": roof, "phases_roofline": per_phase, "cpu_baseline": cpu,
+            "matvec_quantized": mv}
     print(json.dumps(line), flush=True)
 
 

@@ -65,7 +65,8 @@ typedef enum {
     KQ_OP_CHOLINV = 4,
     KQ_OP_QUANTIZE = 5,
     KQ_OP_UNROTATE = 6,
-    KQ_OP_LOSS = 7
+    KQ_OP_LOSS = 7,
+    KQ_OP_MATVEC = 8   /* n = number of tokens */
 } kq_op;
 
 /* Workspace bytes needed by `op` for a layer of o x i weights, n calibration tokens (X dtype
@@ -179,6 +180,25 @@ kq_status kq_sensitivity(const double* HX, int64_t i, int64_t ldh, const float* 
 kq_status kq_unrotate(const float* Q, int64_t o, int64_t i, int64_t ldq, const int8_t* sign_in,
                       const int8_t* sign_out, const float* Sinv, kq_hg_form form, int64_t blk, float* What,
                       int64_t ldw, void* ws, size_t ws_bytes, kq_stream stream);
+
+/*
+ * Inference-side product with the quantized layer, y = W^ x for a block of nt tokens, with
+ * W^ = S^{-1} V^T Q'' U^T applied factor by factor instead of materialising W^ (review page,
+ * Limitations (3): inference reverts the orthogonal transforms online at Theta(d log d) per layer,
+ * which a fused kernel keeps close to the cost of the weight matvec):
+ *     x' = U^T x = H_i (s * x) / sqrt(i)         (fast transform per token)
+ *     z  = Q'' x'                                 (dequantized on the fly from the packed codes)
+ *     y  = S^{-1} V^T z = S^{-1} (t * H_o^T z) / sqrt(o)
+ * codes, scale, offset: as written by kq_quantize_layer for this (o, i, bits, group); group must be
+ * 0 or a multiple of 32 dividing i; bits in 2..8; o a multiple of 4. sign_in (i), sign_out (o), Sinv (storage
+ * form of H_G): as for kq_unrotate. X: nt x i fp32 tokens, leading dimension ldx (16-byte aligned);
+ * Y: nt x o fp32, leading dimension ldy (must not alias X). Workspace: kq_workspace_bytes with
+ * op KQ_OP_MATVEC and n = nt.
+ */
+kq_status kq_matvec_quantized(const uint32_t* codes, const float* scale, const float* offset, int64_t o, int64_t i,
+                              int bits, int group, const int8_t* sign_in, const int8_t* sign_out, const float* Sinv,
+                              kq_hg_form form, int64_t blk, const float* X, int64_t ldx, int64_t nt, float* Y,
+                              int64_t ldy, void* ws, size_t ws_bytes, kq_stream stream);
 
 /*
  * Verification: layer loss in rotated coordinates, sum_r (Q - W2)_r HX2 (Q - W2)_r^T, which equals

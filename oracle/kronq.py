@@ -335,6 +335,19 @@ def unrotate(Q2: np.ndarray, s: np.ndarray, t: np.ndarray, Sinv: np.ndarray, for
     return _unrot(A, s, axis=1)                             # (.) U^T: row a -> s * (H_i^T a) / sqrt(i)
 
 
+def matvec_quantized(words: np.ndarray, mu: np.ndarray, scale: np.ndarray, bits: int, group: int, s: np.ndarray,
+                     t: np.ndarray, Sinv: np.ndarray, form: str, X: np.ndarray) -> np.ndarray:
+    """Inference-side product Y = X W^^T for token rows X (n x i), from the packed codes.
+
+    KronQ review page, Limitations (3): at inference the stored Q'' is used through the
+    reverted transforms, W^ = S^{-1} V^T Q'' U^T. Written as the definition: decode the codes,
+    dequantize, revert the rotations and H_G^{1/2}, then multiply."""
+    X = np.asarray(X, np.float64)
+    Q2 = dequantize(unpack(words, bits, X.shape[1]), np.asarray(mu, np.float64), np.asarray(scale, np.float64), group)
+    What = unrotate(Q2, s, t, Sinv, form)
+    return X @ What.T
+
+
 def kfac_loss(W: np.ndarray, What: np.ndarray, HX: np.ndarray, HG: np.ndarray, form: str) -> float:
     """tr(H_G dW H_X dW^T) with the undamped H_X."""
     dW = np.asarray(What, np.float64) - np.asarray(W, np.float64)

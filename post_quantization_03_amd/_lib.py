@@ -13,10 +13,10 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkq.so")
 KQ_F32, KQ_BF16 = 0, 1
 HG_FORM = {"diag": 0, "block": 1, "full": 2}
 OP = {"hessian": 0, "rotate_in": 1, "hg_sqrt": 2, "rotate_out": 3, "cholinv": 4, "quantize": 5, "unrotate": 6,
-      "loss": 7}
+      "loss": 7, "matvec": 8}
 EXPORTS = ("kq_workspace_bytes", "kq_hessian_accum", "kq_rotate_in", "kq_hg_sqrt", "kq_rotate_out", "kq_cholinv",
            "kq_quantize_layer", "kq_sensitivity", "kq_unrotate", "kq_layer_loss", "kq_strerror", "kq_last_error",
-           "kq_hadamard_order", "kq_version", "kq_allocate_bits")
+           "kq_hadamard_order", "kq_version", "kq_allocate_bits", "kq_matvec_quantized")
 
 
 class KQError(RuntimeError):
@@ -54,6 +54,8 @@ def lib() -> ctypes.CDLL:
         "kq_version": (_int, []),
         "kq_allocate_bits": (_int, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_i64), _i64, ctypes.c_double, _int,
                                     _int, ctypes.POINTER(ctypes.c_int32)]),
+        "kq_matvec_quantized": (_int, [_vp, _vp, _vp, _i64, _i64, _int, _int, _vp, _vp, _vp, _int, _i64, _vp, _i64, _i64,
+                                       _vp, _i64, _vp, _sz, _vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -171,6 +173,17 @@ def kq_unrotate(Q, sign_in, sign_out, Sinv, form: str, blk: int, What, ws=None, 
     w, wb = _ws(ws)
     _check("kq_unrotate", lib().kq_unrotate(_p(Q), o, i, Q.stride(0), _p(sign_in), _p(sign_out), _p(Sinv),
                                             HG_FORM[form], blk, _p(What), What.stride(0), w, wb, _stream(stream)))
+
+
+def kq_matvec_quantized(codes, scale, offset, o: int, i: int, bits: int, group: int, sign_in, sign_out, Sinv,
+                        form: str, blk: int, X, Y, ws=None, stream=None) -> None:
+    """Y (nt x o) = W^ X^T for the tokens in the rows of X (nt x i), from the packed codes."""
+    nt = X.shape[0]
+    w, wb = _ws(ws)
+    _check("kq_matvec_quantized", lib().kq_matvec_quantized(_p(codes), _p(scale), _p(offset), o, i, bits, group,
+                                                            _p(sign_in), _p(sign_out), _p(Sinv), HG_FORM[form], blk,
+                                                            _p(X), X.stride(0), nt, _p(Y), Y.stride(0), w, wb,
+                                                            _stream(stream)))
 
 
 def kq_layer_loss(W2, Q, HX2, row_loss, loss, ws=None, stream=None) -> None:

@@ -14,6 +14,7 @@ size_t rotate_out_ws(int64_t o, int64_t i, kq_hg_form form);
 size_t unrotate_ws(int64_t o, int64_t i, kq_hg_form form);
 size_t quantize_ws(int64_t o);
 size_t loss_ws(int64_t o, int64_t i);
+size_t matvec_ws(int64_t o, int64_t i, int64_t nt, kq_hg_form form);
 
 namespace kq {
 
@@ -72,6 +73,7 @@ extern "C" size_t kq_workspace_bytes(kq_op op, int64_t o, int64_t i, int64_t n, 
         case KQ_OP_QUANTIZE: return quantize_ws(o);
         case KQ_OP_UNROTATE: return unrotate_ws(o, i, form);
         case KQ_OP_LOSS: return loss_ws(o, i);
+        case KQ_OP_MATVEC: return matvec_ws(o, i, n, form);
     }
     return 0;
 }

@@ -119,7 +119,8 @@ __global__ void paley_kernel(T* P, int m, Field f, int transpose) {
 template <int IN, typename T>
 __global__ __launch_bounds__(256) void fwht_rows_kernel(const void* __restrict__ in, int64_t ldin, T* __restrict__ out,
                                                         int64_t ldout, int64_t d, int lp2, const int8_t* __restrict__ pre,
-                                                        const int8_t* __restrict__ post, T scale) {
+                                                        const int8_t* __restrict__ post, T scale,
+                                                        const float* __restrict__ post_scale) {
     extern __shared__ __align__(16) unsigned char xr_raw[];
     T* xr = reinterpret_cast<T*>(xr_raw);
     const int64_t r = blockIdx.x;
@@ -174,7 +175,11 @@ __global__ __launch_bounds__(256) void fwht_rows_kernel(const void* __restrict__
     T* dst = out + r * ldout;
     for (int64_t c = 4 * tid; c < d; c += 1024) {
 #pragma unroll
-        for (int e = 0; e < 4; e++) dst[c + e] = post ? xr[c + e] * scale * (T)post[c + e] : xr[c + e] * scale;
+        for (int e = 0; e < 4; e++) {
+            T v = post ? xr[c + e] * scale * (T)post[c + e] : xr[c + e] * scale;
+            if (post_scale) v *= (T)post_scale[c + e];
+            dst[c + e] = v;
+        }
     }
 }
 
@@ -242,7 +247,8 @@ __global__ __launch_bounds__(256) void fwht_cols_kernel(const T* __restrict__ in
 // in_kind: 0 bf16, 1 fp32, 2 fp64.
 template <typename T>
 static kq_status rows_transform(const void* in, int in_kind, int64_t ldin, T* out, int64_t ldout, int64_t R, int64_t d,
-                                int64_t p2, const int8_t* pre, const int8_t* post, T scale, hipStream_t st) {
+                                int64_t p2, const int8_t* pre, const int8_t* post, T scale, hipStream_t st,
+                                const float* post_scale = nullptr) {
     if (R <= 0) return KQ_OK;
     int lp2 = 0;
     while ((int64_t(1) << lp2) < p2) lp2++;
@@ -257,11 +263,11 @@ static kq_status rows_transform(const void* in, int in_kind, int64_t ldin, T* ou
         attr = true;
     }
     if (in_kind == 0)
-        hipLaunchKernelGGL((fwht_rows_kernel<0, T>), dim3((unsigned)R), dim3(256), smem, st, in, ldin, out, ldout, d, lp2, pre, post, scale);
+        hipLaunchKernelGGL((fwht_rows_kernel<0, T>), dim3((unsigned)R), dim3(256), smem, st, in, ldin, out, ldout, d, lp2, pre, post, scale, post_scale);
     else if (in_kind == 1)
-        hipLaunchKernelGGL((fwht_rows_kernel<1, T>), dim3((unsigned)R), dim3(256), smem, st, in, ldin, out, ldout, d, lp2, pre, post, scale);
+        hipLaunchKernelGGL((fwht_rows_kernel<1, T>), dim3((unsigned)R), dim3(256), smem, st, in, ldin, out, ldout, d, lp2, pre, post, scale, post_scale);
     else
-        hipLaunchKernelGGL((fwht_rows_kernel<2, T>), dim3((unsigned)R), dim3(256), smem, st, in, ldin, out, ldout, d, lp2, pre, post, scale);
+        hipLaunchKernelGGL((fwht_rows_kernel<2, T>), dim3((unsigned)R), dim3(256), smem, st, in, ldin, out, ldout, d, lp2, pre, post, scale, post_scale);
     return check_launch("fwht_rows");
 }
 
@@ -533,4 +539,246 @@ extern "C" kq_status kq_unrotate(const float* Q, int64_t o, int64_t i, int64_t l
         cur = other;
     }
     return rows_transform<float>(cur, 1, i, What, ldw, o, i, pi, nullptr, sign_in, inv_i, st);
+}
+
+// ------------------------------------------------------------------------- few long vectors
+// out_r = post_scale * post * scale * ((P (x) H_p2) (pre * in_r)) for a handful of rows r of length
+// d = m p2, spread over many workgroups (one row per workgroup would leave the chip idle). The
+// Sylvester part factors along the index c = hi * VT_BL + lo as H_{p2/VT_BL} (x) H_{VT_BL}: the
+// block pass transforms lo inside LDS, the stride pass transforms hi in registers, and the Paley
+// pass mixes the m chunks of p2 (each output element is one row of P against a column of chunks).
+namespace kq {
+
+constexpr int VT_BL = 512;      // block of the first pass (two elements per thread)
+constexpr int VT_MAXL = 64;     // longest stride pass: p2 <= VT_BL * VT_MAXL
+
+struct VecOps {
+    const int8_t* pre = nullptr;
+    const int8_t* post = nullptr;
+    const float* post_scale = nullptr;
+    float scale = 1.0f;
+};
+
+__device__ __forceinline__ float vt_post(float v, int64_t idx, const VecOps& op) {
+    v *= op.scale;
+    if (op.post) v *= (float)op.post[idx];
+    if (op.post_scale) v *= op.post_scale[idx];
+    return v;
+}
+
+// Sylvester transform of `bl` consecutive elements (bl = min(p2, VT_BL), a power of two)
+__global__ __launch_bounds__(256) void vt_block_kernel(const float* __restrict__ in, int64_t ldin, float* __restrict__ out,
+                                                       int64_t ldout, int bl, int lbl, VecOps op, int last) {
+    __shared__ float sh[VT_BL];
+    const int tid = threadIdx.x;
+    const int64_t r = blockIdx.y, base = (int64_t)blockIdx.x * bl;
+    const float* src = in + r * ldin + base;
+    for (int e = tid; e < bl; e += 256) sh[e] = op.pre ? src[e] * (float)op.pre[base + e] : src[e];
+    __syncthreads();
+    for (int l = 0; l < lbl; l++) {
+        const int h = 1 << l;
+        for (int g = tid; g < bl / 2; g += 256) {
+            const int j = ((g >> l) << (l + 1)) + (g & (h - 1));
+            const float a = sh[j], b = sh[j + h];
+            sh[j] = a + b;
+            sh[j + h] = a - b;
+        }
+        __syncthreads();
+    }
+    float* dst = out + r * ldout + base;
+    for (int e = tid; e < bl; e += 256) dst[e] = last ? vt_post(sh[e], base + e, op) : sh[e];
+}
+
+// Sylvester transform along hi (length L = p2 / VT_BL) for every (chunk, lo) column, in registers
+template <int L>
+__global__ __launch_bounds__(256) void vt_stride_kernel(const float* __restrict__ in, int64_t ldin, float* __restrict__ out,
+                                                        int64_t ldout, int64_t d, int64_t p2, VecOps op, int last) {
+    const int64_t r = blockIdx.y;
+    const int64_t col = (int64_t)blockIdx.x * 256 + threadIdx.x;    // chunk * VT_BL + lo
+    if (col >= d / L) return;
+    const int64_t chunk = col / VT_BL, lo = col % VT_BL;
+    const int64_t b0 = chunk * p2 + lo;
+    float v[L];
+#pragma unroll
+    for (int k = 0; k < L; k++) v[k] = in[r * ldin + b0 + (int64_t)k * VT_BL];
+#pragma unroll
+    for (int h = 1; h < L; h <<= 1)
+#pragma unroll
+        for (int k = 0; k < L; k++)
+            if ((k & h) == 0) {
+                const float a = v[k], b = v[k + h];
+                v[k] = a + b;
+                v[k + h] = a - b;
+            }
+#pragma unroll
+    for (int k = 0; k < L; k++) {
+        const int64_t idx = b0 + (int64_t)k * VT_BL;
+        out[r * ldout + idx] = last ? vt_post(v[k], idx, op) : v[k];
+    }
+}
+
+// out[j p2 + c] = post(sum_a P[j][a] in[a p2 + c])
+__global__ __launch_bounds__(256) void vt_paley_kernel(const float* __restrict__ P, int m, const float* __restrict__ in,
+                                                       int64_t ldin, float* __restrict__ out, int64_t ldout, int64_t p2,
+                                                       VecOps op) {
+    const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int j = blockIdx.y;
+    const int64_t r = blockIdx.z;
+    if (c >= p2) return;
+    const float* src = in + r * ldin + c;
+    const float* prow = P + (int64_t)j * m;
+    // four independent partial sums (a mod 4) keep several loads in flight
+    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    int a = 0;
+    for (; a + 4 <= m; a += 4) {
+#pragma unroll
+        for (int q = 0; q < 4; q++) acc[q] = fmaf(prow[a + q], src[(int64_t)(a + q) * p2], acc[q]);
+    }
+    for (; a < m; a++) acc[a & 3] = fmaf(prow[a], src[(int64_t)a * p2], acc[a & 3]);
+    const float sum = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+    const int64_t idx = (int64_t)j * p2 + c;
+    out[r * ldout + idx] = vt_post(sum, idx, op);
+}
+
+// R rows (R <= 65535) of length d = m p2 (p2 a power of two, p2 <= VT_BL * VT_MAXL); tmp: R x d
+// scratch (leading dimension d), may not alias in or out; out may alias in.
+static kq_status vec_transform(const float* in, int64_t ldin, float* out, int64_t ldout, int64_t R, int64_t m, int64_t p2,
+                               const float* P, const VecOps& op, float* tmp, hipStream_t st) {
+    const int64_t d = m * p2;
+    if (R <= 0) return KQ_OK;
+    if (R > 65535 || p2 > (int64_t)VT_BL * VT_MAXL || m > 65535) return fail(KQ_ESHAPE, "vector transform: too large");
+    const int bl = (int)(p2 < VT_BL ? p2 : VT_BL);
+    int lbl = 0;
+    while ((1 << lbl) < bl) lbl++;
+    const int64_t L = p2 / bl;
+    // pass results go to tmp or out so that the last pass writes out
+    const int passes = 1 + (L > 1) + (m > 1);
+    VecOps first = op, mid;
+    first.post = nullptr; first.post_scale = nullptr; first.scale = 1.0f;
+    mid.scale = 1.0f;
+    int done = 0;
+    auto dst_of = [&](int k) { return (passes - k) % 2 == 1 ? out : tmp; };   // the last pass writes out
+    auto ld_of = [&](float* p) { return p == out ? ldout : d; };
+    const float* cur = in;
+    int64_t ldc = ldin;
+    {
+        float* dst = dst_of(done);
+        const bool last = ++done == passes;
+        VecOps o1 = first;
+        if (last) { o1.post = op.post; o1.post_scale = op.post_scale; o1.scale = op.scale; }
+        hipLaunchKernelGGL(vt_block_kernel, dim3((unsigned)(d / bl), (unsigned)R), dim3(256), 0, st, cur, ldc, dst,
+                           ld_of(dst), bl, lbl, o1, last ? 1 : 0);
+        KQ_TRY(check_launch("vt_block"));
+        cur = dst; ldc = ld_of(dst);
+    }
+    if (L > 1) {
+        float* dst = dst_of(done);
+        const bool last = ++done == passes;
+        const VecOps o2 = last ? op : mid;
+        const dim3 grid((unsigned)((d / L + 255) / 256), (unsigned)R);
+        switch (L) {
+#define KQ_VT_STRIDE(n) case n: hipLaunchKernelGGL((vt_stride_kernel<n>), grid, dim3(256), 0, st, cur, ldc, dst, ld_of(dst), d, p2, o2, last ? 1 : 0); break;
+            KQ_VT_STRIDE(2) KQ_VT_STRIDE(4) KQ_VT_STRIDE(8) KQ_VT_STRIDE(16) KQ_VT_STRIDE(32) KQ_VT_STRIDE(64)
+#undef KQ_VT_STRIDE
+            default: return fail(KQ_ESHAPE, "vector transform: bad stride length");
+        }
+        KQ_TRY(check_launch("vt_stride"));
+        cur = dst; ldc = ld_of(dst);
+    }
+    if (m > 1) {
+        float* dst = dst_of(done);
+        ++done;
+        const dim3 grid((unsigned)((p2 + 255) / 256), (unsigned)m, (unsigned)R);
+        hipLaunchKernelGGL(vt_paley_kernel, grid, dim3(256), 0, st, P, (int)m, cur, ldc, dst, ld_of(dst), p2, op);
+        KQ_TRY(check_launch("vt_paley"));
+    }
+    return KQ_OK;
+}
+
+}  // namespace kq
+
+// ------------------------------------------------------------------------- inference-side matvec
+namespace kq {
+kq_status dequant_gemv(const uint32_t* codes, const float* scale, const float* offset, int64_t o, int64_t i, int bits,
+                       int group, const float* X, int64_t ldx, int64_t nt, float* Zt, int64_t ldz, float* Zp,
+                       hipStream_t st);
+size_t dequant_ws(int64_t o, int64_t i, int64_t nt);
+kq_status sinv_gemv(const float* A, int64_t o, int64_t blk, const float* Zt, int64_t ldz, int64_t nt, float* Y,
+                    int64_t ldy, hipStream_t st);
+}  // namespace kq
+
+size_t matvec_ws(int64_t o, int64_t i, int64_t nt, kq_hg_form form) {
+    int64_t mo, po, mi, pi;
+    Field fo, fi;
+    if (!hadamard_split(o, mo, po, fo) || !hadamard_split(i, mi, pi, fi) || nt <= 0) return 0;
+    Sizer z;
+    z.take<float>((size_t)mo * mo);
+    z.take<float>((size_t)mi * mi);
+    z.take<float>((size_t)nt * i);   // X'
+    z.take<float>((size_t)nt * i);   // Paley scratch
+    z.take<float>((size_t)nt * o);   // Z^T
+    z.take<float>((size_t)nt * o);   // Paley scratch
+    z.take<float>((size_t)nt * o);   // V^T z
+    z.take<char>(dequant_ws(o, i, nt));
+    (void)form;
+    return z.used;
+}
+
+extern "C" kq_status kq_matvec_quantized(const uint32_t* codes, const float* scale, const float* offset, int64_t o,
+                                         int64_t i, int bits, int group, const int8_t* sign_in, const int8_t* sign_out,
+                                         const float* Sinv, kq_hg_form form, int64_t blk, const float* X, int64_t ldx,
+                                         int64_t nt, float* Y, int64_t ldy, void* ws, size_t ws_bytes,
+                                         kq_stream stream) {
+    if (!codes || !scale || !offset || !sign_in || !sign_out || !Sinv || !X || !Y)
+        return fail(KQ_EINVAL, "kq_matvec_quantized: null pointer");
+    if (o <= 0 || i <= 0 || nt <= 0 || nt > 65535 || ldx < i || ldy < o)
+        return fail(KQ_ESHAPE, "kq_matvec_quantized: bad sizes");
+    if (bits < 2 || bits > 8) return fail(KQ_EUNSUPPORTED, "kq_matvec_quantized: bits");
+    if (group != 0 && (group % 32 || i % group)) return fail(KQ_EUNSUPPORTED, "kq_matvec_quantized: group");
+    if (i % 32 || (i * bits) % 32) return fail(KQ_ESHAPE, "kq_matvec_quantized: i must be a multiple of 32");
+    if (ldx % 4 || !aligned16(X)) return fail(KQ_EINVAL, "kq_matvec_quantized: X alignment");
+    if (form == KQ_HG_BLOCK && (blk <= 0 || o % blk)) return fail(KQ_ESHAPE, "kq_matvec_quantized: bad block size");
+    if (form != KQ_HG_DIAG && form != KQ_HG_BLOCK && form != KQ_HG_FULL) return fail(KQ_EINVAL, "kq_matvec_quantized: form");
+    int64_t mo, po, mi, pi;
+    Field fo, fi;
+    if (!hadamard_split(o, mo, po, fo) || !hadamard_split(i, mi, pi, fi))
+        return fail(KQ_EUNSUPPORTED, "kq_matvec_quantized: no Hadamard order");
+    if (o % 4) return fail(KQ_ESHAPE, "kq_matvec_quantized: o must be a multiple of 4");
+    if (!ws || ws_bytes < matvec_ws(o, i, nt, form)) return fail(KQ_EWORKSPACE, "kq_matvec_quantized: workspace too small");
+    hipStream_t st = hs(stream);
+    Arena ar(ws, ws_bytes);
+    float* Po = ar.take<float>((size_t)mo * mo);
+    float* Pi = ar.take<float>((size_t)mi * mi);
+    float* Xr = ar.take<float>((size_t)nt * i);
+    float* Xt = ar.take<float>((size_t)nt * i);
+    float* Zt = ar.take<float>((size_t)nt * o);
+    float* T1 = ar.take<float>((size_t)nt * o);
+    float* T2 = ar.take<float>((size_t)nt * o);
+    const size_t zp_bytes = dequant_ws(o, i, nt);
+    float* Zp = zp_bytes ? reinterpret_cast<float*>(ar.take<char>(zp_bytes)) : nullptr;
+    // x' = U^T x: every token row x -> H_i (s * x) / sqrt(i)
+    VecOps xin;
+    xin.pre = sign_in;
+    xin.scale = (float)(1.0 / std::sqrt((double)i));
+    if (mi > 1) KQ_TRY(make_paley<float>(Pi, mi, fi, false, st));
+    KQ_TRY(vec_transform(X, ldx, Xr, i, nt, mi, pi, Pi, xin, Xt, st));
+    // z^T = x'^T Q''^T from the packed codes, one row of length o per token
+    KQ_TRY(dequant_gemv(codes, scale, offset, o, i, bits, group, Xr, i, nt, Zt, o, Zp, st));
+    // V^T z = t * (H_o^T z) / sqrt(o) along each token row, H_o^T = P_o^T (x) H; a diagonal S^{-1}
+    // is folded into the same pass and written straight to Y
+    VecOps vout;
+    vout.post = sign_out;
+    vout.scale = (float)(1.0 / std::sqrt((double)o));
+    if (form == KQ_HG_DIAG) vout.post_scale = Sinv;
+    if (mo > 1) KQ_TRY(make_paley<float>(Po, mo, fo, true, st));
+    if (form == KQ_HG_DIAG) return vec_transform(Zt, o, Y, ldy, nt, mo, po, Po, vout, T1, st);
+    KQ_TRY(vec_transform(Zt, o, T2, o, nt, mo, po, Po, vout, T1, st));
+    const int64_t b = form == KQ_HG_FULL ? o : blk;
+    if (sinv_gemv(Sinv, o, b, T2, o, nt, Y, ldy, st) == KQ_OK) return KQ_OK;   // up to 8 tokens
+    // y_t = S^{-1} v_t for every token: Y = V S^{-T} (blockwise for the block form)
+    GemmArgs<float> g = gemm_args<float>(nt, b, b, T2, o, Sinv, b, Y, ldy, 1.0f, 0.0f);
+    if (form == KQ_HG_BLOCK) {
+        g.nb1 = o / blk; g.sA1 = blk; g.sB1 = blk * blk; g.sC1 = blk;
+    }
+    return gemm<float>(g, false, true, st);
 }

@@ -72,3 +72,23 @@ def hx_tol(n: int) -> float:
     1e-5 relative bound on H_X for every n >= 32."""
     return 1e-6 * (32.0 / n) ** 0.5
 
+
+
+def matvec_error_scale(words: np.ndarray, mu: np.ndarray, scale: np.ndarray, bits: int, group: int, s: np.ndarray,
+                       Sinv: np.ndarray, form: str, X: np.ndarray) -> np.ndarray:
+    """Per-token scale of the fp32 rounding error of the factored product y = S^{-1} V^T Q'' U^T x:
+    ||S^{-1}||_2 * || |Q''| |x'| ||_2 with x' = U^T x. The sums over the codes carry an error of at
+    most a few ulps of |Q''| |x'| per element; the orthogonal transforms keep 2-norms, and S^{-1}
+    can grow them by at most its spectral norm."""
+    X = np.asarray(X, np.float64)
+    i = X.shape[1]
+    Q2 = kq.dequantize(kq.unpack(words, bits, i), np.asarray(mu, np.float64), np.asarray(scale, np.float64), group)
+    Xr = kq.rotate_in_weights(X, s)                     # rows x' = U^T x
+    Z = np.abs(Xr) @ np.abs(Q2).T                       # n x o
+    if form == "diag":
+        nrm = np.max(np.abs(Sinv))
+    elif form == "block":
+        nrm = max(np.linalg.norm(b, 2) for b in np.asarray(Sinv, np.float64))
+    else:
+        nrm = np.linalg.norm(np.asarray(Sinv, np.float64), 2)
+    return nrm * np.linalg.norm(Z, axis=1)

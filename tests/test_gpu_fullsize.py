@@ -180,3 +180,24 @@ def test_fullsize_stack():
             Q = np.stack([cmp["Q"][q] for q in range(len(rows))])
             assert rel_fro(host(out.Q[kk])[rows], Q) <= 1e-4
         say(f"  layer {li}: 7 sublayers match on sampled rows")
+
+
+@pytest.mark.parametrize("name,nt", [("C2", 1), ("C2", 8), ("C4", 1)])
+def test_fullsize_matvec(name, nt):
+    """Inference-side product at the layer's full size and code layout (random packed words, the
+    same grid of slices and token passes as the benchmark's calls), every output against the oracle."""
+    from tests.test_gpu_ops import matvec_case, run_matvec
+    from tests.parity import matvec_error_scale
+    sp = synth.CONFIGS[name]
+    blk = sp.hg_blk if sp.hg_form == "block" else 0
+    say(f"matvec full size {name} o={sp.o} i={sp.i} bits={sp.bits} group={sp.group} nt={nt}")
+    rng = np.random.default_rng(sp.o + nt)
+    words, sc, mu, s, t, Si, X = matvec_case(rng, sp.o, sp.i, sp.bits, sp.group, nt, sp.hg_form, blk)
+    Y = run_matvec(words, sc, mu, sp.o, sp.i, sp.bits, sp.group, s, t, Si, sp.hg_form, blk, X)
+    say("  GPU done")
+    ref = kq.matvec_quantized(words, mu, sc, sp.bits, sp.group, s, t, Si.astype(np.float64), sp.hg_form, X)
+    scale = matvec_error_scale(words, mu, sc, sp.bits, sp.group, s, Si, sp.hg_form, X)
+    err = np.linalg.norm(Y - ref, axis=1)
+    say(f"  max error / scale {(err / scale).max():.2e}")
+    assert np.all(np.isfinite(Y))
+    assert np.all(err <= 1e-5 * scale)

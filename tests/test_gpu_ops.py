@@ -11,7 +11,7 @@ import synth
 from oracle import kronq as kq
 from post_quantization_03_amd import _lib as K
 from tests.gpu_util import host, say, to_dev, torch_dev, ws_tensor
-from tests.parity import gpu_words_to_codes, hx_tol, rel_fro, replay_compare
+from tests.parity import gpu_words_to_codes, hx_tol, matvec_error_scale, rel_fro, replay_compare
 
 pytestmark = pytest.mark.gpu
 f32 = np.float32
@@ -255,6 +255,61 @@ def test_unrotate_and_loss(form, o, i, blk):
     assert np.allclose(host(rl), lref, rtol=1e-4)
 
 
+# ----------------------------------------------------------------------------- inference-side product
+MATVEC_TOL = 1e-5
+
+
+def matvec_case(rng, o, i, bits, group, nt, form, blk):
+    """Random packed codes (any word is a valid stream), group scales s > 0 and offsets about
+    -s 2^(b-1) as a min-max grid would give, tokens with log-normal channel scales."""
+    g = group if group else i
+    words = rng.integers(0, 2 ** 32, size=(o, i * bits // 32), dtype=np.uint64).astype(np.uint32)
+    sc = (0.002 * np.exp(0.5 * rng.standard_normal((o, i // g)))).astype(f32)
+    mu = (-sc * (2 ** (bits - 1)) * (1 + 0.1 * rng.standard_normal((o, i // g)))).astype(f32)
+    s, t = signs(rng, i), signs(rng, o)
+    if form == "diag":
+        Si = np.exp(rng.standard_normal(o)).astype(f32)
+    elif form == "block":
+        Si = np.stack([spd_f32(rng, blk) for _ in range(o // blk)])
+    else:
+        Si = spd_f32(rng, o)
+    X = (rng.standard_normal((nt, i)) * np.exp(rng.standard_normal(i))).astype(f32)
+    return words, sc, mu, s, t, Si, X
+
+
+def run_matvec(words, sc, mu, o, i, bits, group, s, t, Si, form, blk, X):
+    torch, dev = torch_dev()
+    nt = X.shape[0]
+    Y = torch.full((nt, o), float("nan"), dtype=torch.float32, device=dev)
+    ws = ws_tensor(K.kq_workspace_bytes("matvec", o, i, nt, form=form, blk=blk))
+    K.kq_matvec_quantized(torch.from_numpy(words.view(np.int32)).to(dev), to_dev(sc), to_dev(mu), o, i, bits, group,
+                          to_dev(s, "i8"), to_dev(t, "i8"), to_dev(Si), form, blk, to_dev(X), Y, ws)
+    return host(Y)
+
+
+@pytest.mark.parametrize("form,o,i,bits,group,nt,blk", [
+    ("diag", 256, 256, 4, 128, 1, 0),
+    ("full", 320, 512, 3, 128, 3, 0),
+    ("block", 256, 1728, 2, 0, 5, 64),
+    ("diag", 40, 5120, 5, 64, 8, 0),       # ragged rows, ragged last column slice
+    ("diag", 96, 4096, 6, 32, 11, 0),      # two token passes (8 + 3), column slices
+    ("full", 64, 13824, 7, 128, 2, 0),     # Paley input order, six slices
+    ("block", 128, 2048, 8, 256, 4, 128),
+    ("full", 128, 256, 4, 32, 9, 0),       # more than 8 tokens: S^{-1} through the general GEMM
+    ("block", 96, 256, 3, 128, 2, 6),      # block size not a multiple of 4: general GEMM
+])
+def test_matvec_quantized(form, o, i, bits, group, nt, blk):
+    say(f"matvec {form} o={o} i={i} bits={bits} group={group} nt={nt}")
+    rng = np.random.default_rng(o * 31 + i + bits)
+    words, sc, mu, s, t, Si, X = matvec_case(rng, o, i, bits, group, nt, form, blk)
+    Y = run_matvec(words, sc, mu, o, i, bits, group, s, t, Si, form, blk, X)
+    ref = kq.matvec_quantized(words, mu, sc, bits, group, s, t, Si.astype(np.float64), form, X)
+    scale = matvec_error_scale(words, mu, sc, bits, group, s, Si, form, X)
+    err = np.linalg.norm(Y - ref, axis=1)
+    assert np.all(np.isfinite(Y))
+    assert np.all(err <= MATVEC_TOL * scale), (err / scale).max()
+
+
 def test_argument_errors_are_reported():
     torch, dev = torch_dev()
     W = torch.zeros((8, 100), dtype=torch.float32, device=dev)
@@ -265,3 +320,34 @@ def test_argument_errors_are_reported():
     with pytest.raises(K.KQError) as e:
         K.kq_rotate_in(W, W, None, torch.ones(100, dtype=torch.int8, device=dev), ws_tensor(1 << 20))
     assert e.value.status == 4   # 100 = 25 * 4: no Hadamard order
+
+
+def test_matvec_quantized_graph_replays():
+    """The product captured in a HIP graph (as a decode loop would replay it): every replay, with
+    eager work and synchronisations between replays, equals the eager call."""
+    torch, dev = torch_dev()
+    o, i, bits, group, nt, form, blk = 256, 4096, 3, 128, 2, "full", 0
+    rng = np.random.default_rng(77)
+    words, sc, mu, s, t, Si, X = matvec_case(rng, o, i, bits, group, nt, form, blk)
+    args = [torch.from_numpy(words.view(np.int32)).to(dev), to_dev(sc), to_dev(mu), o, i, bits, group,
+            to_dev(s, "i8"), to_dev(t, "i8"), to_dev(Si), form, blk]
+    x = to_dev(X)
+    ws = ws_tensor(K.kq_workspace_bytes("matvec", o, i, nt, form=form, blk=blk))
+    y_eager = torch.empty((nt, o), dtype=torch.float32, device=dev)
+    K.kq_matvec_quantized(*args, x, y_eager, ws)
+    ref = host(y_eager).copy()
+    y = torch.full((nt, o), float("nan"), dtype=torch.float32, device=dev)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            K.kq_matvec_quantized(*args, x, y, ws)
+    torch.cuda.current_stream().wait_stream(side)
+    for k in range(3):
+        y.fill_(float("nan"))
+        K.kq_matvec_quantized(*args, x, y_eager, ws)     # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(host(y), ref), k

@@ -369,6 +369,58 @@ def test_pack_matches_big_integer_bitstream():
     assert int(kq.pack(c, 3)[0, 0]) == w0
 
 
+# ----------------------------------------------------------------------------- P13
+@pytest.mark.parametrize("form", ["diag", "full"])
+def test_p13_matvec_zero_codes_closed_form(form):
+    """Inference-side product (KronQ review page, Limitations (3)) with every code 0 and mu = 1
+    (one group per row): Q'' = 1 1^T, and with a Sylvester Hadamard (first row and column all
+    ones) U 1 = sqrt(i) s_0 e_0 and V^T 1 = sqrt(o) t_0 e_0, so W^ x = sqrt(o i) s_0 t_0 x_0 S^{-1} e_0."""
+    rng = np.random.default_rng(21)
+    o, i, bits, n = 16, 64, 4, 3
+    s, t = signs(rng, i), signs(rng, o)
+    Si = np.exp(rng.standard_normal(o)) if form == "diag" else spd(rng, o)
+    words = np.zeros((o, i * bits // 32), np.uint32)
+    mu = np.ones((o, 1))
+    sc = rng.random((o, 1))
+    X = rng.standard_normal((n, i))
+    Y = kq.matvec_quantized(words, mu, sc, bits, 0, s, t, Si, form, X)
+    e0 = np.zeros(o)
+    e0[0] = 1.0
+    col0 = Si * e0 if form == "diag" else Si[:, 0]       # S^{-1} e_0
+    want = np.sqrt(o * i) * s[0] * t[0] * X[:, :1] * col0[None, :]
+    assert np.allclose(Y, want, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("bits,group", [(3, 0), (2, 32), (5, 32)])
+def test_p13_matvec_brute_force(bits, group):
+    """The same product by brute force on a tiny layer: codes read bit by bit from the words as
+    one big integer per row, w = mu + s q per element, dense Sylvester matrices from scipy, and
+    y = S^{-1} V^T Q'' U^T x as plain dense products."""
+    from scipy.linalg import hadamard as sylvester
+    rng = np.random.default_rng(bits * 7 + group)
+    o, i, n = 8, 64, 2
+    words = rng.integers(0, 2 ** 32, size=(o, i * bits // 32), dtype=np.uint64).astype(np.uint32)
+    g = group if group else i
+    mu = rng.standard_normal((o, i // g))
+    sc = rng.random((o, i // g))
+    s, t = signs(rng, i), signs(rng, o)
+    Si = spd(rng, o)
+    X = rng.standard_normal((n, i))
+    Q = np.zeros((o, i))
+    for r in range(o):
+        big = 0
+        for k, wd in enumerate(words[r].tolist()):
+            big |= int(wd) << (32 * k)
+        for c in range(i):
+            q = (big >> (bits * c)) & ((1 << bits) - 1)
+            Q[r, c] = mu[r, c // g] + sc[r, c // g] * q
+    U = np.diag(s.astype(float)) @ sylvester(i).T / np.sqrt(i)
+    V = sylvester(o) @ np.diag(t.astype(float)) / np.sqrt(o)
+    What = Si @ V.T @ Q @ U.T
+    Y = kq.matvec_quantized(words, mu, sc, bits, group, s, t, Si, "full", X)
+    assert np.allclose(Y, X @ What.T, rtol=1e-11, atol=1e-11)
+
+
 def test_golden_regression_small_layer():
     """Stored oracle outputs of the small 256x256 workload (written by tests/golden/make_golden.py,
     which calls only the oracle) guard the oracle against accidental change."""
