@@ -308,6 +308,103 @@ def matvec_only(sp) -> dict:
     return time_matvec(sp, cfg, codes, scale, offset, s, t, Sinv, ws)
 
 
+def hg_variants(sp, ranks=(64, 256, 1024), q: int = 2) -> dict:
+    """Effect of the H_G preparation on the layer: H_G streamed from the gradient rows
+    (kq_hessian_accum on G), then quantized with the output-side root taken from the exact H_G, its
+    128-block diagonal, its diagonal, the low-rank-plus-isotropic approximation of rank k built from
+    G alone (kq_hg_lowrank), and no H_G at all (S = I). Every variant is scored with the exact
+    K-FAC loss tr(H_G dW H_X dW^T) in the original coordinates (kq_kfac_loss); prep_ms is the time of
+    forming S and S^{-1} (HIP events on the stream the calls run on)."""
+    import torch
+
+    from post_quantization_03_amd import _lib as K
+    from post_quantization_03_amd.layer import LayerCfg
+
+    if sp.hg_form != "full":
+        raise ValueError("the variants start from a full H_G")
+    dev = torch.device("cuda:0")
+    d = synth.layer_inputs(sp)
+    G = torch.from_numpy(synth.gen_G(sp)).to(dev)
+
+    def to(a, kind):
+        if kind == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    X, W = to(d["X"], sp.x_dtype), to(d["W"], sp.w_dtype)
+    s, t = to(d["s"], "i8"), to(d["t"], "i8")
+    del d
+    o, i, n, ng = sp.o, sp.i, sp.n, sp.hg_ng
+    f32, f64 = dict(dtype=torch.float32, device=dev), dict(dtype=torch.float64, device=dev)
+    cfg = LayerCfg(bits=sp.bits, group=sp.group, damp=sp.damp, form="full", blk=0)
+    xdt = K.KQ_BF16 if sp.x_dtype == "bf16" else K.KQ_F32
+    kmax = max(ranks)
+    ws = torch.empty(max(K.kq_workspace_bytes(op, o, i, n, xdt, sp.bits, sp.group, form, 128)
+                         for op in ("hessian", "rotate_in", "hg_sqrt", "rotate_out", "cholinv", "quantize",
+                                    "unrotate", "kfac_loss") for form in ("full", "block", "diag")),
+                     dtype=torch.uint8, device=dev)
+    ws_g = torch.empty(max(K.kq_workspace_bytes("hessian", 0, o, ng, K.KQ_F32),
+                           K.kq_workspace_bytes("hg_lowrank", o, kmax, ng)), dtype=torch.uint8, device=dev)
+
+    def timed(fn):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1)
+    # shared by every variant: H_X, the input rotation, the damped factor
+    HX = torch.empty((i, i), **f64)
+    K.kq_hessian_accum(X, HX, 1.0 / n, 0.0, ws)
+    HX2 = HX.clone()
+    W1 = torch.empty((o, i), **f32)
+    K.kq_rotate_in(W, W1, HX2, s, ws)
+    R = torch.empty((i, i), **f32)
+    info = torch.zeros(4, dtype=torch.int32, device=dev)
+    K.kq_cholinv(HX2, sp.damp, R, info[0:1], ws)
+    # H_G streamed from the gradient rows, then its storage forms
+    HG64 = torch.empty((o, o), **f64)
+    stream_ms = timed(lambda: K.kq_hessian_accum(G, HG64, 1.0 / ng, 0.0, ws_g))
+    HGf = torch.empty((o, o), **f32)
+    K.kq_hg_extract(HG64, "full", 0, HGf)
+    HGb = torch.empty((o // 128, 128, 128), **f32)
+    K.kq_hg_extract(HG64, "block", 128, HGb)
+    HGd = torch.empty((o,), **f32)
+    K.kq_hg_extract(HG64, "diag", 0, HGd)
+    ng_ = i // sp.group if sp.group else 1
+    codes = torch.empty((o, i * sp.bits // 32), dtype=torch.int32, device=dev)
+    scale, offset = torch.empty((o, ng_), **f32), torch.empty((o, ng_), **f32)
+    loss = torch.empty(1, **f64)
+
+    def run(form, blk, S, Sinv):
+        W2 = W1.clone()
+        K.kq_rotate_out(W2, S, form, blk, t, ws)
+        K.kq_quantize_layer(W2, R, sp.bits, sp.group, 128, codes, scale, offset, None, ws)
+        What = torch.empty((o, i), **f32)
+        K.kq_unrotate(W2, s, t, Sinv, form, blk, What, ws)
+        K.kq_kfac_loss(W, What, HX, HGf, "full", 0, loss, ws)
+        torch.cuda.synchronize()
+        return float(loss.item())
+    out = {}
+    for name, form, blk, HGv in (("full", "full", 0, HGf), ("block128", "block", 128, HGb), ("diag", "diag", 0, HGd)):
+        S, Si = torch.empty_like(HGv), torch.empty_like(HGv)
+        ms = timed(lambda: K.kq_hg_sqrt(HGv, form, o, blk, S, Si, info[1:2], ws))
+        out[name] = {"prep_ms": round(ms, 3), "kfac_loss": run(form, blk, S, Si), "info": int(info[1].item())}
+    for k in ranks:
+        omega = torch.from_numpy(synth.gen_omega(sp, k)).to(dev)
+        S, Si = torch.empty((o, o), **f32), torch.empty((o, o), **f32)
+        sig = torch.empty(2, **f64)
+        ms = timed(lambda: K.kq_hg_lowrank(G, k, q, omega, S, Si, None, sig, info[2:3], ws_g))
+        out[f"lowrank{k}"] = {"prep_ms": round(ms, 3), "kfac_loss": run("full", 0, S, Si), "info": int(info[2].item()),
+                              "sigma": float(sig[0].item())}
+    ones = torch.ones((o,), **f32)
+    out["identity"] = {"prep_ms": 0.0, "kfac_loss": run("diag", 0, ones, ones), "info": 0}
+    base = out["full"]["kfac_loss"]
+    for v in out.values():
+        v["loss_vs_full"] = round(v["kfac_loss"] / base, 5)
+    return {"workload": sp.name, "gradient_rows": ng, "power_steps": q, "streamed_hg_ms": round(stream_ms, 3),
+            "hg_variants": out}
+
+
 def cpu_baseline(sp, budget_s: float = 30.0) -> dict:
     """The float64 oracle, as it stands, on a bounded sample of the same layer; extrapolated per phase."""
     from oracle import kronq as kq
@@ -366,6 +463,9 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first run one plain device copy of MIB MiB (fp32 elementwise kernel), the reference "
                          "for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters to bytes")
+    ap.add_argument("--hg-variants", action="store_true",
+                    help="quantize the C2 layer with H_G prepared in several ways (exact, 128-block, diagonal, "
+                         "low-rank of several ranks, none) and print the exact K-FAC loss of each as its own JSON line")
     ap.add_argument("--matvec-only", action="store_true",
                     help="time only the inference-side product (kq_matvec_quantized) on the workload's layer shape "
                          "with random codes, and print its own JSON line (not the benchmark line)")
@@ -375,6 +475,9 @@ def main():
               "(multi-GPU sharding is described in DESIGN.md, not implemented).", file=sys.stderr)
         sys.exit(2)
     sp = synth.CONFIGS[args.workload]
+    if args.hg_variants:
+        print(json.dumps(hg_variants(sp)), flush=True)
+        return
     if args.matvec_only:
         print(json.dumps({"workload": sp.name, "o": sp.o, "i": sp.i, "bits": sp.bits, "group": sp.group,
                           "hg_form": sp.hg_form, "matvec_quantized": matvec_only(sp)}), flush=True)

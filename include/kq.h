@@ -66,7 +66,9 @@ typedef enum {
     KQ_OP_QUANTIZE = 5,
     KQ_OP_UNROTATE = 6,
     KQ_OP_LOSS = 7,
-    KQ_OP_MATVEC = 8   /* n = number of tokens */
+    KQ_OP_MATVEC = 8,      /* n = number of tokens */
+    KQ_OP_HG_LOWRANK = 9,  /* n = gradient rows, o, i = rank k */
+    KQ_OP_KFAC_LOSS = 10   /* o, i, form, blk */
 } kq_op;
 
 /* Workspace bytes needed by `op` for a layer of o x i weights, n calibration tokens (X dtype
@@ -199,6 +201,47 @@ kq_status kq_matvec_quantized(const uint32_t* codes, const float* scale, const f
                               int bits, int group, const int8_t* sign_in, const int8_t* sign_out, const float* Sinv,
                               kq_hg_form form, int64_t blk, const float* X, int64_t ldx, int64_t nt, float* Y,
                               int64_t ldy, void* ws, size_t ws_bytes, kq_stream stream);
+
+/*
+ * H_G storage forms from an fp64 covariance H (o x o, leading dimension ldh), e.g. H_G = G^T G / n
+ * accumulated from gradient rows by kq_hessian_accum (KronQ review page, Method: the gradient
+ * covariance from one calibration backward pass; Limitations (2): its full d_out x d_out size).
+ * form FULL: HG = H (o x o); BLOCK: the o/blk diagonal blocks (blk x blk each, stored one after
+ * another; the 128-block approximation for blk = 128); DIAG: the diagonal (o). Values rounded to
+ * fp32 (nearest even).
+ */
+kq_status kq_hg_extract(const double* H, int64_t o, int64_t ldh, kq_hg_form form, int64_t blk, float* HG,
+                        kq_stream stream);
+
+/*
+ * Low-rank-plus-isotropic approximation of H_G = G^T G / n from the gradient rows G alone (the o x o
+ * covariance is never formed), with its square root and inverse square root (KronQ review page,
+ * Sparks: low-rank or blockwise approximations of H_G against the transient d_out^2 memory of the
+ * bidirectional preprocessing; the approximation below is this library's reading):
+ *     Q = orthonormal basis of range(H^{q+1} Omega)   (randomised range finder, q power steps)
+ *     B = Q^T H Q,  sigma = (tr H - tr B) / (o - k)
+ *     H^ = Q B Q^T + sigma (I - Q Q^T)                 (same trace as H)
+ *     S = H^{1/2} = sqrt(sigma) I + Q (B^{1/2} - sqrt(sigma) I) Q^T,  S^{-1} likewise with B^{-1/2}
+ * G: n x o fp32 rows (leading dimension ldg); Omega: o x k fp32 (the caller's Gaussian test
+ * matrix); 0 < k < o, k <= n, 0 <= q <= 15. Out (device, fp32 o x o, full storage form): S, and
+ * optionally Sinv and HGhat = H^ (may be NULL); sigma (may be NULL): two doubles {sigma, tr H}.
+ * info (device int32): 0; 1 the range basis lost rank; 2 sigma <= 0; 3 the k x k square root failed.
+ * Work in fp64 (G widened once). Workspace: kq_workspace_bytes(KQ_OP_HG_LOWRANK, o, k, n, ...).
+ */
+kq_status kq_hg_lowrank(const float* G, int64_t n, int64_t o, int64_t ldg, int64_t k, int q, const float* omega,
+                        float* S, float* Sinv, float* HGhat, double* sigma, int32_t* info, void* ws, size_t ws_bytes,
+                        kq_stream stream);
+
+/*
+ * K-FAC layer loss tr(H_G dW H_X dW^T), dW = W^ - W, in the original coordinates (KronQ review page,
+ * Background: H ~ H_X (x) H_G; the loss that the bidirectional transforms turn into a GPTQ loss).
+ * W: o x i fp32 or bf16 (wdt), leading dimension ldw; What: o x i fp32 (ldq); HX: i x i fp64 (ldh);
+ * HG in its storage form. loss: one device double. fp64 throughout (two fp64 GEMMs and a fixed-order
+ * reduction). Workspace: kq_workspace_bytes(KQ_OP_KFAC_LOSS, o, i, 0, ..., form, blk).
+ */
+kq_status kq_kfac_loss(const void* W, kq_dtype wdt, int64_t ldw, const float* What, int64_t ldq, int64_t o, int64_t i,
+                       const double* HX, int64_t ldh, const float* HG, kq_hg_form form, int64_t blk, double* loss,
+                       void* ws, size_t ws_bytes, kq_stream stream);
 
 /*
  * Verification: layer loss in rotated coordinates, sum_r (Q - W2)_r HX2 (Q - W2)_r^T, which equals

@@ -335,6 +335,49 @@ def unrotate(Q2: np.ndarray, s: np.ndarray, t: np.ndarray, Sinv: np.ndarray, for
     return _unrot(A, s, axis=1)                             # (.) U^T: row a -> s * (H_i^T a) / sqrt(i)
 
 
+# ============================================================================= H_G preparation
+
+
+def hg_forms(H: np.ndarray, form: str, blk: int = 128) -> np.ndarray:
+    """Storage form of an o x o covariance: the matrix, its blk x blk diagonal blocks, or its
+    diagonal (KronQ review page, Sparks: blockwise approximations of H_G)."""
+    H = np.asarray(H)
+    o = H.shape[0]
+    if form == "full":
+        return H.copy()
+    if form == "block":
+        return np.stack([H[b:b + blk, b:b + blk] for b in range(0, o, blk)])
+    return np.diag(H).copy()
+
+
+def _sym_fn(A: np.ndarray, f) -> np.ndarray:
+    w, V = np.linalg.eigh((A + A.T) / 2)
+    return (V * f(w)) @ V.T
+
+
+def hg_lowrank(G: np.ndarray, k: int, q: int, omega: np.ndarray) -> dict:
+    """Low-rank-plus-isotropic approximation of H = G^T G / n (KronQ review page, Sparks: low-rank
+    approximations of H_G; the form below is this build's reading). The range of H^{q+1} Omega is
+    found step by step (re-orthonormalised after every product with H, which leaves the range
+    unchanged); with Q its orthonormal basis, B = Q^T H Q and sigma = (tr H - tr B) / (o - k),
+    H^ = Q B Q^T + sigma (I - Q Q^T). S and S^{-1} are the principal square root of H^ and its
+    inverse, taken from H^'s eigendecomposition."""
+    G = np.asarray(G, np.float64)
+    n, o = G.shape
+    H = G.T @ G / n
+    Q, _ = np.linalg.qr(H @ np.asarray(omega, np.float64))
+    for _ in range(q):
+        Q, _ = np.linalg.qr(H @ Q)
+    B = Q.T @ H @ Q
+    sigma = (np.trace(H) - np.trace(B)) / (o - k)
+    Hhat = Q @ B @ Q.T + sigma * (np.eye(o) - Q @ Q.T)
+    out = {"H": H, "Hhat": Hhat, "sigma": float(sigma), "trH": float(np.trace(H)), "Q": Q, "B": B}
+    if sigma > 0:
+        out["S"] = _sym_fn(Hhat, np.sqrt)
+        out["Sinv"] = _sym_fn(Hhat, lambda w: 1.0 / np.sqrt(w))
+    return out
+
+
 def matvec_quantized(words: np.ndarray, mu: np.ndarray, scale: np.ndarray, bits: int, group: int, s: np.ndarray,
                      t: np.ndarray, Sinv: np.ndarray, form: str, X: np.ndarray) -> np.ndarray:
     """Inference-side product Y = X W^^T for token rows X (n x i), from the packed codes.

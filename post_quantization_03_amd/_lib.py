@@ -13,10 +13,11 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkq.so")
 KQ_F32, KQ_BF16 = 0, 1
 HG_FORM = {"diag": 0, "block": 1, "full": 2}
 OP = {"hessian": 0, "rotate_in": 1, "hg_sqrt": 2, "rotate_out": 3, "cholinv": 4, "quantize": 5, "unrotate": 6,
-      "loss": 7, "matvec": 8}
+      "loss": 7, "matvec": 8, "hg_lowrank": 9, "kfac_loss": 10}
 EXPORTS = ("kq_workspace_bytes", "kq_hessian_accum", "kq_rotate_in", "kq_hg_sqrt", "kq_rotate_out", "kq_cholinv",
            "kq_quantize_layer", "kq_sensitivity", "kq_unrotate", "kq_layer_loss", "kq_strerror", "kq_last_error",
-           "kq_hadamard_order", "kq_version", "kq_allocate_bits", "kq_matvec_quantized")
+           "kq_hadamard_order", "kq_version", "kq_allocate_bits", "kq_matvec_quantized",
+           "kq_hg_extract", "kq_hg_lowrank", "kq_kfac_loss")
 
 
 class KQError(RuntimeError):
@@ -56,6 +57,10 @@ def lib() -> ctypes.CDLL:
                                     _int, ctypes.POINTER(ctypes.c_int32)]),
         "kq_matvec_quantized": (_int, [_vp, _vp, _vp, _i64, _i64, _int, _int, _vp, _vp, _vp, _int, _i64, _vp, _i64, _i64,
                                        _vp, _i64, _vp, _sz, _vp]),
+        "kq_hg_extract": (_int, [_vp, _i64, _i64, _int, _i64, _vp, _vp]),
+        "kq_hg_lowrank": (_int, [_vp, _i64, _i64, _i64, _i64, _int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+        "kq_kfac_loss": (_int, [_vp, _int, _i64, _vp, _i64, _i64, _i64, _vp, _i64, _vp, _int, _i64, _vp, _vp, _sz,
+                                _vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -184,6 +189,26 @@ def kq_matvec_quantized(codes, scale, offset, o: int, i: int, bits: int, group: 
                                                             _p(sign_in), _p(sign_out), _p(Sinv), HG_FORM[form], blk,
                                                             _p(X), X.stride(0), nt, _p(Y), Y.stride(0), w, wb,
                                                             _stream(stream)))
+
+
+def kq_hg_extract(H, form: str, blk: int, HG, stream=None) -> None:
+    o = H.shape[0]
+    _check("kq_hg_extract", lib().kq_hg_extract(_p(H), o, H.stride(0), HG_FORM[form], blk, _p(HG), _stream(stream)))
+
+
+def kq_hg_lowrank(G, k: int, q: int, omega, S, Sinv, HGhat, sigma, info, ws=None, stream=None) -> None:
+    n, o = G.shape
+    w, wb = _ws(ws)
+    _check("kq_hg_lowrank", lib().kq_hg_lowrank(_p(G), n, o, G.stride(0), k, q, _p(omega), _p(S), _p(Sinv),
+                                                _p(HGhat), _p(sigma), _p(info), w, wb, _stream(stream)))
+
+
+def kq_kfac_loss(W, What, HX, HG, form: str, blk: int, loss, ws=None, stream=None) -> None:
+    o, i = What.shape
+    w, wb = _ws(ws)
+    _check("kq_kfac_loss", lib().kq_kfac_loss(_p(W), _xdt(W), W.stride(0), _p(What), What.stride(0), o, i, _p(HX),
+                                              HX.stride(0), _p(HG), HG_FORM[form], blk, _p(loss), w, wb,
+                                              _stream(stream)))
 
 
 def kq_layer_loss(W2, Q, HX2, row_loss, loss, ws=None, stream=None) -> None:

@@ -14,7 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libkq.so")
-SOURCES = ("api", "dense", "gj", "syrk", "hadamard", "sweep", "dequant")
+SOURCES = ("api", "dense", "gj", "syrk", "hadamard", "sweep", "dequant", "hgprep")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-Wno-unused-result", "-Wno-unused-value",
          "-Wno-pass-failed", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 

@@ -703,7 +703,8 @@ constexpr int DB_MAXIT = 7;
 constexpr double DB_TOL = 1e-8;
 constexpr int NORM_PARTS = 32;
 
-__global__ void db_init_kernel(const float* HG, int64_t n, int64_t nbk, double* YZ, int* flags) {
+template <typename T>
+__global__ void db_init_kernel(const T* HG, int64_t n, int64_t nbk, double* YZ, int* flags) {
     const int64_t nn = n * n;
     for (int64_t e = blockIdx.x * 256 + threadIdx.x; e < nbk * nn; e += (int64_t)gridDim.x * 256) {
         const int64_t b = e / nn, rc = e % nn, r = rc / n, c = rc % n;
@@ -885,22 +886,12 @@ size_t hg_sqrt_ws(kq_hg_form form, int64_t o, int64_t blk) {
     return z.used;
 }
 
-extern "C" kq_status kq_hg_sqrt(const float* HG, kq_hg_form form, int64_t o, int64_t blk, float* S, float* Sinv,
-                                int32_t* info, void* ws, size_t ws_bytes, kq_stream stream) {
-    if (!HG || !S || !info) return fail(KQ_EINVAL, "kq_hg_sqrt: null pointer");
-    if (o <= 0) return fail(KQ_ESHAPE, "kq_hg_sqrt: o must be positive");
-    hipStream_t st = hs(stream);
-    if (form == KQ_HG_DIAG) {
-        KQ_TRY(fill<int>(reinterpret_cast<int*>(info), 1, 0, st));
-        const unsigned blocks = (unsigned)((o + 255) / 256 < 1024 ? (o + 255) / 256 : 1024);
-        hipLaunchKernelGGL(hg_diag_kernel, dim3(blocks), dim3(256), 0, st, HG, o, S, Sinv, info);
-        return check_launch("hg_diag");
-    }
-    if (form != KQ_HG_BLOCK && form != KQ_HG_FULL) return fail(KQ_EINVAL, "kq_hg_sqrt: bad form");
-    if (form == KQ_HG_BLOCK && (blk <= 0 || o % blk)) return fail(KQ_ESHAPE, "kq_hg_sqrt: o must be a multiple of blk");
-    const int64_t n = form == KQ_HG_FULL ? o : blk, nbk = form == KQ_HG_FULL ? 1 : o / blk;
-    if (n > 65535 * (int64_t)GJ_RT) return fail(KQ_ESHAPE, "kq_hg_sqrt: too large");
-    if (!ws || ws_bytes < hg_sqrt_ws(form, o, blk)) return fail(KQ_EWORKSPACE, "kq_hg_sqrt: workspace too small");
+// Denman-Beavers square root of nbk SPD n x n matrices (fp32 HGf or fp64 HGd, exactly one given);
+// on return the workspace holds Y = A^{1/2} (items 0 .. nbk-1) and Z = A^{-1/2} (items nbk ..) in
+// fp64 at *Y64 (Z at *Y64 + nbk n^2). info: 0, or o_info + 1 when the iteration did not converge
+// or a matrix is not positive definite.
+static kq_status db_sqrt(const float* HGf, const double* HGd, int64_t n, int64_t nbk, int32_t o_info, int32_t* info,
+                         void* ws, size_t ws_bytes, double** Y64, hipStream_t st) {
     Arena ar(ws, ws_bytes);
     const size_t nn = (size_t)n * n, items = 2 * (size_t)nbk;
     double* YZ = ar.take<double>(items * nn);
@@ -923,7 +914,8 @@ extern "C" kq_status kq_hg_sqrt(const float* HG, kq_hg_form form, int64_t o, int
     KQ_TRY(fill<int>(reinterpret_cast<int*>(info), 1, 0, st));
     KQ_TRY(fill<int>(reinterpret_cast<int*>(finfo), items, 0, st));
     const unsigned eb = (unsigned)((nbk * nn + 255) / 256 < 4096 ? (nbk * nn + 255) / 256 : 4096);
-    hipLaunchKernelGGL(db_init_kernel, dim3(eb), dim3(256), 0, st, HG, n, nbk, YZ, flags);
+    if (HGd) hipLaunchKernelGGL(db_init_kernel<double>, dim3(eb), dim3(256), 0, st, HGd, n, nbk, YZ, flags);
+    else hipLaunchKernelGGL(db_init_kernel<float>, dim3(eb), dim3(256), 0, st, HGf, n, nbk, YZ, flags);
     KQ_TRY(check_launch("db_init"));
     hipLaunchKernelGGL(sym_norm_part_kernel, dim3(NORM_PARTS, (unsigned)nbk), dim3(256), 0, st, YZ, n, (int64_t)nn, nrmA,
                        flags, -1);
@@ -948,8 +940,39 @@ extern "C" kq_status kq_hg_sqrt(const float* HG, kq_hg_form form, int64_t o, int
                            info);
         KQ_TRY(check_launch("db_converge"));
     }
-    hipLaunchKernelGGL(db_final_kernel, dim3(1), dim3(64), 0, st, flags, info, (int32_t)(o + 1));
+    hipLaunchKernelGGL(db_final_kernel, dim3(1), dim3(64), 0, st, flags, info, o_info + 1);
     KQ_TRY(check_launch("db_final"));
+    *Y64 = YZ;
+    return KQ_OK;
+}
+
+kq_status kq::spd_sqrt_f64(const double* A, int64_t n, int32_t* info, void* ws, size_t ws_bytes, double** Y64,
+                           hipStream_t st) {
+    if (!ws || ws_bytes < hg_sqrt_ws(KQ_HG_FULL, n, 0)) return fail(KQ_EWORKSPACE, "square root: workspace too small");
+    if (n > 65535 * (int64_t)GJ_RT) return fail(KQ_ESHAPE, "square root: too large");
+    return db_sqrt(nullptr, A, n, 1, (int32_t)n, info, ws, ws_bytes, Y64, st);
+}
+
+extern "C" kq_status kq_hg_sqrt(const float* HG, kq_hg_form form, int64_t o, int64_t blk, float* S, float* Sinv,
+                                int32_t* info, void* ws, size_t ws_bytes, kq_stream stream) {
+    if (!HG || !S || !info) return fail(KQ_EINVAL, "kq_hg_sqrt: null pointer");
+    if (o <= 0) return fail(KQ_ESHAPE, "kq_hg_sqrt: o must be positive");
+    hipStream_t st = hs(stream);
+    if (form == KQ_HG_DIAG) {
+        KQ_TRY(fill<int>(reinterpret_cast<int*>(info), 1, 0, st));
+        const unsigned blocks = (unsigned)((o + 255) / 256 < 1024 ? (o + 255) / 256 : 1024);
+        hipLaunchKernelGGL(hg_diag_kernel, dim3(blocks), dim3(256), 0, st, HG, o, S, Sinv, info);
+        return check_launch("hg_diag");
+    }
+    if (form != KQ_HG_BLOCK && form != KQ_HG_FULL) return fail(KQ_EINVAL, "kq_hg_sqrt: bad form");
+    if (form == KQ_HG_BLOCK && (blk <= 0 || o % blk)) return fail(KQ_ESHAPE, "kq_hg_sqrt: o must be a multiple of blk");
+    const int64_t n = form == KQ_HG_FULL ? o : blk, nbk = form == KQ_HG_FULL ? 1 : o / blk;
+    if (n > 65535 * (int64_t)GJ_RT) return fail(KQ_ESHAPE, "kq_hg_sqrt: too large");
+    if (!ws || ws_bytes < hg_sqrt_ws(form, o, blk)) return fail(KQ_EWORKSPACE, "kq_hg_sqrt: workspace too small");
+    double* YZ = nullptr;
+    KQ_TRY(db_sqrt(HG, nullptr, n, nbk, (int32_t)o, info, ws, ws_bytes, &YZ, st));
+    const size_t nn = (size_t)n * n;
+    const unsigned eb = (unsigned)((nbk * nn + 255) / 256 < 4096 ? (nbk * nn + 255) / 256 : 4096);
     hipLaunchKernelGGL(db_out_kernel, dim3(eb), dim3(256), 0, st, YZ, n, nbk, S, Sinv);
     return check_launch("db_out");
 }

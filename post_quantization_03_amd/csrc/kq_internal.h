@@ -109,8 +109,18 @@ kq_status chol_inv_diag128(double* A, int64_t lda, int64_t sA, double* X, int64_
                            const int* skip, hipStream_t st);
 int64_t chol_scratch_doubles();
 
+// Square root of one SPD n x n fp64 matrix A by the scaled Denman-Beavers iteration (the same
+// iteration as kq_hg_sqrt). On return *Y64 points into ws: A^{1/2} (n x n) followed by A^{-1/2}.
+// info: 0, or n + 1 if A is not positive definite or the iteration did not converge.
+// ws: hg_sqrt_ws(KQ_HG_FULL, n, 0) bytes.
+kq_status spd_sqrt_f64(const double* A, int64_t n, int32_t* info, void* ws, size_t ws_bytes, double** Y64,
+                       hipStream_t st);
+
 // ------------------------------------------------------------------------------------ helpers
 template <typename T>
 kq_status fill(T* p, size_t count, T value, hipStream_t st, const int* skip = nullptr);
 
 }  // namespace kq
+
+// workspace size of kq_hg_sqrt (defined with it)
+size_t hg_sqrt_ws(kq_hg_form form, int64_t o, int64_t blk);

@@ -18,7 +18,7 @@ from typing import Iterator
 
 import numpy as np
 
-TAG_W, TAG_X, TAG_G, TAG_S, TAG_T, TAG_OUT = 0, 1, 2, 3, 4, 5
+TAG_W, TAG_X, TAG_G, TAG_S, TAG_T, TAG_OUT, TAG_OMEGA = 0, 1, 2, 3, 4, 5, 6
 
 
 def rng(cfg: int, layer: int, sub: int, tag: int) -> np.random.Generator:
@@ -207,6 +207,28 @@ def gen_HG(spec: LayerSpec) -> np.ndarray:
         H /= spec.hg_ng
         return (0.5 * (H + H.T)).astype(np.float32)
     raise ValueError(spec.hg_form)
+
+
+def gen_G(spec: LayerSpec) -> np.ndarray:
+    """The gradient rows behind a full-form H_G (hg_ng x o, fp32): the same draws as gen_HG, so
+    G^T G / hg_ng is gen_HG's matrix up to the fp32 rounding of G."""
+    if spec.hg_form != "full":
+        raise ValueError("gradient rows are generated for the full form only")
+    g = rng(spec.cfg, spec.layer, spec.sub, TAG_G)
+    o = spec.o
+    sc = np.abs(g.standard_t(3, size=o))
+    out = np.empty((spec.hg_ng, o), dtype=np.float32)
+    r0 = 0
+    while r0 < spec.hg_ng:
+        m = min(4096, spec.hg_ng - r0)
+        out[r0:r0 + m] = (g.standard_normal((m, o)) * sc[None, :]).astype(np.float32)
+        r0 += m
+    return out
+
+
+def gen_omega(spec: LayerSpec, k: int) -> np.ndarray:
+    """Gaussian test matrix (o x k, fp32) for the randomised range finder of a low-rank H_G."""
+    return rng(spec.cfg, spec.layer, spec.sub, TAG_OMEGA).standard_normal((spec.o, k)).astype(np.float32)
 
 
 def gen_signs(spec: LayerSpec) -> tuple[np.ndarray, np.ndarray]:

@@ -4,6 +4,7 @@ No GPU needed: nothing here launches a kernel."""
 import os
 import re
 
+import numpy as np
 import pytest
 
 from oracle import hadamard as hd
@@ -81,3 +82,13 @@ def test_allocation_matches_oracle():
         assert np.array_equal(got, want)
         assert np.dot(got, sizes) <= 3.0 * sizes.sum()
     assert np.array_equal(K.kq_allocate_bits(np.ones(7), np.full(7, 100)), np.full(7, 3))
+
+
+def test_gradient_rows_match_the_full_hg_draws():
+    """gen_G draws the same gradient rows that gen_HG accumulates (full form)."""
+    import synth
+    sp = synth.scaled(synth.CONFIGS["C2"], o=96, hg_ng=5000)
+    G = synth.gen_G(sp).astype(np.float64)
+    H = synth.gen_HG(sp).astype(np.float64)
+    assert np.abs(G.T @ G / sp.hg_ng - H).max() <= 1e-6 * np.abs(H).max()
+    assert synth.gen_omega(sp, 8).shape == (96, 8)

@@ -201,3 +201,31 @@ def test_fullsize_matvec(name, nt):
     say(f"  max error / scale {(err / scale).max():.2e}")
     assert np.all(np.isfinite(Y))
     assert np.all(err <= 1e-5 * scale)
+
+
+def test_fullsize_hg_lowrank():
+    """Low-rank-plus-isotropic H_G at C2's size (16384 gradient rows x 4096, rank 256, 2 power
+    steps), from the same gradient rows as C2's full H_G: S, S^{-1} and H^ against the oracle."""
+    from tests.test_gpu_ops import f32
+    torch, dev = torch_dev()
+    sp = synth.CONFIGS["C2"]
+    k, q = 256, 2
+    G = synth.gen_G(sp)
+    omega = synth.gen_omega(sp, k)
+    say(f"hg_lowrank full size: G {G.shape}, k={k}, q={q}")
+    o = sp.o
+    S, Si, Hh = (torch.empty((o, o), dtype=torch.float32, device=dev) for _ in range(3))
+    sig = torch.empty(2, dtype=torch.float64, device=dev)
+    info = torch.full((1,), -1, dtype=torch.int32, device=dev)
+    ws = ws_tensor(K.kq_workspace_bytes("hg_lowrank", o, k, G.shape[0]))
+    K.kq_hg_lowrank(to_dev(G), k, q, to_dev(omega), S, Si, Hh, sig, info, ws)
+    assert int(host(info)[0]) == 0
+    say("  GPU done")
+    ref = kq.hg_lowrank(G.astype(np.float64), k, q, omega.astype(np.float64))
+    say("  oracle done")
+    s_gpu = host(sig)
+    assert abs(s_gpu[0] / ref["sigma"] - 1) <= 1e-8 and abs(s_gpu[1] / ref["trH"] - 1) <= 1e-12
+    for name, g in (("Hhat", Hh), ("S", S), ("Sinv", Si)):
+        err = rel_fro(host(g), ref[name])
+        say(f"  {name}: {err:.2e}")
+        assert err <= 1e-6

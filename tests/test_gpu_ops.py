@@ -351,3 +351,76 @@ def test_matvec_quantized_graph_replays():
         g.replay()
         torch.cuda.synchronize()
         assert np.array_equal(host(y), ref), k
+
+
+# ----------------------------------------------------------------------------- H_G preparation, K-FAC loss
+@pytest.mark.parametrize("form,blk", [("full", 0), ("block", 64), ("diag", 0)])
+def test_hg_extract(form, blk):
+    torch, dev = torch_dev()
+    rng = np.random.default_rng(4)
+    o = 320
+    H = spd_f32(rng, o).astype(np.float64) * (1 + 1e-9 * rng.standard_normal((o, o)))
+    H = (H + H.T) / 2
+    want = kq.hg_forms(H, form, blk).astype(np.float32)
+    out = torch.empty(want.shape, dtype=torch.float32, device=dev)
+    K.kq_hg_extract(to_dev(H, "f64"), form, blk, out)
+    assert np.array_equal(host(out), want)
+
+
+@pytest.mark.parametrize("o,n,k,q", [(512, 2048, 64, 2), (384, 1000, 200, 0), (256, 300, 128, 4)])
+def test_hg_lowrank(o, n, k, q):
+    torch, dev = torch_dev()
+    say(f"hg_lowrank o={o} n={n} k={k} q={q}")
+    rng = np.random.default_rng(o + k)
+    scales = np.abs(rng.standard_t(3, size=o)) + 0.05
+    G = (rng.standard_normal((n, o)) * scales).astype(f32)
+    omega = rng.standard_normal((o, k)).astype(f32)
+    ref = kq.hg_lowrank(G.astype(np.float64), k, q, omega.astype(np.float64))
+    S, Si, Hh = (torch.empty((o, o), dtype=torch.float32, device=dev) for _ in range(3))
+    sig = torch.empty(2, dtype=torch.float64, device=dev)
+    info = torch.full((1,), -1, dtype=torch.int32, device=dev)
+    ws = ws_tensor(K.kq_workspace_bytes("hg_lowrank", o, k, n))
+    K.kq_hg_lowrank(to_dev(G), k, q, to_dev(omega), S, Si, Hh, sig, info, ws)
+    assert int(host(info)[0]) == 0
+    s_gpu = host(sig)
+    assert abs(s_gpu[0] / ref["sigma"] - 1) <= 1e-9 and abs(s_gpu[1] / ref["trH"] - 1) <= 1e-12
+    assert rel_fro(host(Hh), ref["Hhat"]) <= 1e-6
+    assert rel_fro(host(S), ref["S"]) <= 1e-6
+    assert rel_fro(host(Si), ref["Sinv"]) <= 1e-6
+
+
+def test_hg_lowrank_reports_rank_loss():
+    """G of rank k/2 < k: the range basis of H Omega cannot have rank k (info = 1)."""
+    torch, dev = torch_dev()
+    rng = np.random.default_rng(8)
+    o, n, k = 256, 512, 64
+    G = (rng.standard_normal((n, k // 2)) @ rng.standard_normal((k // 2, o))).astype(f32)
+    S = torch.empty((o, o), dtype=torch.float32, device=dev)
+    info = torch.zeros(1, dtype=torch.int32, device=dev)
+    ws = ws_tensor(K.kq_workspace_bytes("hg_lowrank", o, k, n))
+    K.kq_hg_lowrank(to_dev(G), k, 1, to_dev(rng.standard_normal((o, k)).astype(f32)), S, None, None, None, info, ws)
+    assert int(host(info)[0]) == 1
+
+
+@pytest.mark.parametrize("form,o,i,blk,wdt", [("full", 256, 320, 0, "f32"), ("block", 256, 384, 64, "bf16"),
+                                              ("diag", 200, 256, 0, "f32")])
+def test_kfac_loss(form, o, i, blk, wdt):
+    torch, dev = torch_dev()
+    rng = np.random.default_rng(o * i)
+    W = (rng.standard_normal((o, i)) * 0.02).astype(f32)
+    if wdt == "bf16":
+        W = synth.bf16_round(W)
+    What = (W + rng.standard_normal((o, i)) * 0.003).astype(f32)
+    HX = spd_f32(rng, i).astype(np.float64)
+    if form == "diag":
+        HG = np.exp(rng.standard_normal(o)).astype(f32)
+    elif form == "block":
+        HG = np.stack([spd_f32(rng, blk) for _ in range(o // blk)])
+    else:
+        HG = spd_f32(rng, o)
+    ref = kq.kfac_loss(W.astype(np.float64), What.astype(np.float64), HX, HG.astype(np.float64), form)
+    Wd = to_dev(synth.f32_to_bf16_bits(W), "bf16") if wdt == "bf16" else to_dev(W)
+    loss = torch.empty(1, dtype=torch.float64, device=dev)
+    ws = ws_tensor(K.kq_workspace_bytes("kfac_loss", o, i, form=form, blk=blk))
+    K.kq_kfac_loss(Wd, to_dev(What), to_dev(HX, "f64"), to_dev(HG), form, blk, loss, ws)
+    assert abs(host(loss)[0] / ref - 1) <= 1e-10

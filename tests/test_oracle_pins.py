@@ -421,6 +421,56 @@ def test_p13_matvec_brute_force(bits, group):
     assert np.allclose(Y, X @ What.T, rtol=1e-11, atol=1e-11)
 
 
+# ----------------------------------------------------------------------------- P14
+def test_p14_lowrank_diagonal_closed_form():
+    """H = diag(h) with Omega = the first k unit vectors: the range is exactly those coordinates for
+    any number of power steps, so H^ = diag(h_1..h_k, sigma, .., sigma), sigma = mean of the rest."""
+    o, k, n = 12, 4, 12
+    h = np.linspace(5.0, 0.5, o)
+    G = np.zeros((n, o))
+    G[np.arange(o), np.arange(o)] = np.sqrt(n * h)
+    omega = np.eye(o)[:, :k]
+    for q in (0, 2):
+        r = kq.hg_lowrank(G, k, q, omega)
+        sig = h[k:].mean()
+        assert np.isclose(r["sigma"], sig, rtol=1e-13)
+        want = np.diag(np.concatenate([h[:k], np.full(o - k, sig)]))
+        assert np.allclose(r["Hhat"], want, atol=1e-12)
+        assert np.allclose(r["S"], np.sqrt(want), atol=1e-12)
+        assert np.allclose(r["Sinv"] @ r["S"], np.eye(o), atol=1e-12)
+
+
+def test_p14_lowrank_exact_rank_and_trace():
+    """G of rank k: H^ = H (sigma = 0) for a generic Omega; for any G the trace is kept and S^2 = H^."""
+    rng = np.random.default_rng(5)
+    o, k, n = 40, 6, 60
+    G = rng.standard_normal((n, k)) @ rng.standard_normal((k, o))
+    r = kq.hg_lowrank(G, k, 1, rng.standard_normal((o, k)))
+    assert abs(r["sigma"]) < 1e-12 * r["trH"]
+    assert np.allclose(r["Hhat"], r["H"], atol=1e-10 * np.abs(r["H"]).max())
+    G = rng.standard_normal((n, o)) * np.exp(rng.standard_normal(o))
+    r = kq.hg_lowrank(G, k, 2, rng.standard_normal((o, k)))
+    assert np.isclose(np.trace(r["Hhat"]), np.trace(r["H"]), rtol=1e-12)
+    assert np.allclose(r["S"] @ r["S"], r["Hhat"], atol=1e-10 * np.abs(r["Hhat"]).max())
+    assert np.allclose(r["Sinv"] @ r["S"], np.eye(o), atol=1e-9)
+    # on the captured subspace H^ acts as H: Q^T H^ Q = Q^T H Q
+    Q = r["Q"]
+    assert np.allclose(Q.T @ r["Hhat"] @ Q, Q.T @ r["H"] @ Q, atol=1e-10 * np.abs(r["H"]).max())
+    # a full-rank k = o - 1 capture of the top eigenspace with many power steps approaches H
+    w, V = np.linalg.eigh(r["H"])
+    r2 = kq.hg_lowrank(G, o - 1, 30, rng.standard_normal((o, o - 1)))
+    assert np.isclose(r2["sigma"], w[0], rtol=1e-6)
+
+
+def test_p14_forms_are_slices():
+    rng = np.random.default_rng(2)
+    H = spd(rng, 8)
+    assert np.array_equal(kq.hg_forms(H, "diag"), np.diag(H))
+    blocks = kq.hg_forms(H, "block", 4)
+    assert blocks.shape == (2, 4, 4) and np.array_equal(blocks[1], H[4:, 4:])
+    assert np.array_equal(kq.hg_forms(H, "full"), H)
+
+
 def test_golden_regression_small_layer():
     """Stored oracle outputs of the small 256x256 workload (written by tests/golden/make_golden.py,
     which calls only the oracle) guard the oracle against accidental change."""
