@@ -405,6 +405,68 @@ def hg_variants(sp, ranks=(64, 256, 1024), q: int = 2) -> dict:
             "hg_variants": out}
 
 
+def solver_variants(sp, candidates: int = 500, reps: int = 3) -> dict:
+    """The layer with the solver variants the pages describe for a related method: grids chosen by a
+    Hessian-aware search over `candidates` scales, and 128-column blocks swept in descending trace of
+    H_X'. Per variant: median time of the whole layer step (HIP events), and the exact K-FAC loss
+    tr(H_G dW H_X dW^T) of its result relative to the plain solver's."""
+    import dataclasses
+
+    import torch
+
+    from post_quantization_03_amd import _lib as K
+    from post_quantization_03_amd.layer import LayerCfg, quantize_layer, workspace_bytes
+
+    dev = torch.device("cuda:0")
+    d = synth.layer_inputs(sp)
+
+    def to(a, kind):
+        if kind == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    X, W, HG = to(d["X"], sp.x_dtype), to(d["W"], sp.w_dtype), to(d["HG"], "f32")
+    s, t = to(d["s"], "i8"), to(d["t"], "i8")
+    del d
+    o, i, n = sp.o, sp.i, sp.n
+    xdt = K.KQ_BF16 if sp.x_dtype == "bf16" else K.KQ_F32
+    base = LayerCfg(bits=sp.bits, group=sp.group, damp=sp.damp, form=sp.hg_form,
+                    blk=sp.hg_blk if sp.hg_form == "block" else 0)
+    ws = torch.empty(max(workspace_bytes(o, i, n, xdt, base, verify=True),
+                         K.kq_workspace_bytes("kfac_loss", o, i, form=base.form, blk=base.blk)),
+                     dtype=torch.uint8, device=dev)
+    HX = torch.empty((i, i), dtype=torch.float64, device=dev)
+    K.kq_hessian_accum(X, HX, 1.0 / n, 0.0, ws)
+    Sc = torch.empty((o, o) if base.form == "full" else HG.shape, dtype=torch.float32, device=dev)
+    Sic = torch.empty_like(Sc)
+    info = torch.zeros(1, dtype=torch.int32, device=dev)
+    K.kq_hg_sqrt(HG, base.form, o, base.blk, Sc, Sic, info, ws)   # S cached: the variants differ after it
+    loss = torch.empty(1, dtype=torch.float64, device=dev)
+    out = {}
+    for name, kw in (("plain", {}), (f"search{candidates}", {"search": candidates}), ("trace_order", {"order": "trace"}),
+                     (f"search{candidates}+trace_order", {"search": candidates, "order": "trace"})):
+        cfg = dataclasses.replace(base, **kw)
+        times = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            r = quantize_layer(X, W, HG, s, t, cfg, ws=ws, S_cached=(Sc, Sic), verify=True)
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        K.kq_kfac_loss(W, r["What"], HX, HG, base.form, base.blk, loss, ws)
+        torch.cuda.synchronize()
+        out[name] = {"layer_ms_S_cached": round(float(np.median(times)), 3), "kfac_loss": float(loss.item()),
+                     "info": host_list(r["info"])}
+    ref = out["plain"]["kfac_loss"]
+    for v in out.values():
+        v["loss_vs_plain"] = round(v["kfac_loss"] / ref, 5)
+    return {"workload": sp.name, "variants": out}
+
+
+def host_list(t) -> list:
+    return [int(v) for v in t.cpu().tolist()]
+
+
 def cpu_baseline(sp, budget_s: float = 30.0) -> dict:
     """The float64 oracle, as it stands, on a bounded sample of the same layer; extrapolated per phase."""
     from oracle import kronq as kq
@@ -466,6 +528,9 @@ def main():
     ap.add_argument("--hg-variants", action="store_true",
                     help="quantize the C2 layer with H_G prepared in several ways (exact, 128-block, diagonal, "
                          "low-rank of several ranks, none) and print the exact K-FAC loss of each as its own JSON line")
+    ap.add_argument("--solver-variants", action="store_true",
+                    help="run the workload's layer with the Hessian-aware grid search and/or trace-ordered blocks and "
+                         "print time and exact K-FAC loss of each as its own JSON line")
     ap.add_argument("--matvec-only", action="store_true",
                     help="time only the inference-side product (kq_matvec_quantized) on the workload's layer shape "
                          "with random codes, and print its own JSON line (not the benchmark line)")
@@ -475,6 +540,9 @@ def main():
               "(multi-GPU sharding is described in DESIGN.md, not implemented).", file=sys.stderr)
         sys.exit(2)
     sp = synth.CONFIGS[args.workload]
+    if args.solver_variants:
+        print(json.dumps(solver_variants(sp)), flush=True)
+        return
     if args.hg_variants:
         print(json.dumps(hg_variants(sp)), flush=True)
         return

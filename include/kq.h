@@ -166,6 +166,41 @@ kq_status kq_quantize_layer(float* W, int64_t o, int64_t i, int64_t ldw, const f
                             void* ws, size_t ws_bytes, kq_stream stream);
 
 /*
+ * kq_quantize_layer with a Hessian-aware choice of every grid (H_Z-PTQ page, Weight scales and
+ * rounding: the scale of a quantization tile picked by a grid search over candidates for the
+ * smallest curvature-weighted rounding error; its experimental settings: 500 candidates over one
+ * half to all of the full range). Each grid's [min, max] range (over the row, group = 0, or over the
+ * group's current values when the sweep reaches it) is shrunk about its midpoint by the factor
+ * alpha_m = 1/2 + m / (2 (candidates - 1)), m = 0 .. candidates-1, and the first alpha minimising
+ *     sum_c (w_c - w^_c(alpha))^2 / R_cc^2
+ * over the grid's columns is kept: offset = mid - alpha h, scale = 2 alpha h / (2^b - 1), h the half
+ * range. alpha = 1 is the min-max grid. candidates = 0 is kq_quantize_layer; 1..4096 otherwise.
+ */
+kq_status kq_quantize_layer_search(float* W, int64_t o, int64_t i, int64_t ldw, const float* R, int64_t ldr, int bits,
+                                   int group, int block, int candidates, uint32_t* codes, float* scale, float* offset,
+                                   float* row_loss, void* ws, size_t ws_bytes, kq_stream stream);
+
+/*
+ * Trace-sorted block order (H_Z-PTQ page, Weight scales and rounding: the blocks with larger
+ * curvature traces are quantized first, as GPTQ's act-order does for columns). H: i x i fp64
+ * (leading dimension ldh), i a multiple of width, at most 4096 blocks. order (device int32, 2 i/width
+ * entries): order[k] = the block with the k-th largest trace of its diagonal part of H (ties: lower
+ * index first), order[i/width + b] = the position of block b (the inverse permutation).
+ * Used with width = 128 (the sweep's block), so groups and packed words stay within blocks: permute
+ * W'' and H_X' (both axes) forward, factor and sweep, then undo the permutation on W, the codes (4 b
+ * words per row and block) and the group scales and offsets (128/group per row and block).
+ */
+kq_status kq_block_order(const double* H, int64_t i, int64_t ldh, int64_t width, int32_t* order, kq_stream stream);
+
+/*
+ * out block k = in block perm[k], for column blocks (axis 0) or row blocks (axis 1) of a rows x cols
+ * row-major matrix of 4- or 8-byte elements (leading dimensions ldi, ldo; in and out must differ).
+ * perm: device int32, one entry per block of `width` elements.
+ */
+kq_status kq_permute_blocks(const void* in, int64_t ldi, void* out, int64_t ldo, int64_t rows, int64_t cols,
+                            int64_t width, int axis, int elem_bytes, const int32_t* perm, kq_stream stream);
+
+/*
  * Sublayer sensitivity tr(H_G) * tr(H_X), both undamped (review page, Method (2)). HX: i x i fp64,
  * leading dimension ldh (a rotated H_X gives the same trace up to rounding). HG in its storage
  * form. score: one device double.

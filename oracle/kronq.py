@@ -178,6 +178,40 @@ def quantize(w: np.ndarray, mu: np.ndarray, s: np.ndarray, bits: int):
     return q.astype(np.int64), mu + s * q, delta
 
 
+def search_alphas(M: int) -> np.ndarray:
+    """The candidate range factors: M values spread evenly over [1/2, 1] (1 alone for M = 1)."""
+    return 0.5 + 0.5 * np.arange(M) / (M - 1) if M > 1 else np.ones(1)
+
+
+def grid_search(v: np.ndarray, d: np.ndarray, bits: int, M: int, near_scale: np.ndarray | None = None):
+    """Hessian-aware choice of the grid of each row of v (H_Z-PTQ page, Weight scales and rounding:
+    a grid search over a few candidate scales for the one with the smallest curvature-weighted
+    rounding error; its experimental settings: 500 candidates spread evenly over [max|w|, 2 max|w|],
+    i.e. one half to all of the full range). Asymmetric reading for the shifted grid here: the
+    [min, max] range is shrunk about its midpoint by alpha in [1/2, 1]; the weight of column c is
+    d_c, the curvature the sweep charges an error in column c with (1 / R_cc^2). alpha = 1 is the
+    min-max grid, so the chosen grid never has a larger weighted rounding error.
+
+    Returns mu, s, the chosen candidate index and every candidate's objective (rows x M). With
+    ``near_scale`` the candidate whose step is nearest to it is taken instead of the argmin (replay
+    of another implementation's choice; the caller checks its objective)."""
+    L = 2 ** bits - 1
+    mn, mx = v.min(axis=-1), v.max(axis=-1)
+    c, h = (mn + mx) / 2, (mx - mn) / 2
+    alphas = search_alphas(M)
+    obj = np.empty((v.shape[0], M))
+    for m, a in enumerate(alphas):
+        mu_a, s_a = c - a * h, 2 * a * h / L
+        _, deq, _ = quantize(v, mu_a[:, None], s_a[:, None], bits)
+        obj[:, m] = ((v - deq) ** 2 * d[None, :]).sum(axis=-1)
+    idx = obj.argmin(axis=-1)
+    if near_scale is not None:
+        steps = 2 * alphas[None, :] * h[:, None] / L
+        idx = np.abs(steps - np.asarray(near_scale, np.float64)[:, None]).argmin(axis=-1)
+    a = alphas[idx]
+    return c - a * h, 2 * a * h / L, idx, obj
+
+
 def sweep_plain(W2: np.ndarray, R: np.ndarray, bits: int, group: int = 0,
                 force_mask: np.ndarray | None = None, force_codes: np.ndarray | None = None,
                 stop: int | None = None) -> dict:
@@ -222,11 +256,15 @@ def sweep_plain(W2: np.ndarray, R: np.ndarray, bits: int, group: int = 0,
 
 
 def sweep_blocked(W2: np.ndarray, R: np.ndarray, bits: int, group: int = 0, block: int = 128,
-                  force_mask: np.ndarray | None = None, force_codes: np.ndarray | None = None) -> dict:
+                  force_mask: np.ndarray | None = None, force_codes: np.ndarray | None = None,
+                  search: int = 0, near_scale: np.ndarray | None = None) -> dict:
     """Same sweep with GPTQ's lazy batch updates over ``block`` columns: in-block steps update only
     the block's own columns, and after the block W[:, b1:] -= E R[b0:b1, b1:] (spec:
     "lazy trailing updates W[:, j+B:] -= E Hinv[B, j+B:]"). Exactly equal to ``sweep_plain`` in exact
-    arithmetic when group divides block or block divides group."""
+    arithmetic when group divides block or block divides group.
+
+    ``search`` > 0 chooses every grid by ``grid_search`` over that many candidates with the column
+    weights 1 / R_cc^2 instead of min-max; ``near_scale`` (o x groups) replays given steps there."""
     W = np.array(W2, dtype=np.float64)
     o, i = W.shape
     if group and (block % group) and (group % block):
@@ -237,15 +275,26 @@ def sweep_blocked(W2: np.ndarray, R: np.ndarray, bits: int, group: int = 0, bloc
     mu_all = np.zeros((o, ng))
     sc_all = np.zeros((o, ng))
     loss = np.zeros(o)
+    dw = 1.0 / np.diag(np.asarray(R, np.float64)) ** 2
+    chosen = np.zeros((o, ng), dtype=np.int64)
+    objs = np.zeros((o, ng, max(search, 1)))
+
+    def pick(v, dcol, g):
+        if not search:
+            return grid_params(v, bits)
+        ns = None if near_scale is None else near_scale[:, g]
+        m, st, idx, obj = grid_search(v, dcol, bits, search, ns)
+        chosen[:, g], objs[:, g] = idx, obj
+        return m, st
     if not group:
-        mu, s = grid_params(W, bits)
+        mu, s = pick(W, dw, 0)
         mu_all[:, 0], sc_all[:, 0] = mu, s
     for b0 in range(0, i, block):
         b1 = min(b0 + block, i)
         E = np.zeros((o, b1 - b0))
         for j in range(b0, b1):
             if group and j % group == 0:
-                mu, s = grid_params(W[:, j:j + group], bits)
+                mu, s = pick(W[:, j:j + group], dw[j:j + group], j // group)
                 mu_all[:, j // group], sc_all[:, j // group] = mu, s
             q, deq, dl = quantize(W[:, j], mu, s, bits)
             if force_mask is not None and force_mask[:, j].any():
@@ -261,7 +310,10 @@ def sweep_blocked(W2: np.ndarray, R: np.ndarray, bits: int, group: int = 0, bloc
             loss += e * e
         if b1 < i:
             W[:, b1:] -= E @ R[b0:b1, b1:]
-    return {"codes": codes, "mu": mu_all, "scale": sc_all, "Q": W, "row_loss": loss, "delta": delta}
+    out = {"codes": codes, "mu": mu_all, "scale": sc_all, "Q": W, "row_loss": loss, "delta": delta}
+    if search:
+        out["chosen"], out["objectives"] = chosen, objs
+    return out
 
 
 def sweep_obs_naive(W2: np.ndarray, H: np.ndarray, bits: int, group: int = 0) -> dict:
@@ -425,10 +477,51 @@ def sensitivity(HX: np.ndarray, HG: np.ndarray, form: str) -> float:
 # ============================================================================= whole layer
 
 
+def block_trace_order(H: np.ndarray, width: int = 128) -> np.ndarray:
+    """Blocks of `width` columns in descending order of the trace of their diagonal part of H (ties:
+    lower index first). H_Z-PTQ page, Weight scales and rounding: the blocks with larger curvature
+    traces are quantized first (GPTQ's act-order at block granularity)."""
+    d = np.diag(np.asarray(H, np.float64))
+    tr = d.reshape(-1, width).sum(axis=1)
+    return np.lexsort((np.arange(tr.size), -tr))
+
+
+def block_perm_index(order: np.ndarray, width: int) -> np.ndarray:
+    """Column index of the permuted matrix: position k * width + c holds column order[k] * width + c."""
+    return (np.asarray(order)[:, None] * width + np.arange(width)[None, :]).ravel()
+
+
+def sweep_trace_order(W2: np.ndarray, H: np.ndarray, bits: int, group: int, block: int = 128, search: int = 0,
+                      order: np.ndarray | None = None) -> dict:
+    """The sweep with blocks taken in trace order: permute the columns of W'' and both axes of the
+    damped H by blocks, factor and sweep there, and put the results back in the natural order (the
+    codes and grids of a block move with it, since groups and packed words stay inside blocks)."""
+    o, i = W2.shape
+    if order is None:
+        order = block_trace_order(H, block)
+    p = block_perm_index(order, block)
+    Hp = np.asarray(H, np.float64)[np.ix_(p, p)]
+    R = inverse_upper_factor(Hp)
+    sw = sweep_blocked(np.asarray(W2, np.float64)[:, p], R, bits, group, block, search=search)
+    inv = np.argsort(p)
+    out = dict(sw)
+    out["Q"] = sw["Q"][:, inv]
+    out["codes"] = sw["codes"][:, inv]
+    out["delta"] = sw["delta"][:, inv]
+    if group:
+        gp = block_perm_index(order, block // group) if block >= group else None
+        ginv = np.argsort(gp)
+        out["mu"], out["scale"] = sw["mu"][:, ginv], sw["scale"][:, ginv]
+    out["order"], out["R_perm"] = np.asarray(order), R
+    return out
+
+
 def quantize_layer(X, W, HG, form: str, s, t, bits: int, group: int, block: int = 128,
                    damp: float = 0.01, rotate_in: bool = True, rotate_out_on: bool = True,
-                   mode: str = "blocked", verify: bool = True) -> dict:
-    """All steps of the per-layer solver on float64 copies of the inputs."""
+                   mode: str = "blocked", verify: bool = True, search: int = 0, order: str = "natural") -> dict:
+    """All steps of the per-layer solver on float64 copies of the inputs. ``search``: candidates of
+    the Hessian-aware grid search (0: min-max); ``order``: "natural" or "trace" (blocks in descending
+    trace of the damped, rotated H_X)."""
     HX = hessian(X)
     W = np.asarray(W, np.float64)
     o, i = W.shape
@@ -442,8 +535,13 @@ def quantize_layer(X, W, HG, form: str, s, t, bits: int, group: int, block: int 
     else:
         W2 = form_matmul(S, form, W1)
     H, lam = damped(HX2, damp)
-    R = inverse_upper_factor(H)
-    sw = (sweep_blocked(W2, R, bits, group, block) if mode == "blocked" else sweep_plain(W2, R, bits, group))
+    if order == "trace":
+        sw = sweep_trace_order(W2, H, bits, group, block, search)
+        R = sw["R_perm"]
+    else:
+        R = inverse_upper_factor(H)
+        sw = (sweep_blocked(W2, R, bits, group, block, search=search) if mode == "blocked"
+              else sweep_plain(W2, R, bits, group))
     out = {"HX": HX, "W1": W1, "HX2": HX2, "S": S, "Sinv": Sinv, "W2": W2, "lam": lam, "R": R,
            "score": sensitivity(HX, HG, form), "words": pack(sw["codes"], bits) if (i * bits) % 32 == 0 else None, **sw}
     if verify:

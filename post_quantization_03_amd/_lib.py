@@ -17,7 +17,8 @@ OP = {"hessian": 0, "rotate_in": 1, "hg_sqrt": 2, "rotate_out": 3, "cholinv": 4,
 EXPORTS = ("kq_workspace_bytes", "kq_hessian_accum", "kq_rotate_in", "kq_hg_sqrt", "kq_rotate_out", "kq_cholinv",
            "kq_quantize_layer", "kq_sensitivity", "kq_unrotate", "kq_layer_loss", "kq_strerror", "kq_last_error",
            "kq_hadamard_order", "kq_version", "kq_allocate_bits", "kq_matvec_quantized",
-           "kq_hg_extract", "kq_hg_lowrank", "kq_kfac_loss")
+           "kq_hg_extract", "kq_hg_lowrank", "kq_kfac_loss", "kq_quantize_layer_search",
+           "kq_block_order", "kq_permute_blocks")
 
 
 class KQError(RuntimeError):
@@ -58,6 +59,10 @@ def lib() -> ctypes.CDLL:
         "kq_matvec_quantized": (_int, [_vp, _vp, _vp, _i64, _i64, _int, _int, _vp, _vp, _vp, _int, _i64, _vp, _i64, _i64,
                                        _vp, _i64, _vp, _sz, _vp]),
         "kq_hg_extract": (_int, [_vp, _i64, _i64, _int, _i64, _vp, _vp]),
+        "kq_block_order": (_int, [_vp, _i64, _i64, _i64, _vp, _vp]),
+        "kq_permute_blocks": (_int, [_vp, _i64, _vp, _i64, _i64, _i64, _i64, _int, _int, _vp, _vp]),
+        "kq_quantize_layer_search": (_int, [_vp, _i64, _i64, _i64, _vp, _i64, _int, _int, _int, _int, _vp, _vp, _vp,
+                                            _vp, _vp, _sz, _vp]),
         "kq_hg_lowrank": (_int, [_vp, _i64, _i64, _i64, _i64, _int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
         "kq_kfac_loss": (_int, [_vp, _int, _i64, _vp, _i64, _i64, _i64, _vp, _i64, _vp, _int, _i64, _vp, _vp, _sz,
                                 _vp]),
@@ -165,6 +170,26 @@ def kq_quantize_layer(W, R, bits: int, group: int, block: int, codes, scale, off
     _check("kq_quantize_layer", lib().kq_quantize_layer(_p(W), o, i, W.stride(0), _p(R), R.stride(0), bits, group,
                                                         block, _p(codes), _p(scale), _p(offset), _p(row_loss), w, wb,
                                                         _stream(stream)))
+
+
+def kq_quantize_layer_search(W, R, bits: int, group: int, block: int, candidates: int, codes, scale, offset,
+                             row_loss=None, ws=None, stream=None) -> None:
+    o, i = W.shape
+    w, wb = _ws(ws)
+    _check("kq_quantize_layer_search",
+           lib().kq_quantize_layer_search(_p(W), o, i, W.stride(0), _p(R), R.stride(0), bits, group, block, candidates,
+                                          _p(codes), _p(scale), _p(offset), _p(row_loss), w, wb, _stream(stream)))
+
+
+def kq_block_order(H, width: int, order, stream=None) -> None:
+    i = H.shape[0]
+    _check("kq_block_order", lib().kq_block_order(_p(H), i, H.stride(0), width, _p(order), _stream(stream)))
+
+
+def kq_permute_blocks(src, dst, width: int, axis: int, perm, stream=None) -> None:
+    rows, cols = src.shape
+    _check("kq_permute_blocks", lib().kq_permute_blocks(_p(src), src.stride(0), _p(dst), dst.stride(0), rows, cols,
+                                                        width, axis, src.element_size(), _p(perm), _stream(stream)))
 
 
 def kq_sensitivity(HX, HG, form: str, o: int, blk: int, score, stream=None) -> None:

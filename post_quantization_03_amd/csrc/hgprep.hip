@@ -382,3 +382,72 @@ extern "C" kq_status kq_kfac_loss(const void* W, kq_dtype wdt, int64_t ldw, cons
     hipLaunchKernelGGL(sum_parts_kernel, dim3(1), dim3(256), 0, st, part, loss);
     return check_launch("kfac sum");
 }
+
+// ------------------------------------------------------------------------------ block column order
+// Trace-sorted block order (H_Z-PTQ page, Weight scales and rounding: before the sweep the block
+// rows and columns are sorted so that blocks with larger curvature traces are quantized first, as
+// GPTQ's act-order does for columns). order[k] = the block with the k-th largest trace of its
+// diagonal of H (ties: lower block index first); order[nb + b] = the position of block b.
+__global__ void block_order_kernel(const double* __restrict__ H, int64_t ldh, int64_t nb, int64_t width,
+                                   int32_t* __restrict__ order) {
+    extern __shared__ double tr[];
+    for (int64_t b = threadIdx.x; b < nb; b += blockDim.x) {
+        double s = 0.0;
+        for (int64_t c = 0; c < width; c++) s += H[(b * width + c) * ldh + b * width + c];
+        tr[b] = s;
+    }
+    __syncthreads();
+    for (int64_t b = threadIdx.x; b < nb; b += blockDim.x) {
+        int64_t rank = 0;
+        for (int64_t a = 0; a < nb; a++) rank += (tr[a] > tr[b]) || (tr[a] == tr[b] && a < b);
+        order[rank] = (int32_t)b;
+        order[nb + b] = (int32_t)rank;
+    }
+}
+
+// Column blocks (axis 0) or row blocks (axis 1) of a rows x cols matrix: out block k = in block
+// perm[k] (pass the second half of kq_block_order's output to undo its first half).
+template <typename T>
+__global__ void permute_blocks_kernel(const T* __restrict__ in, int64_t ldi, T* __restrict__ out, int64_t ldo,
+                                      int64_t rows, int64_t cols, int64_t width, int axis, const int32_t* __restrict__ perm) {
+    const int64_t total = rows * cols;
+    for (int64_t e = blockIdx.x * (int64_t)256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256) {
+        const int64_t r = e / cols, c = e % cols;
+        const int64_t idx = axis == 0 ? c : r;            // position along the permuted axis (output)
+        const int64_t src = (int64_t)perm[idx / width] * width + idx % width;
+        out[r * ldo + c] = axis == 0 ? in[r * ldi + src] : in[src * ldi + c];
+    }
+}
+
+extern "C" kq_status kq_block_order(const double* H, int64_t i, int64_t ldh, int64_t width, int32_t* order,
+                                    kq_stream stream) {
+    if (!H || !order) return fail(KQ_EINVAL, "kq_block_order: null pointer");
+    if (i <= 0 || width <= 0 || i % width || ldh < i) return fail(KQ_ESHAPE, "kq_block_order: bad sizes");
+    const int64_t nb = i / width;
+    if (nb > 4096) return fail(KQ_ESHAPE, "kq_block_order: at most 4096 blocks");
+    hipStream_t st = hs(stream);
+    hipLaunchKernelGGL(block_order_kernel, dim3(1), dim3(256), (size_t)nb * sizeof(double), st, H, ldh, nb, width, order);
+    return check_launch("block_order");
+}
+
+extern "C" kq_status kq_permute_blocks(const void* in, int64_t ldi, void* out, int64_t ldo, int64_t rows, int64_t cols,
+                                       int64_t width, int axis, int elem_bytes, const int32_t* perm,
+                                       kq_stream stream) {
+    if (!in || !out || !perm) return fail(KQ_EINVAL, "kq_permute_blocks: null pointer");
+    if (in == out) return fail(KQ_EINVAL, "kq_permute_blocks: in and out must differ");
+    if (rows <= 0 || cols <= 0 || width <= 0 || ldi < cols || ldo < cols) return fail(KQ_ESHAPE, "kq_permute_blocks: bad sizes");
+    if ((axis == 0 && cols % width) || (axis == 1 && rows % width) || (axis != 0 && axis != 1))
+        return fail(KQ_ESHAPE, "kq_permute_blocks: the permuted extent must be a multiple of width");
+    hipStream_t st = hs(stream);
+    const int64_t total = rows * cols;
+    const unsigned g = grid_for(total);
+    if (elem_bytes == 4)
+        hipLaunchKernelGGL(permute_blocks_kernel<uint32_t>, dim3(g), dim3(256), 0, st, static_cast<const uint32_t*>(in),
+                           ldi, static_cast<uint32_t*>(out), ldo, rows, cols, width, axis, perm);
+    else if (elem_bytes == 8)
+        hipLaunchKernelGGL(permute_blocks_kernel<uint64_t>, dim3(g), dim3(256), 0, st, static_cast<const uint64_t*>(in),
+                           ldi, static_cast<uint64_t*>(out), ldo, rows, cols, width, axis, perm);
+    else
+        return fail(KQ_EINVAL, "kq_permute_blocks: elements must be 4 or 8 bytes");
+    return check_launch("permute_blocks");
+}

@@ -18,6 +18,11 @@ namespace kq {
 constexpr int SW_B = 128;         // column block
 constexpr int SW_ROWS = 16;       // rows per work-group (16 lanes each)
 
+// Candidate range factor m of nsearch: spread evenly over [1/2, 1] (Hessian-aware scale search).
+__device__ __forceinline__ float search_alpha(int m, int nsearch) {
+    return nsearch > 1 ? 0.5f + 0.5f * (float)m / (float)(nsearch - 1) : 1.0f;
+}
+
 // Per-row grid over the whole row before the sweep (group = 0): offset = min, scale = (max-min)/L.
 __global__ __launch_bounds__(256) void row_grid_kernel(const float* __restrict__ W, int64_t i, int64_t ldw, float L,
                                                        float* __restrict__ scale, float* __restrict__ offset) {
@@ -45,6 +50,69 @@ __global__ __launch_bounds__(256) void row_grid_kernel(const float* __restrict__
     }
 }
 
+// Per-row Hessian-aware grid (group = 0): the [min, max] range shrunk about its midpoint by the
+// factor (of nsearch in [1/2, 1]) with the smallest rounding error weighted by 1 / R_cc^2 (first
+// minimum). The row and the weights sit in LDS (8 i bytes); per candidate every thread sums its
+// columns, the wavefronts reduce by shuffles and the four partials are added in a fixed order by
+// every thread, so all threads take the same decision.
+__global__ __launch_bounds__(256) void row_grid_search_kernel(const float* __restrict__ W, int64_t i, int64_t ldw,
+                                                              float L, float* __restrict__ scale,
+                                                              float* __restrict__ offset, const float* __restrict__ R,
+                                                              int64_t ldr, int nsearch) {
+    extern __shared__ __align__(16) float rg_sm[];
+    float* vrow = rg_sm;            // i
+    float* wgt = rg_sm + i;         // i
+    __shared__ float part[2][4];
+    __shared__ float smin[4], smax[4];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t r = blockIdx.x;
+    float mn = INFINITY, mx = -INFINITY;
+    for (int64_t c = tid; c < i; c += 256) {
+        const float v = W[r * ldw + c];
+        const float rc = R[c * ldr + c];
+        vrow[c] = v;
+        wgt[c] = 1.0f / (rc * rc);
+        mn = fminf(mn, v);
+        mx = fmaxf(mx, v);
+    }
+#pragma unroll
+    for (int m = 32; m > 0; m >>= 1) {
+        mn = fminf(mn, __shfl_xor(mn, m, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, m, 64));
+    }
+    if (lane == 0) { smin[wave] = mn; smax[wave] = mx; }
+    __syncthreads();
+    mn = fminf(fminf(smin[0], smin[1]), fminf(smin[2], smin[3]));
+    mx = fmaxf(fmaxf(smax[0], smax[1]), fmaxf(smax[2], smax[3]));
+    if (!(mx > mn)) {
+        if (tid == 0) { offset[r] = mn; scale[r] = (mx - mn) / L; }
+        return;
+    }
+    const float c = 0.5f * (mn + mx), h = 0.5f * (mx - mn);
+    float best = INFINITY, ba = 1.0f;
+    for (int m = 0; m < nsearch; m++) {
+        const float a = search_alpha(m, nsearch);
+        const float sa = 2.0f * a * h / L, ma = c - a * h, ia = 1.0f / sa;
+        float err = 0.0f;
+        for (int64_t col = tid; col < i; col += 256) {
+            const float v = vrow[col];
+            const float qf = fminf(fmaxf(rintf((v - ma) * ia), 0.0f), L);
+            const float dv = v - fmaf(sa, qf, ma);
+            err = fmaf(dv * dv, wgt[col], err);
+        }
+#pragma unroll
+        for (int k = 32; k > 0; k >>= 1) err += __shfl_xor(err, k, 64);
+        if (lane == 0) part[m & 1][wave] = err;
+        __syncthreads();
+        const float tot = (part[m & 1][0] + part[m & 1][1]) + (part[m & 1][2] + part[m & 1][3]);
+        if (tot < best) { best = tot; ba = a; }
+    }
+    if (tid == 0) {
+        offset[r] = c - ba * h;
+        scale[r] = 2.0f * ba * h / L;
+    }
+}
+
 // Value of lane `src` of each 16-lane row, broadcast to the whole row (DPP row_newbcast: a VALU move,
 // no LDS round trip). `src` must fold to a constant after unrolling.
 __device__ inline float row_bcast(float x, int src) {
@@ -60,13 +128,13 @@ __device__ inline float row_bcast(float x, int src) {
     return __int_as_float(r);
 }
 
-template <int G>
+template <int G, bool SEARCH>
 __global__ __launch_bounds__(256) void sweep_block_kernel(float* __restrict__ W, int64_t o, int64_t i, int64_t ldw,
                                                           const float* __restrict__ R, int64_t ldr, int64_t b0,
                                                           int bits, uint32_t* __restrict__ codes,
                                                           float* __restrict__ scale, float* __restrict__ offset,
                                                           float* __restrict__ row_loss, float* __restrict__ E,
-                                                          int64_t lde, int first) {
+                                                          int64_t lde, int first, int nsearch) {
     extern __shared__ __align__(16) float sm[];
     float* Rb = sm;                        // 128 x 128
     float* rdiag = sm + SW_B * SW_B;       // 128 reciprocals of R_jj
@@ -141,6 +209,40 @@ __global__ __launch_bounds__(256) void sweep_block_kernel(float* __restrict__ W,
                 }
                 mu = mn;
                 s = (mx - mn) / L;
+                if (SEARCH && nsearch > 0 && mx > mn) {
+                    // Hessian-aware grid: the range shrunk about its midpoint by the factor (of nsearch
+                    // in [1/2, 1]) with the smallest rounding error weighted by 1 / R_cc^2; the row's
+                    // total is taken from lane 0 of the 16 so that every lane makes the same choice
+                    const float c = 0.5f * (mn + mx), h = 0.5f * (mx - mn);
+                    float wd[8];
+#pragma unroll
+                    for (int u = 0; u < 8; u++) {
+                        const float rr_ = rdiag[16 * u + cq];
+                        wd[u] = rr_ * rr_;
+                    }
+                    float best = INFINITY, ba = 1.0f;
+                    for (int m = 0; m < nsearch; m++) {
+                        const float a = search_alpha(m, nsearch);
+                        const float sa = 2.0f * a * h / L, ma = c - a * h, ia = 1.0f / sa;
+                        float err = 0.0f;
+#pragma unroll
+                        for (int u = 0; u < 8; u++) {
+                            if (16 * u + 15 < j || 16 * u >= j + G) continue;
+                            const int col = 16 * u + cq;
+                            if (col >= j && col < j + G) {
+                                const float qf = fminf(fmaxf(rintf((v[u] - ma) * ia), 0.0f), L);
+                                const float dv = v[u] - fmaf(sa, qf, ma);
+                                err = fmaf(dv * dv, wd[u], err);
+                            }
+                        }
+#pragma unroll
+                        for (int w = 8; w > 0; w >>= 1) err += __shfl_xor(err, w, 16);
+                        err = row_bcast(err, 0);
+                        if (err < best) { best = err; ba = a; }
+                    }
+                    mu = c - ba * h;
+                    s = 2.0f * ba * h / L;
+                }
                 invs = s > 0.0f ? 1.0f / s : 0.0f;
                 if (live && cq == 0) {
                     const int64_t gidx = (b0 + j) / (G > 0 ? G : 1);
@@ -205,10 +307,12 @@ size_t quantize_ws(int64_t o) {
     return z.used;
 }
 
-extern "C" kq_status kq_quantize_layer(float* W, int64_t o, int64_t i, int64_t ldw, const float* R, int64_t ldr, int bits,
-                                       int group, int block, uint32_t* codes, float* scale, float* offset,
-                                       float* row_loss, void* ws, size_t ws_bytes, kq_stream stream) {
+extern "C" kq_status kq_quantize_layer_search(float* W, int64_t o, int64_t i, int64_t ldw, const float* R, int64_t ldr,
+                                              int bits, int group, int block, int candidates, uint32_t* codes,
+                                              float* scale, float* offset, float* row_loss, void* ws, size_t ws_bytes,
+                                              kq_stream stream) {
     if (!W || !R || !codes || !scale || !offset) return fail(KQ_EINVAL, "kq_quantize_layer: null pointer");
+    if (candidates < 0 || candidates > 4096) return fail(KQ_EINVAL, "kq_quantize_layer: candidates must be in 0..4096");
     if (o <= 0 || i <= 0 || ldw < i || ldr < i) return fail(KQ_ESHAPE, "kq_quantize_layer: bad sizes");
     if (bits < 2 || bits > 8) return fail(KQ_EUNSUPPORTED, "kq_quantize_layer: bits must be in 2..8");
     if (block != SW_B) return fail(KQ_EUNSUPPORTED, "kq_quantize_layer: block must be 128");
@@ -224,17 +328,30 @@ extern "C" kq_status kq_quantize_layer(float* W, int64_t o, int64_t i, int64_t l
     if (o > 2147483647LL * SW_ROWS) return fail(KQ_ESHAPE, "kq_quantize_layer: o too large");
     const float L = (float)((1 << bits) - 1);
     if (group == 0) {
-        hipLaunchKernelGGL(row_grid_kernel, dim3((unsigned)o), dim3(256), 0, st, W, i, ldw, L, scale, offset);
+        if (candidates > 0) {
+            const size_t rsm = (size_t)2 * i * sizeof(float);
+            if (rsm > 150 * 1024) return fail(KQ_ESHAPE, "kq_quantize_layer: rows too long for the per-row grid search");
+            static bool rattr = false;
+            if (!rattr) {
+                hipFuncSetAttribute(reinterpret_cast<const void*>(&row_grid_search_kernel),
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, 150 * 1024);
+                rattr = true;
+            }
+            hipLaunchKernelGGL(row_grid_search_kernel, dim3((unsigned)o), dim3(256), rsm, st, W, i, ldw, L, scale, offset,
+                               R, ldr, candidates);
+        } else {
+            hipLaunchKernelGGL(row_grid_kernel, dim3((unsigned)o), dim3(256), 0, st, W, i, ldw, L, scale, offset);
+        }
         KQ_TRY(check_launch("row_grid"));
     }
     const size_t smem = (SW_B * SW_B + SW_B) * sizeof(float) + SW_ROWS * SW_B;
     static bool attr = false;
     if (!attr) {
-        hipFuncSetAttribute(reinterpret_cast<const void*>(&sweep_block_kernel<0>), hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-        hipFuncSetAttribute(reinterpret_cast<const void*>(&sweep_block_kernel<16>), hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-        hipFuncSetAttribute(reinterpret_cast<const void*>(&sweep_block_kernel<32>), hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-        hipFuncSetAttribute(reinterpret_cast<const void*>(&sweep_block_kernel<64>), hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-        hipFuncSetAttribute(reinterpret_cast<const void*>(&sweep_block_kernel<128>), hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+#define KQ_SW_ATTR(g) \
+        hipFuncSetAttribute(reinterpret_cast<const void*>(&sweep_block_kernel<g, false>), hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem); \
+        hipFuncSetAttribute(reinterpret_cast<const void*>(&sweep_block_kernel<g, true>), hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+        KQ_SW_ATTR(0) KQ_SW_ATTR(16) KQ_SW_ATTR(32) KQ_SW_ATTR(64) KQ_SW_ATTR(128)
+#undef KQ_SW_ATTR
         attr = true;
     }
     const dim3 grid((unsigned)((o + SW_ROWS - 1) / SW_ROWS));
@@ -243,13 +360,17 @@ extern "C" kq_status kq_quantize_layer(float* W, int64_t o, int64_t i, int64_t l
         for (int64_t b0 = s0; b0 < s1; b0 += SW_B) {
             const int first = b0 == 0;
             float* Eb = E + (b0 - s0);
+#define KQ_SW(g, srch) hipLaunchKernelGGL((sweep_block_kernel<g, srch>), grid, dim3(256), smem, st, W, o, i, ldw, R, ldr, b0, bits, codes, scale, offset, row_loss, Eb, (int64_t)SW_SB, first, candidates)
+#define KQ_SW2(g) if (candidates > 0) KQ_SW(g, true); else KQ_SW(g, false);
             switch (group) {
-                case 0: hipLaunchKernelGGL(sweep_block_kernel<0>, grid, dim3(256), smem, st, W, o, i, ldw, R, ldr, b0, bits, codes, scale, offset, row_loss, Eb, (int64_t)SW_SB, first); break;
-                case 16: hipLaunchKernelGGL(sweep_block_kernel<16>, grid, dim3(256), smem, st, W, o, i, ldw, R, ldr, b0, bits, codes, scale, offset, row_loss, Eb, (int64_t)SW_SB, first); break;
-                case 32: hipLaunchKernelGGL(sweep_block_kernel<32>, grid, dim3(256), smem, st, W, o, i, ldw, R, ldr, b0, bits, codes, scale, offset, row_loss, Eb, (int64_t)SW_SB, first); break;
-                case 64: hipLaunchKernelGGL(sweep_block_kernel<64>, grid, dim3(256), smem, st, W, o, i, ldw, R, ldr, b0, bits, codes, scale, offset, row_loss, Eb, (int64_t)SW_SB, first); break;
-                default: hipLaunchKernelGGL(sweep_block_kernel<128>, grid, dim3(256), smem, st, W, o, i, ldw, R, ldr, b0, bits, codes, scale, offset, row_loss, Eb, (int64_t)SW_SB, first); break;
+                case 0: KQ_SW2(0) break;
+                case 16: KQ_SW2(16) break;
+                case 32: KQ_SW2(32) break;
+                case 64: KQ_SW2(64) break;
+                default: KQ_SW2(128) break;
             }
+#undef KQ_SW2
+#undef KQ_SW
             KQ_TRY(check_launch("sweep_block"));
             // the rest of the super-block: W[:, b1:s1] -= E_b R[b0:b1, b1:s1]
             const int64_t b1 = b0 + SW_B;
@@ -267,6 +388,13 @@ extern "C" kq_status kq_quantize_layer(float* W, int64_t o, int64_t i, int64_t l
         }
     }
     return KQ_OK;
+}
+
+extern "C" kq_status kq_quantize_layer(float* W, int64_t o, int64_t i, int64_t ldw, const float* R, int64_t ldr, int bits,
+                                       int group, int block, uint32_t* codes, float* scale, float* offset,
+                                       float* row_loss, void* ws, size_t ws_bytes, kq_stream stream) {
+    return kq_quantize_layer_search(W, o, i, ldw, R, ldr, bits, group, block, 0, codes, scale, offset, row_loss, ws,
+                                    ws_bytes, stream);
 }
 
 // ----------------------------------------------------------------------------------- sensitivity

@@ -27,6 +27,8 @@ class LayerCfg:
     damp: float = 0.01
     form: str = "diag"      # H_G storage form
     blk: int = 0            # block size of a block-diagonal H_G
+    search: int = 0         # candidates of the Hessian-aware grid search (0: min-max grids)
+    order: str = "natural"  # "natural" or "trace": 128-column blocks in descending trace of H_X'
 
 
 def workspace_bytes(o: int, i: int, n: int, xdt: int, cfg: LayerCfg, verify: bool = False) -> int:
@@ -72,17 +74,44 @@ def quantize_layer(X: torch.Tensor, W: torch.Tensor, HG: torch.Tensor, s: torch.
     else:
         S, Sinv = S_cached
     K.kq_rotate_out(W2, S, cfg.form, cfg.blk, t, ws)
-    R = torch.empty((i, i), **f32)
-    K.kq_cholinv(H, cfg.damp, R, info[1:2], ws)
     W2_in = W2.clone() if verify else None
     ng = i // cfg.group if cfg.group else 1
     codes = torch.empty((o, i * cfg.bits // 32), dtype=torch.int32, device=dev)
     scale = torch.empty((o, ng), **f32)
     offset = torch.empty((o, ng), **f32)
     row_loss = torch.empty((o,), **f32)
-    K.kq_quantize_layer(W2, R, cfg.bits, cfg.group, cfg.block, codes, scale, offset, row_loss, ws)
+    R = torch.empty((i, i), **f32)
+    order = None
+    if cfg.order == "trace":
+        # blocks in descending trace of H_X': permute W'' and H_X' forward, factor and sweep there,
+        # then move the outputs back (groups and packed words stay inside 128-column blocks)
+        nb = i // cfg.block
+        order = torch.empty((2 * nb,), dtype=torch.int32, device=dev)
+        K.kq_block_order(H, cfg.block, order)
+        Ht, Hp = torch.empty_like(H), torch.empty_like(H)
+        K.kq_permute_blocks(H, Ht, cfg.block, 0, order[:nb])
+        K.kq_permute_blocks(Ht, Hp, cfg.block, 1, order[:nb])
+        del Ht
+        Wp = torch.empty_like(W2)
+        K.kq_permute_blocks(W2, Wp, cfg.block, 0, order[:nb])
+        K.kq_cholinv(Hp, cfg.damp, R, info[1:2], ws)
+        del Hp
+        cp = torch.empty_like(codes)
+        # per-row grids (group 0) do not move; group grids move with their blocks
+        sp_, op_ = (torch.empty_like(scale), torch.empty_like(offset)) if cfg.group else (scale, offset)
+        K.kq_quantize_layer_search(Wp, R, cfg.bits, cfg.group, cfg.block, cfg.search, cp, sp_, op_, row_loss, ws)
+        back = order[nb:]
+        K.kq_permute_blocks(Wp, W2, cfg.block, 0, back)
+        K.kq_permute_blocks(cp, codes, cfg.block * cfg.bits // 32, 0, back)
+        if cfg.group:
+            K.kq_permute_blocks(sp_, scale, cfg.block // cfg.group, 0, back)
+            K.kq_permute_blocks(op_, offset, cfg.block // cfg.group, 0, back)
+    else:
+        K.kq_cholinv(H, cfg.damp, R, info[1:2], ws)
+        K.kq_quantize_layer_search(W2, R, cfg.bits, cfg.group, cfg.block, cfg.search, codes, scale, offset, row_loss,
+                                   ws)
     out = {"H": H, "score": score, "Q": W2, "R": R, "codes": codes, "scale": scale, "offset": offset,
-           "row_loss": row_loss, "info": info, "S": S, "Sinv": Sinv}
+           "row_loss": row_loss, "info": info, "S": S, "Sinv": Sinv, "order": order}
     if verify:
         What = torch.empty((o, i), **f32)
         K.kq_unrotate(W2, s, t, Sinv, cfg.form, cfg.blk, What, ws)

@@ -20,14 +20,19 @@ def gpu_words_to_codes(words: np.ndarray, bits: int, i: int) -> np.ndarray:
 
 
 def replay_compare(gpu_codes: np.ndarray, W2: np.ndarray, R: np.ndarray, bits: int, group: int, block: int,
-                   rows=None, tie: float = TIE, max_replays_per_row: int = 64) -> dict:
+                   rows=None, tie: float = TIE, max_replays_per_row: int = 64, search: int = 0,
+                   gpu_scale: np.ndarray | None = None) -> dict:
     """Compare GPU codes with the oracle sweep on W2 / R (float64), replaying near-tie flips.
 
     ``rows``: row indices of W2 / gpu_codes to check (all by default). W2 and gpu_codes are indexed by
-    the same row numbers. Returns counts and the oracle codes / outputs after replay for those rows."""
+    the same row numbers. Returns counts and the oracle codes / outputs after replay for those rows.
+    With ``search`` the grids are chosen by the Hessian-aware search; ``gpu_scale`` (rows x groups)
+    replays the GPU's candidate at every grid, and the candidates' objectives are returned so that
+    the caller can check that choice against the oracle's minimum."""
     o, i = gpu_codes.shape
     rows = np.arange(o) if rows is None else np.asarray(rows)
-    out = {"replays": 0, "fail": [], "codes": {}, "Q": {}, "row_loss": {}, "mu": {}, "scale": {}}
+    out = {"replays": 0, "fail": [], "codes": {}, "Q": {}, "row_loss": {}, "mu": {}, "scale": {}, "chosen": {},
+           "objectives": {}}
     for r in rows:
         w = W2[r:r + 1]
         g = gpu_codes[r]
@@ -35,7 +40,9 @@ def replay_compare(gpu_codes: np.ndarray, W2: np.ndarray, R: np.ndarray, bits: i
         fc = np.zeros((1, i), np.int64)
         n_rep = 0
         while True:
-            res = kq.sweep_blocked(w, R, bits, group, block, force_mask=fm, force_codes=fc)
+            ns = None if gpu_scale is None else np.asarray(gpu_scale, np.float64)[r:r + 1]
+            res = kq.sweep_blocked(w, R, bits, group, block, force_mask=fm, force_codes=fc, search=search,
+                                   near_scale=ns)
             c = res["codes"][0]
             diff = np.nonzero(c != g)[0]
             if diff.size == 0:
@@ -54,6 +61,9 @@ def replay_compare(gpu_codes: np.ndarray, W2: np.ndarray, R: np.ndarray, bits: i
         out["row_loss"][int(r)] = res["row_loss"][0]
         out["mu"][int(r)] = res["mu"][0]
         out["scale"][int(r)] = res["scale"][0]
+        if search:
+            out["chosen"][int(r)] = res["chosen"][0]
+            out["objectives"][int(r)] = res["objectives"][0]
     return out
 
 

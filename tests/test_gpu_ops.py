@@ -211,6 +211,57 @@ def test_quantize_layer(o, i, bits, group):
     assert rel_fro(host(offset), mu) <= 1e-4 and rel_fro(host(scale), sc) <= 1e-4
 
 
+@pytest.mark.parametrize("o,i,bits,group,cands", [(37, 384, 3, 128, 500), (20, 512, 2, 0, 500), (16, 256, 4, 32, 64),
+                                                  (64, 256, 2, 64, 500)])
+def test_quantize_layer_search(o, i, bits, group, cands):
+    """Hessian-aware grids: the GPU's candidate at every grid is replayed in the oracle, must be the
+    oracle's minimum up to 1e-4 relative (the objective is summed in fp32 on the GPU) and never worse
+    than min-max; then codes, words, w^, row loss and grid parameters as for the min-max sweep."""
+    torch, dev = torch_dev()
+    say(f"quantize search o={o} i={i} b={bits} g={group} candidates={cands}")
+    sp = synth.scaled(synth.CONFIGS["C2"], o=o, i=i, n=4 * i, hg_ng=2 * o if o >= 64 else 256, n_outliers=2)
+    d = synth.layer_inputs(sp)
+    hg = d["HG"] if o >= 64 else np.ones(o, f32)
+    form = "full" if o >= 64 else "diag"
+    r = kq.quantize_layer(synth.widen(d["X"], "bf16"), synth.widen(d["W"], "bf16"), hg.astype(np.float64), form,
+                          d["s"], d["t"], bits, group, verify=False, rotate_out_on=False)
+    W2 = r["W2"].astype(f32)
+    R = r["R"].astype(f32)
+    Wd = to_dev(W2)
+    codes = torch.empty((o, i * bits // 32), dtype=torch.int32, device=dev)
+    ng = i // group if group else 1
+    scale = torch.empty((o, ng), dtype=torch.float32, device=dev)
+    offset = torch.empty((o, ng), dtype=torch.float32, device=dev)
+    rl = torch.empty((o,), dtype=torch.float32, device=dev)
+    ws = ws_tensor(K.kq_workspace_bytes("quantize", o, i))
+    K.kq_quantize_layer_search(Wd, to_dev(R), bits, group, 128, cands, codes, scale, offset, rl, ws)
+    words = host(codes)
+    gc = gpu_words_to_codes(words, bits, i)
+    sc_gpu = host(scale)
+    cmp = replay_compare(gc, W2.astype(np.float64), R.astype(np.float64), bits, group, 128, search=cands,
+                         gpu_scale=sc_gpu)
+    say(f"  replays={cmp['replays']} fail={cmp['fail'][:3]}")
+    assert not cmp["fail"]
+    shrunk = 0
+    for k in range(o):
+        obj, ch = cmp["objectives"][k], cmp["chosen"][k]
+        for g in range(ng):
+            best = obj[g].min()
+            assert obj[g, ch[g]] <= best * (1 + 1e-4) + 1e-30, (k, g, ch[g], obj[g].argmin())
+            assert obj[g, ch[g]] <= obj[g, -1] * (1 + 1e-6) + 1e-30
+            shrunk += int(ch[g] < cands - 1)
+    say(f"  grids narrower than min-max: {shrunk} of {o * ng}")
+    oc = np.stack([cmp["codes"][k] for k in range(o)])
+    assert np.array_equal(kq.pack(oc, bits), words.view(np.uint32))
+    Q = np.stack([cmp["Q"][k] for k in range(o)])
+    assert rel_fro(host(Wd), Q) <= 1e-5
+    loss = np.array([cmp["row_loss"][k] for k in range(o)])
+    assert np.allclose(host(rl), loss, rtol=1e-3, atol=1e-12)
+    mu = np.stack([cmp["mu"][k] for k in range(o)])
+    sc = np.stack([cmp["scale"][k] for k in range(o)])
+    assert rel_fro(host(offset), mu) <= 1e-4 and rel_fro(sc_gpu, sc) <= 1e-4
+
+
 # ----------------------------------------------------------------------------- sensitivity, unrotate, loss
 @pytest.mark.parametrize("form", ["diag", "block", "full"])
 def test_sensitivity(form):
@@ -424,3 +475,68 @@ def test_kfac_loss(form, o, i, blk, wdt):
     ws = ws_tensor(K.kq_workspace_bytes("kfac_loss", o, i, form=form, blk=blk))
     K.kq_kfac_loss(Wd, to_dev(What), to_dev(HX, "f64"), to_dev(HG), form, blk, loss, ws)
     assert abs(host(loss)[0] / ref - 1) <= 1e-10
+
+
+# ----------------------------------------------------------------------------- trace-ordered blocks
+def test_block_order_and_permute():
+    torch, dev = torch_dev()
+    rng = np.random.default_rng(31)
+    i, o, nb = 1024, 40, 8
+    A = rng.standard_normal((3 * i, i)) * np.exp(rng.standard_normal(i))
+    H = A.T @ A / (3 * i)
+    order = torch.empty(2 * nb, dtype=torch.int32, device=dev)
+    Hd = to_dev(H, "f64")
+    K.kq_block_order(Hd, 128, order)
+    want = kq.block_trace_order(H, 128)
+    got = host(order)
+    assert list(got[:nb]) == list(want) and list(got[nb:]) == list(np.argsort(want))
+    p = kq.block_perm_index(want, 128)
+    Ht, Hp = torch.empty_like(Hd), torch.empty_like(Hd)
+    K.kq_permute_blocks(Hd, Ht, 128, 0, order[:nb])
+    K.kq_permute_blocks(Ht, Hp, 128, 1, order[:nb])
+    assert np.array_equal(host(Hp), H[np.ix_(p, p)])
+    W = rng.standard_normal((o, i)).astype(f32)
+    Wd, Wp, Wb = to_dev(W), torch.empty((o, i), dtype=torch.float32, device=dev), torch.empty((o, i), dtype=torch.float32, device=dev)
+    K.kq_permute_blocks(Wd, Wp, 128, 0, order[:nb])
+    assert np.array_equal(host(Wp), W[:, p])
+    K.kq_permute_blocks(Wp, Wb, 128, 0, order[nb:])
+    assert np.array_equal(host(Wb), W)
+
+
+@pytest.mark.parametrize("bits,group,search", [(3, 128, 500), (2, 0, 0), (4, 32, 64)])
+def test_layer_trace_order(bits, group, search):
+    """The layer with blocks in trace order (and the grid search): GPU block order equal to the
+    oracle's; codes and packed words compared on the permuted problem (near-tie and candidate
+    replays as for the plain sweep); w^ and the grids back in natural order."""
+    from post_quantization_03_amd.layer import LayerCfg, quantize_layer
+    torch, dev = torch_dev()
+    o, i = 48, 640
+    say(f"trace order o={o} i={i} b={bits} g={group} search={search}")
+    sp = synth.scaled(synth.CONFIGS["C3"], o=o, i=i, n=4 * i, n_outliers=2)
+    d = synth.layer_inputs(sp)
+    X, W = to_dev(d["X"], "bf16"), to_dev(d["W"], "bf16")
+    cfg = LayerCfg(bits=bits, group=group, form="diag", search=search, order="trace")
+    out = quantize_layer(X, W, to_dev(d["HG"]), to_dev(d["s"], "i8"), to_dev(d["t"], "i8"), cfg)
+    assert host(out["info"]).tolist() == [0, 0]
+    ref = kq.quantize_layer(synth.widen(d["X"], "bf16"), synth.widen(d["W"], "bf16"), d["HG"].astype(np.float64),
+                            "diag", d["s"], d["t"], bits, group, verify=False, search=search, order="trace")
+    nb = i // 128
+    order = host(out["order"])[:nb]
+    assert list(order) == list(ref["order"])
+    p = kq.block_perm_index(order, 128)
+    words = host(out["codes"])
+    gc = gpu_words_to_codes(words, bits, i)
+    sc = host(out["scale"])
+    gsc = sc[:, kq.block_perm_index(order, 128 // group)] if group else sc
+    # the permuted problem with the GPU's fp32 factor
+    W2p = ref["W2"][:, p]
+    Rg = host(out["R"]).astype(np.float64)
+    cmp = replay_compare(gc[:, p], W2p, Rg, bits, group, 128, search=search, gpu_scale=gsc if search else None)
+    say(f"  replays={cmp['replays']} fail={cmp['fail'][:3]}")
+    assert not cmp["fail"]
+    oc = np.stack([cmp["codes"][k] for k in range(o)])
+    inv = np.argsort(p)
+    assert np.array_equal(kq.pack(oc[:, inv], bits), words.view(np.uint32))
+    Q = np.stack([cmp["Q"][k] for k in range(o)])[:, inv]
+    assert rel_fro(host(out["Q"]), Q) <= 1e-5
+    assert rel_fro(Rg, ref["R_perm"]) <= 1e-5

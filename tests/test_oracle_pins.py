@@ -471,6 +471,95 @@ def test_p14_forms_are_slices():
     assert np.array_equal(kq.hg_forms(H, "full"), H)
 
 
+# ----------------------------------------------------------------------------- P15
+def test_p15_grid_search_brute_force_and_bound():
+    """Hessian-aware grid: the argmin over the candidates by explicit scalar loops (round half to
+    even written out), the min-max grid as the alpha = 1 candidate, and a weighted error never above
+    the min-max grid's."""
+    rng = np.random.default_rng(9)
+    bits, M = 3, 41
+    L = 2 ** bits - 1
+    v = rng.standard_normal((5, 6))
+    d = np.exp(rng.standard_normal(6))
+    mu, s, idx, obj = kq.grid_search(v, d, bits, M)
+    mu1, s1 = kq.grid_params(v, bits)
+    assert np.allclose(obj[:, -1], [np.sum(d * (v[r] - kq.quantize(v[r], mu1[r], s1[r], bits)[1]) ** 2)
+                                    for r in range(5)], rtol=1e-12)
+    assert np.all(obj[np.arange(5), idx] <= obj[:, -1])
+
+    def rne(x):
+        f = np.floor(x)
+        frac = x - f
+        return f + 1 if frac > 0.5 else f if frac < 0.5 else (f if f % 2 == 0 else f + 1)
+    for r in range(5):
+        lo, hi = v[r].min(), v[r].max()
+        best, bi = None, None
+        for m in range(M):
+            a = 0.5 + 0.5 * m / (M - 1)
+            st = 2 * a * (hi - lo) / 2 / L
+            off = (lo + hi) / 2 - a * (hi - lo) / 2
+            e = 0.0
+            for c in range(6):
+                q = min(max(rne((v[r, c] - off) / st), 0), L)
+                e += d[c] * (v[r, c] - (off + st * q)) ** 2
+            if best is None or e < best:
+                best, bi = e, m
+        assert bi == idx[r] and np.isclose(best, obj[r, idx[r]], rtol=1e-12)
+
+
+def test_p15_grid_search_special_cases():
+    """Values exactly on the min-max grid keep it (zero error, every smaller range errs); a
+    low-weight outlier is clipped (a smaller range wins); one candidate is min-max; the sweep with
+    one candidate equals the plain sweep."""
+    bits, L = 2, 3
+    v = np.array([[0.0, 1.0, 2.0, 3.0, 1.0, 2.0]])
+    mu, s, idx, obj = kq.grid_search(v, np.ones(6), bits, 500)
+    assert idx[0] == 499 and obj[0, 499] == 0.0 and np.all(obj[0, :499] > 0)
+    v = np.array([[0.0, 0.1, 0.2, 0.3, 0.15, 10.0]])
+    d = np.array([1.0, 1.0, 1.0, 1.0, 1.0, 1e-9])
+    mu, s, idx, obj = kq.grid_search(v, d, bits, 500)
+    assert idx[0] < 499 and obj[0, idx[0]] < obj[0, 499]
+    rng = np.random.default_rng(1)
+    W = rng.standard_normal((6, 256))
+    R = np.triu(rng.standard_normal((256, 256)) * 0.01) + np.eye(256)
+    a = kq.sweep_blocked(W, R, 3, 32, 128)
+    b = kq.sweep_blocked(W, R, 3, 32, 128, search=1)
+    assert np.array_equal(a["codes"], b["codes"]) and np.allclose(a["Q"], b["Q"], atol=1e-12)
+
+
+# ----------------------------------------------------------------------------- P16
+def test_p16_trace_order():
+    """Trace-ordered blocks: the order sorts block traces descending (stable); blocks already in that
+    order give the plain sweep; two blocks in ascending order equal the plain sweep on hand-swapped
+    inputs, swapped back; the row loss equals dW (H_X' + lambda I) dW^T in natural coordinates."""
+    rng = np.random.default_rng(12)
+    d = np.array([1.0, 5.0, 3.0, 5.0])
+    H = np.diag(np.repeat(d, 2))
+    assert list(kq.block_trace_order(H, 2)) == [1, 3, 2, 0]
+    i, o, bits, g = 256, 5, 3, 64
+    A = rng.standard_normal((2 * i, i))
+    Hx0 = A.T @ A / (2 * i)
+    D = np.ones(i)
+    D[:128] = 2.0                           # congruence keeps H SPD; first block's trace x4: identity order
+    Hx = Hx0 * np.outer(D, D)
+    H, lam = kq.damped(Hx)
+    W = rng.standard_normal((o, i))
+    a = kq.sweep_trace_order(W, H, bits, g)
+    assert list(a["order"]) == [0, 1]
+    b = kq.sweep_blocked(W, kq.inverse_upper_factor(H), bits, g)
+    assert np.array_equal(a["codes"], b["codes"]) and np.allclose(a["Q"], b["Q"], atol=1e-12)
+    D[:128] = 0.5                           # now the second block leads
+    H2, _ = kq.damped(Hx0 * np.outer(D, D))
+    c = kq.sweep_trace_order(W, H2, bits, g)
+    assert list(c["order"]) == [1, 0]
+    p = np.concatenate([np.arange(128, 256), np.arange(0, 128)])
+    ref = kq.sweep_blocked(W[:, p], kq.inverse_upper_factor(H2[np.ix_(p, p)]), bits, g)
+    assert np.array_equal(c["codes"][:, p], ref["codes"]) and np.allclose(c["Q"][:, p], ref["Q"], atol=1e-12)
+    assert np.allclose(c["scale"], np.concatenate([ref["scale"][:, 2:], ref["scale"][:, :2]], axis=1))
+    dW = W - c["Q"]
+    assert np.allclose(np.einsum("ri,ij,rj->r", dW, H2, dW), c["row_loss"], rtol=1e-9)
+
+
 def test_golden_regression_small_layer():
     """Stored oracle outputs of the small 256x256 workload (written by tests/golden/make_golden.py,
     which calls only the oracle) guard the oracle against accidental change."""
