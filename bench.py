@@ -463,6 +463,69 @@ def solver_variants(sp, candidates: int = 500, reps: int = 3) -> dict:
     return {"workload": sp.name, "variants": out}
 
 
+def drift_study(sp, rel: float = 0.05, reps: int = 3) -> dict:
+    """Input-drift correction on the workload's layer: the inputs drift by `rel` of each channel's
+    scale (synth.gen_X_drift). Solvers: GPTQ on the clean H_X (target W), GPTQ on the drifted H~
+    (target W), and the drift-corrected solver (target W* = W C (H~ + lambda I)^{-1} with H~). Each is
+    scored by tr(H_G (W^ - W*) H~ (W^ - W*)^T), the part of the output error on the drifted inputs,
+    tr(H_G (W^ X~^T - W X^T)(...)^T) / n, that depends on W^ (kq_kfac_loss with W* and H~), and
+    timed as a whole layer step with S cached (HIP events, median)."""
+    import torch
+
+    from post_quantization_03_amd import _lib as K
+    from post_quantization_03_amd.layer import LayerCfg, quantize_layer, workspace_bytes
+
+    dev = torch.device("cuda:0")
+    d = synth.layer_inputs(sp)
+
+    def to(a, kind):
+        if kind == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    X, W, HG = to(d["X"], sp.x_dtype), to(d["W"], sp.w_dtype), to(d["HG"], "f32")
+    Xt = to(synth.gen_X_drift(sp, rel=rel), sp.x_dtype)
+    s, t = to(d["s"], "i8"), to(d["t"], "i8")
+    del d
+    o, i, n = sp.o, sp.i, sp.n
+    xdt = K.KQ_BF16 if sp.x_dtype == "bf16" else K.KQ_F32
+    cfg = LayerCfg(bits=sp.bits, group=sp.group, damp=sp.damp, form=sp.hg_form,
+                   blk=sp.hg_blk if sp.hg_form == "block" else 0)
+    ws = torch.empty(max(workspace_bytes(o, i, n, xdt, cfg, verify=True),
+                         K.kq_workspace_bytes("kfac_loss", o, i, form=cfg.form, blk=cfg.blk),
+                         K.kq_workspace_bytes("cross", 0, i, n), K.kq_workspace_bytes("drift", o, i)),
+                     dtype=torch.uint8, device=dev)
+    Ht = torch.empty((i, i), dtype=torch.float64, device=dev)
+    K.kq_hessian_accum(Xt, Ht, 1.0 / n, 0.0, ws)
+    C = torch.empty((i, i), dtype=torch.float64, device=dev)
+    K.kq_cross_accum(X, Xt, C, 1.0 / n, 0.0, ws)
+    R0 = torch.empty((i, i), dtype=torch.float32, device=dev)
+    info = torch.zeros(2, dtype=torch.int32, device=dev)
+    K.kq_cholinv(Ht, sp.damp, R0, info[0:1], ws)
+    Wstar = torch.empty((o, i), dtype=torch.float32, device=dev)
+    K.kq_drift_target(W, C, R0, Wstar, ws)
+    Sc = torch.empty((o, o) if cfg.form == "full" else HG.shape, dtype=torch.float32, device=dev)
+    Sic = torch.empty_like(Sc)
+    K.kq_hg_sqrt(HG, cfg.form, o, cfg.blk, Sc, Sic, info[1:2], ws)
+    loss = torch.empty(1, dtype=torch.float64, device=dev)
+    out = {}
+    for name, xa, xd in (("gptq_clean_H", X, None), ("gptq_drifted_H", Xt, None), ("drift_corrected", X, Xt)):
+        times = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            r = quantize_layer(xa, W, HG, s, t, cfg, ws=ws, S_cached=(Sc, Sic), verify=True, X_drift=xd)
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        K.kq_kfac_loss(Wstar, r["What"], Ht, HG, cfg.form, cfg.blk, loss, ws)
+        torch.cuda.synchronize()
+        out[name] = {"layer_ms_S_cached": round(float(np.median(times)), 3), "drift_objective": float(loss.item())}
+    ref = out["gptq_drifted_H"]["drift_objective"]
+    for v in out.values():
+        v["vs_gptq_drifted_H"] = round(v["drift_objective"] / ref, 5)
+    return {"workload": sp.name, "drift_rel": rel, "variants": out}
+
+
 def host_list(t) -> list:
     return [int(v) for v in t.cpu().tolist()]
 
@@ -531,6 +594,9 @@ def main():
     ap.add_argument("--solver-variants", action="store_true",
                     help="run the workload's layer with the Hessian-aware grid search and/or trace-ordered blocks and "
                          "print time and exact K-FAC loss of each as its own JSON line")
+    ap.add_argument("--drift", action="store_true",
+                    help="compare GPTQ with the input-drift-corrected solver on drifted synthetic inputs and print "
+                         "the result as its own JSON line")
     ap.add_argument("--matvec-only", action="store_true",
                     help="time only the inference-side product (kq_matvec_quantized) on the workload's layer shape "
                          "with random codes, and print its own JSON line (not the benchmark line)")
@@ -540,6 +606,9 @@ def main():
               "(multi-GPU sharding is described in DESIGN.md, not implemented).", file=sys.stderr)
         sys.exit(2)
     sp = synth.CONFIGS[args.workload]
+    if args.drift:
+        print(json.dumps(drift_study(sp)), flush=True)
+        return
     if args.solver_variants:
         print(json.dumps(solver_variants(sp)), flush=True)
         return

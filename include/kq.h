@@ -68,7 +68,9 @@ typedef enum {
     KQ_OP_LOSS = 7,
     KQ_OP_MATVEC = 8,      /* n = number of tokens */
     KQ_OP_HG_LOWRANK = 9,  /* n = gradient rows, o, i = rank k */
-    KQ_OP_KFAC_LOSS = 10   /* o, i, form, blk */
+    KQ_OP_KFAC_LOSS = 10,  /* o, i, form, blk */
+    KQ_OP_CROSS = 11,      /* n tokens, i */
+    KQ_OP_DRIFT = 12       /* o, i */
 } kq_op;
 
 /* Workspace bytes needed by `op` for a layer of o x i weights, n calibration tokens (X dtype
@@ -277,6 +279,29 @@ kq_status kq_hg_lowrank(const float* G, int64_t n, int64_t o, int64_t ldg, int64
 kq_status kq_kfac_loss(const void* W, kq_dtype wdt, int64_t ldw, const float* What, int64_t ldq, int64_t o, int64_t i,
                        const double* HX, int64_t ldh, const float* HG, kq_hg_form form, int64_t blk, double* loss,
                        void* ws, size_t ws_bytes, kq_stream stream);
+
+/*
+ * Cross-covariance of two token matrices, C <- beta C + alpha A^T B (d x d fp64, leading dimension d),
+ * for the input-drift correction below (A = X the full-precision inputs, B = X~ the drifted ones,
+ * alpha = 1/n). A, B: n x d fp32 or bf16 (dt), leading dimensions lda, ldb. fp64 accumulation (rows
+ * widened in chunks of 8192). Workspace: kq_workspace_bytes(KQ_OP_CROSS, 0, d, n, ...).
+ */
+kq_status kq_cross_accum(const void* A, const void* B, kq_dtype dt, int64_t n, int64_t d, int64_t lda, int64_t ldb,
+                         double alpha, double beta, double* C, void* ws, size_t ws_bytes, kq_stream stream);
+
+/*
+ * Input-drift correction (KronQ review page, Prior limitations: GPTAQ corrects the drift of a layer's
+ * input caused by quantizing earlier layers; the pages do not give its formula, so this is this
+ * library's reading): the layer should reproduce W X^T from the drifted X~, and
+ *     || W^ X~^T - W X^T ||^2 = || (W^ - W*) X~^T ||^2 + const,  W* = W C (H~ + lambda I)^{-1}
+ * with C = X^T X~ / n (kq_cross_accum) and H~ = X~^T X~ / n, so the unchanged sweep runs on the
+ * target W* with H~ (lambda = damp mean diag H~: the ridge solution). Wt (o x i fp32, ldt) = W C R^T R
+ * with R the damped factor of H~ from kq_cholinv ((H~ + lambda I)^{-1} = R^T R). W: fp32 or bf16;
+ * C: fp64 (ldc); R: fp32 (ldr). fp64 products. Workspace: kq_workspace_bytes(KQ_OP_DRIFT, o, i, ...).
+ */
+kq_status kq_drift_target(const void* W, kq_dtype wdt, int64_t ldw, int64_t o, int64_t i, const double* C, int64_t ldc,
+                          const float* R, int64_t ldr, float* Wt, int64_t ldt, void* ws, size_t ws_bytes,
+                          kq_stream stream);
 
 /*
  * Verification: layer loss in rotated coordinates, sum_r (Q - W2)_r HX2 (Q - W2)_r^T, which equals

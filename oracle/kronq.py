@@ -477,6 +477,21 @@ def sensitivity(HX: np.ndarray, HG: np.ndarray, form: str) -> float:
 # ============================================================================= whole layer
 
 
+def drift_target(W: np.ndarray, X: np.ndarray, Xt: np.ndarray, damp: float = 0.01) -> dict:
+    """Target of the input-drift correction (KronQ review page, Prior limitations: GPTAQ corrects for
+    the drift of the input caused by quantizing earlier layers; the formula is not on the pages, so
+    this follows the reading that the layer should reproduce W X^T from the drifted inputs X~):
+    || W^ X~^T - W X^T ||^2 + n lambda ||W^||^2 is minimised by W* = W C (H~ + lambda I)^{-1},
+    C = X^T X~ / n, H~ = X~^T X~ / n, lambda = damp mean diag H~; the sweep then runs on (W*, H~)."""
+    X = np.asarray(X, np.float64)
+    Xt = np.asarray(Xt, np.float64)
+    n = X.shape[0]
+    C = X.T @ Xt / n
+    Ht = Xt.T @ Xt / n
+    H, lam = damped(Ht, damp)
+    return {"W": np.asarray(W, np.float64) @ C @ np.linalg.inv(H), "C": C, "H": Ht, "lam": lam}
+
+
 def block_trace_order(H: np.ndarray, width: int = 128) -> np.ndarray:
     """Blocks of `width` columns in descending order of the trace of their diagonal part of H (ties:
     lower index first). H_Z-PTQ page, Weight scales and rounding: the blocks with larger curvature
@@ -518,12 +533,18 @@ def sweep_trace_order(W2: np.ndarray, H: np.ndarray, bits: int, group: int, bloc
 
 def quantize_layer(X, W, HG, form: str, s, t, bits: int, group: int, block: int = 128,
                    damp: float = 0.01, rotate_in: bool = True, rotate_out_on: bool = True,
-                   mode: str = "blocked", verify: bool = True, search: int = 0, order: str = "natural") -> dict:
+                   mode: str = "blocked", verify: bool = True, search: int = 0, order: str = "natural",
+                   Xt=None) -> dict:
     """All steps of the per-layer solver on float64 copies of the inputs. ``search``: candidates of
     the Hessian-aware grid search (0: min-max); ``order``: "natural" or "trace" (blocks in descending
-    trace of the damped, rotated H_X)."""
-    HX = hessian(X)
+    trace of the damped, rotated H_X); ``Xt``: drifted inputs (the sweep then runs on the drift
+    target W* with H~ = X~^T X~ / n)."""
     W = np.asarray(W, np.float64)
+    if Xt is not None:
+        dr = drift_target(W, X, Xt, damp)
+        HX, W = dr["H"], dr["W"]
+    else:
+        HX = hessian(X)
     o, i = W.shape
     if rotate_in:
         W1, HX2 = rotate_in_weights(W, s), rotate_in_hessian(HX, s)

@@ -13,12 +13,12 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkq.so")
 KQ_F32, KQ_BF16 = 0, 1
 HG_FORM = {"diag": 0, "block": 1, "full": 2}
 OP = {"hessian": 0, "rotate_in": 1, "hg_sqrt": 2, "rotate_out": 3, "cholinv": 4, "quantize": 5, "unrotate": 6,
-      "loss": 7, "matvec": 8, "hg_lowrank": 9, "kfac_loss": 10}
+      "loss": 7, "matvec": 8, "hg_lowrank": 9, "kfac_loss": 10, "cross": 11, "drift": 12}
 EXPORTS = ("kq_workspace_bytes", "kq_hessian_accum", "kq_rotate_in", "kq_hg_sqrt", "kq_rotate_out", "kq_cholinv",
            "kq_quantize_layer", "kq_sensitivity", "kq_unrotate", "kq_layer_loss", "kq_strerror", "kq_last_error",
            "kq_hadamard_order", "kq_version", "kq_allocate_bits", "kq_matvec_quantized",
            "kq_hg_extract", "kq_hg_lowrank", "kq_kfac_loss", "kq_quantize_layer_search",
-           "kq_block_order", "kq_permute_blocks")
+           "kq_block_order", "kq_permute_blocks", "kq_cross_accum", "kq_drift_target")
 
 
 class KQError(RuntimeError):
@@ -60,6 +60,9 @@ def lib() -> ctypes.CDLL:
                                        _vp, _i64, _vp, _sz, _vp]),
         "kq_hg_extract": (_int, [_vp, _i64, _i64, _int, _i64, _vp, _vp]),
         "kq_block_order": (_int, [_vp, _i64, _i64, _i64, _vp, _vp]),
+        "kq_cross_accum": (_int, [_vp, _vp, _int, _i64, _i64, _i64, _i64, ctypes.c_double, ctypes.c_double, _vp, _vp,
+                                  _sz, _vp]),
+        "kq_drift_target": (_int, [_vp, _int, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _sz, _vp]),
         "kq_permute_blocks": (_int, [_vp, _i64, _vp, _i64, _i64, _i64, _i64, _int, _int, _vp, _vp]),
         "kq_quantize_layer_search": (_int, [_vp, _i64, _i64, _i64, _vp, _i64, _int, _int, _int, _int, _vp, _vp, _vp,
                                             _vp, _vp, _sz, _vp]),
@@ -190,6 +193,22 @@ def kq_permute_blocks(src, dst, width: int, axis: int, perm, stream=None) -> Non
     rows, cols = src.shape
     _check("kq_permute_blocks", lib().kq_permute_blocks(_p(src), src.stride(0), _p(dst), dst.stride(0), rows, cols,
                                                         width, axis, src.element_size(), _p(perm), _stream(stream)))
+
+
+def kq_cross_accum(A, B, C, alpha: float, beta: float, ws=None, stream=None) -> None:
+    n, d = A.shape
+    if B.shape != A.shape or B.dtype != A.dtype:
+        raise ValueError("kq_cross_accum: A and B must have the same shape and dtype")
+    w, wb = _ws(ws)
+    _check("kq_cross_accum", lib().kq_cross_accum(_p(A), _p(B), _xdt(A), n, d, A.stride(0), B.stride(0), alpha, beta,
+                                                  _p(C), w, wb, _stream(stream)))
+
+
+def kq_drift_target(W, C, R, Wt, ws=None, stream=None) -> None:
+    o, i = W.shape
+    w, wb = _ws(ws)
+    _check("kq_drift_target", lib().kq_drift_target(_p(W), _xdt(W), W.stride(0), o, i, _p(C), C.stride(0), _p(R),
+                                                    R.stride(0), _p(Wt), Wt.stride(0), w, wb, _stream(stream)))
 
 
 def kq_sensitivity(HX, HG, form: str, o: int, blk: int, score, stream=None) -> None:

@@ -17,6 +17,8 @@ size_t loss_ws(int64_t o, int64_t i);
 size_t matvec_ws(int64_t o, int64_t i, int64_t nt, kq_hg_form form);
 size_t hg_lowrank_ws(int64_t n, int64_t o, int64_t k);
 size_t kfac_loss_ws(int64_t o, int64_t i, kq_hg_form form, int64_t blk);
+size_t cross_ws(int64_t n, int64_t d);
+size_t drift_ws(int64_t o, int64_t i);
 
 namespace kq {
 
@@ -78,6 +80,8 @@ extern "C" size_t kq_workspace_bytes(kq_op op, int64_t o, int64_t i, int64_t n, 
         case KQ_OP_MATVEC: return matvec_ws(o, i, n, form);
         case KQ_OP_HG_LOWRANK: return hg_lowrank_ws(n, o, i);
         case KQ_OP_KFAC_LOSS: return kfac_loss_ws(o, i, form, blk);
+        case KQ_OP_CROSS: return cross_ws(n, i);
+        case KQ_OP_DRIFT: return drift_ws(o, i);
     }
     return 0;
 }

@@ -451,3 +451,103 @@ extern "C" kq_status kq_permute_blocks(const void* in, int64_t ldi, void* out, i
         return fail(KQ_EINVAL, "kq_permute_blocks: elements must be 4 or 8 bytes");
     return check_launch("permute_blocks");
 }
+
+// ------------------------------------------------------------------------------ input drift
+// GPTAQ-style correction of the input drift (KronQ review page, Prior limitations: GPTAQ corrects for
+// the drift of a layer's input caused by quantizing earlier layers, still with H_X only; the
+// solver's formula is not on the pages). Reading used here: with X the full-precision inputs and
+// X~ the drifted ones, || W^ X~^T - W X^T ||^2 = || (W^ - W*) X~^T ||^2 + const for
+//     W* = W C (H~ + lambda I)^{-1},  C = X^T X~ / n,  H~ = X~^T X~ / n
+// (exact for lambda = 0; with lambda the ridge solution), so the drift moves the target from W to W*
+// and the unchanged sweep then runs on (W*, H~).
+
+__global__ void widen_any_kernel(const void* __restrict__ src, int bf16, int64_t ld, int64_t rows, int64_t cols,
+                                 double* __restrict__ dst) {
+    const int64_t total = rows * cols;
+    for (int64_t e = blockIdx.x * (int64_t)256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256) {
+        const int64_t r = e / cols, c = e % cols;
+        dst[e] = bf16 ? (double)__uint_as_float((uint32_t)static_cast<const uint16_t*>(src)[r * ld + c] << 16)
+                      : (double)static_cast<const float*>(src)[r * ld + c];
+    }
+}
+
+__global__ void narrow_kernel(const double* __restrict__ src, int64_t rows, int64_t cols, float* __restrict__ dst,
+                              int64_t ldd) {
+    const int64_t total = rows * cols;
+    for (int64_t e = blockIdx.x * (int64_t)256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256)
+        dst[(e / cols) * ldd + e % cols] = (float)src[e];
+}
+
+constexpr int64_t XC_CHUNK = 8192;   // token rows widened per step
+
+size_t cross_ws(int64_t n, int64_t d) {
+    const int64_t c = n < XC_CHUNK ? n : XC_CHUNK;
+    Sizer z;
+    z.take<double>((size_t)c * d);
+    z.take<double>((size_t)c * d);
+    return z.used;
+}
+
+extern "C" kq_status kq_cross_accum(const void* A, const void* B, kq_dtype dt, int64_t n, int64_t d, int64_t lda,
+                                    int64_t ldb, double alpha, double beta, double* C, void* ws, size_t ws_bytes,
+                                    kq_stream stream) {
+    if (!A || !B || !C) return fail(KQ_EINVAL, "kq_cross_accum: null pointer");
+    if (n <= 0 || d <= 0 || lda < d || ldb < d) return fail(KQ_ESHAPE, "kq_cross_accum: bad sizes");
+    if (dt != KQ_F32 && dt != KQ_BF16) return fail(KQ_EINVAL, "kq_cross_accum: inputs must be fp32 or bf16");
+    if (!ws || ws_bytes < cross_ws(n, d)) return fail(KQ_EWORKSPACE, "kq_cross_accum: workspace too small");
+    hipStream_t st = hs(stream);
+    Arena ar(ws, ws_bytes);
+    const int64_t chunk = n < XC_CHUNK ? n : XC_CHUNK;
+    double* Ad = ar.take<double>((size_t)chunk * d);
+    double* Bd = ar.take<double>((size_t)chunk * d);
+    const int bf = dt == KQ_BF16 ? 1 : 0;
+    const size_t es = bf ? 2 : 4;
+    for (int64_t r0 = 0; r0 < n; r0 += chunk) {
+        const int64_t m = n - r0 < chunk ? n - r0 : chunk;
+        hipLaunchKernelGGL(widen_any_kernel, dim3(grid_for(m * d)), dim3(256), 0, st,
+                           static_cast<const char*>(A) + (size_t)r0 * lda * es, bf, lda, m, d, Ad);
+        hipLaunchKernelGGL(widen_any_kernel, dim3(grid_for(m * d)), dim3(256), 0, st,
+                           static_cast<const char*>(B) + (size_t)r0 * ldb * es, bf, ldb, m, d, Bd);
+        KQ_TRY(check_launch("cross widen"));
+        // C = alpha A^T B + (first chunk: beta, then 1) C
+        GemmArgs<double> g = gemm_args<double>(d, d, m, Ad, d, Bd, d, C, d, alpha, r0 == 0 ? beta : 1.0);
+        KQ_TRY(gemm<double>(g, true, false, st));
+    }
+    return KQ_OK;
+}
+
+size_t drift_ws(int64_t o, int64_t i) {
+    Sizer z;
+    z.take<double>((size_t)o * i);   // W
+    z.take<double>((size_t)o * i);   // W C
+    z.take<double>((size_t)o * i);   // (W C) R^T
+    z.take<double>((size_t)i * i);   // R
+    return z.used;
+}
+
+extern "C" kq_status kq_drift_target(const void* W, kq_dtype wdt, int64_t ldw, int64_t o, int64_t i, const double* C,
+                                     int64_t ldc, const float* R, int64_t ldr, float* Wt, int64_t ldt, void* ws,
+                                     size_t ws_bytes, kq_stream stream) {
+    if (!W || !C || !R || !Wt) return fail(KQ_EINVAL, "kq_drift_target: null pointer");
+    if (o <= 0 || i <= 0 || ldw < i || ldc < i || ldr < i || ldt < i) return fail(KQ_ESHAPE, "kq_drift_target: bad sizes");
+    if (wdt != KQ_F32 && wdt != KQ_BF16) return fail(KQ_EINVAL, "kq_drift_target: W must be fp32 or bf16");
+    if (!ws || ws_bytes < drift_ws(o, i)) return fail(KQ_EWORKSPACE, "kq_drift_target: workspace too small");
+    hipStream_t st = hs(stream);
+    Arena ar(ws, ws_bytes);
+    double* Wd = ar.take<double>((size_t)o * i);
+    double* T1 = ar.take<double>((size_t)o * i);
+    double* T2 = ar.take<double>((size_t)o * i);
+    double* Rd = ar.take<double>((size_t)i * i);
+    hipLaunchKernelGGL(widen_any_kernel, dim3(grid_for(o * i)), dim3(256), 0, st, W, wdt == KQ_BF16 ? 1 : 0, ldw, o, i, Wd);
+    hipLaunchKernelGGL(widen_rows_kernel, dim3(grid_for(i * i)), dim3(256), 0, st, R, ldr, i, i, Rd);
+    KQ_TRY(check_launch("drift widen"));
+    // W* = ((W C) R^T) R with (H~ + lambda I)^{-1} = R^T R
+    GemmArgs<double> a = gemm_args<double>(o, i, i, Wd, i, C, ldc, T1, i, 1.0, 0.0);
+    KQ_TRY(gemm<double>(a, false, false, st));
+    GemmArgs<double> b = gemm_args<double>(o, i, i, T1, i, Rd, i, T2, i, 1.0, 0.0);
+    KQ_TRY(gemm<double>(b, false, true, st));
+    GemmArgs<double> c = gemm_args<double>(o, i, i, T2, i, Rd, i, T1, i, 1.0, 0.0);
+    KQ_TRY(gemm<double>(c, false, false, st));
+    hipLaunchKernelGGL(narrow_kernel, dim3(grid_for(o * i)), dim3(256), 0, st, T1, o, i, Wt, ldt);
+    return check_launch("drift narrow");
+}

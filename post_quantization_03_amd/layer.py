@@ -46,8 +46,10 @@ def hg_factor_shape(o: int, cfg: LayerCfg):
 
 def quantize_layer(X: torch.Tensor, W: torch.Tensor, HG: torch.Tensor, s: torch.Tensor, t: torch.Tensor,
                    cfg: LayerCfg, ws: torch.Tensor | None = None, S_cached=None, verify: bool = False,
-                   x_batch: int | None = None) -> dict:
-    """All steps of the per-layer solver on device-resident inputs. Returns device tensors."""
+                   x_batch: int | None = None, X_drift: torch.Tensor | None = None) -> dict:
+    """All steps of the per-layer solver on device-resident inputs. Returns device tensors.
+    X_drift: the layer's inputs once earlier layers are quantized; the sweep then runs on the drift
+    target W* = W C (H~ + lambda I)^{-1} with H~ from X_drift (kq_drift_target)."""
     dev = W.device
     o, i = W.shape
     n = X.shape[0]
@@ -57,11 +59,24 @@ def quantize_layer(X: torch.Tensor, W: torch.Tensor, HG: torch.Tensor, s: torch.
                          dtype=torch.uint8, device=dev)
     f32 = dict(dtype=torch.float32, device=dev)
     H = torch.empty((i, i), dtype=torch.float64, device=dev)
+    Xh = X if X_drift is None else X_drift
     if x_batch is None or x_batch >= n:
-        K.kq_hessian_accum(X, H, 1.0 / n, 0.0, ws)
+        K.kq_hessian_accum(Xh, H, 1.0 / n, 0.0, ws)
     else:
         for k0 in range(0, n, x_batch):
-            K.kq_hessian_accum(X[k0:k0 + x_batch], H, 1.0 / n, 0.0 if k0 == 0 else 1.0, ws)
+            K.kq_hessian_accum(Xh[k0:k0 + x_batch], H, 1.0 / n, 0.0 if k0 == 0 else 1.0, ws)
+    if X_drift is not None:
+        C = torch.empty((i, i), dtype=torch.float64, device=dev)
+        wsx = torch.empty(max(K.kq_workspace_bytes("cross", 0, i, n), K.kq_workspace_bytes("drift", o, i),
+                              K.kq_workspace_bytes("cholinv", o, i)), dtype=torch.uint8, device=dev)
+        K.kq_cross_accum(X, X_drift, C, 1.0 / n, 0.0, wsx)
+        R0 = torch.empty((i, i), **f32)
+        info0 = torch.zeros((1,), dtype=torch.int32, device=dev)
+        K.kq_cholinv(H, cfg.damp, R0, info0, wsx)
+        Wt = torch.empty((o, i), **f32)
+        K.kq_drift_target(W, C, R0, Wt, wsx)
+        del C, R0, wsx
+        W = Wt
     score = torch.empty((1,), dtype=torch.float64, device=dev)
     K.kq_sensitivity(H, HG, cfg.form, o, cfg.blk, score)
     W2 = torch.empty((o, i), **f32)

@@ -7,6 +7,6 @@ any of the method's arithmetic.
 """
 from .configs import (  # noqa: F401
     CONFIGS, LayerSpec, C5_SUBLAYERS, C5_INPUTS, C5_LAYERS, C5_TOKENS, c5_specs, scaled,
-    layer_inputs, gen_W, gen_X, gen_X_chunks, gen_HG, gen_G, gen_omega, gen_signs,
+    layer_inputs, gen_W, gen_X, gen_X_chunks, gen_HG, gen_G, gen_omega, gen_signs, gen_X_drift,
     bf16_round, bf16_to_f32, f32_to_bf16_bits, widen, rng,
 )

@@ -18,7 +18,7 @@ from typing import Iterator
 
 import numpy as np
 
-TAG_W, TAG_X, TAG_G, TAG_S, TAG_T, TAG_OUT, TAG_OMEGA = 0, 1, 2, 3, 4, 5, 6
+TAG_W, TAG_X, TAG_G, TAG_S, TAG_T, TAG_OUT, TAG_OMEGA, TAG_DRIFT = 0, 1, 2, 3, 4, 5, 6, 7
 
 
 def rng(cfg: int, layer: int, sub: int, tag: int) -> np.random.Generator:
@@ -156,6 +156,27 @@ def gen_X_chunks(spec: LayerSpec, rows: int | None = None, chunk: int = 4096) ->
             x = z * sc[None, :]
         yield _store(x, spec.x_dtype)
         done += m
+
+
+def gen_X_drift(spec: LayerSpec, rows: int | None = None, rel: float = 0.05) -> np.ndarray:
+    """Drifted calibration inputs X~ (what the layer sees once earlier layers are quantized), n x i in
+    the storage type: the same draws as gen_X plus independent noise of `rel` times each channel's
+    scale (1 for the ReLU recipe), added before the storage rounding."""
+    n = spec.n if rows is None else min(rows, spec.n)
+    g = rng(spec.cfg, spec.layer, spec.x_sub, TAG_X)
+    gd = rng(spec.cfg, spec.layer, spec.x_sub, TAG_DRIFT)
+    sc = _x_channel_scales(spec, g)
+    dt = np.uint16 if spec.x_dtype == "bf16" else np.float32
+    out = np.empty((n, spec.i), dtype=dt)
+    done = 0
+    while done < n:
+        m = min(4096, n - done)
+        z = g.standard_normal((m, spec.i))
+        x = np.maximum(z + 0.2533, 0.0) if spec.x_recipe == "relu" else z * sc[None, :]
+        noise = gd.standard_normal((m, spec.i)) * (1.0 if sc is None else sc[None, :])
+        out[done:done + m] = _store(x + rel * noise, spec.x_dtype)
+        done += m
+    return out
 
 
 def gen_X(spec: LayerSpec, rows: int | None = None) -> np.ndarray:

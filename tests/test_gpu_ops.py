@@ -540,3 +540,66 @@ def test_layer_trace_order(bits, group, search):
     Q = np.stack([cmp["Q"][k] for k in range(o)])[:, inv]
     assert rel_fro(host(out["Q"]), Q) <= 1e-5
     assert rel_fro(Rg, ref["R_perm"]) <= 1e-5
+
+
+# ----------------------------------------------------------------------------- input drift
+@pytest.mark.parametrize("n,d,dt", [(10000, 256, "bf16"), (3000, 320, "f32")])
+def test_cross_accum(n, d, dt):
+    torch, dev = torch_dev()
+    rng = np.random.default_rng(n + d)
+    A = (rng.standard_normal((n, d)) * np.exp(rng.standard_normal(d))).astype(f32)
+    B = (A + 0.1 * rng.standard_normal((n, d))).astype(f32)
+    if dt == "bf16":
+        A, B = synth.bf16_round(A), synth.bf16_round(B)
+        Ad, Bd = to_dev(synth.f32_to_bf16_bits(A), "bf16"), to_dev(synth.f32_to_bf16_bits(B), "bf16")
+    else:
+        Ad, Bd = to_dev(A), to_dev(B)
+    C = to_dev(np.eye(d), "f64")
+    K.kq_cross_accum(Ad, Bd, C, 1.0 / n, 0.5, ws_tensor(K.kq_workspace_bytes("cross", 0, d, n)))
+    ref = A.astype(np.float64).T @ B.astype(np.float64) / n + 0.5 * np.eye(d)
+    assert rel_fro(host(C), ref) <= 1e-12
+
+
+def test_drift_target():
+    torch, dev = torch_dev()
+    rng = np.random.default_rng(5)
+    o, i, n = 96, 384, 2000
+    X = rng.standard_normal((n, i)) * np.exp(rng.standard_normal(i))
+    Xt = X + 0.05 * rng.standard_normal((n, i))
+    W = (rng.standard_normal((o, i)) * 0.02).astype(f32)
+    dr = kq.drift_target(W, X, Xt)
+    H, lam = kq.damped(dr["H"])
+    R = kq.inverse_upper_factor(H).astype(f32)
+    ref = W.astype(np.float64) @ dr["C"] @ (R.astype(np.float64).T @ R.astype(np.float64))
+    Wt = torch.empty((o, i), dtype=torch.float32, device=dev)
+    K.kq_drift_target(to_dev(W), to_dev(dr["C"], "f64"), to_dev(R), Wt, ws_tensor(K.kq_workspace_bytes("drift", o, i)))
+    assert rel_fro(host(Wt), ref) <= 1e-7
+    assert rel_fro(host(Wt), dr["W"]) <= 1e-4     # R rounded to fp32 on both sides of the first check
+
+
+@pytest.mark.parametrize("bits,group", [(3, 128), (2, 0)])
+def test_layer_drift(bits, group):
+    """The layer with drifted inputs: target W* and H~ from the GPU against the oracle, codes on the
+    sweep's input with near-tie replays, w^ in rotated coordinates."""
+    from post_quantization_03_amd.layer import LayerCfg, quantize_layer
+    torch, dev = torch_dev()
+    o, i = 64, 512
+    say(f"drift o={o} i={i} b={bits} g={group}")
+    sp = synth.scaled(synth.CONFIGS["C2"], o=o, i=i, n=4 * i, hg_ng=2 * o, n_outliers=2)
+    d = synth.layer_inputs(sp)
+    Xt = synth.gen_X_drift(sp)
+    cfg = LayerCfg(bits=bits, group=group, form="full")
+    out = quantize_layer(to_dev(d["X"], "bf16"), to_dev(d["W"], "bf16"), to_dev(d["HG"]), to_dev(d["s"], "i8"),
+                         to_dev(d["t"], "i8"), cfg, X_drift=to_dev(Xt, "bf16"))
+    assert host(out["info"]).tolist() == [0, 0]
+    ref = kq.quantize_layer(synth.widen(d["X"], "bf16"), synth.widen(d["W"], "bf16"), d["HG"].astype(np.float64),
+                            "full", d["s"], d["t"], bits, group, verify=False, Xt=synth.widen(Xt, "bf16"))
+    assert rel_fro(host(out["H"]), ref["HX2"]) <= hx_tol(sp.n)
+    words = host(out["codes"])
+    gc = gpu_words_to_codes(words, bits, i)
+    Rg = host(out["R"]).astype(np.float64)
+    cmp = replay_compare(gc, ref["W2"], Rg, bits, group, 128)
+    say(f"  replays={cmp['replays']} fail={cmp['fail'][:3]}")
+    assert not cmp["fail"]
+    Q = np.stack([cmp["Q"][k] for k in range(o)])
+    assert rel_fro(host(out["Q"]), Q) <= 1e-4

@@ -560,6 +560,27 @@ def test_p16_trace_order():
     assert np.allclose(np.einsum("ri,ij,rj->r", dW, H2, dW), c["row_loss"], rtol=1e-9)
 
 
+# ----------------------------------------------------------------------------- P17
+def test_p17_drift_target():
+    """Input-drift target: no drift and no damping gives W back; without damping the residual
+    splits exactly (W* is the least-squares fit of W X^T from X~); with damping the ridge gradient
+    vanishes at W*. Parity of GPTAQ's own column-wise formula is unpinned (not on the pages)."""
+    rng = np.random.default_rng(17)
+    n, i, o = 300, 24, 7
+    X = rng.standard_normal((n, i)) * np.exp(rng.standard_normal(i))
+    Xt = X + 0.1 * rng.standard_normal((n, i))
+    W = rng.standard_normal((o, i))
+    assert np.allclose(kq.drift_target(W, X, X, damp=0.0)["W"], W, atol=1e-10)
+    Ws = kq.drift_target(W, X, Xt, damp=0.0)["W"]
+    V = W + rng.standard_normal((o, i))
+    lhs = np.sum((V @ Xt.T - W @ X.T) ** 2)
+    rhs = np.sum(((V - Ws) @ Xt.T) ** 2) + np.sum((Ws @ Xt.T - W @ X.T) ** 2)
+    assert np.isclose(lhs, rhs, rtol=1e-10)
+    d = kq.drift_target(W, X, Xt, damp=0.05)
+    grad = (d["W"] @ Xt.T - W @ X.T) @ Xt + n * d["lam"] * d["W"]
+    assert np.abs(grad).max() <= 1e-9 * np.abs(W @ X.T @ Xt).max()
+
+
 def test_golden_regression_small_layer():
     """Stored oracle outputs of the small 256x256 workload (written by tests/golden/make_golden.py,
     which calls only the oracle) guard the oracle against accidental change."""
