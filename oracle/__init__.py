@@ -16,10 +16,13 @@ PTQ page used for identities) that it follows:
 * "A Unified Hessian-Guided Framework for Post-Training Quantization" (hub.valency.io),
   sections Background (quantization scales, transformations), Modeling the Hessian
   matrices (Table 1), and the appendix on the quantization loss decomposition.
+* The H_Z-PTQ page's "Weight scales and rounding" section and experimental settings
+  (the Hessian-aware scale search and the trace-sorted block order).
 
 Parity unpinned: the choice of principal square root for non-diagonal H_G (a
 reading; any factor S with S^T S = H_G gives the same loss reduction), the
-bit-allocation rule (a reading of "upgrade ordering"), and GPTAQ's drift term
-(not on the pages; the solver here is the X~ = X case).
+bit-allocation rule (a reading of "upgrade ordering"), and GPTAQ's own column-wise
+drift update (not on the pages; ``kronq.drift_target`` is a least-squares reading of
+the drift correction, pinned to that reading's algebra, not to GPTAQ).
 """
 from . import hadamard, kronq, alloc  # noqa: F401
