@@ -311,7 +311,7 @@ static int64_t dq_slice(int64_t o, int64_t i, int NT) {
     return kc;
 }
 
-size_t dequant_ws(int64_t o, int64_t i, int64_t nt) {
+static size_t dequant_ws_valu(int64_t o, int64_t i, int64_t nt) {
     int64_t ks = 1;
     for (int NT = 1; NT <= 8; NT *= 2) {
         if (NT > 1 && NT / 2 >= nt) break;
@@ -349,6 +349,373 @@ static kq_status dq_dispatch(int NT, dim3 grid, size_t smem, hipStream_t st, con
     return check_launch("dequant_gemv");
 }
 
+// ----------------------------------------------------------------------- matrix-core variant
+// The same product on the int8 matrix cores (v_mfma_i32_16x16x64_i8), for groups that are a multiple
+// of 128 columns (or one group per row). Codes are exact int8 operands; each token's x' is scaled
+// by a power of two so that |x'| < 2^22 and split into three balanced base-256 digits (int8 limbs,
+// 22 bits, about fp32's precision), so every partial product is exact and the int32 sums are
+// exact; the three limb sums are recombined in fp32 once per group and scaled by the group's s,
+// while mu multiplies the group's float sums of x'. One instruction covers 16 rows x 64 codes x 16
+// tokens, so 1 to 16 tokens cost the same.
+//
+// Layout. A row's 128-code window is split among the four lane groups g of the operand layout:
+// group g owns codes 32 g .. 32 g + 31 (exactly `B` words, loaded by one lane), and instruction j
+// (0, 1) of the window takes codes 16 j .. 16 j + 15 of each group's chunk. The 16 codes sit in the
+// A operand's 16 bytes in an order chosen per width so that unpacking is a few masks (slot()), and
+// the staged limbs of x' use the same byte order, so the instruction pairs every code with its own
+// column (the instruction sums A(lane i + 16 g)[b] * B(lane j + 16 g)[b] over g and b).
+typedef int dm_v4i __attribute__((ext_vector_type(4)));
+
+constexpr int DM_T = 16;            // tokens per pass
+constexpr int DM_NW = 8;            // 128-column windows per slice (slices of at most 1024 columns)
+constexpr int DM_ROWS = 64;         // rows per row block (4 wavefronts x 16)
+
+// byte slot (4 * register + byte) of code c (0..15) of an instruction's 16 codes
+template <int B>
+__device__ __forceinline__ int dm_slot(int c) {
+    if constexpr (B == 2) return 4 * (c & 3) + (c >> 2);
+    else if constexpr (B == 4) return 4 * (2 * (c >> 3) + (c & 1)) + ((c & 7) >> 1);
+    else return c;
+}
+
+// the code held in byte slot s (the inverse of dm_slot)
+template <int B>
+__device__ __forceinline__ int dm_code(int s) {
+    if constexpr (B == 2) return 4 * (s & 3) + (s >> 2);
+    else if constexpr (B == 4) return 8 * ((s >> 2) >> 1) + 2 * (s & 3) + ((s >> 2) & 1);
+    else return s;
+}
+
+// A operand of instruction j from the lane's `B` words (codes 16 j .. 16 j + 15 of its chunk)
+template <int B>
+__device__ __forceinline__ dm_v4i dm_unpack(const uint32_t (&w)[B], int j) {
+    dm_v4i a;
+    if constexpr (B == 2) {
+        const uint32_t x = w[j];
+        a[0] = (int)(x & 0x03030303u);
+        a[1] = (int)((x >> 2) & 0x03030303u);
+        a[2] = (int)((x >> 4) & 0x03030303u);
+        a[3] = (int)((x >> 6) & 0x03030303u);
+    } else if constexpr (B == 4) {
+        const uint32_t x0 = w[2 * j], x1 = w[2 * j + 1];
+        a[0] = (int)(x0 & 0x0F0F0F0Fu);
+        a[1] = (int)((x0 >> 4) & 0x0F0F0F0Fu);
+        a[2] = (int)(x1 & 0x0F0F0F0Fu);
+        a[3] = (int)((x1 >> 4) & 0x0F0F0F0Fu);
+    } else if constexpr (B == 8) {
+#pragma unroll
+        for (int r = 0; r < 4; r++) a[r] = (int)(w[4 * j + r] ^ 0x80808080u);   // q - 128 as int8
+    } else {
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+            uint32_t v = 0;
+#pragma unroll
+            for (int b = 0; b < 4; b++) {
+                const int bit = (16 * j + 4 * r + b) * B, wi = bit >> 5, sh = bit & 31;
+                uint32_t q = (sh + B > 32) ? __builtin_amdgcn_alignbit(w[wi + 1], w[wi], sh) : (w[wi] >> sh);
+                v |= (q & ((1u << B) - 1u)) << (8 * b);
+            }
+            a[r] = (int)v;
+        }
+    }
+    return a;
+}
+
+template <int B, int NTS, int RB>
+__global__ __launch_bounds__(256) void dequant_mfma_kernel(const uint32_t* __restrict__ codes, const float* __restrict__ scale,
+                                                           const float* __restrict__ offset, int64_t o, int64_t i,
+                                                           int64_t G, int64_t KC, const float* __restrict__ X,
+                                                           int64_t ldx, int nt, float* __restrict__ Z, int64_t zsr,
+                                                           int64_t zst, int64_t zslice) {
+    extern __shared__ __align__(16) unsigned char dm_sm[];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t col0 = (int64_t)blockIdx.x * KC;
+    const int kc = (int)((i - col0) < KC ? (i - col0) : KC);    // multiple of 128
+    const int nwin = kc >> 7, nch = kc >> 5, cpt = (int)(KC >> 5);
+    unsigned char* limbs = dm_sm;                                              // [KC/128][4][2][3][NTS][16]
+    unsigned char* zero16 = dm_sm + (size_t)KC * 3 * NTS;                      // 16 zero bytes
+    float* ps = reinterpret_cast<float*>(zero16 + 16);                         // [NTS][KC/32] chunk sums
+    float* tinv = ps + (size_t)NTS * cpt;                                      // [NTS] 2^-e_t
+    unsigned int* tmax = reinterpret_cast<unsigned int*>(tinv + NTS);          // [NTS] max |x'| bits
+
+    // the wavefront's codes (every window of the slice) and its first group's grid parameters are
+    // requested before the staging, so their latency overlaps it
+    const int64_t ng = i / G;
+    const int64_t wpr = i * B / 32;
+    const int tl = lane & 15, lg = lane >> 4;                 // token (output column) / lane group
+    const int64_t rw0 = ((int64_t)blockIdx.y * 4 + wave) * (16 * RB);
+    const bool wlive = rw0 < o;
+    const uint32_t* cb[RB];
+#pragma unroll
+    for (int k = 0; k < RB; k++) {
+        const int64_t r = rw0 + 16 * k + tl;
+        cb[k] = codes + (r < o ? r : o - 1) * wpr + ((col0 >> 5) + lg) * B;
+    }
+    uint32_t wall[DM_NW][RB][B];
+#pragma unroll
+    for (int W = 0; W < DM_NW; W++)
+#pragma unroll
+        for (int k = 0; k < RB; k++)
+#pragma unroll
+            for (int q = 0; q < B; q++)
+                wall[W][k][q] = (wlive && W < nwin) ? __builtin_nontemporal_load(cb[k] + W * 4 * B + q) : 0u;
+    int64_t prow[RB][4];
+#pragma unroll
+    for (int k = 0; k < RB; k++)
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+            const int64_t row = rw0 + 16 * k + 4 * lg + r;
+            prow[k][r] = (row < o ? row : o - 1) * ng;
+        }
+    float svn[RB][4], mvn[RB][4];
+    {
+        const int64_t g0 = col0 / G;
+#pragma unroll
+        for (int k = 0; k < RB; k++)
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                svn[k][r] = scale[prow[k][r] + g0];
+                mvn[k][r] = offset[prow[k][r] + g0];
+            }
+    }
+
+    // stage x' over (token, 32-column chunk) pairs, at most two per thread, kept in registers: chunk
+    // sums and each token's max |x'| (an integer max of non-negative float bits, order-free), then
+    // the int8 limbs, each (instruction, limb) fragment of 16 bytes assembled and stored at once
+    if (tid < NTS) tmax[tid] = 0u;
+    if (tid < 4) reinterpret_cast<uint32_t*>(zero16)[tid] = 0u;
+    __syncthreads();
+    float v[2][32];
+#pragma unroll
+    for (int pp = 0; pp < 2; pp++) {
+        const int p = tid + 256 * pp;
+        const int t = p / nch, ch = p - t * nch;
+        float sacc = 0.0f, mx = 0.0f;
+        const bool on = p < NTS * nch && t < nt;
+        const float* xr = X + (int64_t)(on ? t : 0) * ldx + col0 + 32 * (on ? ch : 0);
+#pragma unroll
+        for (int q = 0; q < 8; q++) {
+            const float4 x4 = on ? *reinterpret_cast<const float4*>(xr + 4 * q) : make_float4(0.f, 0.f, 0.f, 0.f);
+            v[pp][4 * q] = x4.x; v[pp][4 * q + 1] = x4.y; v[pp][4 * q + 2] = x4.z; v[pp][4 * q + 3] = x4.w;
+            sacc += (x4.x + x4.y) + (x4.z + x4.w);
+            mx = fmaxf(mx, fmaxf(fmaxf(fabsf(x4.x), fabsf(x4.y)), fmaxf(fabsf(x4.z), fabsf(x4.w))));
+        }
+        if (p < NTS * nch) {
+            ps[t * cpt + ch] = sacc;
+            atomicMax(&tmax[t], __float_as_uint(mx));
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int pp = 0; pp < 2; pp++) {
+        const int p = tid + 256 * pp;
+        if (p >= NTS * nch) continue;
+        const int t = p / nch, ch = p - t * nch;
+        const int W = ch >> 2, g = ch & 3;
+        unsigned char* base0 = limbs + ((((size_t)W * 4 + g) * 2) * 3) * (NTS * 16) + t * 16;
+        const float mx = __uint_as_float(tmax[t]);
+        const int e = mx > 0.0f ? 21 - ilogbf(mx) : 0;       // |x'| 2^e < 2^22
+        if (ch == 0) tinv[t] = ldexpf(1.0f, -e);
+        const float f = ldexpf(1.0f, e);
+#pragma unroll
+        for (int j = 0; j < 2; j++) {
+            int u[16];
+#pragma unroll
+            for (int c = 0; c < 16; c++) u[c] = (int)rintf(v[pp][16 * j + c] * f);
+            unsigned char* base = base0 + (size_t)j * 3 * (NTS * 16);
+#pragma unroll
+            for (int l3 = 2; l3 >= 0; l3--) {
+                // digit l3 of every code (l3 = 2 the lowest), then remove it
+                int dg[16];
+#pragma unroll
+                for (int c = 0; c < 16; c++) {
+                    dg[c] = l3 == 0 ? u[c] : ((u[c] + 128) & 255) - 128;
+                    u[c] = (u[c] - dg[c]) >> 8;
+                }
+                uint32_t wd[4];
+#pragma unroll
+                for (int r = 0; r < 4; r++) {
+                    uint32_t x = 0;
+#pragma unroll
+                    for (int bb = 0; bb < 4; bb++) x |= ((uint32_t)dg[dm_code<B>(4 * r + bb)] & 0xFFu) << (8 * bb);
+                    wd[r] = x;
+                }
+                *reinterpret_cast<uint4*>(base + l3 * (NTS * 16)) = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+            }
+        }
+    }
+    __syncthreads();
+    if (!wlive) return;
+
+    // main loop: one read of the x' fragments per instruction serves the wavefront's RB row blocks
+    const float tinv_t = tl < NTS ? tinv[tl] : 0.0f;
+    float zf[RB][4];
+    dm_v4i acc[RB][3];
+#pragma unroll
+    for (int k = 0; k < RB; k++) {
+#pragma unroll
+        for (int r = 0; r < 4; r++) zf[k][r] = 0.0f;
+#pragma unroll
+        for (int l3 = 0; l3 < 3; l3++) acc[k][l3] = dm_v4i{0, 0, 0, 0};
+    }
+    int run0 = 0;     // first window of the open group run
+#pragma unroll
+    for (int W = 0; W < DM_NW; W++) {
+        if (W >= nwin) break;
+#pragma unroll
+        for (int j = 0; j < 2; j++) {
+            dm_v4i bv[3];
+#pragma unroll
+            for (int l3 = 0; l3 < 3; l3++) {
+                const unsigned char* src = tl < NTS
+                    ? limbs + ((((size_t)W * 4 + lg) * 2 + j) * 3 + l3) * (NTS * 16) + tl * 16 : zero16;
+                bv[l3] = *reinterpret_cast<const dm_v4i*>(src);
+            }
+#pragma unroll
+            for (int k = 0; k < RB; k++) {
+                const dm_v4i a = dm_unpack<B>(wall[W][k], j);
+#pragma unroll
+                for (int l3 = 0; l3 < 3; l3++) acc[k][l3] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, bv[l3], acc[k][l3], 0, 0, 0);
+            }
+        }
+        const int64_t cend = col0 + (int64_t)(W + 1) * 128;
+        if (cend % G == 0 || W + 1 == nwin) {
+            // close the run: windows run0 .. W of one group (its s and mu were requested ahead)
+            float gsum = 0.0f;
+            if (tl < NTS)
+                for (int ch = 4 * run0; ch < 4 * (W + 1); ch++) gsum += ps[tl * cpt + ch];
+            const bool more = W + 1 < nwin;
+            const int64_t gn = cend / G;          // the next group, if the slice goes on
+#pragma unroll
+            for (int k = 0; k < RB; k++) {
+#pragma unroll
+                for (int r = 0; r < 4; r++) {
+                    const float sv = svn[k][r], mv = mvn[k][r];
+                    if (more) {
+                        svn[k][r] = scale[prow[k][r] + gn];
+                        mvn[k][r] = offset[prow[k][r] + gn];
+                    }
+                    const float dot = fmaf((float)acc[k][0][r], 65536.0f, fmaf((float)acc[k][1][r], 256.0f, (float)acc[k][2][r]));
+                    const float mo = B == 8 ? fmaf(128.0f, sv, mv) : mv;
+                    zf[k][r] = fmaf(sv, dot * tinv_t, fmaf(mo, gsum, zf[k][r]));
+                }
+#pragma unroll
+                for (int l3 = 0; l3 < 3; l3++) acc[k][l3] = dm_v4i{0, 0, 0, 0};
+            }
+            run0 = W + 1;
+        }
+    }
+    if (tl < nt) {
+        float* zb = Z + (int64_t)blockIdx.x * zslice;
+#pragma unroll
+        for (int k = 0; k < RB; k++)
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                const int64_t row = rw0 + 16 * k + 4 * lg + r;
+                if (row < o) zb[row * zsr + tl * zst] = zf[k][r];
+            }
+    }
+}
+
+static bool dm_eligible(int64_t i, int G) { return i % 128 == 0 && G % 128 == 0; }
+
+// tokens staged per pass for nt tokens
+static int dm_nts(int64_t nt) { return nt <= 1 ? 1 : nt <= 2 ? 2 : nt <= 4 ? 4 : nt <= 8 ? 8 : 16; }
+
+static size_t dm_smem(int64_t KC, int NTS) {
+    return (size_t)KC * 3 * NTS + 16 + ((size_t)NTS * (KC / 32) + 2 * NTS) * sizeof(float);
+}
+
+// Slice width: 1024 columns (all of a slice's codes fit in a lane's registers), narrowed to 256 at
+// most while the grid has fewer than 512 workgroups; one block of 16 rows per wavefront.
+static void dm_plan(int64_t o, int64_t i, int NTS, int64_t& KC, int64_t& ks, int& RB) {
+    KC = 128 * DM_NW;
+    RB = 1;
+    (void)NTS;
+    auto wgs = [&](int64_t kc) { return ((o + 63) / 64) * ((i + kc - 1) / kc); };
+    while (wgs(KC) < 512 && KC > 256) KC /= 2;
+    ks = (i + KC - 1) / KC;
+}
+
+template <int B, int NTS>
+static void dm_launch_rb(int RB, dim3 grid, size_t smem, hipStream_t st, const uint32_t* codes, const float* scale,
+                         const float* offset, int64_t o, int64_t i, int64_t G, int64_t KC, const float* X, int64_t ldx,
+                         int nt, float* Z, int64_t zsr, int64_t zst, int64_t zslice) {
+    (void)RB;   // one block of 16 rows per wavefront (dm_plan)
+    static bool attr = false;
+    if (!attr) {
+        hipFuncSetAttribute(reinterpret_cast<const void*>(&dequant_mfma_kernel<B, NTS, 1>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, 72 * 1024);
+        attr = true;
+    }
+    hipLaunchKernelGGL((dequant_mfma_kernel<B, NTS, 1>), grid, dim3(256), smem, st, codes, scale, offset, o, i, G, KC,
+                       X, ldx, nt, Z, zsr, zst, zslice);
+}
+
+template <int B>
+static void dm_launch(int NTS, int RB, dim3 grid, size_t smem, hipStream_t st, const uint32_t* codes,
+                      const float* scale, const float* offset, int64_t o, int64_t i, int64_t G, int64_t KC,
+                      const float* X, int64_t ldx, int nt, float* Z, int64_t zsr, int64_t zst, int64_t zslice) {
+    switch (NTS) {
+        case 1: dm_launch_rb<B, 1>(RB, grid, smem, st, codes, scale, offset, o, i, G, KC, X, ldx, nt, Z, zsr, zst, zslice); break;
+        case 2: dm_launch_rb<B, 2>(RB, grid, smem, st, codes, scale, offset, o, i, G, KC, X, ldx, nt, Z, zsr, zst, zslice); break;
+        case 4: dm_launch_rb<B, 4>(RB, grid, smem, st, codes, scale, offset, o, i, G, KC, X, ldx, nt, Z, zsr, zst, zslice); break;
+        case 8: dm_launch_rb<B, 8>(RB, grid, smem, st, codes, scale, offset, o, i, G, KC, X, ldx, nt, Z, zsr, zst, zslice); break;
+        default: dm_launch_rb<B, 16>(RB, grid, smem, st, codes, scale, offset, o, i, G, KC, X, ldx, nt, Z, zsr, zst, zslice); break;
+    }
+}
+
+static kq_status dequant_mfma(const uint32_t* codes, const float* scale, const float* offset, int64_t o, int64_t i,
+                              int bits, int G, const float* X, int64_t ldx, int64_t nt, float* Zt, int64_t ldz,
+                              float* Zp, hipStream_t st) {
+    for (int64_t t0 = 0; t0 < nt; t0 += DM_T) {
+        const int cnt = (int)((nt - t0) < DM_T ? (nt - t0) : DM_T);
+        const int NTS = dm_nts(cnt);
+        int64_t KC, ks;
+        int RB;
+        dm_plan(o, i, NTS, KC, ks, RB);
+        if (ks > 1 && !Zp) return fail(KQ_EWORKSPACE, "dequant_gemv: slice workspace missing");
+        const int64_t rgroups = (o + 64LL * RB - 1) / (64LL * RB);
+        if (rgroups > 65535) return fail(KQ_ESHAPE, "dequant_gemv: too many rows");
+        const dim3 grid((unsigned)ks, (unsigned)rgroups);
+        const size_t smem = dm_smem(KC, NTS);
+        const int64_t zslice = o * DM_T;
+        float* dst = ks > 1 ? Zp : Zt + t0 * ldz;
+        const int64_t zsr = ks > 1 ? DM_T : 1, zst = ks > 1 ? 1 : ldz;
+        const float* Xp = X + t0 * ldx;
+#define KQ_DM(b) case b: dm_launch<b>(NTS, RB, grid, smem, st, codes, scale, offset, o, i, (int64_t)G, KC, Xp, ldx, cnt, dst, zsr, zst, zslice); break;
+        switch (bits) {
+            KQ_DM(2) KQ_DM(3) KQ_DM(4) KQ_DM(5) KQ_DM(6) KQ_DM(7) KQ_DM(8)
+            default: return fail(KQ_EUNSUPPORTED, "dequant_gemv: bits");
+        }
+#undef KQ_DM
+        KQ_TRY(check_launch("dequant_mfma"));
+        if (ks > 1) {
+            const int64_t n = o * cnt;
+            const unsigned b = (unsigned)((n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096);
+            hipLaunchKernelGGL(dequant_reduce_kernel, dim3(b), dim3(256), 0, st, Zp, zslice, (int)ks, o, cnt,
+                               (int64_t)DM_T, Zt + t0 * ldz, ldz);
+            KQ_TRY(check_launch("dequant_reduce"));
+        }
+    }
+    return KQ_OK;
+}
+
+// slice partials of either kernel (the larger of the two plans, so any group size fits)
+size_t dequant_ws(int64_t o, int64_t i, int64_t nt) {
+    size_t m = 0;
+    for (int NTS = 1; NTS <= 16; NTS *= 2) {
+        if (NTS > 1 && NTS / 2 >= nt) break;
+        int64_t KC, ks;
+        int RB;
+        dm_plan(o, i, NTS, KC, ks, RB);
+        const size_t mm = ks > 1 ? (size_t)ks * o * DM_T * sizeof(float) : 0;
+        m = mm > m ? mm : m;
+    }
+    const size_t v = dequant_ws_valu(o, i, nt);
+    return m > v ? m : v;
+}
+
 // Zt (nt x o, leading dimension ldz) = X Q''^T for the nt token rows of X (leading dimension ldx);
 // Zp: workspace of dequant_ws(o, i, nt) bytes (may be null when that is 0).
 kq_status dequant_gemv(const uint32_t* codes, const float* scale, const float* offset, int64_t o, int64_t i, int bits,
@@ -359,6 +726,9 @@ kq_status dequant_gemv(const uint32_t* codes, const float* scale, const float* o
     if (bits < 2 || bits > 8) return fail(KQ_EUNSUPPORTED, "dequant_gemv: bits must be in 2..8");
     if (o <= 0 || nt <= 0 || (o + DQ_ROWS_WG - 1) / DQ_ROWS_WG > 65535) return fail(KQ_ESHAPE, "dequant_gemv: bad sizes");
     if (ldx % 4 || reinterpret_cast<uintptr_t>(X) % 16) return fail(KQ_EINVAL, "dequant_gemv: x' rows must be 16-byte aligned");
+    // the matrix-core kernel for token blocks of more than 4 (measured: at 1 token the VALU kernel is
+    // about twice as fast on the C2-C4 layer shapes, at 8 tokens the matrix-core one up to 2.2x)
+    if (dm_eligible(i, G) && nt > 4) return dequant_mfma(codes, scale, offset, o, i, bits, G, X, ldx, nt, Zt, ldz, Zp, st);
     for (int64_t t0 = 0; t0 < nt; t0 += 8) {
         const int cnt = (int)((nt - t0) < 8 ? (nt - t0) : 8);
         const int NT = cnt == 1 ? 1 : cnt == 2 ? 2 : cnt <= 4 ? 4 : 8;

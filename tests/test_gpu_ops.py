@@ -348,6 +348,13 @@ def run_matvec(words, sc, mu, o, i, bits, group, s, t, Si, form, blk, X):
     ("block", 128, 2048, 8, 256, 4, 128),
     ("full", 128, 256, 4, 32, 9, 0),       # more than 8 tokens: S^{-1} through the general GEMM
     ("block", 96, 256, 3, 128, 2, 6),      # block size not a multiple of 4: general GEMM
+    ("diag", 96, 1024, 5, 128, 16, 0),     # matrix-core product: 16 tokens, generic unpacking
+    ("full", 128, 768, 6, 0, 17, 0),       # matrix-core product: two token passes, per-row grids
+    ("diag", 200, 2560, 2, 128, 6, 0),     # matrix-core product: ragged row blocks, 5 slices
+    ("diag", 64, 1024, 8, 128, 8, 0),      # matrix-core product: 8-bit codes (signed shift)
+    ("full", 64, 512, 4, 0, 12, 0),        # matrix-core product: 4-bit codes, per-row grids
+    ("diag", 48, 1536, 3, 256, 5, 0),      # matrix-core product: 3-bit codes, groups over two windows
+    ("diag", 200, 2560, 2, 128, 3, 0),     # same shape at 3 tokens: the VALU product
 ])
 def test_matvec_quantized(form, o, i, bits, group, nt, blk):
     say(f"matvec {form} o={o} i={i} bits={bits} group={group} nt={nt}")
