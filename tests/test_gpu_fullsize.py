@@ -113,31 +113,46 @@ def test_fullsize_layer(name):
     check_rows(g, r, sp, rows)
 
 
-def test_fullsize_stack():
-    """The 32-layer stack: scores of all 224 sublayers, allocation, and per-sublayer parity on sampled
-    rows of layers 0, 15 and 31."""
+def _stack_layer_inputs(li: int):
+    """Host inputs of one layer of the 32-layer stack (run in worker processes: numpy only)."""
+    specs = synth.c5_specs(li)
+    xs = {}
+    for sp in specs:
+        if sp.x_sub not in xs:
+            xs[sp.x_sub] = (synth.gen_X(sp), synth.gen_signs(sp)[0])
+    subs_h = [(sp, synth.gen_W(sp), synth.gen_HG(sp), synth.gen_signs(sp)[1]) for sp in specs]
+    return xs, subs_h
+
+
+@pytest.fixture(scope="module")
+def stack_run():
+    """The whole 32-layer stack on the GPU once for the tests below; inputs drawn by 8 worker
+    processes (the draws are per layer, so the order of the workers does not matter)."""
+    import multiprocessing as mp
+    from concurrent.futures import ProcessPoolExecutor
+
     import torch
 
     from post_quantization_03_amd.stack import Layer, Sublayer, quantize_stack
     torch_dev()
-    layers_dev, layers_host = [], []
-    for li in range(synth.C5_LAYERS):
-        specs = synth.c5_specs(li)
-        xs = {}
-        for sp in specs:
-            if sp.x_sub not in xs:
-                xs[sp.x_sub] = (synth.gen_X(sp), synth.gen_signs(sp)[0])
-        subs_h = [(sp, synth.gen_W(sp), synth.gen_HG(sp), synth.gen_signs(sp)[1]) for sp in specs]
-        layers_host.append((xs, subs_h))
+    with ProcessPoolExecutor(max_workers=8, mp_context=mp.get_context("fork")) as ex:
+        layers_host = list(ex.map(_stack_layer_inputs, range(synth.C5_LAYERS)))
+    say("  stack inputs drawn")
+    layers_dev = []
+    for xs, subs_h in layers_host:
         layers_dev.append(Layer(X=[to_dev(xs[k][0], "bf16") for k in range(4)], s=[to_dev(xs[k][1], "i8") for k in range(4)],
                                 subs=[Sublayer(W=to_dev(w, "bf16"), HG=to_dev(h), t=to_dev(tt, "i8"), x=sp.x_sub)
                                       for (sp, w, h, tt) in subs_h]))
-        if li % 8 == 7:
-            say(f"  inputs for layer {li} on device")
     out = quantize_stack(layers_dev, budget=3.0, group=128, keep_q=True, keep_h=True)
     torch.cuda.synchronize()
+    del layers_dev
+    return layers_host, out
+
+
+def test_fullsize_stack_scores_and_allocation(stack_run):
+    """The 32-layer stack: scores of all 224 sublayers against the oracle, and the allocation."""
+    layers_host, out = stack_run
     assert int(host(out.info).max()) == 0
-    # scores and allocation against the oracle
     osc, sizes = [], []
     for li, (xs, subs_h) in enumerate(layers_host):
         trx = {k: float((synth.widen(v[0], "bf16") ** 2).sum()) / synth.C5_TOKENS for k, v in xs.items()}
@@ -157,29 +172,35 @@ def test_fullsize_stack():
     if not np.array_equal(gbits, obits):
         # allowed only where two candidate upgrades are within the score tolerance of each other
         assert np.sum(gbits != obits) <= 2
-    for li in (0, 15, 31):
-        xs, subs_h = layers_host[li]
-        HX = {k: kq.hessian(synth.widen(v[0], "bf16")) for k, v in xs.items()}
-        HX2 = {k: kq.rotate_in_hessian(HX[k], xs[k][1]) for k in HX}
-        R = {k: kq.inverse_upper_factor(kq.damped(HX2[k], 0.01)[0]) for k in HX}
-        for k in HX:
-            assert rel_fro(host(out.H[li][k]), HX2[k]) <= hx_tol(synth.C5_TOKENS)
-        for j, (sp, w, h, tt) in enumerate(subs_h):
-            kk = li * 7 + j
-            b = int(gbits[kk])
-            sp = synth.scaled(sp, bits=b)
-            rows = np.sort(np.random.default_rng(kk).choice(sp.o, 8, replace=False))
-            W1 = kq.rotate_in_weights(synth.widen(w, "bf16"), xs[sp.x_sub][1])
-            SW1 = np.sqrt(h.astype(np.float64))[:, None] * W1
-            W2r = v_rows(sp.o, tt, rows) @ SW1
-            words = host(out.codes[kk])[rows]
-            cmp = replay_compare(gpu_words_to_codes(words, b, sp.i), W2r, R[sp.x_sub], b, 128, 128)
-            assert not cmp["fail"], (li, sp.name, cmp["fail"][:3])
-            oc = np.stack([cmp["codes"][q] for q in range(len(rows))])
-            assert np.array_equal(kq.pack(oc, b), words.view(np.uint32))
-            Q = np.stack([cmp["Q"][q] for q in range(len(rows))])
-            assert rel_fro(host(out.Q[kk])[rows], Q) <= 1e-4
-        say(f"  layer {li}: 7 sublayers match on sampled rows")
+
+
+@pytest.mark.parametrize("li", [0, 15, 31])
+def test_fullsize_stack_layer(stack_run, li):
+    """Per-sublayer parity of one layer of the stack on sampled rows (codes, words, Q''), and its H_X'."""
+    layers_host, out = stack_run
+    gbits = np.array(out.bits)
+    xs, subs_h = layers_host[li]
+    HX = {k: kq.hessian(synth.widen(v[0], "bf16")) for k, v in xs.items()}
+    HX2 = {k: kq.rotate_in_hessian(HX[k], xs[k][1]) for k in HX}
+    R = {k: kq.inverse_upper_factor(kq.damped(HX2[k], 0.01)[0]) for k in HX}
+    for k in HX:
+        assert rel_fro(host(out.H[li][k]), HX2[k]) <= hx_tol(synth.C5_TOKENS)
+    for j, (sp, w, h, tt) in enumerate(subs_h):
+        kk = li * 7 + j
+        b = int(gbits[kk])
+        sp = synth.scaled(sp, bits=b)
+        rows = np.sort(np.random.default_rng(kk).choice(sp.o, 8, replace=False))
+        W1 = kq.rotate_in_weights(synth.widen(w, "bf16"), xs[sp.x_sub][1])
+        SW1 = np.sqrt(h.astype(np.float64))[:, None] * W1
+        W2r = v_rows(sp.o, tt, rows) @ SW1
+        words = host(out.codes[kk])[rows]
+        cmp = replay_compare(gpu_words_to_codes(words, b, sp.i), W2r, R[sp.x_sub], b, 128, 128)
+        assert not cmp["fail"], (li, sp.name, cmp["fail"][:3])
+        oc = np.stack([cmp["codes"][q] for q in range(len(rows))])
+        assert np.array_equal(kq.pack(oc, b), words.view(np.uint32))
+        Q = np.stack([cmp["Q"][q] for q in range(len(rows))])
+        assert rel_fro(host(out.Q[kk])[rows], Q) <= 1e-4
+    say(f"  layer {li}: 7 sublayers match on sampled rows")
 
 
 @pytest.mark.parametrize("name,nt", [("C2", 1), ("C2", 8), ("C4", 1)])
