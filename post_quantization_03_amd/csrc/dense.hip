@@ -313,12 +313,26 @@ __global__ __launch_bounds__(256) void dgemm_valu_kernel(GemmArgs<double> g) {
         const int64_t nx = (g.N + BN - 1) / BN;
         const int64_t L = g.tri ? (int64_t)gridDim.x : (int64_t)gridDim.x * gridDim.y;
         int64_t lid = g.tri ? (int64_t)blockIdx.x : (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
-        if (L % 8 == 0) lid = (lid % 8) * (L / 8) + lid / 8;
+        // Work-groups go to the 8 XCDs round-robin by id: give XCD x a contiguous run of tiles
+        // (a bijection for any L; runs differ in length by at most one).
+        {
+            const int64_t x = lid % 8, q = lid / 8, base = L / 8, rem = L % 8;
+            lid = x * base + (x < rem ? x : rem) + q;
+        }
         if (g.tri) {
             int64_t r = (int64_t)((sqrt(8.0 * (double)lid + 1.0) - 1.0) * 0.5);
             while (r * (r + 1) / 2 > lid) r--;
             while ((r + 1) * (r + 2) / 2 <= lid) r++;
-            const int64_t c = lid - r * (r + 1) / 2;
+            int64_t c = lid - r * (r + 1) / 2;
+            if (g.compact) {
+                // the grid enumerates the triangle without the skipped 128-wide rows and columns
+                // (BM = BN = 128 here): map the reduced indices back, skipped indices ascending
+                const int64_t s1 = g.skip_tile, s2 = g.skip_tile2;
+                const int64_t lo = (s1 >= 0 && (s2 < 0 || s1 <= s2)) ? s1 : s2;
+                const int64_t hi = (lo == s1) ? s2 : s1;
+                if (lo >= 0) { r += r >= lo; c += c >= lo; }
+                if (hi >= 0 && hi != lo) { r += r >= hi; c += c >= hi; }
+            }
             if (g.tri == 1) { tm = r; tn = c; } else { tm = c; tn = r; }
         } else {
             tm = lid / nx;
@@ -527,9 +541,25 @@ __global__ __launch_bounds__(256) void dgemm_valu_kernel(GemmArgs<double> g) {
 }
 
 template <int BM, int BN>
-static void dgemm_launch(const GemmArgs<double>& g, bool ta, bool tb, bool vec, hipStream_t st) {
+static void dgemm_launch(const GemmArgs<double>& g0, bool ta, bool tb, bool vec, hipStream_t st) {
+    GemmArgs<double> g = g0;
     const int64_t nx = (g.N + BN - 1) / BN, ny = (g.M + BM - 1) / BM;
     int64_t gx = g.tri ? nx * (nx + 1) / 2 : nx;
+    g.compact = 0;
+    if (BM == 128 && BN == 128 && g.tri && g.focus < 0) {
+        // leave the skipped tile rows and columns out of the grid: the work-groups that would only
+        // return would otherwise count against each XCD's share of the chip
+        const int64_t s1 = g.skip_tile, s2 = g.skip_tile2;
+        const int64_t ns = (s1 >= 0 && s1 < nx) + (s2 >= 0 && s2 < nx && s2 != s1);
+        if (ns > 0) {
+            if (s1 >= nx) g.skip_tile = -1;
+            if (s2 >= nx || s2 == s1) g.skip_tile2 = -1;
+            const int64_t nr = nx - ns;
+            gx = nr * (nr + 1) / 2;
+            g.compact = 1;
+            if (gx == 0) return;
+        }
+    }
     if (g.focus >= 0) {  // tiles of the focus rows, then the focus columns below them
         const int64_t R = 128 / BM, f0 = g.focus * R, rf = ny - f0 < R ? ny - f0 : R;
         gx = 0;

@@ -574,7 +574,8 @@ __global__ __launch_bounds__(256) void gj_scatter_kernel(double* __restrict__ A,
 
 // Queues of a device for the pipelined sweep (default priority): `side` runs the pivot chain,
 // `main` the wide rank-128 updates. Events order both with the caller's stream; the mutex keeps the
-// event sequence of one call intact when several host threads enqueue at once.
+// event sequence of one call intact when several host threads enqueue at once. The events only order
+// work of the one device, so they take a device-scope release (no system-scope fence when recorded).
 struct SweepQueues {
     hipStream_t side = nullptr, main = nullptr;
     hipEvent_t ev[9] = {};
@@ -592,7 +593,7 @@ static kq_status sweep_queues(SweepQueues** out) {
             hipStreamCreateWithFlags(&q.main, hipStreamNonBlocking) != hipSuccess)
             return fail(KQ_EHIP, "sweep queues: stream creation failed");
         for (hipEvent_t& e : q.ev)
-            if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess)
+            if (hipEventCreateWithFlags(&e, hipEventDisableTiming | hipEventDisableSystemFence) != hipSuccess)
                 return fail(KQ_EHIP, "sweep queues: event creation failed");
         q.ok = true;
     }
@@ -611,15 +612,15 @@ static kq_status sweep_queues(SweepQueues** out) {
 //
 // Pipeline per pivot step k. The pivot block k + 1 depends on step k's update only through tile row
 // and column k + 1, so:
-//   caller's stream: update those tiles (tile (k + 1, k) excepted) and gather panel k + 1, taking
-//                    tile (k + 1, k) from T_k;
-//   side queue:      invert pivot k + 1, T_{k+1} = C_{k+1} Pinv_{k+1}, write T_k and -Pinv_k back into
-//                    row and column k;
-//   main queue:      the rest of step k's update A_RR -= T_k C_k^T (every tile outside rows and
-//                    columns k, k + 1), concurrently with the side queue.
-// Both queues start on the same event, so the two pivot work-groups are dispatched alongside the
-// update. The queues touch disjoint tiles and alternate the panel buffers; step k + 1 on the
-// caller's stream waits for both.
+//   main queue: update those tiles (tile (k + 1, k) excepted) and gather panel k + 1, taking tile
+//               (k + 1, k) from T_k; then the rest of step k's update A_RR -= T_k C_k^T (every tile
+//               outside rows and columns k, k + 1);
+//   side queue: invert pivot k + 1, T_{k+1} = C_{k+1} Pinv_{k+1}, write T_k and -Pinv_k back into
+//               row and column k, concurrently with the main queue's wide update.
+// The wide update starts only once the side queue has passed its wait for the gather, so the pivot
+// work-groups reach the dispatcher ahead of the update's tiles. The queues touch disjoint tiles and
+// alternate the panel buffers; step k + 1 on the main queue waits for the side queue's step k. The
+// caller's stream waits for both at the end.
 static kq_status gj_inverse_batched(double* A, int64_t n, int64_t lda, int64_t sA, int64_t batch, double* const C[2],
                                     double* const T[2], double* const Pinv[2], int32_t* info, const int* skip,
                                     hipStream_t st) {
@@ -631,8 +632,8 @@ static kq_status gj_inverse_batched(double* A, int64_t n, int64_t lda, int64_t s
     SweepQueues* q = nullptr;
     KQ_TRY(sweep_queues(&q));
     hipStream_t sb = q->side, sm = q->main;
-    hipEvent_t ev0 = q->ev[0], evG[2] = {q->ev[1], q->ev[2]}, evB[2] = {q->ev[3], q->ev[4]},
-               evM[2] = {q->ev[5], q->ev[6]}, evS[2] = {q->ev[7], q->ev[8]};
+    hipEvent_t ev0 = q->ev[0], evG[2] = {q->ev[1], q->ev[2]}, evB[2] = {q->ev[3], q->ev[4]}, evM = q->ev[5],
+               evS[2] = {q->ev[7], q->ev[8]};
     auto nb_of = [&](int64_t k) { return (int)((n - k * GJ_NB) < GJ_NB ? (n - k * GJ_NB) : GJ_NB); };
     auto gather = [&](int64_t k, hipStream_t qg) -> kq_status {
         const int b = (int)(k & 1), nbk = nb_of(k);
@@ -659,20 +660,17 @@ static kq_status gj_inverse_batched(double* A, int64_t n, int64_t lda, int64_t s
     for (int64_t k = 0; k < nt; k++) {
         const int cur = (int)(k & 1), nxt = cur ^ 1, nbk = nb_of(k);
         const int64_t k0 = k * GJ_NB;
-        // caller's stream: T_k ready (and step k - 1 written back), step k - 1's update done
-        KQ_HIP(hipStreamWaitEvent(st, evB[cur], 0));
-        if (k > 0) KQ_HIP(hipStreamWaitEvent(st, evM[nxt], 0));
+        // main queue (step k - 1's update already behind it in order): T_k ready, step k - 1 written back
+        KQ_HIP(hipStreamWaitEvent(sm, evB[cur], 0));
         if (k + 1 < nt) {
             GemmArgs<double> u = gemm_args<double>(n, n, nbk, T[cur], GJ_NB, C[cur], GJ_NB, A, lda, -1.0, 1.0);
             u.nb1 = batch; u.sA1 = sC; u.sB1 = sC; u.sC1 = sA; u.tri = 1; u.skip = skip; u.skip_tile = k;
             u.focus = k + 1;
-            KQ_TRY(gemm<double>(u, false, true, st));
-            KQ_TRY(gather(k + 1, st));
+            KQ_TRY(gemm<double>(u, false, true, sm));
+            KQ_TRY(gather(k + 1, sm));
         }
-        KQ_HIP(hipEventRecord(evG[cur], st));
-        // side queue: pivot k + 1 and the write-back of step k. The main queue starts its update only
-        // once the side queue has passed its wait (evS, recorded before the pivot launch), so the two
-        // pivot work-groups reach the dispatcher ahead of the update's tiles.
+        KQ_HIP(hipEventRecord(evG[cur], sm));
+        // side queue: pivot k + 1 and the write-back of step k; evS marks that it has passed its wait
         KQ_HIP(hipStreamWaitEvent(sb, evG[cur], 0));
         KQ_HIP(hipEventRecord(evS[cur], sb));
         if (k + 1 < nt) KQ_TRY(pivot_t(k + 1));
@@ -687,9 +685,9 @@ static kq_status gj_inverse_batched(double* A, int64_t n, int64_t lda, int64_t s
             u.skip_tile2 = k + 1 < nt ? k + 1 : -1;
             KQ_TRY(gemm<double>(u, false, true, sm));
         }
-        KQ_HIP(hipEventRecord(evM[cur], sm));
     }
-    KQ_HIP(hipStreamWaitEvent(st, evM[(nt - 1) & 1], 0));
+    KQ_HIP(hipEventRecord(evM, sm));
+    KQ_HIP(hipStreamWaitEvent(st, evM, 0));
     KQ_HIP(hipStreamWaitEvent(st, evB[nt & 1], 0));
     return KQ_OK;
 }

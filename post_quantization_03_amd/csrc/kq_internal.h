@@ -71,6 +71,7 @@ struct GemmArgs {
     int64_t skip_tile2;// a second one (-1: none)
     int64_t focus;     // fp64 lower-triangular products only: launch just the 128-wide tile row and
                        // column `focus` (-1: all tiles)
+    int compact;       // set by the fp64 launcher: the grid omits the skipped tile rows and columns
 };
 
 template <typename T>
