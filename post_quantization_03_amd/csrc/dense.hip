@@ -319,7 +319,10 @@ __global__ __launch_bounds__(256) void dgemm_valu_kernel(GemmArgs<double> g) {
             const int64_t x = lid % 8, q = lid / 8, base = L / 8, rem = L % 8;
             lid = x * base + (x < rem ? x : rem) + q;
         }
-        if (g.tri) {
+        if constexpr (BM != BN) {
+            tm = lid / nx;  // row-block tiles (own_rows): never triangular
+            tn = lid % nx;
+        } else if (g.tri) {
             int64_t r = (int64_t)((sqrt(8.0 * (double)lid + 1.0) - 1.0) * 0.5);
             while (r * (r + 1) / 2 > lid) r--;
             while ((r + 1) * (r + 2) / 2 <= lid) r++;
@@ -598,7 +601,10 @@ kq_status gemm<double>(const GemmArgs<double>& g, bool ta, bool tb, hipStream_t 
     const int64_t ty = big ? ny : (g.M + 63) / 64;
     if (!g.tri && ty > 65535) return fail(KQ_ESHAPE, "gemm grid too large");
     if (g.tri && ((g.N + 63) / 64) != ((g.M + 63) / 64)) return fail(KQ_ESHAPE, "gemm: triangular products need a square tile grid");
-    if (big) dgemm_launch<128, 128>(g, ta, tb, vec, st);
+    if (g.own_rows) {
+        if (g.tri || g.focus >= 0 || g.N > 128) return fail(KQ_EINVAL, "gemm: row-block tiles need N <= 128");
+        dgemm_launch<64, 128>(g, ta, tb, vec, st);
+    } else if (big) dgemm_launch<128, 128>(g, ta, tb, vec, st);
     else dgemm_launch<64, 64>(g, ta, tb, vec, st);
     return check_launch("dgemm");
 }
@@ -821,10 +827,11 @@ kq_status potrf_batched(T* A, int64_t lda, int64_t sA, T* X, int64_t ldx, int64_
         else
             return fail(KQ_EUNSUPPORTED, "potrf: fp64 log-determinant not supported");
         if (k1 >= n) break;
-        // panel: A[k1:, k0:k1] <- A[k1:, k0:k1] X_kk^T   (in place: one tile column per work-group row)
+        // panel: A[k1:, k0:k1] <- A[k1:, k0:k1] X_kk^T in place, so each work-group must own whole
+        // rows of the panel (it reads only the rows it writes): 128-wide column tiles
         GemmArgs<T> p = gemm_args<T>(n - k1, nbe, nbe, A + k1 * lda + k0, lda, X + k0 * ldx + k0, ldx,
                                      A + k1 * lda + k0, lda, T(1), T(0));
-        p.nb1 = batch; p.sA1 = sA; p.sB1 = sX; p.sC1 = sA; p.skip = skip;
+        p.nb1 = batch; p.sA1 = sA; p.sB1 = sX; p.sC1 = sA; p.skip = skip; p.own_rows = 1;
         KQ_TRY(gemm<T>(p, false, true, st));
         // trailing: A[k1:, k1:] -= P P^T (lower triangle)
         GemmArgs<T> u = gemm_args<T>(n - k1, n - k1, nbe, A + k1 * lda + k0, lda, A + k1 * lda + k0, lda,

@@ -72,6 +72,8 @@ struct GemmArgs {
     int64_t focus;     // fp64 lower-triangular products only: launch just the 128-wide tile row and
                        // column `focus` (-1: all tiles)
     int compact;       // set by the fp64 launcher: the grid omits the skipped tile rows and columns
+    int own_rows;      // fp64, N <= 128: one work-group per block of C rows, so that C may overwrite A
+                       // (every work-group reads only the rows of A that it writes)
 };
 
 template <typename T>

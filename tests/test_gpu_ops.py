@@ -163,6 +163,36 @@ def test_cholinv(i):
     assert err <= 1e-6
 
 
+def test_cholinv_concurrent_with_hg_sqrt():
+    """The damped factor computed while the H_G square root runs on another stream equals the serial
+    result bit for bit (every work-group of the in-place panel product owns whole rows: with two
+    column tiles per row block, a late tile read what its neighbour had already overwritten)."""
+    torch, dev = torch_dev()
+    i, o = 2048, 2048
+    say(f"cholinv i={i} concurrent with hg_sqrt o={o}")
+    sp = synth.scaled(synth.CONFIGS["C2"], n=2 * i, i=i, o=o, hg_ng=2 * o, n_outliers=4)
+    Hd = to_dev(kq.hessian(synth.widen(synth.gen_X(sp), "bf16")), "f64")
+    HG = to_dev(synth.gen_HG(sp))
+    ws = ws_tensor(K.kq_workspace_bytes("cholinv", 0, i))
+    ws_s = ws_tensor(K.kq_workspace_bytes("hg_sqrt", o, 0, 0, form="full"))
+    S = torch.empty((o, o), dtype=torch.float32, device=dev)
+    R0 = torch.empty((i, i), dtype=torch.float32, device=dev)
+    info = torch.zeros(4, dtype=torch.int32, device=dev)
+    K.kq_cholinv(Hd, 0.01, R0, info[0:1], ws)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream(device=dev)
+    for rep in range(3):
+        R = torch.empty_like(R0)
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            K.kq_hg_sqrt(HG, "full", o, 0, S, None, info[1:2], ws_s)
+        K.kq_cholinv(Hd, 0.01, R, info[2:3], ws)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        assert host(info).tolist()[:3] == [0, 0, 0]
+        assert torch.equal(R, R0), f"repeat {rep}"
+
+
 def test_cholinv_reports_not_positive_definite():
     torch, dev = torch_dev()
     i = 256
