@@ -4,11 +4,13 @@ Order of the calls (KronQ review page, Method and Key idea):
   kq_hessian_accum  H_X = X^T X / n
   kq_sensitivity    tr(H_G) tr(H_X)         (before the rotation: undamped, unrotated H_X)
   kq_rotate_in      W' = W U, H_X' = U^T H_X U
-  kq_hg_sqrt        S = H_G^{1/2}, S^{-1}    (skipped when a cached S is passed)
-  kq_rotate_out     W'' = V S W'
   kq_cholinv        R with (H_X' + lambda I)^{-1} = R^T R
+  kq_hg_sqrt        S = H_G^{1/2}, S^{-1}    (skipped when a cached S is passed; for block and full H_G
+                                             on a second stream, concurrent with the four calls above,
+                                             which do not depend on it)
+  kq_rotate_out     W'' = V S W'
   kq_quantize_layer GPTQ sweep on W'' -> codes, scale, offset, w^ (rotated), row loss
-Torch only allocates device memory and supplies the stream.
+Torch only allocates device memory and supplies the streams.
 """
 from __future__ import annotations
 
@@ -29,6 +31,18 @@ class LayerCfg:
     blk: int = 0            # block size of a block-diagonal H_G
     search: int = 0         # candidates of the Hessian-aware grid search (0: min-max grids)
     order: str = "natural"  # "natural" or "trace": 128-column blocks in descending trace of H_X'
+
+
+_SIDE: dict = {}
+
+
+def _side_stream(dev):
+    """One second stream per device (default priority) for the H_G square root."""
+    import torch
+    key = dev.index if dev.index is not None else torch.cuda.current_device()
+    if key not in _SIDE:
+        _SIDE[key] = torch.cuda.Stream(device=dev)
+    return _SIDE[key]
 
 
 def workspace_bytes(o: int, i: int, n: int, xdt: int, cfg: LayerCfg, verify: bool = False) -> int:
@@ -58,6 +72,26 @@ def quantize_layer(X: torch.Tensor, W: torch.Tensor, HG: torch.Tensor, s: torch.
         ws = torch.empty(max(workspace_bytes(o, i, n if x_batch is None else min(n, x_batch), xdt, cfg, verify), 256),
                          dtype=torch.uint8, device=dev)
     f32 = dict(dtype=torch.float32, device=dev)
+    info = torch.zeros((2,), dtype=torch.int32, device=dev)
+    join = None
+    if S_cached is None:
+        S = torch.empty(hg_factor_shape(o, cfg), **f32)
+        Sinv = torch.empty_like(S) if verify else None
+        if cfg.form != "diag":
+            # S depends on H_G alone: start it on the second stream, join before kq_rotate_out
+            main = torch.cuda.current_stream(dev)
+            side = _side_stream(dev)
+            side.wait_stream(main)
+            with torch.cuda.stream(side):
+                ws_s = torch.empty(max(K.kq_workspace_bytes("hg_sqrt", o, 0, form=cfg.form, blk=cfg.blk), 256),
+                                   dtype=torch.uint8, device=dev)
+                K.kq_hg_sqrt(HG, cfg.form, o, cfg.blk, S, Sinv, info[0:1], ws_s)
+            for t_ in (S, Sinv, info, HG):
+                if t_ is not None:
+                    t_.record_stream(side)
+            join = side
+    else:
+        S, Sinv = S_cached
     H = torch.empty((i, i), dtype=torch.float64, device=dev)
     Xh = X if X_drift is None else X_drift
     if x_batch is None or x_batch >= n:
@@ -81,13 +115,13 @@ def quantize_layer(X: torch.Tensor, W: torch.Tensor, HG: torch.Tensor, s: torch.
     K.kq_sensitivity(H, HG, cfg.form, o, cfg.blk, score)
     W2 = torch.empty((o, i), **f32)
     K.kq_rotate_in(W, W2, H, s, ws)
-    info = torch.zeros((2,), dtype=torch.int32, device=dev)
-    if S_cached is None:
-        S = torch.empty(hg_factor_shape(o, cfg), **f32)
-        Sinv = torch.empty_like(S) if verify else None
+    R = torch.empty((i, i), **f32)
+    if cfg.order != "trace":
+        K.kq_cholinv(H, cfg.damp, R, info[1:2], ws)
+    if join is not None:
+        torch.cuda.current_stream(dev).wait_stream(join)
+    elif S_cached is None:
         K.kq_hg_sqrt(HG, cfg.form, o, cfg.blk, S, Sinv, info[0:1], ws)
-    else:
-        S, Sinv = S_cached
     K.kq_rotate_out(W2, S, cfg.form, cfg.blk, t, ws)
     W2_in = W2.clone() if verify else None
     ng = i // cfg.group if cfg.group else 1
@@ -95,7 +129,6 @@ def quantize_layer(X: torch.Tensor, W: torch.Tensor, HG: torch.Tensor, s: torch.
     scale = torch.empty((o, ng), **f32)
     offset = torch.empty((o, ng), **f32)
     row_loss = torch.empty((o,), **f32)
-    R = torch.empty((i, i), **f32)
     order = None
     if cfg.order == "trace":
         # blocks in descending trace of H_X': permute W'' and H_X' forward, factor and sweep there,
@@ -122,7 +155,6 @@ def quantize_layer(X: torch.Tensor, W: torch.Tensor, HG: torch.Tensor, s: torch.
             K.kq_permute_blocks(sp_, scale, cfg.block // cfg.group, 0, back)
             K.kq_permute_blocks(op_, offset, cfg.block // cfg.group, 0, back)
     else:
-        K.kq_cholinv(H, cfg.damp, R, info[1:2], ws)
         K.kq_quantize_layer_search(W2, R, cfg.bits, cfg.group, cfg.block, cfg.search, codes, scale, offset, row_loss,
                                    ws)
     out = {"H": H, "score": score, "Q": W2, "R": R, "codes": codes, "scale": scale, "offset": offset,
