@@ -116,7 +116,10 @@ kq_status kq_rotate_in(const void* Win, kq_dtype wdt, int64_t ldwin, float* Wout
  * full (o x o). Diagonal: elementwise square root. Block and full: scaled Denman-Beavers
  * iteration in fp64 whose SPD inverses are symmetric block Gauss-Jordan sweeps, stopped on a
  * device-side convergence test (at most 7 steps; enough for cond(H_G) <= 1e16). The sweep runs on
- * two extra queues of the device, forked from and joined back into `stream`.
+ * two extra queues of the device, forked from and joined back into `stream`. The call returns
+ * only after the first step has completed on the device: it reads back that step's interval
+ * bounds (nbk doubles) and launches exactly the further steps they imply; the rest is
+ * asynchronous on `stream`. Not for graph capture.
  * Sinv may be NULL. info (device int32): 0; k in 1..o if H_G (or an iterate) is not positive
  * definite (k = 1 + index of the failing pivot); o + 1 if the iteration did not converge. The
  * caller may free HG once the work has completed in stream order (H_G is only needed

@@ -16,6 +16,7 @@
 // one batch.
 #include <cmath>
 #include <mutex>
+#include <vector>
 
 #include "kq_internal.h"
 
@@ -919,7 +920,8 @@ static kq_status db_sqrt(const float* HGf, const double* HGd, int64_t n, int64_t
                        flags, -1);
     KQ_TRY(check_launch("db_norm"));
     const unsigned cb = (unsigned)((items * nn + 255) / 256 < 4096 ? (items * nn + 255) / 256 : 4096);
-    for (int it = 0; it < DB_MAXIT; it++) {
+    int nsteps = DB_MAXIT;
+    for (int it = 0; it < nsteps; it++) {
         // the first step inverts Y_0 = A only (Z_0 = I)
         const size_t inv_items = it == 0 ? (size_t)nbk : items;
         hipLaunchKernelGGL(copy_d_kernel, dim3(cb), dim3(256), 0, st, YZ, NI, inv_items * nn, done);
@@ -937,6 +939,29 @@ static kq_status db_sqrt(const float* HGf, const double* HGd, int64_t n, int64_t
         hipLaunchKernelGGL(db_converge_kernel, dim3(1), dim3(64), 0, st, part, bnd, nbk, flags, finfo, (int64_t)items,
                            info);
         KQ_TRY(check_launch("db_converge"));
+        if (it == 0) {
+            // After the first step the interval bound of every block is known, and the later bounds
+            // follow from it in closed form (the recursion of db_scale_kernel, in the same fp64
+            // operations): read it back and launch exactly the steps the device test will need,
+            // instead of sweeps that would only skip.
+            std::vector<double> hb((size_t)nbk);
+            int hf[4] = {0, 0, 0, 0};
+            KQ_HIP(hipMemcpyAsync(hb.data(), bnd, (size_t)nbk * sizeof(double), hipMemcpyDeviceToHost, st));
+            KQ_HIP(hipMemcpyAsync(hf, flags, sizeof(hf), hipMemcpyDeviceToHost, st));
+            KQ_HIP(hipStreamSynchronize(st));
+            if (hf[0]) break;  // converged after one step, or stopped on an error (info set)
+            int need = 1;
+            for (int64_t b = 0; b < nbk; b++) {
+                double bb = hb[(size_t)b];
+                int k = 1;
+                while (bb - 1.0 >= DB_TOL && k < DB_MAXIT) {
+                    bb = 0.5 * (sqrt(bb) + 1.0 / sqrt(bb));
+                    k++;
+                }
+                need = need > k ? need : k;
+            }
+            nsteps = need;
+        }
     }
     hipLaunchKernelGGL(db_final_kernel, dim3(1), dim3(64), 0, st, flags, info, o_info + 1);
     KQ_TRY(check_launch("db_final"));

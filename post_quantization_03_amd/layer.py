@@ -6,8 +6,8 @@ Order of the calls (KronQ review page, Method and Key idea):
   kq_rotate_in      W' = W U, H_X' = U^T H_X U
   kq_cholinv        R with (H_X' + lambda I)^{-1} = R^T R
   kq_hg_sqrt        S = H_G^{1/2}, S^{-1}    (skipped when a cached S is passed; for block and full H_G
-                                             on a second stream, concurrent with the four calls above,
-                                             which do not depend on it)
+                                             on a second stream forked before the four calls above,
+                                             which do not depend on it, and run concurrently with them)
   kq_rotate_out     W'' = V S W'
   kq_quantize_layer GPTQ sweep on W'' -> codes, scale, offset, w^ (rotated), row loss
 Torch only allocates device memory and supplies the streams.
@@ -78,18 +78,11 @@ def quantize_layer(X: torch.Tensor, W: torch.Tensor, HG: torch.Tensor, s: torch.
         S = torch.empty(hg_factor_shape(o, cfg), **f32)
         Sinv = torch.empty_like(S) if verify else None
         if cfg.form != "diag":
-            # S depends on H_G alone: start it on the second stream, join before kq_rotate_out
-            main = torch.cuda.current_stream(dev)
-            side = _side_stream(dev)
-            side.wait_stream(main)
-            with torch.cuda.stream(side):
-                ws_s = torch.empty(max(K.kq_workspace_bytes("hg_sqrt", o, 0, form=cfg.form, blk=cfg.blk), 256),
-                                   dtype=torch.uint8, device=dev)
-                K.kq_hg_sqrt(HG, cfg.form, o, cfg.blk, S, Sinv, info[0:1], ws_s)
-            for t_ in (S, Sinv, info, HG):
-                if t_ is not None:
-                    t_.record_stream(side)
-            join = side
+            # S depends on H_G alone: it runs on the second stream, forked here (after the inputs and
+            # outputs above exist) and joined before kq_rotate_out. It is enqueued after the H_X
+            # chain, since kq_hg_sqrt returns only once its first step has run on the device.
+            join = _side_stream(dev)
+            join.wait_stream(torch.cuda.current_stream(dev))
     else:
         S, Sinv = S_cached
     H = torch.empty((i, i), dtype=torch.float64, device=dev)
@@ -119,6 +112,13 @@ def quantize_layer(X: torch.Tensor, W: torch.Tensor, HG: torch.Tensor, s: torch.
     if cfg.order != "trace":
         K.kq_cholinv(H, cfg.damp, R, info[1:2], ws)
     if join is not None:
+        with torch.cuda.stream(join):
+            ws_s = torch.empty(max(K.kq_workspace_bytes("hg_sqrt", o, 0, form=cfg.form, blk=cfg.blk), 256),
+                               dtype=torch.uint8, device=dev)
+            K.kq_hg_sqrt(HG, cfg.form, o, cfg.blk, S, Sinv, info[0:1], ws_s)
+        for t_ in (S, Sinv, info, HG):
+            if t_ is not None:
+                t_.record_stream(join)
         torch.cuda.current_stream(dev).wait_stream(join)
     elif S_cached is None:
         K.kq_hg_sqrt(HG, cfg.form, o, cfg.blk, S, Sinv, info[0:1], ws)
