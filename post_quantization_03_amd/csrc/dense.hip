@@ -342,6 +342,10 @@ __global__ __launch_bounds__(256) void dgemm_valu_kernel(GemmArgs<double> g) {
             tn = lid % nx;
         }
     }
+    // the tile indices are uniform over the work-group: keep them (and what derives from them) in
+    // scalar registers, which leaves the vector registers to the accumulators and operands
+    tm = (int64_t)__builtin_amdgcn_readfirstlane((int)tm);
+    tn = (int64_t)__builtin_amdgcn_readfirstlane((int)tn);
     const int64_t m0 = tm * BM, n0 = tn * BN;
     if (g.skip_tile >= 0 && ((m0 >> 7) == g.skip_tile || (n0 >> 7) == g.skip_tile)) return;
     if (g.skip_tile2 >= 0 && ((m0 >> 7) == g.skip_tile2 || (n0 >> 7) == g.skip_tile2)) return;
