@@ -16,6 +16,7 @@
 // one batch.
 #include <cmath>
 #include <mutex>
+#include <utility>
 #include <vector>
 
 #include "kq_internal.h"
@@ -94,6 +95,28 @@ __device__ inline double recip64(double p) {
     double r = __builtin_amdgcn_rcp(p);
     r = fma(r, fma(-p, r, 1.0), r);
     return fma(r, fma(-p, r, 1.0), r);
+}
+
+// Tm = (A_RJ - E_RJ) D^{-1} for a thread's four rows R = 4tr..4tr+3 in the register sweeps below. The 16
+// lanes of a DPP row share tr: lane tc forms the element (rr, q) = (tc & 3, tc >> 2) from the shifted
+// pivot rows (A_R. - E_R. = A_.R - E_.R by symmetry) and column q of D^{-1}, and a row broadcast hands
+// every lane all sixteen (Tm[rr][q] sits in lane 4q + rr). Same sums, in the same order, as each
+// thread forming all sixteen itself, for a quarter of the LDS reads and FMAs.
+template <int L>
+__device__ __forceinline__ double row_lane(double v) {
+    return __builtin_amdgcn_mov_dpp(v, 0x150 + L, 0xF, 0xF, false);
+}
+template <int... L>
+__device__ __forceinline__ void tm_gather(double v, double (&Tm)[4][4], std::integer_sequence<int, L...>) {
+    ((Tm[L & 3][L >> 2] = row_lane<L>(v)), ...);
+}
+__device__ __forceinline__ void pivot_tm(const double (*rowb)[GJ_NB], const double (*dinv)[4], int tr, int tc,
+                                         double (&Tm)[4][4]) {
+    const int rr = tc & 3, qq = tc >> 2;
+    double t = 0.0;
+#pragma unroll
+    for (int q2 = 0; q2 < 4; q2++) t = fma(rowb[q2][4 * tr + rr], dinv[q2][qq], t);
+    tm_gather(t, Tm, std::make_integer_sequence<int, 16>{});
 }
 
 // Pinv = P^{-1} for the nbk x nbk SPD pivot P = C[k0 : k0 + nbk][0 : nbk] (identity-padded to 128) by
@@ -203,26 +226,8 @@ __global__ __launch_bounds__(GJ_PIV_THREADS) void gj_pivot_kernel(const double* 
     __syncthreads();
     for (int jb = 0; jb < 32; jb++) {
         const int buf = jb & 1;
-        double Di[4][4];
-#pragma unroll
-        for (int q = 0; q < 4; q++)
-#pragma unroll
-            for (int q2 = 0; q2 < 4; q2++) Di[q][q2] = dinv[buf][q][q2];
-        // Tm = (A_RJ - E_RJ) D^{-1}, A_RJ read from the pivot rows (symmetry)
         double Tm[4][4];
-#pragma unroll
-        for (int rr = 0; rr < 4; rr++) {
-            double cv[4];
-#pragma unroll
-            for (int q = 0; q < 4; q++) cv[q] = rowb[buf][q][4 * tr + rr];
-#pragma unroll
-            for (int q = 0; q < 4; q++) {
-                double t = 0.0;
-#pragma unroll
-                for (int q2 = 0; q2 < 4; q2++) t = fma(cv[q2], Di[q2][q], t);
-                Tm[rr][q] = t;
-            }
-        }
+        pivot_tm(rowb[buf], dinv[buf], tr, tc, Tm);
 #pragma unroll
         for (int q = 0; q < 4; q++) {
             double rv[8];
@@ -377,25 +382,8 @@ __global__ __launch_bounds__(GJ_PIV_THREADS) void chol_sweep128_kernel(const dou
     for (int jb = 0; jb < 32; jb++) {
         const int buf = jb & 1;
         pre[jb * 4 * GJ_NB + tid] = (&rowb[buf][0][0])[tid];  // 512 = 4 x 128 values, one per thread
-        double Di[4][4];
-#pragma unroll
-        for (int q = 0; q < 4; q++)
-#pragma unroll
-            for (int q2 = 0; q2 < 4; q2++) Di[q][q2] = dinv[buf][q][q2];
         double Tm[4][4];
-#pragma unroll
-        for (int rr = 0; rr < 4; rr++) {
-            double cv[4];
-#pragma unroll
-            for (int q = 0; q < 4; q++) cv[q] = rowb[buf][q][4 * tr + rr];
-#pragma unroll
-            for (int q = 0; q < 4; q++) {
-                double t = 0.0;
-#pragma unroll
-                for (int q2 = 0; q2 < 4; q2++) t = fma(cv[q2], Di[q2][q], t);
-                Tm[rr][q] = t;
-            }
-        }
+        pivot_tm(rowb[buf], dinv[buf], tr, tc, Tm);
 #pragma unroll
         for (int q = 0; q < 4; q++) {
             double rv[8];
