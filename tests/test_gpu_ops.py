@@ -109,6 +109,33 @@ def test_hg_sqrt(form, o, blk):
     assert rel_fro(host(Si), Si_ref) <= 1e-6
 
 
+@pytest.mark.parametrize("cond,dense", [(1e2, True), (1e6, True), (1e12, False)])
+def test_hg_sqrt_step_counts(cond, dense):
+    """Full-form H_G whose spectral bounds need 5, 6 and 7 Denman-Beavers steps (the last, a diagonal
+    matrix with cond 1e12, is exactly positive definite in fp32): the call reads the first step's
+    bounds back and launches the remaining steps itself, so each must come out converged."""
+    torch, dev = torch_dev()
+    o = 256
+    rng = np.random.default_rng(11)
+    lam = np.logspace(0.0, -np.log10(cond), o)
+    if dense:
+        Q, _ = np.linalg.qr(rng.standard_normal((o, o)))
+        hg = ((Q * lam) @ Q.T).astype(f32)
+        hg = 0.5 * (hg + hg.T)
+    else:
+        hg = np.diag(lam).astype(f32)
+    say(f"hg_sqrt cond={cond:.0e} dense={dense}")
+    S_ref, Si_ref = kq.hg_sqrt(hg.astype(np.float64), "full")
+    S = torch.empty(hg.shape, dtype=torch.float32, device=dev)
+    Si = torch.empty_like(S)
+    info = torch.zeros(1, dtype=torch.int32, device=dev)
+    ws = ws_tensor(K.kq_workspace_bytes("hg_sqrt", o, 0, 0, form="full"))
+    K.kq_hg_sqrt(to_dev(hg), "full", o, 0, S, Si, info, ws)
+    assert int(host(info)[0]) == 0
+    assert rel_fro(host(S), S_ref) <= 1e-6
+    assert rel_fro(host(Si), Si_ref) <= 1e-6
+
+
 def test_hg_sqrt_reports_not_positive_definite():
     torch, dev = torch_dev()
     for form, hg in (("full", -np.eye(128, dtype=f32)), ("diag", -np.ones(64, f32))):
