@@ -638,7 +638,7 @@ def main():
         del src, dst
     ms, ph, out, iters, mv, ms_cached = run_gpu(sp, args.steps, args.warmup, not args.no_phases)
     value = sp.o * sp.i / (ms / 1e3) / 1e6
-    roof, per_phase, s_cached = None, None, None
+    roof, per_phase, s_cached, aggregates = None, None, None, None
     if ph:
         work = algorithmic_work(sp, iters)
         per_phase = {k: roofline_of(k, work[k], ph[k]) for k in work if k in ph and
@@ -648,6 +648,18 @@ def main():
         roof["traffic"] = measured_traffic(dom) if sp.name.startswith("C2") else None
         if ms_cached:
             s_cached = round(sp.o * sp.i / (ms_cached / 1e3) / 1e6, 3)
+        # aggregates over the phases, each phase taken at its own bound: FLOP-weighted for the dense
+        # contractions (algorithmic FLOP / sum of time x peak), byte-weighted for the HBM-bound ones
+        dense = [k for k in per_phase if per_phase[k]["unit"] == "TFLOP/s"]
+        hbm = [k for k in per_phase if per_phase[k]["unit"] == "GB/s"]
+        aggregates = {
+            "dense_phases": dense,
+            "dense_frac": round(sum(work[k]["flop"] for k in dense) /
+                                sum(ph[k] / 1e3 * PEAK[work[k]["peak"]] for k in dense), 4) if dense else None,
+            "hbm_phases": hbm,
+            "hbm_frac": round(sum(work[k]["bytes"] for k in hbm) / (sum(ph[k] for k in hbm) / 1e3 * PEAK["hbm"]), 4)
+            if hbm else None,
+        }
     cpu = None if args.no_cpu_baseline else cpu_baseline(sp)
     line = {"metric": "layer-quant throughput: Mweights/s (4096x4096 W3 g128) + % MFMA/HBM peak",
             "value": round(value, 3), "unit": "Mweights/s", "n_gpus": 1, "steps": args.steps,
@@ -659,7 +671,7 @@ def main():
                                 "and the damped factor; fp32 for the rotations of W and the sweep"},
             "phases_ms": {k: round(v, 4) for k, v in ph.items()} if ph else None,
             "db_steps": iters, "s_cached_mweights_per_s": s_cached,
-            "roofline": roof, "phases_roofline": per_phase, "cpu_baseline": cpu,
+            "roofline": roof, "phases_roofline": per_phase, "phases_aggregate": aggregates, "cpu_baseline": cpu,
             "matvec_quantized": mv}
     print(json.dumps(line), flush=True)
 
