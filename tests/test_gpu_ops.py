@@ -136,6 +136,32 @@ def test_hg_sqrt_step_counts(cond, dense):
     assert rel_fro(host(Si), Si_ref) <= 1e-6
 
 
+def test_hg_sqrt_repeated_calls_identical():
+    """Repeated calls on one workspace (with eager work and host synchronisations between them) and a
+    call on a second workspace give bit-identical roots, equal to the oracle's: the result depends
+    on no state left by an earlier call (sweep queues, events, scratch)."""
+    torch, dev = torch_dev()
+    o = 384
+    hg = synth.gen_HG(synth.scaled(synth.CONFIGS["C2"], o=o, hg_ng=2 * o))
+    S_ref, _ = kq.hg_sqrt(hg.astype(np.float64), "full")
+    HG = to_dev(hg)
+    nb = K.kq_workspace_bytes("hg_sqrt", o, 0, 0, form="full")
+    ws1, ws2 = ws_tensor(nb), ws_tensor(nb)
+    info = torch.zeros(1, dtype=torch.int32, device=dev)
+    outs = []
+    for ws in (ws1, ws1, ws2, ws1):
+        S = torch.empty((o, o), dtype=torch.float32, device=dev)
+        K.kq_hg_sqrt(HG, "full", o, 0, S, None, info, ws)
+        junk = torch.randn((o, o), device=dev) @ torch.randn((o, o), device=dev)  # eager work in between
+        torch.cuda.synchronize()
+        assert int(host(info)[0]) == 0
+        outs.append(host(S).copy())
+        del junk
+    for S in outs[1:]:
+        assert np.array_equal(S, outs[0])
+    assert rel_fro(outs[0], S_ref) <= 1e-6
+
+
 def test_hg_sqrt_reports_not_positive_definite():
     torch, dev = torch_dev()
     for form, hg in (("full", -np.eye(128, dtype=f32)), ("diag", -np.ones(64, f32))):
