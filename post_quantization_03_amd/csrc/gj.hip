@@ -749,8 +749,10 @@ __global__ void db_scale_kernel(const double* nrmA, const double* nrmInv, int64_
 
 // Y <- (mu Y + Zinv / mu) / 2, Z <- (mu Z + Yinv / mu) / 2; NINV holds -inverses (lower triangles).
 // Lower triangle read, both triangles written; per-work-group partial sums of ||dY||^2 and ||Y||^2.
+// The new Y and Z also go to NINV's lower triangles (each element is read there first, by the same
+// thread), which is where the next step's sweep inverts them in place.
 constexpr int DB_UPD_BLOCKS = 1024;
-__global__ void db_update_kernel(double* YZ, const double* NINV, const double* mu, int64_t n, int64_t nbk, double* part,
+__global__ void db_update_kernel(double* YZ, double* NINV, const double* mu, int64_t n, int64_t nbk, double* part,
                                  const int* flags) {
     if (flags[0]) return;
     const bool first = flags[1] == 0;
@@ -780,6 +782,8 @@ __global__ void db_update_kernel(double* YZ, const double* NINV, const double* m
         Y[c * n + r] = yn;
         Z[r * n + c] = zn;
         Z[c * n + r] = zn;
+        NINV[b * nn + r * n + c] = yn;
+        NINV[(nbk + b) * nn + r * n + c] = zn;
     }
     sd[threadIdx.x] = acc_d;
     sn[threadIdx.x] = acc_n;
@@ -910,10 +914,13 @@ static kq_status db_sqrt(const float* HGf, const double* HGd, int64_t n, int64_t
     const unsigned cb = (unsigned)((items * nn + 255) / 256 < 4096 ? (items * nn + 255) / 256 : 4096);
     int nsteps = DB_MAXIT;
     for (int it = 0; it < nsteps; it++) {
-        // the first step inverts Y_0 = A only (Z_0 = I)
+        // the first step inverts Y_0 = A only (Z_0 = I); later steps find Y and Z in NI already
+        // (written there by the previous step's update)
         const size_t inv_items = it == 0 ? (size_t)nbk : items;
-        hipLaunchKernelGGL(copy_d_kernel, dim3(cb), dim3(256), 0, st, YZ, NI, inv_items * nn, done);
-        KQ_TRY(check_launch("db_copy"));
+        if (it == 0) {
+            hipLaunchKernelGGL(copy_d_kernel, dim3(cb), dim3(256), 0, st, YZ, NI, inv_items * nn, done);
+            KQ_TRY(check_launch("db_copy"));
+        }
         KQ_TRY(gj_inverse_batched(NI, n, n, (int64_t)nn, (int64_t)inv_items, C, T, Pinv, finfo, done, st));
         // ||A^{-1}||_F of Y_0 = A (first step only; NI holds -A^{-1})
         hipLaunchKernelGGL(sym_norm_part_kernel, dim3(NORM_PARTS, (unsigned)nbk), dim3(256), 0, st, NI, n, (int64_t)nn,
