@@ -748,9 +748,10 @@ __global__ void db_scale_kernel(const double* nrmA, const double* nrmInv, int64_
 }
 
 // Y <- (mu Y + Zinv / mu) / 2, Z <- (mu Z + Yinv / mu) / 2; NINV holds -inverses (lower triangles).
-// Lower triangle read, both triangles written; per-work-group partial sums of ||dY||^2 and ||Y||^2.
-// The new Y and Z also go to NINV's lower triangles (each element is read there first, by the same
-// thread), which is where the next step's sweep inverts them in place.
+// Lower triangles read and written (the upper ones are filled once, after the last step); per-work-
+// group partial sums of ||dY||^2 and ||Y||^2. The new Y and Z also go to NINV's lower triangles (each
+// element is read there first, by the same thread), which is where the next step's sweep inverts them
+// in place.
 constexpr int DB_UPD_BLOCKS = 1024;
 __global__ void db_update_kernel(double* YZ, double* NINV, const double* mu, int64_t n, int64_t nbk, double* part,
                                  const int* flags) {
@@ -779,9 +780,7 @@ __global__ void db_update_kernel(double* YZ, double* NINV, const double* mu, int
         acc_d += w * (yn - y) * (yn - y);
         acc_n += w * yn * yn;
         Y[r * n + c] = yn;
-        Y[c * n + r] = yn;
         Z[r * n + c] = zn;
-        Z[c * n + r] = zn;
         NINV[b * nn + r * n + c] = yn;
         NINV[(nbk + b) * nn + r * n + c] = zn;
     }
@@ -828,6 +827,26 @@ __global__ void db_out_kernel(const double* YZ, int64_t n, int64_t nbk, float* S
     for (int64_t e = blockIdx.x * 256 + threadIdx.x; e < nbk * nn; e += (int64_t)gridDim.x * 256) {
         S[e] = (float)YZ[e];
         if (Si) Si[e] = (float)YZ[nbk * nn + e];
+    }
+}
+
+// Upper triangles of `items` symmetric n x n matrices from their lower ones, through 32 x 32 LDS tiles
+// so that both the reads and the transposed writes are coalesced. Grid (tiles, tiles, items); tile
+// (I, J) with I >= J reads block (I, J) and writes its transpose into block (J, I).
+__global__ __launch_bounds__(256) void mirror_lower_batched_kernel(double* M, int64_t n) {
+    const int64_t I = blockIdx.x, J = blockIdx.y;
+    if (J > I) return;
+    __shared__ double t[32][33];
+    M += (int64_t)blockIdx.z * n * n;
+    const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+    for (int yy = ty; yy < 32; yy += 8) {
+        const int64_t r = I * 32 + yy, c = J * 32 + tx;
+        t[yy][tx] = (r < n && c < n) ? M[r * n + c] : 0.0;
+    }
+    __syncthreads();
+    for (int yy = ty; yy < 32; yy += 8) {
+        const int64_t r = J * 32 + yy, c = I * 32 + tx;  // upper element (r, c) = lower (c, r)
+        if (r < n && c < n && c > r) M[r * n + c] = t[tx][yy];
     }
 }
 
@@ -960,6 +979,12 @@ static kq_status db_sqrt(const float* HGf, const double* HGd, int64_t n, int64_t
     }
     hipLaunchKernelGGL(db_final_kernel, dim3(1), dim3(64), 0, st, flags, info, o_info + 1);
     KQ_TRY(check_launch("db_final"));
+    {
+        const unsigned tiles = (unsigned)((n + 31) / 32);
+        if (items > 65535) return fail(KQ_ESHAPE, "square root: too many blocks");
+        hipLaunchKernelGGL(mirror_lower_batched_kernel, dim3(tiles, tiles, (unsigned)items), dim3(256), 0, st, YZ, n);
+        KQ_TRY(check_launch("db_mirror"));
+    }
     *Y64 = YZ;
     return KQ_OK;
 }
