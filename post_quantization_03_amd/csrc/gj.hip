@@ -688,7 +688,7 @@ static kq_status gj_inverse_batched(double* A, int64_t n, int64_t lda, int64_t s
 // has not converged after those steps is reported through info (= o + 1).
 constexpr int DB_MAXIT = 7;
 constexpr double DB_TOL = 1e-8;
-constexpr int NORM_PARTS = 32;
+constexpr int NORM_PARTS = 512;  // at most this many partial sums per matrix (one per work-group)
 
 template <typename T>
 __global__ void db_init_kernel(const T* HG, int64_t n, int64_t nbk, double* YZ, int* flags) {
@@ -711,7 +711,7 @@ __global__ void sym_norm_part_kernel(const double* A, int64_t n, int64_t sA, dou
     const int p = blockIdx.x;
     const double* M = A + z * sA;
     double acc = 0;
-    for (int64_t r = p; r < n; r += NORM_PARTS) {
+    for (int64_t r = p; r < n; r += gridDim.x) {
         for (int64_t c = threadIdx.x; c <= r; c += 256) {
             const double v = M[r * n + c];
             acc += (c == r ? 1.0 : 2.0) * v * v;
@@ -728,13 +728,13 @@ __global__ void sym_norm_part_kernel(const double* A, int64_t n, int64_t sA, dou
 
 // Per block b: the scale mu_b of this step and the bound of the next x-interval [1, bnd_b].
 // flags[1] == 0: x in [sqrt(lo), sqrt(hi)], hi = ||A||_F, lo = 1 / ||A^{-1}||_F.
-__global__ void db_scale_kernel(const double* nrmA, const double* nrmInv, int64_t nbk, double* mu, double* bnd,
-                                const int* flags) {
+__global__ void db_scale_kernel(const double* nrmA, const double* nrmInv, int64_t nbk, int parts, double* mu,
+                                double* bnd, const int* flags) {
     if (flags[0]) return;
     for (int64_t b = blockIdx.x * 256 + threadIdx.x; b < nbk; b += (int64_t)gridDim.x * 256) {
         double sA = 0, sI = 0;
         if (flags[1] == 0) {
-            for (int p = 0; p < NORM_PARTS; p++) { sA += nrmA[b * NORM_PARTS + p]; sI += nrmInv[b * NORM_PARTS + p]; }
+            for (int p = 0; p < parts; p++) { sA += nrmA[b * NORM_PARTS + p]; sI += nrmInv[b * NORM_PARTS + p]; }
             const double hi = sqrt(sA), lo = 1.0 / sqrt(sI);
             const double r = sqrt(hi / lo);                  // x-interval ratio
             mu[b] = 1.0 / sqrt(sqrt(hi * lo));
@@ -804,9 +804,19 @@ __global__ void db_update_kernel(double* YZ, double* NINV, const double* mu, int
 // 1; a failed pivot or a non-finite value stops the iteration and is reported through info.
 __global__ void db_converge_kernel(const double* part, const double* bnd, int64_t nbk, int* flags,
                                    const int32_t* finfo, int64_t nitems, int32_t* info) {
-    if (flags[0] || threadIdx.x != 0) return;
-    double d = 0, nn = 0, bmax = 0;
-    for (int b = 0; b < DB_UPD_BLOCKS; b++) { d += part[2 * b]; nn += part[2 * b + 1]; }
+    if (flags[0]) return;
+    // the update's partial sums, strided over the 64 lanes and then added in lane order (fixed order)
+    __shared__ double sd[64], sn[64];
+    double d = 0, nn = 0;
+    for (int b = threadIdx.x; b < DB_UPD_BLOCKS; b += 64) { d += part[2 * b]; nn += part[2 * b + 1]; }
+    sd[threadIdx.x] = d;
+    sn[threadIdx.x] = nn;
+    __syncthreads();
+    if (threadIdx.x != 0) return;
+    d = 0;
+    nn = 0;
+    for (int l = 0; l < 64; l++) { d += sd[l]; nn += sn[l]; }
+    double bmax = 0;
     for (int64_t b = 0; b < nbk; b++) bmax = fmax(bmax, bnd[b] - 1.0);
     int32_t bad = 0;
     for (int64_t k = 0; k < nitems; k++)
@@ -927,7 +937,8 @@ static kq_status db_sqrt(const float* HGf, const double* HGd, int64_t n, int64_t
     if (HGd) hipLaunchKernelGGL(db_init_kernel<double>, dim3(eb), dim3(256), 0, st, HGd, n, nbk, YZ, flags);
     else hipLaunchKernelGGL(db_init_kernel<float>, dim3(eb), dim3(256), 0, st, HGf, n, nbk, YZ, flags);
     KQ_TRY(check_launch("db_init"));
-    hipLaunchKernelGGL(sym_norm_part_kernel, dim3(NORM_PARTS, (unsigned)nbk), dim3(256), 0, st, YZ, n, (int64_t)nn, nrmA,
+    const int parts = (int)(n < NORM_PARTS ? n : NORM_PARTS);  // row-strided partial sums of ||.||_F^2
+    hipLaunchKernelGGL(sym_norm_part_kernel, dim3(parts, (unsigned)nbk), dim3(256), 0, st, YZ, n, (int64_t)nn, nrmA,
                        flags, -1);
     KQ_TRY(check_launch("db_norm"));
     const unsigned cb = (unsigned)((items * nn + 255) / 256 < 4096 ? (items * nn + 255) / 256 : 4096);
@@ -942,10 +953,10 @@ static kq_status db_sqrt(const float* HGf, const double* HGd, int64_t n, int64_t
         }
         KQ_TRY(gj_inverse_batched(NI, n, n, (int64_t)nn, (int64_t)inv_items, C, T, Pinv, finfo, done, st));
         // ||A^{-1}||_F of Y_0 = A (first step only; NI holds -A^{-1})
-        hipLaunchKernelGGL(sym_norm_part_kernel, dim3(NORM_PARTS, (unsigned)nbk), dim3(256), 0, st, NI, n, (int64_t)nn,
+        hipLaunchKernelGGL(sym_norm_part_kernel, dim3(parts, (unsigned)nbk), dim3(256), 0, st, NI, n, (int64_t)nn,
                            nrmI, flags, 0);
         KQ_TRY(check_launch("db_norm_inv"));
-        hipLaunchKernelGGL(db_scale_kernel, dim3((unsigned)((nbk + 255) / 256)), dim3(256), 0, st, nrmA, nrmI, nbk, mu,
+        hipLaunchKernelGGL(db_scale_kernel, dim3((unsigned)((nbk + 255) / 256)), dim3(256), 0, st, nrmA, nrmI, nbk, parts, mu,
                            bnd, flags);
         KQ_TRY(check_launch("db_scale"));
         hipLaunchKernelGGL(db_update_kernel, dim3(DB_UPD_BLOCKS), dim3(256), 0, st, YZ, NI, mu, n, nbk, part, flags);
