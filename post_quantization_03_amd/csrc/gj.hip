@@ -307,7 +307,8 @@ __device__ inline void chol4_spd(const double D[4][4], double L[4][4], double Li
 //                       M = L^{-T} L^{-1} on the leading block and (L^{-1})_JJ = L_JJ^{-1};
 //    and undoes the scaling: L_P = S^{-1} L_A, L_P^{-1} = L_A^{-1} S.
 // Scratch per item: CHOL_SCR doubles.
-constexpr int64_t CHOL_SCR = 2 * 32 * 4 * GJ_NB + 32 * 16;
+constexpr int64_t CHOL_SCR = 2 * 32 * 4 * GJ_NB + 32 * 16 + GJ_NB;
+constexpr int CHOL_EXTRACT_SPLIT = 8;  // work-groups per item of the extraction
 
 __global__ __launch_bounds__(GJ_PIV_THREADS) void chol_sweep128_kernel(const double* __restrict__ A, int64_t lda,
                                                                        int64_t sA, int64_t n, int64_t k0,
@@ -325,6 +326,7 @@ __global__ __launch_bounds__(GJ_PIV_THREADS) void chol_sweep128_kernel(const dou
     double* pre = scr;                       // [32][4][128]
     double* post = scr + 32 * 4 * GJ_NB;     // [32][4][128]
     double* lj = scr + 2 * 32 * 4 * GJ_NB;   // [32][4][4]
+    double* sqs = lj + 32 * 16;              // [128] sqrt of the block's diagonal (the scaling)
     const int nbk = (int)((n - k0) < GJ_NB ? (n - k0) : GJ_NB);
     auto Aget = [&](int r, int c) { return c <= r ? A[(int64_t)r * lda + c] : A[(int64_t)c * lda + r]; };
     double sr[4], sc[8];
@@ -333,6 +335,7 @@ __global__ __launch_bounds__(GJ_PIV_THREADS) void chol_sweep128_kernel(const dou
         const int r = 4 * tr + rr;
         const double p = r < nbk ? A[(int64_t)r * lda + r] : 1.0;
         sr[rr] = p > 0.0 ? 1.0 / sqrt(p) : 1.0;
+        if (tc == 0) sqs[r] = p > 0.0 ? sqrt(p) : 1.0;
     }
 #pragma unroll
     for (int cc = 0; cc < 8; cc++) {
@@ -430,11 +433,11 @@ __global__ __launch_bounds__(512) void chol_extract128_kernel(double* __restrict
     const double* pre = scr;
     const double* post = scr + 32 * 4 * GJ_NB;
     const double* lj = scr + 2 * 32 * 4 * GJ_NB;
+    const double* sqs = lj + 32 * 16;
     const int nbk = (int)((n - k0) < GJ_NB ? (n - k0) : GJ_NB);
-    if (tid < GJ_NB) {
-        const double p = tid < nbk ? A[(int64_t)tid * lda + tid] : 1.0;
-        sq[tid] = p > 0.0 ? sqrt(p) : 1.0;
-    }
+    // the scaling comes from the sweep's scratch, not from A's diagonal, which the work-groups of
+    // this item overwrite (they split the entries below: blockIdx.y of gridDim.y)
+    if (tid < GJ_NB) sq[tid] = sqs[tid];
     if (tid < 32) {
         double L[4][4], Li[4][4];
 #pragma unroll
@@ -464,8 +467,9 @@ __global__ __launch_bounds__(512) void chol_extract128_kernel(double* __restrict
             }
     }
     __syncthreads();
+    const int e0 = (int)blockIdx.y * 512 + tid, es = (int)gridDim.y * 512;
     // L: entry (r, 4 jb + q) for r >= 4 jb
-    for (int e = tid; e < GJ_NB * 32; e += 512) {
+    for (int e = e0; e < GJ_NB * 32; e += es) {
         const int r = e >> 5, jb = e & 31, j0 = 4 * jb;
         if (r < j0 || r >= nbk) continue;
         if (r < j0 + 4) {
@@ -486,7 +490,7 @@ __global__ __launch_bounds__(512) void chol_extract128_kernel(double* __restrict
         }
     }
     // X = L^{-1}: entry (4 jb + q, c) for c < 4 jb + 4
-    for (int e = tid; e < GJ_NB * GJ_NB; e += 512) {
+    for (int e = e0; e < GJ_NB * GJ_NB; e += es) {
         const int r = e >> 7, c = e & 127, jb = r >> 2, q = r & 3;
         if (c > 4 * jb + 3 || r >= nbk || c >= nbk) continue;
         double t = 0.0;
@@ -506,8 +510,8 @@ kq_status kq::chol_inv_diag128(double* A, int64_t lda, int64_t sA, double* X, in
     hipLaunchKernelGGL(chol_sweep128_kernel, dim3((unsigned)batch), dim3(GJ_PIV_THREADS), 0, st, A, lda, sA, n, k0, scr,
                        info, info_stride, skip);
     KQ_TRY(check_launch("chol_sweep128"));
-    hipLaunchKernelGGL(chol_extract128_kernel, dim3((unsigned)batch), dim3(512), 0, st, A, lda, sA, X, ldx, sX, n, k0,
-                       scr, skip);
+    hipLaunchKernelGGL(chol_extract128_kernel, dim3((unsigned)batch, CHOL_EXTRACT_SPLIT), dim3(512), 0, st, A, lda, sA, X,
+                       ldx, sX, n, k0, scr, skip);
     return check_launch("chol_extract128");
 }
 
