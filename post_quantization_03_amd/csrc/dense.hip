@@ -375,6 +375,27 @@ __global__ __launch_bounds__(256) void dgemm_valu_kernel(GemmArgs<double> g) {
 
     double ra[NVA][2], rb[NVB][2];
     const bool fullMN = (m0 + BM <= M) && (n0 + BN <= N);
+    const bool cvec = ((reinterpret_cast<uintptr_t>(C) & 15) == 0) && ((g.ldc & 1) == 0);
+    const bool vec_epi = cvec && fullMN && !rs && !cs && (g.tri == 0 || tm != tn);
+    // C - A B accumulated from -C: the tile's read of C comes first (work-groups alternate, by their
+    // place in their XCD's run, between reading C first and last)
+    const bool pre = g.stagger && vec_epi && g.alpha == -1.0 && g.beta == 1.0 &&
+                     ((blockIdx.x >> 3) & 1) && kb < ke;
+    if (pre) {
+#pragma unroll
+        for (int hi = 0; hi < 2; hi++)
+#pragma unroll
+            for (int i = 0; i < RG; i++)
+#pragma unroll
+                for (int hj = 0; hj < 2; hj++)
+#pragma unroll
+                    for (int j = 0; j < CG; j += 2) {
+                        const int64_t m = m0 + hi * (BM / 2) + tr * RG + i, n = n0 + hj * (BN / 2) + tc * CG + j;
+                        const V16<double> t = *reinterpret_cast<const V16<double>*>(C + m * g.ldc + n);
+                        acc[hi][i][hj][j] = -t.v[0];
+                        acc[hi][i][hj][j + 1] = -t.v[1];
+                    }
+    }
     auto gload = [&](int64_t k0) {
         const bool full = VEC && fullMN && (k0 + BK <= ke);
 #pragma unroll
@@ -478,8 +499,23 @@ __global__ __launch_bounds__(256) void dgemm_valu_kernel(GemmArgs<double> g) {
 
     // Epilogue. Full tiles that lie inside the stored triangle, without sign vectors, take 16-byte
     // loads and stores of C; every other tile goes element by element with the bounds checks.
-    const bool cvec = ((reinterpret_cast<uintptr_t>(C) & 15) == 0) && ((g.ldc & 1) == 0);
-    if (cvec && fullMN && !rs && !cs && (g.tri == 0 || tm != tn)) {
+    if (pre) {
+        // acc = A B - C: store -acc
+#pragma unroll
+        for (int hi = 0; hi < 2; hi++)
+#pragma unroll
+            for (int i = 0; i < RG; i++)
+#pragma unroll
+                for (int hj = 0; hj < 2; hj++)
+#pragma unroll
+                    for (int j = 0; j < CG; j += 2) {
+                        const int64_t m = m0 + hi * (BM / 2) + tr * RG + i, n = n0 + hj * (BN / 2) + tc * CG + j;
+                        *reinterpret_cast<V16<double>*>(C + m * g.ldc + n) =
+                            V16<double>{{-acc[hi][i][hj][j], -acc[hi][i][hj][j + 1]}};
+                    }
+        return;
+    }
+    if (vec_epi) {
         const double alpha = g.alpha, beta = g.beta;
 #pragma unroll
         for (int hi = 0; hi < 2; hi++) {

@@ -606,14 +606,15 @@ static kq_status sweep_queues(SweepQueues** out) {
 // Pipeline per pivot step k. The pivot block k + 1 depends on step k's update only through tile row
 // and column k + 1, so:
 //   main queue: update those tiles (tile (k + 1, k) excepted) and gather panel k + 1, taking tile
-//               (k + 1, k) from T_k; then the rest of step k's update A_RR -= T_k C_k^T (every tile
-//               outside rows and columns k, k + 1);
-//   side queue: invert pivot k + 1, T_{k+1} = C_{k+1} Pinv_{k+1}, write T_k and -Pinv_k back into
-//               row and column k, concurrently with the main queue's wide update.
+//               (k + 1, k) from T_k; then write T_k and -Pinv_k back into row and column k and apply
+//               the rest of step k's update A_RR -= T_k C_k^T (every tile outside rows and columns
+//               k, k + 1);
+//   side queue: invert pivot k + 1 and form T_{k+1} = C_{k+1} Pinv_{k+1}, concurrently with the main
+//               queue's wide update.
 // The wide update starts only once the side queue has passed its wait for the gather, so the pivot
-// work-groups reach the dispatcher ahead of the update's tiles. The queues touch disjoint tiles and
-// alternate the panel buffers; step k + 1 on the main queue waits for the side queue's step k. The
-// caller's stream waits for both at the end.
+// work-groups reach the dispatcher ahead of the update's tiles; the write-back fills that wait. The
+// queues touch disjoint tiles and alternate the panel buffers; step k + 1 on the main queue waits for
+// the side queue's step k + 1 pivot. The caller's stream waits for both at the end.
 static kq_status gj_inverse_batched(double* A, int64_t n, int64_t lda, int64_t sA, int64_t batch, double* const C[2],
                                     double* const T[2], double* const Pinv[2], int32_t* info, const int* skip,
                                     hipStream_t st) {
@@ -663,19 +664,21 @@ static kq_status gj_inverse_batched(double* A, int64_t n, int64_t lda, int64_t s
             KQ_TRY(gather(k + 1, sm));
         }
         KQ_HIP(hipEventRecord(evG[cur], sm));
-        // side queue: pivot k + 1 and the write-back of step k; evS marks that it has passed its wait
+        // side queue: pivot k + 1; evS marks that it has passed its wait
         KQ_HIP(hipStreamWaitEvent(sb, evG[cur], 0));
         KQ_HIP(hipEventRecord(evS[cur], sb));
         if (k + 1 < nt) KQ_TRY(pivot_t(k + 1));
-        hipLaunchKernelGGL(gj_scatter_kernel, gr, dim3(256), 0, sb, A, n, lda, sA, k0, nbk, T[cur], sC, Pinv[cur], skip);
-        KQ_TRY(check_launch("gj_scatter"));
         KQ_HIP(hipEventRecord(evB[nxt], sb));
-        // main queue: the rest of step k's update
+        // main queue: write step k back while the side queue takes its wait (rows and columns k are
+        // outside both the update and the gather), then the rest of step k's update
+        hipLaunchKernelGGL(gj_scatter_kernel, gr, dim3(256), 0, sm, A, n, lda, sA, k0, nbk, T[cur], sC, Pinv[cur], skip);
+        KQ_TRY(check_launch("gj_scatter"));
         KQ_HIP(hipStreamWaitEvent(sm, evS[cur], 0));
         if (nt > 1) {
             GemmArgs<double> u = gemm_args<double>(n, n, nbk, T[cur], GJ_NB, C[cur], GJ_NB, A, lda, -1.0, 1.0);
             u.nb1 = batch; u.sA1 = sC; u.sB1 = sC; u.sC1 = sA; u.tri = 1; u.skip = skip; u.skip_tile = k;
             u.skip_tile2 = k + 1 < nt ? k + 1 : -1;
+            u.stagger = 1;
             KQ_TRY(gemm<double>(u, false, true, sm));
         }
     }

@@ -74,6 +74,8 @@ struct GemmArgs {
     int compact;       // set by the fp64 launcher: the grid omits the skipped tile rows and columns
     int own_rows;      // fp64, N <= 128: one work-group per block of C rows, so that C may overwrite A
                        // (every work-group reads only the rows of A that it writes)
+    int stagger;       // fp64, alpha = -1 and beta = 1: every other work-group reads its tile of C before
+                       // the product instead of after it, so the tiles' reads of C spread over the launch
 };
 
 template <typename T>
