@@ -82,6 +82,160 @@ __global__ __launch_bounds__(256) void gj_gather_kernel(const double* __restrict
     }
 }
 
+// Step k's update of tile row and column f = k + 1, fused with the gather of panel f (n a multiple
+// of 128, so every block is 128 wide). Work-groups take 64 x 64 tiles of the lower triangle in row
+// block f (tiles (i, 0..i) of its two 64-row tiles) and in column block f below it, as the tile
+// focus of the fp64 GEMM does, and apply A_tile -= T_k[rows] C_k[cols]^T with the whole K = 128 of
+// both operands staged in LDS at once, and the tile of A read alongside (one load latency instead of
+// one per 16-deep slice; the sums run over k in the same order). Each new value is also written to the panel of step f: at
+// (row, col - 128 f) when the column is in block f, and transposed, through LDS, when the row is.
+// Tiles in column block k are left out (that block is written back from T_k), and four more
+// work-groups per item copy panel rows of block k from T_k: A(r, 128 f + c) = T_k[128 f + c][r - 128 k].
+constexpr int GF_T = 64, GF_K = GJ_NB, GF_LD = GF_K + 2;  // tile edge; K staged in LDS; LDS row stride
+struct alignas(16) GfPair {
+    double v[2];
+};
+constexpr size_t GF_SMEM = size_t(2) * GF_T * GF_LD * sizeof(double);
+static_assert(GF_SMEM >= GF_T * (GF_T + 1) * sizeof(double) && GF_SMEM >= 32 * (GJ_NB + 1) * sizeof(double),
+              "the transposing and copying stages reuse the operand LDS");
+
+__host__ __device__ inline int64_t gf_tiles(int64_t n, int64_t k) {  // focus tiles of step k per item
+    const int64_t f0 = 2 * (k + 1), ny = n / GF_T;
+    return (f0 + 1) + (f0 + 2) + 2 * (ny - f0 - 2);
+}
+
+__global__ __launch_bounds__(256) void gj_focus_gather_kernel(double* __restrict__ A, int64_t n, int64_t lda,
+                                                              int64_t sA, const double* __restrict__ Tk,
+                                                              const double* __restrict__ Ck, int64_t sC, int64_t k,
+                                                              double* __restrict__ Cf, const int* skip) {
+    if (skip && *skip) return;
+    extern __shared__ __align__(16) double gf_sm[];
+    double* As = gf_sm;
+    double* Bs = gf_sm + GF_T * GF_LD;
+    const int tid = threadIdx.x, tr = tid >> 4, tc = tid & 15;
+    const int64_t z = blockIdx.z, f = k + 1, k0f = f * GJ_NB, p0 = k * GJ_NB;
+    A += z * sA;
+    Tk += z * sC;
+    Ck += z * sC;
+    Cf += z * sC;
+    const int64_t nf = gf_tiles(n, k);
+    int64_t lid = blockIdx.x;
+    if (lid >= nf) {  // panel rows p0 + 32 w .. + 31 from T_k
+        const int64_t r0 = p0 + 32 * (lid - nf);
+        double (*tile)[GJ_NB + 1] = reinterpret_cast<double (*)[GJ_NB + 1]>(gf_sm);
+        for (int e = tid; e < 32 * GJ_NB; e += 256) {
+            const int c = e / 32, rr = e % 32;
+            tile[rr][c] = Tk[(k0f + c) * GJ_NB + (r0 - p0) + rr];
+        }
+        __syncthreads();
+        for (int e = tid; e < 32 * GJ_NB; e += 256) {
+            const int rr = e / GJ_NB, c = e % GJ_NB;
+            Cf[(r0 + rr) * GJ_NB + c] = tile[rr][c];
+        }
+        return;
+    }
+    const int64_t f0 = 2 * f;
+    int64_t tm = -1, tn = 0;
+    for (int64_t q = 0; q < 2 && tm < 0; q++) {
+        if (lid <= f0 + q) { tm = f0 + q; tn = lid; }
+        else lid -= f0 + q + 1;
+    }
+    if (tm < 0) { tm = f0 + 2 + lid / 2; tn = f0 + lid % 2; }
+    if ((tn >> 1) == k) return;
+    tm = (int64_t)__builtin_amdgcn_readfirstlane((int)tm);
+    tn = (int64_t)__builtin_amdgcn_readfirstlane((int)tn);
+    const int64_t m0 = tm * GF_T, n0 = tn * GF_T;
+    // both operand tiles (64 rows x 128) into LDS, row-major in 16-byte pieces (coalesced, no bank
+    // conflicts), and this thread's 16 entries of the tile of A into registers meanwhile
+    double cin[2][2][2][2];
+#pragma unroll
+    for (int hi = 0; hi < 2; hi++)
+#pragma unroll
+        for (int i = 0; i < 2; i++)
+#pragma unroll
+            for (int hj = 0; hj < 2; hj++) {
+                const int64_t m = m0 + hi * 32 + 2 * tr + i, c = n0 + hj * 32 + 2 * tc;
+                const GfPair t = *reinterpret_cast<const GfPair*>(&A[m * lda + c]);
+                cin[hi][i][hj][0] = t.v[0]; cin[hi][i][hj][1] = t.v[1];
+            }
+#pragma unroll 4
+    for (int q = 0; q < GF_T * GF_K / 2 / 256; q++) {
+        const int v = tid + 256 * q, r = v / (GF_K / 2), c2 = (v % (GF_K / 2)) * 2;
+        *reinterpret_cast<GfPair*>(&As[r * GF_LD + c2]) = *reinterpret_cast<const GfPair*>(&Tk[(m0 + r) * GJ_NB + c2]);
+        *reinterpret_cast<GfPair*>(&Bs[r * GF_LD + c2]) = *reinterpret_cast<const GfPair*>(&Ck[(n0 + r) * GJ_NB + c2]);
+    }
+    __syncthreads();
+    // thread (tr, tc): rows h * 32 + 2 tr + i, columns h * 32 + 2 tc + j of the tile
+    double acc[2][2][2][2];
+#pragma unroll
+    for (int hi = 0; hi < 2; hi++)
+#pragma unroll
+        for (int i = 0; i < 2; i++)
+#pragma unroll
+            for (int hj = 0; hj < 2; hj++)
+#pragma unroll
+                for (int j = 0; j < 2; j++) acc[hi][i][hj][j] = 0.0;
+#pragma unroll 4
+    for (int kk = 0; kk < GF_K; kk += 2) {
+        double a[2][2][2], b[2][2][2];
+#pragma unroll
+        for (int h = 0; h < 2; h++)
+#pragma unroll
+            for (int i = 0; i < 2; i++) {
+                const GfPair ta = *reinterpret_cast<const GfPair*>(&As[(h * 32 + 2 * tr + i) * GF_LD + kk]);
+                const GfPair tb = *reinterpret_cast<const GfPair*>(&Bs[(h * 32 + 2 * tc + i) * GF_LD + kk]);
+                a[h][i][0] = ta.v[0]; a[h][i][1] = ta.v[1];
+                b[h][i][0] = tb.v[0]; b[h][i][1] = tb.v[1];
+            }
+#pragma unroll
+        for (int e = 0; e < 2; e++)
+#pragma unroll
+            for (int hi = 0; hi < 2; hi++)
+#pragma unroll
+                for (int i = 0; i < 2; i++)
+#pragma unroll
+                    for (int hj = 0; hj < 2; hj++)
+#pragma unroll
+                        for (int j = 0; j < 2; j++)
+                            acc[hi][i][hj][j] = fma(a[hi][i][e], b[hj][j][e], acc[hi][i][hj][j]);
+    }
+    // A = A - acc on the stored (lower) triangle; panel entries of column block f directly
+    const bool col_f = (n0 >> 7) == f, row_f = (m0 >> 7) == f;
+#pragma unroll
+    for (int hi = 0; hi < 2; hi++)
+#pragma unroll
+        for (int i = 0; i < 2; i++)
+#pragma unroll
+            for (int hj = 0; hj < 2; hj++)
+#pragma unroll
+                for (int j = 0; j < 2; j++) {
+                    const int64_t m = m0 + hi * 32 + 2 * tr + i, c = n0 + hj * 32 + 2 * tc + j;
+                    if (c > m) continue;
+                    const double v = fma(1.0, cin[hi][i][hj][j], -acc[hi][i][hj][j]);
+                    A[m * lda + c] = v;
+                    if (col_f) Cf[m * GJ_NB + (c - k0f)] = v;
+                    acc[hi][i][hj][j] = v;
+                }
+    if (!row_f) return;
+    // row block f: the panel takes the transpose, staged through LDS
+    __syncthreads();
+    double (*L)[GF_T + 1] = reinterpret_cast<double (*)[GF_T + 1]>(gf_sm);
+#pragma unroll
+    for (int hi = 0; hi < 2; hi++)
+#pragma unroll
+        for (int i = 0; i < 2; i++)
+#pragma unroll
+            for (int hj = 0; hj < 2; hj++)
+#pragma unroll
+                for (int j = 0; j < 2; j++) L[hj * 32 + 2 * tc + j][hi * 32 + 2 * tr + i] = acc[hi][i][hj][j];
+    __syncthreads();
+    for (int e = tid; e < GF_T * GF_T; e += 256) {
+        const int cl = e / GF_T, ml = e % GF_T;
+        if (n0 + cl > m0 + ml) continue;
+        Cf[(n0 + cl) * GJ_NB + (m0 - k0f + ml)] = L[cl][ml];
+    }
+}
+
 // Work-group barrier that orders LDS only: global stores issued before it may still be in flight
 // (nothing in the work-group reads them back).
 __device__ inline void lds_barrier() {
@@ -646,6 +800,14 @@ static kq_status gj_inverse_batched(double* A, int64_t n, int64_t lda, int64_t s
         t.nb1 = batch; t.sA1 = sC; t.sB1 = GJ_NB * GJ_NB; t.sC1 = sC; t.skip = skip;
         return gemm<double>(t, false, false, sb);
     };
+    // whole 128-wide blocks: the row and column update of the next pivot and its gather are one kernel
+    const bool fused = n % GJ_NB == 0 && lda % 2 == 0 && sA % 2 == 0 && (reinterpret_cast<uintptr_t>(A) & 15) == 0;
+    static bool gf_attr = false;
+    if (fused && !gf_attr) {
+        KQ_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(&gj_focus_gather_kernel),
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)GF_SMEM));
+        gf_attr = true;
+    }
     KQ_HIP(hipEventRecord(ev0, st));
     KQ_HIP(hipStreamWaitEvent(sb, ev0, 0));
     KQ_TRY(gather(0, sb));
@@ -654,9 +816,13 @@ static kq_status gj_inverse_batched(double* A, int64_t n, int64_t lda, int64_t s
     for (int64_t k = 0; k < nt; k++) {
         const int cur = (int)(k & 1), nxt = cur ^ 1, nbk = nb_of(k);
         const int64_t k0 = k * GJ_NB;
-        // main queue (step k - 1's update already behind it in order): T_k ready, step k - 1 written back
+        // main queue (step k - 1's update already behind it in order): T_k ready
         KQ_HIP(hipStreamWaitEvent(sm, evB[cur], 0));
-        if (k + 1 < nt) {
+        if (k + 1 < nt && fused) {
+            hipLaunchKernelGGL(gj_focus_gather_kernel, dim3((unsigned)(gf_tiles(n, k) + 4), 1, (unsigned)batch),
+                               dim3(256), GF_SMEM, sm, A, n, lda, sA, T[cur], C[cur], sC, k, C[nxt], skip);
+            KQ_TRY(check_launch("gj_focus_gather"));
+        } else if (k + 1 < nt) {
             GemmArgs<double> u = gemm_args<double>(n, n, nbk, T[cur], GJ_NB, C[cur], GJ_NB, A, lda, -1.0, 1.0);
             u.nb1 = batch; u.sA1 = sC; u.sB1 = sC; u.sC1 = sA; u.tri = 1; u.skip = skip; u.skip_tile = k;
             u.focus = k + 1;

@@ -88,7 +88,7 @@ def test_rotate_in(o, i, wdt, with_h):
 
 # ----------------------------------------------------------------------------- H_G square root
 @pytest.mark.parametrize("form,o,blk", [("diag", 1000, 0), ("block", 384, 128), ("full", 256, 0), ("full", 200, 0),
-                                        ("block", 256, 64)])
+                                        ("block", 256, 64), ("full", 1024, 0), ("full", 1000, 0)])
 def test_hg_sqrt(form, o, blk):
     torch, dev = torch_dev()
     say(f"hg_sqrt {form} o={o} blk={blk}")
