@@ -121,9 +121,10 @@ kq_status kq_rotate_in(const void* Win, kq_dtype wdt, int64_t ldwin, float* Wout
  * bounds (nbk doubles) and launches exactly the further steps they imply; the rest is
  * asynchronous on `stream`. Not for graph capture.
  * Sinv may be NULL. info (device int32): 0; k in 1..o if H_G (or an iterate) is not positive
- * definite (k = 1 + index of the failing pivot); o + 1 if the iteration did not converge. The
- * caller may free HG once the work has completed in stream order (H_G is only needed
- * transiently).
+ * definite (k = 1 + index of the failing pivot); o + 1 if the iteration did not converge; -1 if a
+ * device-side hand-over between the sweep's queues timed out (an internal error; S is then
+ * invalid). The caller may free HG once the work has completed in stream order (H_G is only
+ * needed transiently).
  */
 kq_status kq_hg_sqrt(const float* HG, kq_hg_form form, int64_t o, int64_t blk, float* S, float* Sinv,
                      int32_t* info, void* ws, size_t ws_bytes, kq_stream stream);

@@ -315,14 +315,39 @@ __device__ inline int inv4_spd(double D[4][4]) {
     return bad;
 }
 
+// With `ready` set the kernel is launched ahead of the kernel that writes its pivot block: it first
+// waits, in a bounded loop, until *ready reaches `ready_at` (a release store made after that kernel
+// has completed), then acquires at device scope before reading the block. A wait that runs out
+// (never expected) is reported through info as -1 and the block is inverted as found.
+constexpr int GJ_WAIT_POLLS = 1 << 16;  // tens of milliseconds of polling at most
+// Early-launched pivots occupy one compute unit per item while they wait: only for small batches,
+// so that the kernels they wait for always find compute units.
+constexpr int64_t GJ_EARLY_PIVOT_MAX = 16;
+
+__global__ void gj_signal_kernel(uint64_t* ready, uint64_t value) {
+    if (threadIdx.x == 0) __hip_atomic_store(ready, value, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 __global__ __launch_bounds__(GJ_PIV_THREADS) void gj_pivot_kernel(const double* __restrict__ C, int64_t sC,
                                                                   int64_t k0, int nbk, double* __restrict__ Pinv,
-                                                                  int32_t* info, const int* skip) {
+                                                                  int32_t* info, const int* skip,
+                                                                  const uint64_t* ready, uint64_t ready_at) {
     if (skip && *skip) return;
     __shared__ __align__(16) double rowb[2][4][GJ_NB];
     __shared__ __align__(16) double dinv[2][4][4];
     __shared__ int bad_s;
     const int tid = threadIdx.x, tr = tid >> 4, tc = tid & 15;
+    if (ready) {
+        if (tid == 0) {
+            int polls = 0;
+            while (__hip_atomic_load(ready, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < ready_at &&
+                   ++polls < GJ_WAIT_POLLS)
+                __builtin_amdgcn_s_sleep(2);
+            if (polls >= GJ_WAIT_POLLS && info) info[blockIdx.x] = -1;
+        }
+        __syncthreads();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    }
     // column cc of the thread's tile: two runs of four, 64 apart, so that the 16 column groups of a
     // wave read one contiguous 512-byte run per LDS instruction
     auto col = [&](int cc) { return (cc >> 2) * 64 + 4 * tc + (cc & 3); };
@@ -723,9 +748,13 @@ __global__ __launch_bounds__(256) void gj_scatter_kernel(double* __restrict__ A,
 // `main` the wide rank-128 updates. Events order both with the caller's stream; the mutex keeps the
 // event sequence of one call intact when several host threads enqueue at once. The events only order
 // work of the one device, so they take a device-scope release (no system-scope fence when recorded).
+// `ready` is a device counter that only grows (one release store per signalled step, value
+// `signalled`, kept on the host under the mutex), which pivot kernels launched early wait on.
 struct SweepQueues {
     hipStream_t side = nullptr, main = nullptr;
     hipEvent_t ev[9] = {};
+    uint64_t* ready = nullptr;
+    uint64_t signalled = 0;
     bool ok = false;
 };
 static std::mutex g_sweep_mu;
@@ -742,6 +771,10 @@ static kq_status sweep_queues(SweepQueues** out) {
         for (hipEvent_t& e : q.ev)
             if (hipEventCreateWithFlags(&e, hipEventDisableTiming | hipEventDisableSystemFence) != hipSuccess)
                 return fail(KQ_EHIP, "sweep queues: event creation failed");
+        if (hipMalloc(reinterpret_cast<void**>(&q.ready), sizeof(uint64_t)) != hipSuccess ||
+            hipMemsetAsync(q.ready, 0, sizeof(uint64_t), q.side) != hipSuccess ||
+            hipStreamSynchronize(q.side) != hipSuccess)
+            return fail(KQ_EHIP, "sweep queues: counter set-up failed");
         q.ok = true;
     }
     *out = &q;
@@ -760,15 +793,19 @@ static kq_status sweep_queues(SweepQueues** out) {
 // Pipeline per pivot step k. The pivot block k + 1 depends on step k's update only through tile row
 // and column k + 1, so:
 //   main queue: update those tiles (tile (k + 1, k) excepted) and gather panel k + 1, taking tile
-//               (k + 1, k) from T_k; then write T_k and -Pinv_k back into row and column k and apply
-//               the rest of step k's update A_RR -= T_k C_k^T (every tile outside rows and columns
-//               k, k + 1);
-//   side queue: invert pivot k + 1 and form T_{k+1} = C_{k+1} Pinv_{k+1}, concurrently with the main
-//               queue's wide update.
-// The wide update starts only once the side queue has passed its wait for the gather, so the pivot
-// work-groups reach the dispatcher ahead of the update's tiles; the write-back fills that wait. The
-// queues touch disjoint tiles and alternate the panel buffers; step k + 1 on the main queue waits for
-// the side queue's step k + 1 pivot. The caller's stream waits for both at the end.
+//               (k + 1, k) from T_k; then apply the rest of step k's update A_RR -= T_k C_k^T (every
+//               tile outside rows and columns k, k + 1);
+//   side queue: invert pivot k + 1, write T_k and -Pinv_k back into row and column k, form
+//               T_{k+1} = C_{k+1} Pinv_{k+1}, concurrently with the main queue's wide update.
+// The pivot's work-groups need a whole compute unit each (202 VGPRs x 8 waves), so they must be
+// dispatched before the wide update's tiles fill the chip. With whole 128-wide blocks and a small
+// batch the pivot kernel is launched as soon as the side queue reaches it and waits on the device
+// for a counter that the main queue releases right after the gather (a bounded wait; no queue wait
+// sits on that path). Otherwise the side queue waits for an event after the gather, and the wide
+// update for an event the side queue records once past that wait, and the write-back runs on the
+// main queue meanwhile. The queues touch disjoint tiles and alternate the panel buffers; step k + 1
+// on the main queue waits for the side queue's T_{k+1} and write-back of step k. The caller's
+// stream waits for both at the end.
 static kq_status gj_inverse_batched(double* A, int64_t n, int64_t lda, int64_t sA, int64_t batch, double* const C[2],
                                     double* const T[2], double* const Pinv[2], int32_t* info, const int* skip,
                                     hipStream_t st) {
@@ -791,14 +828,32 @@ static kq_status gj_inverse_batched(double* A, int64_t n, int64_t lda, int64_t s
         hipLaunchKernelGGL(gj_gather_kernel, gr, dim3(256), 0, qg, A, n, lda, sA, k0, nbk, C[b], sC, Tp, p0, k0, skip);
         return check_launch("gj_gather");
     };
-    auto pivot_t = [&](int64_t k) -> kq_status {  // side queue: Pinv_k, T_k = C_k Pinv_k
+    // side queue: Pinv_k (waiting on the device counter for `ready_at` when given), T_k = C_k Pinv_k
+    auto pivot = [&](int64_t k, uint64_t ready_at) -> kq_status {
         const int b = (int)(k & 1), nbk = nb_of(k);
         hipLaunchKernelGGL(gj_pivot_kernel, dim3((unsigned)batch), dim3(GJ_PIV_THREADS), 0, sb, C[b], sC, k * GJ_NB,
-                           nbk, Pinv[b], info, skip);
-        KQ_TRY(check_launch("gj_pivot"));
+                           nbk, Pinv[b], info, skip, ready_at ? q->ready : nullptr, ready_at);
+        return check_launch("gj_pivot");
+    };
+    auto tprod = [&](int64_t k) -> kq_status {
+        const int b = (int)(k & 1), nbk = nb_of(k);
         GemmArgs<double> t = gemm_args<double>(n, nbk, nbk, C[b], GJ_NB, Pinv[b], GJ_NB, T[b], GJ_NB, 1.0, 0.0);
         t.nb1 = batch; t.sA1 = sC; t.sB1 = GJ_NB * GJ_NB; t.sC1 = sC; t.skip = skip;
         return gemm<double>(t, false, false, sb);
+    };
+    auto scatter = [&](int64_t k, hipStream_t qs) -> kq_status {
+        const int b = (int)(k & 1);
+        hipLaunchKernelGGL(gj_scatter_kernel, gr, dim3(256), 0, qs, A, n, lda, sA, k * GJ_NB, nb_of(k), T[b], sC,
+                           Pinv[b], skip);
+        return check_launch("gj_scatter");
+    };
+    auto wide_update = [&](int64_t k) -> kq_status {  // main queue: every tile outside rows/columns k, k + 1
+        const int b = (int)(k & 1);
+        GemmArgs<double> u = gemm_args<double>(n, n, nb_of(k), T[b], GJ_NB, C[b], GJ_NB, A, lda, -1.0, 1.0);
+        u.nb1 = batch; u.sA1 = sC; u.sB1 = sC; u.sC1 = sA; u.tri = 1; u.skip = skip; u.skip_tile = k;
+        u.skip_tile2 = k + 1 < nt ? k + 1 : -1;
+        u.stagger = 1;
+        return gemm<double>(u, false, true, sm);
     };
     // whole 128-wide blocks: the row and column update of the next pivot and its gather are one kernel
     const bool fused = n % GJ_NB == 0 && lda % 2 == 0 && sA % 2 == 0 && (reinterpret_cast<uintptr_t>(A) & 15) == 0;
@@ -808,44 +863,69 @@ static kq_status gj_inverse_batched(double* A, int64_t n, int64_t lda, int64_t s
                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)GF_SMEM));
         gf_attr = true;
     }
+    auto focus_gather = [&](int64_t k) -> kq_status {  // main queue: step k on tile row/column k + 1, panel k + 1
+        const int cur = (int)(k & 1);
+        hipLaunchKernelGGL(gj_focus_gather_kernel, dim3((unsigned)(gf_tiles(n, k) + 4), 1, (unsigned)batch), dim3(256),
+                           GF_SMEM, sm, A, n, lda, sA, T[cur], C[cur], sC, k, C[cur ^ 1], skip);
+        return check_launch("gj_focus_gather");
+    };
     KQ_HIP(hipEventRecord(ev0, st));
     KQ_HIP(hipStreamWaitEvent(sb, ev0, 0));
     KQ_TRY(gather(0, sb));
-    KQ_TRY(pivot_t(0));
+    KQ_TRY(pivot(0, 0));
+    KQ_TRY(tprod(0));
     KQ_HIP(hipEventRecord(evB[0], sb));
-    for (int64_t k = 0; k < nt; k++) {
-        const int cur = (int)(k & 1), nxt = cur ^ 1, nbk = nb_of(k);
-        const int64_t k0 = k * GJ_NB;
-        // main queue (step k - 1's update already behind it in order): T_k ready
-        KQ_HIP(hipStreamWaitEvent(sm, evB[cur], 0));
-        if (k + 1 < nt && fused) {
-            hipLaunchKernelGGL(gj_focus_gather_kernel, dim3((unsigned)(gf_tiles(n, k) + 4), 1, (unsigned)batch),
-                               dim3(256), GF_SMEM, sm, A, n, lda, sA, T[cur], C[cur], sC, k, C[nxt], skip);
-            KQ_TRY(check_launch("gj_focus_gather"));
-        } else if (k + 1 < nt) {
-            GemmArgs<double> u = gemm_args<double>(n, n, nbk, T[cur], GJ_NB, C[cur], GJ_NB, A, lda, -1.0, 1.0);
-            u.nb1 = batch; u.sA1 = sC; u.sB1 = sC; u.sC1 = sA; u.tri = 1; u.skip = skip; u.skip_tile = k;
-            u.focus = k + 1;
-            KQ_TRY(gemm<double>(u, false, true, sm));
-            KQ_TRY(gather(k + 1, sm));
+    if (fused && batch <= GJ_EARLY_PIVOT_MAX) {
+        // Step k: main queue: (T_k and the write-back of step k - 1 done) the fused row/column update
+        // and gather, a release of the counter, then the wide update. Side queue: pivot k + 1,
+        // launched at once so its work-groups hold their compute units before the wide update is
+        // dispatched; it waits on the device for the counter, so no queue wait sits between the
+        // gather and the pivot or between the pivot and the wide update. Then the write-back of step
+        // k (rows and columns k, outside the wide update) and T_{k+1}.
+        for (int64_t k = 0; k < nt; k++) {
+            const int cur = (int)(k & 1), nxt = cur ^ 1;
+            KQ_HIP(hipStreamWaitEvent(sm, evB[cur], 0));
+            uint64_t ready_at = 0;
+            if (k + 1 < nt) {
+                KQ_TRY(focus_gather(k));
+                ready_at = ++q->signalled;
+                hipLaunchKernelGGL(gj_signal_kernel, dim3(1), dim3(64), 0, sm, q->ready, ready_at);
+                KQ_TRY(check_launch("gj_signal"));
+                KQ_TRY(pivot(k + 1, ready_at));
+            }
+            KQ_TRY(scatter(k, sb));
+            if (k + 1 < nt) KQ_TRY(tprod(k + 1));
+            KQ_HIP(hipEventRecord(evB[nxt], sb));
+            if (nt > 1) KQ_TRY(wide_update(k));
         }
-        KQ_HIP(hipEventRecord(evG[cur], sm));
-        // side queue: pivot k + 1; evS marks that it has passed its wait
-        KQ_HIP(hipStreamWaitEvent(sb, evG[cur], 0));
-        KQ_HIP(hipEventRecord(evS[cur], sb));
-        if (k + 1 < nt) KQ_TRY(pivot_t(k + 1));
-        KQ_HIP(hipEventRecord(evB[nxt], sb));
-        // main queue: write step k back while the side queue takes its wait (rows and columns k are
-        // outside both the update and the gather), then the rest of step k's update
-        hipLaunchKernelGGL(gj_scatter_kernel, gr, dim3(256), 0, sm, A, n, lda, sA, k0, nbk, T[cur], sC, Pinv[cur], skip);
-        KQ_TRY(check_launch("gj_scatter"));
-        KQ_HIP(hipStreamWaitEvent(sm, evS[cur], 0));
-        if (nt > 1) {
-            GemmArgs<double> u = gemm_args<double>(n, n, nbk, T[cur], GJ_NB, C[cur], GJ_NB, A, lda, -1.0, 1.0);
-            u.nb1 = batch; u.sA1 = sC; u.sB1 = sC; u.sC1 = sA; u.tri = 1; u.skip = skip; u.skip_tile = k;
-            u.skip_tile2 = k + 1 < nt ? k + 1 : -1;
-            u.stagger = 1;
-            KQ_TRY(gemm<double>(u, false, true, sm));
+    } else {
+        for (int64_t k = 0; k < nt; k++) {
+            const int cur = (int)(k & 1), nxt = cur ^ 1, nbk = nb_of(k);
+            // main queue (step k - 1's update already behind it in order): T_k ready
+            KQ_HIP(hipStreamWaitEvent(sm, evB[cur], 0));
+            if (k + 1 < nt && fused) {
+                KQ_TRY(focus_gather(k));
+            } else if (k + 1 < nt) {
+                GemmArgs<double> u = gemm_args<double>(n, n, nbk, T[cur], GJ_NB, C[cur], GJ_NB, A, lda, -1.0, 1.0);
+                u.nb1 = batch; u.sA1 = sC; u.sB1 = sC; u.sC1 = sA; u.tri = 1; u.skip = skip; u.skip_tile = k;
+                u.focus = k + 1;
+                KQ_TRY(gemm<double>(u, false, true, sm));
+                KQ_TRY(gather(k + 1, sm));
+            }
+            KQ_HIP(hipEventRecord(evG[cur], sm));
+            // side queue: pivot k + 1; evS marks that it has passed its wait
+            KQ_HIP(hipStreamWaitEvent(sb, evG[cur], 0));
+            KQ_HIP(hipEventRecord(evS[cur], sb));
+            if (k + 1 < nt) {
+                KQ_TRY(pivot(k + 1, 0));
+                KQ_TRY(tprod(k + 1));
+            }
+            KQ_HIP(hipEventRecord(evB[nxt], sb));
+            // main queue: write step k back while the side queue takes its wait (rows and columns k
+            // are outside both the update and the gather), then the rest of step k's update
+            KQ_TRY(scatter(k, sm));
+            KQ_HIP(hipStreamWaitEvent(sm, evS[cur], 0));
+            if (nt > 1) KQ_TRY(wide_update(k));
         }
     }
     KQ_HIP(hipEventRecord(evM, sm));
