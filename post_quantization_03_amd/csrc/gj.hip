@@ -15,6 +15,7 @@
 // then T and -P^{-1} are scattered back. After all pivots A holds -A^{-1}. Y and Z of every block are
 // one batch.
 #include <cmath>
+#include <cstdlib>
 #include <mutex>
 #include <utility>
 #include <vector>
@@ -316,10 +317,18 @@ __device__ inline int inv4_spd(double D[4][4]) {
 }
 
 // With `ready` set the kernel is launched ahead of the kernel that writes its pivot block: it first
-// waits, in a bounded loop, until *ready reaches `ready_at` (a release store made after that kernel
-// has completed), then acquires at device scope before reading the block. A wait that runs out
-// (never expected) is reported through info as -1 and the block is inverted as found.
-constexpr int GJ_WAIT_POLLS = 1 << 16;  // tens of milliseconds of polling at most
+// waits, in a bounded loop, until ready[0] reaches `ready_at` (a release store made after that
+// kernel has completed), then acquires at device scope before reading the block. A wait that runs
+// out (only when the device runs kernels one at a time) sets ready[1], which ends every later wait
+// at once, and info = -1; the block is inverted as found and the host redoes the call.
+constexpr int GJ_WAIT_POLLS = 1 << 20;  // at most about a second of polling
+// The limit can be lowered through the environment (KQ_SWEEP_WAIT_POLLS, read on each sweep), so
+// that a test can make the wait run out on purpose and check the fallback.
+static int gj_wait_polls() {
+    const char* e = std::getenv("KQ_SWEEP_WAIT_POLLS");
+    const long v = e ? std::strtol(e, nullptr, 10) : 0;
+    return v > 0 && v < GJ_WAIT_POLLS ? (int)v : GJ_WAIT_POLLS;
+}
 // Early-launched pivots occupy one compute unit per item while they wait: only for small batches,
 // so that the kernels they wait for always find compute units.
 constexpr int64_t GJ_EARLY_PIVOT_MAX = 16;
@@ -331,7 +340,8 @@ __global__ void gj_signal_kernel(uint64_t* ready, uint64_t value) {
 __global__ __launch_bounds__(GJ_PIV_THREADS) void gj_pivot_kernel(const double* __restrict__ C, int64_t sC,
                                                                   int64_t k0, int nbk, double* __restrict__ Pinv,
                                                                   int32_t* info, const int* skip,
-                                                                  const uint64_t* ready, uint64_t ready_at) {
+                                                                  const uint64_t* ready, uint64_t ready_at,
+                                                                  int max_polls) {
     if (skip && *skip) return;
     __shared__ __align__(16) double rowb[2][4][GJ_NB];
     __shared__ __align__(16) double dinv[2][4][4];
@@ -340,10 +350,17 @@ __global__ __launch_bounds__(GJ_PIV_THREADS) void gj_pivot_kernel(const double* 
     if (ready) {
         if (tid == 0) {
             int polls = 0;
-            while (__hip_atomic_load(ready, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < ready_at &&
-                   ++polls < GJ_WAIT_POLLS)
+            while (__hip_atomic_load(&ready[0], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < ready_at &&
+                   __hip_atomic_load(&ready[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0 &&
+                   ++polls < max_polls)
                 __builtin_amdgcn_s_sleep(2);
-            if (polls >= GJ_WAIT_POLLS && info) info[blockIdx.x] = -1;
+            if (__hip_atomic_load(&ready[0], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < ready_at) {
+                // the counter never came (the device ran the queues one kernel at a time, as under
+                // some profilers): mark it for the host, which redoes the work with queue waits
+                __hip_atomic_store(const_cast<uint64_t*>(&ready[1]), (uint64_t)1, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+                if (info) info[blockIdx.x] = -1;
+            }
         }
         __syncthreads();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
@@ -753,8 +770,9 @@ __global__ __launch_bounds__(256) void gj_scatter_kernel(double* __restrict__ A,
 struct SweepQueues {
     hipStream_t side = nullptr, main = nullptr;
     hipEvent_t ev[9] = {};
-    uint64_t* ready = nullptr;
+    uint64_t* ready = nullptr;  // [0] the counter, [1] set when a wait on it ran out
     uint64_t signalled = 0;
+    bool early = true;          // pivots launched ahead (cleared for good once a wait ran out)
     bool ok = false;
 };
 static std::mutex g_sweep_mu;
@@ -771,8 +789,8 @@ static kq_status sweep_queues(SweepQueues** out) {
         for (hipEvent_t& e : q.ev)
             if (hipEventCreateWithFlags(&e, hipEventDisableTiming | hipEventDisableSystemFence) != hipSuccess)
                 return fail(KQ_EHIP, "sweep queues: event creation failed");
-        if (hipMalloc(reinterpret_cast<void**>(&q.ready), sizeof(uint64_t)) != hipSuccess ||
-            hipMemsetAsync(q.ready, 0, sizeof(uint64_t), q.side) != hipSuccess ||
+        if (hipMalloc(reinterpret_cast<void**>(&q.ready), 2 * sizeof(uint64_t)) != hipSuccess ||
+            hipMemsetAsync(q.ready, 0, 2 * sizeof(uint64_t), q.side) != hipSuccess ||
             hipStreamSynchronize(q.side) != hipSuccess)
             return fail(KQ_EHIP, "sweep queues: counter set-up failed");
         q.ok = true;
@@ -828,11 +846,12 @@ static kq_status gj_inverse_batched(double* A, int64_t n, int64_t lda, int64_t s
         hipLaunchKernelGGL(gj_gather_kernel, gr, dim3(256), 0, qg, A, n, lda, sA, k0, nbk, C[b], sC, Tp, p0, k0, skip);
         return check_launch("gj_gather");
     };
+    const int polls = gj_wait_polls();
     // side queue: Pinv_k (waiting on the device counter for `ready_at` when given), T_k = C_k Pinv_k
     auto pivot = [&](int64_t k, uint64_t ready_at) -> kq_status {
         const int b = (int)(k & 1), nbk = nb_of(k);
         hipLaunchKernelGGL(gj_pivot_kernel, dim3((unsigned)batch), dim3(GJ_PIV_THREADS), 0, sb, C[b], sC, k * GJ_NB,
-                           nbk, Pinv[b], info, skip, ready_at ? q->ready : nullptr, ready_at);
+                           nbk, Pinv[b], info, skip, ready_at ? q->ready : nullptr, ready_at, polls);
         return check_launch("gj_pivot");
     };
     auto tprod = [&](int64_t k) -> kq_status {
@@ -875,7 +894,7 @@ static kq_status gj_inverse_batched(double* A, int64_t n, int64_t lda, int64_t s
     KQ_TRY(pivot(0, 0));
     KQ_TRY(tprod(0));
     KQ_HIP(hipEventRecord(evB[0], sb));
-    if (fused && batch <= GJ_EARLY_PIVOT_MAX) {
+    if (fused && batch <= GJ_EARLY_PIVOT_MAX && q->early) {
         // Step k: main queue: (T_k and the write-back of step k - 1 done) the fused row/column update
         // and gather, a release of the counter, then the wide update. Side queue: pivot k + 1,
         // launched at once so its work-groups hold their compute units before the wide update is
@@ -931,6 +950,25 @@ static kq_status gj_inverse_batched(double* A, int64_t n, int64_t lda, int64_t s
     KQ_HIP(hipEventRecord(evM, sm));
     KQ_HIP(hipStreamWaitEvent(st, evM, 0));
     KQ_HIP(hipStreamWaitEvent(st, evB[nt & 1], 0));
+    return KQ_OK;
+}
+
+// After work that ran sweeps has been synchronised: true when a pivot's device-side wait ran out
+// in it (the device ran the queues one kernel at a time). The device's sweeps then use queue waits
+// from here on, and the caller redoes the work.
+static kq_status sweep_wait_failed(bool* failed) {
+    std::lock_guard<std::mutex> lock(g_sweep_mu);
+    SweepQueues* q = nullptr;
+    KQ_TRY(sweep_queues(&q));
+    uint64_t f = 0;
+    KQ_HIP(hipMemcpyAsync(&f, q->ready + 1, sizeof(f), hipMemcpyDeviceToHost, q->side));
+    KQ_HIP(hipStreamSynchronize(q->side));
+    *failed = f != 0;
+    if (f) {
+        q->early = false;
+        KQ_HIP(hipMemsetAsync(q->ready + 1, 0, sizeof(uint64_t), q->side));
+        KQ_HIP(hipStreamSynchronize(q->side));
+    }
     return KQ_OK;
 }
 
@@ -1227,6 +1265,9 @@ static kq_status db_sqrt(const float* HGf, const double* HGd, int64_t n, int64_t
             KQ_HIP(hipMemcpyAsync(hb.data(), bnd, (size_t)nbk * sizeof(double), hipMemcpyDeviceToHost, st));
             KQ_HIP(hipMemcpyAsync(hf, flags, sizeof(hf), hipMemcpyDeviceToHost, st));
             KQ_HIP(hipStreamSynchronize(st));
+            bool failed = false;
+            KQ_TRY(sweep_wait_failed(&failed));
+            if (failed) return db_sqrt(HGf, HGd, n, nbk, o_info, info, ws, ws_bytes, Y64, st);
             if (hf[0]) break;  // converged after one step, or stopped on an error (info set)
             int need = 1;
             for (int64_t b = 0; b < nbk; b++) {

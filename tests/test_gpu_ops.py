@@ -162,6 +162,50 @@ def test_hg_sqrt_repeated_calls_identical():
     assert rel_fro(outs[0], S_ref) <= 1e-6
 
 
+_FALLBACK_SCRIPT = r"""
+import sys
+import numpy as np
+import torch
+sys.path.insert(0, sys.argv[1])
+import synth
+from oracle import kronq as kq
+from post_quantization_03_amd import _lib as K
+dev = torch.device("cuda:0")
+o = 512
+hg = synth.gen_HG(synth.scaled(synth.CONFIGS["C2"], o=o, hg_ng=2 * o))
+S_ref, _ = kq.hg_sqrt(hg.astype(np.float64), "full")
+HG = torch.from_numpy(hg).to(dev)
+ws = torch.empty(K.kq_workspace_bytes("hg_sqrt", o, 0, 0, form="full"), dtype=torch.uint8, device=dev)
+for call in range(2):
+    S = torch.empty((o, o), dtype=torch.float32, device=dev)
+    info = torch.zeros(1, dtype=torch.int32, device=dev)
+    K.kq_hg_sqrt(HG, "full", o, 0, S, None, info, ws)
+    torch.cuda.synchronize()
+    err = np.linalg.norm(S.cpu().numpy().astype(np.float64) - S_ref) / np.linalg.norm(S_ref)
+    print(f"call {call}: info {int(info.cpu()[0])} rel err {err:.3e}", flush=True)
+    assert int(info.cpu()[0]) == 0 and err <= 1e-6
+print("OK", flush=True)
+"""
+
+
+def test_hg_sqrt_falls_back_when_device_wait_runs_out():
+    """The sweep's pivot kernels are launched ahead and wait on the device, in a bounded loop, for the
+    other queue's gather. With that bound cut to one poll (KQ_SWEEP_WAIT_POLLS, in a child process,
+    since the switch to queue waits lasts for the process) the first waits run out: the square root
+    notices at its read-back after the first step, redoes the call with queue waits, and still
+    matches the oracle with info 0; a second call does too."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    env = dict(os.environ, KQ_SWEEP_WAIT_POLLS="1")
+    r = subprocess.run([sys.executable, "-c", _FALLBACK_SCRIPT, root], env=env, capture_output=True, text=True,
+                       timeout=180)
+    say(r.stdout.strip())
+    assert r.returncode == 0, r.stdout + r.stderr[-2000:]
+    assert "OK" in r.stdout
+
+
 def test_hg_sqrt_reports_not_positive_definite():
     torch, dev = torch_dev()
     for form, hg in (("full", -np.eye(128, dtype=f32)), ("diag", -np.ones(64, f32))):
