@@ -773,6 +773,7 @@ struct SweepQueues {
     uint64_t* ready = nullptr;  // [0] the counter, [1] set when a wait on it ran out
     uint64_t signalled = 0;
     bool early = true;          // pivots launched ahead (cleared for good once a wait ran out)
+    bool gf_lds = false;        // the fused gather's LDS size has been allowed on this device
     bool ok = false;
 };
 static std::mutex g_sweep_mu;
@@ -876,11 +877,10 @@ static kq_status gj_inverse_batched(double* A, int64_t n, int64_t lda, int64_t s
     };
     // whole 128-wide blocks: the row and column update of the next pivot and its gather are one kernel
     const bool fused = n % GJ_NB == 0 && lda % 2 == 0 && sA % 2 == 0 && (reinterpret_cast<uintptr_t>(A) & 15) == 0;
-    static bool gf_attr = false;
-    if (fused && !gf_attr) {
+    if (fused && !q->gf_lds) {
         KQ_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(&gj_focus_gather_kernel),
                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)GF_SMEM));
-        gf_attr = true;
+        q->gf_lds = true;
     }
     auto focus_gather = [&](int64_t k) -> kq_status {  // main queue: step k on tile row/column k + 1, panel k + 1
         const int cur = (int)(k & 1);
