@@ -285,6 +285,10 @@ template kq_status gemm<float>(const GemmArgs<float>&, bool, bool, hipStream_t);
 // kernel above.
 template <int BM, int BN, bool TA, bool TB, bool VEC>
 __global__ __launch_bounds__(256) void dgemm_valu_kernel(GemmArgs<double> g) {
+    // the launch itself is the signal (nothing of this kernel is published by it), so the store is
+    // relaxed; it comes before the skip test so that a waiter is always released
+    if (g.signal && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x == 0)
+        __hip_atomic_store(g.signal, g.signal_value, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (g.skip && *g.skip) return;
     constexpr int BK = 16, PAD = 2;  // row stride 130 doubles: the transposing stores of a slice spread over the banks
     constexpr int RG = BM / 32, CG = BN / 32;

@@ -317,8 +317,9 @@ __device__ inline int inv4_spd(double D[4][4]) {
 }
 
 // With `ready` set the kernel is launched ahead of the kernel that writes its pivot block: it first
-// waits, in a bounded loop, until ready[0] reaches `ready_at` (a release store made after that
-// kernel has completed), then acquires at device scope before reading the block. A wait that runs
+// waits, in a bounded loop, until ready[0] reaches `ready_at` (stored by the first work-group of the
+// next kernel on that queue, which starts only once that kernel has completed and released its
+// writes), then acquires at device scope before reading the block. A wait that runs
 // out (only when the device runs kernels one at a time) sets ready[1], which ends every later wait
 // at once, and info = -1; the block is inverted as found and the host redoes the call.
 constexpr int GJ_WAIT_POLLS = 1 << 20;  // at most about a second of polling
@@ -333,9 +334,6 @@ static int gj_wait_polls() {
 // so that the kernels they wait for always find compute units.
 constexpr int64_t GJ_EARLY_PIVOT_MAX = 16;
 
-__global__ void gj_signal_kernel(uint64_t* ready, uint64_t value) {
-    if (threadIdx.x == 0) __hip_atomic_store(ready, value, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-}
 
 __global__ __launch_bounds__(GJ_PIV_THREADS) void gj_pivot_kernel(const double* __restrict__ C, int64_t sC,
                                                                   int64_t k0, int nbk, double* __restrict__ Pinv,
@@ -819,8 +817,8 @@ static kq_status sweep_queues(SweepQueues** out) {
 // The pivot's work-groups need a whole compute unit each (202 VGPRs x 8 waves), so they must be
 // dispatched before the wide update's tiles fill the chip. With whole 128-wide blocks and a small
 // batch the pivot kernel is launched as soon as the side queue reaches it and waits on the device
-// for a counter that the main queue releases right after the gather (a bounded wait; no queue wait
-// sits on that path). Otherwise the side queue waits for an event after the gather, and the wide
+// for a counter that the main queue's wide update sets as it starts, right after the gather (a
+// bounded wait; no queue wait or extra launch sits on that path). Otherwise the side queue waits for an event after the gather, and the wide
 // update for an event the side queue records once past that wait, and the write-back runs on the
 // main queue meanwhile. The queues touch disjoint tiles and alternate the panel buffers; step k + 1
 // on the main queue waits for the side queue's T_{k+1} and write-back of step k. The caller's
@@ -867,12 +865,15 @@ static kq_status gj_inverse_batched(double* A, int64_t n, int64_t lda, int64_t s
                            Pinv[b], skip);
         return check_launch("gj_scatter");
     };
-    auto wide_update = [&](int64_t k) -> kq_status {  // main queue: every tile outside rows/columns k, k + 1
+    // main queue: every tile outside rows/columns k, k + 1; with ready_at, the launch also releases
+    // the device counter (it starts only after the gather before it has completed)
+    auto wide_update = [&](int64_t k, uint64_t ready_at) -> kq_status {
         const int b = (int)(k & 1);
         GemmArgs<double> u = gemm_args<double>(n, n, nb_of(k), T[b], GJ_NB, C[b], GJ_NB, A, lda, -1.0, 1.0);
         u.nb1 = batch; u.sA1 = sC; u.sB1 = sC; u.sC1 = sA; u.tri = 1; u.skip = skip; u.skip_tile = k;
         u.skip_tile2 = k + 1 < nt ? k + 1 : -1;
         u.stagger = 1;
+        if (ready_at) { u.signal = q->ready; u.signal_value = ready_at; }
         return gemm<double>(u, false, true, sm);
     };
     // whole 128-wide blocks: the row and column update of the next pivot and its gather are one kernel
@@ -896,11 +897,12 @@ static kq_status gj_inverse_batched(double* A, int64_t n, int64_t lda, int64_t s
     KQ_HIP(hipEventRecord(evB[0], sb));
     if (fused && batch <= GJ_EARLY_PIVOT_MAX && q->early) {
         // Step k: main queue: (T_k and the write-back of step k - 1 done) the fused row/column update
-        // and gather, a release of the counter, then the wide update. Side queue: pivot k + 1,
+        // and gather, then the wide update, whose start releases the counter. Side queue: pivot k + 1,
         // launched at once so its work-groups hold their compute units before the wide update is
         // dispatched; it waits on the device for the counter, so no queue wait sits between the
-        // gather and the pivot or between the pivot and the wide update. Then the write-back of step
-        // k (rows and columns k, outside the wide update) and T_{k+1}.
+        // gather and the pivot or between the pivot and the wide update. The write-back of step k
+        // (rows and columns k, outside the wide update and the gather) goes just before the pivot,
+        // T_{k+1} after it.
         for (int64_t k = 0; k < nt; k++) {
             const int cur = (int)(k & 1), nxt = cur ^ 1;
             KQ_HIP(hipStreamWaitEvent(sm, evB[cur], 0));
@@ -908,14 +910,19 @@ static kq_status gj_inverse_batched(double* A, int64_t n, int64_t lda, int64_t s
             if (k + 1 < nt) {
                 KQ_TRY(focus_gather(k));
                 ready_at = ++q->signalled;
-                hipLaunchKernelGGL(gj_signal_kernel, dim3(1), dim3(64), 0, sm, q->ready, ready_at);
-                KQ_TRY(check_launch("gj_signal"));
-                KQ_TRY(pivot(k + 1, ready_at));
+                // the wide update's launch releases the counter: enqueue it before the pivot that waits
+                KQ_TRY(wide_update(k, ready_at));
+            } else if (nt > 1) {
+                KQ_TRY(wide_update(k, 0));
             }
+            // the write-back first, while the previous wide update drains and before this one fills
+            // the chip, then the pivot, so that only T_{k+1} runs beside the update
             KQ_TRY(scatter(k, sb));
-            if (k + 1 < nt) KQ_TRY(tprod(k + 1));
+            if (k + 1 < nt) {
+                KQ_TRY(pivot(k + 1, ready_at));
+                KQ_TRY(tprod(k + 1));
+            }
             KQ_HIP(hipEventRecord(evB[nxt], sb));
-            if (nt > 1) KQ_TRY(wide_update(k));
         }
     } else {
         for (int64_t k = 0; k < nt; k++) {
@@ -944,7 +951,7 @@ static kq_status gj_inverse_batched(double* A, int64_t n, int64_t lda, int64_t s
             // are outside both the update and the gather), then the rest of step k's update
             KQ_TRY(scatter(k, sm));
             KQ_HIP(hipStreamWaitEvent(sm, evS[cur], 0));
-            if (nt > 1) KQ_TRY(wide_update(k));
+            if (nt > 1) KQ_TRY(wide_update(k, 0));
         }
     }
     KQ_HIP(hipEventRecord(evM, sm));

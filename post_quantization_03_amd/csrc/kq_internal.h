@@ -76,6 +76,8 @@ struct GemmArgs {
                        // (every work-group reads only the rows of A that it writes)
     int stagger;       // fp64, alpha = -1 and beta = 1: every other work-group reads its tile of C before
                        // the product instead of after it, so the tiles' reads of C spread over the launch
+    uint64_t* signal;  // fp64: when set, the first work-group stores signal_value there as the launch
+    uint64_t signal_value;  // starts (after the kernels before it on the queue have completed)
 };
 
 template <typename T>
