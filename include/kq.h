@@ -119,7 +119,10 @@ kq_status kq_rotate_in(const void* Win, kq_dtype wdt, int64_t ldwin, float* Wout
  * two extra queues of the device, forked from and joined back into `stream`. The call returns
  * only after the first step has completed on the device: it reads back that step's interval
  * bounds (nbk doubles) and launches exactly the further steps they imply; the rest is
- * asynchronous on `stream`. Not for graph capture.
+ * asynchronous on `stream`. Not for graph capture. The sweep's pivot kernels wait on the device
+ * for the other queue's work; where the device runs kernels one at a time (some profilers), that
+ * wait runs out in the first step and the call redoes its work with queue waits, once per
+ * process and device.
  * Sinv may be NULL. info (device int32): 0; k in 1..o if H_G (or an iterate) is not positive
  * definite (k = 1 + index of the failing pivot); o + 1 if the iteration did not converge; -1 if a
  * device-side hand-over between the sweep's queues timed out (an internal error; S is then
