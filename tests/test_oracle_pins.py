@@ -595,3 +595,51 @@ def test_golden_regression_small_layer():
     assert hashlib.sha256(r["words"].tobytes()).hexdigest() == g["words_sha256"]
     assert np.isclose(r["loss"], g["loss"], rtol=1e-9)
     assert np.isclose(r["score"], g["score"], rtol=1e-12)
+
+
+# ----------------------------------------------------------------------------- P18: hand-worked values
+def test_p18_hessian_hand_worked():
+    """H_X = X^T X / n, the second moment of the calibration inputs over the token count (review page,
+    Background: the input activation covariance as the layer-Hessian proxy). Worked by hand for two
+    tokens x_1 = (1, 2), x_2 = (3, -1): X^T X = [[1 + 9, 2 - 3], [2 - 3, 4 + 1]] = [[10, -1], [-1, 5]],
+    divided by n = 2. Dividing by n - 1, not dividing, or centring the tokens fails."""
+    X = np.array([[1.0, 2.0], [3.0, -1.0]])
+    assert np.array_equal(kq.hessian(X), np.array([[5.0, -0.5], [-0.5, 2.5]]))
+    # three tokens, one channel: (4 + 1 + 16) / 3 = 7
+    assert np.array_equal(kq.hessian(np.array([[2.0], [-1.0], [4.0]])), np.array([[7.0]]))
+    # the input dtype is widened exactly: bf16-representable values give the same result
+    assert kq.hessian(np.array([[0.5, 0.25]], dtype=np.float32)).dtype == np.float64
+
+
+def test_p18_damping_hand_worked():
+    """lambda = damp * mean(diag H) (GPTQ damping, 1 % of the average diagonal; the workloads' own
+    statement for the smallest layer). H = diag(1, 2, 3, 6): mean diag = 3, so lambda = 0.03 at
+    damp 0.01; 0.01 * max diag (0.06) or 0.01 * trace (0.12) fails. Only the diagonal moves."""
+    H = np.diag([1.0, 2.0, 3.0, 6.0])
+    Hd, lam = kq.damped(H)
+    assert np.isclose(lam, 0.03, rtol=0, atol=1e-15)
+    assert np.allclose(Hd, np.diag([1.03, 2.03, 3.03, 6.03]), rtol=0, atol=1e-15)
+    A = np.array([[4.0, 1.0], [1.0, 2.0]])
+    Ad, lam = kq.damped(A, 0.1)
+    assert np.isclose(lam, 0.3, rtol=0, atol=1e-15)
+    assert np.allclose(Ad, [[4.3, 1.0], [1.0, 2.3]], rtol=0, atol=1e-15)
+
+
+def test_p18_trace_forms_hand_worked():
+    """tr(H_G) in the three storage forms (review page, Method (2): the score tr(H_G) tr(H_X)). Diagonal
+    (1, 2, 3): 6. Two blocks [[1, 5], [7, 2]] and [[3, 0], [0, 4]]: 1 + 2 + 3 + 4 = 10 (off-diagonal
+    entries do not count). Full: the same matrix block-diagonal in dense form, 10."""
+    assert kq.trace_form(np.array([1.0, 2.0, 3.0]), "diag") == 6.0
+    blocks = np.array([[[1.0, 5.0], [7.0, 2.0]], [[3.0, 0.0], [0.0, 4.0]]])
+    assert kq.trace_form(blocks, "block") == 10.0
+    assert kq.trace_form(kq.form_dense(blocks, "block"), "full") == 10.0
+    # the score: tr(H_G) = 1 + 3 = 4 and tr(H_X) = 5 + 2.5 = 7.5 for the two tokens above
+    X = np.array([[1.0, 2.0], [3.0, -1.0]])
+    assert kq.sensitivity(kq.hessian(X), np.array([1.0, 3.0]), "diag") == 30.0
+    hb = np.array([[[1.0, 9.0], [9.0, 3.0]]])
+    assert kq.sensitivity(kq.hessian(X), hb, "block") == 30.0
+    # storage forms of one dense matrix keep the trace only when nothing is dropped from the diagonal
+    rng = np.random.default_rng(18)
+    H = spd(rng, 8)
+    for form in ("diag", "block", "full"):
+        assert np.isclose(kq.trace_form(kq.hg_forms(H, form, 4), form), np.trace(H), rtol=1e-14)
