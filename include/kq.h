@@ -15,17 +15,23 @@
  *    (elements) >= the row length; leading dimensions and base pointers must be multiples of
  *    4 elements / 16 bytes.
  *  - Every pointer is a DEVICE pointer unless stated otherwise. The caller owns every buffer; the
- *    library allocates no device memory. Scratch memory comes from the caller's workspace
- *    (ws, ws_bytes), sized by kq_workspace_bytes(); a call with a smaller workspace returns
- *    KQ_EWORKSPACE and enqueues nothing.
+ *    library never allocates device memory (no hipMalloc or allocating library routine). Scratch
+ *    memory comes from the caller's workspace (ws, ws_bytes), sized by kq_workspace_bytes(); a call
+ *    with a smaller workspace returns KQ_EWORKSPACE and enqueues nothing.
  *  - Calls validate their arguments on the host, enqueue their kernels on `stream` (a
- *    hipStream_t; NULL = the default stream) and return without synchronising the host. Errors
- *    found on the host are returned; numerical failures found on the device (a matrix that is
- *    not positive definite) are written to a device int32 `info` (0 = success) that the caller
- *    reads after synchronising the stream.
+ *    hipStream_t; NULL = the default stream) and return without synchronising the host, except
+ *    kq_hg_sqrt (block and full forms) and kq_hg_lowrank: they wait once, after the first
+ *    Denman-Beavers step, to read back the interval bounds that fix the number of further steps,
+ *    and they refuse (KQ_EINVAL) a stream that is capturing a HIP graph. Errors found on the host
+ *    are returned; numerical failures found on the device (a matrix that is not positive definite)
+ *    are written to a device int32 `info` (0 = success) that the caller reads after synchronising
+ *    the stream.
  *  - Results are deterministic: fixed reduction orders, no order-dependent atomics.
- *  - No C++ exception crosses the ABI. The library keeps no state between calls and is safe to
- *    call from several host threads on different streams.
+ *  - No C++ exception crosses the ABI. Calls keep no data between them and are safe to call from
+ *    several host threads on different streams. Per device, the square root's pipelined sweep uses
+ *    two queues and nine events of the library's own (default priority), created on the device's
+ *    first such call and kept until the process ends; they carry no data from one call to the next,
+ *    and one mutex orders the enqueueing of concurrent calls on them.
  */
 #ifndef KQ_H
 #define KQ_H
@@ -116,32 +122,38 @@ kq_status kq_rotate_in(const void* Win, kq_dtype wdt, int64_t ldwin, float* Wout
  * full (o x o). Diagonal: elementwise square root. Block and full: scaled Denman-Beavers
  * iteration in fp64 whose SPD inverses are symmetric block Gauss-Jordan sweeps, stopped on a
  * device-side convergence test (at most 7 steps; enough for cond(H_G) <= 1e16). The sweep runs on
- * two extra queues of the device, forked from and joined back into `stream`. The call returns
- * only after the first step has completed on the device: it reads back that step's interval
- * bounds (nbk doubles) and launches exactly the further steps they imply; the rest is
- * asynchronous on `stream`. Not for graph capture. The sweep's pivot kernels wait on the device
- * for the other queue's work; where the device runs kernels one at a time (some profilers), that
- * wait runs out in the first step and the call redoes its work with queue waits, once per
- * process and device.
+ * the two queues of the device named above, forked from and joined back into `stream`. The call
+ * returns only after the first step has completed on the device: it reads back that step's
+ * interval bounds (nbk doubles) and launches exactly the further steps they imply; the rest is
+ * asynchronous on `stream`. A stream that is capturing a graph is refused (KQ_EINVAL). The sweep's
+ * pivot kernels wait on the device, in a bounded loop, for the other queue's work, through a counter
+ * in the call's workspace; where the device runs kernels one at a time (some profilers), that wait
+ * runs out in the first step, and the call then redoes its work with queue waits and leaves a notice
+ * in kq_last_error() (which the call clears when it starts). Nothing of this is kept for later calls.
  * Sinv may be NULL. info (device int32): 0; k in 1..o if H_G (or an iterate) is not positive
  * definite (k = 1 + index of the failing pivot); o + 1 if the iteration did not converge; -1 if a
- * device-side hand-over between the sweep's queues timed out (an internal error; S is then
- * invalid). The caller may free HG once the work has completed in stream order (H_G is only
- * needed transiently).
+ * device-side wait ran out after the first step (the device stopped running the two queues side by
+ * side during the call; S is then invalid and the call should be issued again). The caller may free
+ * HG once the work has completed in stream order (H_G is only needed transiently).
  */
 kq_status kq_hg_sqrt(const float* HG, kq_hg_form form, int64_t o, int64_t blk, float* S, float* Sinv,
                      int32_t* info, void* ws, size_t ws_bytes, kq_stream stream);
 
 /*
- * Output-side transform: W <- V S W with V = H_o D_t / sqrt(o) applied along the output axis
- * (columns of the row-major W). S in the storage form given (from kq_hg_sqrt).
+ * Output-side transform (review page, Method (1): on the output side the weights are transformed by
+ * H_G^{1/2} and then rotated; KronQ abstract: the incoherence rotation extended to the output
+ * dimension): W <- V S W with V = H_o D_t / sqrt(o) applied along the output axis (columns of the
+ * row-major W), so that the loss tr(H_G dW H_X dW^T) becomes the GPTQ loss of the new coordinates
+ * (review page, Key idea). S in the storage form given (from kq_hg_sqrt).
  * W: o x i fp32, leading dimension ldw, in place. sign_out: o int8 values +-1.
  */
 kq_status kq_rotate_out(float* W, int64_t o, int64_t i, int64_t ldw, const float* S, kq_hg_form form,
                         int64_t blk, const int8_t* sign_out, void* ws, size_t ws_bytes, kq_stream stream);
 
 /*
- * Damped factor of the inverse Hessian (GPTQ's Cholesky form of H^{-1}).
+ * Damped factor of the inverse Hessian (review page, Prior limitations: GPTQ's column-wise OBS update
+ * built on H_X alone, which KronQ keeps unchanged; its Cholesky form of H^{-1} with the usual 1 %
+ * damping, the damping the smallest workload states).
  *     lambda = damp * mean(diag HX),   H = HX + lambda I,   R upper-triangular, H^{-1} = R^T R
  * computed without forming H^{-1}: with J the reversal permutation, J H J = L L^T (Cholesky) and
  * R = J L^{-1} J. The factorisation and the triangular inverse run in fp64 (MFMA); R is rounded to
@@ -202,6 +214,7 @@ kq_status kq_quantize_layer_search(float* W, int64_t o, int64_t i, int64_t ldw, 
 kq_status kq_block_order(const double* H, int64_t i, int64_t ldh, int64_t width, int32_t* order, kq_stream stream);
 
 /*
+ * Block permutation for the trace-sorted order above (H_Z-PTQ page, Weight scales and rounding):
  * out block k = in block perm[k], for column blocks (axis 0) or row blocks (axis 1) of a rows x cols
  * row-major matrix of 4- or 8-byte elements (leading dimensions ldi, ldo; in and out must differ).
  * perm: device int32, one entry per block of `width` elements.
@@ -218,7 +231,9 @@ kq_status kq_sensitivity(const double* HX, int64_t i, int64_t ldh, const float* 
                          int64_t blk, double* score, kq_stream stream);
 
 /*
- * Verification: dequantized weights in the original coordinates,
+ * Verification: dequantized weights in the original coordinates (review page, Limitations (3): the
+ * stored weights live in the transformed coordinates, and the orthogonal transforms and H_G^{1/2} are
+ * reverted to recover the layer; Method (1) for the transforms themselves),
  *     What = S^{-1} V^T Q U^T
  * Q: o x i fp32 (the w^ output of kq_quantize_layer), leading dimension ldq; What: o x i fp32,
  * leading dimension ldw (must not alias Q). Sinv in the storage form of H_G.
@@ -271,6 +286,8 @@ kq_status kq_hg_extract(const double* H, int64_t o, int64_t ldh, kq_hg_form form
  * optionally Sinv and HGhat = H^ (may be NULL); sigma (may be NULL): two doubles {sigma, tr H}.
  * info (device int32): 0; 1 the range basis lost rank; 2 sigma <= 0; 3 the k x k square root failed.
  * Work in fp64 (G widened once). Workspace: kq_workspace_bytes(KQ_OP_HG_LOWRANK, o, k, n, ...).
+ * The k x k root is kq_hg_sqrt's iteration, so this call too returns only after its first step has
+ * completed on the device, and refuses a stream that is capturing a graph (KQ_EINVAL).
  */
 kq_status kq_hg_lowrank(const float* G, int64_t n, int64_t o, int64_t ldg, int64_t k, int q, const float* omega,
                         float* S, float* Sinv, float* HGhat, double* sigma, int32_t* info, void* ws, size_t ws_bytes,
@@ -288,8 +305,9 @@ kq_status kq_kfac_loss(const void* W, kq_dtype wdt, int64_t ldw, const float* Wh
                        void* ws, size_t ws_bytes, kq_stream stream);
 
 /*
- * Cross-covariance of two token matrices, C <- beta C + alpha A^T B (d x d fp64, leading dimension d),
- * for the input-drift correction below (A = X the full-precision inputs, B = X~ the drifted ones,
+ * Cross-covariance of two token matrices (KronQ review page, Prior limitations: GPTAQ's correction of
+ * the input drift that quantizing earlier layers causes), C <- beta C + alpha A^T B (d x d fp64,
+ * leading dimension d), for the input-drift correction below (A = X the full-precision inputs, B = X~ the drifted ones,
  * alpha = 1/n). A, B: n x d fp32 or bf16 (dt), leading dimensions lda, ldb. fp64 accumulation (rows
  * widened in chunks of 8192). Workspace: kq_workspace_bytes(KQ_OP_CROSS, 0, d, n, ...).
  */
@@ -311,8 +329,10 @@ kq_status kq_drift_target(const void* W, kq_dtype wdt, int64_t ldw, int64_t o, i
                           kq_stream stream);
 
 /*
- * Verification: layer loss in rotated coordinates, sum_r (Q - W2)_r HX2 (Q - W2)_r^T, which equals
- * tr(H_G dW H_X dW^T) in the original coordinates when HX2 is the rotated, undamped H_X.
+ * Verification: layer loss in rotated coordinates (review page, Background: the Kronecker-factored
+ * loss tr(H_G dW H_X dW^T); Key idea: in the transformed coordinates it is the plain GPTQ loss),
+ * sum_r (Q - W2)_r HX2 (Q - W2)_r^T, which equals tr(H_G dW H_X dW^T) in the original coordinates
+ * when HX2 is the rotated, undamped H_X.
  * W2, Q: o x i fp32 (leading dimension ldw); HX2: i x i fp64 (leading dimension ldh).
  * row_loss (may be NULL): o doubles; loss: one device double.
  */
@@ -335,7 +355,8 @@ kq_status kq_allocate_bits(const double* scores, const int64_t* sizes, int64_t c
 /* Text of a status code; thread-local detail of the last error on this host thread. */
 const char* kq_strerror(kq_status status);
 const char* kq_last_error(void);
-/* Hadamard decomposition used for dimension d: returns m (and 2^k in *pow2), or 0 if unsupported. */
+/* Hadamard decomposition used for dimension d (review page, "Where this paper sits": the random
+ * Hadamard rotations): returns m (and 2^k in *pow2), or 0 if unsupported. */
 int64_t kq_hadamard_order(int64_t d, int64_t* pow2);
 int kq_version(void);
 

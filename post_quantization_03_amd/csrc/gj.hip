@@ -319,16 +319,20 @@ __device__ inline int inv4_spd(double D[4][4]) {
 // With `ready` set the kernel is launched ahead of the kernel that writes its pivot block: it first
 // waits, in a bounded loop, until ready[0] reaches `ready_at` (stored by the first work-group of the
 // next kernel on that queue, which starts only once that kernel has completed and released its
-// writes), then acquires at device scope before reading the block. A wait that runs
-// out (only when the device runs kernels one at a time) sets ready[1], which ends every later wait
-// at once, and info = -1; the block is inverted as found and the host redoes the call.
+// writes), then acquires at device scope before reading the block. A wait that runs out (only when
+// the device runs kernels one at a time) sets ready[1], which ends every later wait of the same call
+// at once, and info = -1; the block is inverted as found. `ready` belongs to one call (its workspace):
+// the host reads ready[1] after the call's first step and redoes that call with queue waits.
 constexpr int GJ_WAIT_POLLS = 1 << 20;  // at most about a second of polling
-// The limit can be lowered through the environment (KQ_SWEEP_WAIT_POLLS, read on each sweep), so
-// that a test can make the wait run out on purpose and check the fallback.
-static int gj_wait_polls() {
+// The limit can be lowered through the environment (KQ_SWEEP_WAIT_POLLS, read on each sweep; from the
+// Denman-Beavers step KQ_SWEEP_WAIT_FROM_STEP on, 0 by default), so that a test can make the wait run
+// out on purpose, in the first step or in a later one, and check what the call does then.
+static int gj_wait_polls(int step) {
     const char* e = std::getenv("KQ_SWEEP_WAIT_POLLS");
+    const char* f = std::getenv("KQ_SWEEP_WAIT_FROM_STEP");
     const long v = e ? std::strtol(e, nullptr, 10) : 0;
-    return v > 0 && v < GJ_WAIT_POLLS ? (int)v : GJ_WAIT_POLLS;
+    const long from = f ? std::strtol(f, nullptr, 10) : 0;
+    return v > 0 && v < GJ_WAIT_POLLS && step >= from ? (int)v : GJ_WAIT_POLLS;
 }
 // Early-launched pivots occupy one compute unit per item while they wait: only for small batches,
 // so that the kernels they wait for always find compute units.
@@ -763,19 +767,28 @@ __global__ __launch_bounds__(256) void gj_scatter_kernel(double* __restrict__ A,
 // `main` the wide rank-128 updates. Events order both with the caller's stream; the mutex keeps the
 // event sequence of one call intact when several host threads enqueue at once. The events only order
 // work of the one device, so they take a device-scope release (no system-scope fence when recorded).
-// `ready` is a device counter that only grows (one release store per signalled step, value
-// `signalled`, kept on the host under the mutex), which pivot kernels launched early wait on.
+// The queues and events are created on a device's first sweep and kept until the process ends; they
+// hold no data of any call.
 struct SweepQueues {
     hipStream_t side = nullptr, main = nullptr;
     hipEvent_t ev[9] = {};
-    uint64_t* ready = nullptr;  // [0] the counter, [1] set when a wait on it ran out
-    uint64_t signalled = 0;
-    bool early = true;          // pivots launched ahead (cleared for good once a wait ran out)
     bool gf_lds = false;        // the fused gather's LDS size has been allowed on this device
     bool ok = false;
 };
 static std::mutex g_sweep_mu;
 static SweepQueues g_sweep[64];
+
+// Hand-over state of one call's sweeps. `ready` lives in the call's workspace and is zeroed on the
+// caller's stream when the call starts: [0] is a counter that only grows within the call (one store
+// per signalled step, value `signalled`, kept on the host), which pivot kernels launched early wait
+// on; [1] is set by a pivot whose wait ran out. `early` selects the device-side hand-over; without
+// it the queues wait on events.
+struct SweepSync {
+    uint64_t* ready = nullptr;
+    uint64_t signalled = 0;
+    bool early = true;
+    int step = 0;               // Denman-Beavers step of the sweep being enqueued
+};
 
 static kq_status sweep_queues(SweepQueues** out) {
     int dev = -1;
@@ -788,10 +801,6 @@ static kq_status sweep_queues(SweepQueues** out) {
         for (hipEvent_t& e : q.ev)
             if (hipEventCreateWithFlags(&e, hipEventDisableTiming | hipEventDisableSystemFence) != hipSuccess)
                 return fail(KQ_EHIP, "sweep queues: event creation failed");
-        if (hipMalloc(reinterpret_cast<void**>(&q.ready), 2 * sizeof(uint64_t)) != hipSuccess ||
-            hipMemsetAsync(q.ready, 0, 2 * sizeof(uint64_t), q.side) != hipSuccess ||
-            hipStreamSynchronize(q.side) != hipSuccess)
-            return fail(KQ_EHIP, "sweep queues: counter set-up failed");
         q.ok = true;
     }
     *out = &q;
@@ -825,7 +834,7 @@ static kq_status sweep_queues(SweepQueues** out) {
 // stream waits for both at the end.
 static kq_status gj_inverse_batched(double* A, int64_t n, int64_t lda, int64_t sA, int64_t batch, double* const C[2],
                                     double* const T[2], double* const Pinv[2], int32_t* info, const int* skip,
-                                    hipStream_t st) {
+                                    SweepSync* sync, hipStream_t st) {
     if (batch > 65535) return fail(KQ_ESHAPE, "sweep batch too large");
     const int64_t sC = n * GJ_NB;
     const int64_t nt = (n + GJ_NB - 1) / GJ_NB;
@@ -845,12 +854,12 @@ static kq_status gj_inverse_batched(double* A, int64_t n, int64_t lda, int64_t s
         hipLaunchKernelGGL(gj_gather_kernel, gr, dim3(256), 0, qg, A, n, lda, sA, k0, nbk, C[b], sC, Tp, p0, k0, skip);
         return check_launch("gj_gather");
     };
-    const int polls = gj_wait_polls();
+    const int polls = gj_wait_polls(sync ? sync->step : 0);
     // side queue: Pinv_k (waiting on the device counter for `ready_at` when given), T_k = C_k Pinv_k
     auto pivot = [&](int64_t k, uint64_t ready_at) -> kq_status {
         const int b = (int)(k & 1), nbk = nb_of(k);
         hipLaunchKernelGGL(gj_pivot_kernel, dim3((unsigned)batch), dim3(GJ_PIV_THREADS), 0, sb, C[b], sC, k * GJ_NB,
-                           nbk, Pinv[b], info, skip, ready_at ? q->ready : nullptr, ready_at, polls);
+                           nbk, Pinv[b], info, skip, ready_at ? sync->ready : nullptr, ready_at, polls);
         return check_launch("gj_pivot");
     };
     auto tprod = [&](int64_t k) -> kq_status {
@@ -873,7 +882,7 @@ static kq_status gj_inverse_batched(double* A, int64_t n, int64_t lda, int64_t s
         u.nb1 = batch; u.sA1 = sC; u.sB1 = sC; u.sC1 = sA; u.tri = 1; u.skip = skip; u.skip_tile = k;
         u.skip_tile2 = k + 1 < nt ? k + 1 : -1;
         u.stagger = 1;
-        if (ready_at) { u.signal = q->ready; u.signal_value = ready_at; }
+        if (ready_at) { u.signal = sync->ready; u.signal_value = ready_at; }
         return gemm<double>(u, false, true, sm);
     };
     // whole 128-wide blocks: the row and column update of the next pivot and its gather are one kernel
@@ -895,7 +904,7 @@ static kq_status gj_inverse_batched(double* A, int64_t n, int64_t lda, int64_t s
     KQ_TRY(pivot(0, 0));
     KQ_TRY(tprod(0));
     KQ_HIP(hipEventRecord(evB[0], sb));
-    if (fused && batch <= GJ_EARLY_PIVOT_MAX && q->early) {
+    if (fused && batch <= GJ_EARLY_PIVOT_MAX && sync && sync->early && sync->ready) {
         // Step k: main queue: (T_k and the write-back of step k - 1 done) the fused row/column update
         // and gather, then the wide update, whose start releases the counter. Side queue: pivot k + 1,
         // launched at once so its work-groups hold their compute units before the wide update is
@@ -909,7 +918,7 @@ static kq_status gj_inverse_batched(double* A, int64_t n, int64_t lda, int64_t s
             uint64_t ready_at = 0;
             if (k + 1 < nt) {
                 KQ_TRY(focus_gather(k));
-                ready_at = ++q->signalled;
+                ready_at = ++sync->signalled;
                 // the wide update's launch releases the counter: enqueue it before the pivot that waits
                 KQ_TRY(wide_update(k, ready_at));
             } else if (nt > 1) {
@@ -957,25 +966,6 @@ static kq_status gj_inverse_batched(double* A, int64_t n, int64_t lda, int64_t s
     KQ_HIP(hipEventRecord(evM, sm));
     KQ_HIP(hipStreamWaitEvent(st, evM, 0));
     KQ_HIP(hipStreamWaitEvent(st, evB[nt & 1], 0));
-    return KQ_OK;
-}
-
-// After work that ran sweeps has been synchronised: true when a pivot's device-side wait ran out
-// in it (the device ran the queues one kernel at a time). The device's sweeps then use queue waits
-// from here on, and the caller redoes the work.
-static kq_status sweep_wait_failed(bool* failed) {
-    std::lock_guard<std::mutex> lock(g_sweep_mu);
-    SweepQueues* q = nullptr;
-    KQ_TRY(sweep_queues(&q));
-    uint64_t f = 0;
-    KQ_HIP(hipMemcpyAsync(&f, q->ready + 1, sizeof(f), hipMemcpyDeviceToHost, q->side));
-    KQ_HIP(hipStreamSynchronize(q->side));
-    *failed = f != 0;
-    if (f) {
-        q->early = false;
-        KQ_HIP(hipMemsetAsync(q->ready + 1, 0, sizeof(uint64_t), q->side));
-        KQ_HIP(hipStreamSynchronize(q->side));
-    }
     return KQ_OK;
 }
 
@@ -1190,6 +1180,7 @@ static void hg_layout(Ar& a, int64_t n, int64_t nbk) {
     a.template take<int32_t>(items);                         // per-item info
     a.template take<double>(2 * DB_UPD_BLOCKS);              // partial sums
     a.template take<int>(4);                                 // flags
+    a.template take<uint64_t>(2);                            // sweep hand-over counter and ran-out word
 }
 
 }  // namespace kq
@@ -1209,7 +1200,7 @@ size_t hg_sqrt_ws(kq_hg_form form, int64_t o, int64_t blk) {
 // fp64 at *Y64 (Z at *Y64 + nbk n^2). info: 0, or o_info + 1 when the iteration did not converge
 // or a matrix is not positive definite.
 static kq_status db_sqrt(const float* HGf, const double* HGd, int64_t n, int64_t nbk, int32_t o_info, int32_t* info,
-                         void* ws, size_t ws_bytes, double** Y64, hipStream_t st) {
+                         void* ws, size_t ws_bytes, double** Y64, hipStream_t st, bool early = true) {
     Arena ar(ws, ws_bytes);
     const size_t nn = (size_t)n * n, items = 2 * (size_t)nbk;
     double* YZ = ar.take<double>(items * nn);
@@ -1227,9 +1218,14 @@ static kq_status db_sqrt(const float* HGf, const double* HGd, int64_t n, int64_t
     int32_t* finfo = ar.take<int32_t>(items);
     double* part = ar.take<double>(2 * DB_UPD_BLOCKS);
     int* flags = ar.take<int>(4);
+    uint64_t* ready = ar.take<uint64_t>(2);
     const int* done = flags;
+    SweepSync sync;
+    sync.ready = ready;
+    sync.early = early;
 
     KQ_TRY(fill<int>(reinterpret_cast<int*>(info), 1, 0, st));
+    KQ_TRY(fill<int>(reinterpret_cast<int*>(ready), 4, 0, st));
     KQ_TRY(fill<int>(reinterpret_cast<int*>(finfo), items, 0, st));
     const unsigned eb = (unsigned)((nbk * nn + 255) / 256 < 4096 ? (nbk * nn + 255) / 256 : 4096);
     if (HGd) hipLaunchKernelGGL(db_init_kernel<double>, dim3(eb), dim3(256), 0, st, HGd, n, nbk, YZ, flags);
@@ -1245,11 +1241,12 @@ static kq_status db_sqrt(const float* HGf, const double* HGd, int64_t n, int64_t
         // the first step inverts Y_0 = A only (Z_0 = I); later steps find Y and Z in NI already
         // (written there by the previous step's update)
         const size_t inv_items = it == 0 ? (size_t)nbk : items;
+        sync.step = it;
         if (it == 0) {
             hipLaunchKernelGGL(copy_d_kernel, dim3(cb), dim3(256), 0, st, YZ, NI, inv_items * nn, done);
             KQ_TRY(check_launch("db_copy"));
         }
-        KQ_TRY(gj_inverse_batched(NI, n, n, (int64_t)nn, (int64_t)inv_items, C, T, Pinv, finfo, done, st));
+        KQ_TRY(gj_inverse_batched(NI, n, n, (int64_t)nn, (int64_t)inv_items, C, T, Pinv, finfo, done, &sync, st));
         // ||A^{-1}||_F of Y_0 = A (first step only; NI holds -A^{-1})
         hipLaunchKernelGGL(sym_norm_part_kernel, dim3(parts, (unsigned)nbk), dim3(256), 0, st, NI, n, (int64_t)nn,
                            nrmI, flags, 0);
@@ -1269,12 +1266,19 @@ static kq_status db_sqrt(const float* HGf, const double* HGd, int64_t n, int64_t
             // instead of sweeps that would only skip.
             std::vector<double> hb((size_t)nbk);
             int hf[4] = {0, 0, 0, 0};
+            uint64_t ran_out = 0;
             KQ_HIP(hipMemcpyAsync(hb.data(), bnd, (size_t)nbk * sizeof(double), hipMemcpyDeviceToHost, st));
             KQ_HIP(hipMemcpyAsync(hf, flags, sizeof(hf), hipMemcpyDeviceToHost, st));
+            KQ_HIP(hipMemcpyAsync(&ran_out, ready + 1, sizeof(ran_out), hipMemcpyDeviceToHost, st));
             KQ_HIP(hipStreamSynchronize(st));
-            bool failed = false;
-            KQ_TRY(sweep_wait_failed(&failed));
-            if (failed) return db_sqrt(HGf, HGd, n, nbk, o_info, info, ws, ws_bytes, Y64, st);
+            if (ran_out) {
+                // the device ran the sweep's queues one kernel at a time: redo this call with queue
+                // waits (nothing is kept for later calls)
+                KQ_TRY(db_sqrt(HGf, HGd, n, nbk, o_info, info, ws, ws_bytes, Y64, st, false));
+                set_error("notice: a device-side wait of the square root's sweep ran out; the call was redone "
+                          "with queue waits");
+                return KQ_OK;
+            }
             if (hf[0]) break;  // converged after one step, or stopped on an error (info set)
             int need = 1;
             for (int64_t b = 0; b < nbk; b++) {
@@ -1301,6 +1305,16 @@ static kq_status db_sqrt(const float* HGf, const double* HGd, int64_t n, int64_t
     return KQ_OK;
 }
 
+// The square root reads its first step back to the host, so a stream under graph capture is refused
+// before anything is enqueued.
+kq_status kq::refuse_capture(hipStream_t st, const char* who) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(st, &cs) != hipSuccess) return fail(KQ_EHIP, "%s: stream capture query failed", who);
+    if (cs != hipStreamCaptureStatusNone)
+        return fail(KQ_EINVAL, "%s: the stream is capturing a graph; this call reads back from the device", who);
+    return KQ_OK;
+}
+
 kq_status kq::spd_sqrt_f64(const double* A, int64_t n, int32_t* info, void* ws, size_t ws_bytes, double** Y64,
                            hipStream_t st) {
     if (!ws || ws_bytes < hg_sqrt_ws(KQ_HG_FULL, n, 0)) return fail(KQ_EWORKSPACE, "square root: workspace too small");
@@ -1324,6 +1338,8 @@ extern "C" kq_status kq_hg_sqrt(const float* HG, kq_hg_form form, int64_t o, int
     const int64_t n = form == KQ_HG_FULL ? o : blk, nbk = form == KQ_HG_FULL ? 1 : o / blk;
     if (n > 65535 * (int64_t)GJ_RT) return fail(KQ_ESHAPE, "kq_hg_sqrt: too large");
     if (!ws || ws_bytes < hg_sqrt_ws(form, o, blk)) return fail(KQ_EWORKSPACE, "kq_hg_sqrt: workspace too small");
+    KQ_TRY(refuse_capture(st, "kq_hg_sqrt"));
+    set_error("");
     double* YZ = nullptr;
     KQ_TRY(db_sqrt(HG, nullptr, n, nbk, (int32_t)o, info, ws, ws_bytes, &YZ, st));
     const size_t nn = (size_t)n * n;

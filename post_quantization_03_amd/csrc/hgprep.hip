@@ -241,6 +241,7 @@ extern "C" kq_status kq_hg_lowrank(const float* G, int64_t n, int64_t o, int64_t
     if (q < 0 || q > 15) return fail(KQ_EINVAL, "kq_hg_lowrank: power steps must be in 0..15");
     if (!ws || ws_bytes < hg_lowrank_ws(n, o, k)) return fail(KQ_EWORKSPACE, "kq_hg_lowrank: workspace too small");
     hipStream_t st = hs(stream);
+    KQ_TRY(refuse_capture(st, "kq_hg_lowrank"));
     Arena ar(ws, ws_bytes);
     double* Gd = ar.take<double>((size_t)n * o);
     double* Y = ar.take<double>((size_t)o * k);

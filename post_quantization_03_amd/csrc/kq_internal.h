@@ -123,6 +123,9 @@ int64_t chol_scratch_doubles();
 kq_status spd_sqrt_f64(const double* A, int64_t n, int32_t* info, void* ws, size_t ws_bytes, double** Y64,
                        hipStream_t st);
 
+// KQ_EINVAL when `st` is capturing a HIP graph (for calls that read back from the device).
+kq_status refuse_capture(hipStream_t st, const char* who);
+
 // ------------------------------------------------------------------------------------ helpers
 template <typename T>
 kq_status fill(T* p, size_t count, T value, hipStream_t st, const int* skip = nullptr);

@@ -92,3 +92,41 @@ def test_gradient_rows_match_the_full_hg_draws():
     H = synth.gen_HG(sp).astype(np.float64)
     assert np.abs(G.T @ G / sp.hg_ng - H).max() <= 1e-6 * np.abs(H).max()
     assert synth.gen_omega(sp, 8).shape == (96, 8)
+
+
+HELPERS = {"kq_workspace_bytes", "kq_strerror", "kq_last_error", "kq_version"}
+SECTIONS = ("Background", "Method", "Key idea", "Prior limitations", "Limitations", "Where this paper sits",
+            "Goal", "Sparks", "Weight scales and rounding", "abstract", "Comparison")
+
+
+def header_comments():
+    """{function name: the comment right before its declaration} for every call in include/kq.h."""
+    txt = open(os.path.join(ROOT, "include", "kq.h")).read()
+    out = {}
+    for m in re.finditer(r"/\*(.*?)\*/\s*(?:kq_status|const char\*|int64_t|int|size_t)\s+(kq_[a-z_0-9]+)\s*\(",
+                         txt, flags=re.S):
+        out[m.group(2)] = " ".join(re.sub(r"\n\s*\*", " ", m.group(1)).split())
+    return out
+
+
+def test_every_method_call_cites_a_page_section():
+    """Each call of the method (every declaration but the helpers) names the page section that
+    defines its operation in the comment above it."""
+    comments = header_comments()
+    calls = [n for n in header_functions() if n not in HELPERS and n not in ("kq_strerror", "kq_last_error")]
+    missing = [n for n in calls if n not in comments]
+    assert not missing, f"declarations without a comment: {missing}"
+    uncited = [n for n in calls if "page" not in comments[n] or not any(sec in comments[n] for sec in SECTIONS)]
+    assert not uncited, f"calls whose comment names no page section: {uncited}"
+
+
+def test_header_states_the_library_owned_resources():
+    """The conventions block says what the library keeps per device and which calls read back."""
+    txt = open(os.path.join(ROOT, "include", "kq.h")).read()
+    conv = txt[txt.index("Conventions shared by every call"):txt.index("#ifndef KQ_H")]
+    assert "never allocates device memory" in conv
+    assert "two queues" in conv and "kq_hg_sqrt" in conv and "capturing" in conv
+    src = "".join(open(os.path.join(ROOT, "post_quantization_03_amd", "csrc", f)).read()
+                  for f in os.listdir(os.path.join(ROOT, "post_quantization_03_amd", "csrc")))
+    src = re.sub(r"//[^\n]*", "", src)
+    assert "hipMalloc" not in src and "hipFree" not in src

@@ -163,6 +163,7 @@ def test_hg_sqrt_repeated_calls_identical():
 
 
 _FALLBACK_SCRIPT = r"""
+import os
 import sys
 import numpy as np
 import torch
@@ -176,29 +177,52 @@ hg = synth.gen_HG(synth.scaled(synth.CONFIGS["C2"], o=o, hg_ng=2 * o))
 S_ref, _ = kq.hg_sqrt(hg.astype(np.float64), "full")
 HG = torch.from_numpy(hg).to(dev)
 ws = torch.empty(K.kq_workspace_bytes("hg_sqrt", o, 0, 0, form="full"), dtype=torch.uint8, device=dev)
-for call in range(2):
+
+
+def call(tag):
     S = torch.empty((o, o), dtype=torch.float32, device=dev)
     info = torch.zeros(1, dtype=torch.int32, device=dev)
     K.kq_hg_sqrt(HG, "full", o, 0, S, None, info, ws)
+    note = K.last_error()
     torch.cuda.synchronize()
     err = np.linalg.norm(S.cpu().numpy().astype(np.float64) - S_ref) / np.linalg.norm(S_ref)
-    print(f"call {call}: info {int(info.cpu()[0])} rel err {err:.3e}", flush=True)
-    assert int(info.cpu()[0]) == 0 and err <= 1e-6
+    inf = int(info.cpu()[0])
+    print(f"{tag}: info {inf} rel err {err:.3e} notice {note!r}", flush=True)
+    return inf, err, note
+
+
+# every wait cut to one poll: each call notices after its first step and redoes itself with queue
+# waits (nothing is kept between calls, so the second call does the same)
+os.environ["KQ_SWEEP_WAIT_POLLS"] = "1"
+for c in range(2):
+    inf, err, note = call(f"cut from step 0, call {c}")
+    assert inf == 0 and err <= 1e-6 and "ran out" in note
+# cut only from the second step on: the first step's read-back sees no run-out, a later wait runs out,
+# and the call reports info = -1 (S invalid; the caller re-issues the call)
+os.environ["KQ_SWEEP_WAIT_FROM_STEP"] = "1"
+inf, err, note = call("cut from step 1")
+assert inf == -1 and "ran out" not in note
+# limits restored: the re-issued call matches, with no notice
+del os.environ["KQ_SWEEP_WAIT_POLLS"], os.environ["KQ_SWEEP_WAIT_FROM_STEP"]
+inf, err, note = call("re-issued")
+assert inf == 0 and err <= 1e-6 and note == ""
 print("OK", flush=True)
 """
 
 
 def test_hg_sqrt_falls_back_when_device_wait_runs_out():
     """The sweep's pivot kernels are launched ahead and wait on the device, in a bounded loop, for the
-    other queue's gather. With that bound cut to one poll (KQ_SWEEP_WAIT_POLLS, in a child process,
-    since the switch to queue waits lasts for the process) the first waits run out: the square root
-    notices at its read-back after the first step, redoes the call with queue waits, and still
-    matches the oracle with info 0; a second call does too."""
+    other queue's gather. With that bound cut to one poll (KQ_SWEEP_WAIT_POLLS, in a child process) the
+    first waits run out: the square root notices at its read-back after the first step, redoes the call
+    with queue waits, leaves a notice in kq_last_error and still matches the oracle with info 0; a
+    second call does the same (no state is kept between calls). Cut only from the second step on
+    (KQ_SWEEP_WAIT_FROM_STEP), a later wait runs out and the call reports info = -1; re-issued with the
+    limits restored it matches, with no notice."""
     import os
     import subprocess
     import sys
     root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-    env = dict(os.environ, KQ_SWEEP_WAIT_POLLS="1")
+    env = {k: v for k, v in os.environ.items() if not k.startswith("KQ_SWEEP_WAIT")}
     r = subprocess.run([sys.executable, "-c", _FALLBACK_SCRIPT, root], env=env, capture_output=True, text=True,
                        timeout=180)
     say(r.stdout.strip())
