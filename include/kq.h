@@ -261,6 +261,25 @@ kq_status kq_matvec_quantized(const uint32_t* codes, const float* scale, const f
                               kq_hg_form form, int64_t blk, const float* X, int64_t ldx, int64_t nt, float* Y,
                               int64_t ldy, void* ws, size_t ws_bytes, kq_stream stream);
 
+/* Size of the fixed per-device scratch array of kq_matvec_quantized_static (32 MiB). */
+#define KQ_MATVEC_STATIC_SCRATCH_BYTES (32u << 20)
+
+/*
+ * kq_matvec_quantized without a workspace, for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc. Same arguments (minus ws,
+ * ws_bytes), same kernels and bit-identical results. The scratch comes from a fixed array of
+ * KQ_MATVEC_STATIC_SCRATCH_BYTES per device inside the library, held by every device the library runs
+ * on until the process ends; calls whose kq_workspace_bytes(KQ_OP_MATVEC, o, i, nt, ...) exceeds it
+ * return KQ_EWORKSPACE and enqueue nothing (the workloads of this library fit with up to 16 tokens).
+ * The call allocates nothing. Every call on a device shares that device's array, so calls that overlap
+ * on one device (different streams, or host threads) race: order them on one stream. Nothing in the
+ * array has to start at zero; it keeps the last call's contents.
+ */
+kq_status kq_matvec_quantized_static(const uint32_t* codes, const float* scale, const float* offset, int64_t o,
+                                     int64_t i, int bits, int group, const int8_t* sign_in, const int8_t* sign_out,
+                                     const float* Sinv, kq_hg_form form, int64_t blk, const float* X, int64_t ldx,
+                                     int64_t nt, float* Y, int64_t ldy, kq_stream stream);
+
 /*
  * H_G storage forms from an fp64 covariance H (o x o, leading dimension ldh), e.g. H_G = G^T G / n
  * accumulated from gradient rows by kq_hessian_accum (KronQ review page, Method: the gradient

@@ -18,7 +18,7 @@ EXPORTS = ("kq_workspace_bytes", "kq_hessian_accum", "kq_rotate_in", "kq_hg_sqrt
            "kq_quantize_layer", "kq_sensitivity", "kq_unrotate", "kq_layer_loss", "kq_strerror", "kq_last_error",
            "kq_hadamard_order", "kq_version", "kq_allocate_bits", "kq_matvec_quantized",
            "kq_hg_extract", "kq_hg_lowrank", "kq_kfac_loss", "kq_quantize_layer_search",
-           "kq_block_order", "kq_permute_blocks", "kq_cross_accum", "kq_drift_target")
+           "kq_block_order", "kq_permute_blocks", "kq_cross_accum", "kq_drift_target", "kq_matvec_quantized_static")
 
 
 class KQError(RuntimeError):
@@ -58,6 +58,8 @@ def lib() -> ctypes.CDLL:
                                     _int, ctypes.POINTER(ctypes.c_int32)]),
         "kq_matvec_quantized": (_int, [_vp, _vp, _vp, _i64, _i64, _int, _int, _vp, _vp, _vp, _int, _i64, _vp, _i64, _i64,
                                        _vp, _i64, _vp, _sz, _vp]),
+        "kq_matvec_quantized_static": (_int, [_vp, _vp, _vp, _i64, _i64, _int, _int, _vp, _vp, _vp, _int, _i64, _vp,
+                                              _i64, _i64, _vp, _i64, _vp]),
         "kq_hg_extract": (_int, [_vp, _i64, _i64, _int, _i64, _vp, _vp]),
         "kq_block_order": (_int, [_vp, _i64, _i64, _i64, _vp, _vp]),
         "kq_cross_accum": (_int, [_vp, _vp, _int, _i64, _i64, _i64, _i64, ctypes.c_double, ctypes.c_double, _vp, _vp,
@@ -233,6 +235,16 @@ def kq_matvec_quantized(codes, scale, offset, o: int, i: int, bits: int, group: 
                                                             _p(sign_in), _p(sign_out), _p(Sinv), HG_FORM[form], blk,
                                                             _p(X), X.stride(0), nt, _p(Y), Y.stride(0), w, wb,
                                                             _stream(stream)))
+
+
+def kq_matvec_quantized_static(codes, scale, offset, o: int, i: int, bits: int, group: int, sign_in, sign_out, Sinv,
+                               form: str, blk: int, X, Y, stream=None) -> None:
+    """kq_matvec_quantized on the library's fixed per-device scratch array (no workspace argument)."""
+    nt = X.shape[0]
+    _check("kq_matvec_quantized_static",
+           lib().kq_matvec_quantized_static(_p(codes), _p(scale), _p(offset), o, i, bits, group, _p(sign_in),
+                                            _p(sign_out), _p(Sinv), HG_FORM[form], blk, _p(X), X.stride(0), nt, _p(Y),
+                                            Y.stride(0), _stream(stream)))
 
 
 def kq_hg_extract(H, form: str, blk: int, HG, stream=None) -> None:

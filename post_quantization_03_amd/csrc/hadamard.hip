@@ -12,6 +12,7 @@
 //  - the P_m factor is a dense +-1 contraction, run on the fp32 MFMA GEMM (P is generated on the
 //    device from the finite-field quadratic character).
 #include <cmath>
+#include <mutex>
 
 #include "kq_internal.h"
 
@@ -724,28 +725,40 @@ size_t matvec_ws(int64_t o, int64_t i, int64_t nt, kq_hg_form form) {
     return z.used;
 }
 
-extern "C" kq_status kq_matvec_quantized(const uint32_t* codes, const float* scale, const float* offset, int64_t o,
-                                         int64_t i, int bits, int group, const int8_t* sign_in, const int8_t* sign_out,
-                                         const float* Sinv, kq_hg_form form, int64_t blk, const float* X, int64_t ldx,
-                                         int64_t nt, float* Y, int64_t ldy, void* ws, size_t ws_bytes,
-                                         kq_stream stream) {
+// Host checks of kq_matvec_quantized's arguments (shared with its scratch-array variant); `who` names
+// the entry point in the error text.
+static kq_status matvec_validate(const uint32_t* codes, const float* scale, const float* offset, int64_t o, int64_t i,
+                                 int bits, int group, const int8_t* sign_in, const int8_t* sign_out, const float* Sinv,
+                                 kq_hg_form form, int64_t blk, const float* X, int64_t ldx, int64_t nt, const float* Y,
+                                 int64_t ldy, const char* who) {
     if (!codes || !scale || !offset || !sign_in || !sign_out || !Sinv || !X || !Y)
-        return fail(KQ_EINVAL, "kq_matvec_quantized: null pointer");
+        return fail(KQ_EINVAL, "%s: null pointer", who);
     if (o <= 0 || i <= 0 || nt <= 0 || nt > 65535 || ldx < i || ldy < o)
-        return fail(KQ_ESHAPE, "kq_matvec_quantized: bad sizes");
-    if (bits < 2 || bits > 8) return fail(KQ_EUNSUPPORTED, "kq_matvec_quantized: bits");
-    if (group != 0 && (group % 32 || i % group)) return fail(KQ_EUNSUPPORTED, "kq_matvec_quantized: group");
-    if (i % 32 || (i * bits) % 32) return fail(KQ_ESHAPE, "kq_matvec_quantized: i must be a multiple of 32");
-    if (ldx % 4 || !aligned16(X)) return fail(KQ_EINVAL, "kq_matvec_quantized: X alignment");
-    if (form == KQ_HG_BLOCK && (blk <= 0 || o % blk)) return fail(KQ_ESHAPE, "kq_matvec_quantized: bad block size");
-    if (form != KQ_HG_DIAG && form != KQ_HG_BLOCK && form != KQ_HG_FULL) return fail(KQ_EINVAL, "kq_matvec_quantized: form");
+        return fail(KQ_ESHAPE, "%s: bad sizes", who);
+    if (bits < 2 || bits > 8) return fail(KQ_EUNSUPPORTED, "%s: bits", who);
+    if (group != 0 && (group % 32 || i % group)) return fail(KQ_EUNSUPPORTED, "%s: group", who);
+    if (i % 32 || (i * bits) % 32) return fail(KQ_ESHAPE, "%s: i must be a multiple of 32", who);
+    if (ldx % 4 || !aligned16(X)) return fail(KQ_EINVAL, "%s: X alignment", who);
+    if (form == KQ_HG_BLOCK && (blk <= 0 || o % blk)) return fail(KQ_ESHAPE, "%s: bad block size", who);
+    if (form != KQ_HG_DIAG && form != KQ_HG_BLOCK && form != KQ_HG_FULL) return fail(KQ_EINVAL, "%s: form", who);
     int64_t mo, po, mi, pi;
     Field fo, fi;
     if (!hadamard_split(o, mo, po, fo) || !hadamard_split(i, mi, pi, fi))
-        return fail(KQ_EUNSUPPORTED, "kq_matvec_quantized: no Hadamard order");
-    if (o % 4) return fail(KQ_ESHAPE, "kq_matvec_quantized: o must be a multiple of 4");
-    if (!ws || ws_bytes < matvec_ws(o, i, nt, form)) return fail(KQ_EWORKSPACE, "kq_matvec_quantized: workspace too small");
-    hipStream_t st = hs(stream);
+        return fail(KQ_EUNSUPPORTED, "%s: no Hadamard order", who);
+    if (o % 4) return fail(KQ_ESHAPE, "%s: o must be a multiple of 4", who);
+    return KQ_OK;
+}
+
+// The product itself, on a workspace of at least matvec_ws(o, i, nt, form) bytes. Every scratch slice
+// it uses is written before it is read, so nothing in the workspace has to start at zero.
+static kq_status matvec_run(const uint32_t* codes, const float* scale, const float* offset, int64_t o, int64_t i,
+                            int bits, int group, const int8_t* sign_in, const int8_t* sign_out, const float* Sinv,
+                            kq_hg_form form, int64_t blk, const float* X, int64_t ldx, int64_t nt, float* Y,
+                            int64_t ldy, void* ws, size_t ws_bytes, hipStream_t st) {
+    int64_t mo, po, mi, pi;
+    Field fo, fi;
+    hadamard_split(o, mo, po, fo);
+    hadamard_split(i, mi, pi, fi);
     Arena ar(ws, ws_bytes);
     float* Po = ar.take<float>((size_t)mo * mo);
     float* Pi = ar.take<float>((size_t)mi * mi);
@@ -781,4 +794,60 @@ extern "C" kq_status kq_matvec_quantized(const uint32_t* codes, const float* sca
         g.nb1 = o / blk; g.sA1 = blk; g.sB1 = blk * blk; g.sC1 = blk;
     }
     return gemm<float>(g, false, true, st);
+}
+
+extern "C" kq_status kq_matvec_quantized(const uint32_t* codes, const float* scale, const float* offset, int64_t o,
+                                         int64_t i, int bits, int group, const int8_t* sign_in, const int8_t* sign_out,
+                                         const float* Sinv, kq_hg_form form, int64_t blk, const float* X, int64_t ldx,
+                                         int64_t nt, float* Y, int64_t ldy, void* ws, size_t ws_bytes,
+                                         kq_stream stream) {
+    KQ_TRY(matvec_validate(codes, scale, offset, o, i, bits, group, sign_in, sign_out, Sinv, form, blk, X, ldx, nt, Y,
+                           ldy, "kq_matvec_quantized"));
+    if (!ws || ws_bytes < matvec_ws(o, i, nt, form)) return fail(KQ_EWORKSPACE, "kq_matvec_quantized: workspace too small");
+    return matvec_run(codes, scale, offset, o, i, bits, group, sign_in, sign_out, Sinv, form, blk, X, ldx, nt, Y, ldy, ws,
+                      ws_bytes, hs(stream));
+}
+
+// ------------------------------------------------------------------ the product without a workspace
+// Scratch of kq_matvec_quantized_static: one array per device, part of the library's code object, held
+// by every device the library runs on until the process ends. Host code never passes the array's name
+// to a kernel (on the host it only stands for the symbol): its device address is fetched once per
+// device with hipGetSymbolAddress and kept in g_scratch_ptr, and that address is what the kernels get.
+static __device__ __align__(256) unsigned char scratch[KQ_MATVEC_STATIC_SCRATCH_BYTES];
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[64];
+
+static kq_status scratch_address(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return fail(KQ_EHIP, "kq_matvec_quantized_static: no current device");
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(KQ_EHIP, "kq_matvec_quantized_static: scratch address: %s", hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return KQ_OK;
+}
+
+extern "C" kq_status kq_matvec_quantized_static(const uint32_t* codes, const float* scale, const float* offset,
+                                                int64_t o, int64_t i, int bits, int group, const int8_t* sign_in,
+                                                const int8_t* sign_out, const float* Sinv, kq_hg_form form,
+                                                int64_t blk, const float* X, int64_t ldx, int64_t nt, float* Y,
+                                                int64_t ldy, kq_stream stream) {
+    KQ_TRY(matvec_validate(codes, scale, offset, o, i, bits, group, sign_in, sign_out, Sinv, form, blk, X, ldx, nt, Y,
+                           ldy, "kq_matvec_quantized_static"));
+    const size_t need = matvec_ws(o, i, nt, form);
+    if (need > (size_t)KQ_MATVEC_STATIC_SCRATCH_BYTES)
+        return fail(KQ_EWORKSPACE,
+                    "kq_matvec_quantized_static: o = %lld, i = %lld, %lld tokens need %zu scratch bytes, more than the "
+                    "library's fixed %zu; use kq_matvec_quantized with a workspace, or fewer tokens per call",
+                    (long long)o, (long long)i, (long long)nt, need, (size_t)KQ_MATVEC_STATIC_SCRATCH_BYTES);
+    void* ws = nullptr;
+    KQ_TRY(scratch_address(&ws));
+    return matvec_run(codes, scale, offset, o, i, bits, group, sign_in, sign_out, Sinv, form, blk, X, ldx, nt, Y, ldy, ws,
+                      (size_t)KQ_MATVEC_STATIC_SCRATCH_BYTES, hs(stream));
 }

@@ -116,7 +116,11 @@ def test_every_method_call_cites_a_page_section():
     calls = [n for n in header_functions() if n not in HELPERS and n not in ("kq_strerror", "kq_last_error")]
     missing = [n for n in calls if n not in comments]
     assert not missing, f"declarations without a comment: {missing}"
-    uncited = [n for n in calls if "page" not in comments[n] or not any(sec in comments[n] for sec in SECTIONS)]
+    # the entry point without a workspace names the callers it is for instead of a passage
+    no_alloc = [n for n in calls if "callers that cannot allocate" in comments[n]]
+    assert no_alloc == ["kq_matvec_quantized_static"]
+    uncited = [n for n in calls if n not in no_alloc and
+               ("page" not in comments[n] or not any(sec in comments[n] for sec in SECTIONS))]
     assert not uncited, f"calls whose comment names no page section: {uncited}"
 
 
