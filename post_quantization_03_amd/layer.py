@@ -163,6 +163,7 @@ def quantize_layer(X: torch.Tensor, W: torch.Tensor, HG: torch.Tensor, s: torch.
         What = torch.empty((o, i), **f32)
         K.kq_unrotate(W2, s, t, Sinv, cfg.form, cfg.blk, What, ws)
         loss = torch.empty((1,), dtype=torch.float64, device=dev)
-        K.kq_layer_loss(W2_in, W2, H, None, loss, ws)
-        out.update({"W2": W2_in, "What": What, "loss": loss})
+        loss_rows = torch.empty((o,), dtype=torch.float64, device=dev)
+        K.kq_layer_loss(W2_in, W2, H, loss_rows, loss, ws)
+        out.update({"W2": W2_in, "What": What, "loss": loss, "loss_rows": loss_rows})
     return out

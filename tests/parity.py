@@ -25,20 +25,41 @@ def replay_compare(gpu_codes: np.ndarray, W2: np.ndarray, R: np.ndarray, bits: i
     """Compare GPU codes with the oracle sweep on W2 / R (float64), replaying near-tie flips.
 
     ``rows``: row indices of W2 / gpu_codes to check (all by default). W2 and gpu_codes are indexed by
-    the same row numbers. Returns counts and the oracle codes / outputs after replay for those rows.
-    With ``search`` the grids are chosen by the Hessian-aware search; ``gpu_scale`` (rows x groups)
-    replays the GPU's candidate at every grid, and the candidates' objectives are returned so that
-    the caller can check that choice against the oracle's minimum."""
+    the same row numbers. The oracle first sweeps all those rows at once (rows are independent given
+    R); only rows whose codes differ are then walked one by one with replays. Returns counts and the
+    oracle codes / outputs after replay for those rows. With ``search`` the grids are chosen by the
+    Hessian-aware search; ``gpu_scale`` (rows x groups) replays the GPU's candidate at every grid, and
+    the candidates' objectives are returned so that the caller can check that choice against the
+    oracle's minimum."""
     o, i = gpu_codes.shape
     rows = np.arange(o) if rows is None else np.asarray(rows)
     out = {"replays": 0, "fail": [], "codes": {}, "Q": {}, "row_loss": {}, "mu": {}, "scale": {}, "chosen": {},
-           "objectives": {}}
-    for r in rows:
+           "objectives": {}, "delta": {}, "replayed_rows": []}
+
+    def keep(r, res, k):
+        out["codes"][int(r)] = res["codes"][k]
+        out["Q"][int(r)] = res["Q"][k]
+        out["row_loss"][int(r)] = res["row_loss"][k]
+        out["mu"][int(r)] = res["mu"][k]
+        out["scale"][int(r)] = res["scale"][k]
+        out["delta"][int(r)] = res["delta"][k]
+        if search:
+            out["chosen"][int(r)] = res["chosen"][k]
+            out["objectives"][int(r)] = res["objectives"][k]
+
+    ns_all = None if gpu_scale is None else np.asarray(gpu_scale, np.float64)[rows]
+    first = kq.sweep_blocked(W2[rows], R, bits, group, block, search=search, near_scale=ns_all)
+    for k, r in enumerate(rows):
+        if np.array_equal(first["codes"][k], gpu_codes[r]):
+            keep(r, first, k)
+            continue
+        out["replayed_rows"].append(int(r))
         w = W2[r:r + 1]
         g = gpu_codes[r]
         fm = np.zeros((1, i), bool)
         fc = np.zeros((1, i), np.int64)
         n_rep = 0
+        res = None
         while True:
             ns = None if gpu_scale is None else np.asarray(gpu_scale, np.float64)[r:r + 1]
             res = kq.sweep_blocked(w, R, bits, group, block, force_mask=fm, force_codes=fc, search=search,
@@ -56,15 +77,24 @@ def replay_compare(gpu_codes: np.ndarray, W2: np.ndarray, R: np.ndarray, bits: i
             fc[0, j] = g[j]
             n_rep += 1
         out["replays"] += n_rep
-        out["codes"][int(r)] = res["codes"][0]
-        out["Q"][int(r)] = res["Q"][0]
-        out["row_loss"][int(r)] = res["row_loss"][0]
-        out["mu"][int(r)] = res["mu"][0]
-        out["scale"][int(r)] = res["scale"][0]
-        if search:
-            out["chosen"][int(r)] = res["chosen"][0]
-            out["objectives"][int(r)] = res["objectives"][0]
+        keep(r, res, 0)
     return out
+
+
+def stack_rows(cmp: dict, key: str, rows) -> np.ndarray:
+    return np.stack([cmp[key][int(r)] for r in rows])
+
+
+def grid_steps(gpu_mu: np.ndarray, gpu_scale: np.ndarray, or_mu: np.ndarray, or_scale: np.ndarray, bits: int):
+    """Differences of the grid parameters measured in grid steps of the oracle's grid: |d mu| / s and
+    (2^b - 1) |d s| / s, the largest shift they cause in a pre-rounding value u = (w - mu) / s with u in
+    [0, 2^b - 1]. Groups with s = 0 (every value equal) must match exactly and are left out."""
+    L = 2 ** bits - 1
+    or_scale = np.asarray(or_scale, np.float64)
+    pos = or_scale > 0
+    dmu = np.abs(np.asarray(gpu_mu, np.float64) - or_mu)[pos] / or_scale[pos]
+    ds = L * np.abs(np.asarray(gpu_scale, np.float64) - or_scale)[pos] / or_scale[pos]
+    return (float(dmu.max()) if dmu.size else 0.0), (float(ds.max()) if ds.size else 0.0)
 
 
 def rel_fro(a, b) -> float:

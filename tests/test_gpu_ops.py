@@ -11,7 +11,7 @@ import synth
 from oracle import kronq as kq
 from post_quantization_03_amd import _lib as K
 from tests.gpu_util import host, say, to_dev, torch_dev, ws_tensor
-from tests.parity import gpu_words_to_codes, hx_tol, matvec_error_scale, rel_fro, replay_compare
+from tests.parity import TIE, grid_steps, gpu_words_to_codes, hx_tol, matvec_error_scale, rel_fro, replay_compare
 
 pytestmark = pytest.mark.gpu
 f32 = np.float32
@@ -360,6 +360,9 @@ def test_quantize_layer(o, i, bits, group):
     mu = np.stack([cmp["mu"][k] for k in range(o)])
     sc = np.stack([cmp["scale"][k] for k in range(o)])
     assert rel_fro(host(offset), mu) <= 1e-4 and rel_fro(host(scale), sc) <= 1e-4
+    dmu, ds = grid_steps(host(offset), host(scale), mu, sc, bits)
+    say(f"  grid parameters: |d mu|/s {dmu:.2e}, L |d s|/s {ds:.2e} grid steps")
+    assert dmu <= TIE and ds <= 2 * TIE
 
 
 @pytest.mark.parametrize("o,i,bits,group,cands", [(37, 384, 3, 128, 500), (20, 512, 2, 0, 500), (16, 256, 4, 32, 64),
