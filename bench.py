@@ -208,7 +208,37 @@ def phase_times(sp, X, W, HG, s, t, cfg, ws, reps: int = 3) -> dict:
         torch.cuda.synchronize()
         for k, (name, _) in enumerate(calls):
             res[name].append(ev[k].elapsed_time(ev[k + 1]))
-    return {k: float(np.median(v)) for k, v in res.items()}
+    out = {k: float(np.median(v)) for k, v in res.items()}
+    out["_chain"] = sweep_chain(sp, W2, R, cfg, reps)
+    return out
+
+
+def sweep_chain(sp, W2, R, cfg, reps: int = 3) -> float:
+    """The sweep's dependent chain (ms): kq_quantize_layer on 16 rows alone, i.e. one work-group per
+    128-column block, so the time is the i dependent column steps of a row plus what separates the
+    blocks (launches, the lazy trailing updates). No schedule of the sweep can finish a row sooner."""
+    import torch
+
+    from post_quantization_03_amd import _lib as K
+
+    dev = W2.device
+    rows = 16
+    Wr = W2[:rows].clone()
+    ng = sp.i // cfg.group if cfg.group else 1
+    codes = torch.empty((rows, sp.i * cfg.bits // 32), dtype=torch.int32, device=dev)
+    scale = torch.empty((rows, ng), dtype=torch.float32, device=dev)
+    offset = torch.empty((rows, ng), dtype=torch.float32, device=dev)
+    rl = torch.empty((rows,), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(K.kq_workspace_bytes("quantize", rows, sp.i), 256), dtype=torch.uint8, device=dev)
+    times = []
+    for _ in range(reps + 1):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        K.kq_quantize_layer(Wr, R, cfg.bits, cfg.group, cfg.block, codes, scale, offset, rl, ws)
+        b.record()
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b))
+    return float(np.median(times[1:]))
 
 
 def matvec_times(sp, out, HG, s, t, cfg, reps: int = 200) -> dict:
@@ -539,18 +569,52 @@ def host_list(t) -> list:
     return [int(v) for v in t.cpu().tolist()]
 
 
-def cpu_baseline(sp, budget_s: float = 30.0) -> dict:
-    """The float64 oracle, as it stands, on a bounded sample of the same layer; extrapolated per phase."""
-    from oracle import kronq as kq
-
+def _blas_threads():
     cores = len(os.sched_getaffinity(0))
     try:
         from threadpoolctl import threadpool_limits
         limiter = threadpool_limits(limits=cores)
     except Exception:  # pragma: no cover
         limiter = None
-    n_tok = 2048
-    n_rows = 128
+    return cores, limiter
+
+
+def _time_hessian_rotation(kq, HX, s_in, rows: int = 2048) -> tuple[float, str]:
+    """Seconds of the oracle's H_X' = U^T H_X U: the row pass on at most `rows` rows of H_X, scaled to the
+    i rows, times two (the column pass transforms i columns of the same length)."""
+    i = HX.shape[0]
+    r = min(rows, i)
+    t0 = time.perf_counter()
+    kq._rot(HX[:r], s_in, axis=1)
+    dt = (time.perf_counter() - t0) * i / r * 2
+    return dt, ("in full" if r == i else f"from {r} of {i} rows of one pass")
+
+
+def _time_factor(kq, HX2, damp: float, cap: int = 4096) -> tuple[float, str]:
+    """Seconds of the oracle's damped factor (inverse and Cholesky, O(i^3)): in full up to i = cap, else on
+    the leading cap x cap block of the damped H, scaled by (i / cap)^3."""
+    i = HX2.shape[0]
+    k = min(i, cap)
+    t0 = time.perf_counter()
+    H, _ = kq.damped(HX2[:k, :k], damp)
+    kq.inverse_upper_factor(H)
+    dt = (time.perf_counter() - t0) * (i / k) ** 3
+    return dt, ("in full" if k == i else f"on the leading {k} x {k} block scaled by (i/{k})^3")
+
+
+def cpu_baseline(sp) -> dict:
+    """The float64 oracle, as it stands, on a bounded sample of the same layer (about 10-30 s of CPU work),
+    timed per phase and scaled to the whole layer: H_X on at most 2048 tokens, the input rotation of W on
+    at most 2048 rows (H_X's rotation in full), the output transform on at most 512 columns (all rows:
+    it mixes rows), the sweep on at most 128 rows; the H_G square root and the damped factor in full.
+    Stand-in values (rows of W'U, and an untimed factor of the unrotated H_X) feed the column-sampled output
+    transform and the row-sampled sweep; the oracle's time does not depend on the values. Above 4096 the
+    damped factor is timed on the leading 4096 x 4096 block and scaled by the cube of the width ratio, and
+    the rotation of H_X on 2048 rows of one pass (scaled to both passes)."""
+    from oracle import kronq as kq
+
+    cores, limiter = _blas_threads()
+    n_tok, r_in, c_out, n_rows = min(sp.n, 2048), min(sp.o, 2048), min(sp.i, 512), min(sp.o, 128)
     d = synth.layer_inputs(sp, x_rows=n_tok)
     X = synth.widen(d["X"], sp.x_dtype)
     W = synth.widen(d["W"], sp.w_dtype)
@@ -559,31 +623,182 @@ def cpu_baseline(sp, budget_s: float = 30.0) -> dict:
     t0 = time.perf_counter()
     HX = kq.hessian(X)
     t["hessian"] = (time.perf_counter() - t0) * sp.n / n_tok
+    del X
     t0 = time.perf_counter()
-    W1 = kq.rotate_in_weights(W, d["s"])
-    HX2 = kq.rotate_in_hessian(HX, d["s"])
-    t["rotate_in"] = time.perf_counter() - t0
+    W1 = kq.rotate_in_weights(W[:r_in], d["s"])
+    t["rotate_in"] = (time.perf_counter() - t0) * sp.o / r_in
+    dt, how_rot = _time_hessian_rotation(kq, HX, d["s"])
+    t["rotate_in"] += dt
     t0 = time.perf_counter()
     S, _ = kq.hg_sqrt(HG, sp.hg_form)
     t["hg_sqrt"] = time.perf_counter() - t0
     t0 = time.perf_counter()
-    W2 = kq.rotate_out(W1, S, sp.hg_form, d["t"])
-    t["rotate_out"] = time.perf_counter() - t0
+    kq.rotate_out(W[:, :c_out], S, sp.hg_form, d["t"])
+    t["rotate_out"] = (time.perf_counter() - t0) * sp.i / c_out
+    dt, how_fac = _time_factor(kq, HX, sp.damp)
+    t["cholinv"] = dt
+    # the sweep needs a factor of the whole width: R of the (unrotated) H_X, untimed, stands in for R of H_X'
+    H, _ = kq.damped(HX, sp.damp)
+    R = np.linalg.cholesky(np.linalg.inv(H)).T if sp.i <= 4096 else np.diag(1.0 / np.sqrt(np.diag(H)))
     t0 = time.perf_counter()
-    H, _ = kq.damped(HX2, sp.damp)
-    R = kq.inverse_upper_factor(H)
-    t["cholinv"] = time.perf_counter() - t0
-    t0 = time.perf_counter()
-    kq.sweep_blocked(W2[:n_rows], R, sp.bits, sp.group, sp.block)
+    kq.sweep_blocked(W1[:n_rows], R, sp.bits, sp.group, sp.block)
     t["quantize"] = (time.perf_counter() - t0) * sp.o / n_rows
-    if limiter is not None:
-        limiter.unregister() if hasattr(limiter, "unregister") else None
+    if limiter is not None and hasattr(limiter, "unregister"):
+        limiter.unregister()
     total = sum(t.values())
+    sample = (f"H_X on {n_tok} of {sp.n} tokens, rotation of W on {r_in} of {sp.o} rows, output transform on "
+              f"{c_out} of {sp.i} columns, sweep on {n_rows} of {sp.o} rows (each scaled to the whole layer); "
+              f"rotation of H_X {how_rot}, damped factor (of H_X: the same size and cost as of H_X') {how_fac}, "
+              f"H_G square root (eigh) in full")
     return {"value": sp.o * sp.i / total / 1e6, "unit": "Mweights/s", "cores": cores, "kind": "oracle",
-            "sample": (f"float64 oracle phases on the same layer: H_X on the first {n_tok} of {sp.n} tokens "
-                       f"(x{sp.n // n_tok}), sweep on {n_rows} of {sp.o} rows (x{sp.o // n_rows}), rotations, "
-                       f"H_G square root (eigh) and damped factor in full; extrapolated layer time {total:.1f} s"),
+            "sample": f"float64 oracle, {sample}; layer time {total:.1f} s",
             "phases_s": {k: round(v, 3) for k, v in t.items()}}
+
+
+# ----------------------------------------------------------------------------- the 32-layer stack
+def _stack_layer_host(li: int):
+    """Host inputs of one layer of the stack (worker processes: numpy only)."""
+    specs = synth.c5_specs(li)
+    xs = {}
+    for sp in specs:
+        if sp.x_sub not in xs:
+            xs[sp.x_sub] = (synth.gen_X(sp), synth.gen_signs(sp)[0])
+    return xs, [(synth.gen_W(sp), synth.gen_HG(sp), synth.gen_signs(sp)[1], sp.x_sub) for sp in specs]
+
+
+def stack_work() -> dict:
+    """Algorithmic work of one pass over the stack, summed over its 224 sublayers and 128 inputs, with the
+    per-layer formulas of algorithmic_work (H_X, its rotation and R once per distinct input)."""
+    tot = {"hessian": 0, "rotate_in": 0, "rotate_out": 0, "cholinv": 0, "quantize": 0}
+    n = synth.C5_TOKENS
+    for (_, o, i, x) in synth.C5_SUBLAYERS:
+        tot["rotate_in"] += o * i * (2 + 4)
+        tot["rotate_out"] += 8 * o * i
+        tot["quantize"] += int((8 + 3 / 8 + 8 / 128) * o * i)   # at the 3.0-bit average
+    for (_, i, _) in synth.C5_INPUTS:
+        tot["hessian"] += n * i * (i + 1)
+        tot["rotate_in"] += 32 * i * i
+        tot["cholinv"] += 2 * i ** 3 // 3
+        tot["quantize"] += 2 * i * i
+    L = synth.C5_LAYERS
+    return {"hessian": {"flop": L * tot["hessian"], "peak": "bf16_mfma"},
+            "rotate_in": {"bytes": L * tot["rotate_in"], "peak": "hbm"},
+            "rotate_out": {"bytes": L * tot["rotate_out"], "peak": "hbm"},
+            "cholinv": {"flop": L * tot["cholinv"], "peak": "fp64_alu"},
+            "quantize": {"bytes": L * tot["quantize"], "peak": "hbm"}}
+
+
+def run_stack(steps: int, warmup: int):
+    """The whole 32-layer stack: scores, allocation, then every sublayer quantized; `steps` timed passes
+    after `warmup` passes over the first layer alone. Phase times from HIP events between the calls."""
+    import multiprocessing as mp
+    from concurrent.futures import ProcessPoolExecutor
+
+    import torch
+
+    from post_quantization_03_amd.stack import Layer, Sublayer, quantize_stack
+
+    dev = torch.device("cuda:0")
+
+    def to(a, kind):
+        if kind == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    t0 = time.time()
+    workers = max(1, min(16, len(os.sched_getaffinity(0))))
+    layers = []
+    with ProcessPoolExecutor(max_workers=workers, mp_context=mp.get_context("fork")) as ex:
+        for li, (xs, subs) in enumerate(ex.map(_stack_layer_host, range(synth.C5_LAYERS))):
+            layers.append(Layer(X=[to(xs[k][0], "bf16") for k in range(4)], s=[to(xs[k][1], "i8") for k in range(4)],
+                                subs=[Sublayer(W=to(w, "bf16"), HG=to(h, "f32"), t=to(tt, "i8"), x=x)
+                                      for (w, h, tt, x) in subs]))
+            if li % 8 == 7:
+                print(f"# stack inputs: {li + 1} layers on the device ({time.time() - t0:.0f}s)", file=sys.stderr,
+                      flush=True)
+    from post_quantization_03_amd.stack import _ws_bytes
+    ws = torch.empty(_ws_bytes(layers, 128), dtype=torch.uint8, device=dev)
+    for k in range(warmup):
+        quantize_stack(layers[:1], ws=ws)
+        torch.cuda.synchronize()
+        print(f"# warmup {k + 1}/{warmup} done", file=sys.stderr, flush=True)
+    times, phases = [], {}
+    for k in range(steps):
+        marks = []
+        torch.cuda.synchronize()
+        t_start = time.perf_counter()
+        out = quantize_stack(layers, ws=ws, marks=marks)
+        torch.cuda.synchronize()
+        times.append(time.perf_counter() - t_start)
+        for (name, a), (_, b) in zip(marks[:-1], marks[1:]):
+            phases[name] = phases.get(name, 0.0) + a.elapsed_time(b) / steps
+        print(f"# timed pass {k + 1}/{steps}: {times[-1]:.3f} s", file=sys.stderr, flush=True)
+    if int(out.info.max().item()) != 0 or int(out.info.min().item()) != 0:
+        raise RuntimeError("a factorisation failed in the stack")
+    bits = np.array(out.bits)
+    sizes = np.array([o * i for (_, o, i, _) in synth.C5_SUBLAYERS] * synth.C5_LAYERS)
+    alloc = {"bits_2_3_4": np.bincount(bits, minlength=5)[2:].tolist(),
+             "avg_bits": round(float(np.dot(bits, sizes) / sizes.sum()), 4)}
+    return float(np.mean(times)) * 1e3, phases, alloc
+
+
+def stack_cpu_baseline() -> dict:
+    """The oracle on a bounded sample of the stack, scaled to all 32 layers: layer 0 with H_X on 1024 of
+    8192 tokens per input, the rotation of H_X and the damped factor in full for its 4 inputs, and per
+    sublayer the rotation of W on 512 rows, the output transform on 256 columns and the sweep on 64 rows
+    (stand-in values), each scaled to the whole sublayer; then x32. The rotation of H_X and the damped
+    factor are sampled as in cpu_baseline."""
+    from oracle import kronq as kq
+
+    cores, limiter = _blas_threads()
+    n_tok, r_in, c_out, n_rows = 1024, 512, 256, 64
+    specs = synth.c5_specs(0)
+    t = {"hessian": 0.0, "rotate_in": 0.0, "hg_sqrt": 0.0, "rotate_out": 0.0, "cholinv": 0.0, "quantize": 0.0}
+    Rs, ss = {}, {}
+    for sp in specs:
+        if sp.x_sub in Rs:
+            continue
+        X = synth.widen(synth.gen_X(sp, n_tok), "bf16")
+        s_in = synth.gen_signs(sp)[0]
+        t0 = time.perf_counter()
+        HX = kq.hessian(X)
+        t["hessian"] += (time.perf_counter() - t0) * sp.n / n_tok
+        dt, _ = _time_hessian_rotation(kq, HX, s_in)
+        t["rotate_in"] += dt
+        dt, _ = _time_factor(kq, HX, 0.01)
+        t["cholinv"] += dt
+        H, _ = kq.damped(HX, 0.01)
+        # untimed stand-in factor of the whole width for the sampled sweeps
+        Rs[sp.x_sub] = np.diag(1.0 / np.sqrt(np.diag(H)))
+        ss[sp.x_sub] = s_in
+    for sp in specs:
+        W = synth.widen(synth.gen_W(sp), "bf16")
+        h = synth.gen_HG(sp).astype(np.float64)
+        tt = synth.gen_signs(sp)[1]
+        t0 = time.perf_counter()
+        W1 = kq.rotate_in_weights(W[:r_in], ss[sp.x_sub])
+        t["rotate_in"] += (time.perf_counter() - t0) * sp.o / r_in
+        t0 = time.perf_counter()
+        S, _ = kq.hg_sqrt(h, "diag")
+        t["hg_sqrt"] += time.perf_counter() - t0
+        t0 = time.perf_counter()
+        kq.rotate_out(W[:, :c_out], S, "diag", tt)
+        t["rotate_out"] += (time.perf_counter() - t0) * sp.i / c_out
+        t0 = time.perf_counter()
+        kq.sweep_blocked(W1[:n_rows], Rs[sp.x_sub], 3, 128, 128)
+        t["quantize"] += (time.perf_counter() - t0) * sp.o / n_rows
+    if limiter is not None and hasattr(limiter, "unregister"):
+        limiter.unregister()
+    layer = sum(t.values())
+    total = layer * synth.C5_LAYERS
+    weights = sum(o * i for (_, o, i, _) in synth.C5_SUBLAYERS) * synth.C5_LAYERS
+    return {"value": weights / total / 1e6, "unit": "Mweights/s", "cores": cores, "kind": "oracle",
+            "sample": (f"float64 oracle on layer 0 of 32 (extrapolated x32): H_X on {n_tok} of 8192 tokens per input, "
+                       f"rotation of H_X from 2048 rows of one pass, damped factor on at most a 4096 x 4096 block "
+                       f"(scaled by the cube of the width ratio), per sublayer the rotation of W on {r_in} rows, "
+                       f"the output transform on {c_out} columns and the sweep on {n_rows} rows, each scaled; "
+                       f"stack time {total:.0f} s"),
+            "phases_s": {k: round(v * synth.C5_LAYERS, 2) for k, v in t.items()}}
 
 
 def main():
@@ -591,7 +806,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--workload", default="C2", choices=["C2", "C3", "C4"])
+    ap.add_argument("--workload", default="C2", choices=["C1", "C2", "C3", "C4", "C5"],
+                    help="C2 (default) is the 4096 x 4096 layer the metric is quoted on; C1, C3, C4 the other layers; "
+                         "C5 the 32-layer stack (one timed pass by default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-phases", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -614,6 +831,9 @@ def main():
         print("bench.py measures one GPU: the per-layer solver runs on a single MI355X in this build "
               "(multi-GPU sharding is described in DESIGN.md, not implemented).", file=sys.stderr)
         sys.exit(2)
+    if args.workload == "C5":
+        run_stack_line(args)
+        return
     sp = synth.CONFIGS[args.workload]
     if args.drift:
         print(json.dumps(drift_study(sp)), flush=True)
@@ -638,8 +858,11 @@ def main():
         del src, dst
     ms, ph, out, iters, mv, ms_cached = run_gpu(sp, args.steps, args.warmup, not args.no_phases)
     value = sp.o * sp.i / (ms / 1e3) / 1e6
-    roof, per_phase, s_cached, aggregates = None, None, None, None
+    roof, per_phase, s_cached, aggregates, chain = None, None, None, None, None
     if ph:
+        chain_ms = ph.pop("_chain")
+        chain = {"rows": 16, "ms": round(chain_ms, 4), "per_step_ns": round(chain_ms / sp.i * 1e6, 2),
+                 "quantize_ms": round(ph["quantize"], 4), "quantize_over_chain": round(ph["quantize"] / chain_ms, 3)}
         work = algorithmic_work(sp, iters)
         per_phase = {k: roofline_of(k, work[k], ph[k]) for k in work if k in ph and
                      (work[k].get("flop") or work[k].get("bytes"))}
@@ -671,8 +894,39 @@ def main():
                                 "and the damped factor; fp32 for the rotations of W and the sweep"},
             "phases_ms": {k: round(v, 4) for k, v in ph.items()} if ph else None,
             "db_steps": iters, "s_cached_mweights_per_s": s_cached,
-            "roofline": roof, "phases_roofline": per_phase, "phases_aggregate": aggregates, "cpu_baseline": cpu,
-            "matvec_quantized": mv}
+            "roofline": roof, "phases_roofline": per_phase, "phases_aggregate": aggregates,
+            "sweep_critical_path": chain, "cpu_baseline": cpu, "matvec_quantized": mv}
+    print(json.dumps(line), flush=True)
+
+
+def run_stack_line(args) -> None:
+    """One JSON line for the 32-layer stack (C5): whole-stack throughput, summed phase times, the
+    allocation, per-phase roofline and the oracle on a bounded sample."""
+    steps = args.steps if args.steps != 5 else 1   # one pass by default: a pass quantizes 6.5e9 weights
+    ms, ph, alloc = run_stack(steps, args.warmup if args.warmup != 2 else 1)
+    weights = sum(o * i for (_, o, i, _) in synth.C5_SUBLAYERS) * synth.C5_LAYERS
+    work = stack_work()
+    per_phase = {k: roofline_of(k, work[k], ph[k]) for k in work if k in ph}
+    dense = [k for k in per_phase if per_phase[k]["unit"] == "TFLOP/s"]
+    hbm = [k for k in per_phase if per_phase[k]["unit"] == "GB/s"]
+    aggregates = {
+        "dense_phases": dense,
+        "dense_frac": round(sum(work[k]["flop"] for k in dense) / sum(ph[k] / 1e3 * PEAK[work[k]["peak"]] for k in dense), 4),
+        "hbm_phases": hbm,
+        "hbm_frac": round(sum(work[k]["bytes"] for k in hbm) / (sum(ph[k] for k in hbm) / 1e3 * PEAK["hbm"]), 4),
+    }
+    dom = max(per_phase, key=lambda k: ph[k])
+    cpu = None if args.no_cpu_baseline else stack_cpu_baseline()
+    line = {"metric": "layer-quant throughput: Mweights/s (4096x4096 W3 g128) + % MFMA/HBM peak",
+            "value": round(weights / (ms / 1e3) / 1e6, 3), "unit": "Mweights/s", "n_gpus": 1, "steps": steps,
+            "warmup": args.warmup if args.warmup != 2 else 1, "ms_per_step": round(ms, 2), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "fp32", "data": "synthetic",
+            "config": {"workload": "C5 32-layer stack x 7 sublayers, {2,3,4} bits under a 3.0 budget, g128",
+                       "layers": synth.C5_LAYERS, "tokens": synth.C5_TOKENS, "weights": weights, "hg_form": "diag",
+                       "allocation": alloc},
+            "phases_ms": {k: round(v, 3) for k, v in ph.items()},
+            "roofline": per_phase[dom], "phases_roofline": per_phase, "phases_aggregate": aggregates,
+            "cpu_baseline": cpu}
     print(json.dumps(line), flush=True)
 
 

@@ -62,8 +62,19 @@ def _ws_bytes(layers, group: int) -> int:
 
 
 def quantize_stack(layers: list, budget: float = 3.0, group: int = 128, damp: float = 0.01, keep_q: bool = False,
-                   keep_h: bool = False, ws: torch.Tensor | None = None, H_cache: list | None = None) -> StackOut:
+                   keep_h: bool = False, ws: torch.Tensor | None = None, H_cache: list | None = None,
+                   marks: list | None = None) -> StackOut:
+    """``marks``: when a list is given, a timing event is recorded on the current stream before every
+    call, as (phase name, event), and one ("end", event) after the last; the time from one mark to the
+    next belongs to the first one's phase."""
     dev = layers[0].X[0].device
+
+    def mark(name: str) -> None:
+        if marks is not None:
+            e = torch.cuda.Event(enable_timing=True)
+            e.record()
+            marks.append((name, e))
+
     if ws is None:
         ws = torch.empty(_ws_bytes(layers, group), dtype=torch.uint8, device=dev)
     f32 = dict(dtype=torch.float32, device=dev)
@@ -77,14 +88,17 @@ def quantize_stack(layers: list, budget: float = 3.0, group: int = 128, damp: fl
         for x, X in enumerate(L.X):
             n, i = X.shape
             H = H_cache[li][x] if H_cache is not None else torch.empty((i, i), dtype=torch.float64, device=dev)
+            mark("hessian")
             K.kq_hessian_accum(X, H, 1.0 / n, 0.0, ws)
             hl.append(H)
         for sl in L.subs:
             o = sl.W.shape[0]
+            mark("sensitivity")
             K.kq_sensitivity(hl[sl.x], sl.HG, "diag", o, 0, scores[k:k + 1])
             k += 1
         Hs.append(hl)
     sizes = [sl.W.shape[0] * sl.W.shape[1] for L in layers for sl in L.subs]
+    mark("allocate")
     bits = K.kq_allocate_bits(scores.cpu().numpy(), sizes, budget, 2, 4).tolist()
     out = StackOut(scores=scores, bits=bits)
     # ---- pass 2
@@ -95,23 +109,29 @@ def quantize_stack(layers: list, budget: float = 3.0, group: int = 128, damp: fl
         Rs = []
         for x, H in enumerate(Hs[li]):
             i = H.shape[0]
+            mark("rotate_in")
             K.kq_rotate_in_hessian(H, L.s[x], ws)
             R = torch.empty((i, i), **f32)
+            mark("cholinv")
             K.kq_cholinv(H, damp, R, info[li, x:x + 1], ws)
             Rs.append(R)
         for j, sl in enumerate(L.subs):
             o, i = sl.W.shape
             b = bits[k]
             W2 = torch.empty((o, i), **f32)
+            mark("rotate_in")
             K.kq_rotate_in(sl.W, W2, None, L.s[sl.x], ws)
             S = torch.empty((o,), **f32)
+            mark("hg_sqrt")
             K.kq_hg_sqrt(sl.HG, "diag", o, 0, S, None, info[li, 8 + j:9 + j], ws)
+            mark("rotate_out")
             K.kq_rotate_out(W2, S, "diag", 0, sl.t, ws)
             ng = i // group if group else 1
             codes = torch.empty((o, i * b // 32), dtype=torch.int32, device=dev)
             scale = torch.empty((o, ng), **f32)
             offset = torch.empty((o, ng), **f32)
             rl = torch.empty((o,), **f32)
+            mark("quantize")
             K.kq_quantize_layer(W2, Rs[sl.x], b, group, 128, codes, scale, offset, rl, ws)
             out.codes.append(codes)
             out.scale.append(scale)
@@ -124,5 +144,6 @@ def quantize_stack(layers: list, budget: float = 3.0, group: int = 128, damp: fl
             out.H.append(Hs[li])
             out.R.append(Rs)
     out.info = info
+    mark("end")
     return out
 
