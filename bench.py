@@ -730,8 +730,12 @@ def run_stack(steps: int, warmup: int):
         out = quantize_stack(layers, ws=ws, marks=marks)
         torch.cuda.synchronize()
         times.append(time.perf_counter() - t_start)
-        for (name, a), (_, b) in zip(marks[:-1], marks[1:]):
+        seq = [m for m in marks if len(m) == 2]
+        for (name, a), (_, b) in zip(seq[:-1], seq[1:]):
             phases[name] = phases.get(name, 0.0) + a.elapsed_time(b) / steps
+        for (name, a, b) in (m for m in marks if len(m) == 3):
+            key = name + "_side"
+            phases[key] = phases.get(key, 0.0) + a.elapsed_time(b) / steps
         print(f"# timed pass {k + 1}/{steps}: {times[-1]:.3f} s", file=sys.stderr, flush=True)
     if int(out.info.max().item()) != 0 or int(out.info.min().item()) != 0:
         raise RuntimeError("a factorisation failed in the stack")
@@ -906,16 +910,22 @@ def run_stack_line(args) -> None:
     ms, ph, alloc = run_stack(steps, args.warmup if args.warmup != 2 else 1)
     weights = sum(o * i for (_, o, i, _) in synth.C5_SUBLAYERS) * synth.C5_LAYERS
     work = stack_work()
-    per_phase = {k: roofline_of(k, work[k], ph[k]) for k in work if k in ph}
+    # the damped factors (and the rotations of H_X before them) run on their own streams, beside the
+    # sublayers' work: their phase times are the sums of their own intervals, which overlap the rest
+    ph_work = dict(ph)
+    ph_work["cholinv"] = ph.get("cholinv_side", 0.0)
+    ph_work["rotate_in"] = ph.get("rotate_in", 0.0) + ph.get("rotate_in_side", 0.0)
+    per_phase = {k: roofline_of(k, work[k], ph_work[k]) for k in work if ph_work.get(k)}
     dense = [k for k in per_phase if per_phase[k]["unit"] == "TFLOP/s"]
     hbm = [k for k in per_phase if per_phase[k]["unit"] == "GB/s"]
     aggregates = {
         "dense_phases": dense,
-        "dense_frac": round(sum(work[k]["flop"] for k in dense) / sum(ph[k] / 1e3 * PEAK[work[k]["peak"]] for k in dense), 4),
+        "dense_frac": round(sum(work[k]["flop"] for k in dense) /
+                            sum(ph_work[k] / 1e3 * PEAK[work[k]["peak"]] for k in dense), 4),
         "hbm_phases": hbm,
-        "hbm_frac": round(sum(work[k]["bytes"] for k in hbm) / (sum(ph[k] for k in hbm) / 1e3 * PEAK["hbm"]), 4),
+        "hbm_frac": round(sum(work[k]["bytes"] for k in hbm) / (sum(ph_work[k] for k in hbm) / 1e3 * PEAK["hbm"]), 4),
     }
-    dom = max(per_phase, key=lambda k: ph[k])
+    dom = max(per_phase, key=lambda k: ph_work[k])
     cpu = None if args.no_cpu_baseline else stack_cpu_baseline()
     line = {"metric": "layer-quant throughput: Mweights/s (4096x4096 W3 g128) + % MFMA/HBM peak",
             "value": round(weights / (ms / 1e3) / 1e6, 3), "unit": "Mweights/s", "n_gpus": 1, "steps": steps,

@@ -5,6 +5,7 @@
 //   kq_hg_sqrt  - principal square root of H_G and its inverse (output side of bidirectional
 //                 incoherence processing), by the scaled Denman-Beavers iteration in fp64.
 #include <cmath>
+#include <mutex>
 
 #include "kq_internal.h"
 
@@ -319,14 +320,24 @@ __global__ __launch_bounds__(256) void dgemm_valu_kernel(GemmArgs<double> g) {
         const int64_t L = g.tri ? (int64_t)gridDim.x : (int64_t)gridDim.x * gridDim.y;
         int64_t lid = g.tri ? (int64_t)blockIdx.x : (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
         // Work-groups go to the 8 XCDs round-robin by id: give XCD x a contiguous run of tiles
-        // (a bijection for any L; runs differ in length by at most one).
-        {
+        // (a bijection for any L; runs differ in length by at most one). Not when the K range depends
+        // on the tile (triangular operands): a contiguous run of rows would give one XCD all the long
+        // tiles, so those keep the round-robin spread.
+        if (g.kmode == 0) {
             const int64_t x = lid % 8, q = lid / 8, base = L / 8, rem = L % 8;
             lid = x * base + (x < rem ? x : rem) + q;
         }
         if constexpr (BM != BN) {
             tm = lid / nx;  // row-block tiles (own_rows): never triangular
             tn = lid % nx;
+        } else if (g.kmode && !g.tri) {
+            // longest K ranges first: K grows with the tile row when it ends at the row (bit 2) and
+            // with the tile column when it ends at the column (bit 3)
+            const int64_t ny = (g.M + BM - 1) / BM;
+            tm = lid / nx;
+            tn = lid % nx;
+            if (g.kmode & 4) tm = ny - 1 - tm;
+            if (g.kmode & 8) tn = nx - 1 - tn;
         } else if (g.tri) {
             int64_t r = (int64_t)((sqrt(8.0 * (double)lid + 1.0) - 1.0) * 0.5);
             while (r * (r + 1) / 2 > lid) r--;
@@ -964,6 +975,98 @@ __global__ void reverse_upper_kernel(const double* X, int64_t n, float* R) {
         R[a * n + b] = (b >= a) ? (float)X[(n - 1 - a) * n + (n - 1 - b)] : 0.0f;
 }
 
+// Look-ahead queues of kq_cholinv (default priority), per device: four side queues, handed to calls in
+// turn so that calls running side by side on different streams do not share one, with two events each.
+// Created on a device's first large factorisation and kept until the process ends; they carry no data
+// from one call to the next. The mutex keeps one call's event sequence intact against other threads.
+constexpr int LA_QUEUES = 4;
+constexpr int64_t LA_MIN_N = 6144;  // below this the trailing updates are shorter than a diagonal block
+struct LookaheadQueues {
+    hipStream_t side[LA_QUEUES] = {};
+    hipEvent_t evF[LA_QUEUES] = {}, evP[LA_QUEUES] = {};
+    int next = 0;
+    bool ok = false;
+};
+static std::mutex g_la_mu;
+static LookaheadQueues g_la[64];
+
+static kq_status la_queues(LookaheadQueues** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return fail(KQ_EHIP, "cholinv queues: no device");
+    LookaheadQueues& q = g_la[dev];
+    if (!q.ok) {
+        for (int k = 0; k < LA_QUEUES; k++) {
+            if (hipStreamCreateWithFlags(&q.side[k], hipStreamNonBlocking) != hipSuccess)
+                return fail(KQ_EHIP, "cholinv queues: stream creation failed");
+            if (hipEventCreateWithFlags(&q.evF[k], hipEventDisableTiming | hipEventDisableSystemFence) != hipSuccess ||
+                hipEventCreateWithFlags(&q.evP[k], hipEventDisableTiming | hipEventDisableSystemFence) != hipSuccess)
+                return fail(KQ_EHIP, "cholinv queues: event creation failed");
+        }
+        q.ok = true;
+    }
+    *out = &q;
+    return KQ_OK;
+}
+
+#define KQ_HIPC(expr)                                                                   \
+    do {                                                                                \
+        if ((expr) != hipSuccess) return fail(KQ_EHIP, "%s failed", #expr);            \
+    } while (0)
+
+// Lower Cholesky of one n x n fp64 matrix A (lda = n, lower triangle) with the inverses of its 128-wide
+// diagonal blocks in X, like potrf_batched, with one step of look-ahead: after block k's panel, the
+// caller's stream updates block column k + 1 by step k first and then the rest of the trailing matrix,
+// while a side queue factors diagonal block k + 1 and forms its panel. The two touch disjoint parts of
+// A and X: block column k + 1 (side) against block columns k + 2 onwards (caller's stream).
+static kq_status potrf_lookahead(double* A, int64_t n, double* X, int32_t* info, double* scr, hipStream_t st) {
+    constexpr int64_t NB = 128;
+    std::lock_guard<std::mutex> lock(g_la_mu);
+    LookaheadQueues* q = nullptr;
+    KQ_TRY(la_queues(&q));
+    const int slot = q->next;
+    q->next = (q->next + 1) % LA_QUEUES;
+    hipStream_t sd = q->side[slot];
+    hipEvent_t evF = q->evF[slot], evP = q->evP[slot];
+    auto lo = [&](int64_t k) { return k * NB; };
+    auto hi = [&](int64_t k) { return (k + 1) * NB < n ? (k + 1) * NB : n; };
+    auto diag = [&](int64_t k, hipStream_t s) {
+        return chol_inv_diag128(A, n, 0, X, n, 0, n, lo(k), 1, scr, info, 0, nullptr, s);
+    };
+    auto panel = [&](int64_t k, hipStream_t s) -> kq_status {  // A[k1:, k0:k1] <- A[k1:, k0:k1] X_kk^T
+        const int64_t k0 = lo(k), k1 = hi(k);
+        if (k1 >= n) return KQ_OK;
+        GemmArgs<double> p = gemm_args<double>(n - k1, k1 - k0, k1 - k0, A + k1 * n + k0, n, X + k0 * n + k0, n,
+                                               A + k1 * n + k0, n, 1.0, 0.0);
+        p.own_rows = 1;
+        return gemm<double>(p, false, true, s);
+    };
+    const int64_t nb = (n + NB - 1) / NB;
+    KQ_TRY(diag(0, st));
+    KQ_TRY(panel(0, st));
+    for (int64_t k = 0; k + 1 < nb; k++) {
+        const int64_t k0 = lo(k), k1 = hi(k), k2 = hi(k + 1);
+        // block column k + 1 by step k: A[k1:, k1:k2] -= L[k1:, k0:k1] L[k1:k2, k0:k1]^T
+        GemmArgs<double> f = gemm_args<double>(n - k1, k2 - k1, k1 - k0, A + k1 * n + k0, n, A + k1 * n + k0, n,
+                                               A + k1 * n + k1, n, -1.0, 1.0);
+        KQ_TRY(gemm<double>(f, false, true, st));
+        KQ_HIPC(hipEventRecord(evF, st));
+        KQ_HIPC(hipStreamWaitEvent(sd, evF, 0));
+        KQ_TRY(diag(k + 1, sd));
+        KQ_TRY(panel(k + 1, sd));
+        KQ_HIPC(hipEventRecord(evP, sd));
+        // the rest of step k: A[k2:, k2:] -= L[k2:, k0:k1] L[k2:, k0:k1]^T (lower)
+        if (k2 < n) {
+            GemmArgs<double> u = gemm_args<double>(n - k2, n - k2, k1 - k0, A + k2 * n + k0, n, A + k2 * n + k0, n,
+                                                   A + k2 * n + k2, n, -1.0, 1.0);
+            u.tri = 1;
+            KQ_TRY(gemm<double>(u, false, true, st));
+        }
+        KQ_HIPC(hipStreamWaitEvent(st, evP, 0));
+    }
+    return KQ_OK;
+}
+#undef KQ_HIPC
+
 static void cholinv_layout(Sizer& z, int64_t n) {
     z.take<double>(1);
     z.take<double>((size_t)n * n);
@@ -998,7 +1101,8 @@ extern "C" kq_status kq_cholinv(const double* HX, int64_t n, int64_t ldh, double
     hipLaunchKernelGGL(reverse_damped_kernel, g2, dim3(256), 0, st, HX, n, ldh, lam, Hr);
     KQ_TRY(check_launch("reverse"));
     KQ_TRY(fill<double>(X, (size_t)n * n, 0.0, st));
-    KQ_TRY(potrf_batched<double>(Hr, n, 0, X, n, 0, n, 1, info, 0, nullptr, nullptr, st, Cscr));
+    if (n >= LA_MIN_N) KQ_TRY(potrf_lookahead(Hr, n, X, info, Cscr, st));
+    else KQ_TRY(potrf_batched<double>(Hr, n, 0, X, n, 0, n, 1, info, 0, nullptr, nullptr, st, Cscr));
     KQ_TRY(trtri_batched<double>(Hr, n, 0, X, n, 0, n, 1, Tscr, nullptr, st));
     hipLaunchKernelGGL(reverse_upper_kernel, g2, dim3(256), 0, st, X, n, R);
     return check_launch("reverse_upper");

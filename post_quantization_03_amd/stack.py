@@ -9,6 +9,10 @@ reads it (kq_sensitivity). Host: kq_allocate_bits over all scores.
 Pass 2 (per layer): per distinct input one rotation of H_X and one damped factor R (kq_rotate_in with
 no weights, kq_cholinv): sublayers that read the same input share U and R. Per sublayer: kq_rotate_in
 (weights), kq_hg_sqrt, kq_rotate_out, kq_quantize_layer at its bit-width.
+
+The damped factors depend only on pass 1, and each one is a chain of small dependent steps, so they run
+on streams of their own (one per distinct input of a layer, each with its own workspace), ahead of and
+beside the sublayers' work on the caller's stream, which waits only for the factor it needs.
 """
 from __future__ import annotations
 
@@ -47,6 +51,27 @@ class StackOut:
     H: list = field(default_factory=list)
 
 
+_FACTOR_STREAMS: dict = {}
+
+
+def _factor_streams(dev, count: int) -> list:
+    """Streams (default priority) for the damped factors, kept per device."""
+    key = dev.index if dev.index is not None else torch.cuda.current_device()
+    have = _FACTOR_STREAMS.setdefault(key, [])
+    while len(have) < count:
+        have.append(torch.cuda.Stream(device=dev))
+    return have[:count]
+
+
+def _factor_ws_bytes(layers) -> int:
+    need = 256
+    for L in layers:
+        for X in L.X:
+            i = X.shape[1]
+            need = max(need, K.kq_workspace_bytes("rotate_in", 0, i), K.kq_workspace_bytes("cholinv", 0, i))
+    return need
+
+
 def _ws_bytes(layers, group: int) -> int:
     need = 256
     for L in layers:
@@ -66,7 +91,8 @@ def quantize_stack(layers: list, budget: float = 3.0, group: int = 128, damp: fl
                    marks: list | None = None) -> StackOut:
     """``marks``: when a list is given, a timing event is recorded on the current stream before every
     call, as (phase name, event), and one ("end", event) after the last; the time from one mark to the
-    next belongs to the first one's phase."""
+    next belongs to the first one's phase. Work on the factor streams is marked by its own start and
+    end events, as (phase name, start, end); those intervals overlap the caller's stream's."""
     dev = layers[0].X[0].device
 
     def mark(name: str) -> None:
@@ -104,20 +130,45 @@ def quantize_stack(layers: list, budget: float = 3.0, group: int = 128, damp: fl
     # ---- pass 2
     # info[layer, input] from the damped factors, info[layer, 8 + sublayer] from the H_G roots
     info = torch.zeros((len(layers), 16), dtype=torch.int32, device=dev)
+    main = torch.cuda.current_stream(dev)
+    nf = max(len(L.X) for L in layers)
+    fstreams = _factor_streams(dev, nf)
+    fbytes = _factor_ws_bytes(layers)
+    fws = []
+    for fs in fstreams:
+        fs.wait_stream(main)   # pass 1 (H_X) and the allocations above
+        with torch.cuda.stream(fs):
+            fws.append(torch.empty(fbytes, dtype=torch.uint8, device=dev))
+    mark("factors_enqueued")
     k = 0
     for li, L in enumerate(layers):
-        Rs = []
+        Rs, ready = [], []
         for x, H in enumerate(Hs[li]):
             i = H.shape[0]
-            mark("rotate_in")
-            K.kq_rotate_in_hessian(H, L.s[x], ws)
-            R = torch.empty((i, i), **f32)
-            mark("cholinv")
-            K.kq_cholinv(H, damp, R, info[li, x:x + 1], ws)
+            fs = fstreams[x]
+            with torch.cuda.stream(fs):
+                t = [torch.cuda.Event(enable_timing=True) for _ in range(3)] if marks is not None else None
+                if t:
+                    t[0].record(fs)
+                K.kq_rotate_in_hessian(H, L.s[x], fws[x])
+                R = torch.empty((i, i), **f32)
+                if t:
+                    t[1].record(fs)
+                K.kq_cholinv(H, damp, R, info[li, x:x + 1], fws[x])
+                ev = torch.cuda.Event(enable_timing=t is not None)
+                ev.record(fs)
+                if t:
+                    marks.append(("rotate_in", t[0], t[1]))
+                    marks.append(("cholinv", t[1], ev))
+            R.record_stream(main)
+            H.record_stream(fs)
             Rs.append(R)
+            ready.append(ev)
         for j, sl in enumerate(L.subs):
             o, i = sl.W.shape
             b = bits[k]
+            mark("wait_factor")
+            main.wait_event(ready[sl.x])
             W2 = torch.empty((o, i), **f32)
             mark("rotate_in")
             K.kq_rotate_in(sl.W, W2, None, L.s[sl.x], ws)
@@ -143,6 +194,8 @@ def quantize_stack(layers: list, budget: float = 3.0, group: int = 128, damp: fl
         if keep_h:
             out.H.append(Hs[li])
             out.R.append(Rs)
+    for fs in fstreams:
+        main.wait_stream(fs)
     out.info = info
     mark("end")
     return out

@@ -264,11 +264,12 @@ def test_rotate_out(form, o, i, blk):
 
 
 # ----------------------------------------------------------------------------- damped factor
-@pytest.mark.parametrize("i", [200, 384, 1000, 128])
+@pytest.mark.parametrize("i", [200, 384, 1000, 128, 6200])
 def test_cholinv(i):
+    """Widths of 6144 and more take the look-ahead factorisation (6200: ragged last block)."""
     torch, dev = torch_dev()
     say(f"cholinv i={i}")
-    sp = synth.scaled(synth.CONFIGS["C2"], n=4 * i, i=i, n_outliers=max(1, i // 100))
+    sp = synth.scaled(synth.CONFIGS["C2"], n=(4 if i < 4096 else 2) * i, i=i, n_outliers=max(1, i // 100))
     H64 = kq.hessian(synth.widen(synth.gen_X(sp), "bf16"))
     H, _ = kq.damped(H64, 0.01)
     R_ref = kq.inverse_upper_factor(H)
@@ -312,6 +313,36 @@ def test_cholinv_concurrent_with_hg_sqrt():
         torch.cuda.synchronize()
         assert host(info).tolist()[:3] == [0, 0, 0]
         assert torch.equal(R, R0), f"repeat {rep}"
+
+
+def test_cholinv_lookahead_calls_side_by_side():
+    """Two look-ahead factorisations enqueued on two streams at once (each call takes its own side queue)
+    equal the same calls made one after the other, bit for bit."""
+    torch, dev = torch_dev()
+    i = 6400
+    say(f"cholinv i={i} twice, side by side")
+    Hs, Rs, R0s = [], [], []
+    for k in range(2):
+        sp = synth.scaled(synth.CONFIGS["C2"], n=2 * i, i=i, n_outliers=8, layer=k)
+        Hs.append(to_dev(kq.hessian(synth.widen(synth.gen_X(sp), "bf16")), "f64"))
+    ws = [ws_tensor(K.kq_workspace_bytes("cholinv", 0, i)) for _ in range(2)]
+    info = torch.zeros(4, dtype=torch.int32, device=dev)
+    for k in range(2):
+        R0s.append(torch.empty((i, i), dtype=torch.float32, device=dev))
+        K.kq_cholinv(Hs[k], 0.01, R0s[k], info[k:k + 1], ws[k])
+        torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(device=dev) for _ in range(2)]
+    for k in range(2):
+        Rs.append(torch.empty_like(R0s[k]))
+        streams[k].wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(streams[k]):
+            K.kq_cholinv(Hs[k], 0.01, Rs[k], info[2 + k:3 + k], ws[k])
+    for st in streams:
+        torch.cuda.current_stream().wait_stream(st)
+    torch.cuda.synchronize()
+    assert host(info).tolist() == [0, 0, 0, 0]
+    for k in range(2):
+        assert torch.equal(Rs[k], R0s[k])
 
 
 def test_cholinv_reports_not_positive_definite():
