@@ -827,6 +827,10 @@ def main():
     ap.add_argument("--drift", action="store_true",
                     help="compare GPTQ with the input-drift-corrected solver on drifted synthetic inputs and print "
                          "the result as its own JSON line")
+    ap.add_argument("--profile-phases", action="store_true",
+                    help="for rocprofv3 counter runs: each phase of the workload's layer alone, twice, after one full "
+                         "step, with a marker dispatch before each (prints a JSON line naming the phases, not the "
+                         "benchmark line)")
     ap.add_argument("--matvec-only", action="store_true",
                     help="time only the inference-side product (kq_matvec_quantized) on the workload's layer shape "
                          "with random codes, and print its own JSON line (not the benchmark line)")
@@ -839,6 +843,9 @@ def main():
         run_stack_line(args)
         return
     sp = synth.CONFIGS[args.workload]
+    if args.profile_phases:
+        profile_phases(sp)
+        return
     if args.drift:
         print(json.dumps(drift_study(sp)), flush=True)
         return
@@ -901,6 +908,69 @@ def main():
             "roofline": roof, "phases_roofline": per_phase, "phases_aggregate": aggregates,
             "sweep_critical_path": chain, "cpu_baseline": cpu, "matvec_quantized": mv}
     print(json.dumps(line), flush=True)
+
+
+PROFILE_PHASES = ("copy", "hessian", "rotate_in", "hg_sqrt", "rotate_out", "cholinv", "quantize")
+
+
+def profile_phases(sp, reps: int = 2) -> None:
+    """For counter collection: one full layer step (which leaves every intermediate in place), then a plain
+    fp32 copy of 64 MiB (the reference that scales FETCH_SIZE / WRITE_SIZE to bytes), then each phase of
+    the layer alone, `reps` times. A marker dispatch (kq_hg_extract on a 4 x 4 matrix: hg_extract_kernel,
+    which the layer never runs) precedes the copy and every phase, so that the profiler's per-dispatch
+    records split into PROFILE_PHASES in that order."""
+    import torch
+
+    from post_quantization_03_amd import _lib as K
+    from post_quantization_03_amd.layer import LayerCfg, hg_factor_shape, quantize_layer, workspace_bytes
+
+    dev = torch.device("cuda:0")
+    d = synth.layer_inputs(sp)
+
+    def to(a, kind):
+        if kind == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    X, W, HG = to(d["X"], sp.x_dtype), to(d["W"], sp.w_dtype), to(d["HG"], "f32")
+    s, t = to(d["s"], "i8"), to(d["t"], "i8")
+    del d
+    cfg = LayerCfg(bits=sp.bits, group=sp.group, damp=sp.damp, form=sp.hg_form,
+                   blk=sp.hg_blk if sp.hg_form == "block" else 0)
+    xdt = K.KQ_BF16 if sp.x_dtype == "bf16" else K.KQ_F32
+    ws = torch.empty(workspace_bytes(sp.o, sp.i, sp.n, xdt, cfg), dtype=torch.uint8, device=dev)
+    quantize_layer(X, W, HG, s, t, cfg, ws=ws)
+    torch.cuda.synchronize()
+    o, i, n = sp.o, sp.i, sp.n
+    f32 = dict(dtype=torch.float32, device=dev)
+    H = torch.empty((i, i), dtype=torch.float64, device=dev)
+    W2 = torch.empty((o, i), **f32)
+    S = torch.empty(hg_factor_shape(o, cfg), **f32)
+    R = torch.empty((i, i), **f32)
+    info = torch.zeros(2, dtype=torch.int32, device=dev)
+    ng = i // cfg.group if cfg.group else 1
+    codes = torch.empty((o, i * cfg.bits // 32), dtype=torch.int32, device=dev)
+    scale, offset, rl = torch.empty((o, ng), **f32), torch.empty((o, ng), **f32), torch.empty((o,), **f32)
+    Hm, hm = torch.eye(4, dtype=torch.float64, device=dev), torch.empty(4, **f32)
+    src = torch.ones(64 << 18, **f32)
+    dst = torch.empty_like(src)
+    calls = {
+        "copy": lambda: torch.mul(src, 1.0, out=dst),
+        "hessian": lambda: K.kq_hessian_accum(X, H, 1.0 / n, 0.0, ws),
+        "rotate_in": lambda: K.kq_rotate_in(W, W2, H, s, ws),
+        "hg_sqrt": lambda: K.kq_hg_sqrt(HG, cfg.form, o, cfg.blk, S, None, info[0:1], ws),
+        "rotate_out": lambda: K.kq_rotate_out(W2, S, cfg.form, cfg.blk, t, ws),
+        "cholinv": lambda: K.kq_cholinv(H, cfg.damp, R, info[1:2], ws),
+        "quantize": lambda: K.kq_quantize_layer(W2, R, cfg.bits, cfg.group, cfg.block, codes, scale, offset, rl, ws),
+    }
+    for name in PROFILE_PHASES:
+        K.kq_hg_extract(Hm, "diag", 0, hm)
+        for _ in range(1 if name == "copy" else reps):
+            calls[name]()
+        torch.cuda.synchronize()
+        print(f"# profiled phase {name}", file=sys.stderr, flush=True)
+    print(json.dumps({"profiled": sp.name, "phases": PROFILE_PHASES, "reps": reps, "copy_bytes": src.numel() * 4}),
+          flush=True)
 
 
 def run_stack_line(args) -> None:

@@ -357,14 +357,19 @@ def test_cholinv_reports_not_positive_definite():
 
 # ----------------------------------------------------------------------------- sweep
 @pytest.mark.parametrize("o,i,bits,group", [(37, 384, 3, 128), (37, 384, 4, 0), (64, 256, 2, 128), (20, 512, 2, 0),
-                                            (16, 256, 3, 64), (9, 256, 8, 32), (130, 1024, 3, 128)])
+                                            (16, 256, 3, 64), (9, 256, 8, 32), (130, 1024, 3, 128),
+                                            (16400, 256, 2, 0), (16400, 128, 3, 128)])
 def test_quantize_layer(o, i, bits, group):
+    """From 16384 rows the sweep runs on row panels side by side (16400: four panels, the last one
+    shorter and not a multiple of the 16-row work-group)."""
     torch, dev = torch_dev()
     say(f"quantize o={o} i={i} b={bits} g={group}")
-    sp = synth.scaled(synth.CONFIGS["C2"], o=o, i=i, n=4 * i, hg_ng=2 * o if o >= 64 else 256, n_outliers=2)
+    tall = o > 4096
+    sp = synth.scaled(synth.CONFIGS["C2"], o=o, i=i, n=4 * i, hg_ng=2 * o if 64 <= o <= 4096 else 256, n_outliers=2,
+                      hg_form="diag" if tall else "full")
     d = synth.layer_inputs(sp)
-    hg = d["HG"] if o >= 64 else np.ones(o, f32)
-    form = "full" if o >= 64 else "diag"
+    hg = d["HG"] if 64 <= o <= 4096 else np.ones(o, f32)
+    form = "full" if 64 <= o <= 4096 else "diag"
     r = kq.quantize_layer(synth.widen(d["X"], "bf16"), synth.widen(d["W"], "bf16"), hg.astype(np.float64), form,
                           d["s"], d["t"], bits, group, verify=False, rotate_out_on=False)
     W2 = r["W2"].astype(f32)
@@ -404,10 +409,12 @@ def test_quantize_layer_search(o, i, bits, group, cands):
     than min-max; then codes, words, w^, row loss and grid parameters as for the min-max sweep."""
     torch, dev = torch_dev()
     say(f"quantize search o={o} i={i} b={bits} g={group} candidates={cands}")
-    sp = synth.scaled(synth.CONFIGS["C2"], o=o, i=i, n=4 * i, hg_ng=2 * o if o >= 64 else 256, n_outliers=2)
+    tall = o > 4096
+    sp = synth.scaled(synth.CONFIGS["C2"], o=o, i=i, n=4 * i, hg_ng=2 * o if 64 <= o <= 4096 else 256, n_outliers=2,
+                      hg_form="diag" if tall else "full")
     d = synth.layer_inputs(sp)
-    hg = d["HG"] if o >= 64 else np.ones(o, f32)
-    form = "full" if o >= 64 else "diag"
+    hg = d["HG"] if 64 <= o <= 4096 else np.ones(o, f32)
+    form = "full" if 64 <= o <= 4096 else "diag"
     r = kq.quantize_layer(synth.widen(d["X"], "bf16"), synth.widen(d["W"], "bf16"), hg.astype(np.float64), form,
                           d["s"], d["t"], bits, group, verify=False, rotate_out_on=False)
     W2 = r["W2"].astype(f32)
