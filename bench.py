@@ -60,7 +60,8 @@ def algorithmic_work(sp, db_iters: int) -> dict:
     return {
         "hessian": {"flop": n * i * (i + 1), "bytes": n * i * xb + 8 * i * i, "peak": "bf16_mfma"},
         "rotate_in": {"bytes": o * i * (wb + 4) + 32 * i * i, "peak": "hbm"},
-        "hg_sqrt": {"flop": (2 * db_iters - 1) * o ** 3 if full else 0, "peak": "fp64_alu"},
+        "hg_sqrt": {"flop": (2 * db_iters - 1) * (o ** 3 if full else (o // sp.hg_blk) * sp.hg_blk ** 3)
+                    if sp.hg_form != "diag" else 0, "peak": "fp64_alu"},
         "rotate_out": ({"flop": 2 * o * o * i, "peak": "fp32_mfma"} if full else {"bytes": 8 * o * i, "peak": "hbm"}),
         "cholinv": {"flop": 2 * i ** 3 // 3, "peak": "fp64_alu"},
         "quantize": {"bytes": int((8 + b / 8 + (8 / g if g else 0)) * o * i + 2 * i * i),
@@ -74,6 +75,8 @@ def sources_digest() -> str:
     import glob
     h = hashlib.sha256()
     for f in sorted(glob.glob(os.path.join(ROOT, "post_quantization_03_amd", "csrc", "*"))):
+        if os.path.basename(f) == "probe.hip":   # the throughput probes are not part of the library
+            continue
         with open(f, "rb") as fh:
             h.update(os.path.basename(f).encode() + b"\0" + fh.read())
     return h.hexdigest()
@@ -124,7 +127,8 @@ def run_gpu(sp, steps: int, warmup: int, phases: bool):
             return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
         return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
-    iters = db_steps(d["HG"]) if sp.hg_form == "full" else 0
+    iters = db_steps(d["HG"]) if sp.hg_form == "full" else (
+        max(db_steps(b) for b in d["HG"]) if sp.hg_form == "block" else 0)
     X, W, HG = to(d["X"], sp.x_dtype), to(d["W"], sp.w_dtype), to(d["HG"], "f32")
     s, t = to(d["s"], "i8"), to(d["t"], "i8")
     del d
@@ -602,7 +606,7 @@ def _time_factor(kq, HX2, damp: float, cap: int = 4096) -> tuple[float, str]:
     return dt, ("in full" if k == i else f"on the leading {k} x {k} block scaled by (i/{k})^3")
 
 
-def cpu_baseline(sp) -> dict:
+def cpu_baseline(sp, full: bool = False) -> dict:
     """The float64 oracle, as it stands, on a bounded sample of the same layer (about 10-30 s of CPU work),
     timed per phase and scaled to the whole layer: H_X on at most 2048 tokens, the input rotation of W on
     at most 2048 rows (H_X's rotation in full), the output transform on at most 512 columns (all rows:
@@ -615,6 +619,8 @@ def cpu_baseline(sp) -> dict:
 
     cores, limiter = _blas_threads()
     n_tok, r_in, c_out, n_rows = min(sp.n, 2048), min(sp.o, 2048), min(sp.i, 512), min(sp.o, 128)
+    if full:
+        n_tok, r_in, c_out, n_rows = sp.n, sp.o, sp.i, sp.o
     d = synth.layer_inputs(sp, x_rows=n_tok)
     X = synth.widen(d["X"], sp.x_dtype)
     W = synth.widen(d["W"], sp.w_dtype)
@@ -627,25 +633,45 @@ def cpu_baseline(sp) -> dict:
     t0 = time.perf_counter()
     W1 = kq.rotate_in_weights(W[:r_in], d["s"])
     t["rotate_in"] = (time.perf_counter() - t0) * sp.o / r_in
-    dt, how_rot = _time_hessian_rotation(kq, HX, d["s"])
-    t["rotate_in"] += dt
+    if full:
+        t0 = time.perf_counter()
+        HX2 = kq.rotate_in_hessian(HX, d["s"])
+        t["rotate_in"] += time.perf_counter() - t0
+        how_rot = "in full"
+    else:
+        dt, how_rot = _time_hessian_rotation(kq, HX, d["s"])
+        t["rotate_in"] += dt
     t0 = time.perf_counter()
     S, _ = kq.hg_sqrt(HG, sp.hg_form)
     t["hg_sqrt"] = time.perf_counter() - t0
     t0 = time.perf_counter()
     kq.rotate_out(W[:, :c_out], S, sp.hg_form, d["t"])
     t["rotate_out"] = (time.perf_counter() - t0) * sp.i / c_out
-    dt, how_fac = _time_factor(kq, HX, sp.damp)
-    t["cholinv"] = dt
-    # the sweep needs a factor of the whole width: R of the (unrotated) H_X, untimed, stands in for R of H_X'
-    H, _ = kq.damped(HX, sp.damp)
-    R = np.linalg.cholesky(np.linalg.inv(H)).T if sp.i <= 4096 else np.diag(1.0 / np.sqrt(np.diag(H)))
+    if full:
+        # the whole layer as the oracle computes it: R of the rotated H_X, the sweep on W'' = V S W'
+        t0 = time.perf_counter()
+        H, _ = kq.damped(HX2, sp.damp)
+        R = kq.inverse_upper_factor(H)
+        t["cholinv"] = time.perf_counter() - t0
+        how_fac = "in full"
+        W2 = kq.rotate_out(W1, S, sp.hg_form, d["t"])
+    else:
+        dt, how_fac = _time_factor(kq, HX, sp.damp)
+        t["cholinv"] = dt
+        # the sweep needs a factor of the whole width: R of the (unrotated) H_X, untimed, stands in for R of H_X'
+        H, _ = kq.damped(HX, sp.damp)
+        R = np.linalg.cholesky(np.linalg.inv(H)).T if sp.i <= 4096 else np.diag(1.0 / np.sqrt(np.diag(H)))
+        W2 = W1
     t0 = time.perf_counter()
-    kq.sweep_blocked(W1[:n_rows], R, sp.bits, sp.group, sp.block)
+    kq.sweep_blocked(W2[:n_rows], R, sp.bits, sp.group, sp.block)
     t["quantize"] = (time.perf_counter() - t0) * sp.o / n_rows
     if limiter is not None and hasattr(limiter, "unregister"):
         limiter.unregister()
     total = sum(t.values())
+    if full:
+        return {"value": sp.o * sp.i / total / 1e6, "unit": "Mweights/s", "cores": cores, "kind": "oracle",
+                "sample": f"float64 oracle on the whole layer, every phase in full; layer time {total:.1f} s",
+                "phases_s": {k: round(v, 3) for k, v in t.items()}}
     sample = (f"H_X on {n_tok} of {sp.n} tokens, rotation of W on {r_in} of {sp.o} rows, output transform on "
               f"{c_out} of {sp.i} columns, sweep on {n_rows} of {sp.o} rows (each scaled to the whole layer); "
               f"rotation of H_X {how_rot}, damped factor (of H_X: the same size and cost as of H_X') {how_fac}, "
@@ -827,6 +853,12 @@ def main():
     ap.add_argument("--drift", action="store_true",
                     help="compare GPTQ with the input-drift-corrected solver on drifted synthetic inputs and print "
                          "the result as its own JSON line")
+    ap.add_argument("--cpu-full", action="store_true",
+                    help="time the float64 oracle on the whole workload layer (every phase in full, minutes for the "
+                         "large layers) and print it as a JSON line (no GPU work)")
+    ap.add_argument("--probe-peaks", action="store_true",
+                    help="measure the fp64/fp32 vector and fp64/fp32/bf16 matrix-core throughput and the HBM copy rate "
+                         "of this GPU (prints a JSON line, not the benchmark line)")
     ap.add_argument("--profile-phases", action="store_true",
                     help="for rocprofv3 counter runs: each phase of the workload's layer alone, twice, after one full "
                          "step, with a marker dispatch before each (prints a JSON line naming the phases, not the "
@@ -839,10 +871,16 @@ def main():
         print("bench.py measures one GPU: the per-layer solver runs on a single MI355X in this build "
               "(multi-GPU sharding is described in DESIGN.md, not implemented).", file=sys.stderr)
         sys.exit(2)
+    if args.probe_peaks:
+        print(json.dumps({"probe_peaks": probe_peaks()}), flush=True)
+        return
     if args.workload == "C5":
         run_stack_line(args)
         return
     sp = synth.CONFIGS[args.workload]
+    if args.cpu_full:
+        print(json.dumps({"workload": sp.name, "cpu_oracle_full": cpu_baseline(sp, full=True)}), flush=True)
+        return
     if args.profile_phases:
         profile_phases(sp)
         return
@@ -908,6 +946,45 @@ def main():
             "roofline": roof, "phases_roofline": per_phase, "phases_aggregate": aggregates,
             "sweep_critical_path": chain, "cpu_baseline": cpu, "matvec_quantized": mv}
     print(json.dumps(line), flush=True)
+
+
+def probe_peaks() -> dict:
+    """Measured ceilings of the execution units and HBM on this GPU (libkqprobe.so): dependency-free
+    fp64/fp32 vector FMA loops, fp64/fp32/bf16 matrix-core loops over every compute unit, and a 4 GiB
+    device copy; each timed with HIP events after a warm-up launch. The vendor figures (PEAK) stay the
+    roofline denominators; these say what the units deliver here."""
+    import ctypes
+
+    import torch
+
+    path = os.path.join(ROOT, "post_quantization_03_amd", "libkqprobe.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built: run `python -m post_quantization_03_amd.build`")
+    L = ctypes.CDLL(path)
+    L.kq_probe_run.restype = ctypes.c_int
+    L.kq_probe_run.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
+                               ctypes.c_void_p, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)]
+    dev = torch.device("cuda:0")
+    scratch = torch.empty(8 << 20, dtype=torch.uint8, device=dev)
+    nbytes = 4 << 30
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    kinds = {"fp64_vector_fma": (0, 20000, "TFLOP/s", 78.6), "fp64_mfma_16x16x4": (1, 20000, "TFLOP/s", 78.6),
+             "fp32_mfma_16x16x4": (2, 20000, "TFLOP/s", 157.3), "bf16_mfma_16x16x32": (3, 20000, "TFLOP/s", 2500.0),
+             "fp32_vector_fma": (4, 20000, "TFLOP/s", 157.3), "hbm_copy": (5, 0, "GB/s", 8000.0),
+             "fp64_mfma_and_vector_side_by_side": (6, 20000, "TFLOP/s", 78.6)}
+    out = {}
+    for name, (kind, iters, unit, vendor) in kinds.items():
+        sec, work = ctypes.c_double(), ctypes.c_double()
+        rc = L.kq_probe_run(kind, iters, nbytes, scratch.data_ptr(), src.data_ptr(), dst.data_ptr(),
+                            ctypes.byref(sec), ctypes.byref(work))
+        if rc != 0:
+            raise RuntimeError(f"probe {name} failed ({rc})")
+        rate = work.value / sec.value / (1e12 if unit == "TFLOP/s" else 1e9)
+        out[name] = {"measured": round(rate, 2), "unit": unit, "vendor_peak": vendor, "frac_of_vendor": round(rate / vendor, 3),
+                     "ms": round(sec.value * 1e3, 3)}
+        print(f"# probe {name}: {rate:.1f} {unit}", file=sys.stderr, flush=True)
+    return out
 
 
 PROFILE_PHASES = ("copy", "hessian", "rotate_in", "hg_sqrt", "rotate_out", "cholinv", "quantize")

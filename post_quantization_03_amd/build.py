@@ -14,6 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libkq.so")
+PROBE_LIB = os.path.join(HERE, "libkqprobe.so")
 SOURCES = ("api", "dense", "gj", "syrk", "hadamard", "sweep", "dequant", "hgprep")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-Wno-unused-result", "-Wno-unused-value",
          "-Wno-pass-failed", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
@@ -45,8 +46,16 @@ def build(verbose: bool = True) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr[-4000:]}")
     os.replace(tmp, LIB)
+    # the throughput probes of the execution units and HBM: a library of their own, outside the C ABI
+    pobj = _compile("probe")
+    ptmp = PROBE_LIB + ".tmp"
+    r = subprocess.run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", ptmp, pobj], capture_output=True,
+                       text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"probe link failed:\n{r.stderr[-4000:]}")
+    os.replace(ptmp, PROBE_LIB)
     if verbose:
-        print(f"built {LIB}", file=sys.stderr)
+        print(f"built {LIB} and {PROBE_LIB}", file=sys.stderr)
     return LIB
 
 
