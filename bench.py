@@ -626,9 +626,15 @@ def cpu_baseline(sp, full: bool = False) -> dict:
     W = synth.widen(d["W"], sp.w_dtype)
     HG = d["HG"].astype(np.float64)
     t = {}
+
+    def done(phase: str) -> None:   # progress of the long full-size runs
+        if full:
+            print(f"# oracle {phase}: {t.get(phase, 0.0):.1f} s", file=sys.stderr, flush=True)
+
     t0 = time.perf_counter()
     HX = kq.hessian(X)
     t["hessian"] = (time.perf_counter() - t0) * sp.n / n_tok
+    done("hessian")
     del X
     t0 = time.perf_counter()
     W1 = kq.rotate_in_weights(W[:r_in], d["s"])
@@ -637,6 +643,7 @@ def cpu_baseline(sp, full: bool = False) -> dict:
         t0 = time.perf_counter()
         HX2 = kq.rotate_in_hessian(HX, d["s"])
         t["rotate_in"] += time.perf_counter() - t0
+        done("rotate_in")
         how_rot = "in full"
     else:
         dt, how_rot = _time_hessian_rotation(kq, HX, d["s"])
@@ -644,15 +651,18 @@ def cpu_baseline(sp, full: bool = False) -> dict:
     t0 = time.perf_counter()
     S, _ = kq.hg_sqrt(HG, sp.hg_form)
     t["hg_sqrt"] = time.perf_counter() - t0
+    done("hg_sqrt")
     t0 = time.perf_counter()
     kq.rotate_out(W[:, :c_out], S, sp.hg_form, d["t"])
     t["rotate_out"] = (time.perf_counter() - t0) * sp.i / c_out
+    done("rotate_out")
     if full:
         # the whole layer as the oracle computes it: R of the rotated H_X, the sweep on W'' = V S W'
         t0 = time.perf_counter()
         H, _ = kq.damped(HX2, sp.damp)
         R = kq.inverse_upper_factor(H)
         t["cholinv"] = time.perf_counter() - t0
+        done("cholinv")
         how_fac = "in full"
         W2 = kq.rotate_out(W1, S, sp.hg_form, d["t"])
     else:
@@ -662,15 +672,26 @@ def cpu_baseline(sp, full: bool = False) -> dict:
         H, _ = kq.damped(HX, sp.damp)
         R = np.linalg.cholesky(np.linalg.inv(H)).T if sp.i <= 4096 else np.diag(1.0 / np.sqrt(np.diag(H)))
         W2 = W1
-    t0 = time.perf_counter()
-    kq.sweep_blocked(W2[:n_rows], R, sp.bits, sp.group, sp.block)
-    t["quantize"] = (time.perf_counter() - t0) * sp.o / n_rows
+    if full:
+        # rows are independent once R is fixed: the whole sweep in row chunks, with progress between them
+        t["quantize"] = 0.0
+        for r0 in range(0, sp.o, 4096):
+            t0 = time.perf_counter()
+            kq.sweep_blocked(W2[r0:r0 + 4096], R, sp.bits, sp.group, sp.block)
+            t["quantize"] += time.perf_counter() - t0
+            print(f"# oracle sweep: rows {r0}..{min(sp.o, r0 + 4096)} done", file=sys.stderr, flush=True)
+    else:
+        t0 = time.perf_counter()
+        kq.sweep_blocked(W2[:n_rows], R, sp.bits, sp.group, sp.block)
+        t["quantize"] = (time.perf_counter() - t0) * sp.o / n_rows
+    done("quantize")
     if limiter is not None and hasattr(limiter, "unregister"):
         limiter.unregister()
     total = sum(t.values())
     if full:
         return {"value": sp.o * sp.i / total / 1e6, "unit": "Mweights/s", "cores": cores, "kind": "oracle",
-                "sample": f"float64 oracle on the whole layer, every phase in full; layer time {total:.1f} s",
+                "sample": (f"float64 oracle on the whole layer, every phase in full (the sweep over row chunks of 4096, "
+                           f"rows being independent once R is fixed); layer time {total:.1f} s"),
                 "phases_s": {k: round(v, 3) for k, v in t.items()}}
     sample = (f"H_X on {n_tok} of {sp.n} tokens, rotation of W on {r_in} of {sp.o} rows, output transform on "
               f"{c_out} of {sp.i} columns, sweep on {n_rows} of {sp.o} rows (each scaled to the whole layer); "
