@@ -320,10 +320,9 @@ __global__ __launch_bounds__(256) void dgemm_valu_kernel(GemmArgs<double> g) {
         const int64_t L = g.tri ? (int64_t)gridDim.x : (int64_t)gridDim.x * gridDim.y;
         int64_t lid = g.tri ? (int64_t)blockIdx.x : (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
         // Work-groups go to the 8 XCDs round-robin by id: give XCD x a contiguous run of tiles
-        // (a bijection for any L; runs differ in length by at most one). Not when the K range depends
-        // on the tile (triangular operands): a contiguous run of rows would give one XCD all the long
-        // tiles, so those keep the round-robin spread.
-        if (g.kmode == 0) {
+        // (a bijection for any L; runs differ in length by at most one), so that tiles sharing a row
+        // panel of A meet in one XCD's L2.
+        {
             const int64_t x = lid % 8, q = lid / 8, base = L / 8, rem = L % 8;
             lid = x * base + (x < rem ? x : rem) + q;
         }
@@ -331,12 +330,20 @@ __global__ __launch_bounds__(256) void dgemm_valu_kernel(GemmArgs<double> g) {
             tm = lid / nx;  // row-block tiles (own_rows): never triangular
             tn = lid % nx;
         } else if (g.kmode && !g.tri) {
-            // longest K ranges first: K grows with the tile row when it ends at the row (bit 2) and
-            // with the tile column when it ends at the column (bit 3)
+            // K ranges that depend on the tile (triangular operands): the runs above take the rows in
+            // the order of their residue mod 8 (rows 0, 8, 16, .., then 1, 9, ..), so each XCD gets
+            // whole rows (A panels shared in its L2) spread over the matrix (long and short K ranges
+            // alike); within a residue class and a row, the longest K ranges come first (K grows with
+            // the tile row when it ends at the row, bit 2, and with the column when it ends there, bit 3)
             const int64_t ny = (g.M + BM - 1) / BM;
-            tm = lid / nx;
+            const int64_t rho = lid / nx, b8 = ny / 8, r8 = ny % 8;
+            int64_t c = 0;
+            while (c + 1 < 8 && (c + 1) * b8 + (c + 1 < r8 ? c + 1 : r8) <= rho) c++;
+            const int64_t start = c * b8 + (c < r8 ? c : r8), len = b8 + (c < r8 ? 1 : 0);
+            int64_t w = rho - start;
+            if (g.kmode & 4) w = len - 1 - w;
+            tm = c + 8 * w;
             tn = lid % nx;
-            if (g.kmode & 4) tm = ny - 1 - tm;
             if (g.kmode & 8) tn = nx - 1 - tn;
         } else if (g.tri) {
             int64_t r = (int64_t)((sqrt(8.0 * (double)lid + 1.0) - 1.0) * 0.5);
