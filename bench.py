@@ -665,6 +665,7 @@ def cpu_baseline(sp, full: bool = False) -> dict:
         done("cholinv")
         how_fac = "in full"
         W2 = kq.rotate_out(W1, S, sp.hg_form, d["t"])
+        print("# oracle: W'' for the sweep ready (untimed, the same product as rotate_out)", file=sys.stderr, flush=True)
     else:
         dt, how_fac = _time_factor(kq, HX, sp.damp)
         t["cholinv"] = dt
@@ -674,12 +675,15 @@ def cpu_baseline(sp, full: bool = False) -> dict:
         W2 = W1
     if full:
         # rows are independent once R is fixed: the whole sweep in row chunks, with progress between them
+        # (chunks of about a minute: the sweep's cost per row grows with the square of the width)
         t["quantize"] = 0.0
-        for r0 in range(0, sp.o, 4096):
+        chunk = 4096 if sp.i <= 4096 else 1024
+        for r0 in range(0, sp.o, chunk):
             t0 = time.perf_counter()
-            kq.sweep_blocked(W2[r0:r0 + 4096], R, sp.bits, sp.group, sp.block)
+            kq.sweep_blocked(W2[r0:r0 + chunk], R, sp.bits, sp.group, sp.block)
             t["quantize"] += time.perf_counter() - t0
-            print(f"# oracle sweep: rows {r0}..{min(sp.o, r0 + 4096)} done", file=sys.stderr, flush=True)
+            print(f"# oracle sweep: rows {r0}..{min(sp.o, r0 + chunk)} done ({t['quantize']:.0f} s)", file=sys.stderr,
+                  flush=True)
     else:
         t0 = time.perf_counter()
         kq.sweep_blocked(W2[:n_rows], R, sp.bits, sp.group, sp.block)
@@ -690,7 +694,7 @@ def cpu_baseline(sp, full: bool = False) -> dict:
     total = sum(t.values())
     if full:
         return {"value": sp.o * sp.i / total / 1e6, "unit": "Mweights/s", "cores": cores, "kind": "oracle",
-                "sample": (f"float64 oracle on the whole layer, every phase in full (the sweep over row chunks of 4096, "
+                "sample": (f"float64 oracle on the whole layer, every phase in full (the sweep over row chunks of {chunk}, "
                            f"rows being independent once R is fixed); layer time {total:.1f} s"),
                 "phases_s": {k: round(v, 3) for k, v in t.items()}}
     sample = (f"H_X on {n_tok} of {sp.n} tokens, rotation of W on {r_in} of {sp.o} rows, output transform on "

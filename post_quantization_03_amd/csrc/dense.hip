@@ -279,10 +279,11 @@ template kq_status gemm<float>(const GemmArgs<float>&, bool, bool, hipStream_t);
 // dependency-free loop, while the fp64 vector FMA pipe sustains about 59 (both measured on MI355X with
 // one-kernel probes), so fp64 products run on vector FMAs. 256 threads own a BM x BN tile of C; thread
 // (tr, tc) = (tid / 16, tid % 16) keeps a register tile of rows h * BM/2 + tr * RG + i and columns
-// h * BN/2 + tc * CG + j (h = 0, 1; RG = BM/32, CG = BN/32). Operands are staged k-major in LDS
-// (double-buffered 16-deep K slices, one barrier per slice) and read as 16-byte vectors; the lanes of a
-// wave that share a row group read the same A address (broadcast) and the 16 column groups read one
-// contiguous run of B. Tile order, triangular launch, K restriction and epilogue follow the MFMA
+// h * BN/2 + 32 p + 2 tc + e (h = 0, 1; RG = BM/32; CG = BN/32 columns per half as CG/2 pairs p, e = 0, 1).
+// Operands are staged k-major in LDS (double-buffered 16-deep K slices, one barrier per slice) and read
+// as 16-byte vectors; the lanes of a wave that share a row group read the same A address (broadcast),
+// and the 16 column groups read one contiguous 256-byte run of B per instruction (column pairs 32
+// apart: four adjacent columns per thread would put the lanes 32 bytes apart, a two-way bank conflict). Tile order, triangular launch, K restriction and epilogue follow the MFMA
 // kernel above.
 template <int BM, int BN, bool TA, bool TB, bool VEC>
 __global__ __launch_bounds__(256) void dgemm_valu_kernel(GemmArgs<double> g) {
@@ -413,7 +414,7 @@ __global__ __launch_bounds__(256) void dgemm_valu_kernel(GemmArgs<double> g) {
                 for (int hj = 0; hj < 2; hj++)
 #pragma unroll
                     for (int j = 0; j < CG; j += 2) {
-                        const int64_t m = m0 + hi * (BM / 2) + tr * RG + i, n = n0 + hj * (BN / 2) + tc * CG + j;
+                        const int64_t m = m0 + hi * (BM / 2) + tr * RG + i, n = n0 + hj * (BN / 2) + (j >> 1) * 32 + 2 * tc + (j & 1);
                         const V16<double> t = *reinterpret_cast<const V16<double>*>(C + m * g.ldc + n);
                         acc[hi][i][hj][j] = -t.v[0];
                         acc[hi][i][hj][j + 1] = -t.v[1];
@@ -501,7 +502,7 @@ __global__ __launch_bounds__(256) void dgemm_valu_kernel(GemmArgs<double> g) {
                     }
 #pragma unroll
                     for (int j = 0; j < CG; j += 2) {
-                        const V16<double> t = *reinterpret_cast<const V16<double>*>(&Bs[buf][kk][h * (BN / 2) + tc * CG + j]);
+                        const V16<double> t = *reinterpret_cast<const V16<double>*>(&Bs[buf][kk][h * (BN / 2) + (j >> 1) * 32 + 2 * tc]);
                         b[h][j] = t.v[0]; b[h][j + 1] = t.v[1];
                     }
                 }
@@ -532,7 +533,7 @@ __global__ __launch_bounds__(256) void dgemm_valu_kernel(GemmArgs<double> g) {
                 for (int hj = 0; hj < 2; hj++)
 #pragma unroll
                     for (int j = 0; j < CG; j += 2) {
-                        const int64_t m = m0 + hi * (BM / 2) + tr * RG + i, n = n0 + hj * (BN / 2) + tc * CG + j;
+                        const int64_t m = m0 + hi * (BM / 2) + tr * RG + i, n = n0 + hj * (BN / 2) + (j >> 1) * 32 + 2 * tc + (j & 1);
                         *reinterpret_cast<V16<double>*>(C + m * g.ldc + n) =
                             V16<double>{{-acc[hi][i][hj][j], -acc[hi][i][hj][j + 1]}};
                     }
@@ -550,7 +551,7 @@ __global__ __launch_bounds__(256) void dgemm_valu_kernel(GemmArgs<double> g) {
                     for (int hj = 0; hj < 2; hj++)
 #pragma unroll
                         for (int j = 0; j < CG; j += 2) {
-                            const int64_t m = m0 + hi * (BM / 2) + tr * RG + i, n = n0 + hj * (BN / 2) + tc * CG + j;
+                            const int64_t m = m0 + hi * (BM / 2) + tr * RG + i, n = n0 + hj * (BN / 2) + (j >> 1) * 32 + 2 * tc + (j & 1);
                             cv[i][hj][j / 2] = *reinterpret_cast<const V16<double>*>(C + m * g.ldc + n);
                         }
             }
@@ -560,7 +561,7 @@ __global__ __launch_bounds__(256) void dgemm_valu_kernel(GemmArgs<double> g) {
                 for (int hj = 0; hj < 2; hj++)
 #pragma unroll
                     for (int j = 0; j < CG; j += 2) {
-                        const int64_t m = m0 + hi * (BM / 2) + tr * RG + i, n = n0 + hj * (BN / 2) + tc * CG + j;
+                        const int64_t m = m0 + hi * (BM / 2) + tr * RG + i, n = n0 + hj * (BN / 2) + (j >> 1) * 32 + 2 * tc + (j & 1);
                         V16<double> v;
                         v.v[0] = alpha * acc[hi][i][hj][j];
                         v.v[1] = alpha * acc[hi][i][hj][j + 1];
@@ -583,7 +584,7 @@ __global__ __launch_bounds__(256) void dgemm_valu_kernel(GemmArgs<double> g) {
                 for (int hj = 0; hj < 2; hj++)
 #pragma unroll
                     for (int j = 0; j < CG; j++) {
-                        const int64_t m = m0 + hi * (BM / 2) + tr * RG + i, n = n0 + hj * (BN / 2) + tc * CG + j;
+                        const int64_t m = m0 + hi * (BM / 2) + tr * RG + i, n = n0 + hj * (BN / 2) + (j >> 1) * 32 + 2 * tc + (j & 1);
                         cv[i][hj][j] = (m < M && n < N) ? C[m * g.ldc + n] : 0.0;
                     }
         }
@@ -593,7 +594,7 @@ __global__ __launch_bounds__(256) void dgemm_valu_kernel(GemmArgs<double> g) {
             for (int hj = 0; hj < 2; hj++)
 #pragma unroll
                 for (int j = 0; j < CG; j++) {
-                    const int64_t m = m0 + hi * (BM / 2) + tr * RG + i, n = n0 + hj * (BN / 2) + tc * CG + j;
+                    const int64_t m = m0 + hi * (BM / 2) + tr * RG + i, n = n0 + hj * (BN / 2) + (j >> 1) * 32 + 2 * tc + (j & 1);
                     if (m >= M || n >= N) continue;
                     if (g.tri == 1 && n > m) continue;
                     if (g.tri == 2 && m > n) continue;
