@@ -21,8 +21,10 @@
  *  - Calls validate their arguments on the host, enqueue their kernels on `stream` (a
  *    hipStream_t; NULL = the default stream) and return without synchronising the host, except
  *    kq_hg_sqrt (block and full forms) and kq_hg_lowrank: they wait once, after the first
- *    Denman-Beavers step, to read back the interval bounds that fix the number of further steps,
- *    and they refuse (KQ_EINVAL) a stream that is capturing a HIP graph. Errors found on the host
+ *    Denman-Beavers step, to read back the number of further steps (counted on the device from
+ *    that step's interval bounds) into a 16-byte pinned host buffer of the calling host thread
+ *    (allocated on its first such call and kept until the process ends), and they refuse
+ *    (KQ_EINVAL) a stream that is capturing a HIP graph. Errors found on the host
  *    are returned; numerical failures found on the device (a matrix that is not positive definite)
  *    are written to a device int32 `info` (0 = success) that the caller reads after synchronising
  *    the stream.
@@ -124,9 +126,9 @@ kq_status kq_rotate_in(const void* Win, kq_dtype wdt, int64_t ldwin, float* Wout
  * iteration in fp64 whose SPD inverses are symmetric block Gauss-Jordan sweeps, stopped on a
  * device-side convergence test (at most 7 steps; enough for cond(H_G) <= 1e16). The sweep runs on
  * the two queues of the device named above, forked from and joined back into `stream`. The call
- * returns only after the first step has completed on the device: it reads back that step's
- * interval bounds (nbk doubles) and launches exactly the further steps they imply; the rest is
- * asynchronous on `stream`. A stream that is capturing a graph is refused (KQ_EINVAL). The sweep's
+ * returns only after the first step has completed on the device: it reads back the number of
+ * further steps that step's interval bounds imply (counted on the device) and launches exactly
+ * those; the rest is asynchronous on `stream`. A stream that is capturing a graph is refused (KQ_EINVAL). The sweep's
  * pivot kernels wait on the device, in a bounded loop, for the other queue's work, through a counter
  * in the call's workspace; where the device runs kernels one at a time (some profilers), that wait
  * runs out in the first step, and the call then redoes its work with queue waits and leaves a notice

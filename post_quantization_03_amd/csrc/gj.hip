@@ -1116,6 +1116,36 @@ __global__ void db_converge_kernel(const double* part, const double* bnd, int64_
     if (bmax < DB_TOL) flags[0] = 1;
 }
 
+// The number of steps the iteration takes (the first included), from the interval bounds after the
+// first step by the recursion of db_scale_kernel (the same fp64 operations; a non-finite bound
+// counts one step), and the other words the host reads after that step: out[0] = steps, out[1] =
+// flags[0] (stopped: converged or failed), out[2] = 1 if a device-side wait of the sweep ran out.
+__global__ __launch_bounds__(256) void db_plan_kernel(const double* bnd, int64_t nbk, const int* flags,
+                                                      const uint64_t* ready, int* out) {
+    __shared__ int sk[256];
+    int need = 1;
+    for (int64_t b = threadIdx.x; b < nbk; b += 256) {
+        double bb = bnd[b];
+        int k = 1;
+        while (bb - 1.0 >= DB_TOL && k < DB_MAXIT) {
+            bb = 0.5 * (sqrt(bb) + 1.0 / sqrt(bb));
+            k++;
+        }
+        need = need > k ? need : k;
+    }
+    sk[threadIdx.x] = need;
+    __syncthreads();
+    for (int w = 128; w > 0; w >>= 1) {
+        if ((int)threadIdx.x < w) sk[threadIdx.x] = sk[threadIdx.x] > sk[threadIdx.x + w] ? sk[threadIdx.x] : sk[threadIdx.x + w];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) {
+        out[0] = sk[0];
+        out[1] = flags[0];
+        out[2] = ready[1] != 0 ? 1 : 0;
+    }
+}
+
 __global__ void db_final_kernel(const int* flags, int32_t* info, int32_t code) {
     if (threadIdx.x == 0 && !flags[0] && *info == 0) *info = code;
 }
@@ -1181,6 +1211,22 @@ static void hg_layout(Ar& a, int64_t n, int64_t nbk) {
     a.template take<double>(2 * DB_UPD_BLOCKS);              // partial sums
     a.template take<int>(4);                                 // flags
     a.template take<uint64_t>(2);                            // sweep hand-over counter and ran-out word
+    a.template take<int>(4);                                 // words read back after the first step
+}
+
+// Host side of the square root's one readback: pinned memory, which the copy engine writes
+// directly (no staging through a runtime buffer). One 16-byte buffer per host thread, allocated on
+// the thread's first call and kept until the process ends.
+static kq_status plan_host(int** out) {
+    thread_local int* buf = nullptr;
+    if (!buf) {
+        void* p = nullptr;
+        if (hipHostMalloc(&p, 4 * sizeof(int), hipHostMallocPortable) != hipSuccess || !p)
+            return fail(KQ_EHIP, "square root: pinned host buffer for the readback");
+        buf = static_cast<int*>(p);
+    }
+    *out = buf;
+    return KQ_OK;
 }
 
 }  // namespace kq
@@ -1219,6 +1265,7 @@ static kq_status db_sqrt(const float* HGf, const double* HGd, int64_t n, int64_t
     double* part = ar.take<double>(2 * DB_UPD_BLOCKS);
     int* flags = ar.take<int>(4);
     uint64_t* ready = ar.take<uint64_t>(2);
+    int* plan = ar.take<int>(4);
     const int* done = flags;
     SweepSync sync;
     sync.ready = ready;
@@ -1261,16 +1308,15 @@ static kq_status db_sqrt(const float* HGf, const double* HGd, int64_t n, int64_t
         KQ_TRY(check_launch("db_converge"));
         if (it == 0) {
             // After the first step the interval bound of every block is known, and the later bounds
-            // follow from it in closed form (the recursion of db_scale_kernel, in the same fp64
-            // operations): read it back and launch exactly the steps the device test will need,
-            // instead of sweeps that would only skip.
-            std::vector<double> hb((size_t)nbk);
-            int hf[4] = {0, 0, 0, 0};
-            uint64_t ran_out = 0;
-            KQ_HIP(hipMemcpyAsync(hb.data(), bnd, (size_t)nbk * sizeof(double), hipMemcpyDeviceToHost, st));
-            KQ_HIP(hipMemcpyAsync(hf, flags, sizeof(hf), hipMemcpyDeviceToHost, st));
-            KQ_HIP(hipMemcpyAsync(&ran_out, ready + 1, sizeof(ran_out), hipMemcpyDeviceToHost, st));
+            // follow from it in closed form: the device counts the steps they imply, the host reads
+            // that count back and launches exactly those steps, instead of sweeps that would only skip.
+            int* hp = nullptr;
+            KQ_TRY(plan_host(&hp));
+            hipLaunchKernelGGL(db_plan_kernel, dim3(1), dim3(256), 0, st, bnd, nbk, flags, ready, plan);
+            KQ_TRY(check_launch("db_plan"));
+            KQ_HIP(hipMemcpyAsync(hp, plan, 4 * sizeof(int), hipMemcpyDeviceToHost, st));
             KQ_HIP(hipStreamSynchronize(st));
+            const int need = hp[0], stopped = hp[1], ran_out = hp[2];
             if (ran_out) {
                 // the device ran the sweep's queues one kernel at a time: redo this call with queue
                 // waits (nothing is kept for later calls)
@@ -1279,17 +1325,7 @@ static kq_status db_sqrt(const float* HGf, const double* HGd, int64_t n, int64_t
                           "with queue waits");
                 return KQ_OK;
             }
-            if (hf[0]) break;  // converged after one step, or stopped on an error (info set)
-            int need = 1;
-            for (int64_t b = 0; b < nbk; b++) {
-                double bb = hb[(size_t)b];
-                int k = 1;
-                while (bb - 1.0 >= DB_TOL && k < DB_MAXIT) {
-                    bb = 0.5 * (sqrt(bb) + 1.0 / sqrt(bb));
-                    k++;
-                }
-                need = need > k ? need : k;
-            }
+            if (stopped) break;  // converged after one step, or stopped on an error (info set)
             nsteps = need;
         }
     }
