@@ -245,6 +245,14 @@ __device__ inline void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// Orders a wave's LDS writes before its later LDS reads of other lanes' data: the hardware runs a
+// wave's LDS operations in order, so only the compiler has to be kept from reordering them.
+__device__ inline void wave_lds_order() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // 1/p to full fp64 precision: hardware reciprocal estimate refined by two Newton steps.
 __device__ inline double recip64(double p) {
     double r = __builtin_amdgcn_rcp(p);
@@ -276,15 +284,15 @@ __device__ __forceinline__ void pivot_tm(const double (*rowb)[GJ_NB], const doub
 
 // Pinv = P^{-1} for the nbk x nbk SPD pivot P = C[k0 : k0 + nbk][0 : nbk] (identity-padded to 128) by
 // a Gauss-Jordan sweep held in registers: 512 threads, thread (tr, tc) owns rows 4tr..4tr+3 and
-// columns 4tc..4tc+3, 64+4tc..64+4tc+3 (two waves per SIMD). Pivots are taken four at a time (J = 4jb..4jb+3, pivot
+// columns 32p + 2tc + e (p = 0..3, e = 0, 1; two waves per SIMD). Pivots are taken four at a time (J = 4jb..4jb+3, pivot
 // block D = A_JJ) with the symmetric sweep
 //     A_RR -= A_RJ D^{-1} A_JR,  A_RJ <- A_RJ D^{-1},  A_JR <- D^{-1} A_JR,  A_JJ <- -D^{-1},
 // which keeps A symmetric. All four cases are one rank-4 update A -= (A_.J - E_.J) D^{-1} (A_J. - E_J.)
 // (E the identity) followed by A_JJ -= 2I, so every thread runs the same code: it reads the shifted
 // pivot rows A_J. - E_J. and D^{-1} from LDS, takes its column factor from those rows by symmetry and
 // updates its tile. The next step's pivot rows are written by their owners right after their update,
-// and the single thread that holds the next 4 x 4 pivot block inverts it and writes D^{-1}, so one
-// barrier per step separates the steps (LDS double-buffered).
+// and one of those threads reads the next 4 x 4 pivot block back from them, inverts it and writes
+// D^{-1}, so one barrier per step separates the steps (LDS double-buffered).
 // The block is first scaled to unit diagonal (A = S P S, S = diag(P)^{-1/2}); every pivot block of
 // the sweep is then a Schur complement with entries of magnitude <= 1, so the identity shifts cancel
 // nothing larger than the result. After the last step the registers hold -A^{-1}, and
@@ -367,9 +375,10 @@ __global__ __launch_bounds__(GJ_PIV_THREADS) void gj_pivot_kernel(const double* 
         __syncthreads();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     }
-    // column cc of the thread's tile: two runs of four, 64 apart, so that the 16 column groups of a
-    // wave read one contiguous 512-byte run per LDS instruction
-    auto col = [&](int cc) { return (cc >> 2) * 64 + 4 * tc + (cc & 3); };
+    // column cc of the thread's tile: four pairs, 32 apart, so that the 16 column groups of a wave
+    // read one contiguous 256-byte run per 16-byte LDS read (four adjacent columns per thread would
+    // put the lanes 32 bytes apart: a two-way bank conflict)
+    auto col = [&](int cc) { return (cc >> 1) * 32 + 2 * tc + (cc & 1); };
     const int64_t z = blockIdx.x;
     const double* P = C + z * sC + k0 * GJ_NB;
     double sr[4], sc[8];
@@ -402,13 +411,16 @@ __global__ __launch_bounds__(GJ_PIV_THREADS) void gj_pivot_kernel(const double* 
             for (int q = 0; q < 4; q++)
 #pragma unroll
                 for (int cc = 0; cc < 8; cc++) rowb[buf][q][col(cc)] = a[q][cc] - (col(cc) == 4 * j + q ? 1.0 : 0.0);
-            if (tc == (j & 15)) {
+            // the pivot block spans two lanes: one lane reads it back from the rows just published
+            // (LDS operations of a wave complete in order; the wave barrier keeps the compiler from
+            // moving the reads above the writes)
+            wave_lds_order();
+            if (tc == 0) {
                 double D[4][4];
-                const bool hi = j >= 16;
 #pragma unroll
                 for (int q = 0; q < 4; q++)
 #pragma unroll
-                    for (int q2 = 0; q2 < 4; q2++) D[q][q2] = hi ? a[q][4 + q2] : a[q][q2];
+                    for (int q2 = 0; q2 < 4; q2++) D[q][q2] = rowb[buf][q][4 * j + q2] + (q == q2 ? 1.0 : 0.0);
                 const int b = inv4_spd(D);
                 if (b && bad_s == 0) bad_s = 4 * j + b;
 #pragma unroll
@@ -436,13 +448,12 @@ __global__ __launch_bounds__(GJ_PIV_THREADS) void gj_pivot_kernel(const double* 
 #pragma unroll
                 for (int cc = 0; cc < 8; cc++) a[rr][cc] = fma(-Tm[rr][q], rv[cc], a[rr][cc]);
         }
-        if (tr == jb && tc == (jb & 15)) {
-            const int jo = (jb >> 4) * 4;
+        if (tr == jb) {
 #pragma unroll
             for (int q = 0; q < 4; q++)
 #pragma unroll
                 for (int cc = 0; cc < 8; cc++)
-                    if (cc == jo + q) a[q][cc] -= 2.0;
+                    if (col(cc) == 4 * jb + q) a[q][cc] -= 2.0;
         }
         if (jb + 1 < 32) publish(jb + 1);
         __syncthreads();
@@ -517,7 +528,7 @@ __global__ __launch_bounds__(GJ_PIV_THREADS) void chol_sweep128_kernel(const dou
     __shared__ __align__(16) double dinv[2][4][4];
     __shared__ int bad_s;
     const int tid = threadIdx.x, tr = tid >> 4, tc = tid & 15;
-    auto col = [&](int cc) { return (cc >> 2) * 64 + 4 * tc + (cc & 3); };
+    auto col = [&](int cc) { return (cc >> 1) * 32 + 2 * tc + (cc & 1); };  // as in gj_pivot_kernel
     const int64_t z = blockIdx.x;
     A += z * sA + k0 * lda + k0;
     scr += z * CHOL_SCR;
@@ -556,13 +567,13 @@ __global__ __launch_bounds__(GJ_PIV_THREADS) void chol_sweep128_kernel(const dou
             for (int q = 0; q < 4; q++)
 #pragma unroll
                 for (int cc = 0; cc < 8; cc++) rowb[buf][q][col(cc)] = a[q][cc] - (col(cc) == 4 * j + q ? 1.0 : 0.0);
-            if (tc == (j & 15)) {
+            wave_lds_order();  // the pivot block is read back from the published rows, as in gj_pivot_kernel
+            if (tc == 0) {
                 double D[4][4], Lc[4][4], Li[4][4];
-                const bool hi = j >= 16;
 #pragma unroll
                 for (int q = 0; q < 4; q++)
 #pragma unroll
-                    for (int q2 = 0; q2 < 4; q2++) D[q][q2] = hi ? a[q][4 + q2] : a[q][q2];
+                    for (int q2 = 0; q2 < 4; q2++) D[q][q2] = rowb[buf][q][4 * j + q2] + (q == q2 ? 1.0 : 0.0);
                 chol4_spd(D, Lc, Li);
                 const int b = inv4_spd(D);
                 if (b && bad_s == 0) bad_s = 4 * j + b;
@@ -595,13 +606,12 @@ __global__ __launch_bounds__(GJ_PIV_THREADS) void chol_sweep128_kernel(const dou
 #pragma unroll
                 for (int cc = 0; cc < 8; cc++) a[rr][cc] = fma(-Tm[rr][q], rv[cc], a[rr][cc]);
         }
-        if (tr == jb && tc == (jb & 15)) {
-            const int jo = (jb >> 4) * 4;
+        if (tr == jb) {
 #pragma unroll
             for (int q = 0; q < 4; q++)
 #pragma unroll
                 for (int cc = 0; cc < 8; cc++)
-                    if (cc == jo + q) a[q][cc] -= 2.0;
+                    if (col(cc) == 4 * jb + q) a[q][cc] -= 2.0;
         }
         if (tr == jb) {
 #pragma unroll

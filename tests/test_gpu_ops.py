@@ -88,8 +88,10 @@ def test_rotate_in(o, i, wdt, with_h):
 
 # ----------------------------------------------------------------------------- H_G square root
 @pytest.mark.parametrize("form,o,blk", [("diag", 1000, 0), ("block", 384, 128), ("full", 256, 0), ("full", 200, 0),
-                                        ("block", 256, 64), ("full", 1024, 0), ("full", 1000, 0)])
+                                        ("block", 256, 64), ("full", 1024, 0), ("full", 1000, 0), ("full", 2048, 0)])
 def test_hg_sqrt(form, o, blk):
+    """Full form: 256, 1024 and 2048 (whole 128-wide blocks) run the sweep with pivots launched ahead
+    that wait on the device; 200 and 1000 (a ragged last block) run the queue-wait pipeline."""
     torch, dev = torch_dev()
     say(f"hg_sqrt {form} o={o} blk={blk}")
     if form == "diag":
