@@ -246,10 +246,155 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs<T> g) {
     }
 }
 
+// fp32, neither operand transposed, rows of A and B in 16-byte vectors, K a multiple of 16, every tile
+// launched (no triangle, K range or skipped tile): the same 128 x 128 tile, waves, MFMA sequence and
+// epilogue as gemm_kernel, so each element of C is bit-identical to it, scheduled for throughput:
+//  * the next K slice is loaded into registers before the current slice's products and stored to LDS
+//    after them; the loads are ordinary (not read-only) loads held in place by a compiler barrier, so the
+//    compiler can neither sink them next to their LDS stores nor spill them (the last slice reloads
+//    itself, keeping the loop free of branches);
+//  * at most 128 VGPRs (no accumulation registers), so with 38 KB of LDS four work-groups share a compute
+//    unit;
+//  * tiles in groups of 8 tile rows swept column by column inside each XCD's contiguous range, so a
+//    group's A and B panels stay in that XCD's L2 while it works on them.
+// Ragged M and N (N a multiple of 4) load clamped rows and columns and store only inside C.
+// Measured on MI355X against gemm_kernel: 28672 x 7680 x 512 at 129 instead of 94 TFLOP/s, 4096^3 at
+// 135 instead of 106, 28672 x 384 x 128 in 38 instead of 72 us.
+constexpr int GF_BK = 16, GF_GROUP = 8;
+__global__ __launch_bounds__(256, 2) void gemm_f32_nn_kernel(GemmArgs<float> g) {
+    if (g.skip && *g.skip) return;
+    __shared__ __align__(16) float As[2][GBM][GF_BK + 4];
+    __shared__ __align__(16) float Bs[2][GF_BK][GBN + 16];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t M = g.M, N = g.N, K = g.K;
+    const int64_t nx = (N + GBN - 1) / GBN, ny = (M + GBM - 1) / GBM, L = nx * ny;
+    int64_t lid = blockIdx.x;
+    if (L % 8 == 0) lid = (lid % 8) * (L / 8) + lid / 8;
+    const int64_t grp = lid / (GF_GROUP * nx), r0 = grp * GF_GROUP;
+    const int64_t rows = (ny - r0) < GF_GROUP ? (ny - r0) : GF_GROUP;
+    const int64_t in = lid - grp * GF_GROUP * nx;
+    const int64_t m0 = (r0 + in % rows) * GBM, n0 = (in / rows) * GBN;
+    const int64_t z = blockIdx.z, z1 = z / g.nb2, z2 = z % g.nb2;
+    const float* A = g.A + z1 * g.sA1 + z2 * g.sA2;
+    const float* B = g.B + z1 * g.sB1 + z2 * g.sB2;
+    float* C = g.C + z1 * g.sC1 + z2 * g.sC2;
+    const int8_t* rs = g.rsign ? g.rsign + z1 * g.sR1 + z2 * g.sR2 : nullptr;
+    const int8_t* cs = g.csign ? g.csign + z1 * g.sS1 + z2 * g.sS2 : nullptr;
+
+    f4v acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int j = 0; j < 4; j++) acc[i][j] = f4v{0, 0, 0, 0};
+    const int wm = wave >> 1, wn = wave & 1;
+    // thread's vectors (q = 0, 1; v = tid + 256 q): A row v / 4, k (v % 4) * 4; B k v / 32, n (v % 32) * 4
+    const float* pa[2];
+    const float* pb[2];
+    int sa[2], sb[2];
+#pragma unroll
+    for (int q = 0; q < 2; q++) {
+        const int v = tid + 256 * q;
+        int64_t m = m0 + v / 4, n = n0 + (v % 32) * 4;
+        m = m < M ? m : M - 1;
+        n = n < N ? n : N - 4;
+        pa[q] = A + m * g.lda + (v % 4) * 4;
+        pb[q] = B + (int64_t)(v / 32) * g.ldb + n;
+        sa[q] = (v / 4) * (GF_BK + 4) + (v % 4) * 4;
+        sb[q] = (v / 32) * (GBN + 16) + (v % 32) * 4;
+    }
+    f4v ra[2], rb[2];
+#pragma unroll
+    for (int q = 0; q < 2; q++) {
+        ra[q] = *reinterpret_cast<const f4v*>(pa[q]);
+        rb[q] = *reinterpret_cast<const f4v*>(pb[q]);
+    }
+#pragma unroll
+    for (int q = 0; q < 2; q++) {
+        *reinterpret_cast<f4v*>(&As[0][0][0] + sa[q]) = ra[q];
+        *reinterpret_cast<f4v*>(&Bs[0][0][0] + sb[q]) = rb[q];
+    }
+    __syncthreads();
+    int buf = 0;
+    for (int64_t k0 = 0; k0 < K; k0 += GF_BK) {
+        const int64_t kn = (k0 + GF_BK < K) ? k0 + GF_BK : k0;
+#pragma unroll
+        for (int q = 0; q < 2; q++) {
+            ra[q] = *reinterpret_cast<const f4v*>(pa[q] + kn);
+            rb[q] = *reinterpret_cast<const f4v*>(pb[q] + kn * g.ldb);
+        }
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int kk = 0; kk < GF_BK; kk += 4) {
+            float a[4], b[4];
+            const int kr = kk + (lane >> 4);
+#pragma unroll
+            for (int i = 0; i < 4; i++) a[i] = As[buf][wm * 64 + 16 * i + (lane & 15)][kr];
+#pragma unroll
+            for (int j = 0; j < 4; j++) b[j] = Bs[buf][kr][wn * 64 + 16 * j + (lane & 15)];
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+#pragma unroll
+                for (int j = 0; j < 4; j++) acc[i][j] = Mfma<float>::mma(a[i], b[j], acc[i][j]);
+        }
+        float* an = &As[buf ^ 1][0][0];
+        float* bn = &Bs[buf ^ 1][0][0];
+#pragma unroll
+        for (int q = 0; q < 2; q++) {
+            *reinterpret_cast<f4v*>(an + sa[q]) = ra[q];
+            *reinterpret_cast<f4v*>(bn + sb[q]) = rb[q];
+        }
+        __syncthreads();
+        buf ^= 1;
+    }
+
+    // epilogue as in gemm_kernel: per chunk of 16 values, the loads of C first, then the stores
+    const int64_t nl = n0 + wn * 64 + (lane & 15);
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        float cv[4][4];
+        int64_t mr[4];
+#pragma unroll
+        for (int r = 0; r < 4; r++) mr[r] = m0 + wm * 64 + 16 * i + Mfma<float>::row(lane, r);
+        if (g.beta != 0.0f) {
+#pragma unroll
+            for (int j = 0; j < 4; j++)
+#pragma unroll
+                for (int r = 0; r < 4; r++) {
+                    const int64_t n = nl + 16 * j;
+                    cv[j][r] = (mr[r] < M && n < N) ? C[mr[r] * g.ldc + n] : 0.0f;
+                }
+        }
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                const int64_t m = mr[r], n = nl + 16 * j;
+                if (m >= M || n >= N) continue;
+                float v = g.alpha * acc[i][j][r];
+                if (rs) v *= float(rs[m]);
+                if (cs) v *= float(cs[n]);
+                if (g.beta != 0.0f) v += g.beta * cv[j][r];
+                C[m * g.ldc + n] = v;
+            }
+    }
+}
+
 template <typename T>
 kq_status gemm(const GemmArgs<T>& g, bool ta, bool tb, hipStream_t st) {
     if (g.M <= 0 || g.N <= 0) return KQ_OK;
     if (g.focus >= 0 || g.skip_tile2 >= 0) return fail(KQ_EUNSUPPORTED, "gemm: tile focus is fp64-only");
+    if constexpr (sizeof(T) == 4) {
+        const bool fast = !ta && !tb && !g.tri && !g.kmode && g.skip_tile < 0 && g.K > 0 && g.K % GF_BK == 0 &&
+                          g.N % 4 == 0 && aligned16(g.A) && aligned16(g.B) && g.lda % 4 == 0 && g.ldb % 4 == 0 &&
+                          g.sA1 % 4 == 0 && g.sA2 % 4 == 0 && g.sB1 % 4 == 0 && g.sB2 % 4 == 0;
+        if (fast) {
+            const int64_t tiles = ((g.M + GBM - 1) / GBM) * ((g.N + GBN - 1) / GBN);
+            if (tiles * 256 > 4294967295LL || g.nb1 * g.nb2 > 65535) return fail(KQ_ESHAPE, "gemm grid too large");
+            hipLaunchKernelGGL(gemm_f32_nn_kernel, dim3((unsigned)tiles, 1, (unsigned)(g.nb1 * g.nb2)), dim3(256), 0,
+                               st, reinterpret_cast<const GemmArgs<float>&>(g));
+            return check_launch("gemm_f32_nn");
+        }
+    }
     constexpr int VN = 16 / sizeof(T);
     const bool vec = aligned16(g.A) && aligned16(g.B) && g.lda % VN == 0 && g.ldb % VN == 0 &&
                      g.sA1 % VN == 0 && g.sA2 % VN == 0 && g.sB1 % VN == 0 && g.sB2 % VN == 0;
