@@ -31,10 +31,10 @@
  *  - Results are deterministic: fixed reduction orders, no order-dependent atomics.
  *  - No C++ exception crosses the ABI. Calls keep no data between them and are safe to call from
  *    several host threads on different streams. Per device, the square root's pipelined sweep uses
- *    two queues and nine events of the library's own, and the damped factor of widths of 6144 or
- *    more four side queues (handed to calls in turn) with two events each, all default priority,
- *    created on the device's first such call and kept until the process ends; they carry no data
- *    from one call to the next, and a mutex per set orders the enqueueing of concurrent calls.
+ *    two queues and nine events of the library's own, and the column sweep of 16384 rows or more
+ *    three side queues (row panels beside the caller's stream) with four events, all default
+ *    priority, created on the device's first such call and kept until the process ends; they carry
+ *    no data from one call to the next, and a mutex per set orders the enqueueing of concurrent calls.
  */
 #ifndef KQ_H
 #define KQ_H
@@ -159,10 +159,10 @@ kq_status kq_rotate_out(float* W, int64_t o, int64_t i, int64_t ldw, const float
  * damping, the damping the smallest workload states).
  *     lambda = damp * mean(diag HX),   H = HX + lambda I,   R upper-triangular, H^{-1} = R^T R
  * computed without forming H^{-1}: with J the reversal permutation, J H J = L L^T (Cholesky) and
- * R = J L^{-1} J. From a width of 6144 the Cholesky factors each 128-wide diagonal block on a side
- * queue of the library (see the conventions above) while the caller's stream applies the rest of
- * the previous step's trailing update. The factorisation and the triangular inverse run in fp64 (MFMA); R is rounded to
- * fp32, so its error is that rounding rather than sqrt(cond(H)) fp32 steps.
+ * R = J L^{-1} J. From a width of 6144 the Cholesky is blocked in two levels (1024-wide panels
+ * factored in 128-wide steps, then one deep update of the rest per panel); everything runs on
+ * `stream`. The factorisation and the triangular inverse run in fp64 (vector FMA products); R is
+ * rounded to fp32, so its error is that rounding rather than sqrt(cond(H)) fp32 steps.
  * HX: i x i fp64 (only its lower triangle is read), leading dimension ldh.
  * R: i x i fp32, leading dimension i, upper triangle written, strict lower triangle zeroed.
  * info (device int32): 0, or k > 0 if H is not positive definite (k = 1 + index, counted from the

@@ -268,7 +268,8 @@ def test_rotate_out(form, o, i, blk):
 # ----------------------------------------------------------------------------- damped factor
 @pytest.mark.parametrize("i", [200, 384, 1000, 128, 6200])
 def test_cholinv(i):
-    """Widths of 6144 and more take the look-ahead factorisation (6200: ragged last block)."""
+    """Widths of 6144 and more take the two-level panel factorisation (6200: a ragged last panel and
+    diagonal block)."""
     torch, dev = torch_dev()
     say(f"cholinv i={i}")
     sp = synth.scaled(synth.CONFIGS["C2"], n=(4 if i < 4096 else 2) * i, i=i, n_outliers=max(1, i // 100))
@@ -317,9 +318,9 @@ def test_cholinv_concurrent_with_hg_sqrt():
         assert torch.equal(R, R0), f"repeat {rep}"
 
 
-def test_cholinv_lookahead_calls_side_by_side():
-    """Two look-ahead factorisations enqueued on two streams at once (each call takes its own side queue)
-    equal the same calls made one after the other, bit for bit."""
+def test_cholinv_panel_calls_side_by_side():
+    """Two panel factorisations enqueued on two streams at once equal the same calls made one after the
+    other, bit for bit."""
     torch, dev = torch_dev()
     i = 6400
     say(f"cholinv i={i} twice, side by side")
