@@ -19,7 +19,8 @@ typedef float f4v __attribute__((ext_vector_type(4)));
 typedef __bf16 bf8v __attribute__((ext_vector_type(8)));
 
 constexpr int SY_T = 128;   // output tile
-constexpr int SY_K = 64;    // tokens per LDS stage
+constexpr int SY_K = 64;    // tokens per LDS sub-tile (and per fp32 chain flushed into fp64)
+constexpr int SY_H = 2;     // sub-tiles per stage: a stage loads SY_H * SY_K tokens
 
 struct alignas(16) U4 {
     uint32_t w[4];
@@ -41,14 +42,19 @@ __device__ inline int lds_off(int m, int c) { return m * SY_K + ((c ^ (m & 7) ^ 
 
 // 512 threads = 8 waves; wave w owns rows 32 (w / 2) .. + 31 and columns 64 (w % 2) .. + 63 of the
 // tile (2 x 4 MFMA tiles). Threads 0..255 stage X through registers into LDS (an 8 x 8 transpose of
-// 16-bit values per thread), double-buffered with one barrier per 64-token stage.
+// 16-bit values per thread), double-buffered with one barrier per 128-token stage: the loads of the
+// next stage are issued before the current stage's products and have both 64-token halves of them to
+// arrive in (with 64-token stages the waves spent about half their time waiting). 128 KB of LDS.
 constexpr int SY_THREADS = 512;
+constexpr size_t SY_SMEM = size_t(2) * 2 * SY_H * SY_T * SY_K * sizeof(uint16_t);
 __global__ __launch_bounds__(SY_THREADS) void syrk_bf16_kernel(const uint16_t* __restrict__ X, int64_t n, int64_t d,
                                                                int64_t ldx, int64_t tok_per_split, double alpha,
                                                                double beta, double* __restrict__ H,
                                                                double* __restrict__ part, int ntiles) {
-    __shared__ __align__(16) uint16_t As[2][SY_T * SY_K];
-    __shared__ __align__(16) uint16_t Bs[2][SY_T * SY_K];
+    extern __shared__ __align__(16) uint16_t sy_lds[];
+    // [buffer][half][SY_T * SY_K], A then B
+    auto As = [&](int buf, int h) { return sy_lds + (size_t)(buf * SY_H + h) * SY_T * SY_K; };
+    auto Bs = [&](int buf, int h) { return sy_lds + (size_t)((2 + buf) * SY_H + h) * SY_T * SY_K; };
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int tile = blockIdx.x, split = blockIdx.y;
     int tm, tn;
@@ -62,41 +68,45 @@ __global__ __launch_bounds__(SY_THREADS) void syrk_bf16_kernel(const uint16_t* _
     const int op = (tid >> 7) & 1, p = tid & 127, kg = p >> 4, mc = p & 15;
     const int64_t cbase = (op ? n0 : m0) + 8 * mc;
     const bool fullc = cbase + 8 <= d;
-    U4 v[8];
+    U4 v[SY_H][8];
 
     auto gload = [&](int64_t k0) {
 #pragma unroll
-        for (int j = 0; j < 8; j++) {
-            const int64_t k = k0 + 8 * kg + j;
+        for (int jj = 0; jj < SY_H * 8; jj++) {
+            const int h = jj >> 3, j = jj & 7;
+            const int64_t k = k0 + SY_K * h + 8 * kg + j;
             const uint16_t* src = X + k * ldx + cbase;
             if (k < ke && fullc) {
-                v[j] = *reinterpret_cast<const U4*>(src);
+                v[h][j] = *reinterpret_cast<const U4*>(src);
             } else {
                 uint16_t tmp[8];
 #pragma unroll
                 for (int e = 0; e < 8; e++) tmp[e] = (k < ke && cbase + e < d) ? src[e] : (uint16_t)0;
 #pragma unroll
-                for (int q = 0; q < 4; q++) v[j].w[q] = (uint32_t)tmp[2 * q] | ((uint32_t)tmp[2 * q + 1] << 16);
+                for (int q = 0; q < 4; q++) v[h][j].w[q] = (uint32_t)tmp[2 * q] | ((uint32_t)tmp[2 * q + 1] << 16);
             }
         }
     };
     auto sstore = [&](int buf) {
-        // 8 x 8 transpose of 16-bit elements: out[mm] holds k = 0..7 of column 8*mc + mm
-        U4 out[8];
 #pragma unroll
-        for (int q = 0; q < 4; q++) {
+        for (int h = 0; h < SY_H; h++) {
+            // 8 x 8 transpose of 16-bit elements: out[mm] holds k = 0..7 of column 8*mc + mm
+            U4 out[8];
 #pragma unroll
-            for (int jp = 0; jp < 4; jp++) {
-                const uint32_t x = v[2 * jp].w[q], y = v[2 * jp + 1].w[q];
-                out[2 * q].w[jp] = (x & 0xFFFFu) | (y << 16);
-                out[2 * q + 1].w[jp] = (x >> 16) | (y & 0xFFFF0000u);
+            for (int q = 0; q < 4; q++) {
+#pragma unroll
+                for (int jp = 0; jp < 4; jp++) {
+                    const uint32_t x = v[h][2 * jp].w[q], y = v[h][2 * jp + 1].w[q];
+                    out[2 * q].w[jp] = (x & 0xFFFFu) | (y << 16);
+                    out[2 * q + 1].w[jp] = (x >> 16) | (y & 0xFFFF0000u);
+                }
             }
-        }
-        uint16_t* dst = op ? Bs[buf] : As[buf];
+            uint16_t* dst = op ? Bs(buf, h) : As(buf, h);
 #pragma unroll
-        for (int mm = 0; mm < 8; mm++) {
-            const int m = 8 * mc + mm;
-            *reinterpret_cast<U4*>(dst + lds_off(m, kg)) = out[mm];
+            for (int mm = 0; mm < 8; mm++) {
+                const int m = 8 * mc + mm;
+                *reinterpret_cast<U4*>(dst + lds_off(m, kg)) = out[mm];
+            }
         }
     };
 
@@ -116,37 +126,43 @@ __global__ __launch_bounds__(SY_THREADS) void syrk_bf16_kernel(const uint16_t* _
         }
         __syncthreads();
         int buf = 0;
-        for (int64_t k0 = kb; k0 < ke; k0 += SY_K) {
-            const bool more = k0 + SY_K < ke;
-            if (more && loader) gload(k0 + SY_K);
-            f4v pacc[2][4];
+        for (int64_t k0 = kb; k0 < ke; k0 += SY_H * SY_K) {
+            const bool more = k0 + SY_H * SY_K < ke;
+            if (more && loader) gload(k0 + SY_H * SY_K);
 #pragma unroll
-            for (int s = 0; s < 2; s++) {
-                bf8v a[2], b[4];
-                const int c = 4 * s + (lane >> 4);
+            for (int h = 0; h < SY_H; h++) {
+                if (h > 0 && k0 + SY_K * h >= ke) break;   // a last half past the split's end
+                const uint16_t* Ah = As(buf, h);
+                const uint16_t* Bh = Bs(buf, h);
+                f4v pacc[2][4];
 #pragma unroll
-                for (int i = 0; i < 2; i++) {
-                    const int m = wm * 32 + 16 * i + (lane & 15);
-                    a[i] = *reinterpret_cast<const bf8v*>(As[buf] + lds_off(m, c));
-                }
+                for (int s = 0; s < 2; s++) {
+                    bf8v a[2], b[4];
+                    const int c = 4 * s + (lane >> 4);
 #pragma unroll
-                for (int j = 0; j < 4; j++) {
-                    const int nn = wn * 64 + 16 * j + (lane & 15);
-                    b[j] = *reinterpret_cast<const bf8v*>(Bs[buf] + lds_off(nn, c));
+                    for (int i = 0; i < 2; i++) {
+                        const int m = wm * 32 + 16 * i + (lane & 15);
+                        a[i] = *reinterpret_cast<const bf8v*>(Ah + lds_off(m, c));
+                    }
+#pragma unroll
+                    for (int j = 0; j < 4; j++) {
+                        const int nn = wn * 64 + 16 * j + (lane & 15);
+                        b[j] = *reinterpret_cast<const bf8v*>(Bh + lds_off(nn, c));
+                    }
+#pragma unroll
+                    for (int i = 0; i < 2; i++)
+#pragma unroll
+                        for (int j = 0; j < 4; j++)
+                            pacc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j],
+                                                                                 s ? pacc[i][j] : f4v{0, 0, 0, 0}, 0, 0, 0);
                 }
 #pragma unroll
                 for (int i = 0; i < 2; i++)
 #pragma unroll
                     for (int j = 0; j < 4; j++)
-                        pacc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], s ? pacc[i][j] : f4v{0, 0, 0, 0},
-                                                                             0, 0, 0);
+#pragma unroll
+                        for (int r = 0; r < 4; r++) acc[i][j][r] += (double)pacc[i][j][r];
             }
-#pragma unroll
-            for (int i = 0; i < 2; i++)
-#pragma unroll
-                for (int j = 0; j < 4; j++)
-#pragma unroll
-                    for (int r = 0; r < 4; r++) acc[i][j][r] += (double)pacc[i][j][r];
             if (more && loader) sstore(buf ^ 1);
             __syncthreads();
             buf ^= 1;
@@ -224,7 +240,7 @@ static void syrk_plan(int64_t n, int64_t d, int& ntiles, int& nsplit, int64_t& t
     const int64_t smax = (n + 1023) / 1024;
     if (s > smax) s = smax;
     if (s < 1) s = 1;
-    tps = ((n + s - 1) / s + SY_K - 1) / SY_K * SY_K;
+    tps = ((n + s - 1) / s + SY_H * SY_K - 1) / (SY_H * SY_K) * (SY_H * SY_K);
     nsplit = (int)((n + tps - 1) / tps);
     if (nsplit < 1) nsplit = 1;
 }
@@ -281,7 +297,13 @@ extern "C" kq_status kq_hessian_accum(const void* X, kq_dtype xdt, int64_t n, in
         if (!ws || ws_bytes < hessian_ws(n, d, xdt)) return fail(KQ_EWORKSPACE, "kq_hessian_accum: workspace too small");
         part = reinterpret_cast<double*>((reinterpret_cast<uintptr_t>(ws) + 255) & ~uintptr_t(255));
     }
-    hipLaunchKernelGGL(syrk_bf16_kernel, dim3((unsigned)ntiles, (unsigned)nsplit), dim3(SY_THREADS), 0, st,
+    static bool attr = false;
+    if (!attr) {
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&syrk_bf16_kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)SY_SMEM);
+        attr = true;
+    }
+    hipLaunchKernelGGL(syrk_bf16_kernel, dim3((unsigned)ntiles, (unsigned)nsplit), dim3(SY_THREADS), SY_SMEM, st,
                        static_cast<const uint16_t*>(X), n, d, ldx, tps, alpha, beta, H, part, ntiles);
     KQ_TRY(check_launch("syrk_bf16"));
     if (nsplit > 1) {
