@@ -26,42 +26,58 @@ sys.path.insert(0, ROOT)
 import synth  # noqa: E402
 
 PEAK = {"hbm": 8.0e12, "fp32_mfma": 157.3e12, "fp64_alu": 78.6e12, "bf16_mfma": 2.5e15}
-DB_TOL = 1e-8   # stopping bound of the Denman-Beavers square root (same constant as the library)
+DB_TOL = 1e-8      # stopping bound of the Denman-Beavers square root (same constant as the library)
+DB_NS_MAX = 8e-5   # bound under which the library's last step is the Newton-Schulz step (same constant)
 
 
-def db_steps(HG: np.ndarray) -> int:
-    """Number of Denman-Beavers steps the library takes for a full H_G: the x-interval starts at
-    [sqrt(1/||A^-1||_F), sqrt(||A||_F)] and its bound b follows b <- (sqrt(b) + 1/sqrt(b)) / 2 after
-    the first step; the loop stops once b - 1 < DB_TOL."""
-    A = HG.astype(np.float64)
-    hi = np.linalg.norm(A)
-    lo = 1.0 / np.linalg.norm(np.linalg.inv(A))
-    r = math.sqrt(hi / lo)
-    b = 0.5 * (math.sqrt(r) + 1.0 / math.sqrt(r))
-    k = 1
-    while b - 1.0 >= DB_TOL and k < 7:
-        b = 0.5 * (math.sqrt(b) + 1.0 / math.sqrt(b))
-        k += 1
-    return k
+def db_plan(blocks) -> tuple:
+    """Steps the library's square root takes for the given full H_G blocks, and whether the last is the
+    Newton-Schulz step: each block's x-interval starts at [sqrt(1/||A^-1||_F), sqrt(||A||_F)], its bound
+    b follows b <- (sqrt(b) + 1/sqrt(b)) / 2 after the first step, and the loop stops once b - 1 < DB_TOL
+    for every block; the last step is replaced when every bound before it is within DB_NS_MAX of 1."""
+    firsts = []
+    for HG in blocks:
+        A = HG.astype(np.float64)
+        r = math.sqrt(np.linalg.norm(A) * np.linalg.norm(np.linalg.inv(A)))
+        firsts.append(0.5 * (math.sqrt(r) + 1.0 / math.sqrt(r)))
+
+    def after(b, k):   # bound after k steps
+        for _ in range(k - 1):
+            b = 0.5 * (math.sqrt(b) + 1.0 / math.sqrt(b))
+        return b
+
+    need = 1
+    for b in firsts:
+        k = 1
+        while after(b, k) - 1.0 >= DB_TOL and k < 7:
+            k += 1
+        need = max(need, k)
+    ns = need >= 2 and all(after(b, need - 1) - 1.0 <= DB_NS_MAX for b in firsts)
+    return need, ns
 
 
-def algorithmic_work(sp, db_iters: int) -> dict:
+def algorithmic_work(sp, plan: tuple) -> dict:
     """Per-phase algorithmic FLOP / bytes of one layer: what the method must compute or move.
 
     hessian: the symmetric product n i (i+1); rotate_in: W read (bf16/fp32) and W' written (fp32),
     H_X read and written twice (fp64, rows then columns); hg_sqrt (full H_G): one SPD inverse of n^3
-    FLOP in the first Denman-Beavers step and two in every later one; rotate_out: 8 B per weight for
+    FLOP in the first Denman-Beavers step and two in every later one, and for a Newton-Schulz last
+    step the fp64 product E = I - Z Y (lower triangle, n^3; its fp32 product Y E / 2, 2 n^3 on the
+    matrix cores, is not counted against the fp64 peak); rotate_out: 8 B per weight for
     the V pass plus the 2 o^2 i FLOP of S W' (full H_G); cholinv: 2 i^3 / 3; quantize: the sweep's
     bytes (W'' read and Q'' written, codes, grid parameters, R) and the trailing-update FLOP."""
     o, i, n, b, g = sp.o, sp.i, sp.n, sp.bits, sp.group
     xb = 2 if sp.x_dtype == "bf16" else 4
     wb = 2 if sp.w_dtype == "bf16" else 4
     full = sp.hg_form == "full"
+    need, ns = plan
+    dbs = need - 1 if ns else need
+    unit = o ** 3 if full else ((o // sp.hg_blk) * sp.hg_blk ** 3 if sp.hg_form == "block" else 0)
     return {
         "hessian": {"flop": n * i * (i + 1), "bytes": n * i * xb + 8 * i * i, "peak": "bf16_mfma"},
         "rotate_in": {"bytes": o * i * (wb + 4) + 32 * i * i, "peak": "hbm"},
-        "hg_sqrt": {"flop": (2 * db_iters - 1) * (o ** 3 if full else (o // sp.hg_blk) * sp.hg_blk ** 3)
-                    if sp.hg_form != "diag" else 0, "peak": "fp64_alu"},
+        "hg_sqrt": {"flop": ((2 * dbs - 1) + (1 if ns else 0)) * unit if sp.hg_form != "diag" else 0,
+                    "peak": "fp64_alu"},
         "rotate_out": ({"flop": 2 * o * o * i, "peak": "fp32_mfma"} if full else {"bytes": 8 * o * i, "peak": "hbm"}),
         "cholinv": {"flop": 2 * i ** 3 // 3, "peak": "fp64_alu"},
         "quantize": {"bytes": int((8 + b / 8 + (8 / g if g else 0)) * o * i + 2 * i * i),
@@ -127,8 +143,8 @@ def run_gpu(sp, steps: int, warmup: int, phases: bool):
             return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
         return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
-    iters = db_steps(d["HG"]) if sp.hg_form == "full" else (
-        max(db_steps(b) for b in d["HG"]) if sp.hg_form == "block" else 0)
+    iters = db_plan([d["HG"]]) if sp.hg_form == "full" else (
+        db_plan(list(d["HG"])) if sp.hg_form == "block" else (0, False))
     X, W, HG = to(d["X"], sp.x_dtype), to(d["W"], sp.w_dtype), to(d["HG"], "f32")
     s, t = to(d["s"], "i8"), to(d["t"], "i8")
     del d
@@ -967,7 +983,8 @@ def main():
                        "arith": "bf16 MFMA (exact products, fp64 accumulation) for H_X; fp64 for H_G^1/2 "
                                 "and the damped factor; fp32 for the rotations of W and the sweep"},
             "phases_ms": {k: round(v, 4) for k, v in ph.items()} if ph else None,
-            "db_steps": iters, "s_cached_mweights_per_s": s_cached,
+            "db_steps": iters[0], "db_last_step": ("newton-schulz" if iters[1] else "denman-beavers")
+            if iters[0] else None, "s_cached_mweights_per_s": s_cached,
             "roofline": roof, "phases_roofline": per_phase, "phases_aggregate": aggregates,
             "sweep_critical_path": chain, "cpu_baseline": cpu, "matvec_quantized": mv}
     print(json.dumps(line), flush=True)

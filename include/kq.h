@@ -124,7 +124,10 @@ kq_status kq_rotate_in(const void* Win, kq_dtype wdt, int64_t ldwin, float* Wout
  * HG, S and Sinv share the storage form: diag (o floats), block (o/blk blocks of blk x blk), or
  * full (o x o). Diagonal: elementwise square root. Block and full: scaled Denman-Beavers
  * iteration in fp64 whose SPD inverses are symmetric block Gauss-Jordan sweeps, stopped on a
- * device-side convergence test (at most 7 steps; enough for cond(H_G) <= 1e16). The sweep runs on
+ * device-side convergence test (at most 7 steps; enough for cond(H_G) <= 1e16). When the iterates
+ * are already within 8e-5 of convergence before the last step, that step is one Newton-Schulz step
+ * instead (E = I - Z Y in fp64, then S = Y + Y E / 2 and S^{-1} = Z + E Z / 2 with fp32 products),
+ * which meets the same tolerance (relative eigenvalue error under 1e-8). The sweep runs on
  * the two queues of the device named above, forked from and joined back into `stream`. The call
  * returns only after the first step has completed on the device: it reads back the number of
  * further steps that step's interval bounds imply (counted on the device) and launches exactly

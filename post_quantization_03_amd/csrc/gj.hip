@@ -986,6 +986,13 @@ static kq_status gj_inverse_batched(double* A, int64_t n, int64_t lda, int64_t s
 // has not converged after those steps is reported through info (= o + 1).
 constexpr int DB_MAXIT = 7;
 constexpr double DB_TOL = 1e-8;
+// Last step. After step k every eigenvalue of Z_k Y_k is x^2 with x in [1, b_k], and the Newton-Schulz
+// step Y <- Y (3I - Z Y) / 2 = Y + Y E / 2, E = I - Z Y (and Z <- Z + E Z / 2) maps x = 1 + e to
+// 1 - 1.5 e^2 - 0.5 e^3: from b - 1 <= DB_NS_MAX it lands within DB_TOL, as a Denman-Beavers step
+// would, for one fp64 product (E, lower triangle) and one fp32 product per output instead of two SPD
+// inverses. E is formed in fp64 from the fp64 iterates (it is the small difference of I and Z Y);
+// the correction Y E / 2, some 1e-4 of Y, needs only fp32: its rounding error is ~1e-11 of Y.
+constexpr double DB_NS_MAX = 8e-5;
 constexpr int NORM_PARTS = 512;  // at most this many partial sums per matrix (one per work-group)
 
 template <typename T>
@@ -1129,7 +1136,9 @@ __global__ void db_converge_kernel(const double* part, const double* bnd, int64_
 // The number of steps the iteration takes (the first included), from the interval bounds after the
 // first step by the recursion of db_scale_kernel (the same fp64 operations; a non-finite bound
 // counts one step), and the other words the host reads after that step: out[0] = steps, out[1] =
-// flags[0] (stopped: converged or failed), out[2] = 1 if a device-side wait of the sweep ran out.
+// flags[0] (stopped: converged or failed), out[2] = 1 if a device-side wait of the sweep ran out,
+// out[3] = 1 if after steps - 1 steps every block's bound is within DB_NS_MAX of 1 (the last step can
+// be the Newton-Schulz step).
 __global__ __launch_bounds__(256) void db_plan_kernel(const double* bnd, int64_t nbk, const int* flags,
                                                       const uint64_t* ready, int* out) {
     __shared__ int sk[256];
@@ -1149,11 +1158,61 @@ __global__ __launch_bounds__(256) void db_plan_kernel(const double* bnd, int64_t
         if ((int)threadIdx.x < w) sk[threadIdx.x] = sk[threadIdx.x] > sk[threadIdx.x + w] ? sk[threadIdx.x] : sk[threadIdx.x + w];
         __syncthreads();
     }
+    __syncthreads();
+    const int total = sk[0];
+    __syncthreads();
+    // the bound of every block after total - 1 steps
+    int ok = 1;
+    for (int64_t b = threadIdx.x; b < nbk; b += 256) {
+        double bb = bnd[b];
+        for (int k = 1; k < total - 1; k++) bb = 0.5 * (sqrt(bb) + 1.0 / sqrt(bb));
+        if (!(bb - 1.0 <= DB_NS_MAX)) ok = 0;
+    }
+    sk[threadIdx.x] = ok;
+    __syncthreads();
+    for (int w = 128; w > 0; w >>= 1) {
+        if ((int)threadIdx.x < w) sk[threadIdx.x] = sk[threadIdx.x] < sk[threadIdx.x + w] ? sk[threadIdx.x] : sk[threadIdx.x + w];
+        __syncthreads();
+    }
     if (threadIdx.x == 0) {
-        out[0] = sk[0];
+        out[0] = total;
         out[1] = flags[0];
         out[2] = ready[1] != 0 ? 1 : 0;
+        out[3] = total >= 2 && sk[0] ? 1 : 0;
     }
+}
+
+// E = I in the lower triangles of nbk n x n matrices (the Newton-Schulz step's C before -= Z Y).
+__global__ void ns_eye_kernel(double* E, int64_t n, int64_t nbk, const int* flags) {
+    if (flags[0]) return;
+    const int64_t nn = n * n;
+    for (int64_t e = blockIdx.x * 256 + threadIdx.x; e < nbk * nn; e += (int64_t)gridDim.x * 256) {
+        const int64_t rc = e % nn;
+        E[e] = (rc / n == rc % n) ? 1.0 : 0.0;
+    }
+}
+
+// fp32 operands and outputs of the Newton-Schulz step: Yf = S = Y, Zf = Si = Z (when Si is given),
+// Ef = E mirrored from its lower triangle. S and Si receive the correction next, in place.
+__global__ void ns_convert_kernel(const double* YZ, const double* E, int64_t n, int64_t nbk, float* Yf, float* Zf,
+                                  float* Ef, float* S, float* Si) {
+    const int64_t nn = n * n;
+    for (int64_t e = blockIdx.x * 256 + threadIdx.x; e < nbk * nn; e += (int64_t)gridDim.x * 256) {
+        const int64_t b = e / nn, rc = e % nn, r = rc / n, c = rc % n;
+        const float y = (float)YZ[e];
+        Yf[e] = y;
+        S[e] = y;
+        Ef[e] = (float)E[b * nn + (r >= c ? r * n + c : c * n + r)];
+        if (Si) {
+            const float z = (float)YZ[nbk * nn + e];
+            Zf[e] = z;
+            Si[e] = z;
+        }
+    }
+}
+
+__global__ void ns_done_kernel(int* flags) {
+    if (threadIdx.x == 0 && !flags[0]) flags[0] = 1;
 }
 
 __global__ void db_final_kernel(const int* flags, int32_t* info, int32_t code) {
@@ -1222,6 +1281,7 @@ static void hg_layout(Ar& a, int64_t n, int64_t nbk) {
     a.template take<int>(4);                                 // flags
     a.template take<uint64_t>(2);                            // sweep hand-over counter and ran-out word
     a.template take<int>(4);                                 // words read back after the first step
+    a.template take<float>((size_t)nbk * nn);                // E in fp32 (Newton-Schulz step)
 }
 
 // Host side of the square root's one readback: pinned memory, which the copy engine writes
@@ -1254,9 +1314,13 @@ size_t hg_sqrt_ws(kq_hg_form form, int64_t o, int64_t blk) {
 // Denman-Beavers square root of nbk SPD n x n matrices (fp32 HGf or fp64 HGd, exactly one given);
 // on return the workspace holds Y = A^{1/2} (items 0 .. nbk-1) and Z = A^{-1/2} (items nbk ..) in
 // fp64 at *Y64 (Z at *Y64 + nbk n^2). info: 0, or o_info + 1 when the iteration did not converge
-// or a matrix is not positive definite.
+// or a matrix is not positive definite. With fp32 outputs S (and Si, may be null) given, the last
+// step may be the Newton-Schulz step, which writes S and Si itself: *written is then true (and the
+// fp64 iterates hold the step before it).
 static kq_status db_sqrt(const float* HGf, const double* HGd, int64_t n, int64_t nbk, int32_t o_info, int32_t* info,
-                         void* ws, size_t ws_bytes, double** Y64, hipStream_t st, bool early = true) {
+                         void* ws, size_t ws_bytes, double** Y64, hipStream_t st, bool early = true,
+                         float* S = nullptr, float* Si = nullptr, bool* written = nullptr) {
+    if (written) *written = false;
     Arena ar(ws, ws_bytes);
     const size_t nn = (size_t)n * n, items = 2 * (size_t)nbk;
     double* YZ = ar.take<double>(items * nn);
@@ -1276,7 +1340,9 @@ static kq_status db_sqrt(const float* HGf, const double* HGd, int64_t n, int64_t
     int* flags = ar.take<int>(4);
     uint64_t* ready = ar.take<uint64_t>(2);
     int* plan = ar.take<int>(4);
+    float* Ef = ar.take<float>((size_t)nbk * nn);
     const int* done = flags;
+    bool ns = false;
     SweepSync sync;
     sync.ready = ready;
     sync.early = early;
@@ -1330,17 +1396,19 @@ static kq_status db_sqrt(const float* HGf, const double* HGd, int64_t n, int64_t
             if (ran_out) {
                 // the device ran the sweep's queues one kernel at a time: redo this call with queue
                 // waits (nothing is kept for later calls)
-                KQ_TRY(db_sqrt(HGf, HGd, n, nbk, o_info, info, ws, ws_bytes, Y64, st, false));
+                KQ_TRY(db_sqrt(HGf, HGd, n, nbk, o_info, info, ws, ws_bytes, Y64, st, false, S, Si, written));
                 set_error("notice: a device-side wait of the square root's sweep ran out; the call was redone "
                           "with queue waits");
                 return KQ_OK;
             }
             if (stopped) break;  // converged after one step, or stopped on an error (info set)
             nsteps = need;
+            if (S && hp[3]) {
+                ns = true;
+                nsteps = need - 1;
+            }
         }
     }
-    hipLaunchKernelGGL(db_final_kernel, dim3(1), dim3(64), 0, st, flags, info, o_info + 1);
-    KQ_TRY(check_launch("db_final"));
     {
         const unsigned tiles = (unsigned)((n + 31) / 32);
         if (items > 65535) return fail(KQ_ESHAPE, "square root: too many blocks");
@@ -1348,7 +1416,36 @@ static kq_status db_sqrt(const float* HGf, const double* HGd, int64_t n, int64_t
         KQ_TRY(check_launch("db_mirror"));
     }
     *Y64 = YZ;
-    return KQ_OK;
+    if (ns) {
+        // the Newton-Schulz step (skipped on the device when the iteration stopped on an error: S and
+        // Si are then the last iterates, and info is set). E (fp64) in NI's first half, Y and Z in
+        // fp32 in its second half.
+        double* E = NI;
+        float* Yf = reinterpret_cast<float*>(NI + nbk * nn);
+        float* Zf = Yf + nbk * nn;
+        double* Y = YZ;
+        double* Z = YZ + nbk * nn;
+        hipLaunchKernelGGL(ns_eye_kernel, dim3(eb), dim3(256), 0, st, E, n, nbk, flags);
+        KQ_TRY(check_launch("ns_eye"));
+        GemmArgs<double> ge = gemm_args<double>(n, n, n, Z, n, Y, n, E, n, -1.0, 1.0);  // E = I - Z Y (Y = Y^T)
+        ge.tri = 1; ge.nb1 = nbk; ge.sA1 = (int64_t)nn; ge.sB1 = (int64_t)nn; ge.sC1 = (int64_t)nn; ge.skip = flags;
+        KQ_TRY(gemm<double>(ge, false, true, st));
+        hipLaunchKernelGGL(ns_convert_kernel, dim3(eb), dim3(256), 0, st, YZ, E, n, nbk, Yf, Zf, Ef, S, Si);
+        KQ_TRY(check_launch("ns_convert"));
+        GemmArgs<float> gy = gemm_args<float>(n, n, n, Yf, n, Ef, n, S, n, 0.5f, 1.0f);  // S = Y + Y E / 2
+        gy.nb1 = nbk; gy.sA1 = (int64_t)nn; gy.sB1 = (int64_t)nn; gy.sC1 = (int64_t)nn; gy.skip = flags;
+        KQ_TRY(gemm<float>(gy, false, false, st));
+        if (Si) {
+            GemmArgs<float> gz = gemm_args<float>(n, n, n, Ef, n, Zf, n, Si, n, 0.5f, 1.0f);  // Si = Z + E Z / 2
+            gz.nb1 = nbk; gz.sA1 = (int64_t)nn; gz.sB1 = (int64_t)nn; gz.sC1 = (int64_t)nn; gz.skip = flags;
+            KQ_TRY(gemm<float>(gz, false, false, st));
+        }
+        hipLaunchKernelGGL(ns_done_kernel, dim3(1), dim3(64), 0, st, flags);
+        KQ_TRY(check_launch("ns_done"));
+        if (written) *written = true;
+    }
+    hipLaunchKernelGGL(db_final_kernel, dim3(1), dim3(64), 0, st, flags, info, o_info + 1);
+    return check_launch("db_final");
 }
 
 // The square root reads its first step back to the host, so a stream under graph capture is refused
@@ -1387,7 +1484,9 @@ extern "C" kq_status kq_hg_sqrt(const float* HG, kq_hg_form form, int64_t o, int
     KQ_TRY(refuse_capture(st, "kq_hg_sqrt"));
     set_error("");
     double* YZ = nullptr;
-    KQ_TRY(db_sqrt(HG, nullptr, n, nbk, (int32_t)o, info, ws, ws_bytes, &YZ, st));
+    bool written = false;
+    KQ_TRY(db_sqrt(HG, nullptr, n, nbk, (int32_t)o, info, ws, ws_bytes, &YZ, st, true, S, Sinv, &written));
+    if (written) return KQ_OK;
     const size_t nn = (size_t)n * n;
     const unsigned eb = (unsigned)((nbk * nn + 255) / 256 < 4096 ? (nbk * nn + 255) / 256 : 4096);
     hipLaunchKernelGGL(db_out_kernel, dim3(eb), dim3(256), 0, st, YZ, n, nbk, S, Sinv);
