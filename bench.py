@@ -81,7 +81,7 @@ def algorithmic_work(sp, plan: tuple) -> dict:
         "rotate_out": ({"flop": 2 * o * o * i, "peak": "fp32_mfma"} if full else {"bytes": 8 * o * i, "peak": "hbm"}),
         "cholinv": {"flop": 2 * i ** 3 // 3, "peak": "fp64_alu"},
         "quantize": {"bytes": int((8 + b / 8 + (8 / g if g else 0)) * o * i + 2 * i * i),
-                     "flop": o * i * (i - 128), "peak": "hbm"},
+                     "flop": o * i * (i - 128), "peak": "hbm", "flop_peak": "fp32_mfma"},
     }
 
 
@@ -116,7 +116,12 @@ def measured_traffic(phase: str):
 
 
 def roofline_of(name: str, wk: dict, ms: float) -> dict:
+    """The phase's roofline: its algorithmic work over its time against the peak of the resource that
+    bounds it. A phase with both bytes and FLOP (the sweep: HBM streaming and the trailing-update
+    products) is bound by whichever needs the longer time at its peak."""
     pk = wk["peak"]
+    if pk == "hbm" and wk.get("flop_peak") and wk["flop"] / PEAK[wk["flop_peak"]] > wk["bytes"] / PEAK["hbm"]:
+        pk = wk["flop_peak"]
     if pk == "hbm":
         ach = wk["bytes"] / (ms / 1e3)
         return {"bound": "hbm", "kernel": name, "achieved": round(ach / 1e9, 2), "peak": PEAK["hbm"] / 1e9,
@@ -736,12 +741,13 @@ def _stack_layer_host(li: int):
 def stack_work() -> dict:
     """Algorithmic work of one pass over the stack, summed over its 224 sublayers and 128 inputs, with the
     per-layer formulas of algorithmic_work (H_X, its rotation and R once per distinct input)."""
-    tot = {"hessian": 0, "rotate_in": 0, "rotate_out": 0, "cholinv": 0, "quantize": 0}
+    tot = {"hessian": 0, "rotate_in": 0, "rotate_out": 0, "cholinv": 0, "quantize": 0, "quantize_flop": 0}
     n = synth.C5_TOKENS
     for (_, o, i, x) in synth.C5_SUBLAYERS:
         tot["rotate_in"] += o * i * (2 + 4)
         tot["rotate_out"] += 8 * o * i
         tot["quantize"] += int((8 + 3 / 8 + 8 / 128) * o * i)   # at the 3.0-bit average
+        tot["quantize_flop"] += o * i * (i - 128)
     for (_, i, _) in synth.C5_INPUTS:
         tot["hessian"] += n * i * (i + 1)
         tot["rotate_in"] += 32 * i * i
@@ -752,7 +758,8 @@ def stack_work() -> dict:
             "rotate_in": {"bytes": L * tot["rotate_in"], "peak": "hbm"},
             "rotate_out": {"bytes": L * tot["rotate_out"], "peak": "hbm"},
             "cholinv": {"flop": L * tot["cholinv"], "peak": "fp64_alu"},
-            "quantize": {"bytes": L * tot["quantize"], "peak": "hbm"}}
+            "quantize": {"bytes": L * tot["quantize"], "flop": L * tot["quantize_flop"], "peak": "hbm",
+                         "flop_peak": "fp32_mfma"}}
 
 
 def run_stack(steps: int, warmup: int):
@@ -968,7 +975,7 @@ def main():
         aggregates = {
             "dense_phases": dense,
             "dense_frac": round(sum(work[k]["flop"] for k in dense) /
-                                sum(ph[k] / 1e3 * PEAK[work[k]["peak"]] for k in dense), 4) if dense else None,
+                                sum(ph[k] / 1e3 * per_phase[k]["peak"] * 1e12 for k in dense), 4) if dense else None,
             "hbm_phases": hbm,
             "hbm_frac": round(sum(work[k]["bytes"] for k in hbm) / (sum(ph[k] for k in hbm) / 1e3 * PEAK["hbm"]), 4)
             if hbm else None,
@@ -1110,7 +1117,7 @@ def run_stack_line(args) -> None:
     aggregates = {
         "dense_phases": dense,
         "dense_frac": round(sum(work[k]["flop"] for k in dense) /
-                            sum(ph_work[k] / 1e3 * PEAK[work[k]["peak"]] for k in dense), 4),
+                            sum(ph_work[k] / 1e3 * per_phase[k]["peak"] * 1e12 for k in dense), 4),
         "hbm_phases": hbm,
         "hbm_frac": round(sum(work[k]["bytes"] for k in hbm) / (sum(ph_work[k] for k in hbm) / 1e3 * PEAK["hbm"]), 4),
     }
