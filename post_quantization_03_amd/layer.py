@@ -11,6 +11,11 @@ Order of the calls (KronQ review page, Method and Key idea):
   kq_rotate_out     W'' = V S W'
   kq_quantize_layer GPTQ sweep on W'' -> codes, scale, offset, w^ (rotated), row loss
 Torch only allocates device memory and supplies the streams.
+
+The returned info (device int32 [2]) must be read by the caller once the stream is synchronised:
+info[0] from kq_hg_sqrt, info[1] from kq_cholinv, 0 on success. info[0] = -1 means a device-side
+wait of the square root's sweep ran out after its first step (the device stopped running the sweep's
+two queues side by side): S, and so every output, is invalid and the layer should be run again.
 """
 from __future__ import annotations
 
