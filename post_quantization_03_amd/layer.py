@@ -19,6 +19,7 @@ two queues side by side): S, and so every output, is invalid and the layer shoul
 """
 from __future__ import annotations
 
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass
 
 import torch
@@ -39,6 +40,16 @@ class LayerCfg:
 
 
 _SIDE: dict = {}
+_WORKER: dict = {}
+
+
+def _sqrt_worker(dev) -> ThreadPoolExecutor:
+    """One host thread per device, kept for the process, that enqueues the square root (its one readback
+    uses a pinned buffer of the calling thread, allocated once)."""
+    key = dev.index if dev.index is not None else torch.cuda.current_device()
+    if key not in _WORKER:
+        _WORKER[key] = ThreadPoolExecutor(max_workers=1, thread_name_prefix=f"kq_hg_sqrt{key}")
+    return _WORKER[key]
 
 
 def _side_stream(dev):
@@ -84,10 +95,22 @@ def quantize_layer(X: torch.Tensor, W: torch.Tensor, HG: torch.Tensor, s: torch.
         Sinv = torch.empty_like(S) if verify else None
         if cfg.form != "diag":
             # S depends on H_G alone: it runs on the second stream, forked here (after the inputs and
-            # outputs above exist) and joined before kq_rotate_out. It is enqueued after the H_X
-            # chain, since kq_hg_sqrt returns only once its first step has run on the device.
+            # outputs above exist) and joined before kq_rotate_out. kq_hg_sqrt returns only once its
+            # first step has run on the device, and enqueueing the H_X chain can block the host too
+            # (the damped factor's ~150 launches fill the stream's hardware queue, so the host waits
+            # for the device to work through them), so the square root is enqueued from a host thread
+            # of its own, started here: both chains reach the device at once.
             join = _side_stream(dev)
             join.wait_stream(torch.cuda.current_stream(dev))
+            with torch.cuda.stream(join):
+                ws_s = torch.empty(max(K.kq_workspace_bytes("hg_sqrt", o, 0, form=cfg.form, blk=cfg.blk), 256),
+                                   dtype=torch.uint8, device=dev)
+
+            def _sqrt():
+                torch.cuda.set_device(dev)
+                K.kq_hg_sqrt(HG, cfg.form, o, cfg.blk, S, Sinv, info[0:1], ws_s, stream=join)
+
+            sqrt_done = _sqrt_worker(dev).submit(_sqrt)
     else:
         S, Sinv = S_cached
     H = torch.empty((i, i), dtype=torch.float64, device=dev)
@@ -117,11 +140,8 @@ def quantize_layer(X: torch.Tensor, W: torch.Tensor, HG: torch.Tensor, s: torch.
     if cfg.order != "trace":
         K.kq_cholinv(H, cfg.damp, R, info[1:2], ws)
     if join is not None:
-        with torch.cuda.stream(join):
-            ws_s = torch.empty(max(K.kq_workspace_bytes("hg_sqrt", o, 0, form=cfg.form, blk=cfg.blk), 256),
-                               dtype=torch.uint8, device=dev)
-            K.kq_hg_sqrt(HG, cfg.form, o, cfg.blk, S, Sinv, info[0:1], ws_s)
-        for t_ in (S, Sinv, info, HG):
+        sqrt_done.result()   # the square root is enqueued (its errors are raised here)
+        for t_ in (S, Sinv, info, HG, ws_s):
             if t_ is not None:
                 t_.record_stream(join)
         torch.cuda.current_stream(dev).wait_stream(join)
