@@ -460,6 +460,21 @@ __global__ __launch_bounds__(256) void dgemm_valu_kernel(GemmArgs<double> g) {
             else lid -= f0 + q + 1;
         }
         if (tm < 0) { tm = f0 + rf + lid / rf; tn = f0 + lid % rf; }
+    } else if (BM == BN && g.kmode && !g.tri && (!(g.kmode & 10) || !(g.kmode & 5))) {
+        // K ranges that depend on the tile (triangular operands) along one of the tile indices: tiles go
+        // out longest K first, in the launch order itself (consecutive ids reach the 8 XCDs in turn, so
+        // each XCD receives every 8th tile of that order and its share differs from the others' by at
+        // most one tile). A K range set by the tile column runs down the columns (all rows of a column
+        // share one B panel and one K range); one set by the tile row runs along the rows.
+        const int64_t nx = (g.N + BN - 1) / BN, ny = (g.M + BM - 1) / BM;
+        const int64_t lid = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
+        if (g.kmode & 10) {
+            tm = lid % ny;
+            tn = (g.kmode & 8) ? nx - 1 - lid / ny : lid / ny;
+        } else {
+            tn = lid % nx;
+            tm = (g.kmode & 4) ? ny - 1 - lid / nx : lid / nx;
+        }
     } else {
         const int64_t nx = (g.N + BN - 1) / BN;
         const int64_t L = g.tri ? (int64_t)gridDim.x : (int64_t)gridDim.x * gridDim.y;
@@ -474,22 +489,6 @@ __global__ __launch_bounds__(256) void dgemm_valu_kernel(GemmArgs<double> g) {
         if constexpr (BM != BN) {
             tm = lid / nx;  // row-block tiles (own_rows): never triangular
             tn = lid % nx;
-        } else if (g.kmode && !g.tri) {
-            // K ranges that depend on the tile (triangular operands): the runs above take the rows in
-            // the order of their residue mod 8 (rows 0, 8, 16, .., then 1, 9, ..), so each XCD gets
-            // whole rows (A panels shared in its L2) spread over the matrix (long and short K ranges
-            // alike); within a residue class and a row, the longest K ranges come first (K grows with
-            // the tile row when it ends at the row, bit 2, and with the column when it ends there, bit 3)
-            const int64_t ny = (g.M + BM - 1) / BM;
-            const int64_t rho = lid / nx, b8 = ny / 8, r8 = ny % 8;
-            int64_t c = 0;
-            while (c + 1 < 8 && (c + 1) * b8 + (c + 1 < r8 ? c + 1 : r8) <= rho) c++;
-            const int64_t start = c * b8 + (c < r8 ? c : r8), len = b8 + (c < r8 ? 1 : 0);
-            int64_t w = rho - start;
-            if (g.kmode & 4) w = len - 1 - w;
-            tm = c + 8 * w;
-            tn = lid % nx;
-            if (g.kmode & 8) tn = nx - 1 - tn;
         } else if (g.tri) {
             int64_t r = (int64_t)((sqrt(8.0 * (double)lid + 1.0) - 1.0) * 0.5);
             while (r * (r + 1) / 2 > lid) r--;
@@ -627,13 +626,19 @@ __global__ __launch_bounds__(256) void dgemm_valu_kernel(GemmArgs<double> g) {
     };
 
     if (kb < ke) {
-        gload(kb);
+        // A K range that starts at the tile (and ends where its neighbours' do) is walked from its end
+        // down: tiles that share an operand panel then read each slice of it at about the same time
+        const int64_t nsl = (ke - kb + BK - 1) / BK;
+        const bool krev = (g.kmode & 3) && !(g.kmode & 12);
+        const int64_t dk = krev ? -BK : BK;
+        int64_t k0 = krev ? kb + (nsl - 1) * BK : kb;
+        gload(k0);
         sstore(0);
         __syncthreads();
         int buf = 0;
-        for (int64_t k0 = kb; k0 < ke; k0 += BK) {
-            const bool more = k0 + BK < ke;
-            if (more) gload(k0 + BK);
+        for (int64_t sl = 0; sl < nsl; sl++, k0 += dk) {
+            const bool more = sl + 1 < nsl;
+            if (more) gload(k0 + dk);
 #pragma unroll 2
             for (int kk = 0; kk < BK; kk++) {
                 double a[2][RG], b[2][CG];
