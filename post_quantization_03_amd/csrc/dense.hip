@@ -1133,31 +1133,42 @@ __global__ void reverse_upper_kernel(const double* X, int64_t n, float* R) {
 }
 
 // Lower Cholesky of one n x n fp64 matrix A (lda = n, lower triangle) with the inverses of its 128-wide
-// diagonal blocks in X, blocked in two levels: the columns of a PANEL_W-wide panel are factored by the
-// 128-wide steps of potrf_batched, whose rank-128 updates reach only the panel's own columns (all rows
-// below), and the matrix right of the panel then receives the whole panel in one update with
-// K = PANEL_W. Most of the n^3/3 FLOP thus run in deep-K products instead of rank-128 ones.
-// Measured on MI355X: layer steps with widths 13824 and 8192 take 2.2 and 1.5 ms less than with one
-// step of look-ahead (the diagonal block factored on a side queue beside the trailing update: its
-// kernel needs a whole compute unit and waited for one while the update filled the chip); at width
-// 4096 the factor takes 5.73 instead of 5.64 ms, so below PANELS_FROM the 128-wide steps run alone.
+// diagonal blocks in X, blocked in two levels: the columns of a W-wide panel are factored by 128-wide
+// steps whose rank-128 updates reach only the panel's own columns (all rows below), and the matrix right
+// of the panel then receives the whole panel in one update with K = W. Most of the n^3/3 FLOP thus run
+// in deep-K products instead of rank-128 ones (W = n: one panel, every update rank-128).
+// For even n each step's update inside the panel is one launch with the sweep of the next diagonal
+// block (chol_step_fused): the sweep, which needs one compute unit for ~75 us, runs beside the update
+// instead of after it. Only the first block of a panel is swept alone, after the panel's big update.
+// Measured on MI355X (before the fused steps): layer steps with widths 13824 and 8192 took 2.2 and 1.5
+// ms less with panels than with one step of look-ahead (the diagonal block factored on a side queue
+// beside the trailing update: its kernel needs a whole compute unit and waited for one while the update
+// filled the chip).
 constexpr int64_t PANEL_W = 1024, PANELS_FROM = 6144;
-static kq_status potrf_panels(double* A, int64_t n, double* X, int32_t* info, double* scr, hipStream_t st) {
+static kq_status potrf_panels(double* A, int64_t n, int64_t W, double* X, int32_t* info, double* scr, hipStream_t st) {
     constexpr int64_t NB = 128;
-    for (int64_t J0 = 0; J0 < n; J0 += PANEL_W) {
-        const int64_t J1 = J0 + PANEL_W < n ? J0 + PANEL_W : n;
+    const bool fuse = (n & 1) == 0 && (reinterpret_cast<uintptr_t>(A) & 15) == 0;
+    bool swept = false;  // the diagonal block at k0 was swept by the fused step before it
+    for (int64_t J0 = 0; J0 < n; J0 += W) {
+        const int64_t J1 = J0 + W < n ? J0 + W : n;
         for (int64_t k0 = J0; k0 < J1; k0 += NB) {
             const int64_t k1 = k0 + NB < J1 ? k0 + NB : J1;
-            KQ_TRY(chol_inv_diag128(A, n, 0, X, n, 0, n, k0, 1, scr, info, 0, nullptr, st));
+            if (swept) KQ_TRY(chol_extract_diag128(A, n, X, n, n, k0, scr, st));
+            else KQ_TRY(chol_inv_diag128(A, n, 0, X, n, 0, n, k0, 1, scr, info, 0, nullptr, st));
+            swept = false;
             if (k1 >= n) break;
             // A[k1:, k0:k1] <- A[k1:, k0:k1] X_kk^T in place (each work-group owns whole rows)
             GemmArgs<double> p = gemm_args<double>(n - k1, k1 - k0, k1 - k0, A + k1 * n + k0, n, X + k0 * n + k0, n,
                                                    A + k1 * n + k0, n, 1.0, 0.0);
             p.own_rows = 1;
             KQ_TRY(gemm<double>(p, false, true, st));
-            // the rest of the panel: A[k1:, k1:J1] -= L[k1:, k0:k1] L[k1:J1, k0:k1]^T (the part of its
-            // diagonal block above the diagonal is written too; only lower triangles are ever read)
-            if (k1 < J1) {
+            // the rest of the panel: A[k1:, k1:J1] -= L[k1:, k0:k1] L[k1:J1, k0:k1]^T
+            if (k1 < J1 && fuse) {
+                KQ_TRY(chol_step_fused(A, n, n, k0, J1, scr, info, st));
+                swept = true;
+            } else if (k1 < J1) {
+                // (the part of its diagonal block above the diagonal is written too; only lower
+                // triangles are ever read)
                 GemmArgs<double> u = gemm_args<double>(n - k1, J1 - k1, k1 - k0, A + k1 * n + k0, n, A + k1 * n + k0, n,
                                                        A + k1 * n + k1, n, -1.0, 1.0);
                 KQ_TRY(gemm<double>(u, false, true, st));
@@ -1208,7 +1219,8 @@ extern "C" kq_status kq_cholinv(const double* HX, int64_t n, int64_t ldh, double
     hipLaunchKernelGGL(reverse_damped_kernel, g2, dim3(256), 0, st, HX, n, ldh, lam, Hr);
     KQ_TRY(check_launch("reverse"));
     KQ_TRY(fill<double>(X, (size_t)n * n, 0.0, st));
-    if (n >= PANELS_FROM) KQ_TRY(potrf_panels(Hr, n, X, info, Cscr, st));
+    if (n >= PANELS_FROM) KQ_TRY(potrf_panels(Hr, n, PANEL_W, X, info, Cscr, st));
+    else if (n % 2 == 0) KQ_TRY(potrf_panels(Hr, n, n, X, info, Cscr, st));
     else KQ_TRY(potrf_batched<double>(Hr, n, 0, X, n, 0, n, 1, info, 0, nullptr, nullptr, st, Cscr));
     KQ_TRY(trtri_batched<double>(Hr, n, 0, X, n, 0, n, 1, Tscr, nullptr, st));
     hipLaunchKernelGGL(reverse_upper_kernel, g2, dim3(256), 0, st, X, n, R);

@@ -519,46 +519,42 @@ __device__ inline void chol4_spd(const double D[4][4], double L[4][4], double Li
 constexpr int64_t CHOL_SCR = 2 * 32 * 4 * GJ_NB + 32 * 16 + GJ_NB;
 constexpr int CHOL_EXTRACT_SPLIT = 8;  // work-groups per item of the extraction
 
-__global__ __launch_bounds__(GJ_PIV_THREADS) void chol_sweep128_kernel(const double* __restrict__ A, int64_t lda,
-                                                                       int64_t sA, int64_t n, int64_t k0,
-                                                                       double* __restrict__ scr, int32_t* info,
-                                                                       int64_t info_stride, const int* skip) {
-    if (skip && *skip) return;
+// The sweep of chol_sweep128_kernel on a block whose entries (unscaled; thread (tr, tc) holds rows
+// 4tr..4tr+3 and columns col(cc) as in gj_pivot_kernel) are already in registers; dg(r) returns the
+// unscaled diagonal entry r < nbk. Writes the scratch of the item and, for a non-positive pivot,
+// info[info_slot] (if still 0).
+template <typename Diag>
+__device__ __forceinline__ void chol_sweep128_body(double (&a)[4][8], Diag dg, int nbk, double* __restrict__ scr,
+                                                   int32_t* info, int64_t info_slot, int64_t k0) {
     __shared__ __align__(16) double rowb[2][4][GJ_NB];
     __shared__ __align__(16) double dinv[2][4][4];
     __shared__ int bad_s;
     const int tid = threadIdx.x, tr = tid >> 4, tc = tid & 15;
     auto col = [&](int cc) { return (cc >> 1) * 32 + 2 * tc + (cc & 1); };  // as in gj_pivot_kernel
-    const int64_t z = blockIdx.x;
-    A += z * sA + k0 * lda + k0;
-    scr += z * CHOL_SCR;
     double* pre = scr;                       // [32][4][128]
     double* post = scr + 32 * 4 * GJ_NB;     // [32][4][128]
     double* lj = scr + 2 * 32 * 4 * GJ_NB;   // [32][4][4]
     double* sqs = lj + 32 * 16;              // [128] sqrt of the block's diagonal (the scaling)
-    const int nbk = (int)((n - k0) < GJ_NB ? (n - k0) : GJ_NB);
-    auto Aget = [&](int r, int c) { return c <= r ? A[(int64_t)r * lda + c] : A[(int64_t)c * lda + r]; };
     double sr[4], sc[8];
 #pragma unroll
     for (int rr = 0; rr < 4; rr++) {
         const int r = 4 * tr + rr;
-        const double p = r < nbk ? A[(int64_t)r * lda + r] : 1.0;
+        const double p = r < nbk ? dg(r) : 1.0;
         sr[rr] = p > 0.0 ? 1.0 / sqrt(p) : 1.0;
         if (tc == 0) sqs[r] = p > 0.0 ? sqrt(p) : 1.0;
     }
 #pragma unroll
     for (int cc = 0; cc < 8; cc++) {
         const int c = col(cc);
-        const double p = c < nbk ? A[(int64_t)c * lda + c] : 1.0;
+        const double p = c < nbk ? dg(c) : 1.0;
         sc[cc] = p > 0.0 ? 1.0 / sqrt(p) : 1.0;
     }
-    double a[4][8];
 #pragma unroll
     for (int rr = 0; rr < 4; rr++)
 #pragma unroll
         for (int cc = 0; cc < 8; cc++) {
             const int r = 4 * tr + rr, c = col(cc);
-            a[rr][cc] = (r < nbk && c < nbk) ? Aget(r, c) * sr[rr] * sc[cc] : (r == c ? 1.0 : 0.0);
+            a[rr][cc] = (r < nbk && c < nbk) ? a[rr][cc] * sr[rr] * sc[cc] : (r == c ? 1.0 : 0.0);
         }
     auto publish = [&](int j) {
         if (tr == j) {
@@ -622,8 +618,30 @@ __global__ __launch_bounds__(GJ_PIV_THREADS) void chol_sweep128_kernel(const dou
         if (jb + 1 < 32) publish(jb + 1);
         lds_barrier();
     }
-    if (tid == 0 && bad_s && bad_s <= nbk && info && info[z * info_stride] == 0)
-        info[z * info_stride] = (int32_t)(k0 + bad_s);
+    if (tid == 0 && bad_s && bad_s <= nbk && info && info[info_slot] == 0) info[info_slot] = (int32_t)(k0 + bad_s);
+}
+
+__global__ __launch_bounds__(GJ_PIV_THREADS) void chol_sweep128_kernel(const double* __restrict__ A, int64_t lda,
+                                                                       int64_t sA, int64_t n, int64_t k0,
+                                                                       double* __restrict__ scr, int32_t* info,
+                                                                       int64_t info_stride, const int* skip) {
+    if (skip && *skip) return;
+    const int tid = threadIdx.x, tr = tid >> 4, tc = tid & 15;
+    auto col = [&](int cc) { return (cc >> 1) * 32 + 2 * tc + (cc & 1); };
+    const int64_t z = blockIdx.x;
+    A += z * sA + k0 * lda + k0;
+    const int nbk = (int)((n - k0) < GJ_NB ? (n - k0) : GJ_NB);
+    auto Aget = [&](int r, int c) { return c <= r ? A[(int64_t)r * lda + c] : A[(int64_t)c * lda + r]; };
+    double a[4][8];
+#pragma unroll
+    for (int rr = 0; rr < 4; rr++)
+#pragma unroll
+        for (int cc = 0; cc < 8; cc++) {
+            const int r = 4 * tr + rr, c = col(cc);
+            a[rr][cc] = (r < nbk && c < nbk) ? Aget(r, c) : 0.0;
+        }
+    chol_sweep128_body(a, [&](int r) { return A[(int64_t)r * lda + r]; }, nbk, scr + z * CHOL_SCR, info,
+                       z * info_stride, k0);
 }
 
 __global__ __launch_bounds__(512) void chol_extract128_kernel(double* __restrict__ A, int64_t lda, int64_t sA,
@@ -708,6 +726,227 @@ __global__ __launch_bounds__(512) void chol_extract128_kernel(double* __restrict
     }
 }
 
+// ------------------------------------------------------------------------- fused Cholesky step
+// One launch per step of the blocked lower Cholesky of a single matrix (row-major, lda even) that runs
+// the factorization of the next 128-wide diagonal block beside the update of the columns below it, so
+// that the one-work-group sweep no longer waits for the whole update:
+//   work-group 0: D = A[k1:k1+nb, k1:k1+nb] - L_k L_k^T, with L_k = A[k1:k1+nb, k0:k1] the rows of the
+//     columns just factored, formed in the sweep's register layout (L_k^T staged in LDS), then the sweep
+//     of chol_sweep128_kernel on D, whose scratch chol_extract128_kernel turns into L and L^{-1};
+//   every other work-group: two 256-thread halves, each one 128 x 128 tile (tm, tn), tn <= tm, of
+//     A[k1:n, k1:J1] -= L L^T (L = A[k1:n, k0:k1]) other than the diagonal block, with 8 x 8 register
+//     tiles and 16-deep slices double-buffered in LDS.
+// Tiles above the diagonal are left out (only lower triangles are read), and the diagonal block keeps
+// its old entries in A (the extraction overwrites its lower triangle with the factor).
+constexpr int CS_BK = 16, CS_LD = GJ_NB + 2;
+constexpr size_t CS_SMEM = size_t(2) * 2 * 2 * CS_BK * CS_LD * sizeof(double);  // 2 halves x (A, B) x 2 buffers
+static_assert(CS_SMEM >= size_t(GJ_NB) * CS_LD * sizeof(double), "the staged L_k^T fits the tile buffers");
+typedef double cs_d2 __attribute__((ext_vector_type(2)));
+
+__global__ __launch_bounds__(512) void chol_step_kernel(double* A, int64_t lda, int64_t n, int64_t k0, int64_t J1,
+                                                        int64_t ntiles, int64_t Nt, double* __restrict__ scr,
+                                                        int32_t* info) {
+    extern __shared__ __align__(16) unsigned char cs_raw[];
+    double* lds = reinterpret_cast<double*>(cs_raw);
+    const int tid = threadIdx.x;
+    const int64_t k1 = k0 + GJ_NB, M = n - k1, N = J1 - k1;
+    const double* L = A + k1 * lda + k0;
+    double* C = A + k1 * lda + k1;
+    if (blockIdx.x == 0) {
+        __shared__ double dg[GJ_NB];
+        const int tr = tid >> 4, tc = tid & 15;
+        auto col = [&](int cc) { return (cc >> 1) * 32 + 2 * tc + (cc & 1); };
+        const int nb = (int)(M < GJ_NB ? M : GJ_NB);
+        for (int v = tid; v < GJ_NB * GJ_NB / 2; v += 512) {  // lds[k][r] = L_k[r][k]
+            const int r = v >> 6, kp = (v & 63) * 2;
+            cs_d2 t = {0.0, 0.0};
+            if (r < nb) t = *reinterpret_cast<const cs_d2*>(L + (int64_t)r * lda + kp);
+            lds[kp * CS_LD + r] = t.x;
+            lds[(kp + 1) * CS_LD + r] = t.y;
+        }
+        double a[4][8];
+#pragma unroll
+        for (int rr = 0; rr < 4; rr++)
+#pragma unroll
+            for (int cc = 0; cc < 8; cc++) {
+                const int r = 4 * tr + rr, c = col(cc);
+                a[rr][cc] = (r < nb && c < nb) ? (c <= r ? C[(int64_t)r * lda + c] : C[(int64_t)c * lda + r]) : 0.0;
+            }
+        __syncthreads();
+        for (int k = 0; k < GJ_NB; k++) {
+            const double* lr = lds + k * CS_LD;
+            const cs_d2 p01 = *reinterpret_cast<const cs_d2*>(lr + 4 * tr);
+            const cs_d2 p23 = *reinterpret_cast<const cs_d2*>(lr + 4 * tr + 2);
+            const double pr[4] = {p01.x, p01.y, p23.x, p23.y};
+            double pc[8];
+#pragma unroll
+            for (int g = 0; g < 4; g++) {
+                const cs_d2 q = *reinterpret_cast<const cs_d2*>(lr + g * 32 + 2 * tc);
+                pc[2 * g] = q.x;
+                pc[2 * g + 1] = q.y;
+            }
+#pragma unroll
+            for (int rr = 0; rr < 4; rr++)
+#pragma unroll
+                for (int cc = 0; cc < 8; cc++) a[rr][cc] = fma(-pr[rr], pc[cc], a[rr][cc]);
+        }
+#pragma unroll
+        for (int rr = 0; rr < 4; rr++)
+#pragma unroll
+            for (int cc = 0; cc < 8; cc++)
+                if (4 * tr + rr == col(cc)) dg[4 * tr + rr] = a[rr][cc];
+        __syncthreads();
+        chol_sweep128_body(a, [&](int r) { return dg[r]; }, nb, scr, info, 0, k1);
+        return;
+    }
+    // ---- update tiles: tile list = the triangle of tile rows 0..Nt-1, then the rows below it
+    const int h = __builtin_amdgcn_readfirstlane(tid >> 8), t = tid & 255, tr = t >> 4, tc = t & 15;
+    int64_t idx = 1 + 2 * ((int64_t)blockIdx.x - 1) + h;
+    const bool live = idx < ntiles;
+    if (!live) idx = ntiles - 1;  // a real tile: its loads stay in bounds, nothing is stored
+    int64_t tm, tn;
+    const int64_t T = Nt * (Nt + 1) / 2;
+    if (idx < T) {
+        tm = (int64_t)((sqrt(8.0 * (double)idx + 1.0) - 1.0) * 0.5);
+        while (tm * (tm + 1) / 2 > idx) tm--;
+        while ((tm + 1) * (tm + 2) / 2 <= idx) tm++;
+        tn = idx - tm * (tm + 1) / 2;
+    } else {
+        tm = Nt + (idx - T) / Nt;
+        tn = (idx - T) % Nt;
+    }
+    tm = (int64_t)__builtin_amdgcn_readfirstlane((int)tm);
+    tn = (int64_t)__builtin_amdgcn_readfirstlane((int)tn);
+    const int64_t m0 = tm * GJ_NB, n0 = tn * GJ_NB;
+    double* As = lds + h * (2 * 2 * CS_BK * CS_LD);  // [buf][k][m]
+    double* Bs = As + 2 * CS_BK * CS_LD;
+    double acc[2][4][2][4];
+#pragma unroll
+    for (int hi = 0; hi < 2; hi++)
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+#pragma unroll
+            for (int hj = 0; hj < 2; hj++)
+#pragma unroll
+                for (int j = 0; j < 4; j++) acc[hi][i][hj][j] = 0.0;
+    cs_d2 ra[4], rb[4];
+    const bool rows_in = m0 + GJ_NB <= M && n0 + GJ_NB <= M;  // uniform: no per-row checks on the loads
+    auto gload = [&](int kk0) {
+        if (rows_in) {
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+                const int v = t + 256 * q, row = v >> 3, kp = (v & 7) * 2;
+                ra[q] = *reinterpret_cast<const cs_d2*>(L + (m0 + row) * lda + kk0 + kp);
+                rb[q] = *reinterpret_cast<const cs_d2*>(L + (n0 + row) * lda + kk0 + kp);
+            }
+        } else {
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+                const int v = t + 256 * q, row = v >> 3, kp = (v & 7) * 2;
+                const int64_t gm = m0 + row, gn = n0 + row;
+                ra[q] = gm < M ? *reinterpret_cast<const cs_d2*>(L + gm * lda + kk0 + kp) : cs_d2{0.0, 0.0};
+                rb[q] = gn < M ? *reinterpret_cast<const cs_d2*>(L + gn * lda + kk0 + kp) : cs_d2{0.0, 0.0};
+            }
+        }
+    };
+    auto sstore = [&](int buf) {
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+            const int v = t + 256 * q, row = v >> 3, kp = (v & 7) * 2;
+            As[(buf * CS_BK + kp) * CS_LD + row] = ra[q].x;
+            As[(buf * CS_BK + kp + 1) * CS_LD + row] = ra[q].y;
+            Bs[(buf * CS_BK + kp) * CS_LD + row] = rb[q].x;
+            Bs[(buf * CS_BK + kp + 1) * CS_LD + row] = rb[q].y;
+        }
+    };
+    gload(0);
+    sstore(0);
+    __syncthreads();
+    int buf = 0;
+    for (int kk0 = 0; kk0 < GJ_NB; kk0 += CS_BK) {
+        const bool more = kk0 + CS_BK < GJ_NB;
+        if (more) gload(kk0 + CS_BK);
+#pragma unroll 2
+        for (int kk = 0; kk < CS_BK; kk++) {
+            const double* ar = As + (buf * CS_BK + kk) * CS_LD;
+            const double* br = Bs + (buf * CS_BK + kk) * CS_LD;
+            double av[2][4], bv[2][4];
+#pragma unroll
+            for (int hh = 0; hh < 2; hh++) {
+#pragma unroll
+                for (int i = 0; i < 4; i += 2) {
+                    const cs_d2 x = *reinterpret_cast<const cs_d2*>(ar + hh * 64 + tr * 4 + i);
+                    av[hh][i] = x.x;
+                    av[hh][i + 1] = x.y;
+                }
+#pragma unroll
+                for (int j = 0; j < 4; j += 2) {
+                    const cs_d2 x = *reinterpret_cast<const cs_d2*>(br + hh * 64 + (j >> 1) * 32 + 2 * tc);
+                    bv[hh][j] = x.x;
+                    bv[hh][j + 1] = x.y;
+                }
+            }
+#pragma unroll
+            for (int hi = 0; hi < 2; hi++)
+#pragma unroll
+                for (int i = 0; i < 4; i++)
+#pragma unroll
+                    for (int hj = 0; hj < 2; hj++)
+#pragma unroll
+                        for (int j = 0; j < 4; j++) acc[hi][i][hj][j] = fma(av[hi][i], bv[hj][j], acc[hi][i][hj][j]);
+        }
+        if (more) sstore(buf ^ 1);
+        __syncthreads();
+        buf ^= 1;
+    }
+    if (!live) return;
+    const bool full = m0 + GJ_NB <= M && n0 + GJ_NB <= N;
+    // C -= acc, half a tile at a time: every load of C is issued before the first store (the stores
+    // could alias later loads, so interleaved they would wait for each other)
+#pragma unroll
+    for (int hi = 0; hi < 2; hi++) {
+        if (full) {
+            cs_d2 cv[4][2][2];
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+#pragma unroll
+                for (int hj = 0; hj < 2; hj++)
+#pragma unroll
+                    for (int j = 0; j < 4; j += 2) {
+                        const int64_t m = m0 + hi * 64 + tr * 4 + i, c = n0 + hj * 64 + (j >> 1) * 32 + 2 * tc;
+                        cv[i][hj][j >> 1] = *reinterpret_cast<const cs_d2*>(C + m * lda + c);
+                    }
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+#pragma unroll
+                for (int hj = 0; hj < 2; hj++)
+#pragma unroll
+                    for (int j = 0; j < 4; j += 2) {
+                        const int64_t m = m0 + hi * 64 + tr * 4 + i, c = n0 + hj * 64 + (j >> 1) * 32 + 2 * tc;
+                        cs_d2 v = cv[i][hj][j >> 1];
+                        v.x -= acc[hi][i][hj][j];
+                        v.y -= acc[hi][i][hj][j + 1];
+                        *reinterpret_cast<cs_d2*>(C + m * lda + c) = v;
+                    }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+#pragma unroll
+                for (int hj = 0; hj < 2; hj++)
+#pragma unroll
+                    for (int j = 0; j < 4; j += 2) {
+                        const int64_t m = m0 + hi * 64 + tr * 4 + i, c = n0 + hj * 64 + (j >> 1) * 32 + 2 * tc;
+                        double* p = C + m * lda + c;
+                        if (m < M) {
+                            if (c < N) p[0] -= acc[hi][i][hj][j];
+                            if (c + 1 < N) p[1] -= acc[hi][i][hj][j + 1];
+                        }
+                    }
+        }
+    }
+}
+
+
 }  // namespace kq
 
 kq_status kq::chol_inv_diag128(double* A, int64_t lda, int64_t sA, double* X, int64_t ldx, int64_t sX, int64_t n,
@@ -724,6 +963,31 @@ kq_status kq::chol_inv_diag128(double* A, int64_t lda, int64_t sA, double* X, in
 }
 
 int64_t kq::chol_scratch_doubles() { return CHOL_SCR; }
+
+kq_status kq::chol_step_fused(double* A, int64_t lda, int64_t n, int64_t k0, int64_t J1, double* scr, int32_t* info,
+                              hipStream_t st) {
+    const int64_t k1 = k0 + GJ_NB;
+    if (k1 >= J1 || J1 > n || (lda & 1) || (reinterpret_cast<uintptr_t>(A) & 15) || !scr)
+        return fail(KQ_EINVAL, "chol_step_fused: bad step");
+    const int64_t Mt = (n - k1 + GJ_NB - 1) / GJ_NB, Nt = (J1 - k1 + GJ_NB - 1) / GJ_NB;
+    const int64_t ntiles = Nt * (Nt + 1) / 2 + (Mt - Nt) * Nt;
+    static bool attr = false;
+    if (!attr) {
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&chol_step_kernel),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)CS_SMEM);
+        attr = true;
+    }
+    hipLaunchKernelGGL(chol_step_kernel, dim3((unsigned)(1 + ntiles / 2)), dim3(512), CS_SMEM, st, A, lda, n, k0, J1,
+                       ntiles, Nt, scr, info);
+    return check_launch("chol_step");
+}
+
+kq_status kq::chol_extract_diag128(double* A, int64_t lda, double* X, int64_t ldx, int64_t n, int64_t k0, double* scr,
+                                   hipStream_t st) {
+    hipLaunchKernelGGL(chol_extract128_kernel, dim3(1, CHOL_EXTRACT_SPLIT), dim3(512), 0, st, A, lda, (int64_t)0, X, ldx,
+                       (int64_t)0, n, k0, scr, nullptr);
+    return check_launch("chol_extract128");
+}
 
 namespace kq {
 

@@ -115,6 +115,14 @@ kq_status chol_inv_diag128(double* A, int64_t lda, int64_t sA, double* X, int64_
                            int64_t k0, int64_t batch, double* scr, int32_t* info, int64_t info_stride,
                            const int* skip, hipStream_t st);
 int64_t chol_scratch_doubles();
+// One step k0 of a single matrix's blocked Cholesky (128-wide blocks, lda even, A 16-byte aligned): the
+// update A[k1:n, k1:J1] -= L L^T by the columns k0..k1 = k0 + 128 just factored (lower tiles only, the
+// diagonal block k1 left as it was) together with the sweep of that diagonal block, updated, into scr
+// (k1 < J1 <= n). chol_extract_diag128 then writes its factor into A and its inverse into X.
+kq_status chol_step_fused(double* A, int64_t lda, int64_t n, int64_t k0, int64_t J1, double* scr, int32_t* info,
+                          hipStream_t st);
+kq_status chol_extract_diag128(double* A, int64_t lda, double* X, int64_t ldx, int64_t n, int64_t k0, double* scr,
+                               hipStream_t st);
 
 // Square root of one SPD n x n fp64 matrix A by the scaled Denman-Beavers iteration (the same
 // iteration as kq_hg_sqrt). On return *Y64 points into ws: A^{1/2} (n x n) followed by A^{-1/2}.

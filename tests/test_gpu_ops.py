@@ -266,10 +266,11 @@ def test_rotate_out(form, o, i, blk):
 
 
 # ----------------------------------------------------------------------------- damped factor
-@pytest.mark.parametrize("i", [200, 384, 1000, 128, 6200])
+@pytest.mark.parametrize("i", [200, 384, 1000, 128, 6200, 333, 6147])
 def test_cholinv(i):
     """Widths of 6144 and more take the two-level panel factorisation (6200: a ragged last panel and
-    diagonal block)."""
+    diagonal block). Even widths run each step's update and the next diagonal sweep in one launch
+    (200, 1000, 6200: ragged last tiles); odd widths (333, 6147) keep separate launches."""
     torch, dev = torch_dev()
     say(f"cholinv i={i}")
     sp = synth.scaled(synth.CONFIGS["C2"], n=(4 if i < 4096 else 2) * i, i=i, n_outliers=max(1, i // 100))
