@@ -1115,13 +1115,24 @@ __global__ void damp_kernel(const double* H, int64_t n, int64_t ldh, double damp
 }
 
 // Hr[a][b] = H[n-1-a][n-1-b] + lambda [a == b] in fp64, lower triangle only (read from H's lower
-// triangle).
-__global__ void reverse_damped_kernel(const double* H, int64_t n, int64_t ldh, const double* lam, double* Hr) {
-    const int64_t a = blockIdx.y;
-    for (int64_t b = blockIdx.x * 256 + threadIdx.x; b <= a && b < n; b += (int64_t)gridDim.x * 256) {
-        double v = H[(n - 1 - b) * ldh + (n - 1 - a)];
-        if (a == b) v += *lam;
-        Hr[a * n + b] = v;
+// triangle: H[n-1-b][n-1-a]). 64 x 64 tiles of Hr through LDS, so that the reads run along rows of H
+// and the writes along rows of Hr; tiles above the diagonal return at once.
+__global__ __launch_bounds__(256) void reverse_damped_kernel(const double* H, int64_t n, int64_t ldh, const double* lam,
+                                                             double* Hr) {
+    __shared__ double t[64][65];
+    const int64_t a0 = (int64_t)blockIdx.y * 64, b0 = (int64_t)blockIdx.x * 64;
+    if (b0 > a0) return;
+    const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+    const int64_t a = a0 + 63 - tx;  // lane tx reads column n-1-a of H: consecutive lanes, consecutive columns
+    for (int j = ty; j < 64; j += 4) {
+        const int64_t b = b0 + j;
+        if (a < n && b < n && b <= a) t[63 - tx][j] = H[(n - 1 - b) * ldh + (n - 1 - a)];
+    }
+    __syncthreads();
+    const double l = *lam;
+    for (int i = ty; i < 64; i += 4) {
+        const int64_t ar = a0 + i, b = b0 + tx;
+        if (ar < n && b <= ar) Hr[ar * n + b] = t[i][tx] + (ar == b ? l : 0.0);
     }
 }
 
@@ -1216,7 +1227,8 @@ extern "C" kq_status kq_cholinv(const double* HX, int64_t n, int64_t ldh, double
     KQ_TRY(check_launch("damp"));
     dim3 g2((unsigned)((n + 255) / 256 < 64 ? (n + 255) / 256 : 64), (unsigned)n);
     if (n > 65535) return fail(KQ_ESHAPE, "kq_cholinv: n too large");
-    hipLaunchKernelGGL(reverse_damped_kernel, g2, dim3(256), 0, st, HX, n, ldh, lam, Hr);
+    const unsigned nt64 = (unsigned)((n + 63) / 64);
+    hipLaunchKernelGGL(reverse_damped_kernel, dim3(nt64, nt64), dim3(256), 0, st, HX, n, ldh, lam, Hr);
     KQ_TRY(check_launch("reverse"));
     KQ_TRY(fill<double>(X, (size_t)n * n, 0.0, st));
     if (n >= PANELS_FROM) KQ_TRY(potrf_panels(Hr, n, PANEL_W, X, info, Cscr, st));
