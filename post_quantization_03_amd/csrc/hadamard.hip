@@ -117,34 +117,40 @@ __global__ void paley_kernel(T* P, int m, Field f, int transpose) {
 
 // ------------------------------------------------------------------------------ row transform
 // IN: 0 = bf16 bits, 1 = fp32, 2 = fp64. T: arithmetic and output type (fp32 or fp64).
+// Work-group b transforms the seg columns [s0, s0 + seg) of row r (r = b / (d / seg), s0 = (b % (d /
+// seg)) * seg): the whole row when p2 = d, else a run of whole 2^lp2 chunks, so that the LDS tile stays
+// small and many work-groups share a compute unit. Loads are issued eight vectors at a time.
 template <int IN, typename T>
 __global__ __launch_bounds__(256) void fwht_rows_kernel(const void* __restrict__ in, int64_t ldin, T* __restrict__ out,
-                                                        int64_t ldout, int64_t d, int lp2, const int8_t* __restrict__ pre,
-                                                        const int8_t* __restrict__ post, T scale,
-                                                        const float* __restrict__ post_scale) {
+                                                        int64_t ldout, int64_t d, int64_t seg, int lp2,
+                                                        const int8_t* __restrict__ pre, const int8_t* __restrict__ post,
+                                                        T scale, const float* __restrict__ post_scale) {
     extern __shared__ __align__(16) unsigned char xr_raw[];
     T* xr = reinterpret_cast<T*>(xr_raw);
-    const int64_t r = blockIdx.x;
+    const int64_t nseg = d / seg;
+    const int64_t r = blockIdx.x / nseg, s0 = (blockIdx.x % nseg) * seg;
     const int tid = threadIdx.x;
-    for (int64_t c = 4 * tid; c < d; c += 1024) {
+#pragma unroll 8
+    for (int64_t c = 4 * tid; c < seg; c += 1024) {
+        const int64_t gc = s0 + c;
         T v[4];
         if (IN == 0) {
-            const uint2 u = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(in) + r * ldin + c);
+            const uint2 u = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(in) + r * ldin + gc);
             v[0] = (T)__uint_as_float(u.x << 16);
             v[1] = (T)__uint_as_float(u.x & 0xFFFF0000u);
             v[2] = (T)__uint_as_float(u.y << 16);
             v[3] = (T)__uint_as_float(u.y & 0xFFFF0000u);
         } else if (IN == 1) {
-            const float4 u = *reinterpret_cast<const float4*>(static_cast<const float*>(in) + r * ldin + c);
+            const float4 u = *reinterpret_cast<const float4*>(static_cast<const float*>(in) + r * ldin + gc);
             v[0] = (T)u.x; v[1] = (T)u.y; v[2] = (T)u.z; v[3] = (T)u.w;
         } else {
-            const double* src = static_cast<const double*>(in) + r * ldin + c;
+            const double* src = static_cast<const double*>(in) + r * ldin + gc;
             const double2 u0 = *reinterpret_cast<const double2*>(src);
             const double2 u1 = *reinterpret_cast<const double2*>(src + 2);
             v[0] = (T)u0.x; v[1] = (T)u0.y; v[2] = (T)u1.x; v[3] = (T)u1.y;
         }
 #pragma unroll
-        for (int e = 0; e < 4; e++) xr[c + e] = pre ? v[e] * (T)pre[c + e] : v[e];
+        for (int e = 0; e < 4; e++) xr[c + e] = pre ? v[e] * (T)pre[gc + e] : v[e];
     }
     __syncthreads();
     const int64_t p2 = int64_t(1) << lp2;
@@ -152,7 +158,7 @@ __global__ __launch_bounds__(256) void fwht_rows_kernel(const void* __restrict__
     while ((int64_t(1) << lh) < p2) {
         const int64_t h = int64_t(1) << lh;
         if (2 * h < p2) {
-            for (int64_t g = tid; g < d / 4; g += 256) {
+            for (int64_t g = tid; g < seg / 4; g += 256) {
                 const int64_t j = ((g >> lh) << (lh + 2)) + (g & (h - 1));
                 const T a0 = xr[j], a1 = xr[j + h], a2 = xr[j + 2 * h], a3 = xr[j + 3 * h];
                 const T b0 = a0 + a1, b1 = a0 - a1, b2 = a2 + a3, b3 = a2 - a3;
@@ -163,7 +169,7 @@ __global__ __launch_bounds__(256) void fwht_rows_kernel(const void* __restrict__
             }
             lh += 2;
         } else {
-            for (int64_t g = tid; g < d / 2; g += 256) {
+            for (int64_t g = tid; g < seg / 2; g += 256) {
                 const int64_t j = ((g >> lh) << (lh + 1)) + (g & (h - 1));
                 const T a0 = xr[j], a1 = xr[j + h];
                 xr[j] = a0 + a1;
@@ -173,12 +179,13 @@ __global__ __launch_bounds__(256) void fwht_rows_kernel(const void* __restrict__
         }
         __syncthreads();
     }
-    T* dst = out + r * ldout;
-    for (int64_t c = 4 * tid; c < d; c += 1024) {
+    T* dst = out + r * ldout + s0;
+#pragma unroll 4
+    for (int64_t c = 4 * tid; c < seg; c += 1024) {
 #pragma unroll
         for (int e = 0; e < 4; e++) {
-            T v = post ? xr[c + e] * scale * (T)post[c + e] : xr[c + e] * scale;
-            if (post_scale) v *= (T)post_scale[c + e];
+            T v = post ? xr[c + e] * scale * (T)post[s0 + c + e] : xr[c + e] * scale;
+            if (post_scale) v *= (T)post_scale[s0 + c + e];
             dst[c + e] = v;
         }
     }
@@ -186,7 +193,7 @@ __global__ __launch_bounds__(256) void fwht_rows_kernel(const void* __restrict__
 
 // --------------------------------------------------------------------------- column digit pass
 // Rows r = (hi * D + t) * S + lo, t = 0..D-1, transformed along t for 64 columns per work-group.
-template <typename T>
+template <typename T, int NL>
 __global__ __launch_bounds__(256) void fwht_cols_kernel(const T* __restrict__ in, int64_t ldin, T* __restrict__ out,
                                                         int64_t ldout, int64_t ncols, int lD, int64_t S,
                                                         const float* __restrict__ pre_scale,
@@ -200,12 +207,23 @@ __global__ __launch_bounds__(256) void fwht_cols_kernel(const T* __restrict__ in
     const int64_t c0 = (int64_t)blockIdx.x * 64, lo = blockIdx.y, hi = blockIdx.z;
     const int c = tid & 63;
     const bool cin = c0 + c < ncols;
-    for (int t = tid >> 6; t < D; t += 4) {
-        const int64_t r = (hi * D + t) * S + lo;
-        T v = cin ? in[r * ldin + c0 + c] : T(0);
-        if (pre_scale) v *= (T)pre_scale[r];
-        if (pre_sign) v *= (T)pre_sign[r];
-        xc[t * 64 + c] = v;
+    // every load of the thread is issued before the first LDS store (D <= 4 NL rows)
+    T v[NL];
+#pragma unroll
+    for (int q = 0; q < NL; q++) {
+        const int t = (tid >> 6) + 4 * q;
+        if (t < D) v[q] = cin ? in[((hi * D + t) * S + lo) * ldin + c0 + c] : T(0);
+    }
+#pragma unroll
+    for (int q = 0; q < NL; q++) {
+        const int t = (tid >> 6) + 4 * q;
+        if (t < D) {
+            const int64_t r = (hi * D + t) * S + lo;
+            T x = v[q];
+            if (pre_scale) x *= (T)pre_scale[r];
+            if (pre_sign) x *= (T)pre_sign[r];
+            xc[t * 64 + c] = x;
+        }
     }
     __syncthreads();
     int lh = 0;
@@ -253,9 +271,19 @@ static kq_status rows_transform(const void* in, int in_kind, int64_t ldin, T* ou
     if (R <= 0) return KQ_OK;
     int lp2 = 0;
     while ((int64_t(1) << lp2) < p2) lp2++;
-    const size_t smem = (size_t)d * sizeof(T);
+    // columns per work-group: the whole row, or (several chunks of p2) the most whole chunks, a divisor
+    // of the chunk count, within 2048 columns
+    int64_t seg = d;
+    if (p2 < d) {
+        const int64_t m = d / p2;
+        int64_t g = 1;
+        for (int64_t c = 1; c <= m && c * p2 <= 2048; c++)
+            if (m % c == 0 && (c * p2) % 4 == 0) g = c;
+        seg = (g * p2) % 4 == 0 ? g * p2 : d;
+    }
+    const size_t smem = (size_t)seg * sizeof(T);
     if (smem > 160 * 1024) return fail(KQ_ESHAPE, "row transform: row of %lld elements does not fit in LDS", (long long)d);
-    if (R > 2147483647) return fail(KQ_ESHAPE, "row transform: too many rows");
+    if (R * (d / seg) > 2147483647) return fail(KQ_ESHAPE, "row transform: too many rows");
     static bool attr = false;
     if (!attr) {
         hipFuncSetAttribute(reinterpret_cast<const void*>(&fwht_rows_kernel<0, T>), hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
@@ -263,12 +291,13 @@ static kq_status rows_transform(const void* in, int in_kind, int64_t ldin, T* ou
         hipFuncSetAttribute(reinterpret_cast<const void*>(&fwht_rows_kernel<2, T>), hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
         attr = true;
     }
+    const dim3 grid((unsigned)(R * (d / seg)));
     if (in_kind == 0)
-        hipLaunchKernelGGL((fwht_rows_kernel<0, T>), dim3((unsigned)R), dim3(256), smem, st, in, ldin, out, ldout, d, lp2, pre, post, scale, post_scale);
+        hipLaunchKernelGGL((fwht_rows_kernel<0, T>), grid, dim3(256), smem, st, in, ldin, out, ldout, d, seg, lp2, pre, post, scale, post_scale);
     else if (in_kind == 1)
-        hipLaunchKernelGGL((fwht_rows_kernel<1, T>), dim3((unsigned)R), dim3(256), smem, st, in, ldin, out, ldout, d, lp2, pre, post, scale, post_scale);
+        hipLaunchKernelGGL((fwht_rows_kernel<1, T>), grid, dim3(256), smem, st, in, ldin, out, ldout, d, seg, lp2, pre, post, scale, post_scale);
     else
-        hipLaunchKernelGGL((fwht_rows_kernel<2, T>), dim3((unsigned)R), dim3(256), smem, st, in, ldin, out, ldout, d, lp2, pre, post, scale, post_scale);
+        hipLaunchKernelGGL((fwht_rows_kernel<2, T>), grid, dim3(256), smem, st, in, ldin, out, ldout, d, seg, lp2, pre, post, scale, post_scale);
     return check_launch("fwht_rows");
 }
 
@@ -301,9 +330,15 @@ static kq_status cols_transform(const T* in, int64_t ldin, T* out, int64_t ldout
         const size_t smem = (size_t)D * 64 * sizeof(T);
         dim3 grid((unsigned)((ncols + 63) / 64), (unsigned)S, (unsigned)(R / ((int64_t)D * S)));
         if (S > 65535 || R / ((int64_t)D * S) > 65535) return fail(KQ_ESHAPE, "column transform grid too large");
-        hipLaunchKernelGGL(fwht_cols_kernel<T>, grid, dim3(256), smem, st, first ? in : out, first ? ldin : ldout, out,
-                           ldout, ncols, lD, S, first ? ops.pre_scale : nullptr, first ? ops.pre_sign : nullptr,
-                           last ? ops.post_scale : nullptr, last ? ops.post_sign : nullptr, (T)(last ? ops.scale : 1.0));
+#define KQ_FC(NL_) hipLaunchKernelGGL((fwht_cols_kernel<T, NL_>), grid, dim3(256), smem, st, first ? in : out,               \
+                                   first ? ldin : ldout, out, ldout, ncols, lD, S, first ? ops.pre_scale : nullptr,     \
+                                   first ? ops.pre_sign : nullptr, last ? ops.post_scale : nullptr,                     \
+                                   last ? ops.post_sign : nullptr, (T)(last ? ops.scale : 1.0))
+        if (D <= 16) KQ_FC(4);
+        else if (D <= 64) KQ_FC(16);
+        else if (D <= 128) KQ_FC(32);
+        else KQ_FC(64);
+#undef KQ_FC
         KQ_TRY(check_launch("fwht_cols"));
         S *= D;
         done += lD;
