@@ -1136,9 +1136,27 @@ __global__ __launch_bounds__(256) void reverse_damped_kernel(const double* H, in
     }
 }
 
-// R[a][b] = X[n-1-a][n-1-b] for a <= b (rounded to fp32), 0 below the diagonal.
+// R[a][b] = X[n-1-a][n-1-b] for a <= b (rounded to fp32), 0 below the diagonal. For n a multiple of 4
+// (and R 16-byte aligned) each thread takes four consecutive b: one 16-byte store of R, two 16-byte
+// loads of X.
 __global__ void reverse_upper_kernel(const double* X, int64_t n, float* R) {
     const int64_t a = blockIdx.y;
+    if (n % 4 == 0 && (reinterpret_cast<uintptr_t>(R) & 15) == 0) {
+        const double* xr = X + (n - 1 - a) * n;
+        for (int64_t b = 4 * (blockIdx.x * 256 + threadIdx.x); b < n; b += (int64_t)gridDim.x * 1024) {
+            float4 v = {0.0f, 0.0f, 0.0f, 0.0f};
+            if (b + 3 >= a) {
+                const double2 hi = *reinterpret_cast<const double2*>(xr + (n - 2 - b));   // columns n-2-b, n-1-b
+                const double2 lo = *reinterpret_cast<const double2*>(xr + (n - 4 - b));   // columns n-4-b, n-3-b
+                v.x = b >= a ? (float)hi.y : 0.0f;
+                v.y = b + 1 >= a ? (float)hi.x : 0.0f;
+                v.z = b + 2 >= a ? (float)lo.y : 0.0f;
+                v.w = (float)lo.x;
+            }
+            *reinterpret_cast<float4*>(R + a * n + b) = v;
+        }
+        return;
+    }
     for (int64_t b = blockIdx.x * 256 + threadIdx.x; b < n; b += (int64_t)gridDim.x * 256)
         R[a * n + b] = (b >= a) ? (float)X[(n - 1 - a) * n + (n - 1 - b)] : 0.0f;
 }
@@ -1230,7 +1248,8 @@ extern "C" kq_status kq_cholinv(const double* HX, int64_t n, int64_t ldh, double
     const unsigned nt64 = (unsigned)((n + 63) / 64);
     hipLaunchKernelGGL(reverse_damped_kernel, dim3(nt64, nt64), dim3(256), 0, st, HX, n, ldh, lam, Hr);
     KQ_TRY(check_launch("reverse"));
-    KQ_TRY(fill<double>(X, (size_t)n * n, 0.0, st));
+    // X needs no clearing: the diagonal-block steps write whole 128-wide blocks (zero above the
+    // diagonal), the triangular inverse whole blocks below them, and nothing reads above them
     if (n >= PANELS_FROM) KQ_TRY(potrf_panels(Hr, n, PANEL_W, X, info, Cscr, st));
     else if (n % 2 == 0) KQ_TRY(potrf_panels(Hr, n, n, X, info, Cscr, st));
     else KQ_TRY(potrf_batched<double>(Hr, n, 0, X, n, 0, n, 1, info, 0, nullptr, nullptr, st, Cscr));

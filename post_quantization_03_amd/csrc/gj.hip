@@ -715,10 +715,14 @@ __global__ __launch_bounds__(512) void chol_extract128_kernel(double* __restrict
             }
         }
     }
-    // X = L^{-1}: entry (4 jb + q, c) for c < 4 jb + 4
+    // X = L^{-1}: entry (4 jb + q, c) for c < 4 jb + 4, zero right of that in the block
     for (int e = e0; e < GJ_NB * GJ_NB; e += es) {
         const int r = e >> 7, c = e & 127, jb = r >> 2, q = r & 3;
-        if (c > 4 * jb + 3 || r >= nbk || c >= nbk) continue;
+        if (r >= nbk || c >= nbk) continue;
+        if (c > 4 * jb + 3) {
+            X[(int64_t)r * ldx + c] = 0.0;
+            continue;
+        }
         double t = 0.0;
 #pragma unroll
         for (int q2 = 0; q2 < 4; q2++) t = fma(ljs[jb][q2][q], post[(jb * 4 + q2) * GJ_NB + c], t);

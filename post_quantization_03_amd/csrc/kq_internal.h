@@ -95,7 +95,8 @@ kq_status gemm(const GemmArgs<T>& g, bool ta, bool tb, hipStream_t st);
 
 // ------------------------------------------------------------------------------- SPD toolkit
 // Batched in-place lower Cholesky of n x n matrices A (item stride sA) with the inverses of the
-// diagonal blocks written to X (item stride sX, X must be zero beforehand), logdet[z] += sum log L_ii
+// diagonal blocks written to X (item stride sX; fp32: X must be zero beforehand, fp64: the whole 128-wide
+// diagonal blocks are written, zero above the diagonal), logdet[z] += sum log L_ii
 // (may be null), info[z] set to 1 + index of the first failing pivot (may be null).
 template <typename T>
 kq_status potrf_batched(T* A, int64_t lda, int64_t sA, T* X, int64_t ldx, int64_t sX, int64_t n, int64_t batch,
