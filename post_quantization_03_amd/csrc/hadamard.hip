@@ -353,10 +353,61 @@ static kq_status make_paley(T* P, int64_t m, const Field& f, bool transpose, hip
     return check_launch("paley");
 }
 
+// Paley mix of small order (m <= PM_MAX) in fp32, at HBM rate: every column vector (r, c), r < R,
+// c < C, has its m entries at in + r ldr_in + b gs_in + c (b < m); out gets alpha P times it at the
+// same places of out. A thread takes four adjacent vectors: m 16-byte loads, m^2 4-wide FMAs with P
+// from LDS, m 16-byte stores (a GEMM with K = m < 16 runs on the general tiles at a fraction of this).
+constexpr int PM_MAX = 32;
+typedef float pm_f4 __attribute__((ext_vector_type(4)));
+__global__ __launch_bounds__(256) void paley_mix_kernel(const float* __restrict__ P, int m, const float* __restrict__ in,
+                                                        int64_t ldr_in, int64_t gs_in, float* __restrict__ out,
+                                                        int64_t ldr_out, int64_t gs_out, int64_t R, int64_t C,
+                                                        float alpha) {
+    __shared__ float Ps[PM_MAX * PM_MAX];
+    for (int e = threadIdx.x; e < m * m; e += 256) Ps[e] = P[e];
+    __syncthreads();
+    const int64_t cq = C / 4, tot = R * cq;
+    for (int64_t v = (int64_t)blockIdx.x * 256 + threadIdx.x; v < tot; v += (int64_t)gridDim.x * 256) {
+        const int64_t r = v / cq, c = (v - r * cq) * 4;
+        const float* src = in + r * ldr_in + c;
+        pm_f4 x[PM_MAX];
+#pragma unroll
+        for (int b = 0; b < PM_MAX; b++)
+            if (b < m) x[b] = *reinterpret_cast<const pm_f4*>(src + b * gs_in);
+        float* dst = out + r * ldr_out + c;
+        for (int a = 0; a < m; a++) {
+            pm_f4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int b = 0; b < PM_MAX; b++)
+                if (b < m) acc += Ps[a * m + b] * x[b];
+            *reinterpret_cast<pm_f4*>(dst + a * gs_out) = alpha * acc;
+        }
+    }
+}
+
+static bool paley_mix_ok(int64_t m, int64_t C, const void* in, const void* out, int64_t ldr_in, int64_t gs_in,
+                         int64_t ldr_out, int64_t gs_out) {
+    return m >= 2 && m <= PM_MAX && C % 4 == 0 && aligned16(in) && aligned16(out) && ldr_in % 4 == 0 &&
+           gs_in % 4 == 0 && ldr_out % 4 == 0 && gs_out % 4 == 0;
+}
+
+static kq_status paley_mix(const float* P, int64_t m, const float* in, int64_t ldr_in, int64_t gs_in, float* out,
+                           int64_t ldr_out, int64_t gs_out, int64_t R, int64_t C, float alpha, hipStream_t st) {
+    const int64_t tot = R * (C / 4);
+    if (tot <= 0) return KQ_OK;
+    const int64_t wg = (tot + 255) / 256;
+    hipLaunchKernelGGL(paley_mix_kernel, dim3((unsigned)(wg < 65536 ? wg : 65536)), dim3(256), 0, st, P, (int)m, in,
+                       ldr_in, gs_in, out, ldr_out, gs_out, R, C, alpha);
+    return check_launch("paley_mix");
+}
+
 // out_r = alpha * P in_r for every row r, each row seen as an m x p2 matrix (row mix of chunks).
 template <typename T>
 static kq_status paley_rows(const T* P, const T* in, int64_t ldin, T* out, int64_t ldout, int64_t R, int64_t m,
                             int64_t p2, T alpha, hipStream_t st) {
+    if constexpr (sizeof(T) == 4)
+        if (paley_mix_ok(m, p2, in, out, ldin, p2, ldout, p2))
+            return paley_mix(P, m, in, ldin, p2, out, ldout, p2, R, p2, alpha, st);
     for (int64_t r0 = 0; r0 < R; r0 += 65535) {
         const int64_t cnt = (R - r0) < 65535 ? (R - r0) : 65535;
         GemmArgs<T> g = gemm_args<T>(m, p2, m, P, m, in + r0 * ldin, p2, out + r0 * ldout, p2, alpha, T(0));
@@ -370,6 +421,9 @@ static kq_status paley_rows(const T* P, const T* in, int64_t ldin, T* out, int64
 template <typename T>
 static kq_status paley_cols(const T* P, const T* in, int64_t ldin, T* out, int64_t ldout, int64_t m, int64_t p2,
                             int64_t ncols, T alpha, hipStream_t st) {
+    if constexpr (sizeof(T) == 4)
+        if (paley_mix_ok(m, ncols, in, out, ldin, p2 * ldin, ldout, p2 * ldout))
+            return paley_mix(P, m, in, ldin, p2 * ldin, out, ldout, p2 * ldout, p2, ncols, alpha, st);
     if (ldin == ncols && ldout == ncols) {
         GemmArgs<T> g = gemm_args<T>(m, p2 * ncols, m, P, m, in, p2 * ncols, out, p2 * ncols, alpha, T(0));
         return gemm<T>(g, false, false, st);
