@@ -362,10 +362,12 @@ def test_cholinv_reports_not_positive_definite():
 # ----------------------------------------------------------------------------- sweep
 @pytest.mark.parametrize("o,i,bits,group", [(37, 384, 3, 128), (37, 384, 4, 0), (64, 256, 2, 128), (20, 512, 2, 0),
                                             (16, 256, 3, 64), (9, 256, 8, 32), (130, 1024, 3, 128),
+                                            (130, 2048, 3, 128), (48, 2560, 2, 0),
                                             (16400, 256, 2, 0), (16400, 128, 3, 128)])
 def test_quantize_layer(o, i, bits, group):
     """From 16384 rows the sweep runs on row panels side by side (16400: four panels, the last one
-    shorter and not a multiple of the 16-row work-group)."""
+    shorter and not a multiple of the 16-row work-group). 2048 and 2560 columns take four and five
+    512-column super-blocks, each followed by its deep (K = 512) trailing update."""
     torch, dev = torch_dev()
     say(f"quantize o={o} i={i} b={bits} g={group}")
     tall = o > 4096
