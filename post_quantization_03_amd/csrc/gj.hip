@@ -1263,15 +1263,28 @@ constexpr double DB_TOL = 1e-8;
 constexpr double DB_NS_MAX = 8e-5;
 constexpr int NORM_PARTS = 512;  // at most this many partial sums per matrix (one per work-group)
 
+// Y_0 = H_G in fp64 (also into NI, where the first step's sweep inverts it in place), Z_0 = I, and the
+// call's words cleared: flags, the caller's info, the sweep's hand-over counter and the pivots' info.
+// It is the call's first kernel, and everything that reads those words runs after it on this queue or
+// on queues forked from it (each separate clearing launch had to wait for a compute unit while the
+// work already on the chip drained).
 template <typename T>
-__global__ void db_init_kernel(const T* HG, int64_t n, int64_t nbk, double* YZ, int* flags) {
+__global__ void db_init_kernel(const T* HG, int64_t n, int64_t nbk, double* YZ, double* NI, int* flags,
+                               int32_t* info, uint64_t* ready, int32_t* finfo, int64_t items) {
     const int64_t nn = n * n;
     for (int64_t e = blockIdx.x * 256 + threadIdx.x; e < nbk * nn; e += (int64_t)gridDim.x * 256) {
         const int64_t b = e / nn, rc = e % nn, r = rc / n, c = rc % n;
-        YZ[e] = (double)HG[b * nn + rc];
+        const double h = (double)HG[b * nn + rc];
+        YZ[e] = h;
+        NI[e] = h;
         YZ[(nbk + b) * nn + rc] = (r == c) ? 1.0 : 0.0;
     }
-    if (blockIdx.x == 0 && threadIdx.x < 4) flags[threadIdx.x] = 0;
+    if (blockIdx.x == 0) {
+        if (threadIdx.x < 4) flags[threadIdx.x] = 0;
+        if (threadIdx.x < 2) ready[threadIdx.x] = 0;
+        if (threadIdx.x == 0) *info = 0;
+        for (int64_t k = threadIdx.x; k < items; k += 256) finfo[k] = 0;
+    }
 }
 
 // Partial sums of the squared Frobenius norm of symmetric matrices stored in their lower triangles;
@@ -1515,11 +1528,6 @@ __global__ __launch_bounds__(256) void mirror_lower_batched_kernel(double* M, in
     }
 }
 
-__global__ void copy_d_kernel(const double* src, double* dst, size_t count, const int* skip) {
-    if (*skip) return;
-    for (size_t e = blockIdx.x * (size_t)256 + threadIdx.x; e < count; e += (size_t)gridDim.x * 256) dst[e] = src[e];
-}
-
 __global__ void hg_diag_kernel(const float* h, int64_t o, float* S, float* Si, int32_t* info) {
     for (int64_t r = blockIdx.x * 256 + threadIdx.x; r < o; r += (int64_t)gridDim.x * 256) {
         const float v = h[r];
@@ -1615,28 +1623,24 @@ static kq_status db_sqrt(const float* HGf, const double* HGd, int64_t n, int64_t
     sync.ready = ready;
     sync.early = early;
 
-    KQ_TRY(fill<int>(reinterpret_cast<int*>(info), 1, 0, st));
-    KQ_TRY(fill<int>(reinterpret_cast<int*>(ready), 4, 0, st));
-    KQ_TRY(fill<int>(reinterpret_cast<int*>(finfo), items, 0, st));
     const unsigned eb = (unsigned)((nbk * nn + 255) / 256 < 4096 ? (nbk * nn + 255) / 256 : 4096);
-    if (HGd) hipLaunchKernelGGL(db_init_kernel<double>, dim3(eb), dim3(256), 0, st, HGd, n, nbk, YZ, flags);
-    else hipLaunchKernelGGL(db_init_kernel<float>, dim3(eb), dim3(256), 0, st, HGf, n, nbk, YZ, flags);
+    if (HGd)
+        hipLaunchKernelGGL(db_init_kernel<double>, dim3(eb), dim3(256), 0, st, HGd, n, nbk, YZ, NI, flags, info, ready,
+                           finfo, (int64_t)items);
+    else
+        hipLaunchKernelGGL(db_init_kernel<float>, dim3(eb), dim3(256), 0, st, HGf, n, nbk, YZ, NI, flags, info, ready,
+                           finfo, (int64_t)items);
     KQ_TRY(check_launch("db_init"));
     const int parts = (int)(n < NORM_PARTS ? n : NORM_PARTS);  // row-strided partial sums of ||.||_F^2
     hipLaunchKernelGGL(sym_norm_part_kernel, dim3(parts, (unsigned)nbk), dim3(256), 0, st, YZ, n, (int64_t)nn, nrmA,
                        flags, -1);
     KQ_TRY(check_launch("db_norm"));
-    const unsigned cb = (unsigned)((items * nn + 255) / 256 < 4096 ? (items * nn + 255) / 256 : 4096);
     int nsteps = DB_MAXIT;
     for (int it = 0; it < nsteps; it++) {
         // the first step inverts Y_0 = A only (Z_0 = I); later steps find Y and Z in NI already
         // (written there by the previous step's update)
         const size_t inv_items = it == 0 ? (size_t)nbk : items;
         sync.step = it;
-        if (it == 0) {
-            hipLaunchKernelGGL(copy_d_kernel, dim3(cb), dim3(256), 0, st, YZ, NI, inv_items * nn, done);
-            KQ_TRY(check_launch("db_copy"));
-        }
         KQ_TRY(gj_inverse_batched(NI, n, n, (int64_t)nn, (int64_t)inv_items, C, T, Pinv, finfo, done, &sync, st));
         // ||A^{-1}||_F of Y_0 = A (first step only; NI holds -A^{-1})
         hipLaunchKernelGGL(sym_norm_part_kernel, dim3(parts, (unsigned)nbk), dim3(256), 0, st, NI, n, (int64_t)nn,
