@@ -162,7 +162,7 @@ kq_status kq_rotate_out(float* W, int64_t o, int64_t i, int64_t ldw, const float
  * damping, the damping the smallest workload states).
  *     lambda = damp * mean(diag HX),   H = HX + lambda I,   R upper-triangular, H^{-1} = R^T R
  * computed without forming H^{-1}: with J the reversal permutation, J H J = L L^T (Cholesky) and
- * R = J L^{-1} J. From a width of 6144 the Cholesky is blocked in two levels (1024-wide panels
+ * R = J L^{-1} J. From a width of 6144 the Cholesky is blocked in two levels (2048-wide panels
  * factored in 128-wide steps, then one deep update of the rest per panel); everything runs on
  * `stream`. The factorisation and the triangular inverse run in fp64 (vector FMA products); R is
  * rounded to fp32, so its error is that rounding rather than sqrt(cond(H)) fp32 steps.

@@ -1172,8 +1172,10 @@ __global__ void reverse_upper_kernel(const double* X, int64_t n, float* R) {
 // Measured on MI355X (before the fused steps): layer steps with widths 13824 and 8192 took 2.2 and 1.5
 // ms less with panels than with one step of look-ahead (the diagonal block factored on a side queue
 // beside the trailing update: its kernel needs a whole compute unit and waited for one while the update
-// filled the chip).
-constexpr int64_t PANEL_W = 1024, PANELS_FROM = 6144;
+// filled the chip). Panel widths measured on MI355X: 2048 took less than 512, 1024 and 4096 on the
+// widths 13824 and 8192 (damped factor 53.4 and 17.5 ms with 1024-wide panels, 52.7 and 17.0 with
+// 2048); below 6144 panels took longer than the single 128-wide steps.
+constexpr int64_t PANEL_W = 2048, PANELS_FROM = 6144;
 static kq_status potrf_panels(double* A, int64_t n, int64_t W, double* X, int32_t* info, double* scr, hipStream_t st) {
     constexpr int64_t NB = 128;
     const bool fuse = (n & 1) == 0 && (reinterpret_cast<uintptr_t>(A) & 15) == 0;

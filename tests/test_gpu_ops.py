@@ -366,8 +366,8 @@ def test_cholinv_reports_not_positive_definite():
                                             (16400, 256, 2, 0), (16400, 128, 3, 128)])
 def test_quantize_layer(o, i, bits, group):
     """From 16384 rows the sweep runs on row panels side by side (16400: four panels, the last one
-    shorter and not a multiple of the 16-row work-group). 2048 and 2560 columns take four and five
-    512-column super-blocks, each followed by its deep (K = 512) trailing update."""
+    shorter and not a multiple of the 16-row work-group). 2048 and 2560 columns take two and three
+    1024-column super-blocks, each followed by its deep (K = 1024) trailing update."""
     torch, dev = torch_dev()
     say(f"quantize o={o} i={i} b={bits} g={group}")
     tall = o > 4096
